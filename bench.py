@@ -1,0 +1,187 @@
+#!/usr/bin/env python3
+"""Benchmark: effective TFLOP/s (2MNK / t) of half-precision GEMM on one MI355X.
+
+One step = one pass of the hot path on the 4096^3 bfloat16 workload (A, B
+i.i.d. N(0,1)/sqrt(K), fp32 accumulate, bfloat16 out): plan with the roofline
+cost model (which picks classic, one-level or two-level), then run the planned
+product (for an LCMA plan: combine pre-pass + persistent fused group kernel).
+Inputs are resident in HBM before timing starts.
+
+Besides the step, every algorithm is timed kernel by kernel with HIP events
+on the stream the kernels run on, so the JSON line also reports the classic
+and LCMA rates, the pre-pass bandwidth, the roofline of the dominant kernel
+and the CPU oracle's rate on a bounded sample.
+
+Prints ONE JSON line.  Single GPU only.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA, published
+HBM_GBPS = 8000.0      # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--only", default="", help="time only these algorithms (comma list), for profiling runs")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import complexity_half_precision_amd as L
+    import seeded_inputs as si
+
+    wl = si.SQUARE_4096_BF16
+    M, N, K, dtype = wl["M"], wl["N"], wl["K"], wl["dtype"]
+    dev = "cuda"
+    A, B = si.gen(**wl)
+    Ad, Bd = A.to(dev), B.to(dev)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    flops = 2.0 * M * N * K
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def time_calls(fn, reps, warm):
+        """Mean ms per call over `reps` back-to-back calls, HIP events on the kernels' stream."""
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    detail = {}
+    only = set(a for a in args.only.split(",") if a)
+    plans = {}
+    for algo in ("classic", "l1", "l2"):
+        if only and algo not in only:
+            continue
+        try:
+            p = L.lcma_plan_ex(M, N, K, dtype, force=algo)
+        except L.LcmaError:
+            continue
+        plans[algo] = (p, L.workspace_for(p))
+    reps = max(args.steps, 10)
+    for algo, (p, ws) in plans.items():
+        t_all = time_calls(lambda: L.lcma_gemm(p, Ad, Bd, C, ws), reps, args.warmup)
+        d = {"ms": t_all, "eff_tflops": flops / (t_all * 1e-3) / 1e12, "est_ms": L.lcma_plan_info(p)[2] * 1e3}
+        if algo != "classic":
+            t_pre = time_calls(lambda: L.lcma_prepass(p, Ad, Bd, ws), reps, args.warmup)
+            L.lcma_prepass(p, Ad, Bd, ws)
+            t_fu = time_calls(lambda: L.lcma_fused(p, Ad, Bd, C, ws), reps, args.warmup)
+            R = 7 if algo == "l1" else 49
+            S = 2 if algo == "l1" else 4
+            mfma_flops = 2.0 * R * (M // S) * (N // S) * (K // S)
+            # bytes the pre-pass must move: read A and B once, write the combined operands
+            written = sum(1 for r in range(R) if L.lcma_plan_operand(p, 0, r)[0] >= 0) * (M // S) * (K // S) \
+                + sum(1 for r in range(R) if L.lcma_plan_operand(p, 1, r)[0] >= 0) * (K // S) * (N // S)
+            pre_bytes = 2.0 * (M * K + K * N) + 2.0 * written
+            d.update({"prepass_ms": t_pre, "fused_ms": t_fu, "fused_mfma_tflop": mfma_flops / 1e12,
+                      "fused_tflops_actual": mfma_flops / (t_fu * 1e-3) / 1e12,
+                      "prepass_bytes": pre_bytes, "prepass_gbps": pre_bytes / (t_pre * 1e-3) / 1e9})
+        detail[algo] = d
+
+    # ---- the step: plan + planned product on the workload
+    def step():
+        p = L.lcma_plan(M, N, K, dtype)
+        ws = plans.get(L.lcma_plan_info(p)[0], (None, None))[1]
+        L.lcma_gemm(p, Ad, Bd, C, ws)
+
+    auto = L.lcma_plan(M, N, K, dtype)
+    chosen = L.lcma_plan_info(auto)[0]
+    if chosen not in plans:
+        plans[chosen] = (auto, L.workspace_for(auto))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = max(e0.elapsed_time(e1), 0.0) / args.steps
+    ms_step = max(ms_step, wall * 1e3 / args.steps)
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    # ---- roofline of the dominant kernel of the chosen path
+    if chosen == "classic":
+        t_k = detail["classic"]["ms"]
+        achieved = flops / (t_k * 1e-3) / 1e12
+        kname = "k_classic (256x256 tile)"
+    else:
+        t_k = detail[chosen]["fused_ms"]
+        achieved = detail[chosen]["fused_mfma_tflop"] * 1e12 / (t_k * 1e-3) / 1e12
+        kname = "k_fused"
+    roofline = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 1), "peak": PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": None,
+                "kernel_ms": round(t_k, 4)}
+
+    out = {
+        "metric": "effective TFLOP/s (2MNK/t) FP16/BF16 GEMM at 1 GPU; % of MFMA peak",
+        "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "square GEMM M=N=K=4096, bf16 A,B ~ N(0,1)/sqrt(K), fp32 accumulate, bf16 out",
+                   "M": M, "N": N, "K": K, "algo_chosen": chosen},
+        "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2),
+        "roofline": roofline,
+        "detail": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                   for k, v in detail.items()},
+    }
+    if "l1" in detail and "classic" in detail:
+        out["l1_over_classic"] = round(detail["classic"]["ms"] / detail["l1"]["ms"], 4)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(A, B, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(A, B, target_s):
+    """The fp64 oracle on a row slice of the same product (all host threads)."""
+    import numpy as np
+    import oracle
+    import seeded_inputs as si
+    A64, B64 = si.f64(A), si.f64(B)
+    M, K = A64.shape
+    N = B64.shape[1]
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    rows = 64
+    t0 = time.perf_counter()
+    oracle.gemm_rows(A64, B64, 0, rows)
+    dt = time.perf_counter() - t0
+    rows = int(min(M, max(64, rows * target_s / max(dt, 1e-6))))
+    t0 = time.perf_counter()
+    oracle.gemm_rows(A64, B64, 0, rows)
+    dt = time.perf_counter() - t0
+    tflops = 2.0 * rows * N * K / dt / 1e12
+    return {"value": round(tflops, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"rows 0..{rows} of the {M}x{N}x{K} product (fp64, k ascending), {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

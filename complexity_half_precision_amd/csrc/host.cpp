@@ -1,0 +1,754 @@
+// host.cpp -- C ABI of the library: descriptor checks, the roofline cost
+// model, the planner (geometry, persistent schedule, workspace layout) and
+// the launch orchestration of the gfx950 kernels.
+//
+// Sources: "FalconGEMM: Surpassing Hardware Peaks with Lower-Complexity
+// Matrix Multiplication" (HyperAI write-up), sections "从 Strassen 出发" (LCMA
+// description), "从 LCMA 到 FalconGEMM" (pipeline, groups, split) and
+// "从缓存重排到 Cost Model" (a roofline-like model from FLOPs, bytes and the
+// target GPU's peak and bandwidth that aims to pick the right algorithm, not
+// to predict time); "Kernel 与性能" notes, section "Roofline".
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "kernels.hpp"
+#include "lcma.h"
+#include "schedule.hpp"
+#include "strassen.hpp"
+
+using namespace lcma;
+
+namespace {
+
+// ---------------------------------------------------------------- descriptors
+
+int8_t g_U1[7 * 4], g_V1[7 * 4], g_W1[7 * 4];
+int8_t g_U2[49 * 16], g_V2[49 * 16], g_W2[49 * 16];
+std::once_flag g_tables_once;
+
+void init_tables()
+{
+    for (int r = 0; r < 7; ++r)
+        for (int b = 0; b < 4; ++b) {
+            g_U1[r * 4 + b] = (int8_t)Scheme<1>::u(r, b / 2, b % 2);
+            g_V1[r * 4 + b] = (int8_t)Scheme<1>::v(r, b / 2, b % 2);
+            g_W1[r * 4 + b] = (int8_t)Scheme<1>::w(r, b / 2, b % 2);
+        }
+    for (int r = 0; r < 49; ++r)
+        for (int b = 0; b < 16; ++b) {
+            g_U2[r * 16 + b] = (int8_t)Scheme<2>::u(r, b / 4, b % 4);
+            g_V2[r * 16 + b] = (int8_t)Scheme<2>::v(r, b / 4, b % 4);
+            g_W2[r * 16 + b] = (int8_t)Scheme<2>::w(r, b / 4, b % 4);
+        }
+}
+
+bool desc_shape_ok(const lcma_desc* d)
+{
+    return d->ms >= 1 && d->ks >= 1 && d->ns >= 1 && d->rank >= 1 && d->ms <= 16 && d->ks <= 16 &&
+           d->ns <= 16 && d->rank <= 4096 && d->U && d->V && d->W;
+}
+
+// Brent's identity, exact integers: for every (i,k) of A, (k2,j) of B and
+// (i2,j2) of C, sum_r U[r][i,k] V[r][k2,j] W[r][i2,j2] = [k==k2][i==i2][j==j2].
+bool brent_ok(const lcma_desc* d)
+{
+    const int ms = d->ms, ks = d->ks, ns = d->ns, R = d->rank;
+    for (int x = 0; x < R * ms * ks; ++x)
+        if (d->U[x] < -8 || d->U[x] > 8)
+            return false;
+    for (int x = 0; x < R * ks * ns; ++x)
+        if (d->V[x] < -8 || d->V[x] > 8)
+            return false;
+    for (int x = 0; x < R * ms * ns; ++x)
+        if (d->W[x] < -8 || d->W[x] > 8)
+            return false;
+    for (int i = 0; i < ms; ++i)
+        for (int k = 0; k < ks; ++k)
+            for (int k2 = 0; k2 < ks; ++k2)
+                for (int j = 0; j < ns; ++j)
+                    for (int i2 = 0; i2 < ms; ++i2)
+                        for (int j2 = 0; j2 < ns; ++j2) {
+                            long s = 0;
+                            for (int r = 0; r < R; ++r)
+                                s += (long)d->U[r * ms * ks + i * ks + k] * d->V[r * ks * ns + k2 * ns + j] *
+                                     d->W[r * ms * ns + i2 * ns + j2];
+                            if (s != ((k == k2 && i == i2 && j == j2) ? 1 : 0))
+                                return false;
+                        }
+    return true;
+}
+
+// 1 / 2 when d is exactly the built-in one- / two-level Strassen scheme, else 0.
+int builtin_kind(const lcma_desc* d)
+{
+    std::call_once(g_tables_once, init_tables);
+    if (d->ms == 2 && d->ks == 2 && d->ns == 2 && d->rank == 7 && !memcmp(d->U, g_U1, 28) &&
+        !memcmp(d->V, g_V1, 28) && !memcmp(d->W, g_W1, 28))
+        return 1;
+    if (d->ms == 4 && d->ks == 4 && d->ns == 4 && d->rank == 49 && !memcmp(d->U, g_U2, 784) &&
+        !memcmp(d->V, g_V2, 784) && !memcmp(d->W, g_W2, 784))
+        return 2;
+    return 0;
+}
+
+// ---------------------------------------------------------------- device facts
+
+int query_cus(int* out)
+{
+    static std::mutex mu;
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return -1;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!cached[dev]) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            return -1;
+        cached[dev] = v;
+    }
+    *out = cached[dev];
+    return 0;
+}
+
+bool log_enabled()
+{
+    static int v = -1;
+    if (v < 0) {
+        const char* e = getenv("LCMA_LOG");
+        v = (e && *e && *e != '0') ? 1 : 0;
+    }
+    return v == 1;
+}
+
+// ---------------------------------------------------------------- cost model
+//
+// t(alg) = sum over its kernels of
+//          max( F / (eta_F * peak * q),  B_hbm / (eta_B * bw),  F / (I_tile * bw_L2 * q) )
+//          + t_launch
+// F: MFMA flops of the kernel; B_hbm: the bytes it must move at least;
+// I_tile: flops per byte a workgroup tile draws from L2 (BM*BN/(BM+BN) for a
+// BM x BN tile); q: wave-quantisation efficiency = (work units / P) /
+// (rounds actually needed).  The first two terms are the roofline of the
+// notes page; the L2 term keeps small fused tiles from looking free, and q is
+// the tail effect the FalconGEMM write-up measures on coarse groups.
+
+struct Machine {
+    double peak, bw, l2bw, launch;
+    double eta_mfma, eta_fused, eta_bw;
+    int P;
+};
+
+double quant(double units, int P)
+{
+    if (units <= 0)
+        return 1.0;
+    const double rounds = std::ceil(units / P);
+    return units / (rounds * P);
+}
+
+double kernel_time(double F, double B, double itile, double q, double eta, const Machine& m)
+{
+    double t = F / (eta * m.peak * q);
+    t = std::max(t, B / (m.eta_bw * m.bw));
+    if (itile > 0)
+        t = std::max(t, F / (itile * m.l2bw * q));
+    return t + m.launch;
+}
+
+int classic_tile_for(int64_t M, int64_t N, int P)
+{
+    if (M <= 64)
+        return kTile32;
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    if (t256 >= P)
+        return kTile256;
+    return kTile128;
+}
+
+double est_classic(int64_t M, int64_t N, int64_t K, const Machine& m)
+{
+    const double s = 2.0;
+    const double F = 2.0 * M * N * K;
+    const double B = s * ((double)M * K + (double)K * N + (double)M * N);
+    int bm, bn;
+    classic_tile_dims(classic_tile_for(M, N, m.P), &bm, &bn);
+    const double tiles = (double)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    return kernel_time(F, B, (double)bm * bn / (bm + bn), quant(tiles, m.P), m.eta_mfma, m);
+}
+
+// Geometry of an LCMA plan at `levels`.
+struct Geo {
+    int64_t Mb, Nb, Kb;
+    int tile, gy, gx, G, R, S;
+};
+
+Geo lcma_geo(int64_t M, int64_t N, int64_t K, int levels)
+{
+    Geo g;
+    g.S = levels == 1 ? 2 : 4;
+    g.R = levels == 1 ? 7 : 49;
+    g.Mb = M / g.S; g.Nb = N / g.S; g.Kb = K / g.S;
+    g.tile = fused_tile(levels);
+    g.gy = (int)((g.Mb + g.tile - 1) / g.tile);
+    g.gx = (int)((g.Nb + g.tile - 1) / g.tile);
+    g.G = g.gy * g.gx;
+    return g;
+}
+
+int split_mode_for(lcma_split req, int G, int P)
+{
+    if (req == LCMA_SPLIT_NONE)
+        return kSplitNone;
+    if (req == LCMA_SPLIT_ALL)
+        return kSplitAll;
+    const int T = G % P;
+    return (T > 0 && 2 * T <= P) ? kSplitTail : kSplitNone;
+}
+
+// Number of combined operands the pre-pass writes per side.
+void written_counts(int levels, bool write_all, int* nA, int* nB)
+{
+    std::call_once(g_tables_once, init_tables);
+    const int R = levels == 1 ? 7 : 49, SS = levels == 1 ? 4 : 16;
+    const int8_t* U = levels == 1 ? g_U1 : g_U2;
+    const int8_t* V = levels == 1 ? g_V1 : g_V2;
+    *nA = *nB = 0;
+    for (int r = 0; r < R; ++r) {
+        int a = 0, b = 0;
+        for (int x = 0; x < SS; ++x) {
+            a += U[r * SS + x] != 0;
+            b += V[r * SS + x] != 0;
+        }
+        *nA += (write_all || a > 1);
+        *nB += (write_all || b > 1);
+    }
+}
+
+double est_lcma(int64_t M, int64_t N, int64_t K, int levels, int split_req, bool write_all, const Machine& m)
+{
+    const double s = 2.0;
+    const Geo g = lcma_geo(M, N, K, levels);
+    int nA, nB;
+    written_counts(levels, write_all, &nA, &nB);
+    // pre-pass: read A and B once, write the combined operands
+    const double Bpre = s * ((double)M * K + (double)K * N) +
+                        s * (nA * (double)g.Mb * g.Kb + nB * (double)g.Kb * g.Nb);
+    const double t_pre = Bpre / (m.eta_bw * m.bw) + m.launch;
+    // fused: R products of Mb x Nb x Kb
+    const double F = 2.0 * g.R * (double)g.Mb * g.Nb * g.Kb;
+    const double Bf = s * g.R * ((double)g.Mb * g.Kb + (double)g.Kb * g.Nb) + s * (double)M * N;
+    const int mode = split_mode_for((lcma_split)split_req, g.G, m.P);
+    double q;
+    if (mode == kSplitTail) {
+        const double rounds = (double)(g.G / m.P) + 0.5;
+        q = ((double)g.G / m.P) / rounds;
+    } else {
+        q = quant(g.G, m.P);
+    }
+    const double t_f = kernel_time(F, Bf, g.tile / 2.0, q, m.eta_fused, m);
+    return t_pre + t_f;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- plan
+
+struct lcma_plan_s {
+    int64_t M, N, K;
+    lcma_dtype dt;
+    lcma_algo chosen;
+    int levels;            // 0 = classic
+    int op_bf16;           // combined-operand type (LCMA)
+    int write_all;         // pre-pass copies single-block operands too
+    int classic_tile;
+    int P;
+    Geo geo;
+    SchedParams sp;
+    int grid;
+    int8_t order[kMaxRank];
+    int n_slots;
+    int64_t offA, offB, offPart, offCtr;
+    int64_t slotA[kMaxRank], slotB[kMaxRank];   // index among written operands, -1 = in place
+    int blockA[kMaxRank], blockB[kMaxRank];     // block index of an in-place operand
+    size_t ws_bytes;
+    double est[4];
+};
+
+static int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+extern "C" {
+
+const char* lcma_status_str(lcma_status s)
+{
+    switch (s) {
+    case LCMA_OK: return "ok";
+    case LCMA_E_INVALID: return "invalid argument";
+    case LCMA_E_UNSUPPORTED: return "unsupported shape, alignment or algorithm";
+    case LCMA_E_BAD_DESCRIPTOR: return "descriptor fails Brent's identity or is malformed";
+    case LCMA_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case LCMA_E_HIP: return "HIP runtime error";
+    case LCMA_E_NOMEM: return "out of host memory";
+    }
+    return "unknown status";
+}
+
+lcma_status lcma_desc_builtin(int32_t levels, lcma_desc* out)
+{
+    if (!out || (levels != 1 && levels != 2))
+        return LCMA_E_INVALID;
+    std::call_once(g_tables_once, init_tables);
+    if (levels == 1)
+        *out = lcma_desc{2, 2, 2, 7, g_U1, g_V1, g_W1};
+    else
+        *out = lcma_desc{4, 4, 4, 49, g_U2, g_V2, g_W2};
+    return LCMA_OK;
+}
+
+lcma_status lcma_desc_validate(const lcma_desc* d)
+{
+    if (!d)
+        return LCMA_E_INVALID;
+    if (!desc_shape_ok(d) || !brent_ok(d))
+        return LCMA_E_BAD_DESCRIPTOR;
+    return LCMA_OK;
+}
+
+lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const lcma_desc* desc,
+                         lcma_algo force, const lcma_options* opts, lcma_plan_t* out)
+{
+    if (!out)
+        return LCMA_E_INVALID;
+    *out = nullptr;
+    if (M < 0 || N < 0 || K < 0 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+        return LCMA_E_INVALID;
+    if (dt != LCMA_F16 && dt != LCMA_BF16)
+        return LCMA_E_INVALID;
+    if (force < LCMA_ALGO_AUTO || force > LCMA_ALGO_L2)
+        return LCMA_E_INVALID;
+    lcma_options o{};
+    if (opts)
+        o = *opts;
+    if (o.split < LCMA_SPLIT_AUTO || o.split > LCMA_SPLIT_ALL || o.combine < LCMA_COMBINE_AUTO ||
+        o.combine > LCMA_COMBINE_AT_LOAD || o.num_cus < 0 || o.peak_tflops < 0 || o.hbm_gbps < 0 ||
+        o.bf16_ops_f16 < -1 || o.bf16_ops_f16 > 1)
+        return LCMA_E_INVALID;
+
+    // Which LCMA levels the description allows.
+    bool allow_l1 = true, allow_l2 = true;
+    if (desc) {
+        if (!desc_shape_ok(desc) || !brent_ok(desc))
+            return LCMA_E_BAD_DESCRIPTOR;
+        const int kind = builtin_kind(desc);
+        allow_l1 = kind == 1;
+        allow_l2 = kind == 1 || kind == 2;
+    }
+    if (o.combine == LCMA_COMBINE_AT_LOAD)
+        return LCMA_E_UNSUPPORTED;   // not built yet
+
+    Machine m;
+    m.peak = (o.peak_tflops > 0 ? o.peak_tflops : 2516.0) * 1e12;
+    m.bw = (o.hbm_gbps > 0 ? o.hbm_gbps : 8000.0) * 1e9;
+    m.l2bw = 8.0 * 2048.0 * 2.4e9;
+    m.launch = 4e-6;
+    m.eta_mfma = 0.75;
+    m.eta_fused = 0.75;
+    m.eta_bw = 0.8;
+    if (o.num_cus > 0) {
+        m.P = o.num_cus;
+    } else if (query_cus(&m.P) != 0) {
+        return LCMA_E_HIP;
+    }
+
+    // Operand type of the combined operands (bfloat16 inputs may use binary16).
+    auto op_bf16_for = [&](int levels) -> int {
+        if (dt == LCMA_F16)
+            return 0;
+        if (o.bf16_ops_f16 == 1)
+            return 0;
+        if (o.bf16_ops_f16 == -1)
+            return 1;
+        return levels == 2 ? 0 : 1;
+    };
+    // Admissibility: blocks must split evenly and keep 16-byte rows.
+    auto admissible = [&](int levels) -> bool {
+        const int64_t S = levels == 1 ? 2 : 4;
+        if (M % S || N % S || K % S)
+            return false;
+        const int64_t Mb = M / S, Nb = N / S, Kb = K / S;
+        return Mb >= 1 && Nb >= 8 && Kb >= 8 && Nb % 8 == 0 && Kb % 8 == 0;
+    };
+
+    double est[4] = {-1, -1, -1, -1};
+    est[LCMA_ALGO_CLASSIC] = est_classic(M, N, K, m);
+    bool ok1 = allow_l1 && admissible(1), ok2 = allow_l2 && admissible(2);
+    if (ok1)
+        est[LCMA_ALGO_L1] = est_lcma(M, N, K, 1, o.split, op_bf16_for(1) != (dt == LCMA_BF16), m);
+    if (ok2)
+        est[LCMA_ALGO_L2] = est_lcma(M, N, K, 2, o.split, op_bf16_for(2) != (dt == LCMA_BF16), m);
+
+    lcma_algo chosen = force;
+    if (force == LCMA_ALGO_L1 && !ok1)
+        return LCMA_E_UNSUPPORTED;
+    if (force == LCMA_ALGO_L2 && !ok2)
+        return LCMA_E_UNSUPPORTED;
+    if (force == LCMA_ALGO_AUTO) {
+        // Ties (within 2%) go to classic, then to fewer levels.  Two levels
+        // with binary16 inputs is never picked automatically: rounding the
+        // combined operands to binary16 loses too much accuracy there.
+        chosen = LCMA_ALGO_CLASSIC;
+        double best = est[LCMA_ALGO_CLASSIC];
+        if (ok1 && est[LCMA_ALGO_L1] < 0.98 * best) {
+            chosen = LCMA_ALGO_L1;
+            best = est[LCMA_ALGO_L1];
+        }
+        if (ok2 && dt == LCMA_BF16 && op_bf16_for(2) == 0 && est[LCMA_ALGO_L2] < 0.98 * best) {
+            chosen = LCMA_ALGO_L2;
+            best = est[LCMA_ALGO_L2];
+        }
+    }
+
+    lcma_plan_s* p = new (std::nothrow) lcma_plan_s();
+    if (!p)
+        return LCMA_E_NOMEM;
+    p->M = M; p->N = N; p->K = K; p->dt = dt; p->chosen = chosen; p->P = m.P;
+    for (int a = 0; a < 4; ++a)
+        p->est[a] = est[a];
+    p->classic_tile = classic_tile_for(M, N, m.P);
+    p->levels = chosen == LCMA_ALGO_L1 ? 1 : chosen == LCMA_ALGO_L2 ? 2 : 0;
+    p->ws_bytes = 0;
+    p->n_slots = 0;
+    if (p->levels > 0) {
+        const int L = p->levels;
+        p->op_bf16 = op_bf16_for(L);
+        p->write_all = p->op_bf16 != (dt == LCMA_BF16 ? 1 : 0);
+        p->geo = lcma_geo(M, N, K, L);
+        const Geo& g = p->geo;
+        SchedParams& sp = p->sp;
+        sp.G = g.G; sp.gy = g.gy; sp.gx = g.gx; sp.R = g.R; sp.P = m.P;
+        sp.mode = split_mode_for(o.split, g.G, m.P);
+        sp.h = (g.R + 1) / 2;
+        sp.raster = 8;
+        if (sp.mode == kSplitTail) {
+            p->n_slots = g.G % m.P;
+            p->grid = g.G / m.P > 0 ? m.P : 2 * (g.G % m.P);
+        } else if (sp.mode == kSplitAll) {
+            p->n_slots = g.G;
+            p->grid = std::min(2 * g.G, m.P);
+        } else {
+            p->grid = std::min(g.G, m.P);
+        }
+        fused_order(L, p->order);
+        // workspace layout
+        std::call_once(g_tables_once, init_tables);
+        const int SS = g.S * g.S;
+        const int8_t* U = L == 1 ? g_U1 : g_U2;
+        const int8_t* V = L == 1 ? g_V1 : g_V2;
+        int nA = 0, nB = 0;
+        for (int r = 0; r < g.R; ++r) {
+            int na = 0, nb = 0, ba = -1, bb = -1, ca = 0, cb = 0;
+            for (int x = 0; x < SS; ++x) {
+                if (U[r * SS + x]) { ++na; ba = x; ca = U[r * SS + x]; }
+                if (V[r * SS + x]) { ++nb; bb = x; cb = V[r * SS + x]; }
+            }
+            // Same rule as the pre-pass kernel: a single-block operand is read
+            // in place (the built-in schemes give it coefficient +1).
+            (void)ca; (void)cb;
+            const bool wa = p->write_all || na > 1;
+            const bool wb = p->write_all || nb > 1;
+            p->slotA[r] = wa ? nA++ : -1;
+            p->slotB[r] = wb ? nB++ : -1;
+            p->blockA[r] = ba;
+            p->blockB[r] = bb;
+        }
+        int64_t off = 0;
+        p->offA = off;
+        off = align_up(off + (int64_t)nA * g.Mb * g.Kb * 2, 256);
+        p->offB = off;
+        off = align_up(off + (int64_t)nB * g.Kb * g.Nb * 2, 256);
+        p->offPart = off;
+        off = align_up(off + (int64_t)p->n_slots * 2 * fused_partial_bytes(L), 256);
+        p->offCtr = off;
+        off = align_up(off + (int64_t)p->n_slots * 4, 256);
+        p->ws_bytes = (size_t)off;
+    }
+    if (log_enabled())
+        fprintf(stderr, "[lcma] plan M=%lld N=%lld K=%lld %s: est classic=%.3g L1=%.3g L2=%.3g s -> %s (ws %zu B)\n",
+                (long long)M, (long long)N, (long long)K, dt == LCMA_BF16 ? "bf16" : "f16", est[1], est[2],
+                est[3], chosen == LCMA_ALGO_CLASSIC ? "classic" : chosen == LCMA_ALGO_L1 ? "L1" : "L2",
+                p->ws_bytes);
+    *out = p;
+    return LCMA_OK;
+}
+
+lcma_status lcma_plan(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const lcma_desc* desc, lcma_algo force,
+                      lcma_plan_t* out)
+{
+    return lcma_plan_ex(M, N, K, dt, desc, force, nullptr, out);
+}
+
+lcma_status lcma_plan_info(lcma_plan_t p, lcma_algo* chosen, size_t* ws, double* est)
+{
+    if (!p)
+        return LCMA_E_INVALID;
+    if (chosen)
+        *chosen = p->chosen;
+    if (ws)
+        *ws = p->ws_bytes;
+    if (est)
+        *est = p->est[p->chosen];
+    return LCMA_OK;
+}
+
+lcma_status lcma_plan_estimate(lcma_plan_t p, lcma_algo algo, double* est)
+{
+    if (!p || !est || algo < LCMA_ALGO_CLASSIC || algo > LCMA_ALGO_L2)
+        return LCMA_E_INVALID;
+    *est = p->est[algo];
+    return LCMA_OK;
+}
+
+lcma_status lcma_plan_operand(lcma_plan_t p, int32_t side, int32_t r, int64_t* offset, int64_t* ld,
+                              lcma_dtype* dtype)
+{
+    if (!p || p->levels == 0 || side < 0 || side > 1 || r < 0 || r >= p->geo.R)
+        return LCMA_E_INVALID;
+    const int64_t slot = side == 0 ? p->slotA[r] : p->slotB[r];
+    if (offset)
+        *offset = slot < 0 ? -1
+                           : (side == 0 ? p->offA + slot * p->geo.Mb * p->geo.Kb * 2
+                                        : p->offB + slot * p->geo.Kb * p->geo.Nb * 2);
+    if (ld)
+        *ld = side == 0 ? p->geo.Kb : p->geo.Nb;
+    if (dtype)
+        *dtype = p->op_bf16 ? LCMA_BF16 : LCMA_F16;
+    return LCMA_OK;
+}
+
+lcma_status lcma_plan_schedule(lcma_plan_t p, int32_t* items, int64_t cap, int64_t* count, int32_t* order)
+{
+    if (!p || p->levels == 0 || !count || (cap > 0 && !items))
+        return LCMA_E_INVALID;
+    int64_t n = 0;
+    for (int w = 0; w < p->grid; ++w) {
+        const int c = sched_count(p->sp, w);
+        for (int i = 0; i < c; ++i, ++n) {
+            if (n < cap) {
+                const Item it = sched_item(p->sp, w, i);
+                int32_t* o = items + 5 * n;
+                o[0] = w; o[1] = it.g; o[2] = it.pos0; o[3] = it.pos1; o[4] = it.slot;
+            }
+        }
+    }
+    *count = n;
+    if (order)
+        for (int r = 0; r < p->geo.R; ++r)
+            order[r] = p->order[r];
+    return LCMA_OK;
+}
+
+void lcma_plan_destroy(lcma_plan_t p) { delete p; }
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- launching
+
+namespace {
+
+struct Io {
+    bool vec, vec4;
+};
+
+lcma_status check_io(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                     const void* C, int64_t ldc, Io* io, bool check_c = true)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return LCMA_E_INVALID;
+    if (check_c && M > 0 && N > 0 && (!C || ldc < std::max<int64_t>(N, 1)))
+        return LCMA_E_INVALID;
+    if (M > 0 && N > 0 && K > 0) {
+        if (!A || !B || lda < K || ldb < N)
+            return LCMA_E_INVALID;
+    }
+    // 32-bit buffer offsets: a tile spans at most 256 rows of a leading dimension.
+    const int64_t kMaxLd = (int64_t)1 << 21;
+    if (lda >= kMaxLd || ldb >= kMaxLd || (check_c && ldc >= kMaxLd))
+        return LCMA_E_UNSUPPORTED;
+    const auto al = [](const void* x, uintptr_t a) { return ((uintptr_t)x % a) == 0; };
+    io->vec = al(A, 16) && al(B, 16) && lda % 8 == 0 && ldb % 8 == 0 && K % 8 == 0 && N % 8 == 0;
+    io->vec4 = check_c ? (al(C, 8) && ldc % 4 == 0 && N % 4 == 0) : false;
+    return LCMA_OK;
+}
+
+lcma_status run_classic(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const void* A, int64_t lda, const void* B,
+                        int64_t ldb, void* C, int64_t ldc, const Io& io, int tile, int P, hipStream_t st)
+{
+    if (M == 0 || N == 0)
+        return LCMA_OK;
+    ClassicLaunch L;
+    L.A = A; L.lda = lda; L.B = B; L.ldb = ldb; L.C = C; L.ldc = ldc;
+    L.M = (int32_t)M; L.N = (int32_t)N; L.K = (int32_t)K;
+    L.bf16 = dt == LCMA_BF16; L.vec = io.vec; L.vec4 = io.vec4; L.tile = tile; L.P = P;
+    return launch_classic(L, st) == hipSuccess ? LCMA_OK : LCMA_E_HIP;
+}
+
+lcma_status check_ws(const lcma_plan_s* p, void* ws, size_t ws_bytes)
+{
+    if (p->ws_bytes == 0)
+        return LCMA_OK;
+    if (!ws || ws_bytes < p->ws_bytes || ((uintptr_t)ws % 256) != 0)
+        return LCMA_E_WORKSPACE;
+    return LCMA_OK;
+}
+
+lcma_status do_prepass(const lcma_plan_s* p, const void* A, int64_t lda, const void* B, int64_t ldb, void* ws,
+                       hipStream_t st)
+{
+    PrepassLaunch L;
+    L.A = A; L.lda = lda; L.B = B; L.ldb = ldb;
+    L.Mb = (int32_t)p->geo.Mb; L.Kb = (int32_t)p->geo.Kb; L.Nb = (int32_t)p->geo.Nb;
+    L.outA = (char*)ws + p->offA;
+    L.outB = (char*)ws + p->offB;
+    L.strideA = p->geo.Mb * p->geo.Kb;
+    L.strideB = p->geo.Kb * p->geo.Nb;
+    L.levels = p->levels;
+    L.in_bf16 = p->dt == LCMA_BF16;
+    L.op_bf16 = p->op_bf16;
+    L.write_all = p->write_all;
+    L.counters = (int32_t*)((char*)ws + p->offCtr);
+    L.n_counters = p->n_slots;
+    return launch_prepass(L, st) == hipSuccess ? LCMA_OK : LCMA_E_HIP;
+}
+
+lcma_status do_fused(const lcma_plan_s* p, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                     int64_t ldc, const Io& io, void* ws, hipStream_t st)
+{
+    FusedLaunch L;
+    memset(&L, 0, sizeof L);
+    const Geo& g = p->geo;
+    for (int r = 0; r < g.R; ++r) {
+        if (p->slotA[r] >= 0) {
+            L.p.a[r] = (const uint16_t*)((char*)ws + p->offA) + p->slotA[r] * g.Mb * g.Kb;
+            L.p.lda[r] = g.Kb;
+        } else {
+            const int bi = p->blockA[r] / g.S, bk = p->blockA[r] % g.S;
+            L.p.a[r] = (const uint16_t*)A + bi * g.Mb * lda + bk * g.Kb;
+            L.p.lda[r] = lda;
+        }
+        if (p->slotB[r] >= 0) {
+            L.p.b[r] = (const uint16_t*)((char*)ws + p->offB) + p->slotB[r] * g.Kb * g.Nb;
+            L.p.ldb[r] = g.Nb;
+        } else {
+            const int bk = p->blockB[r] / g.S, bj = p->blockB[r] % g.S;
+            L.p.b[r] = (const uint16_t*)B + bk * g.Kb * ldb + bj * g.Nb;
+            L.p.ldb[r] = ldb;
+        }
+        L.p.order[r] = p->order[r];
+        const int8_t* W = p->levels == 1 ? g_W1 : g_W2;
+        for (int o = 0; o < g.S * g.S; ++o)
+            L.p.w[r][o] = W[r * g.S * g.S + o];
+    }
+    L.p.C = (uint16_t*)C;
+    L.p.ldc = ldc;
+    L.p.Mb = (int32_t)g.Mb; L.p.Nb = (int32_t)g.Nb; L.p.Kb = (int32_t)g.Kb;
+    L.p.vec4 = io.vec4;
+    L.p.sp = p->sp;
+    L.p.partial = (float*)((char*)ws + p->offPart);
+    L.p.counters = (int32_t*)((char*)ws + p->offCtr);
+    L.levels = p->levels;
+    L.op_bf16 = p->op_bf16;
+    L.out_bf16 = p->dt == LCMA_BF16;
+    L.grid = p->grid;
+    return launch_fused(L, st) == hipSuccess ? LCMA_OK : LCMA_E_HIP;
+}
+
+lcma_status check_lcma_call(const lcma_plan_s* p, const void* A, int64_t lda, const void* B, int64_t ldb,
+                            const void* C, int64_t ldc, void* ws, size_t ws_bytes, bool need_c, Io* io)
+{
+    lcma_status s = check_io(p->M, p->N, p->K, A, lda, B, ldb, C, ldc, io, need_c);
+    if (s != LCMA_OK)
+        return s;
+    if (!io->vec)
+        return LCMA_E_UNSUPPORTED;
+    return check_ws(p, ws, ws_bytes);
+}
+
+}  // namespace
+
+extern "C" {
+
+lcma_status gemm_classic(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const void* A, int64_t lda, const void* B,
+                         int64_t ldb, void* C, int64_t ldc, void* stream)
+{
+    if (dt != LCMA_F16 && dt != LCMA_BF16)
+        return LCMA_E_INVALID;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+        return LCMA_E_INVALID;
+    Io io;
+    lcma_status s = check_io(M, N, K, A, lda, B, ldb, C, ldc, &io);
+    if (s != LCMA_OK)
+        return s;
+    if (M == 0 || N == 0)
+        return LCMA_OK;
+    int P = 0;
+    if (query_cus(&P) != 0)
+        return LCMA_E_HIP;
+    return run_classic(M, N, K, dt, A, lda, B, ldb, C, ldc, io, classic_tile_for(M, N, P), P, (hipStream_t)stream);
+}
+
+lcma_status lcma_gemm(lcma_plan_t p, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                      void* ws, size_t ws_bytes, void* stream)
+{
+    if (!p)
+        return LCMA_E_INVALID;
+    hipStream_t st = (hipStream_t)stream;
+    if (p->levels == 0) {
+        Io io;
+        lcma_status s = check_io(p->M, p->N, p->K, A, lda, B, ldb, C, ldc, &io);
+        if (s != LCMA_OK)
+            return s;
+        return run_classic(p->M, p->N, p->K, p->dt, A, lda, B, ldb, C, ldc, io, p->classic_tile, p->P, st);
+    }
+    Io io;
+    lcma_status s = check_lcma_call(p, A, lda, B, ldb, C, ldc, ws, ws_bytes, true, &io);
+    if (s != LCMA_OK)
+        return s;
+    s = do_prepass(p, A, lda, B, ldb, ws, st);
+    if (s != LCMA_OK)
+        return s;
+    return do_fused(p, A, lda, B, ldb, C, ldc, io, ws, st);
+}
+
+lcma_status lcma_prepass(lcma_plan_t p, const void* A, int64_t lda, const void* B, int64_t ldb, void* ws,
+                         size_t ws_bytes, void* stream)
+{
+    if (!p || p->levels == 0)
+        return LCMA_E_INVALID;
+    Io io;
+    lcma_status s = check_lcma_call(p, A, lda, B, ldb, nullptr, 0, ws, ws_bytes, false, &io);
+    if (s != LCMA_OK)
+        return s;
+    return do_prepass(p, A, lda, B, ldb, ws, (hipStream_t)stream);
+}
+
+lcma_status lcma_fused(lcma_plan_t p, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                       void* ws, size_t ws_bytes, void* stream)
+{
+    if (!p || p->levels == 0)
+        return LCMA_E_INVALID;
+    Io io;
+    lcma_status s = check_lcma_call(p, A, lda, B, ldb, C, ldc, ws, ws_bytes, true, &io);
+    if (s != LCMA_OK)
+        return s;
+    return do_fused(p, A, lda, B, ldb, C, ldc, io, ws, (hipStream_t)stream);
+}
+
+}  // extern "C"

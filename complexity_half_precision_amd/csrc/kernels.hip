@@ -1,0 +1,776 @@
+// kernels.hip -- gfx950 (MI355X) kernels of the half-precision GEMM library.
+//
+//  * k_classic  -- tiled MFMA GEMM, C = A * B (fp32 accumulate, one RNE cast).
+//  * k_prepass  -- combine-A/B pass: every combined operand of an LCMA scheme,
+//                  summed in fp32 and rounded once to the operand type.
+//  * k_fused    -- persistent group kernel: all product tiles of one output
+//                  coordinate run on one workgroup, accumulated into the C
+//                  tiles in registers (fp32), never writing a product to
+//                  memory; tail groups may be split over two workgroups with
+//                  a last-arriver fp32 fix-up.
+//
+// Sources: "FalconGEMM: Surpassing Hardware Peaks with Lower-Complexity
+// Matrix Multiplication", sections "从 LCMA 到 FalconGEMM" (combine A/B,
+// spatial groups accumulated on chip, split over two compute units, L2-aware
+// ordering, persistent kernel) and "从缓存重排到 Cost Model" (fp32 on-chip
+// combination, one final cast); "CUDA-L2 ..." section "核心贡献与发现的技术"
+// (double-buffered staging, wide epilogue stores, block swizzling).
+//
+// Data layout shared by all kernels: row-major halves.  Each k-tile of 64
+// stages an A tile (BM rows x 64 k) and a B tile (BN columns x 64 k, stored
+// transposed so that both MFMA operands read 8 consecutive k per lane with
+// one 16-byte LDS read).  LDS rows are padded from 128 to 144 bytes so that
+// reads and writes are bank-conflict free with affine addresses.
+//
+// MFMA: v_mfma_f32_32x32x16_{f16,bf16}.  Operands are fed swapped (the B
+// fragment as the A operand), so the accumulator of lane l holds 4
+// consecutive output columns of output row (l % 32) per group of 4
+// registers, which the epilogue stores as one 8-byte write.
+
+#include <hip/hip_runtime.h>
+
+#include <utility>
+
+#include "kernels.hpp"
+#include "schedule.hpp"
+#include "strassen.hpp"
+
+namespace lcma {
+namespace {
+
+using u16 = uint16_t;
+using u32 = uint32_t;
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+
+// MFMA shapes: 32x32x16 (16 fp32 accumulators per lane) and 16x16x32 (4).
+template <int MT>
+struct Mma;
+template <>
+struct Mma<32> {
+    using acc_t = f32x16;
+    static constexpr int NACC = 16;
+    static constexpr int KSTEP = 16;
+};
+template <>
+struct Mma<16> {
+    using acc_t = f32x4;
+    static constexpr int NACC = 4;
+    static constexpr int KSTEP = 32;
+};
+
+template <bool BF>
+__device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c)
+{
+    if constexpr (BF)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(b8, a),
+                                                       __builtin_bit_cast(b8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, a),
+                                                      __builtin_bit_cast(h8, b), c, 0, 0, 0);
+}
+
+template <bool BF>
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c)
+{
+    if constexpr (BF)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a),
+                                                       __builtin_bit_cast(b8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a),
+                                                      __builtin_bit_cast(h8, b), c, 0, 0, 0);
+}
+
+// fp32 -> half bits, round to nearest even.
+template <bool BF>
+__device__ __forceinline__ u16 f2h(float x)
+{
+    if constexpr (BF)
+        return __builtin_bit_cast(u16, (__bf16)x);
+    else
+        return __builtin_bit_cast(u16, (_Float16)x);
+}
+
+template <bool BF>
+__device__ __forceinline__ float h2f(u16 x)
+{
+    if constexpr (BF)
+        return __builtin_bit_cast(float, (u32)x << 16);
+    else
+        return (float)__builtin_bit_cast(_Float16, x);
+}
+
+template <bool BF>
+__device__ __forceinline__ u32 pack2(float lo, float hi)
+{
+    return (u32)f2h<BF>(lo) | ((u32)f2h<BF>(hi) << 16);
+}
+
+// LDS rows hold 64 halves (128 bytes) padded to 144 bytes: 8 consecutive
+// rows at the same 16-byte chunk then start 9 slots apart modulo the 256-byte
+// bank width, so the 8 lanes of a 16-byte access phase never share banks,
+// and every offset is affine in (row, chunk) (immediate-offset LDS reads).
+constexpr u32 kRow = 144;
+
+__device__ __forceinline__ u32 lds_off(u32 row, u32 ch) { return row * kRow + ch * 16u; }
+
+template <int BM_, int BN_, int WM_, int WN_, int MT_ = 32, int BKB_ = 8>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, BK = 64, WM = WM_, WN = WN_, MT = MT_;
+    static constexpr int BKB = BKB_;                      // k rows per staged B block (2, 4 or 8)
+    static constexpr int NT = WM * WN * 64;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int FM = WTM / MT, FN = WTN / MT;
+    using acc_t = typename Mma<MT>::acc_t;
+    static constexpr int NACC = Mma<MT>::NACC;
+    static constexpr int A_CH = BM * 8 / NT;              // 16-byte A chunks per thread
+    static constexpr int B_BLK = (BK / BKB) * (BN / 8);   // BKB x 8 B blocks per tile
+    static constexpr int B_PER = (B_BLK + NT - 1) / NT;   // B blocks per thread
+    static constexpr int A_BYTES = BM * kRow, B_BYTES = BN * kRow;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int LDS = 2 * STAGE;
+    static_assert(BM * 8 % NT == 0 && A_CH >= 1, "A tile must split evenly over the threads");
+    static_assert(FM >= 1 && FN >= 1, "wave tile must hold one MFMA tile");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(BKB == 2 || BKB == 4 || BKB == 8, "B block height");
+};
+
+using Cfg256 = Cfg<256, 256, 2, 2, 32, 8>;   // classic: 4 waves of 128 x 128
+using Cfg128 = Cfg<128, 128, 2, 2, 32, 4>;   // classic: 4 waves of 64 x 64
+using Cfg32 = Cfg<32, 64, 1, 2, 32, 4>;      // classic skinny: 2 waves of 32 x 32
+using CfgF1 = Cfg<128, 128, 2, 4, 32, 2>;    // fused one-level: 8 waves of 64 x 32
+using CfgF2 = Cfg<64, 64, 4, 2, 16, 2>;      // fused two-level: 8 waves of 16 x 32 (16x16x32 MFMA)
+
+// Buffer resources: global loads and stores go through a buffer descriptor
+// based at the tile origin with 32-bit byte offsets.  An offset of
+// kOob (beyond num_records) reads as zero and drops stores, which handles
+// every edge without branches or 64-bit address arithmetic.
+constexpr u32 kOob = 0x80000000u;
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+
+// Where one tile sequence reads from: `a` is the first row of the A tile
+// (column 0), `b` is column 0 of the B tile (row 0); rows/cols beyond
+// a_rows / b_cols and k beyond K read as zero.  Buffer descriptors are
+// re-based at every k-tile so 32-bit offsets stay small for any K (leading
+// dimensions are limited to 2^21 elements by the host).
+struct Src {
+    const u16* a; int lda; int a_rows;
+    const u16* b; int ldb; int b_cols;
+    int K;
+};
+
+__device__ __forceinline__ Src make_src(const u16* a, int64_t lda, int a_rows, const u16* b, int64_t ldb,
+                                        int b_cols, int K)
+{
+    return Src{a, (int)lda, a_rows, b, (int)ldb, b_cols, K};
+}
+
+template <class C>
+struct Regs {
+    u32x4 a[C::A_CH];
+    u32x4 b[C::B_PER][C::BKB];
+};
+
+__device__ __forceinline__ u32x4 load16(const rsrc_t& r, u32 off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// 8 halves starting at element (row, col) of a row-major matrix with leading
+// dimension ld; elements with row >= rows or col + x >= cols read as zero.
+template <bool VEC>
+__device__ __forceinline__ u32x4 load_row8(const rsrc_t& r, int ld, int row, int col, int rows, int cols)
+{
+    if constexpr (VEC) {
+        const u32 off = (row < rows && col < cols) ? (u32)(row * ld + col) * 2u : kOob;
+        return load16(r, off);
+    } else {
+        u32 e[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            const u32 off = (row < rows && col + x < cols) ? (u32)(row * ld + col + x) * 2u : kOob;
+            e[x] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+        }
+        return u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+    }
+}
+
+template <class C, bool VEC>
+__device__ __forceinline__ void load_tile(Regs<C>& R, const Src& s, int k0, int tid)
+{
+    const rsrc_t ra = make_rsrc(s.a + k0);
+    const rsrc_t rb = make_rsrc(s.b + (int64_t)k0 * s.ldb);
+    const int kleft = s.K - k0;
+#pragma unroll
+    for (int i = 0; i < C::A_CH; ++i) {
+        const int c = tid + i * C::NT;
+        R.a[i] = load_row8<VEC>(ra, s.lda, c >> 3, (c & 7) * 8, s.a_rows, kleft);
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_PER; ++i) {
+        const int blk = tid + i * C::NT;
+        if (C::B_BLK % C::NT == 0 || blk < C::B_BLK) {
+            const int kb = blk % (C::BK / C::BKB), n = (blk / (C::BK / C::BKB)) * 8;
+#pragma unroll
+            for (int r = 0; r < C::BKB; ++r)
+                R.b[i][r] = load_row8<VEC>(rb, s.ldb, kb * C::BKB + r, n, kleft, s.b_cols);
+        }
+    }
+}
+
+// Registers -> LDS stage.  A chunks go straight to their swizzled slot.  Each
+// BKB (k) x 8 (n) B block is transposed in registers: output dword (n, k
+// pair) takes half n of rows k and k+1 with one byte permute, and column n's
+// BKB values are written with one BKB*2-byte LDS store.
+template <class C>
+__device__ __forceinline__ void store_tile(char* stage, const Regs<C>& R, int tid)
+{
+    char* sA = stage;
+    char* sB = stage + C::A_BYTES;
+#pragma unroll
+    for (int i = 0; i < C::A_CH; ++i) {
+        const int c = tid + i * C::NT;
+        *reinterpret_cast<u32x4*>(sA + lds_off(c >> 3, c & 7)) = R.a[i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_PER; ++i) {
+        const int blk = tid + i * C::NT;
+        if (C::B_BLK % C::NT == 0 || blk < C::B_BLK) {
+            // consecutive lanes take consecutive k blocks of one 8-column
+            // block, so a 16-byte store phase covers 8 distinct rows' slots
+            const int kb = blk % (C::BK / C::BKB), nb = blk / (C::BK / C::BKB);
+            const int k = kb * C::BKB;               // first k of the block within the tile
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+                const int d = n >> 1;
+                const u32 sel = (n & 1) ? 0x07060302u : 0x05040100u;
+                u32 v[C::BKB / 2];
+#pragma unroll
+                for (int pr = 0; pr < C::BKB / 2; ++pr)
+                    v[pr] = __builtin_amdgcn_perm(R.b[i][2 * pr + 1][d], R.b[i][2 * pr][d], sel);
+                char* dst = sB + lds_off(nb * 8 + n, k >> 3) + (k & 7) * 2;
+                if constexpr (C::BKB == 8)
+                    *reinterpret_cast<u32x4*>(dst) = u32x4{v[0], v[1], v[2], v[3]};
+                else if constexpr (C::BKB == 4)
+                    *reinterpret_cast<u32x2*>(dst) = u32x2{v[0], v[1]};
+                else
+                    *reinterpret_cast<u32*>(dst) = v[0];
+            }
+        }
+    }
+}
+
+template <class C, bool BF>
+__device__ __forceinline__ void compute_stage(const char* stage, typename C::acc_t (&acc)[C::FM][C::FN],
+                                              int wm, int wn, int lane)
+{
+    const char* sA = stage;
+    const char* sB = stage + C::A_BYTES;
+    // Lane l feeds row (l % MT) of each operand tile with 8 consecutive k:
+    // k chunk (l / MT) of the MFMA's k step.
+    constexpr int KSTEPS = C::BK / Mma<C::MT>::KSTEP;
+    constexpr int CPS = Mma<C::MT>::KSTEP / 8;   // 16-byte chunks per k step
+    const int r = lane % C::MT, hi = lane / C::MT;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+        u32x4 af[C::FM], bf[C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+            af[i] = *reinterpret_cast<const u32x4*>(sA + lds_off(wm * C::WTM + i * C::MT + r, CPS * s + hi));
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+            bf[j] = *reinterpret_cast<const u32x4*>(sB + lds_off(wn * C::WTN + j * C::MT + r, CPS * s + hi));
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                acc[i][j] = mfma<BF>(bf[j], af[i], acc[i][j]);
+    }
+}
+
+// Stores one accumulator tile: `Cp` is the tile origin, rows/cols the valid
+// extent from there.  With operands swapped, lane l holds output row
+// (l % MT) and, per group of 4 accumulators, 4 consecutive columns:
+// 32x32: column 8*g + 4*(l/32) + e of group g; 16x16: column 4*(l/16) + e.
+template <class C, bool BF>
+__device__ __forceinline__ void store_c(const typename C::acc_t (&acc)[C::FM][C::FN], u16* Cp, int64_t ldc,
+                                        int rows, int cols, bool vec4, int wm, int wn, int lane)
+{
+    const rsrc_t rc = make_rsrc(Cp);
+    const int ld = (int)ldc;
+    const int r = lane % C::MT, hi = lane / C::MT;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        const int m = wm * C::WTM + i * C::MT + r;
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int g = 0; g < C::NACC / 4; ++g) {
+                const int n = wn * C::WTN + j * C::MT + (C::MT == 32 ? 8 * g + 4 * hi : 4 * hi);
+                const float x0 = acc[i][j][4 * g], x1 = acc[i][j][4 * g + 1];
+                const float x2 = acc[i][j][4 * g + 2], x3 = acc[i][j][4 * g + 3];
+                if (vec4) {
+                    // cols is a multiple of 4 here, so the 4 columns are all valid or all not.
+                    const u32 off = (m < rows && n < cols) ? (u32)(m * ld + n) * 2u : kOob;
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
+                                           u32x2{pack2<BF>(x0, x1), pack2<BF>(x2, x3)}),
+                        rc, off, 0, 0);
+                } else {
+                    const float xs[4] = {x0, x1, x2, x3};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const u32 off = (m < rows && n + e < cols) ? (u32)(m * ld + n + e) * 2u : kOob;
+                        __builtin_amdgcn_raw_buffer_store_b16(f2h<BF>(xs[e]), rc, off, 0, 0);
+                    }
+                }
+            }
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void zero_acc(typename C::acc_t (&acc)[C::FM][C::FN])
+{
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int e = 0; e < C::NACC; ++e)
+                acc[i][j][e] = 0.0f;
+}
+
+// ------------------------------------------------------------------ classic
+
+template <class C, bool BF, bool VEC>
+__global__ void __launch_bounds__(C::NT)
+k_classic(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb,
+          u16* __restrict__ Cm, int64_t ldc, int M, int N, int K, int gy, int gx, int P, int vec4)
+{
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    int p, q;
+    tile_coords((int32_t)blockIdx.x, gy, gx, P, 8, &p, &q);
+    const int m0 = p * C::BM, n0 = q * C::BN;
+    const Src s = make_src(A + (int64_t)m0 * lda, lda, M - m0, B + n0, ldb, N - n0, K);
+
+    typename C::acc_t acc[C::FM][C::FN];
+    zero_acc<C>(acc);
+    const int nk = (K + C::BK - 1) / C::BK;
+    Regs<C> R;
+    load_tile<C, VEC>(R, s, 0, tid);
+    store_tile<C>(smem, R, tid);
+    __syncthreads();
+    for (int t = 0; t < nk; ++t) {
+        if (t + 1 < nk)
+            load_tile<C, VEC>(R, s, (t + 1) * C::BK, tid);
+        compute_stage<C, BF>(smem + (t & 1) * C::STAGE, acc, wm, wn, lane);
+        if (t + 1 < nk)
+            store_tile<C>(smem + ((t + 1) & 1) * C::STAGE, R, tid);
+        __syncthreads();
+    }
+    store_c<C, BF>(acc, Cm + (int64_t)m0 * ldc + n0, ldc, M - m0, N - n0, vec4 != 0, wm, wn, lane);
+}
+
+template <class C, bool BF, bool VEC>
+hipError_t launch_classic_t(const ClassicLaunch& L, hipStream_t st)
+{
+    const int gy = (L.M + C::BM - 1) / C::BM, gx = (L.N + C::BN - 1) / C::BN;
+    const long tiles = (long)gy * gx;
+    if (tiles == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((k_classic<C, BF, VEC>), dim3((unsigned)tiles), dim3(C::NT), 0, st,
+                       (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, (u16*)L.C, L.ldc, L.M, L.N, L.K,
+                       gy, gx, L.P, L.vec4);
+    return hipGetLastError();
+}
+
+template <class C>
+hipError_t launch_classic_c(const ClassicLaunch& L, hipStream_t st)
+{
+    if (L.bf16)
+        return L.vec ? launch_classic_t<C, true, true>(L, st) : launch_classic_t<C, true, false>(L, st);
+    return L.vec ? launch_classic_t<C, false, true>(L, st) : launch_classic_t<C, false, false>(L, st);
+}
+
+// ------------------------------------------------------------------ pre-pass
+
+template <int LEVELS, bool ALL>
+constexpr bool written_a(int r)
+{
+    int nnz = 0;
+    for (int i = 0; i < Scheme<LEVELS>::S; ++i)
+        for (int k = 0; k < Scheme<LEVELS>::S; ++k)
+            nnz += Scheme<LEVELS>::u(r, i, k) != 0;
+    return ALL || nnz > 1;
+}
+
+template <int LEVELS, bool ALL>
+constexpr bool written_b(int r)
+{
+    int nnz = 0;
+    for (int k = 0; k < Scheme<LEVELS>::S; ++k)
+        for (int j = 0; j < Scheme<LEVELS>::S; ++j)
+            nnz += Scheme<LEVELS>::v(r, k, j) != 0;
+    return ALL || nnz > 1;
+}
+
+template <int LEVELS, bool ALL, bool SIDE_B>
+constexpr int slot_of(int r)
+{
+    int s = 0;
+    for (int x = 0; x < r; ++x)
+        s += SIDE_B ? written_b<LEVELS, ALL>(x) : written_a<LEVELS, ALL>(x);
+    return s;
+}
+
+struct PrepassParams {
+    const u16* A; int64_t lda;
+    const u16* B; int64_t ldb;
+    int Mb, Kb, Nb;
+    u16* outA; u16* outB;
+    int64_t strideA, strideB;
+    int blocksA;
+    int* counters; int n_counters;
+};
+
+// One product's combination for one 8-element chunk: fp32 sum of the
+// coefficient-weighted blocks in block order, then one RNE rounding.
+template <int LEVELS, bool SIDE_B, bool OBF, int R>
+__device__ __forceinline__ void combine_one(const float (&x)[Scheme<LEVELS>::S * Scheme<LEVELS>::S][8],
+                                            u16* dst)
+{
+    constexpr int S = Scheme<LEVELS>::S;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        acc[e] = 0.0f;
+    [&]<int... B>(std::integer_sequence<int, B...>) {
+        ([&] {
+            constexpr int c = SIDE_B ? Scheme<LEVELS>::v(R, B / S, B % S) : Scheme<LEVELS>::u(R, B / S, B % S);
+            if constexpr (c != 0) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[e] += (float)c * x[B][e];
+            }
+        }(), ...);
+    }(std::make_integer_sequence<int, S * S>{});
+    *reinterpret_cast<u32x4*>(dst) = u32x4{pack2<OBF>(acc[0], acc[1]), pack2<OBF>(acc[2], acc[3]),
+                                           pack2<OBF>(acc[4], acc[5]), pack2<OBF>(acc[6], acc[7])};
+}
+
+template <int LEVELS, bool IBF, bool OBF, bool ALL>
+__global__ void __launch_bounds__(256) k_prepass(const PrepassParams pp)
+{
+    constexpr int S = Scheme<LEVELS>::S, R = Scheme<LEVELS>::R;
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < pp.n_counters; i += blockDim.x)
+            pp.counters[i] = 0;
+    const bool side_b = (int)blockIdx.x >= pp.blocksA;
+    const int64_t idx = (int64_t)(side_b ? blockIdx.x - pp.blocksA : blockIdx.x) * blockDim.x + threadIdx.x;
+    // A side: positions (i, j8) over Mb x Kb/8 of each block; B side: (k, j8) over Kb x Nb/8.
+    const int cols8 = side_b ? pp.Nb / 8 : pp.Kb / 8;
+    const int rows = side_b ? pp.Kb : pp.Mb;
+    if (idx >= (int64_t)rows * cols8)
+        return;
+    const int i = (int)(idx / cols8), j = (int)(idx % cols8) * 8;
+    const u16* src = side_b ? pp.B : pp.A;
+    const int64_t ld = side_b ? pp.ldb : pp.lda;
+    const int br = side_b ? pp.Kb : pp.Mb;   // block rows
+    const int bc = side_b ? pp.Nb : pp.Kb;   // block cols
+    float x[S * S][8];
+#pragma unroll
+    for (int b = 0; b < S * S; ++b) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + (int64_t)((b / S) * br + i) * ld + (b % S) * bc + j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[b][2 * e] = h2f<IBF>((u16)(v[e] & 0xffffu));
+            x[b][2 * e + 1] = h2f<IBF>((u16)(v[e] >> 16));
+        }
+    }
+    const int64_t off = (int64_t)i * bc + j;
+    if (!side_b) {
+        [&]<int... Rs>(std::integer_sequence<int, Rs...>) {
+            ([&] {
+                if constexpr (written_a<LEVELS, ALL>(Rs))
+                    combine_one<LEVELS, false, OBF, Rs>(x, pp.outA + slot_of<LEVELS, ALL, false>(Rs) * pp.strideA + off);
+            }(), ...);
+        }(std::make_integer_sequence<int, R>{});
+    } else {
+        [&]<int... Rs>(std::integer_sequence<int, Rs...>) {
+            ([&] {
+                if constexpr (written_b<LEVELS, ALL>(Rs))
+                    combine_one<LEVELS, true, OBF, Rs>(x, pp.outB + slot_of<LEVELS, ALL, true>(Rs) * pp.strideB + off);
+            }(), ...);
+        }(std::make_integer_sequence<int, R>{});
+    }
+}
+
+template <int LEVELS, bool IBF, bool OBF, bool ALL>
+hipError_t launch_prepass_t(const PrepassLaunch& L, hipStream_t st)
+{
+    PrepassParams pp;
+    pp.A = (const u16*)L.A; pp.lda = L.lda;
+    pp.B = (const u16*)L.B; pp.ldb = L.ldb;
+    pp.Mb = L.Mb; pp.Kb = L.Kb; pp.Nb = L.Nb;
+    pp.outA = (u16*)L.outA; pp.outB = (u16*)L.outB;
+    pp.strideA = L.strideA; pp.strideB = L.strideB;
+    pp.counters = L.counters; pp.n_counters = L.n_counters;
+    const int64_t na = (int64_t)L.Mb * (L.Kb / 8), nb = (int64_t)L.Kb * (L.Nb / 8);
+    pp.blocksA = (int)((na + 255) / 256);
+    const int blocks = pp.blocksA + (int)((nb + 255) / 256);
+    if (blocks == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((k_prepass<LEVELS, IBF, OBF, ALL>), dim3(blocks), dim3(256), 0, st, pp);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ fused group kernel
+
+template <int LEVELS>
+struct FusedCfg;
+template <>
+struct FusedCfg<1> { using C = CfgF1; };
+template <>
+struct FusedCfg<2> { using C = CfgF2; };
+
+// C_o += W[r][o] * H for every output block o.  The coefficients are
+// uniform kernel arguments; zero ones are skipped by a scalar branch.
+template <int NOUT, class C>
+__device__ __forceinline__ void combine_h(const int8_t* w, const typename C::acc_t (&H)[C::FM][C::FN],
+                                          typename C::acc_t (&Cacc)[NOUT][C::FM][C::FN])
+{
+#pragma unroll
+    for (int o = 0; o < NOUT; ++o) {
+        const int c = w[o];
+        if (c != 0) {
+            const float fc = (float)c;
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j)
+                    Cacc[o][i][j] += fc * H[i][j];
+        }
+    }
+}
+
+template <int LEVELS, bool OBF, bool CBF>
+__global__ void __launch_bounds__(FusedCfg<LEVELS>::C::NT) k_fused(const FusedParams fp)
+{
+    using C = typename FusedCfg<LEVELS>::C;
+    constexpr int S = Scheme<LEVELS>::S, NOUT = S * S;
+    constexpr int G4 = C::NACC / 4;                     // float4 groups per accumulator tile
+    constexpr int PART_F4 = NOUT * C::FM * C::FN * G4;  // float4 per thread in a partial
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    __shared__ int sh_old;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int w = blockIdx.x;
+    const int n_items = sched_count(fp.sp, w);
+    const int nk = (fp.Kb + C::BK - 1) / C::BK;
+
+    for (int it = 0; it < n_items; ++it) {
+        const Item item = sched_item(fp.sp, w, it);
+        int p, q;
+        tile_coords(item.g, fp.sp.gy, fp.sp.gx, fp.sp.P, fp.sp.raster, &p, &q);
+        const int m0 = p * C::BM, n0 = q * C::BN;
+
+        typename C::acc_t Cacc[NOUT][C::FM][C::FN];
+#pragma unroll
+        for (int o = 0; o < NOUT; ++o)
+            zero_acc<C>(Cacc[o]);
+        typename C::acc_t H[C::FM][C::FN];
+        zero_acc<C>(H);
+
+        auto src_of = [&](int pos) {
+            const int r = fp.order[pos];
+            return make_src(fp.a[r] + (int64_t)m0 * fp.lda[r], fp.lda[r], fp.Mb - m0,
+                            fp.b[r] + n0, fp.ldb[r], fp.Nb - n0, fp.Kb);
+        };
+        const int ntiles = (item.pos1 - item.pos0) * nk;
+        Src nxt = src_of(item.pos0);
+        Regs<C> Rg;
+        load_tile<C, true>(Rg, nxt, 0, tid);
+        store_tile<C>(smem, Rg, tid);
+        __syncthreads();
+        for (int t = 0; t < ntiles; ++t) {
+            const int t1 = t + 1;
+            if (t1 < ntiles) {
+                const int k1 = t1 % nk;
+                if (k1 == 0)
+                    nxt = src_of(item.pos0 + t1 / nk);
+                load_tile<C, true>(Rg, nxt, k1 * C::BK, tid);
+            }
+            compute_stage<C, OBF>(smem + (t & 1) * C::STAGE, H, wm, wn, lane);
+            if (t % nk == nk - 1) {
+                combine_h<NOUT, C>(fp.w[fp.order[item.pos0 + t / nk]], H, Cacc);
+                zero_acc<C>(H);
+            }
+            if (t1 < ntiles)
+                store_tile<C>(smem + (t1 & 1) * C::STAGE, Rg, tid);
+            __syncthreads();
+        }
+
+        bool store = true;
+        if (item.slot >= 0) {
+            // Split group: publish this piece's fp32 partial, then the second
+            // arriver adds the other piece's partial and writes C.
+            const int which = item.pos0 == 0 ? 0 : 1;
+            f32x4* mine = reinterpret_cast<f32x4*>(fp.partial) + ((int64_t)item.slot * 2 + which) * PART_F4 * C::NT;
+            const f32x4* other = reinterpret_cast<const f32x4*>(fp.partial) + ((int64_t)item.slot * 2 + (1 - which)) * PART_F4 * C::NT;
+#pragma unroll
+            for (int o = 0; o < NOUT; ++o)
+#pragma unroll
+                for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                        for (int g = 0; g < G4; ++g) {
+                            const int e = ((o * C::FM + i) * C::FN + j) * G4 + g;
+                            mine[(int64_t)e * C::NT + tid] =
+                                f32x4{Cacc[o][i][j][4 * g], Cacc[o][i][j][4 * g + 1],
+                                      Cacc[o][i][j][4 * g + 2], Cacc[o][i][j][4 * g + 3]};
+                        }
+            __threadfence();
+            __syncthreads();
+            if (tid == 0)
+                sh_old = __hip_atomic_fetch_add(fp.counters + item.slot, 1, __ATOMIC_ACQ_REL,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            store = sh_old == 1;
+            if (store) {
+                __threadfence();
+#pragma unroll
+                for (int o = 0; o < NOUT; ++o) {
+                    // One output block at a time: keeps the compiler from
+                    // hoisting every partial load ahead of the adds.
+                    asm volatile("" ::: "memory");
+#pragma unroll
+                    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                            for (int g = 0; g < G4; ++g) {
+                                const int e = ((o * C::FM + i) * C::FN + j) * G4 + g;
+                                const f32x4 v = __builtin_nontemporal_load(other + (int64_t)e * C::NT + tid);
+                                Cacc[o][i][j][4 * g] += v.x;
+                                Cacc[o][i][j][4 * g + 1] += v.y;
+                                Cacc[o][i][j][4 * g + 2] += v.z;
+                                Cacc[o][i][j][4 * g + 3] += v.w;
+                            }
+                }
+                if (tid == 0)
+                    __hip_atomic_store(fp.counters + item.slot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        if (store) {
+#pragma unroll
+            for (int o = 0; o < NOUT; ++o) {
+                const int bi = o / S, bj = o % S;
+                store_c<C, CBF>(Cacc[o], fp.C + (int64_t)(bi * fp.Mb + m0) * fp.ldc + bj * fp.Nb + n0, fp.ldc,
+                                fp.Mb - m0, fp.Nb - n0, fp.vec4 != 0, wm, wn, lane);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <int LEVELS, bool OBF, bool CBF>
+hipError_t launch_fused_t(const FusedLaunch& L, hipStream_t st)
+{
+    using C = typename FusedCfg<LEVELS>::C;
+    if (L.grid <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((k_fused<LEVELS, OBF, CBF>), dim3(L.grid), dim3(C::NT), 0, st, L.p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ host entry points
+
+void classic_tile_dims(int32_t tile, int32_t* bm, int32_t* bn)
+{
+    switch (tile) {
+    case kTile256: *bm = Cfg256::BM; *bn = Cfg256::BN; break;
+    case kTile128: *bm = Cfg128::BM; *bn = Cfg128::BN; break;
+    default: *bm = Cfg32::BM; *bn = Cfg32::BN; break;
+    }
+}
+
+hipError_t launch_classic(const ClassicLaunch& L, hipStream_t st)
+{
+    switch (L.tile) {
+    case kTile256: return launch_classic_c<Cfg256>(L, st);
+    case kTile128: return launch_classic_c<Cfg128>(L, st);
+    default: return launch_classic_c<Cfg32>(L, st);
+    }
+}
+
+hipError_t launch_prepass(const PrepassLaunch& L, hipStream_t st)
+{
+    const bool all = L.write_all != 0;
+    if (L.levels == 1) {
+        if (L.in_bf16)
+            return L.op_bf16 ? (all ? launch_prepass_t<1, true, true, true>(L, st) : launch_prepass_t<1, true, true, false>(L, st))
+                             : launch_prepass_t<1, true, false, true>(L, st);
+        return launch_prepass_t<1, false, false, false>(L, st);
+    }
+    if (L.in_bf16)
+        return L.op_bf16 ? (all ? launch_prepass_t<2, true, true, true>(L, st) : launch_prepass_t<2, true, true, false>(L, st))
+                         : launch_prepass_t<2, true, false, true>(L, st);
+    return launch_prepass_t<2, false, false, false>(L, st);
+}
+
+int32_t fused_tile(int32_t levels) { return levels == 1 ? FusedCfg<1>::C::BM : FusedCfg<2>::C::BM; }
+static_assert(FusedCfg<1>::C::BM == FusedCfg<1>::C::BN && FusedCfg<2>::C::BM == FusedCfg<2>::C::BN,
+              "fused tiles are square");
+
+int64_t fused_partial_bytes(int32_t levels)
+{
+    if (levels == 1) {
+        using C = FusedCfg<1>::C;
+        return (int64_t)4 * C::BM * C::BN * 4;
+    }
+    using C = FusedCfg<2>::C;
+    return (int64_t)16 * C::BM * C::BN * 4;
+}
+
+void fused_order(int32_t levels, int8_t* order)
+{
+    // One level: P3, P5, P2, P4, P1, P6, P7 (0-based 2, 4, 1, 3, 0, 5, 6):
+    // a split after the first four leaves each piece touching few outputs.
+    static const int8_t o1[7] = {2, 4, 1, 3, 0, 5, 6};
+    if (levels == 1) {
+        for (int i = 0; i < 7; ++i)
+            order[i] = o1[i];
+        return;
+    }
+    for (int a = 0; a < 7; ++a)
+        for (int b = 0; b < 7; ++b)
+            order[a * 7 + b] = (int8_t)(o1[a] * 7 + o1[b]);
+}
+
+hipError_t launch_fused(const FusedLaunch& L, hipStream_t st)
+{
+    if (L.levels == 1) {
+        if (L.out_bf16)
+            return L.op_bf16 ? launch_fused_t<1, true, true>(L, st) : launch_fused_t<1, false, true>(L, st);
+        return launch_fused_t<1, false, false>(L, st);
+    }
+    if (L.out_bf16)
+        return L.op_bf16 ? launch_fused_t<2, true, true>(L, st) : launch_fused_t<2, false, true>(L, st);
+    return launch_fused_t<2, false, false>(L, st);
+}
+
+}  // namespace lcma

@@ -1,0 +1,215 @@
+/*
+ * lcma.h -- C ABI of the MI355X (gfx950) half-precision GEMM library:
+ * a classic MFMA GEMM and low-complexity (LCMA / Strassen-type) products.
+ *
+ * Operation (all entry points): C = A * B, C overwritten (no alpha/beta).
+ *   A: M x K, B: K x N, C: M x N, row-major with leading dimensions
+ *   lda >= K, ldb >= N, ldc >= N (elements).  A, B and C share one storage
+ *   type (binary16 or bfloat16).  Products accumulate in fp32 and C is
+ *   rounded once, to nearest even, to the storage type.  NaN/Inf propagate
+ *   as IEEE arithmetic makes them; nothing is checked.
+ *
+ * Sources (cited by page title and section):
+ *   [FG] "FalconGEMM: Surpassing Hardware Peaks with Lower-Complexity Matrix
+ *        Multiplication" (HyperAI write-up of the talk):
+ *        "从 Strassen 出发" -- Strassen 8 -> 7, two levels 64 -> 49, the LCMA
+ *            description (which input blocks are combined, how many
+ *            products, how products combine into C);
+ *        "从 LCMA 到 FalconGEMM" -- combine A/B, 7 batched products, combine
+ *            H; spatial groups on one compute unit with on-chip accumulation
+ *            into C; split of a group over two compute units; reordering for
+ *            L2 locality; persistent kernel;
+ *        "从缓存重排到 Cost Model" -- roofline-like cost model that picks the
+ *            algorithm per shape; fp32 on-chip combination with one final
+ *            cast.
+ *   [KP] "Kernel 与性能" notes page, section "Roofline" (I = FLOPs / bytes,
+ *        F <= min(F_max, I * B_max)).
+ *
+ * Memory ownership: the caller owns A, B, C and the workspace (device
+ * memory).  The library never allocates device memory.  A plan owns only
+ * host memory.  A plan is immutable after lcma_plan() and may be used from
+ * several threads, each with its own workspace.
+ *
+ * Streams: launching calls only enqueue work on `stream` (a hipStream_t; 0
+ * is the null stream) and never synchronise.  Launch failures are reported
+ * as LCMA_E_HIP (from hipGetLastError).
+ *
+ * Errors: every call returns an lcma_status; no exception crosses the ABI.
+ * All argument checks run before any device call, so invalid calls never
+ * touch the GPU.
+ */
+#ifndef LCMA_H_
+#define LCMA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LCMA_F16 = 0, LCMA_BF16 = 1 } lcma_dtype;
+
+typedef enum {
+    LCMA_ALGO_AUTO = 0,     /* cost model picks */
+    LCMA_ALGO_CLASSIC = 1,  /* one tiled MFMA GEMM */
+    LCMA_ALGO_L1 = 2,       /* one-level Strassen: 7 block products */
+    LCMA_ALGO_L2 = 3        /* two-level Strassen: 49 block products */
+} lcma_algo;
+
+typedef enum {
+    LCMA_OK = 0,
+    LCMA_E_INVALID = 1,        /* bad argument (negative size, null pointer, ld too small, ...) */
+    LCMA_E_UNSUPPORTED = 2,    /* valid but not implemented (alignment, forced algo on an unsplittable shape) */
+    LCMA_E_BAD_DESCRIPTOR = 3, /* descriptor fails Brent's identity or is malformed */
+    LCMA_E_WORKSPACE = 4,      /* workspace missing or smaller than lcma_plan_info() reports */
+    LCMA_E_HIP = 5,            /* a HIP runtime call failed */
+    LCMA_E_NOMEM = 6           /* host allocation failed */
+} lcma_status;
+
+/* How a tail group may be split over two compute units ([FG] "从 LCMA 到
+ * FalconGEMM": a group is split over two compute units when needed). */
+typedef enum {
+    LCMA_SPLIT_AUTO = 0,  /* split the last, partial round of groups when that shortens it */
+    LCMA_SPLIT_NONE = 1,  /* never split */
+    LCMA_SPLIT_ALL = 2    /* split every group (testing the fix-up path) */
+} lcma_split;
+
+/* How the combined operands reach the fused kernel. */
+typedef enum {
+    LCMA_COMBINE_AUTO = 0,
+    LCMA_COMBINE_PREPASS = 1, /* a separate bandwidth-bound pass writes each combined operand to the workspace */
+    LCMA_COMBINE_AT_LOAD = 2  /* the fused kernel forms the combinations while staging tiles (one-level only) */
+} lcma_combine;
+
+/*
+ * An LCMA description ([FG] "从 Strassen 出发").  A is split into ms x ks
+ * blocks, B into ks x ns, C into ms x ns; product r (0-based) is
+ *   Ahat_r = sum_{i,k} U[r*ms*ks + i*ks + k] * A_ik
+ *   Bhat_r = sum_{k,j} V[r*ks*ns + k*ns + j] * B_kj
+ *   H_r    = Ahat_r * Bhat_r
+ *   C_ij   = sum_r W[r*ms*ns + i*ns + j] * H_r
+ * Tables are row-major int8, rank rows each.  Block (i, k) of a two-level
+ * split uses i = 2*i_outer + i_inner (outer-major).
+ */
+typedef struct {
+    int32_t ms, ks, ns, rank;
+    const int8_t* U;
+    const int8_t* V;
+    const int8_t* W;
+} lcma_desc;
+
+/* Optional planning knobs; pass NULL to lcma_plan_ex for the defaults
+ * (all-zero fields mean "default"). */
+typedef struct {
+    lcma_split split;
+    lcma_combine combine;
+    int32_t bf16_ops_f16;   /* bfloat16 inputs only: 1 = combined operands are rounded to
+                               binary16 (3 more fraction bits; requires |combinations| < 65504),
+                               0 = default (binary16 operands for two-level, bfloat16 for one-level),
+                               -1 = always bfloat16 operands */
+    int32_t num_cus;        /* 0 = query the current device; >0 = plan for that many compute units
+                               (host-only planning and tests) */
+    double peak_tflops;     /* 0 = 2516 (dense fp16/bf16 MFMA: 256 CUs x 4096 FLOP/clk x 2.4 GHz) */
+    double hbm_gbps;        /* 0 = 8000 */
+} lcma_options;
+
+typedef struct lcma_plan_s* lcma_plan_t;
+
+/* Built-in Strassen schemes: levels = 1 (2x2x2, rank 7) or 2 (4x4x4, rank
+ * 49, the Kronecker square of the one-level scheme).  The tables are static
+ * storage owned by the library (do not free).
+ * Errors: LCMA_E_INVALID (levels not 1 or 2, out == NULL). */
+lcma_status lcma_desc_builtin(int32_t levels, lcma_desc* out);
+
+/* Checks a description: positive sizes, coefficients in [-8, 8], and
+ * Brent's identity sum_r U[r][i,k] V[r][k',j] W[r][i',j'] =
+ * [k==k'][i==i'][j==j'] (exact integers).  LCMA_OK or LCMA_E_BAD_DESCRIPTOR
+ * (LCMA_E_INVALID for NULL). */
+lcma_status lcma_desc_validate(const lcma_desc* desc);
+
+/* Plans C = A * B for an M x N x K product of storage type dt.
+ *   desc:  NULL = built-in Strassen schemes; otherwise validated
+ *          (LCMA_E_BAD_DESCRIPTOR) and deep-copied.  A description that is
+ *          not one of the built-in schemes is LCMA_E_UNSUPPORTED when an
+ *          LCMA path is forced, and is ignored by LCMA_ALGO_AUTO.
+ *   force: LCMA_ALGO_AUTO lets the roofline cost model pick among the
+ *          admissible algorithms (ties go to classic);
+ *          a forced L1/L2 on a shape it cannot split returns
+ *          LCMA_E_UNSUPPORTED.
+ * Sizes: M, N, K >= 0 (negative: LCMA_E_INVALID).  Zero-sized products are
+ * valid (K = 0 writes C = 0).  Performs no device work; the only HIP call
+ * is a device-property query when opts->num_cus is 0.
+ * On success *out receives a plan to free with lcma_plan_destroy. */
+lcma_status lcma_plan(int64_t M, int64_t N, int64_t K, lcma_dtype dt,
+                      const lcma_desc* desc, lcma_algo force, lcma_plan_t* out);
+lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt,
+                         const lcma_desc* desc, lcma_algo force,
+                         const lcma_options* opts, lcma_plan_t* out);
+
+/* What the plan chose: algorithm, workspace bytes the caller must pass to
+ * lcma_gemm, and the cost model's time estimate in seconds (any output
+ * pointer may be NULL). */
+lcma_status lcma_plan_info(lcma_plan_t plan, lcma_algo* chosen, size_t* workspace_bytes,
+                           double* est_seconds);
+
+/* Cost-model estimate (seconds) the plan computed for one algorithm;
+ * a negative value means the algorithm was not admissible for the shape. */
+lcma_status lcma_plan_estimate(lcma_plan_t plan, lcma_algo algo, double* est_seconds);
+
+/* Runs the planned product on `stream`.  A, B, C: device pointers as above.
+ * Fast path: pointers 16-byte aligned and lda, ldb multiples of 8; classic
+ * accepts any alignment (slower element loads), LCMA paths require it
+ * (LCMA_E_UNSUPPORTED otherwise).  workspace: device memory of at least
+ * the planned size (may be NULL when that size is 0); it must not be used
+ * by two calls that can overlap.
+ * Errors: LCMA_E_INVALID (NULL pointers with nonzero sizes, ld too small),
+ * LCMA_E_WORKSPACE, LCMA_E_UNSUPPORTED, LCMA_E_HIP. */
+lcma_status lcma_gemm(lcma_plan_t plan, const void* A, int64_t lda, const void* B, int64_t ldb,
+                      void* C, int64_t ldc, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* The two halves of lcma_gemm for an LCMA plan using the pre-pass, exposed
+ * so each kernel can be checked and timed on its own: lcma_prepass writes
+ * the combined operands (and clears the split counters) in the workspace;
+ * lcma_fused then runs the persistent group kernel from them.  Calling
+ * lcma_prepass then lcma_fused on one stream equals lcma_gemm.  For other
+ * plans: LCMA_E_INVALID. */
+lcma_status lcma_prepass(lcma_plan_t plan, const void* A, int64_t lda, const void* B, int64_t ldb,
+                         void* workspace, size_t workspace_bytes, void* stream);
+lcma_status lcma_fused(lcma_plan_t plan, const void* A, int64_t lda, const void* B, int64_t ldb,
+                       void* C, int64_t ldc, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Where the pre-pass puts the combined operand of product r (0-based) in the
+ * workspace: side 0 = A (an (M/ms) x (K/ks) matrix), side 1 = B (a (K/ks) x
+ * (N/ns) matrix).  *offset_bytes receives its byte offset and *ld its
+ * leading dimension; *offset_bytes = -1 when the operand is a single input
+ * block read in place (not copied).  *dtype receives the operand type. */
+lcma_status lcma_plan_operand(lcma_plan_t plan, int32_t side, int32_t r, int64_t* offset_bytes,
+                              int64_t* ld, lcma_dtype* dtype);
+
+/* Schedule of the persistent kernel, for host-side checking.  Fills up to
+ * `cap` work items, 5 int32 each: worker, group, first product position,
+ * end product position (in the kernel's product order), split slot (-1 for
+ * a whole group).  *count receives the total number of items (call with
+ * cap = 0 to size).  *order (if not NULL, `rank` entries) receives the
+ * kernel's product order.  LCMA_E_INVALID for a classic plan. */
+lcma_status lcma_plan_schedule(lcma_plan_t plan, int32_t* items, int64_t cap, int64_t* count,
+                               int32_t* order);
+
+/* Classic MFMA GEMM without a plan (enqueues one kernel on `stream`).
+ * Same layout, alignment and error rules as lcma_gemm. */
+lcma_status gemm_classic(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const void* A, int64_t lda,
+                         const void* B, int64_t ldb, void* C, int64_t ldc, void* stream);
+
+void lcma_plan_destroy(lcma_plan_t plan);
+
+/* Static text for a status code. */
+const char* lcma_status_str(lcma_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCMA_H_ */

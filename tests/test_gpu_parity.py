@@ -1,0 +1,321 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Gates (normwise, from the accuracy target of the build):
+  e_nw = ||C - C_ref||_F / (||A||_F ||B||_F) <= 1e-3 (binary16), <= 8e-3 (bfloat16),
+  e_nw(LCMA) <= 4 * e_nw(classic GPU) on the same inputs.
+Because e_nw shrinks like 1/sqrt(K) for independent entries, every float case
+also requires e_rel = ||C - C_ref||_F / ||C_ref||_F <= 4 u_out (whole matrix
+and per output block); integer-valued inputs must match bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import complexity_half_precision_amd as L
+import oracle
+import seeded_inputs as si
+from oracle import metrics
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def gen(M, N, K, dtype, dist, seed=0):
+    A, B = si.gen(M, N, K, dtype, dist, seed)
+    return A, B, si.f64(A), si.f64(B)
+
+
+def classic(A, B):
+    M, K = A.shape
+    N = B.shape[1]
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    C = torch.empty((M, N), dtype=A.dtype, device=DEV)
+    L.gemm_classic(Ad, Bd, C)
+    torch.cuda.synchronize()
+    return C.cpu()
+
+
+def planned(A, B, algo, **kw):
+    M, K = A.shape
+    N = B.shape[1]
+    plan = L.lcma_plan_ex(M, N, K, A.dtype, force=algo, **kw)
+    assert L.lcma_plan_info(plan)[0] == algo
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    C = torch.empty((M, N), dtype=A.dtype, device=DEV)
+    ws = L.workspace_for(plan)
+    L.lcma_gemm(plan, Ad, Bd, C, ws)
+    torch.cuda.synchronize()
+    return C.cpu()
+
+
+def check_float(C, A64, B64, dtype, C_ref=None, blocks=1):
+    C_ref = oracle.gemm(A64, B64) if C_ref is None else C_ref
+    c = si.f64(C)
+    assert np.all(np.isfinite(c))
+    e = metrics.e_nw(c, C_ref, A64, B64)
+    assert e <= metrics.GATE_NW[dtype], e
+    u = metrics.UNIT_ROUNDOFF[dtype]
+    assert metrics.e_rel(c, C_ref) <= 4 * u
+    if blocks > 1:
+        assert max(metrics.e_rel_blocks(c, C_ref, blocks)) <= 4 * u
+    return e
+
+
+def check_exact(C, A64, B64, dtype):
+    want = oracle.encode(dtype, oracle.gemm(A64, B64))
+    got = si.bits(C)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:3].tolist()}"
+
+
+# ---------------------------------------------------------------- classic
+
+CLASSIC_SHAPES = [
+    (1, 8, 8), (7, 13, 5), (3, 1, 9), (33, 40, 24), (64, 64, 64), (65, 72, 136),
+    (100, 200, 304), (257, 136, 72), (300, 520, 1000), (513, 264, 520),
+    (4100, 4104, 72),          # 256 x 256 tiles with ragged tails in M and N
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K", CLASSIC_SHAPES)
+def test_classic_matches_oracle(M, N, K, dtype):
+    say("classic", M, N, K, dtype)
+    A, B, A64, B64 = gen(M, N, K, dtype, "uniform", seed=M + N + K)
+    check_float(classic(A, B), A64, B64, dtype)
+
+
+@pytest.mark.parametrize("dtype,dist", [("f16", "int2"), ("bf16", "int1")])
+@pytest.mark.parametrize("M,N,K", [(33, 40, 24), (130, 200, 96), (257, 136, 120), (512, 512, 256), (4100, 264, 64)])
+def test_classic_integer_inputs_are_exact(M, N, K, dtype, dist):
+    say("classic exact", M, N, K, dtype)
+    A, B, A64, B64 = gen(M, N, K, dtype, dist, seed=7)
+    check_exact(classic(A, B), A64, B64, dtype)
+
+
+def test_classic_strided_operands_and_output():
+    say("classic strided")
+    M, N, K = 200, 136, 72
+    Abig, Bbig, _, _ = gen(M, N + 24, K + 40, "f16", "uniform", seed=3)
+    A = Abig[:, :K]                     # lda = K + 40
+    B = Bbig[:K, :N]                    # ldb = N + 24
+    A64, B64 = si.f64(A), si.f64(B)
+    Ad, Bd = Abig.to(DEV)[:, :K], Bbig.to(DEV)[:K, :N]
+    Cbig = torch.full((M, N + 16), 7.0, dtype=torch.float16, device=DEV)
+    C = Cbig[:, :N]
+    L.gemm_classic(Ad, Bd, C)
+    torch.cuda.synchronize()
+    check_float(C.cpu(), A64, B64, "f16")
+    assert torch.all(Cbig[:, N:].cpu() == 7.0)     # nothing written outside C
+
+
+def test_classic_unaligned_pointers():
+    say("classic unaligned")
+    M, N, K = 96, 80, 64
+    A, B, A64, B64 = gen(M, N, K, "bf16", "uniform", seed=4)
+    flatA = torch.zeros(M * K + 1, dtype=torch.bfloat16, device=DEV)
+    flatA[1:] = A.reshape(-1).to(DEV)
+    Ad = flatA[1:].view(M, K)            # 2-byte offset: element-wise load path
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    L.gemm_classic(Ad, B.to(DEV), C)
+    torch.cuda.synchronize()
+    check_float(C.cpu(), A64, B64, "bf16")
+
+
+def test_classic_empty_and_zero_k():
+    say("classic empty")
+    A = torch.empty((0, 16), dtype=torch.float16, device=DEV)
+    B = torch.ones((16, 8), dtype=torch.float16, device=DEV)
+    C = torch.empty((0, 8), dtype=torch.float16, device=DEV)
+    L.gemm_classic(A, B, C)
+    A = torch.ones((5, 0), dtype=torch.float16, device=DEV)
+    B = torch.ones((0, 24), dtype=torch.float16, device=DEV)
+    C = torch.full((5, 24), 3.0, dtype=torch.float16, device=DEV)
+    L.gemm_classic(A, B, C, K=0)
+    torch.cuda.synchronize()
+    assert torch.all(C.cpu() == 0)
+
+
+def test_classic_is_deterministic():
+    say("classic determinism")
+    A, B, _, _ = gen(1024, 1024, 1024, "bf16", "normal_sqrtk", seed=5)
+    r = [si.bits(classic(A, B)) for _ in range(3)]
+    assert np.array_equal(r[0], r[1]) and np.array_equal(r[0], r[2])
+
+
+# ---------------------------------------------------------------- one level
+
+def test_l1_square_512_f16_matches_oracle_and_ratio():
+    say("l1 512 f16")
+    A, B, A64, B64 = gen(**si.SQUARE_512_F16)
+    C_ref = oracle.gemm(A64, B64)
+    e_c = check_float(classic(A, B), A64, B64, "f16", C_ref)
+    C1 = planned(A, B, "l1")
+    e_1 = check_float(C1, A64, B64, "f16", C_ref, blocks=2)
+    assert e_1 <= 4 * e_c, (e_1, e_c)
+    # against the oracle's evaluation with binary16 combined operands: only
+    # fp32 accumulation order and the final rounding differ
+    C_sh, n = oracle.lcma(A64, B64, oracle.strassen(), 1, round_operands="f16")
+    assert n == 7
+    assert metrics.e_rel(si.f64(C1), C_sh) <= 2 * metrics.UNIT_ROUNDOFF["f16"]
+
+
+@pytest.mark.parametrize("algo", ["l1", "l2"])
+def test_lcma_integer_inputs_are_exact(algo):
+    say("exact", algo)
+    A, B, A64, B64 = gen(**si.SQUARE_512_F16_INT)
+    check_exact(planned(A, B, algo), A64, B64, "f16")
+    A, B, A64, B64 = gen(256, 512, 384, "bf16", "int1", seed=2)
+    check_exact(planned(A, B, algo), A64, B64, "bf16")
+
+
+@pytest.mark.parametrize("ops", [-1, 1])
+def test_l1_bf16_operand_modes(ops):
+    say("l1 bf16 ops", ops)
+    A, B, A64, B64 = gen(1024, 1024, 1024, "bf16", "normal_sqrtk", seed=9)
+    C_ref = oracle.gemm(A64, B64)
+    e_c = check_float(classic(A, B), A64, B64, "bf16", C_ref)
+    e_1 = check_float(planned(A, B, "l1", bf16_ops_f16=ops), A64, B64, "bf16", C_ref, blocks=2)
+    assert e_1 <= 4 * e_c
+
+
+def test_prepass_operands_are_rne_of_the_exact_combination():
+    say("prepass bits")
+    M = N = K = 512
+    for dtype, dist in (("f16", "uniform"), ("bf16", "normal_sqrtk")):
+        A, B, A64, B64 = gen(M, N, K, dtype, dist, seed=11)
+        plan = L.lcma_plan_ex(M, N, K, dtype, force="l1")
+        ws = L.workspace_for(plan)
+        L.lcma_prepass(plan, A.to(DEV), B.to(DEV), ws)
+        torch.cuda.synchronize()
+        wsh = ws.cpu()
+        d = oracle.strassen()
+        for side, X, T in ((0, A64, d.U), (1, B64, d.V)):
+            for r in range(7):
+                off, ld, odt = L.lcma_plan_operand(plan, side, r)
+                if off < 0:
+                    continue
+                odt = "f16" if odt == L.F16 else "bf16"
+                rows, cols = (M // 2, K // 2) if side == 0 else (K // 2, N // 2)
+                got = wsh[off:off + rows * cols * 2].view(torch.int16).numpy().view(np.uint16).reshape(rows, cols)
+                exact = oracle.combine_block(X, T[r], 2, 2)
+                want = oracle.encode(odt, exact)
+                # the kernel sums in fp32: where that sum is exact the result must be bitwise equal
+                fp32_exact = np.float32(exact).astype(np.float64) == exact
+                assert np.array_equal(got[fp32_exact], want[fp32_exact]), (side, r)
+                assert fp32_exact.mean() > 0.99
+
+
+@pytest.mark.parametrize("split", ["none", "all"])
+def test_l1_split_modes_reproducible(split):
+    say("l1 split", split)
+    A, B, A64, B64 = gen(1024, 768, 512, "f16", "uniform", seed=13)
+    C_ref = oracle.gemm(A64, B64)
+    runs = [planned(A, B, "l1", split=split) for _ in range(3)]
+    check_float(runs[0], A64, B64, "f16", C_ref, blocks=2)
+    b = [si.bits(c) for c in runs]
+    assert np.array_equal(b[0], b[1]) and np.array_equal(b[0], b[2])
+
+
+@pytest.mark.parametrize("n", [2560, 6144])
+def test_l1_tail_split_shapes(n):
+    # 2560: 100 groups on 256 CUs (every group split); 6144: 576 groups (64-group split tail)
+    say("l1 tail", n)
+    A, B, A64, B64 = gen(n, n, 512, "bf16", "normal_sqrtk", seed=n)
+    plan = L.lcma_plan_ex(n, n, 512, "bf16", force="l1")
+    items, _ = L.lcma_plan_schedule(plan)
+    assert any(it[4] >= 0 for it in items)
+    C = si.f64(planned(A, B, "l1"))
+    rows = np.random.default_rng(1).choice(n, 24, replace=False)
+    ref = np.stack([oracle.gemm_rows(A64, B64, r, r + 1)[0] for r in rows])
+    assert metrics.e_rel(C[rows], ref) <= 4 * metrics.UNIT_ROUNDOFF["bf16"]
+    assert metrics.freivalds(C, A64, B64) <= 4 * metrics.UNIT_ROUNDOFF["bf16"]
+
+
+# ---------------------------------------------------------------- two levels
+
+def test_l2_bf16_matches_oracle_and_ratio():
+    say("l2 bf16")
+    A, B, A64, B64 = gen(1024, 1024, 1024, "bf16", "normal_sqrtk", seed=17)
+    C_ref = oracle.gemm(A64, B64)
+    e_c = check_float(classic(A, B), A64, B64, "bf16", C_ref)
+    C2 = planned(A, B, "l2")
+    e_2 = check_float(C2, A64, B64, "bf16", C_ref, blocks=4)
+    assert e_2 <= 4 * e_c
+    C_sh, n = oracle.lcma(A64, B64, oracle.strassen2(), 1, round_operands="f16")
+    assert n == 49
+    assert metrics.e_rel(si.f64(C2), C_sh) <= 2 * metrics.UNIT_ROUNDOFF["bf16"]
+
+
+def test_l2_f16_and_split_all():
+    say("l2 f16 split")
+    A, B, A64, B64 = gen(512, 768, 1024, "f16", "uniform", seed=19)
+    C_ref = oracle.gemm(A64, B64)
+    C0 = planned(A, B, "l2")
+    check_float(C0, A64, B64, "f16", C_ref, blocks=4)
+    C1 = planned(A, B, "l2", split="all")
+    check_float(C1, A64, B64, "f16", C_ref, blocks=4)
+    assert np.array_equal(si.bits(C1), si.bits(planned(A, B, "l2", split="all")))
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+def test_square_4096_bf16_classic_and_one_level():
+    say("4096 bf16")
+    A, B, A64, B64 = gen(**si.SQUARE_4096_BF16)
+    C_ref = oracle.gemm(A64, B64)
+    e_c = check_float(classic(A, B), A64, B64, "bf16", C_ref, blocks=2)
+    for ops in (-1, 1):
+        C1 = planned(A, B, "l1", bf16_ops_f16=ops)
+        e_1 = check_float(C1, A64, B64, "bf16", C_ref, blocks=2)
+        assert e_1 <= 4 * e_c, (ops, e_1, e_c)
+        assert metrics.freivalds(si.f64(C1), A64, B64) <= 4 * metrics.UNIT_ROUNDOFF["bf16"]
+
+
+@pytest.mark.parametrize("m", si.DECODE_MS)
+def test_skinny_decode_shapes(m):
+    say("decode", m)
+    w = si.decode_shape(m)
+    A, B, A64, B64 = gen(**w)
+    plan = L.lcma_plan(w["M"], w["N"], w["K"], "bf16")
+    assert L.lcma_plan_info(plan)[0] == "classic"
+    check_float(classic(A, B), A64, B64, "bf16")
+
+
+def test_sweep_shapes_auto():
+    for wl in si.sweep_workloads():
+        M, N, K = wl["M"], wl["N"], wl["K"]
+        say("sweep", M, N, K)
+        A, B, A64, B64 = gen(**wl)
+        plan = L.lcma_plan(M, N, K, "f16")
+        algo = L.lcma_plan_info(plan)[0]
+        Ad, Bd = A.to(DEV), B.to(DEV)
+        C = torch.empty((M, N), dtype=torch.float16, device=DEV)
+        L.lcma_gemm(plan, Ad, Bd, C, L.workspace_for(plan))
+        torch.cuda.synchronize()
+        check_float(C.cpu(), A64, B64, "f16")
+        del Ad, Bd, C
+
+
+def test_square_16384_bf16_sampled():
+    say("16384 bf16")
+    w = si.SQUARE_16384_BF16
+    A, B = si.gen(**w)
+    A64, B64 = si.f64(A), si.f64(B)
+    n = w["M"]
+    rows = np.random.default_rng(2).choice(n, 8, replace=False)
+    ref = np.stack([oracle.gemm_rows(A64, B64, r, r + 1)[0] for r in rows])
+    u = metrics.UNIT_ROUNDOFF["bf16"]
+    res = {}
+    for algo in ("classic", "l1", "l2"):
+        say("16384", algo)
+        C = si.f64(planned(A, B, algo))
+        res[algo] = metrics.e_rel(C[rows], ref)
+        assert res[algo] <= 4 * u, (algo, res[algo])
+        assert metrics.freivalds(C, A64, B64, seeds=(11,)) <= 4 * u
+        del C
+    assert res["l1"] <= 4 * res["classic"] and res["l2"] <= 4 * res["classic"]
