@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--only", default="", help="time only these algorithms (comma list), for profiling runs")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="first run 3 device copies of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -55,6 +57,13 @@ def main():
     C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
     flops = 2.0 * M * N * K
+    if args.copy_calib_mib:
+        src = torch.ones(args.copy_calib_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def ev():
         return torch.cuda.Event(enable_timing=True)

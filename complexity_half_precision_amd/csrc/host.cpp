@@ -676,7 +676,8 @@ lcma_status check_lcma_call(const lcma_plan_s* p, const void* A, int64_t lda, co
     lcma_status s = check_io(p->M, p->N, p->K, A, lda, B, ldb, C, ldc, io, need_c);
     if (s != LCMA_OK)
         return s;
-    if (!io->vec)
+    // LCMA paths use 16-byte operand loads and 8-byte C stores only.
+    if (!io->vec || (need_c && !io->vec4))
         return LCMA_E_UNSUPPORTED;
     return check_ws(p, ws, ws_bytes);
 }

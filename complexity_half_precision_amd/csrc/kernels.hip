@@ -269,31 +269,54 @@ __device__ __forceinline__ void store_tile(char* stage, const Regs<C>& R, int ti
     }
 }
 
-template <class C, bool BF>
-__device__ __forceinline__ void compute_stage(const char* stage, typename C::acc_t (&acc)[C::FM][C::FN],
-                                              int wm, int wn, int lane)
+// MFMA fragments of k step `s` of a stage: lane l feeds row (l % MT) of each
+// operand tile with 8 consecutive k, k chunk (l / MT) of the step.
+template <class C>
+__device__ __forceinline__ void read_frags(const char* stage, int s, u32x4 (&af)[C::FM], u32x4 (&bf)[C::FN],
+                                           int wm, int wn, int lane)
 {
+    constexpr int CPS = Mma<C::MT>::KSTEP / 8;   // 16-byte chunks per k step
     const char* sA = stage;
     const char* sB = stage + C::A_BYTES;
-    // Lane l feeds row (l % MT) of each operand tile with 8 consecutive k:
-    // k chunk (l / MT) of the MFMA's k step.
-    constexpr int KSTEPS = C::BK / Mma<C::MT>::KSTEP;
-    constexpr int CPS = Mma<C::MT>::KSTEP / 8;   // 16-byte chunks per k step
     const int r = lane % C::MT, hi = lane / C::MT;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-        u32x4 af[C::FM], bf[C::FN];
+    for (int i = 0; i < C::FM; ++i)
+        af[i] = *reinterpret_cast<const u32x4*>(sA + lds_off(wm * C::WTM + i * C::MT + r, CPS * s + hi));
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-            af[i] = *reinterpret_cast<const u32x4*>(sA + lds_off(wm * C::WTM + i * C::MT + r, CPS * s + hi));
+    for (int j = 0; j < C::FN; ++j)
+        bf[j] = *reinterpret_cast<const u32x4*>(sB + lds_off(wn * C::WTN + j * C::MT + r, CPS * s + hi));
+}
+
+template <class C, bool BF>
+__device__ __forceinline__ void mma_step(const u32x4 (&af)[C::FM], const u32x4 (&bf)[C::FN],
+                                         typename C::acc_t (&acc)[C::FM][C::FN])
+{
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
-            bf[j] = *reinterpret_cast<const u32x4*>(sB + lds_off(wn * C::WTN + j * C::MT + r, CPS * s + hi));
+            acc[i][j] = mfma<BF>(bf[j], af[i], acc[i][j]);
+}
+
+// One k-tile from LDS stage `cur`.  Fragments are double-buffered so the
+// reads of step s+1 are in flight while step s's MFMAs run.  With MORE, the
+// next tile (already loaded into R) is written to stage `nxt` during the last
+// MFMA step; `nxt` was last read one tile earlier, before the barrier that
+// ended it, so no wave still reads it.
+template <class C, bool BF, bool MORE>
+__device__ __forceinline__ void ktile(const char* cur, char* nxt, const Regs<C>& R,
+                                      typename C::acc_t (&acc)[C::FM][C::FN], int wm, int wn, int lane, int tid)
+{
+    constexpr int KSTEPS = C::BK / Mma<C::MT>::KSTEP;
+    u32x4 af[2][C::FM], bf[2][C::FN];
+    read_frags<C>(cur, 0, af[0], bf[0], wm, wn, lane);
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j)
-                acc[i][j] = mfma<BF>(bf[j], af[i], acc[i][j]);
+    for (int s = 0; s < KSTEPS; ++s) {
+        if (s + 1 < KSTEPS)
+            read_frags<C>(cur, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1], wm, wn, lane);
+        if (MORE && s == KSTEPS - 1)
+            store_tile<C>(nxt, R, tid);
+        mma_step<C, BF>(af[s & 1], bf[s & 1], acc);
     }
 }
 
@@ -301,9 +324,9 @@ __device__ __forceinline__ void compute_stage(const char* stage, typename C::acc
 // extent from there.  With operands swapped, lane l holds output row
 // (l % MT) and, per group of 4 accumulators, 4 consecutive columns:
 // 32x32: column 8*g + 4*(l/32) + e of group g; 16x16: column 4*(l/16) + e.
-template <class C, bool BF>
+template <class C, bool BF, bool VEC4>
 __device__ __forceinline__ void store_c(const typename C::acc_t (&acc)[C::FM][C::FN], u16* Cp, int64_t ldc,
-                                        int rows, int cols, bool vec4, int wm, int wn, int lane)
+                                        int rows, int cols, int wm, int wn, int lane)
 {
     const rsrc_t rc = make_rsrc(Cp);
     const int ld = (int)ldc;
@@ -318,7 +341,7 @@ __device__ __forceinline__ void store_c(const typename C::acc_t (&acc)[C::FM][C:
                 const int n = wn * C::WTN + j * C::MT + (C::MT == 32 ? 8 * g + 4 * hi : 4 * hi);
                 const float x0 = acc[i][j][4 * g], x1 = acc[i][j][4 * g + 1];
                 const float x2 = acc[i][j][4 * g + 2], x3 = acc[i][j][4 * g + 3];
-                if (vec4) {
+                if constexpr (VEC4) {
                     // cols is a multiple of 4 here, so the 4 columns are all valid or all not.
                     const u32 off = (m < rows && n < cols) ? (u32)(m * ld + n) * 2u : kOob;
                     __builtin_amdgcn_raw_buffer_store_b64(
@@ -371,15 +394,20 @@ k_classic(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int
     load_tile<C, VEC>(R, s, 0, tid);
     store_tile<C>(smem, R, tid);
     __syncthreads();
-    for (int t = 0; t < nk; ++t) {
-        if (t + 1 < nk)
-            load_tile<C, VEC>(R, s, (t + 1) * C::BK, tid);
-        compute_stage<C, BF>(smem + (t & 1) * C::STAGE, acc, wm, wn, lane);
-        if (t + 1 < nk)
-            store_tile<C>(smem + ((t + 1) & 1) * C::STAGE, R, tid);
+    // Tile t is computed from stage t % 2 while tile t+1 is fetched into
+    // registers and then written to the other stage; one barrier per tile.
+    int t = 0;
+    for (; t + 1 < nk; ++t) {
+        load_tile<C, VEC>(R, s, (t + 1) * C::BK, tid);
+        ktile<C, BF, true>(smem + (t & 1) * C::STAGE, smem + ((t + 1) & 1) * C::STAGE, R, acc, wm, wn, lane, tid);
         __syncthreads();
     }
-    store_c<C, BF>(acc, Cm + (int64_t)m0 * ldc + n0, ldc, M - m0, N - n0, vec4 != 0, wm, wn, lane);
+    if (t < nk)
+        ktile<C, BF, false>(smem + (t & 1) * C::STAGE, nullptr, R, acc, wm, wn, lane, tid);
+    if (vec4)
+        store_c<C, BF, true>(acc, Cm + (int64_t)m0 * ldc + n0, ldc, M - m0, N - n0, wm, wn, lane);
+    else
+        store_c<C, BF, false>(acc, Cm + (int64_t)m0 * ldc + n0, ldc, M - m0, N - n0, wm, wn, lane);
 }
 
 template <class C, bool BF, bool VEC>
@@ -535,6 +563,252 @@ hipError_t launch_prepass_t(const PrepassLaunch& L, hipStream_t st)
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ ping-pong engine
+//
+// The fast path for 16-byte aligned operands.  A workgroup of 8 waves owns a
+// BM x BN output tile; waves w and w+4 share a SIMD.  Tiles of 32 k are
+// copied global -> LDS by direct (LDS-DMA) buffer loads into a ring of 4
+// stages, two tiles ahead of use, so no VGPR staging and no VALU transposes
+// are needed:
+//   * A stage: BM rows of 32 k (64 bytes, four 16-byte chunks); logical chunk
+//     c of row m sits at chunk c ^ ((m >> 2) & 3).  16 consecutive rows then
+//     cover all 16 bank slots, so the 16-byte MFMA operand reads are
+//     conflict free.
+//   * B stage: 32 k rows of BN columns (row-major, as in memory); logical
+//     16-byte chunk c of row k sits at chunk c ^ (4 * (k & 3)).  The MFMA
+//     operand (8 consecutive k of one column per lane) is read with two
+//     ds_read_b64_tr_b16: within each 16-lane group, source lane s points at
+//     B[k0 + s/4][n0 + 4 (s % 4)] and lane i receives B[k0..k0+3][n0 + i].
+// The two waves of a SIMD alternate phases: while one issues the k-tile's
+// MFMAs from registers, the other reads the next k-tile's fragments from LDS
+// (and, for waves 0-3, issues the DMA of the tile two ahead).  A raw
+// s_barrier separates phases; explicit waitcnts order the DMA and the reads.
+namespace pp {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define LCMA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }       // lgkmcnt(0)
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }         // vmcnt(0)
+__device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct PCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = 32, WM = WM_, WN = WN_, MT = 32;
+    static constexpr int NSTAGE = 4, KSTEPS = BK / 16;
+    static constexpr int NW = WM * WN;
+    static constexpr int NT = NW * 64;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int FM = WTM / 32, FN = WTN / 32;
+    using acc_t = f32x16;
+    static constexpr int NACC = 16;
+    static constexpr int AROW = BK * 2;               // bytes per A row
+    static constexpr int BROW = BN * 2;               // bytes per B row
+    static constexpr int A_BYTES = BM * AROW;
+    static constexpr int B_BYTES = BK * BROW;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int LDS = NSTAGE * STAGE;
+    static constexpr int LOADERS = NW / 2;
+    static constexpr int A_PER = A_BYTES / 1024 / LOADERS;   // 1 KB DMA instructions per loader wave
+    static constexpr int B_PER = B_BYTES / 1024 / LOADERS;
+    static_assert(NW == 8, "ping-pong pairs two waves per SIMD");
+    static_assert(A_BYTES % (1024 * LOADERS) == 0 && B_BYTES % (1024 * LOADERS) == 0, "DMA split");
+    static_assert(BROW % 256 == 0 && FM >= 1 && FN >= 1, "tile shape");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(A_PER + B_PER < 16, "one tile's DMA count fits the vmcnt immediate");
+};
+
+__device__ __forceinline__ u32 a_swz(u32 m) { return (m >> 2) & 3u; }
+__device__ __forceinline__ u32 b_swz(u32 k) { return 4u * (k & 3u); }
+
+// Where k-tile data comes from: A rows from `a` (a_rows valid), B columns
+// from `b` (b_cols valid), k0 of K.
+struct TileSrc {
+    const u16* a; int lda; int a_rows;
+    const u16* b; int ldb; int b_cols;
+    int k0, K;
+};
+
+// DMA of one k-tile into `stage` by loader wave xw (0..LOADERS-1).
+template <class C>
+__device__ __forceinline__ void dma_tile(char* stage, const TileSrc& s, int xw, int lane)
+{
+    const rsrc_t ra = make_rsrc(s.a + s.k0);
+    const rsrc_t rb = make_rsrc(s.b + (int64_t)s.k0 * s.ldb);
+    const int kleft = s.K - s.k0;
+#pragma unroll
+    for (int i = 0; i < C::A_PER; ++i) {
+        const int ins = xw * C::A_PER + i;                 // rows 16*ins .. 16*ins+15
+        const int r = ins * 16 + (lane >> 2);
+        const int k = ((lane & 3) ^ (int)a_swz(r)) * 8;
+        const u32 off0 = (u32)(r * s.lda + k) * 2u;
+        const u32 off = ((r < s.a_rows) & (k < kleft)) ? off0 : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, LCMA_LDS(stage + ins * 1024), 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_PER; ++i) {
+        const int ins = xw * C::B_PER + i;
+        const int byte = ins * 1024 + lane * 16;
+        const int r = byte / C::BROW;
+        const int n = (((byte % C::BROW) >> 4) ^ (int)b_swz(r)) * 8;
+        const u32 off0 = (u32)(r * s.ldb + n) * 2u;
+        const u32 off = ((r < kleft) & (n < s.b_cols)) ? off0 : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LCMA_LDS(stage + C::A_BYTES + ins * 1024), 16, off, 0, 0, 0);
+    }
+}
+
+template <class C>
+struct Frags {
+    u32x4 a[C::KSTEPS][C::FM];
+    u32x4 b[C::KSTEPS][C::FN];
+};
+
+template <class C>
+__device__ __forceinline__ void read_frags(const char* stage, Frags<C>& F, int wm, int wn, int lane)
+{
+    const char* sA = stage;
+    const char* sB = stage + C::A_BYTES;
+    // A: lane -> row (lane & 31), logical chunk 2 st + (lane >> 5)
+    const u32 m = wm * C::WTM + (lane & 31);
+    const u32 f = a_swz(m);
+    const u32 abase = m * (u32)C::AROW + ((((lane >> 5) ^ f) & 1u) << 4) + ((f & 2u) << 4);
+    // B: 16-lane group g, lane s: k row 8 (g/2) + s/4 (+4), column 16 (g%2) + 4 (s%4)
+    const int g = lane >> 4, s = lane & 15;
+    const u32 kr = 8 * (g >> 1) + (s >> 2);
+    const u32 xb = b_swz(kr);
+#pragma unroll
+    for (int st = 0; st < C::KSTEPS; ++st) {
+        const u32 ao = abase ^ ((u32)st << 5);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+            F.a[st][i] = *reinterpret_cast<const u32x4*>(sA + ao + i * 32 * C::AROW);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+            const u32 n = wn * C::WTN + j * 32 + 16 * (g & 1) + 4 * (s & 3);
+            const u32 boff = (kr + 16 * st) * C::BROW + (((n >> 3) ^ xb) << 4) + (n & 7) * 2;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(sB + boff));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(sB + boff + 4 * C::BROW));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            F.b[st][j] = u32x4{l2.x, l2.y, h2.x, h2.y};
+        }
+    }
+}
+
+template <class C, bool BF>
+__device__ __forceinline__ void mma_frags(const Frags<C>& F, f32x16 (&acc)[C::FM][C::FN])
+{
+#pragma unroll
+    for (int st = 0; st < C::KSTEPS; ++st)
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                acc[i][j] = mfma<BF>(F.b[st][j], F.a[st][i], acc[i][j]);
+}
+
+// Runs `ntiles` k-tiles (tile t's source from src(t)) through the ping-pong
+// schedule for one role.  after(t) runs right after this wave's MFMAs of
+// tile t (used to fold a finished product into the outputs).  Both roles pass
+// 1 + 2*ntiles barriers.
+template <class C, bool BF, bool LOADER, class SrcFn, class AfterFn>
+__device__ __forceinline__ void run_tiles(char* smem, int ntiles, SrcFn src, AfterFn after, int wave, int wm, int wn,
+                                          int lane, f32x16 (&acc)[C::FM][C::FN])
+{
+    Frags<C> F;
+    if (LOADER) {
+        if (ntiles > 0)
+            dma_tile<C>(smem, src(0), wave, lane);
+        if (ntiles > 1) {
+            dma_tile<C>(smem + C::STAGE, src(1), wave, lane);
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (C::A_PER + C::B_PER));   // tile 0 landed
+        } else {
+            wait_vm0();
+        }
+    }
+    bar();
+    for (int t = 0; t < ntiles; ++t) {
+        const char* cur = smem + (t % C::NSTAGE) * C::STAGE;
+        if (LOADER) {
+            read_frags<C>(cur, F, wm, wn, lane);
+            if (t + 2 < ntiles)
+                dma_tile<C>(smem + ((t + 2) % C::NSTAGE) * C::STAGE, src(t + 2), wave, lane);
+            wait_lgkm0();
+            bar();
+            mma_frags<C, BF>(F, acc);
+            after(t);
+            if (t + 2 < ntiles)
+                __builtin_amdgcn_s_waitcnt(0x0F70 | (C::A_PER + C::B_PER));   // tile t+1 landed
+            else
+                wait_vm0();
+            bar();
+        } else {
+            if (t > 0) {
+                mma_frags<C, BF>(F, acc);
+                after(t - 1);
+            }
+            bar();
+            read_frags<C>(cur, F, wm, wn, lane);
+            wait_lgkm0();
+            bar();
+        }
+    }
+    if (!LOADER && ntiles > 0) {
+        mma_frags<C, BF>(F, acc);
+        after(ntiles - 1);
+    }
+}
+
+}  // namespace pp
+
+using PC256 = pp::PCfg<256, 256, 2, 4>;    // classic: 8 waves of 128 x 64
+using PCF1 = pp::PCfg<128, 128, 2, 4>;     // fused one-level: 8 waves of 64 x 32
+
+template <class C, bool BF>
+__global__ void __launch_bounds__(C::NT)
+k_classic_pp(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb, u16* __restrict__ Cm,
+             int64_t ldc, int M, int N, int K, int gy, int gx, int P, int vec4)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    int p, q;
+    tile_coords((int32_t)blockIdx.x, gy, gx, P, 8, &p, &q);
+    const int m0 = p * C::BM, n0 = q * C::BN;
+    const u16* Ab = A + (int64_t)m0 * lda;
+    const u16* Bb = B + n0;
+    const int nk = (K + C::BK - 1) / C::BK;
+    f32x16 acc[C::FM][C::FN];
+    zero_acc<C>(acc);
+    auto src = [&](int t) {
+        return pp::TileSrc{Ab, (int)lda, M - m0, Bb, (int)ldb, N - n0, t * C::BK, K};
+    };
+    auto after = [](int) {};
+    if (wave < C::NW / 2)
+        pp::run_tiles<C, BF, true>(smem, nk, src, after, wave, wm, wn, lane, acc);
+    else
+        pp::run_tiles<C, BF, false>(smem, nk, src, after, wave, wm, wn, lane, acc);
+    if (vec4)
+        store_c<C, BF, true>(acc, Cm + (int64_t)m0 * ldc + n0, ldc, M - m0, N - n0, wm, wn, lane);
+    else
+        store_c<C, BF, false>(acc, Cm + (int64_t)m0 * ldc + n0, ldc, M - m0, N - n0, wm, wn, lane);
+}
+
+template <class C, bool BF>
+hipError_t launch_classic_pp_t(const ClassicLaunch& L, hipStream_t st)
+{
+    const int gy = (L.M + C::BM - 1) / C::BM, gx = (L.N + C::BN - 1) / C::BN;
+    const long tiles = (long)gy * gx;
+    if (tiles == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((k_classic_pp<C, BF>), dim3((unsigned)tiles), dim3(C::NT), 0, st,
+                       (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, (u16*)L.C, L.ldc, L.M, L.N, L.K,
+                       gy, gx, L.P, L.vec4);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ fused group kernel
 
 template <int LEVELS>
@@ -564,13 +838,82 @@ __device__ __forceinline__ void combine_h(const int8_t* w, const typename C::acc
     }
 }
 
+// Writes a group's output blocks.  A split piece first publishes its fp32
+// partial; the second piece to arrive (agent-scope acquire/release through a
+// per-slot counter) adds the other partial, writes C and resets the counter.
+// fp32 addition commutes, so the result does not depend on arrival order.
+template <int NOUT, class C, bool CBF>
+__device__ __forceinline__ void fused_epilogue(const FusedParams& fp, const Item& item, int m0, int n0,
+                                               typename C::acc_t (&Cacc)[NOUT][C::FM][C::FN], int tid, int wm,
+                                               int wn, int lane, int* sh_old)
+{
+    constexpr int S = NOUT == 4 ? 2 : 4;
+    constexpr int G4 = C::NACC / 4;                     // float4 groups per accumulator tile
+    constexpr int PART_F4 = NOUT * C::FM * C::FN * G4;  // float4 per thread in a partial
+    bool store = true;
+    if (item.slot >= 0) {
+        const int which = item.pos0 == 0 ? 0 : 1;
+        f32x4* mine = reinterpret_cast<f32x4*>(fp.partial) + ((int64_t)item.slot * 2 + which) * PART_F4 * C::NT;
+        const f32x4* other = reinterpret_cast<const f32x4*>(fp.partial) + ((int64_t)item.slot * 2 + (1 - which)) * PART_F4 * C::NT;
+#pragma unroll
+        for (int o = 0; o < NOUT; ++o)
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                    for (int g = 0; g < G4; ++g) {
+                        const int e = ((o * C::FM + i) * C::FN + j) * G4 + g;
+                        mine[(int64_t)e * C::NT + tid] =
+                            f32x4{Cacc[o][i][j][4 * g], Cacc[o][i][j][4 * g + 1],
+                                  Cacc[o][i][j][4 * g + 2], Cacc[o][i][j][4 * g + 3]};
+                    }
+        __threadfence();
+        __syncthreads();
+        if (tid == 0)
+            *sh_old = __hip_atomic_fetch_add(fp.counters + item.slot, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        store = *sh_old == 1;
+        if (store) {
+            __threadfence();
+#pragma unroll
+            for (int o = 0; o < NOUT; ++o) {
+                // One output block at a time keeps the partial loads from all
+                // being hoisted ahead of the adds.
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                        for (int g = 0; g < G4; ++g) {
+                            const int e = ((o * C::FM + i) * C::FN + j) * G4 + g;
+                            const f32x4 v = __builtin_nontemporal_load(other + (int64_t)e * C::NT + tid);
+                            Cacc[o][i][j][4 * g] += v.x;
+                            Cacc[o][i][j][4 * g + 1] += v.y;
+                            Cacc[o][i][j][4 * g + 2] += v.z;
+                            Cacc[o][i][j][4 * g + 3] += v.w;
+                        }
+            }
+            if (tid == 0)
+                __hip_atomic_store(fp.counters + item.slot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (store) {
+#pragma unroll
+        for (int o = 0; o < NOUT; ++o) {
+            const int bi = o / S, bj = o % S;
+            store_c<C, CBF, true>(Cacc[o], fp.C + (int64_t)(bi * fp.Mb + m0) * fp.ldc + bj * fp.Nb + n0, fp.ldc,
+                                  fp.Mb - m0, fp.Nb - n0, wm, wn, lane);
+        }
+    }
+}
+
 template <int LEVELS, bool OBF, bool CBF>
 __global__ void __launch_bounds__(FusedCfg<LEVELS>::C::NT) k_fused(const FusedParams fp)
 {
     using C = typename FusedCfg<LEVELS>::C;
     constexpr int S = Scheme<LEVELS>::S, NOUT = S * S;
-    constexpr int G4 = C::NACC / 4;                     // float4 groups per accumulator tile
-    constexpr int PART_F4 = NOUT * C::FM * C::FN * G4;  // float4 per thread in a partial
     __shared__ __attribute__((aligned(16))) char smem[C::LDS];
     __shared__ int sh_old;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -603,86 +946,94 @@ __global__ void __launch_bounds__(FusedCfg<LEVELS>::C::NT) k_fused(const FusedPa
         load_tile<C, true>(Rg, nxt, 0, tid);
         store_tile<C>(smem, Rg, tid);
         __syncthreads();
+        // The tile sequence runs through the group's products back to back:
+        // the first tile of the next product is fetched while the last tile
+        // of the current one is computed.
         for (int t = 0; t < ntiles; ++t) {
             const int t1 = t + 1;
+            const char* cur = smem + (t & 1) * C::STAGE;
             if (t1 < ntiles) {
                 const int k1 = t1 % nk;
                 if (k1 == 0)
                     nxt = src_of(item.pos0 + t1 / nk);
                 load_tile<C, true>(Rg, nxt, k1 * C::BK, tid);
+                ktile<C, OBF, true>(cur, smem + (t1 & 1) * C::STAGE, Rg, H, wm, wn, lane, tid);
+            } else {
+                ktile<C, OBF, false>(cur, nullptr, Rg, H, wm, wn, lane, tid);
             }
-            compute_stage<C, OBF>(smem + (t & 1) * C::STAGE, H, wm, wn, lane);
             if (t % nk == nk - 1) {
                 combine_h<NOUT, C>(fp.w[fp.order[item.pos0 + t / nk]], H, Cacc);
                 zero_acc<C>(H);
             }
-            if (t1 < ntiles)
-                store_tile<C>(smem + (t1 & 1) * C::STAGE, Rg, tid);
             __syncthreads();
         }
 
-        bool store = true;
-        if (item.slot >= 0) {
-            // Split group: publish this piece's fp32 partial, then the second
-            // arriver adds the other piece's partial and writes C.
-            const int which = item.pos0 == 0 ? 0 : 1;
-            f32x4* mine = reinterpret_cast<f32x4*>(fp.partial) + ((int64_t)item.slot * 2 + which) * PART_F4 * C::NT;
-            const f32x4* other = reinterpret_cast<const f32x4*>(fp.partial) + ((int64_t)item.slot * 2 + (1 - which)) * PART_F4 * C::NT;
-#pragma unroll
-            for (int o = 0; o < NOUT; ++o)
-#pragma unroll
-                for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-                        for (int g = 0; g < G4; ++g) {
-                            const int e = ((o * C::FM + i) * C::FN + j) * G4 + g;
-                            mine[(int64_t)e * C::NT + tid] =
-                                f32x4{Cacc[o][i][j][4 * g], Cacc[o][i][j][4 * g + 1],
-                                      Cacc[o][i][j][4 * g + 2], Cacc[o][i][j][4 * g + 3]};
-                        }
-            __threadfence();
-            __syncthreads();
-            if (tid == 0)
-                sh_old = __hip_atomic_fetch_add(fp.counters + item.slot, 1, __ATOMIC_ACQ_REL,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-            __syncthreads();
-            store = sh_old == 1;
-            if (store) {
-                __threadfence();
-#pragma unroll
-                for (int o = 0; o < NOUT; ++o) {
-                    // One output block at a time: keeps the compiler from
-                    // hoisting every partial load ahead of the adds.
-                    asm volatile("" ::: "memory");
-#pragma unroll
-                    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-                        for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-                            for (int g = 0; g < G4; ++g) {
-                                const int e = ((o * C::FM + i) * C::FN + j) * G4 + g;
-                                const f32x4 v = __builtin_nontemporal_load(other + (int64_t)e * C::NT + tid);
-                                Cacc[o][i][j][4 * g] += v.x;
-                                Cacc[o][i][j][4 * g + 1] += v.y;
-                                Cacc[o][i][j][4 * g + 2] += v.z;
-                                Cacc[o][i][j][4 * g + 3] += v.w;
-                            }
-                }
-                if (tid == 0)
-                    __hip_atomic_store(fp.counters + item.slot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        if (store) {
-#pragma unroll
-            for (int o = 0; o < NOUT; ++o) {
-                const int bi = o / S, bj = o % S;
-                store_c<C, CBF>(Cacc[o], fp.C + (int64_t)(bi * fp.Mb + m0) * fp.ldc + bj * fp.Nb + n0, fp.ldc,
-                                fp.Mb - m0, fp.Nb - n0, fp.vec4 != 0, wm, wn, lane);
-            }
-        }
+        fused_epilogue<NOUT, C, CBF>(fp, item, m0, n0, Cacc, tid, wm, wn, lane, &sh_old);
         __syncthreads();
     }
+}
+
+// One-level fused group kernel on the ping-pong engine (8 waves, 128 x 128
+// group tile, 64 x 32 per wave): the product tiles of an item run back to
+// back through the DMA ring; after each product's last k-tile every wave folds
+// its H sub-tile into its four output sub-tiles.
+template <bool OBF, bool CBF>
+__global__ void __launch_bounds__(PCF1::NT) k_fused1_pp(const FusedParams fp)
+{
+    using C = PCF1;
+    constexpr int NOUT = 4;
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+    __shared__ int sh_old;
+    const int tid = threadIdx.x, lane0 = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int w = blockIdx.x;
+    const int n_items = sched_count(fp.sp, w);
+    const int nk = (fp.Kb + C::BK - 1) / C::BK;
+    for (int it = 0; it < n_items; ++it) {
+        // Opaque per item: keeps lane-derived addresses from being hoisted out
+        // of the item loop and held in registers across the whole kernel.
+        int lane = lane0;
+        asm volatile("" : "+v"(lane));
+        const Item item = sched_item(fp.sp, w, it);
+        int p, q;
+        tile_coords(item.g, fp.sp.gy, fp.sp.gx, fp.sp.P, fp.sp.raster, &p, &q);
+        const int m0 = p * C::BM, n0 = q * C::BN;
+        f32x16 Cacc[NOUT][C::FM][C::FN];
+#pragma unroll
+        for (int o = 0; o < NOUT; ++o)
+            zero_acc<C>(Cacc[o]);
+        f32x16 H[C::FM][C::FN];
+        zero_acc<C>(H);
+        const int ntiles = (item.pos1 - item.pos0) * nk;
+        auto src = [&](int t) {
+            const int r = fp.order[item.pos0 + t / nk];
+            return pp::TileSrc{fp.a[r] + (int64_t)m0 * fp.lda[r], (int)fp.lda[r], fp.Mb - m0,
+                               fp.b[r] + n0, (int)fp.ldb[r], fp.Nb - n0, (t % nk) * C::BK, fp.Kb};
+        };
+        auto after = [&](int t) {
+            if (t % nk == nk - 1) {
+                combine_h<NOUT, C>(fp.w[fp.order[item.pos0 + t / nk]], H, Cacc);
+                zero_acc<C>(H);
+            }
+        };
+        if (wave < C::NW / 2)
+            pp::run_tiles<C, OBF, true>(smem, ntiles, src, after, wave, wm, wn, lane, H);
+        else
+            pp::run_tiles<C, OBF, false>(smem, ntiles, src, after, wave, wm, wn, lane, H);
+        __syncthreads();
+        fused_epilogue<NOUT, C, CBF>(fp, item, m0, n0, Cacc, tid, wm, wn, lane, &sh_old);
+        __syncthreads();
+    }
+}
+
+template <bool OBF, bool CBF>
+hipError_t launch_fused1_pp(const FusedLaunch& L, hipStream_t st)
+{
+    if (L.grid <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((k_fused1_pp<OBF, CBF>), dim3(L.grid), dim3(PCF1::NT), 0, st, L.p);
+    return hipGetLastError();
 }
 
 template <int LEVELS, bool OBF, bool CBF>
@@ -711,7 +1062,10 @@ void classic_tile_dims(int32_t tile, int32_t* bm, int32_t* bn)
 hipError_t launch_classic(const ClassicLaunch& L, hipStream_t st)
 {
     switch (L.tile) {
-    case kTile256: return launch_classic_c<Cfg256>(L, st);
+    case kTile256:
+        if (L.vec)
+            return L.bf16 ? launch_classic_pp_t<PC256, true>(L, st) : launch_classic_pp_t<PC256, false>(L, st);
+        return launch_classic_c<Cfg256>(L, st);
     case kTile128: return launch_classic_c<Cfg128>(L, st);
     default: return launch_classic_c<Cfg32>(L, st);
     }
@@ -732,16 +1086,15 @@ hipError_t launch_prepass(const PrepassLaunch& L, hipStream_t st)
     return launch_prepass_t<2, false, false, false>(L, st);
 }
 
-int32_t fused_tile(int32_t levels) { return levels == 1 ? FusedCfg<1>::C::BM : FusedCfg<2>::C::BM; }
+int32_t fused_tile(int32_t levels) { return levels == 1 ? PCF1::BM : FusedCfg<2>::C::BM; }
+static_assert(PCF1::BM == PCF1::BN, "fused tiles are square");
 static_assert(FusedCfg<1>::C::BM == FusedCfg<1>::C::BN && FusedCfg<2>::C::BM == FusedCfg<2>::C::BN,
               "fused tiles are square");
 
 int64_t fused_partial_bytes(int32_t levels)
 {
-    if (levels == 1) {
-        using C = FusedCfg<1>::C;
-        return (int64_t)4 * C::BM * C::BN * 4;
-    }
+    if (levels == 1)
+        return (int64_t)4 * PCF1::BM * PCF1::BN * 4;
     using C = FusedCfg<2>::C;
     return (int64_t)16 * C::BM * C::BN * 4;
 }
@@ -765,8 +1118,8 @@ hipError_t launch_fused(const FusedLaunch& L, hipStream_t st)
 {
     if (L.levels == 1) {
         if (L.out_bf16)
-            return L.op_bf16 ? launch_fused_t<1, true, true>(L, st) : launch_fused_t<1, false, true>(L, st);
-        return launch_fused_t<1, false, false>(L, st);
+            return L.op_bf16 ? launch_fused1_pp<true, true>(L, st) : launch_fused1_pp<false, true>(L, st);
+        return launch_fused1_pp<false, false>(L, st);
     }
     if (L.out_bf16)
         return L.op_bf16 ? launch_fused_t<2, true, true>(L, st) : launch_fused_t<2, false, true>(L, st);
