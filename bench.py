@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--only", default="", help="time only these algorithms (comma list), for profiling runs")
+    ap.add_argument("--size", type=int, default=0,
+                    help="time the algorithms on an n^3 bfloat16 product instead of the 4096^3 workload "
+                         "(detail only; the headline workload is fixed)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="first run 3 device copies of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -70,7 +73,9 @@ def main():
     import complexity_half_precision_amd as L
     import seeded_inputs as si
 
-    wl = si.SQUARE_4096_BF16
+    wl = dict(si.SQUARE_4096_BF16)
+    if args.size:
+        wl.update(M=args.size, N=args.size, K=args.size)
     M, N, K, dtype = wl["M"], wl["N"], wl["K"], wl["dtype"]
     dev = "cuda"
     A, B = si.gen(**wl)
@@ -191,7 +196,7 @@ def main():
         "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "square GEMM M=N=K=4096, bf16 A,B ~ N(0,1)/sqrt(K), fp32 accumulate, bf16 out",
+        "config": {"workload": f"square GEMM M=N=K={M}, bf16 A,B ~ N(0,1)/sqrt(K), fp32 accumulate, bf16 out",
                    "M": M, "N": N, "K": K, "algo_chosen": chosen},
         "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2),
         "roofline": roofline,

@@ -44,7 +44,8 @@ class lcma_desc(ctypes.Structure):
 
 class lcma_options(ctypes.Structure):
     _fields_ = [("split", _i32), ("combine", _i32), ("bf16_ops_f16", _i32), ("num_cus", _i32),
-                ("peak_tflops", ctypes.c_double), ("hbm_gbps", ctypes.c_double)]
+                ("peak_tflops", ctypes.c_double), ("hbm_gbps", ctypes.c_double),
+                ("classic_eff", ctypes.c_double), ("fused_eff", ctypes.c_double)]
 
 
 def _sig(name, res, args):
@@ -177,10 +178,11 @@ class Plan:
 
 
 def lcma_plan_ex(M, N, K, dtype, desc: Desc | None = None, force="auto", split="auto", combine="auto",
-                 bf16_ops_f16=0, num_cus=0, peak_tflops=0.0, hbm_gbps=0.0) -> Plan:
+                 bf16_ops_f16=0, num_cus=0, peak_tflops=0.0, hbm_gbps=0.0, classic_eff=0.0,
+                 fused_eff=0.0) -> Plan:
     opts = lcma_options(_SPLIT[split] if isinstance(split, str) else split,
                         _COMBINE[combine] if isinstance(combine, str) else combine,
-                        bf16_ops_f16, num_cus, peak_tflops, hbm_gbps)
+                        bf16_ops_f16, num_cus, peak_tflops, hbm_gbps, classic_eff, fused_eff)
     h = _vp()
     st = _lib_plan_ex(M, N, K, _dt(dtype), ctypes.byref(desc.c) if desc is not None else None,
                       _ALGO[force] if isinstance(force, str) else force, ctypes.byref(opts), ctypes.byref(h))

@@ -135,6 +135,9 @@ bool log_enabled()
 //          max( F / (eta_F * peak * q),  B_hbm / (eta_B * bw),  F / (I_tile * bw_L2 * q) )
 //          + t_launch
 // F: MFMA flops of the kernel; B_hbm: the bytes it must move at least;
+// eta_F: the fraction of the MFMA peak the kernel sustains when compute-bound,
+// measured per kernel (the classic kernel and the fused kernel at each level
+// differ a lot, so one shared factor would misrank them);
 // I_tile: flops per byte a workgroup tile draws from L2 (BM*BN/(BM+BN) for a
 // BM x BN tile); q: wave-quantisation efficiency = (work units / P) /
 // (rounds actually needed).  The first two terms are the roofline of the
@@ -143,7 +146,7 @@ bool log_enabled()
 
 struct Machine {
     double peak, bw, l2bw, launch;
-    double eta_mfma, eta_fused, eta_bw;
+    double eta_mfma, eta_fused1, eta_fused2, eta_bw;
     int P;
 };
 
@@ -254,7 +257,7 @@ double est_lcma(int64_t M, int64_t N, int64_t K, int levels, int split_req, bool
     } else {
         q = quant(g.G, m.P);
     }
-    const double t_f = kernel_time(F, Bf, g.tile / 2.0, q, m.eta_fused, m);
+    const double t_f = kernel_time(F, Bf, g.tile / 2.0, q, levels == 1 ? m.eta_fused1 : m.eta_fused2, m);
     return t_pre + t_f;
 }
 
@@ -339,7 +342,8 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         o = *opts;
     if (o.split < LCMA_SPLIT_AUTO || o.split > LCMA_SPLIT_ALL || o.combine < LCMA_COMBINE_AUTO ||
         o.combine > LCMA_COMBINE_AT_LOAD || o.num_cus < 0 || o.peak_tflops < 0 || o.hbm_gbps < 0 ||
-        o.bf16_ops_f16 < -1 || o.bf16_ops_f16 > 1)
+        o.bf16_ops_f16 < -1 || o.bf16_ops_f16 > 1 || !(o.classic_eff >= 0 && o.classic_eff <= 1) ||
+        !(o.fused_eff >= 0 && o.fused_eff <= 1))
         return LCMA_E_INVALID;
 
     // Which LCMA levels the description allows.
@@ -359,8 +363,13 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     m.bw = (o.hbm_gbps > 0 ? o.hbm_gbps : 8000.0) * 1e9;
     m.l2bw = 8.0 * 2048.0 * 2.4e9;
     m.launch = 4e-6;
-    m.eta_mfma = 0.75;
-    m.eta_fused = 0.75;
+    // Sustained fractions of the MFMA peak measured on MI355X (256 CUs) for
+    // the kernels as they stand: classic 256x256 tile 0.41-0.45 over
+    // 4096^3..16384^3; fused one-level group kernel 0.145-0.17; fused
+    // two-level kernel about 0.03.
+    m.eta_mfma = o.classic_eff > 0 ? o.classic_eff : 0.43;
+    m.eta_fused1 = o.fused_eff > 0 ? o.fused_eff : 0.155;
+    m.eta_fused2 = o.fused_eff > 0 ? o.fused_eff : 0.032;
     m.eta_bw = 0.8;
     if (o.num_cus > 0) {
         m.P = o.num_cus;

@@ -158,12 +158,29 @@ def test_auto_never_picks_two_levels_for_binary16_inputs():
         assert L.lcma_plan_info(p)[0] != "l2"
 
 
-def test_lower_peak_makes_lcma_attractive_only_when_compute_bound():
-    # With a much lower MFMA peak the ridge drops and big squares become compute-bound enough for LCMA.
-    p = L.lcma_plan_ex(16384, 16384, 16384, "bf16", num_cus=CUS, peak_tflops=200.0)
+def test_efficient_fused_kernel_makes_lcma_attractive_only_when_compute_bound():
+    # With a fused kernel as efficient as the classic one, the 1/8 fewer
+    # multiplications win on big squares but never on memory-bound shapes.
+    p = L.lcma_plan_ex(16384, 16384, 16384, "bf16", num_cus=CUS, classic_eff=0.45, fused_eff=0.45)
     assert L.lcma_plan_info(p)[0] in ("l1", "l2")
-    p = L.lcma_plan_ex(1, 14336, 4096, "bf16", num_cus=CUS, peak_tflops=200.0)
+    p = L.lcma_plan_ex(1, 14336, 4096, "bf16", num_cus=CUS, classic_eff=0.45, fused_eff=0.45)
     assert L.lcma_plan_info(p)[0] == "classic"
+    # with a lower MFMA peak the ridge drops, and the same holds
+    p = L.lcma_plan_ex(16384, 16384, 16384, "bf16", num_cus=CUS, peak_tflops=200.0, fused_eff=0.43)
+    assert L.lcma_plan_info(p)[0] in ("l1", "l2")
+
+
+def test_measured_efficiencies_pick_classic_on_big_squares():
+    # the fused kernels as they stand sustain a much lower fraction of peak
+    for n in (4096, 8192, 16384):
+        p = L.lcma_plan_ex(n, n, n, "bf16", num_cus=CUS)
+        assert L.lcma_plan_info(p)[0] == "classic", n
+
+
+def test_efficiency_options_are_validated():
+    for kw in ({"classic_eff": -0.1}, {"classic_eff": 1.5}, {"fused_eff": 2.0}, {"fused_eff": float("nan")}):
+        with pytest.raises(L.LcmaError):
+            L.lcma_plan_ex(512, 512, 512, "f16", num_cus=CUS, **kw)
 
 
 def test_workspace_layout_of_one_level_plan():
