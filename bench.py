@@ -178,7 +178,7 @@ def main():
     if chosen == "classic":
         t_k = detail["classic"]["ms"]
         achieved = flops / (t_k * 1e-3) / 1e12
-        kname, kprefix = "k_classic_pp (256x256 tile, 2MNK flops per launch)", "k_classic_pp"
+        kname, kprefix = "k_classic_q4 (256x256 tile, 2MNK flops per launch)", "k_classic_q4"
     else:
         t_k = detail[chosen]["fused_ms"]
         achieved = detail[chosen]["fused_mfma_tflop"] * 1e12 / (t_k * 1e-3) / 1e12

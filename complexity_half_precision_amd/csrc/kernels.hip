@@ -762,12 +762,305 @@ __device__ __forceinline__ void run_tiles(char* smem, int ntiles, SrcFn src, Aft
 
 }  // namespace pp
 
-using PC256 = pp::PCfg<256, 256, 2, 4>;    // classic: 8 waves of 128 x 64
 using PCF1 = pp::PCfg<128, 128, 2, 4>;     // fused one-level: 8 waves of 64 x 32
 
+
+// ------------------------------------------------------------------ four-wave engine
+//
+// One wave per SIMD, each owning a 128 x 128 output tile (16 MFMA tiles,
+// 256 accumulator registers): per byte read from LDS this does 1.5x the
+// MFMA work of a 128 x 64 wave tile.  k-tiles of 32 stream through a
+// 4-stage LDS ring by direct-to-LDS loads issued 3 tiles ahead; fragments
+// are double-buffered in registers by k-step, so the LDS reads of one k-step
+// run under the MFMAs of the other.  One barrier per k-tile.
+
+namespace q4 {
+
+template <int BM_, int BN_>
+struct QCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = 32, WM = 2, WN = 2, MT = 32;
+    static constexpr int NSTAGE = 4, KSTEPS = 2, AHEAD = 3;
+    static constexpr int NW = WM * WN;
+    static constexpr int NT = NW * 64;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int FM = WTM / 32, FN = WTN / 32;
+    using acc_t = f32x16;
+    static constexpr int NACC = 16;
+    static constexpr int AROW = BK * 2;
+    static constexpr int BROW = BN * 2;
+    static constexpr int A_BYTES = BM * AROW;
+    static constexpr int B_BYTES = BK * BROW;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int LDS = NSTAGE * STAGE;
+    static constexpr int LOADERS = NW;
+    static constexpr int A_PER = A_BYTES / 1024 / LOADERS;
+    static constexpr int B_PER = B_BYTES / 1024 / LOADERS;
+    static constexpr int PER = A_PER + B_PER;                // DMA instructions per wave per k-tile
+    static_assert(A_BYTES % (1024 * LOADERS) == 0 && B_BYTES % (1024 * LOADERS) == 0, "DMA split");
+    static_assert(BROW % 256 == 0 && FM >= 1 && FN >= 1, "tile shape");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(PER * (AHEAD - 1) < 64, "outstanding DMA count fits the 6-bit vmcnt");
+};
+
+// Fragments of one k-step (16 k) of a wave tile.
+template <class C>
+struct Step {
+    u32x4 a[C::FM];
+    u32x4 b[C::FN];
+};
+
 template <class C, bool BF>
-__global__ void __launch_bounds__(C::NT)
-k_classic_pp(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb, u16* __restrict__ Cm,
+__device__ __forceinline__ void mma_step(const Step<C>& F, f32x16 (&acc)[C::FM][C::FN])
+{
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+            acc[i][j] = mfma<BF>(F.b[j], F.a[i], acc[i][j]);
+}
+
+// Buffer descriptor words (base, no stride, 2^31 - 1 bytes, raw dwords),
+// matching make_rsrc.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base)
+{
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return u32x4{(u32)a, (u32)(a >> 32) & 0xffffu, 0x7fffffffu, 0x00020000u};
+}
+
+__device__ __forceinline__ u32 lds_addr(const void* p)
+{
+    return (u32)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+
+// One direct-to-LDS load of 16 bytes per lane: buffer bytes at `off` go to
+// LDS address lds + 16 * lane.  Written as inline assembly so the compiler
+// does not treat it as a possible writer of every later LDS read (it would
+// otherwise drain vmcnt before each transposed read); the kernels order these
+// loads against LDS reads themselves with vmcnt waits and barriers.  The
+// LDS address goes in M0, which must be written one instruction ahead of
+// the load.
+__device__ __forceinline__ void dma16(u32x4 rs, u32 off, u32 lds)
+{
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(off), "s"(rs), "{m0}"(lds)
+                 : "memory");
+}
+
+// Instruction i (0 .. PER-1) of wave xw's share of a k-tile DMA: the first
+// A_PER move A rows, the rest B rows (same layout as pp::dma_tile).
+template <class C, bool EDGE>
+__device__ __forceinline__ void dma_one(char* stage, const pp::TileSrc& s, int xw, int lane, int i)
+{
+    const int kleft = s.K - s.k0;
+    const u32 base = lds_addr(stage);
+    if (i < C::A_PER) {
+        const int ins = xw * C::A_PER + i;
+        const int r = ins * 16 + (lane >> 2);
+        const int k = ((lane & 3) ^ (int)pp::a_swz(r)) * 8;
+        const u32 off0 = (u32)(r * s.lda + k) * 2u;
+        const u32 off = !EDGE || ((r < s.a_rows) & (k < kleft)) ? off0 : kOob;
+        dma16(rsrc_words(s.a + s.k0), off, base + ins * 1024);
+    } else {
+        const int ins = xw * C::B_PER + (i - C::A_PER);
+        const int byte = ins * 1024 + lane * 16;
+        const int r = byte / C::BROW;
+        const int n = (((byte % C::BROW) >> 4) ^ (int)pp::b_swz(r)) * 8;
+        const u32 off0 = (u32)(r * s.ldb + n) * 2u;
+        const u32 off = !EDGE || ((r < kleft) & (n < s.b_cols)) ? off0 : kOob;
+        dma16(rsrc_words(s.b + (int64_t)s.k0 * s.ldb), off, base + C::A_BYTES + ins * 1024);
+    }
+}
+
+// DMA of wave xw's share of one k-tile into `stage`.
+template <class C, bool EDGE>
+__device__ __forceinline__ void dma_tile(char* stage, const pp::TileSrc& s, int xw, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < C::PER; ++i)
+        dma_one<C, EDGE>(stage, s, xw, lane, i);
+}
+
+// s_waitcnt vmcnt(N): vmcnt is split over bits 3:0 and 15:14; expcnt and
+// lgkmcnt at their maxima (no wait).
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Wait until at most n k-tiles of this wave's loads are in flight
+// (0 <= n < AHEAD; n < 0 waits for all).
+template <class C>
+__device__ __forceinline__ void wait_tiles(int n)
+{
+    static_assert(C::AHEAD <= 4, "cases below");
+    if (n >= 3)
+        wait_vm<3 * C::PER>();
+    else if (n == 2)
+        wait_vm<2 * C::PER>();
+    else if (n == 1)
+        wait_vm<C::PER>();
+    else
+        pp::wait_vm0();
+}
+
+
+// Single LDS reads of a k-step's fragments, so they can be slotted between
+// MFMAs: A fragment i (one 16-byte read) and half h of B fragment j (one
+// transposed 8-byte read; h = 0 covers k 0..7 of the step, h = 1 k 8..15).
+template <class C>
+struct Addr {
+    u32 a0;     // A byte offset of fragment 0 at k-step 0
+    u32 b[C::FN];
+};
+
+template <class C>
+__device__ __forceinline__ Addr<C> frag_addr(int wm, int wn, int lane)
+{
+    Addr<C> ad;
+    const u32 m = wm * C::WTM + (lane & 31);
+    const u32 f = pp::a_swz(m);
+    ad.a0 = m * (u32)C::AROW + ((((lane >> 5) ^ f) & 1u) << 4) + ((f & 2u) << 4);
+    const int g = lane >> 4, s = lane & 15;
+    const u32 kr = 8 * (g >> 1) + (s >> 2);
+    const u32 xb = pp::b_swz(kr);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+        const u32 n = wn * C::WTN + j * 32 + 16 * (g & 1) + 4 * (s & 3);
+        ad.b[j] = C::A_BYTES + kr * C::BROW + (((n >> 3) ^ xb) << 4) + (n & 7) * 2;
+    }
+    return ad;
+}
+
+// Read number x (0 .. FM + 2 FN - 1) of k-step st from `stage`.
+template <class C>
+__device__ __forceinline__ void read_one(const char* stage, const Addr<C>& ad, int st, int x, Step<C>& F,
+                                         u32x2 (&bh)[C::FN][2])
+{
+    if (x < C::FM) {
+        F.a[x] = *reinterpret_cast<const u32x4*>(stage + (ad.a0 ^ ((u32)st << 5)) + x * 32 * C::AROW);
+    } else {
+        const int y = x - C::FM, j = y >> 1, h = y & 1;
+        const pp::s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) pp::s16x4*)(stage + ad.b[j] + (16 * st + 4 * h) * C::BROW));
+        bh[j][h] = __builtin_bit_cast(u32x2, v);
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void join_b(Step<C>& F, const u32x2 (&bh)[C::FN][2])
+{
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+        F.b[j] = u32x4{bh[j][0].x, bh[j][0].y, bh[j][1].x, bh[j][1].y};
+}
+
+}  // namespace q4
+
+namespace q4 {
+
+// K loop of one output tile through the four-wave engine; k-tile t's
+// operands come from src(t).  Direct-to-LDS loads for tile t+3 are slotted
+// between MFMAs, half in each k-step, into the stage tile t-1 used (free once
+// this tile's barrier has passed).  EDGE applies the row / column / k bounds
+// to the loads; tiles wholly inside the matrices skip them.
+template <class C, bool BF, bool EDGE, class SrcFn>
+__device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, int wave, int lane, const Addr<C>& ad,
+                                         f32x16 (&acc)[C::FM][C::FN])
+{
+    constexpr int NMF = C::FM * C::FN;
+    constexpr int NRD = C::FM + 2 * C::FN;          // LDS reads per k-step
+    constexpr int RPS = 3;                          // reads slotted after one MFMA
+    constexpr int HALF = C::PER / 2;                // loads slotted per k-step
+    constexpr int LSLOT = NRD / RPS + 1;            // first load slot; loads every other MFMA
+    static_assert(NRD % RPS == 0 && C::PER % 2 == 0 && LSLOT + 2 * (HALF - 1) < NMF, "interleave slots");
+    static_assert(C::AHEAD == 3 && C::NSTAGE == 4, "stage reuse below assumes a 4-stage ring, 3 ahead");
+    Step<C> F0, F1;
+    u32x2 bh[C::FN][2];
+#pragma unroll
+    for (int t = 0; t < C::AHEAD; ++t)
+        if (t < nk)
+            dma_tile<C, EDGE>(smem + t * C::STAGE, src(t), wave, lane);
+    wait_tiles<C>(min(nk, C::AHEAD) - 1);
+    pp::bar();
+    if (nk > 0) {
+#pragma unroll
+        for (int x = 0; x < NRD; ++x)
+            read_one<C>(smem, ad, 0, x, F0, bh);
+        join_b<C>(F0, bh);
+    }
+    int t = 0;
+    // Steady state: every k-tile has a successor and a tile to prefetch.
+    for (; t + C::AHEAD < nk; ++t) {
+        const char* cur = smem + (t % C::NSTAGE) * C::STAGE;
+        const char* nxt = smem + ((t + 1) % C::NSTAGE) * C::STAGE;
+        char* pre = smem + ((t + C::AHEAD) % C::NSTAGE) * C::STAGE;
+        const pp::TileSrc ps = src(t + C::AHEAD);
+        // k-step 0 MFMAs; k-step 1 reads and the first half of the prefetch
+#pragma unroll
+        for (int x = 0; x < NMF; ++x) {
+            acc[x / C::FN][x % C::FN] = mfma<BF>(F0.b[x % C::FN], F0.a[x / C::FN], acc[x / C::FN][x % C::FN]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (x < NRD / RPS) {
+#pragma unroll
+                for (int r = 0; r < RPS; ++r)
+                    read_one<C>(cur, ad, 1, x * RPS + r, F1, bh);
+            } else if (x >= LSLOT && ((x - LSLOT) & 1) == 0 && (x - LSLOT) / 2 < HALF) {
+                dma_one<C, EDGE>(pre, ps, wave, lane, (x - LSLOT) / 2);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        join_b<C>(F1, bh);
+        wait_vm<C::PER>();      // tile t+1 landed (at most one tile's loads in flight)
+        pp::wait_lgkm0();       // k-step 1 fragments are in registers
+        pp::bar();
+        __builtin_amdgcn_sched_barrier(0);
+        // k-step 1 MFMAs; next tile's k-step 0 reads and the second half of the prefetch
+#pragma unroll
+        for (int x = 0; x < NMF; ++x) {
+            acc[x / C::FN][x % C::FN] = mfma<BF>(F1.b[x % C::FN], F1.a[x / C::FN], acc[x / C::FN][x % C::FN]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (x < NRD / RPS) {
+#pragma unroll
+                for (int r = 0; r < RPS; ++r)
+                    read_one<C>(nxt, ad, 0, x * RPS + r, F0, bh);
+            } else if (x >= LSLOT && ((x - LSLOT) & 1) == 0 && (x - LSLOT) / 2 < HALF) {
+                dma_one<C, EDGE>(pre, ps, wave, lane, HALF + (x - LSLOT) / 2);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        join_b<C>(F0, bh);
+    }
+    // Last AHEAD k-tiles: nothing left to prefetch.
+    for (; t < nk; ++t) {
+        const char* cur = smem + (t % C::NSTAGE) * C::STAGE;
+#pragma unroll
+        for (int x = 0; x < NRD; ++x)
+            read_one<C>(cur, ad, 1, x, F1, bh);
+        join_b<C>(F1, bh);
+        mma_step<C, BF>(F0, acc);
+        if (t + 1 < nk) {
+            wait_tiles<C>(nk - 2 - t);
+            pp::wait_lgkm0();
+            pp::bar();
+#pragma unroll
+            for (int x = 0; x < NRD; ++x)
+                read_one<C>(smem + ((t + 1) % C::NSTAGE) * C::STAGE, ad, 0, x, F0, bh);
+            join_b<C>(F0, bh);
+        }
+        mma_step<C, BF>(F1, acc);
+    }
+}
+
+}  // namespace q4
+
+using QC256 = q4::QCfg<256, 256>;
+
+template <class C, bool BF>
+__global__ void __launch_bounds__(C::NT, 1)
+k_classic_q4(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb, u16* __restrict__ Cm,
              int64_t ldc, int M, int N, int K, int gy, int gx, int P, int vec4)
 {
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
@@ -785,11 +1078,12 @@ k_classic_pp(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, 
     auto src = [&](int t) {
         return pp::TileSrc{Ab, (int)lda, M - m0, Bb, (int)ldb, N - n0, t * C::BK, K};
     };
-    auto after = [](int) {};
-    if (wave < C::NW / 2)
-        pp::run_tiles<C, BF, true>(smem, nk, src, after, wave, wm, wn, lane, acc);
+    const q4::Addr<C> ad = q4::frag_addr<C>(wm, wn, lane);
+    const bool inside = (m0 + C::BM <= M) & (n0 + C::BN <= N) & (K % C::BK == 0);
+    if (inside)
+        q4::run_tile<C, BF, false>(smem, nk, src, wave, lane, ad, acc);
     else
-        pp::run_tiles<C, BF, false>(smem, nk, src, after, wave, wm, wn, lane, acc);
+        q4::run_tile<C, BF, true>(smem, nk, src, wave, lane, ad, acc);
     if (vec4)
         store_c<C, BF, true>(acc, Cm + (int64_t)m0 * ldc + n0, ldc, M - m0, N - n0, wm, wn, lane);
     else
@@ -797,13 +1091,13 @@ k_classic_pp(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, 
 }
 
 template <class C, bool BF>
-hipError_t launch_classic_pp_t(const ClassicLaunch& L, hipStream_t st)
+hipError_t launch_classic_q4_t(const ClassicLaunch& L, hipStream_t st)
 {
     const int gy = (L.M + C::BM - 1) / C::BM, gx = (L.N + C::BN - 1) / C::BN;
     const long tiles = (long)gy * gx;
     if (tiles == 0)
         return hipSuccess;
-    hipLaunchKernelGGL((k_classic_pp<C, BF>), dim3((unsigned)tiles), dim3(C::NT), 0, st,
+    hipLaunchKernelGGL((k_classic_q4<C, BF>), dim3((unsigned)tiles), dim3(C::NT), 0, st,
                        (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, (u16*)L.C, L.ldc, L.M, L.N, L.K,
                        gy, gx, L.P, L.vec4);
     return hipGetLastError();
@@ -1064,7 +1358,7 @@ hipError_t launch_classic(const ClassicLaunch& L, hipStream_t st)
     switch (L.tile) {
     case kTile256:
         if (L.vec)
-            return L.bf16 ? launch_classic_pp_t<PC256, true>(L, st) : launch_classic_pp_t<PC256, false>(L, st);
+            return L.bf16 ? launch_classic_q4_t<QC256, true>(L, st) : launch_classic_q4_t<QC256, false>(L, st);
         return launch_classic_c<Cfg256>(L, st);
     case kTile128: return launch_classic_c<Cfg128>(L, st);
     default: return launch_classic_c<Cfg32>(L, st);
