@@ -1103,6 +1103,192 @@ hipError_t launch_classic_q4_t(const ClassicLaunch& L, hipStream_t st)
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ skinny products
+//
+// M <= 64 (decode-shaped products): the run time is streaming B once from
+// HBM, so the kernel is built for bytes in flight rather than MFMA rate.
+// One workgroup per 64-column strip of B; each of its 4 waves takes every
+// 4th k-tile of 32 through a private 5-stage direct-to-LDS ring (no
+// workgroup barrier inside the K loop: a wave only reads what it loaded),
+// which keeps 4 k-tiles per wave, 128 KB per compute unit, in flight.  The
+// rows of A (padded to 32 or 64 with zeros) ride along in each k-tile.  The
+// four partial tiles are summed through LDS in a fixed order at the end.
+
+namespace sk {
+
+template <int BM_>
+struct SCfg {
+    static constexpr int BM = BM_, BN = 64, BK = 32, MT = 32, NW = 4, NT = 256;
+    static constexpr int WM = 1, WN = 1, WTM = BM, WTN = BN;    // each wave covers the whole tile
+    static constexpr int FM = BM / 32, FN = BN / 32;
+    using acc_t = f32x16;
+    static constexpr int NACC = 16;
+    static constexpr int NSTAGE = 5, AHEAD = 4;
+    static constexpr int AROW = BK * 2, BROW = BN * 2;
+    static constexpr int A_BYTES = BM * AROW, B_BYTES = BK * BROW;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int RING = NSTAGE * STAGE;                  // per wave
+    static constexpr int LDS = NW * RING;
+    static constexpr int A_PER = A_BYTES / 1024, B_PER = B_BYTES / 1024, PER = A_PER + B_PER;
+    static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "DMA granularity");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(PER * (AHEAD - 1) < 64, "vmcnt range");
+    static_assert(NW * FM * FN * NACC * 64 * 4 <= LDS, "partials fit in the ring");
+};
+
+// One wave's loads of k-tile k0 into `stage` (rows / columns / k beyond the
+// operands read as zero).
+template <class C>
+__device__ __forceinline__ void dma_ktile(char* stage, const pp::TileSrc& s, int lane)
+{
+    const u32x4 ra = q4::rsrc_words(s.a + s.k0);
+    const u32x4 rb = q4::rsrc_words(s.b + (int64_t)s.k0 * s.ldb);
+    const int kleft = s.K - s.k0;
+    const u32 base = q4::lds_addr(stage);
+#pragma unroll
+    for (int i = 0; i < C::A_PER; ++i) {
+        const int r = i * 16 + (lane >> 2);
+        const int k = ((lane & 3) ^ (int)pp::a_swz(r)) * 8;
+        const u32 off = ((r < s.a_rows) & (k < kleft)) ? (u32)(r * s.lda + k) * 2u : kOob;
+        q4::dma16(ra, off, base + i * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_PER; ++i) {
+        const int byte = i * 1024 + lane * 16;
+        const int r = byte / C::BROW;
+        const int n = ((byte % C::BROW) >> 4) * 8;
+        const u32 off = ((r < kleft) & (n < s.b_cols)) ? (u32)(r * s.ldb + n) * 2u : kOob;
+        q4::dma16(rb, off, base + C::A_BYTES + i * 1024);
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void wait_tiles(int n)
+{
+    static_assert(C::AHEAD <= 4, "cases below");
+    if (n >= 3)
+        q4::wait_vm<3 * C::PER>();
+    else if (n == 2)
+        q4::wait_vm<2 * C::PER>();
+    else if (n == 1)
+        q4::wait_vm<C::PER>();
+    else
+        pp::wait_vm0();
+}
+
+// All fragments of one k-tile (2 k-steps) and their MFMAs.
+template <class C, bool BF>
+__device__ __forceinline__ void ktile(const char* stage, int lane, f32x16 (&acc)[C::FM][C::FN])
+{
+    const char* sA = stage;
+    const char* sB = stage + C::A_BYTES;
+    const u32 m = lane & 31;
+    const u32 f = pp::a_swz(m);
+    const u32 abase = m * (u32)C::AROW + ((((lane >> 5) ^ f) & 1u) << 4) + ((f & 2u) << 4);
+    const int g = lane >> 4, s = lane & 15;
+    const u32 kr = 8 * (g >> 1) + (s >> 2);
+    u32x4 a[2][C::FM], b[2][C::FN];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+            a[st][i] = *reinterpret_cast<const u32x4*>(sA + (abase ^ ((u32)st << 5)) + i * 32 * C::AROW);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+            const u32 n = j * 32 + 16 * (g & 1) + 4 * (s & 3);
+            const u32 boff = (kr + 16 * st) * C::BROW + n * 2;
+            const pp::s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) pp::s16x4*)(sB + boff));
+            const pp::s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) pp::s16x4*)(sB + boff + 4 * C::BROW));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            b[st][j] = u32x4{l2.x, l2.y, h2.x, h2.y};
+        }
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                acc[i][j] = mfma<BF>(b[st][j], a[st][i], acc[i][j]);
+}
+
+}  // namespace sk
+
+template <class C, bool BF>
+__global__ void __launch_bounds__(C::NT, 1)
+k_skinny(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb, u16* __restrict__ Cm,
+         int64_t ldc, int M, int N, int K, int vec4)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n0 = blockIdx.x * C::BN;
+    const u16* Bb = B + n0;
+    char* ring = smem + wave * C::RING;
+    const int nk = (K + C::BK - 1) / C::BK;
+    const int nu = nk > wave ? (nk - wave + C::NW - 1) / C::NW : 0;    // k-tiles of this wave
+    auto src = [&](int u) {
+        return pp::TileSrc{A, (int)lda, M, Bb, (int)ldb, N - n0, (wave + u * C::NW) * C::BK, K};
+    };
+    f32x16 acc[C::FM][C::FN];
+    zero_acc<C>(acc);
+#pragma unroll
+    for (int u = 0; u < C::AHEAD; ++u)
+        if (u < nu)
+            sk::dma_ktile<C>(ring + u * C::STAGE, src(u), lane);
+    for (int u = 0; u < nu; ++u) {
+        sk::wait_tiles<C>(min(nu - 1 - u, C::AHEAD - 1));   // tile u landed
+        sk::ktile<C, BF>(ring + (u % C::NSTAGE) * C::STAGE, lane, acc);
+        // tile u-1's stage is free: its fragments were consumed by the MFMAs above
+        if (u + C::AHEAD < nu) {
+            pp::wait_lgkm0();
+            sk::dma_ktile<C>(ring + ((u + C::AHEAD) % C::NSTAGE) * C::STAGE, src(u + C::AHEAD), lane);
+        }
+    }
+    // Sum the four waves' partial tiles in a fixed order through LDS.
+    pp::wait_vm0();
+    __syncthreads();
+    float* part = reinterpret_cast<float*>(smem);
+    if (wave > 0) {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                for (int e = 0; e < C::NACC; ++e)
+                    part[((((wave - 1) * C::FM + i) * C::FN + j) * C::NACC + e) * 64 + lane] = acc[i][j][e];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int w = 0; w < C::NW - 1; ++w)
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                    for (int e = 0; e < C::NACC; ++e)
+                        acc[i][j][e] += part[(((w * C::FM + i) * C::FN + j) * C::NACC + e) * 64 + lane];
+        if (vec4)
+            store_c<C, BF, true>(acc, Cm + n0, ldc, M, N - n0, 0, 0, lane);
+        else
+            store_c<C, BF, false>(acc, Cm + n0, ldc, M, N - n0, 0, 0, lane);
+    }
+}
+
+template <class C, bool BF>
+hipError_t launch_skinny_t(const ClassicLaunch& L, hipStream_t st)
+{
+    const int gx = (L.N + C::BN - 1) / C::BN;
+    if (gx == 0 || L.M == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((k_skinny<C, BF>), dim3((unsigned)gx), dim3(C::NT), 0, st, (const u16*)L.A, L.lda,
+                       (const u16*)L.B, L.ldb, (u16*)L.C, L.ldc, L.M, L.N, L.K, L.vec4);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ fused group kernel
 
 template <int LEVELS>
@@ -1361,7 +1547,13 @@ hipError_t launch_classic(const ClassicLaunch& L, hipStream_t st)
             return L.bf16 ? launch_classic_q4_t<QC256, true>(L, st) : launch_classic_q4_t<QC256, false>(L, st);
         return launch_classic_c<Cfg256>(L, st);
     case kTile128: return launch_classic_c<Cfg128>(L, st);
-    default: return launch_classic_c<Cfg32>(L, st);
+    default:
+        // M <= 64 with 16-byte aligned operands: the streaming kernel
+        if (L.vec && L.M <= 32)
+            return L.bf16 ? launch_skinny_t<sk::SCfg<32>, true>(L, st) : launch_skinny_t<sk::SCfg<32>, false>(L, st);
+        if (L.vec && L.M <= 64)
+            return L.bf16 ? launch_skinny_t<sk::SCfg<64>, true>(L, st) : launch_skinny_t<sk::SCfg<64>, false>(L, st);
+        return launch_classic_c<Cfg32>(L, st);
     }
 }
 
