@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--size", type=int, default=0,
                     help="time the algorithms on an n^3 bfloat16 product instead of the 4096^3 workload "
                          "(detail only; the headline workload is fixed)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the decode-shape bandwidth and 24-shape sweep measurements")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="first run 3 device copies of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -206,9 +208,71 @@ def main():
     if "l1" in detail and "classic" in detail:
         out["l1_over_classic"] = round(detail["classic"]["ms"] / detail["l1"]["ms"], 4)
 
+    if not args.no_extra and not args.size:
+        del Ad, Bd, C, plans
+        torch.cuda.empty_cache()
+        out["decode"] = decode_bandwidth(L, si, torch, time_calls)
+        out["sweep"] = sweep_picks(L, si, torch, time_calls)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(A, B, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def decode_bandwidth(L, si, torch, time_calls):
+    """Decode-shaped products (M in 1, 4, 16, 64; K=4096, N=14336, bfloat16): the
+    planned path (the cost model must pick classic), HBM GB/s of the algorithmic
+    bytes 2(MK + KN + MN).  B rotates over 4 resident copies (470 MB, more than
+    the 256 MB last-level cache), so every call streams its B from HBM."""
+    res = {}
+    for m in si.DECODE_MS:
+        w = si.decode_shape(m)
+        A, B = si.gen(**w)
+        Ad = A.to("cuda")
+        Bs = [B.to("cuda")] + [None] * 3
+        for i in range(1, 4):
+            Bs[i] = Bs[0].clone()
+        Cd = torch.empty((m, w["N"]), dtype=torch.bfloat16, device="cuda")
+        p = L.lcma_plan(m, w["N"], w["K"], "bf16")
+        algo = L.lcma_plan_info(p)[0]
+        k = [0]
+
+        def call():
+            L.lcma_gemm(p, Ad, Bs[k[0] & 3], Cd, None)
+            k[0] += 1
+        t = time_calls(call, 200, 20)
+        byts = 2.0 * (m * w["K"] + w["K"] * w["N"] + m * w["N"])
+        res[f"M={m}"] = {"algo": algo, "us": round(t * 1e3, 2), "hbm_gbps": round(byts / (t * 1e-3) / 1e9, 1),
+                         "tflops": round(2.0 * m * w["N"] * w["K"] / (t * 1e-3) / 1e12, 2)}
+        del Ad, Bs, Cd
+    torch.cuda.empty_cache()
+    return res
+
+
+def sweep_picks(L, si, torch, time_calls):
+    """The 24 seeded sweep shapes (binary16): the cost model's pick against the
+    measured fastest admissible algorithm; agreement rate over the shapes."""
+    rows, agree = [], 0
+    for w in si.sweep_workloads():
+        M, N, K = w["M"], w["N"], w["K"]
+        A, B = si.gen(**w)
+        Ad, Bd = A.to("cuda"), B.to("cuda")
+        Cd = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        pick = L.lcma_plan_info(L.lcma_plan(M, N, K, "f16"))[0]
+        times = {}
+        for algo in ("classic", "l1", "l2"):
+            try:
+                p = L.lcma_plan_ex(M, N, K, "f16", force=algo)
+            except L.LcmaError:
+                continue
+            ws = L.workspace_for(p)
+            times[algo] = time_calls(lambda: L.lcma_gemm(p, Ad, Bd, Cd, ws), 20, 3)
+        best = min(times, key=times.get)
+        agree += pick == best
+        rows.append({"shape": [M, N, K], "pick": pick, "best": best,
+                     "ms": {a: round(t, 4) for a, t in times.items()}})
+        del Ad, Bd, Cd
+    torch.cuda.empty_cache()
+    return {"agreement": round(agree / len(rows), 3), "shapes": rows}
 
 
 def cpu_baseline(A, B, target_s):
