@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--size", type=int, default=0,
                     help="time the algorithms on an n^3 bfloat16 product instead of the 4096^3 workload "
                          "(detail only; the headline workload is fixed)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode-shape bandwidth measurement (one JSON line), for profiling runs")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the decode-shape bandwidth and 24-shape sweep measurements")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -74,6 +76,21 @@ def main():
     import torch
     import complexity_half_precision_amd as L
     import seeded_inputs as si
+
+    if args.decode_only:
+        def tc(fn, reps, warm):
+            for _ in range(warm):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+        print(json.dumps({"decode": decode_bandwidth(L, si, torch, tc)}), flush=True)
+        return
 
     wl = dict(si.SQUARE_4096_BF16)
     if args.size:

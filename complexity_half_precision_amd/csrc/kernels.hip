@@ -881,6 +881,64 @@ __device__ __forceinline__ void dma_tile(char* stage, const pp::TileSrc& s, int 
         dma_one<C, EDGE>(stage, s, xw, lane, i);
 }
 
+// Interior tiles: one wave's four A loads (or four B loads) of a k-tile
+// share one M0.  The load's immediate offset moves both the buffer address
+// and the LDS address, so load i uses offset 1024 i with its buffer offset
+// lowered by the same amount.  With K a multiple of 32 (so lda, ldb >= 32)
+// every lowered offset stays non-negative.  The offsets do not depend on the
+// k-tile: the descriptor base moves instead.
+template <class C>
+struct Group {
+    u32 a[C::A_PER];
+    u32 b[C::B_PER];
+};
+
+template <class C>
+__device__ __forceinline__ Group<C> group_offsets(const pp::TileSrc& s, int xw, int lane)
+{
+    static_assert(C::A_PER == 4 && C::B_PER == 4, "four loads per group");
+    Group<C> g;
+#pragma unroll
+    for (int i = 0; i < C::A_PER; ++i) {
+        const int ins = xw * C::A_PER + i;
+        const int r = ins * 16 + (lane >> 2);
+        const int k = ((lane & 3) ^ (int)pp::a_swz(r)) * 8;
+        g.a[i] = (u32)(r * s.lda + k) * 2u - 1024u * i;
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_PER; ++i) {
+        const int ins = xw * C::B_PER + i;
+        const int byte = ins * 1024 + lane * 16;
+        const int r = byte / C::BROW;
+        const int n = (((byte % C::BROW) >> 4) ^ (int)pp::b_swz(r)) * 8;
+        g.b[i] = (u32)(r * s.ldb + n) * 2u - 1024u * i;
+    }
+    return g;
+}
+
+__device__ __forceinline__ void dma16x4(u32x4 rs, const u32 (&off)[4], u32 lds)
+{
+    asm volatile("s_nop 0\n\t"
+                 "buffer_load_dwordx4 %0, %4, 0 offen lds\n\t"
+                 "buffer_load_dwordx4 %1, %4, 0 offen offset:1024 lds\n\t"
+                 "buffer_load_dwordx4 %2, %4, 0 offen offset:2048 lds\n\t"
+                 "buffer_load_dwordx4 %3, %4, 0 offen offset:3072 lds"
+                 :
+                 : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(rs), "{m0}"(lds)
+                 : "memory");
+}
+
+// Wave xw's A loads (side 0) or B loads (side 1) of k-tile source s into `stage`.
+template <class C>
+__device__ __forceinline__ void dma_group(char* stage, const pp::TileSrc& s, const Group<C>& g, int xw, int side)
+{
+    const u32 base = lds_addr(stage);
+    if (side == 0)
+        dma16x4(rsrc_words(s.a + s.k0), g.a, base + xw * C::A_PER * 1024);
+    else
+        dma16x4(rsrc_words(s.b + (int64_t)s.k0 * s.ldb), g.b, base + C::A_BYTES + xw * C::B_PER * 1024);
+}
+
 // s_waitcnt vmcnt(N): vmcnt is split over bits 3:0 and 15:14; expcnt and
 // lgkmcnt at their maxima (no wait).
 template <int N>
@@ -977,12 +1035,23 @@ __device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, int wave
     constexpr int LSLOT = NRD / RPS + 1;            // first load slot; loads every other MFMA
     static_assert(NRD % RPS == 0 && C::PER % 2 == 0 && LSLOT + 2 * (HALF - 1) < NMF, "interleave slots");
     static_assert(C::AHEAD == 3 && C::NSTAGE == 4, "stage reuse below assumes a 4-stage ring, 3 ahead");
+    static_assert(C::A_PER == HALF && C::B_PER == HALF, "first half loads A, second half B");
     Step<C> F0, F1;
     u32x2 bh[C::FN][2];
+    Group<C> go;
+    if constexpr (!EDGE)
+        go = group_offsets<C>(src(0), wave, lane);
 #pragma unroll
-    for (int t = 0; t < C::AHEAD; ++t)
-        if (t < nk)
-            dma_tile<C, EDGE>(smem + t * C::STAGE, src(t), wave, lane);
+    for (int t = 0; t < C::AHEAD; ++t) {
+        if (t < nk) {
+            if constexpr (EDGE) {
+                dma_tile<C, EDGE>(smem + t * C::STAGE, src(t), wave, lane);
+            } else {
+                dma_group<C>(smem + t * C::STAGE, src(t), go, wave, 0);
+                dma_group<C>(smem + t * C::STAGE, src(t), go, wave, 1);
+            }
+        }
+    }
     wait_tiles<C>(min(nk, C::AHEAD) - 1);
     pp::bar();
     if (nk > 0) {
@@ -1007,8 +1076,12 @@ __device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, int wave
 #pragma unroll
                 for (int r = 0; r < RPS; ++r)
                     read_one<C>(cur, ad, 1, x * RPS + r, F1, bh);
-            } else if (x >= LSLOT && ((x - LSLOT) & 1) == 0 && (x - LSLOT) / 2 < HALF) {
-                dma_one<C, EDGE>(pre, ps, wave, lane, (x - LSLOT) / 2);
+            } else if constexpr (EDGE) {
+                if (x >= LSLOT && ((x - LSLOT) & 1) == 0 && (x - LSLOT) / 2 < HALF)
+                    dma_one<C, EDGE>(pre, ps, wave, lane, (x - LSLOT) / 2);
+            } else {
+                if (x == LSLOT)
+                    dma_group<C>(pre, ps, go, wave, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1026,8 +1099,12 @@ __device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, int wave
 #pragma unroll
                 for (int r = 0; r < RPS; ++r)
                     read_one<C>(nxt, ad, 0, x * RPS + r, F0, bh);
-            } else if (x >= LSLOT && ((x - LSLOT) & 1) == 0 && (x - LSLOT) / 2 < HALF) {
-                dma_one<C, EDGE>(pre, ps, wave, lane, HALF + (x - LSLOT) / 2);
+            } else if constexpr (EDGE) {
+                if (x >= LSLOT && ((x - LSLOT) & 1) == 0 && (x - LSLOT) / 2 < HALF)
+                    dma_one<C, EDGE>(pre, ps, wave, lane, HALF + (x - LSLOT) / 2);
+            } else {
+                if (x == LSLOT)
+                    dma_group<C>(pre, ps, go, wave, 1);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
