@@ -1,31 +1,35 @@
 // kernels.hip -- gfx950 (MI355X) kernels of the half-precision GEMM library.
 //
-//  * k_classic  -- tiled MFMA GEMM, C = A * B (fp32 accumulate, one RNE cast).
-//  * k_prepass  -- combine-A/B pass: every combined operand of an LCMA scheme,
-//                  summed in fp32 and rounded once to the operand type.
-//  * k_fused    -- persistent group kernel: all product tiles of one output
-//                  coordinate run on one workgroup, accumulated into the C
-//                  tiles in registers (fp32), never writing a product to
-//                  memory; tail groups may be split over two workgroups with
-//                  a last-arriver fp32 fix-up.
+//  * k_classic_q4 -- classic GEMM, C = A * B (fp32 accumulate, one RNE cast),
+//                    256 x 256 tiles on the four-wave engine (one wave per
+//                    SIMD, 128 x 128 per wave, direct-to-LDS loads).
+//  * k_skinny     -- M <= 64 products, built to stream B from HBM.
+//  * k_classic    -- register-staged tiles for the other shapes and for
+//                    operands that are not 16-byte aligned.
+//  * k_prepass    -- combine-A/B pass: every combined operand of an LCMA scheme,
+//                    summed in fp32 and rounded once to the operand type.
+//  * k_fused1_q4  -- persistent one-level group kernel on the four-wave engine:
+//                    the 7 products of one output coordinate accumulate into
+//                    the 4 output tiles in registers (fp32), no product is
+//                    written to memory; tail groups may be split over two
+//                    workgroups with a last-arriver fp32 fix-up.
+//  * k_fused<2>   -- the same for two levels (49 products, 16 outputs) on the
+//                    register-staged path.
 //
 // Sources: "FalconGEMM: Surpassing Hardware Peaks with Lower-Complexity
 // Matrix Multiplication", sections "从 LCMA 到 FalconGEMM" (combine A/B,
 // spatial groups accumulated on chip, split over two compute units, L2-aware
 // ordering, persistent kernel) and "从缓存重排到 Cost Model" (fp32 on-chip
 // combination, one final cast); "CUDA-L2 ..." section "核心贡献与发现的技术"
-// (double-buffered staging, wide epilogue stores, block swizzling).
+// (multi-stage staging, wide epilogue stores, block swizzling).
 //
-// Data layout shared by all kernels: row-major halves.  Each k-tile of 64
-// stages an A tile (BM rows x 64 k) and a B tile (BN columns x 64 k, stored
-// transposed so that both MFMA operands read 8 consecutive k per lane with
-// one 16-byte LDS read).  LDS rows are padded from 128 to 144 bytes so that
-// reads and writes are bank-conflict free with affine addresses.
-//
-// MFMA: v_mfma_f32_32x32x16_{f16,bf16}.  Operands are fed swapped (the B
-// fragment as the A operand), so the accumulator of lane l holds 4
-// consecutive output columns of output row (l % 32) per group of 4
-// registers, which the epilogue stores as one 8-byte write.
+// MFMA: v_mfma_f32_32x32x16_{f16,bf16} (16x16x32 in the two-level kernel).
+// Operands are fed swapped (the B fragment as the A operand), so the
+// accumulator of lane l holds 4 consecutive output columns of output row
+// (l % 32) per group of 4 registers, which the epilogue stores as one 8-byte
+// write.  The register-staged path stores B transposed in LDS (rows padded to
+// 144 bytes); the direct-to-LDS engines keep B row-major as in memory,
+// XOR-swizzled, and read it with ds_read_b64_tr_b16.
 
 #include <hip/hip_runtime.h>
 
@@ -583,40 +587,13 @@ hipError_t launch_prepass_t(const PrepassLaunch& L, hipStream_t st)
 // MFMAs from registers, the other reads the next k-tile's fragments from LDS
 // (and, for waves 0-3, issues the DMA of the tile two ahead).  A raw
 // s_barrier separates phases; explicit waitcnts order the DMA and the reads.
-namespace pp {
+namespace tiles {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-#define LCMA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }       // lgkmcnt(0)
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }         // vmcnt(0)
 __device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
-
-template <int BM_, int BN_, int WM_, int WN_>
-struct PCfg {
-    static constexpr int BM = BM_, BN = BN_, BK = 32, WM = WM_, WN = WN_, MT = 32;
-    static constexpr int NSTAGE = 4, KSTEPS = BK / 16;
-    static constexpr int NW = WM * WN;
-    static constexpr int NT = NW * 64;
-    static constexpr int WTM = BM / WM, WTN = BN / WN;
-    static constexpr int FM = WTM / 32, FN = WTN / 32;
-    using acc_t = f32x16;
-    static constexpr int NACC = 16;
-    static constexpr int AROW = BK * 2;               // bytes per A row
-    static constexpr int BROW = BN * 2;               // bytes per B row
-    static constexpr int A_BYTES = BM * AROW;
-    static constexpr int B_BYTES = BK * BROW;
-    static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int LDS = NSTAGE * STAGE;
-    static constexpr int LOADERS = NW / 2;
-    static constexpr int A_PER = A_BYTES / 1024 / LOADERS;   // 1 KB DMA instructions per loader wave
-    static constexpr int B_PER = B_BYTES / 1024 / LOADERS;
-    static_assert(NW == 8, "ping-pong pairs two waves per SIMD");
-    static_assert(A_BYTES % (1024 * LOADERS) == 0 && B_BYTES % (1024 * LOADERS) == 0, "DMA split");
-    static_assert(BROW % 256 == 0 && FM >= 1 && FN >= 1, "tile shape");
-    static_assert(LDS <= 160 * 1024, "LDS budget");
-    static_assert(A_PER + B_PER < 16, "one tile's DMA count fits the vmcnt immediate");
-};
 
 __device__ __forceinline__ u32 a_swz(u32 m) { return (m >> 2) & 3u; }
 __device__ __forceinline__ u32 b_swz(u32 k) { return 4u * (k & 3u); }
@@ -629,140 +606,8 @@ struct TileSrc {
     int k0, K;
 };
 
-// DMA of one k-tile into `stage` by loader wave xw (0..LOADERS-1).
-template <class C>
-__device__ __forceinline__ void dma_tile(char* stage, const TileSrc& s, int xw, int lane)
-{
-    const rsrc_t ra = make_rsrc(s.a + s.k0);
-    const rsrc_t rb = make_rsrc(s.b + (int64_t)s.k0 * s.ldb);
-    const int kleft = s.K - s.k0;
-#pragma unroll
-    for (int i = 0; i < C::A_PER; ++i) {
-        const int ins = xw * C::A_PER + i;                 // rows 16*ins .. 16*ins+15
-        const int r = ins * 16 + (lane >> 2);
-        const int k = ((lane & 3) ^ (int)a_swz(r)) * 8;
-        const u32 off0 = (u32)(r * s.lda + k) * 2u;
-        const u32 off = ((r < s.a_rows) & (k < kleft)) ? off0 : kOob;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, LCMA_LDS(stage + ins * 1024), 16, off, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_PER; ++i) {
-        const int ins = xw * C::B_PER + i;
-        const int byte = ins * 1024 + lane * 16;
-        const int r = byte / C::BROW;
-        const int n = (((byte % C::BROW) >> 4) ^ (int)b_swz(r)) * 8;
-        const u32 off0 = (u32)(r * s.ldb + n) * 2u;
-        const u32 off = ((r < kleft) & (n < s.b_cols)) ? off0 : kOob;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LCMA_LDS(stage + C::A_BYTES + ins * 1024), 16, off, 0, 0, 0);
-    }
-}
+}  // namespace tiles
 
-template <class C>
-struct Frags {
-    u32x4 a[C::KSTEPS][C::FM];
-    u32x4 b[C::KSTEPS][C::FN];
-};
-
-template <class C>
-__device__ __forceinline__ void read_frags(const char* stage, Frags<C>& F, int wm, int wn, int lane)
-{
-    const char* sA = stage;
-    const char* sB = stage + C::A_BYTES;
-    // A: lane -> row (lane & 31), logical chunk 2 st + (lane >> 5)
-    const u32 m = wm * C::WTM + (lane & 31);
-    const u32 f = a_swz(m);
-    const u32 abase = m * (u32)C::AROW + ((((lane >> 5) ^ f) & 1u) << 4) + ((f & 2u) << 4);
-    // B: 16-lane group g, lane s: k row 8 (g/2) + s/4 (+4), column 16 (g%2) + 4 (s%4)
-    const int g = lane >> 4, s = lane & 15;
-    const u32 kr = 8 * (g >> 1) + (s >> 2);
-    const u32 xb = b_swz(kr);
-#pragma unroll
-    for (int st = 0; st < C::KSTEPS; ++st) {
-        const u32 ao = abase ^ ((u32)st << 5);
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-            F.a[st][i] = *reinterpret_cast<const u32x4*>(sA + ao + i * 32 * C::AROW);
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-            const u32 n = wn * C::WTN + j * 32 + 16 * (g & 1) + 4 * (s & 3);
-            const u32 boff = (kr + 16 * st) * C::BROW + (((n >> 3) ^ xb) << 4) + (n & 7) * 2;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(sB + boff));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(sB + boff + 4 * C::BROW));
-            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-            F.b[st][j] = u32x4{l2.x, l2.y, h2.x, h2.y};
-        }
-    }
-}
-
-template <class C, bool BF>
-__device__ __forceinline__ void mma_frags(const Frags<C>& F, f32x16 (&acc)[C::FM][C::FN])
-{
-#pragma unroll
-    for (int st = 0; st < C::KSTEPS; ++st)
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j)
-                acc[i][j] = mfma<BF>(F.b[st][j], F.a[st][i], acc[i][j]);
-}
-
-// Runs `ntiles` k-tiles (tile t's source from src(t)) through the ping-pong
-// schedule for one role.  after(t) runs right after this wave's MFMAs of
-// tile t (used to fold a finished product into the outputs).  Both roles pass
-// 1 + 2*ntiles barriers.
-template <class C, bool BF, bool LOADER, class SrcFn, class AfterFn>
-__device__ __forceinline__ void run_tiles(char* smem, int ntiles, SrcFn src, AfterFn after, int wave, int wm, int wn,
-                                          int lane, f32x16 (&acc)[C::FM][C::FN])
-{
-    Frags<C> F;
-    if (LOADER) {
-        if (ntiles > 0)
-            dma_tile<C>(smem, src(0), wave, lane);
-        if (ntiles > 1) {
-            dma_tile<C>(smem + C::STAGE, src(1), wave, lane);
-            __builtin_amdgcn_s_waitcnt(0x0F70 | (C::A_PER + C::B_PER));   // tile 0 landed
-        } else {
-            wait_vm0();
-        }
-    }
-    bar();
-    for (int t = 0; t < ntiles; ++t) {
-        const char* cur = smem + (t % C::NSTAGE) * C::STAGE;
-        if (LOADER) {
-            read_frags<C>(cur, F, wm, wn, lane);
-            if (t + 2 < ntiles)
-                dma_tile<C>(smem + ((t + 2) % C::NSTAGE) * C::STAGE, src(t + 2), wave, lane);
-            wait_lgkm0();
-            bar();
-            mma_frags<C, BF>(F, acc);
-            after(t);
-            if (t + 2 < ntiles)
-                __builtin_amdgcn_s_waitcnt(0x0F70 | (C::A_PER + C::B_PER));   // tile t+1 landed
-            else
-                wait_vm0();
-            bar();
-        } else {
-            if (t > 0) {
-                mma_frags<C, BF>(F, acc);
-                after(t - 1);
-            }
-            bar();
-            read_frags<C>(cur, F, wm, wn, lane);
-            wait_lgkm0();
-            bar();
-        }
-    }
-    if (!LOADER && ntiles > 0) {
-        mma_frags<C, BF>(F, acc);
-        after(ntiles - 1);
-    }
-}
-
-}  // namespace pp
-
-using PCF1 = pp::PCfg<128, 128, 2, 4>;     // fused one-level: 8 waves of 64 x 32
 
 
 // ------------------------------------------------------------------ four-wave engine
@@ -848,16 +693,16 @@ __device__ __forceinline__ void dma16(u32x4 rs, u32 off, u32 lds)
 }
 
 // Instruction i (0 .. PER-1) of wave xw's share of a k-tile DMA: the first
-// A_PER move A rows, the rest B rows (same layout as pp::dma_tile).
+// A_PER move A rows, the rest B rows.
 template <class C, bool EDGE>
-__device__ __forceinline__ void dma_one(char* stage, const pp::TileSrc& s, int xw, int lane, int i)
+__device__ __forceinline__ void dma_one(char* stage, const tiles::TileSrc& s, int xw, int lane, int i)
 {
     const int kleft = s.K - s.k0;
     const u32 base = lds_addr(stage);
     if (i < C::A_PER) {
         const int ins = xw * C::A_PER + i;
         const int r = ins * 16 + (lane >> 2);
-        const int k = ((lane & 3) ^ (int)pp::a_swz(r)) * 8;
+        const int k = ((lane & 3) ^ (int)tiles::a_swz(r)) * 8;
         const u32 off0 = (u32)(r * s.lda + k) * 2u;
         const u32 off = !EDGE || ((r < s.a_rows) & (k < kleft)) ? off0 : kOob;
         dma16(rsrc_words(s.a + s.k0), off, base + ins * 1024);
@@ -865,7 +710,7 @@ __device__ __forceinline__ void dma_one(char* stage, const pp::TileSrc& s, int x
         const int ins = xw * C::B_PER + (i - C::A_PER);
         const int byte = ins * 1024 + lane * 16;
         const int r = byte / C::BROW;
-        const int n = (((byte % C::BROW) >> 4) ^ (int)pp::b_swz(r)) * 8;
+        const int n = (((byte % C::BROW) >> 4) ^ (int)tiles::b_swz(r)) * 8;
         const u32 off0 = (u32)(r * s.ldb + n) * 2u;
         const u32 off = !EDGE || ((r < kleft) & (n < s.b_cols)) ? off0 : kOob;
         dma16(rsrc_words(s.b + (int64_t)s.k0 * s.ldb), off, base + C::A_BYTES + ins * 1024);
@@ -874,15 +719,14 @@ __device__ __forceinline__ void dma_one(char* stage, const pp::TileSrc& s, int x
 
 // DMA of wave xw's share of one k-tile into `stage`.
 template <class C, bool EDGE>
-__device__ __forceinline__ void dma_tile(char* stage, const pp::TileSrc& s, int xw, int lane)
+__device__ __forceinline__ void dma_tile(char* stage, const tiles::TileSrc& s, int xw, int lane)
 {
 #pragma unroll
     for (int i = 0; i < C::PER; ++i)
         dma_one<C, EDGE>(stage, s, xw, lane, i);
 }
 
-// Interior tiles: one wave's four A loads (or four B loads) of a k-tile
-// share one M0.  The load's immediate offset moves both the buffer address
+// Interior tiles: one wave's A loads (or B loads) of a k-tile share one M0.  The load's immediate offset moves both the buffer address
 // and the LDS address, so load i uses offset 1024 i with its buffer offset
 // lowered by the same amount.  With K a multiple of 32 (so lda, ldb >= 32)
 // every lowered offset stays non-negative.  The offsets do not depend on the
@@ -894,15 +738,15 @@ struct Group {
 };
 
 template <class C>
-__device__ __forceinline__ Group<C> group_offsets(const pp::TileSrc& s, int xw, int lane)
+__device__ __forceinline__ Group<C> group_offsets(const tiles::TileSrc& s, int xw, int lane)
 {
-    static_assert(C::A_PER == 4 && C::B_PER == 4, "four loads per group");
+    static_assert(C::A_PER == C::B_PER && (C::A_PER == 2 || C::A_PER == 4), "loads per group");
     Group<C> g;
 #pragma unroll
     for (int i = 0; i < C::A_PER; ++i) {
         const int ins = xw * C::A_PER + i;
         const int r = ins * 16 + (lane >> 2);
-        const int k = ((lane & 3) ^ (int)pp::a_swz(r)) * 8;
+        const int k = ((lane & 3) ^ (int)tiles::a_swz(r)) * 8;
         g.a[i] = (u32)(r * s.lda + k) * 2u - 1024u * i;
     }
 #pragma unroll
@@ -910,33 +754,43 @@ __device__ __forceinline__ Group<C> group_offsets(const pp::TileSrc& s, int xw, 
         const int ins = xw * C::B_PER + i;
         const int byte = ins * 1024 + lane * 16;
         const int r = byte / C::BROW;
-        const int n = (((byte % C::BROW) >> 4) ^ (int)pp::b_swz(r)) * 8;
+        const int n = (((byte % C::BROW) >> 4) ^ (int)tiles::b_swz(r)) * 8;
         g.b[i] = (u32)(r * s.ldb + n) * 2u - 1024u * i;
     }
     return g;
 }
 
-__device__ __forceinline__ void dma16x4(u32x4 rs, const u32 (&off)[4], u32 lds)
+template <int N>
+__device__ __forceinline__ void dma16xN(u32x4 rs, const u32 (&off)[N], u32 lds)
 {
-    asm volatile("s_nop 0\n\t"
-                 "buffer_load_dwordx4 %0, %4, 0 offen lds\n\t"
-                 "buffer_load_dwordx4 %1, %4, 0 offen offset:1024 lds\n\t"
-                 "buffer_load_dwordx4 %2, %4, 0 offen offset:2048 lds\n\t"
-                 "buffer_load_dwordx4 %3, %4, 0 offen offset:3072 lds"
-                 :
-                 : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(rs), "{m0}"(lds)
-                 : "memory");
+    static_assert(N == 2 || N == 4, "group size");
+    if constexpr (N == 4)
+        asm volatile("s_nop 0\n\t"
+                     "buffer_load_dwordx4 %0, %4, 0 offen lds\n\t"
+                     "buffer_load_dwordx4 %1, %4, 0 offen offset:1024 lds\n\t"
+                     "buffer_load_dwordx4 %2, %4, 0 offen offset:2048 lds\n\t"
+                     "buffer_load_dwordx4 %3, %4, 0 offen offset:3072 lds"
+                     :
+                     : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(rs), "{m0}"(lds)
+                     : "memory");
+    else
+        asm volatile("s_nop 0\n\t"
+                     "buffer_load_dwordx4 %0, %2, 0 offen lds\n\t"
+                     "buffer_load_dwordx4 %1, %2, 0 offen offset:1024 lds"
+                     :
+                     : "v"(off[0]), "v"(off[1]), "s"(rs), "{m0}"(lds)
+                     : "memory");
 }
 
 // Wave xw's A loads (side 0) or B loads (side 1) of k-tile source s into `stage`.
 template <class C>
-__device__ __forceinline__ void dma_group(char* stage, const pp::TileSrc& s, const Group<C>& g, int xw, int side)
+__device__ __forceinline__ void dma_group(char* stage, const tiles::TileSrc& s, const Group<C>& g, int xw, int side)
 {
     const u32 base = lds_addr(stage);
     if (side == 0)
-        dma16x4(rsrc_words(s.a + s.k0), g.a, base + xw * C::A_PER * 1024);
+        dma16xN<C::A_PER>(rsrc_words(s.a + s.k0), g.a, base + xw * C::A_PER * 1024);
     else
-        dma16x4(rsrc_words(s.b + (int64_t)s.k0 * s.ldb), g.b, base + C::A_BYTES + xw * C::B_PER * 1024);
+        dma16xN<C::B_PER>(rsrc_words(s.b + (int64_t)s.k0 * s.ldb), g.b, base + C::A_BYTES + xw * C::B_PER * 1024);
 }
 
 // s_waitcnt vmcnt(N): vmcnt is split over bits 3:0 and 15:14; expcnt and
@@ -961,7 +815,7 @@ __device__ __forceinline__ void wait_tiles(int n)
     else if (n == 1)
         wait_vm<C::PER>();
     else
-        pp::wait_vm0();
+        tiles::wait_vm0();
 }
 
 
@@ -979,11 +833,11 @@ __device__ __forceinline__ Addr<C> frag_addr(int wm, int wn, int lane)
 {
     Addr<C> ad;
     const u32 m = wm * C::WTM + (lane & 31);
-    const u32 f = pp::a_swz(m);
+    const u32 f = tiles::a_swz(m);
     ad.a0 = m * (u32)C::AROW + ((((lane >> 5) ^ f) & 1u) << 4) + ((f & 2u) << 4);
     const int g = lane >> 4, s = lane & 15;
     const u32 kr = 8 * (g >> 1) + (s >> 2);
-    const u32 xb = pp::b_swz(kr);
+    const u32 xb = tiles::b_swz(kr);
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
         const u32 n = wn * C::WTN + j * 32 + 16 * (g & 1) + 4 * (s & 3);
@@ -1001,8 +855,8 @@ __device__ __forceinline__ void read_one(const char* stage, const Addr<C>& ad, i
         F.a[x] = *reinterpret_cast<const u32x4*>(stage + (ad.a0 ^ ((u32)st << 5)) + x * 32 * C::AROW);
     } else {
         const int y = x - C::FM, j = y >> 1, h = y & 1;
-        const pp::s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) pp::s16x4*)(stage + ad.b[j] + (16 * st + 4 * h) * C::BROW));
+        const tiles::s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) tiles::s16x4*)(stage + ad.b[j] + (16 * st + 4 * h) * C::BROW));
         bh[j][h] = __builtin_bit_cast(u32x2, v);
     }
 }
@@ -1020,40 +874,48 @@ __device__ __forceinline__ void join_b(Step<C>& F, const u32x2 (&bh)[C::FN][2])
 namespace q4 {
 
 // K loop of one output tile through the four-wave engine; k-tile t's
-// operands come from src(t).  Direct-to-LDS loads for tile t+3 are slotted
-// between MFMAs, half in each k-step, into the stage tile t-1 used (free once
-// this tile's barrier has passed).  EDGE applies the row / column / k bounds
-// to the loads; tiles wholly inside the matrices skip them.
-template <class C, bool BF, bool EDGE, class SrcFn>
-__device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, int wave, int lane, const Addr<C>& ad,
-                                         f32x16 (&acc)[C::FM][C::FN])
+// operands come from src(t), and after(t) runs once k-tile t's MFMAs are
+// issued (a fused group folds a finished product into its outputs there).
+// Both are called exactly once per k-tile, in increasing t; with GROUPED,
+// src(0) is called once more first.
+// Direct-to-LDS loads for tile t+3 are slotted between MFMAs, half in each
+// k-step, into the stage tile t-1 used (free once this tile's barrier has
+// passed).  EDGE applies the row / column / k bounds to the loads; tiles
+// wholly inside the operands skip them.  GROUPED issues each half as one
+// group under one M0 (offsets computed once: every k-tile must share the
+// leading dimensions of src(0)).
+template <class C, bool BF, bool EDGE, bool GROUPED, class SrcFn, class AfterFn>
+__device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, AfterFn after, int wave, int lane,
+                                         const Addr<C>& ad, f32x16 (&acc)[C::FM][C::FN])
 {
     constexpr int NMF = C::FM * C::FN;
     constexpr int NRD = C::FM + 2 * C::FN;          // LDS reads per k-step
     constexpr int RPS = 3;                          // reads slotted after one MFMA
-    constexpr int HALF = C::PER / 2;                // loads slotted per k-step
-    constexpr int LSLOT = NRD / RPS + 1;            // first load slot; loads every other MFMA
-    static_assert(NRD % RPS == 0 && C::PER % 2 == 0 && LSLOT + 2 * (HALF - 1) < NMF, "interleave slots");
+    constexpr int HALF = C::PER / 2;                // loads per k-step
+    constexpr int LSLOT = NRD / RPS;                // first load slot
+    constexpr int STEP = NMF - LSLOT >= 2 * HALF ? 2 : 1;
+    static_assert(NRD % RPS == 0 && C::PER % 2 == 0 && LSLOT + STEP * (HALF - 1) < NMF, "interleave slots");
     static_assert(C::AHEAD == 3 && C::NSTAGE == 4, "stage reuse below assumes a 4-stage ring, 3 ahead");
     static_assert(C::A_PER == HALF && C::B_PER == HALF, "first half loads A, second half B");
+    static_assert(!(GROUPED && EDGE), "grouped loads carry no bounds");
     Step<C> F0, F1;
     u32x2 bh[C::FN][2];
     Group<C> go;
-    if constexpr (!EDGE)
+    if constexpr (GROUPED)
         go = group_offsets<C>(src(0), wave, lane);
 #pragma unroll
     for (int t = 0; t < C::AHEAD; ++t) {
         if (t < nk) {
-            if constexpr (EDGE) {
-                dma_tile<C, EDGE>(smem + t * C::STAGE, src(t), wave, lane);
-            } else {
+            if constexpr (GROUPED) {
                 dma_group<C>(smem + t * C::STAGE, src(t), go, wave, 0);
                 dma_group<C>(smem + t * C::STAGE, src(t), go, wave, 1);
+            } else {
+                dma_tile<C, EDGE>(smem + t * C::STAGE, src(t), wave, lane);
             }
         }
     }
     wait_tiles<C>(min(nk, C::AHEAD) - 1);
-    pp::bar();
+    tiles::bar();
     if (nk > 0) {
 #pragma unroll
         for (int x = 0; x < NRD; ++x)
@@ -1066,7 +928,7 @@ __device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, int wave
         const char* cur = smem + (t % C::NSTAGE) * C::STAGE;
         const char* nxt = smem + ((t + 1) % C::NSTAGE) * C::STAGE;
         char* pre = smem + ((t + C::AHEAD) % C::NSTAGE) * C::STAGE;
-        const pp::TileSrc ps = src(t + C::AHEAD);
+        const tiles::TileSrc ps = src(t + C::AHEAD);
         // k-step 0 MFMAs; k-step 1 reads and the first half of the prefetch
 #pragma unroll
         for (int x = 0; x < NMF; ++x) {
@@ -1076,19 +938,19 @@ __device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, int wave
 #pragma unroll
                 for (int r = 0; r < RPS; ++r)
                     read_one<C>(cur, ad, 1, x * RPS + r, F1, bh);
-            } else if constexpr (EDGE) {
-                if (x >= LSLOT && ((x - LSLOT) & 1) == 0 && (x - LSLOT) / 2 < HALF)
-                    dma_one<C, EDGE>(pre, ps, wave, lane, (x - LSLOT) / 2);
-            } else {
+            } else if constexpr (GROUPED) {
                 if (x == LSLOT)
                     dma_group<C>(pre, ps, go, wave, 0);
+            } else {
+                if (x >= LSLOT && (x - LSLOT) % STEP == 0 && (x - LSLOT) / STEP < HALF)
+                    dma_one<C, EDGE>(pre, ps, wave, lane, (x - LSLOT) / STEP);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
         join_b<C>(F1, bh);
         wait_vm<C::PER>();      // tile t+1 landed (at most one tile's loads in flight)
-        pp::wait_lgkm0();       // k-step 1 fragments are in registers
-        pp::bar();
+        tiles::wait_lgkm0();       // k-step 1 fragments are in registers
+        tiles::bar();
         __builtin_amdgcn_sched_barrier(0);
         // k-step 1 MFMAs; next tile's k-step 0 reads and the second half of the prefetch
 #pragma unroll
@@ -1099,16 +961,18 @@ __device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, int wave
 #pragma unroll
                 for (int r = 0; r < RPS; ++r)
                     read_one<C>(nxt, ad, 0, x * RPS + r, F0, bh);
-            } else if constexpr (EDGE) {
-                if (x >= LSLOT && ((x - LSLOT) & 1) == 0 && (x - LSLOT) / 2 < HALF)
-                    dma_one<C, EDGE>(pre, ps, wave, lane, HALF + (x - LSLOT) / 2);
-            } else {
+            } else if constexpr (GROUPED) {
                 if (x == LSLOT)
                     dma_group<C>(pre, ps, go, wave, 1);
+            } else {
+                if (x >= LSLOT && (x - LSLOT) % STEP == 0 && (x - LSLOT) / STEP < HALF)
+                    dma_one<C, EDGE>(pre, ps, wave, lane, HALF + (x - LSLOT) / STEP);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
         join_b<C>(F0, bh);
+        after(t);
+        __builtin_amdgcn_sched_barrier(0);
     }
     // Last AHEAD k-tiles: nothing left to prefetch.
     for (; t < nk; ++t) {
@@ -1120,14 +984,15 @@ __device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, int wave
         mma_step<C, BF>(F0, acc);
         if (t + 1 < nk) {
             wait_tiles<C>(nk - 2 - t);
-            pp::wait_lgkm0();
-            pp::bar();
+            tiles::wait_lgkm0();
+            tiles::bar();
 #pragma unroll
             for (int x = 0; x < NRD; ++x)
                 read_one<C>(smem + ((t + 1) % C::NSTAGE) * C::STAGE, ad, 0, x, F0, bh);
             join_b<C>(F0, bh);
         }
         mma_step<C, BF>(F1, acc);
+        after(t);
     }
 }
 
@@ -1153,14 +1018,15 @@ k_classic_q4(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, 
     f32x16 acc[C::FM][C::FN];
     zero_acc<C>(acc);
     auto src = [&](int t) {
-        return pp::TileSrc{Ab, (int)lda, M - m0, Bb, (int)ldb, N - n0, t * C::BK, K};
+        return tiles::TileSrc{Ab, (int)lda, M - m0, Bb, (int)ldb, N - n0, t * C::BK, K};
     };
     const q4::Addr<C> ad = q4::frag_addr<C>(wm, wn, lane);
     const bool inside = (m0 + C::BM <= M) & (n0 + C::BN <= N) & (K % C::BK == 0);
+    auto none = [](int) {};
     if (inside)
-        q4::run_tile<C, BF, false>(smem, nk, src, wave, lane, ad, acc);
+        q4::run_tile<C, BF, false, true>(smem, nk, src, none, wave, lane, ad, acc);
     else
-        q4::run_tile<C, BF, true>(smem, nk, src, wave, lane, ad, acc);
+        q4::run_tile<C, BF, true, false>(smem, nk, src, none, wave, lane, ad, acc);
     if (vec4)
         store_c<C, BF, true>(acc, Cm + (int64_t)m0 * ldc + n0, ldc, M - m0, N - n0, wm, wn, lane);
     else
@@ -1216,7 +1082,7 @@ struct SCfg {
 // One wave's loads of k-tile k0 into `stage` (rows / columns / k beyond the
 // operands read as zero).
 template <class C>
-__device__ __forceinline__ void dma_ktile(char* stage, const pp::TileSrc& s, int lane)
+__device__ __forceinline__ void dma_ktile(char* stage, const tiles::TileSrc& s, int lane)
 {
     const u32x4 ra = q4::rsrc_words(s.a + s.k0);
     const u32x4 rb = q4::rsrc_words(s.b + (int64_t)s.k0 * s.ldb);
@@ -1225,7 +1091,7 @@ __device__ __forceinline__ void dma_ktile(char* stage, const pp::TileSrc& s, int
 #pragma unroll
     for (int i = 0; i < C::A_PER; ++i) {
         const int r = i * 16 + (lane >> 2);
-        const int k = ((lane & 3) ^ (int)pp::a_swz(r)) * 8;
+        const int k = ((lane & 3) ^ (int)tiles::a_swz(r)) * 8;
         const u32 off = ((r < s.a_rows) & (k < kleft)) ? (u32)(r * s.lda + k) * 2u : kOob;
         q4::dma16(ra, off, base + i * 1024);
     }
@@ -1250,7 +1116,7 @@ __device__ __forceinline__ void wait_tiles(int n)
     else if (n == 1)
         q4::wait_vm<C::PER>();
     else
-        pp::wait_vm0();
+        tiles::wait_vm0();
 }
 
 // All fragments of one k-tile (2 k-steps) and their MFMAs.
@@ -1260,7 +1126,7 @@ __device__ __forceinline__ void ktile(const char* stage, int lane, f32x16 (&acc)
     const char* sA = stage;
     const char* sB = stage + C::A_BYTES;
     const u32 m = lane & 31;
-    const u32 f = pp::a_swz(m);
+    const u32 f = tiles::a_swz(m);
     const u32 abase = m * (u32)C::AROW + ((((lane >> 5) ^ f) & 1u) << 4) + ((f & 2u) << 4);
     const int g = lane >> 4, s = lane & 15;
     const u32 kr = 8 * (g >> 1) + (s >> 2);
@@ -1274,10 +1140,10 @@ __device__ __forceinline__ void ktile(const char* stage, int lane, f32x16 (&acc)
         for (int j = 0; j < C::FN; ++j) {
             const u32 n = j * 32 + 16 * (g & 1) + 4 * (s & 3);
             const u32 boff = (kr + 16 * st) * C::BROW + n * 2;
-            const pp::s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) pp::s16x4*)(sB + boff));
-            const pp::s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) pp::s16x4*)(sB + boff + 4 * C::BROW));
+            const tiles::s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) tiles::s16x4*)(sB + boff));
+            const tiles::s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) tiles::s16x4*)(sB + boff + 4 * C::BROW));
             const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
             b[st][j] = u32x4{l2.x, l2.y, h2.x, h2.y};
         }
@@ -1307,7 +1173,7 @@ k_skinny(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int6
     const int nk = (K + C::BK - 1) / C::BK;
     const int nu = nk > wave ? (nk - wave + C::NW - 1) / C::NW : 0;    // k-tiles of this wave
     auto src = [&](int u) {
-        return pp::TileSrc{A, (int)lda, M, Bb, (int)ldb, N - n0, (wave + u * C::NW) * C::BK, K};
+        return tiles::TileSrc{A, (int)lda, M, Bb, (int)ldb, N - n0, (wave + u * C::NW) * C::BK, K};
     };
     f32x16 acc[C::FM][C::FN];
     zero_acc<C>(acc);
@@ -1320,12 +1186,12 @@ k_skinny(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int6
         sk::ktile<C, BF>(ring + (u % C::NSTAGE) * C::STAGE, lane, acc);
         // tile u-1's stage is free: its fragments were consumed by the MFMAs above
         if (u + C::AHEAD < nu) {
-            pp::wait_lgkm0();
+            tiles::wait_lgkm0();
             sk::dma_ktile<C>(ring + ((u + C::AHEAD) % C::NSTAGE) * C::STAGE, src(u + C::AHEAD), lane);
         }
     }
     // Sum the four waves' partial tiles in a fixed order through LDS.
-    pp::wait_vm0();
+    tiles::wait_vm0();
     __syncthreads();
     float* part = reinterpret_cast<float*>(smem);
     if (wave > 0) {
@@ -1534,10 +1400,17 @@ __global__ void __launch_bounds__(FusedCfg<LEVELS>::C::NT) k_fused(const FusedPa
 // group tile, 64 x 32 per wave): the product tiles of an item run back to
 // back through the DMA ring; after each product's last k-tile every wave folds
 // its H sub-tile into its four output sub-tiles.
+
+using QCF1 = q4::QCfg<128, 128>;   // fused one-level: 4 waves of 64 x 64
+
+// Fused one-level group kernel on the four-wave engine: the products of a
+// work item stream back to back through the same LDS ring (the prefetch runs
+// across product boundaries); at each product's last k-tile every wave folds
+// H into its four fp32 output sub-tiles.
 template <bool OBF, bool CBF>
-__global__ void __launch_bounds__(PCF1::NT) k_fused1_pp(const FusedParams fp)
+__global__ void __launch_bounds__(QCF1::NT, 1) k_fused1_q4(const FusedParams fp)
 {
-    using C = PCF1;
+    using C = QCF1;
     constexpr int NOUT = 4;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
     __shared__ int sh_old;
@@ -1562,22 +1435,44 @@ __global__ void __launch_bounds__(PCF1::NT) k_fused1_pp(const FusedParams fp)
             zero_acc<C>(Cacc[o]);
         f32x16 H[C::FM][C::FN];
         zero_acc<C>(H);
-        const int ntiles = (item.pos1 - item.pos0) * nk;
-        auto src = [&](int t) {
-            const int r = fp.order[item.pos0 + t / nk];
-            return pp::TileSrc{fp.a[r] + (int64_t)m0 * fp.lda[r], (int)fp.lda[r], fp.Mb - m0,
-                               fp.b[r] + n0, (int)fp.ldb[r], fp.Nb - n0, (t % nk) * C::BK, fp.Kb};
+        const int nprod = item.pos1 - item.pos0;
+        const int ntiles = nprod * nk;
+        // The engine asks for k-tile sources, and reports finished k-tiles, in
+        // increasing order, so both walk a cursor; product parameters (kernel
+        // argument arrays, read through scalar loads) are fetched only when
+        // the product changes.
+        auto prod_src = [&](int j) {
+            const int r = fp.order[item.pos0 + j];
+            return tiles::TileSrc{fp.a[r] + (int64_t)m0 * fp.lda[r], (int)fp.lda[r], fp.Mb - m0,
+                                  fp.b[r] + n0, (int)fp.ldb[r], fp.Nb - n0, 0, fp.Kb};
         };
-        auto after = [&](int t) {
-            if (t % nk == nk - 1) {
-                combine_h<NOUT, C>(fp.w[fp.order[item.pos0 + t / nk]], H, Cacc);
+        int sj = 0, skt = 0;
+        tiles::TileSrc sbase = prod_src(0);
+        auto src = [&](int) {
+            tiles::TileSrc s = sbase;
+            s.k0 = skt * C::BK;
+            if (++skt == nk) {
+                skt = 0;
+                if (++sj < nprod)
+                    sbase = prod_src(sj);
+            }
+            return s;
+        };
+        int aj = 0, akt = 0;
+        auto after = [&](int) {
+            if (++akt == nk) {
+                akt = 0;
+                combine_h<NOUT, C>(fp.w[fp.order[item.pos0 + aj]], H, Cacc);
                 zero_acc<C>(H);
+                ++aj;
             }
         };
-        if (wave < C::NW / 2)
-            pp::run_tiles<C, OBF, true>(smem, ntiles, src, after, wave, wm, wn, lane, H);
+        const q4::Addr<C> ad = q4::frag_addr<C>(wm, wn, lane);
+        const bool inside = (m0 + C::BM <= fp.Mb) & (n0 + C::BN <= fp.Nb) & (fp.Kb % C::BK == 0);
+        if (inside)
+            q4::run_tile<C, OBF, false, false>(smem, ntiles, src, after, wave, lane, ad, H);
         else
-            pp::run_tiles<C, OBF, false>(smem, ntiles, src, after, wave, wm, wn, lane, H);
+            q4::run_tile<C, OBF, true, false>(smem, ntiles, src, after, wave, lane, ad, H);
         __syncthreads();
         fused_epilogue<NOUT, C, CBF>(fp, item, m0, n0, Cacc, tid, wm, wn, lane, &sh_old);
         __syncthreads();
@@ -1585,11 +1480,11 @@ __global__ void __launch_bounds__(PCF1::NT) k_fused1_pp(const FusedParams fp)
 }
 
 template <bool OBF, bool CBF>
-hipError_t launch_fused1_pp(const FusedLaunch& L, hipStream_t st)
+hipError_t launch_fused1_q4(const FusedLaunch& L, hipStream_t st)
 {
     if (L.grid <= 0)
         return hipSuccess;
-    hipLaunchKernelGGL((k_fused1_pp<OBF, CBF>), dim3(L.grid), dim3(PCF1::NT), 0, st, L.p);
+    hipLaunchKernelGGL((k_fused1_q4<OBF, CBF>), dim3(L.grid), dim3(QCF1::NT), 0, st, L.p);
     return hipGetLastError();
 }
 
@@ -1649,15 +1544,15 @@ hipError_t launch_prepass(const PrepassLaunch& L, hipStream_t st)
     return launch_prepass_t<2, false, false, false>(L, st);
 }
 
-int32_t fused_tile(int32_t levels) { return levels == 1 ? PCF1::BM : FusedCfg<2>::C::BM; }
-static_assert(PCF1::BM == PCF1::BN, "fused tiles are square");
+int32_t fused_tile(int32_t levels) { return levels == 1 ? QCF1::BM : FusedCfg<2>::C::BM; }
+static_assert(QCF1::BM == QCF1::BN, "fused tiles are square");
 static_assert(FusedCfg<1>::C::BM == FusedCfg<1>::C::BN && FusedCfg<2>::C::BM == FusedCfg<2>::C::BN,
               "fused tiles are square");
 
 int64_t fused_partial_bytes(int32_t levels)
 {
     if (levels == 1)
-        return (int64_t)4 * PCF1::BM * PCF1::BN * 4;
+        return (int64_t)4 * QCF1::BM * QCF1::BN * 4;
     using C = FusedCfg<2>::C;
     return (int64_t)16 * C::BM * C::BN * 4;
 }
@@ -1681,8 +1576,8 @@ hipError_t launch_fused(const FusedLaunch& L, hipStream_t st)
 {
     if (L.levels == 1) {
         if (L.out_bf16)
-            return L.op_bf16 ? launch_fused1_pp<true, true>(L, st) : launch_fused1_pp<false, true>(L, st);
-        return launch_fused1_pp<false, false>(L, st);
+            return L.op_bf16 ? launch_fused1_q4<true, true>(L, st) : launch_fused1_q4<false, true>(L, st);
+        return launch_fused1_q4<false, false>(L, st);
     }
     if (L.out_bf16)
         return L.op_bf16 ? launch_fused_t<2, true, true>(L, st) : launch_fused_t<2, false, true>(L, st);
