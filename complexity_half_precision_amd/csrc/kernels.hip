@@ -998,7 +998,8 @@ __device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, AfterFn 
 
 }  // namespace q4
 
-using QC256 = q4::QCfg<256, 256>;
+using QC256 = q4::QCfg<256, 256>;   // 4 waves of 128 x 128
+using QC128 = q4::QCfg<128, 128>;   // 4 waves of 64 x 64
 
 template <class C, bool BF>
 __global__ void __launch_bounds__(C::NT, 1)
@@ -1401,7 +1402,7 @@ __global__ void __launch_bounds__(FusedCfg<LEVELS>::C::NT) k_fused(const FusedPa
 // back through the DMA ring; after each product's last k-tile every wave folds
 // its H sub-tile into its four output sub-tiles.
 
-using QCF1 = q4::QCfg<128, 128>;   // fused one-level: 4 waves of 64 x 64
+using QCF1 = QC128;                 // fused one-level group tile
 
 // Fused one-level group kernel on the four-wave engine: the products of a
 // work item stream back to back through the same LDS ring (the prefetch runs
@@ -1518,7 +1519,10 @@ hipError_t launch_classic(const ClassicLaunch& L, hipStream_t st)
         if (L.vec)
             return L.bf16 ? launch_classic_q4_t<QC256, true>(L, st) : launch_classic_q4_t<QC256, false>(L, st);
         return launch_classic_c<Cfg256>(L, st);
-    case kTile128: return launch_classic_c<Cfg128>(L, st);
+    case kTile128:
+        if (L.vec)
+            return L.bf16 ? launch_classic_q4_t<QC128, true>(L, st) : launch_classic_q4_t<QC128, false>(L, st);
+        return launch_classic_c<Cfg128>(L, st);
     default:
         // M <= 64 with 16-byte aligned operands: the streaming kernel
         if (L.vec && L.M <= 32)

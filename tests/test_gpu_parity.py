@@ -78,6 +78,10 @@ CLASSIC_SHAPES = [
     (1, 8, 8), (7, 13, 5), (3, 1, 9), (33, 40, 24), (64, 64, 64), (65, 72, 136),
     (100, 200, 304), (257, 136, 72), (300, 520, 1000), (513, 264, 520),
     (4100, 4104, 72),          # 256 x 256 tiles with ragged tails in M and N
+    (1000, 1064, 256),         # 128 x 128 four-wave tiles: interior (grouped loads) and edge tiles
+    (640, 384, 4096),          # 128 x 128 four-wave tiles, all interior, long K
+    (17, 1000, 520),           # streaming kernel (32-row A), N and K tails
+    (60, 2056, 1000),          # streaming kernel (64-row A), N and K tails
 ]
 
 
@@ -90,7 +94,8 @@ def test_classic_matches_oracle(M, N, K, dtype):
 
 
 @pytest.mark.parametrize("dtype,dist", [("f16", "int2"), ("bf16", "int1")])
-@pytest.mark.parametrize("M,N,K", [(33, 40, 24), (130, 200, 96), (257, 136, 120), (512, 512, 256), (4100, 264, 64)])
+@pytest.mark.parametrize("M,N,K", [(33, 40, 24), (130, 200, 96), (257, 136, 120), (512, 512, 256), (4100, 264, 64),
+                                   (1000, 1064, 256), (4096, 4104, 96), (48, 1000, 200)])
 def test_classic_integer_inputs_are_exact(M, N, K, dtype, dist):
     say("classic exact", M, N, K, dtype)
     A, B, A64, B64 = gen(M, N, K, dtype, dist, seed=7)
@@ -111,6 +116,24 @@ def test_classic_strided_operands_and_output():
     torch.cuda.synchronize()
     check_float(C.cpu(), A64, B64, "f16")
     assert torch.all(Cbig[:, N:].cpu() == 7.0)     # nothing written outside C
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 256), (1024, 768, 512), (40, 1032, 520)])
+def test_classic_strided_aligned_paths(M, N, K):
+    # leading dimensions larger than the extents (multiples of 8 elements, so
+    # the direct-to-LDS kernels run): 256 x 256 and 128 x 128 four-wave tiles
+    # and the streaming kernel
+    say("classic strided aligned", M, N, K)
+    Abig, Bbig, _, _ = gen(M, N + 24, K + 40, "bf16", "normal_sqrtk", seed=21)
+    A, B = Abig[:, :K], Bbig[:K, :N]
+    A64, B64 = si.f64(A), si.f64(B)
+    Ad, Bd = Abig.to(DEV)[:, :K], Bbig.to(DEV)[:K, :N]
+    Cbig = torch.full((M, N + 16), 7.0, dtype=torch.bfloat16, device=DEV)
+    C = Cbig[:, :N]
+    L.gemm_classic(Ad, Bd, C)
+    torch.cuda.synchronize()
+    check_float(C.cpu(), A64, B64, "bf16")
+    assert torch.all(Cbig[:, N:].cpu() == 7.0)
 
 
 def test_classic_unaligned_pointers():
@@ -208,6 +231,22 @@ def test_prepass_operands_are_rne_of_the_exact_combination():
                 fp32_exact = np.float32(exact).astype(np.float64) == exact
                 assert np.array_equal(got[fp32_exact], want[fp32_exact]), (side, r)
                 assert fp32_exact.mean() > 0.99
+
+
+@pytest.mark.parametrize("M,N,K,dtype", [(400, 272, 144, "f16"), (600, 528, 512, "bf16")])
+def test_l1_ragged_group_tiles(M, N, K, dtype):
+    # quadrants that do not fill whole 128 x 128 group tiles (and a k tail in
+    # the first shape): the fused kernel's bounded loads and edge stores
+    say("l1 ragged", M, N, K, dtype)
+    dist = "uniform" if dtype == "f16" else "normal_sqrtk"
+    A, B, A64, B64 = gen(M, N, K, dtype, dist, seed=17)
+    C_ref = oracle.gemm(A64, B64)
+    e_c = check_float(classic(A, B), A64, B64, dtype, C_ref)
+    e_1 = check_float(planned(A, B, "l1"), A64, B64, dtype, C_ref, blocks=2)
+    assert e_1 <= 4 * e_c, (e_1, e_c)
+    idist = "int2" if dtype == "f16" else "int1"
+    A, B, A64, B64 = gen(M, N, min(K, 256), dtype, idist, seed=18)
+    check_exact(planned(A, B, "l1"), A64, B64, dtype)
 
 
 @pytest.mark.parametrize("split", ["none", "all"])
