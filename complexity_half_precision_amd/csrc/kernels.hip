@@ -641,10 +641,14 @@ struct QCfg {
     static constexpr int A_PER = A_BYTES / 1024 / LOADERS;
     static constexpr int B_PER = B_BYTES / 1024 / LOADERS;
     static constexpr int PER = A_PER + B_PER;                // DMA instructions per wave per k-tile
+    static constexpr int SROW = WTN * 2 + 8;                 // staged output row (padded: conflict-free)
+    static constexpr int EPI = NW * WTM * SROW;              // output staging, all waves
+    static constexpr int LDS_ALLOC = LDS > EPI ? LDS : EPI;
     static_assert(A_BYTES % (1024 * LOADERS) == 0 && B_BYTES % (1024 * LOADERS) == 0, "DMA split");
     static_assert(BROW % 256 == 0 && FM >= 1 && FN >= 1, "tile shape");
-    static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(LDS <= 160 * 1024 && EPI <= 160 * 1024, "LDS budget");
     static_assert(PER * (AHEAD - 1) < 64, "outstanding DMA count fits the 6-bit vmcnt");
+    static_assert(WTN % 128 == 0 || WTN == 64, "staged output rows of 8-column chunks");
 };
 
 // Fragments of one k-step (16 k) of a wave tile.
@@ -996,6 +1000,48 @@ __device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, AfterFn 
     }
 }
 
+// Output tile store through LDS.  Straight from the accumulators each store
+// instruction covers 32 rows with 8 bytes per lane; here each wave first
+// writes its bf16/f16 sub-tile into a private LDS region (rows padded by 8
+// bytes, so the 32 rows of a write land in distinct banks), then reads it
+// back a row segment at a time and stores 16 bytes per lane, WTN*2 bytes per
+// row contiguous.  The caller passes a barrier first: the regions overlap the
+// LDS ring other waves may still read.  rows / cols: valid extent from the
+// tile origin Cp (cols a multiple of 8 and Cp 16-byte aligned, ldc a
+// multiple of 8).
+template <class C, bool BF>
+__device__ __forceinline__ void store_c_staged(const f32x16 (&acc)[C::FM][C::FN], char* smem, u16* Cp, int64_t ldc,
+                                               int rows, int cols, int wave, int wm, int wn, int lane)
+{
+    char* reg = smem + wave * C::WTM * C::SROW;
+    const int r = lane & 31, hi = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int row = i * 32 + r, col = j * 32 + 8 * g + 4 * hi;
+                const u32x2 v{pack2<BF>(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
+                              pack2<BF>(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
+                *reinterpret_cast<u32x2*>(reg + row * C::SROW + col * 2) = v;
+            }
+    tiles::wait_lgkm0();
+    const rsrc_t rc = make_rsrc(Cp);
+    const int ld = (int)ldc;
+    constexpr int CHUNKS = C::WTN / 8;            // 16-byte chunks per staged row
+    constexpr int RPI = 64 / CHUNKS;              // rows per store instruction
+#pragma unroll
+    for (int r0 = 0; r0 < C::WTM; r0 += RPI) {
+        const int row = r0 + lane / CHUNKS, ch = lane % CHUNKS;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(reg + row * C::SROW + ch * 16);
+        const int m = wm * C::WTM + row, n = wn * C::WTN + ch * 8;
+        const u32 off = (m < rows && n < cols) ? (u32)(m * ld + n) * 2u : kOob;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v),
+                                               rc, off, 0, 0);
+    }
+}
+
 }  // namespace q4
 
 using QC256 = q4::QCfg<256, 256>;   // 4 waves of 128 x 128
@@ -1004,9 +1050,9 @@ using QC128 = q4::QCfg<128, 128>;   // 4 waves of 64 x 64
 template <class C, bool BF>
 __global__ void __launch_bounds__(C::NT, 1)
 k_classic_q4(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb, u16* __restrict__ Cm,
-             int64_t ldc, int M, int N, int K, int gy, int gx, int P, int vec4)
+             int64_t ldc, int M, int N, int K, int gy, int gx, int P, int vec4, int vec8)
 {
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_ALLOC];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN;
@@ -1028,7 +1074,10 @@ k_classic_q4(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, 
         q4::run_tile<C, BF, false, true>(smem, nk, src, none, wave, lane, ad, acc);
     else
         q4::run_tile<C, BF, true, false>(smem, nk, src, none, wave, lane, ad, acc);
-    if (vec4)
+    if (vec8) {
+        __syncthreads();
+        q4::store_c_staged<C, BF>(acc, smem, Cm + (int64_t)m0 * ldc + n0, ldc, M - m0, N - n0, wave, wm, wn, lane);
+    } else if (vec4)
         store_c<C, BF, true>(acc, Cm + (int64_t)m0 * ldc + n0, ldc, M - m0, N - n0, wm, wn, lane);
     else
         store_c<C, BF, false>(acc, Cm + (int64_t)m0 * ldc + n0, ldc, M - m0, N - n0, wm, wn, lane);
@@ -1041,9 +1090,10 @@ hipError_t launch_classic_q4_t(const ClassicLaunch& L, hipStream_t st)
     const long tiles = (long)gy * gx;
     if (tiles == 0)
         return hipSuccess;
+    const int vec8 = L.vec4 && ((uintptr_t)L.C % 16 == 0) && (L.ldc % 8 == 0) && (L.N % 8 == 0);
     hipLaunchKernelGGL((k_classic_q4<C, BF>), dim3((unsigned)tiles), dim3(C::NT), 0, st,
                        (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, (u16*)L.C, L.ldc, L.M, L.N, L.K,
-                       gy, gx, L.P, L.vec4);
+                       gy, gx, L.P, L.vec4, vec8);
     return hipGetLastError();
 }
 
