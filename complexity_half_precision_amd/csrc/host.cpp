@@ -284,6 +284,12 @@ struct lcma_plan_s {
     int blockA[kMaxRank], blockB[kMaxRank];     // block index of an in-place operand
     size_t ws_bytes;
     double est[4];
+    // unfused path (one level of any valid description)
+    int unfused;
+    int gms, gks, gns, gR;
+    int64_t gMb, gKb, gNb;
+    int8_t gU[kGenMaxRank * kGenMaxBlocks], gV[kGenMaxRank * kGenMaxBlocks], gW[kGenMaxRank * kGenMaxBlocks];
+    int64_t offGA, offGB, offGC;
 };
 
 static int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -341,22 +347,39 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     if (opts)
         o = *opts;
     if (o.split < LCMA_SPLIT_AUTO || o.split > LCMA_SPLIT_ALL || o.combine < LCMA_COMBINE_AUTO ||
-        o.combine > LCMA_COMBINE_AT_LOAD || o.num_cus < 0 || o.peak_tflops < 0 || o.hbm_gbps < 0 ||
+        o.combine > LCMA_COMBINE_UNFUSED || o.num_cus < 0 || o.peak_tflops < 0 || o.hbm_gbps < 0 ||
         o.bf16_ops_f16 < -1 || o.bf16_ops_f16 > 1 || !(o.classic_eff >= 0 && o.classic_eff <= 1) ||
         !(o.fused_eff >= 0 && o.fused_eff <= 1))
         return LCMA_E_INVALID;
 
-    // Which LCMA levels the description allows.
+    // Which LCMA levels the description allows.  A description that is not
+    // a built-in scheme runs one level of itself through the unfused path.
     bool allow_l1 = true, allow_l2 = true;
+    lcma_desc gen{};
+    std::call_once(g_tables_once, init_tables);
     if (desc) {
         if (!desc_shape_ok(desc) || !brent_ok(desc))
             return LCMA_E_BAD_DESCRIPTOR;
         const int kind = builtin_kind(desc);
-        allow_l1 = kind == 1;
         allow_l2 = kind == 1 || kind == 2;
+        if (kind == 1) {
+            gen = lcma_desc{2, 2, 2, 7, g_U1, g_V1, g_W1};
+        } else if (kind == 0) {
+            gen = *desc;
+            allow_l1 = desc->rank <= kGenMaxRank && desc->ms * desc->ks <= kGenMaxBlocks &&
+                       desc->ks * desc->ns <= kGenMaxBlocks && desc->ms * desc->ns <= kGenMaxBlocks;
+        } else {
+            allow_l1 = false;   // a two-level table: run it as L2 of the one-level scheme
+        }
+    } else {
+        gen = lcma_desc{2, 2, 2, 7, g_U1, g_V1, g_W1};
     }
+    const bool generic = desc && builtin_kind(desc) == 0;
+    const bool unfused = generic || o.combine == LCMA_COMBINE_UNFUSED;
     if (o.combine == LCMA_COMBINE_AT_LOAD)
         return LCMA_E_UNSUPPORTED;   // not built yet
+    if (generic && force == LCMA_ALGO_L2)
+        return LCMA_E_UNSUPPORTED;
 
     Machine m;
     m.peak = (o.peak_tflops > 0 ? o.peak_tflops : 2516.0) * 1e12;
@@ -396,11 +419,32 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         return Mb >= 1 && Nb >= 8 && Kb >= 8 && Nb % 8 == 0 && Kb % 8 == 0;
     };
 
+    // One level of the description on the unfused path: even block split,
+    // 16-byte rows, and 32-bit offsets into the fp32 output blocks.
+    auto admissible_unfused = [&]() -> bool {
+        if (M % gen.ms || N % gen.ns || K % gen.ks)
+            return false;
+        const int64_t Mb = M / gen.ms, Nb = N / gen.ns, Kb = K / gen.ks;
+        return Mb >= 1 && Nb >= 8 && Kb >= 8 && Nb % 8 == 0 && Kb % 8 == 0 && Nb <= ((int64_t)1 << 19);
+    };
+
     double est[4] = {-1, -1, -1, -1};
     est[LCMA_ALGO_CLASSIC] = est_classic(M, N, K, m);
-    bool ok1 = allow_l1 && admissible(1), ok2 = allow_l2 && admissible(2);
-    if (ok1)
+    bool ok1 = allow_l1 && (unfused ? admissible_unfused() : admissible(1));
+    bool ok2 = allow_l2 && !unfused && admissible(2);
+    if (ok1 && unfused) {
+        // pre-pass (every operand written), one GEMM per product, fp32
+        // read-modify-write of the touched output blocks, final cast
+        const int64_t Mb = M / gen.ms, Nb = N / gen.ns, Kb = K / gen.ks;
+        int nnzW = 0;
+        for (int x = 0; x < gen.rank * gen.ms * gen.ns; ++x)
+            nnzW += gen.W[x] != 0;
+        const double pre = 2.0 * ((double)M * K + (double)K * N) + 2.0 * gen.rank * ((double)Mb * Kb + (double)Kb * Nb);
+        const double comb = 8.0 * nnzW * (double)Mb * Nb + 6.0 * (double)M * N;
+        est[LCMA_ALGO_L1] = (pre + comb) / (m.eta_bw * m.bw) + gen.rank * est_classic(Mb, Nb, Kb, m) + 3 * m.launch;
+    } else if (ok1) {
         est[LCMA_ALGO_L1] = est_lcma(M, N, K, 1, o.split, op_bf16_for(1) != (dt == LCMA_BF16), m);
+    }
     if (ok2)
         est[LCMA_ALGO_L2] = est_lcma(M, N, K, 2, o.split, op_bf16_for(2) != (dt == LCMA_BF16), m);
 
@@ -415,7 +459,7 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         // combined operands to binary16 loses too much accuracy there.
         chosen = LCMA_ALGO_CLASSIC;
         double best = est[LCMA_ALGO_CLASSIC];
-        if (ok1 && est[LCMA_ALGO_L1] < 0.98 * best) {
+        if (ok1 && !unfused && est[LCMA_ALGO_L1] < 0.98 * best) {
             chosen = LCMA_ALGO_L1;
             best = est[LCMA_ALGO_L1];
         }
@@ -435,7 +479,33 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     p->levels = chosen == LCMA_ALGO_L1 ? 1 : chosen == LCMA_ALGO_L2 ? 2 : 0;
     p->ws_bytes = 0;
     p->n_slots = 0;
-    if (p->levels > 0) {
+    p->unfused = p->levels == 1 && unfused;
+    if (p->unfused) {
+        p->op_bf16 = op_bf16_for(1);
+        p->gms = gen.ms; p->gks = gen.ks; p->gns = gen.ns; p->gR = gen.rank;
+        p->gMb = M / gen.ms; p->gKb = K / gen.ks; p->gNb = N / gen.ns;
+        memset(p->gU, 0, sizeof p->gU);
+        memset(p->gV, 0, sizeof p->gV);
+        memset(p->gW, 0, sizeof p->gW);
+        for (int r = 0; r < gen.rank; ++r) {
+            for (int x = 0; x < gen.ms * gen.ks; ++x)
+                p->gU[r * kGenMaxBlocks + x] = gen.U[r * gen.ms * gen.ks + x];
+            for (int x = 0; x < gen.ks * gen.ns; ++x)
+                p->gV[r * kGenMaxBlocks + x] = gen.V[r * gen.ks * gen.ns + x];
+            for (int x = 0; x < gen.ms * gen.ns; ++x)
+                p->gW[r * kGenMaxBlocks + x] = gen.W[r * gen.ms * gen.ns + x];
+        }
+        // geometry of the one level (for lcma_plan_operand)
+        p->geo.Mb = p->gMb; p->geo.Kb = p->gKb; p->geo.Nb = p->gNb; p->geo.R = gen.rank; p->geo.S = 0;
+        int64_t off = 0;
+        p->offGA = off;
+        off = align_up(off + (int64_t)gen.rank * p->gMb * p->gKb * 2, 256);
+        p->offGB = off;
+        off = align_up(off + (int64_t)gen.rank * p->gKb * p->gNb * 2, 256);
+        p->offGC = off;
+        off = align_up(off + (int64_t)gen.ms * gen.ns * p->gMb * p->gNb * 4, 256);
+        p->ws_bytes = (size_t)off;
+    } else if (p->levels > 0) {
         const int L = p->levels;
         p->op_bf16 = op_bf16_for(L);
         p->write_all = p->op_bf16 != (dt == LCMA_BF16 ? 1 : 0);
@@ -530,6 +600,15 @@ lcma_status lcma_plan_operand(lcma_plan_t p, int32_t side, int32_t r, int64_t* o
 {
     if (!p || p->levels == 0 || side < 0 || side > 1 || r < 0 || r >= p->geo.R)
         return LCMA_E_INVALID;
+    if (p->unfused) {
+        if (offset)
+            *offset = side == 0 ? p->offGA + (int64_t)r * p->gMb * p->gKb * 2 : p->offGB + (int64_t)r * p->gKb * p->gNb * 2;
+        if (ld)
+            *ld = side == 0 ? p->gKb : p->gNb;
+        if (dtype)
+            *dtype = p->op_bf16 ? LCMA_BF16 : LCMA_F16;
+        return LCMA_OK;
+    }
     const int64_t slot = side == 0 ? p->slotA[r] : p->slotB[r];
     if (offset)
         *offset = slot < 0 ? -1
@@ -544,7 +623,7 @@ lcma_status lcma_plan_operand(lcma_plan_t p, int32_t side, int32_t r, int64_t* o
 
 lcma_status lcma_plan_schedule(lcma_plan_t p, int32_t* items, int64_t cap, int64_t* count, int32_t* order)
 {
-    if (!p || p->levels == 0 || !count || (cap > 0 && !items))
+    if (!p || p->levels == 0 || p->unfused || !count || (cap > 0 && !items))
         return LCMA_E_INVALID;
     int64_t n = 0;
     for (int w = 0; w < p->grid; ++w) {
@@ -679,6 +758,64 @@ lcma_status do_fused(const lcma_plan_s* p, const void* A, int64_t lda, const voi
     return launch_fused(L, st) == hipSuccess ? LCMA_OK : LCMA_E_HIP;
 }
 
+// Unfused path, pre-pass half: every combined operand of both sides.
+lcma_status do_gen_prepass(const lcma_plan_s* p, const void* A, int64_t lda, const void* B, int64_t ldb, void* ws,
+                           hipStream_t st)
+{
+    GenPrepassLaunch L;
+    memset(&L, 0, sizeof L);
+    L.in_bf16 = p->dt == LCMA_BF16;
+    L.op_bf16 = p->op_bf16;
+    L.rank = p->gR;
+    // side A: blocks (i, k) of Mb x Kb
+    L.X = A; L.ldx = lda; L.rows = (int32_t)p->gMb; L.cols = (int32_t)p->gKb; L.bcols = p->gks;
+    L.nblocks = p->gms * p->gks;
+    memcpy(L.coef, p->gU, sizeof L.coef);
+    L.out = (char*)ws + p->offGA; L.ldo = p->gKb; L.stride = p->gMb * p->gKb;
+    if (launch_gen_prepass(L, st) != hipSuccess)
+        return LCMA_E_HIP;
+    // side B: blocks (k, j) of Kb x Nb
+    L.X = B; L.ldx = ldb; L.rows = (int32_t)p->gKb; L.cols = (int32_t)p->gNb; L.bcols = p->gns;
+    L.nblocks = p->gks * p->gns;
+    memcpy(L.coef, p->gV, sizeof L.coef);
+    L.out = (char*)ws + p->offGB; L.ldo = p->gNb; L.stride = p->gKb * p->gNb;
+    return launch_gen_prepass(L, st) == hipSuccess ? LCMA_OK : LCMA_E_HIP;
+}
+
+// Unfused path, product half: clear the fp32 output blocks, one GEMM per
+// product adding W[r][i,j] * H_r into them, then round into C.
+lcma_status do_gen_products(const lcma_plan_s* p, void* C, int64_t ldc, void* ws, hipStream_t st)
+{
+    float* acc = (float*)((char*)ws + p->offGC);
+    const int nout = p->gms * p->gns;
+    if (launch_fill_f32(acc, (int64_t)nout * p->gMb * p->gNb, 0.0f, st) != hipSuccess)
+        return LCMA_E_HIP;
+    for (int r = 0; r < p->gR; ++r) {
+        GenProductLaunch L;
+        memset(&L, 0, sizeof L);
+        L.A = (const char*)ws + p->offGA + (int64_t)r * p->gMb * p->gKb * 2; L.lda = p->gKb;
+        L.B = (const char*)ws + p->offGB + (int64_t)r * p->gKb * p->gNb * 2; L.ldb = p->gNb;
+        L.M = (int32_t)p->gMb; L.N = (int32_t)p->gNb; L.K = (int32_t)p->gKb;
+        L.op_bf16 = p->op_bf16; L.P = p->P; L.ldt = p->gNb;
+        for (int o = 0; o < nout; ++o) {
+            const int w = p->gW[r * kGenMaxBlocks + o];
+            if (w != 0) {
+                L.tgt[L.ntgt] = acc + (int64_t)o * p->gMb * p->gNb;
+                L.w[L.ntgt] = (float)w;
+                ++L.ntgt;
+            }
+        }
+        if (L.ntgt == 0)
+            continue;
+        if (launch_gen_product(L, st) != hipSuccess)
+            return LCMA_E_HIP;
+    }
+    GenCastLaunch L;
+    L.src = acc; L.rows = (int32_t)p->gMb; L.cols = (int32_t)p->gNb; L.bcols = p->gns; L.nblocks = nout;
+    L.C = C; L.ldc = ldc; L.out_bf16 = p->dt == LCMA_BF16;
+    return launch_gen_cast(L, st) == hipSuccess ? LCMA_OK : LCMA_E_HIP;
+}
+
 lcma_status check_lcma_call(const lcma_plan_s* p, const void* A, int64_t lda, const void* B, int64_t ldb,
                             const void* C, int64_t ldc, void* ws, size_t ws_bytes, bool need_c, Io* io)
 {
@@ -731,6 +868,10 @@ lcma_status lcma_gemm(lcma_plan_t p, const void* A, int64_t lda, const void* B, 
     lcma_status s = check_lcma_call(p, A, lda, B, ldb, C, ldc, ws, ws_bytes, true, &io);
     if (s != LCMA_OK)
         return s;
+    if (p->unfused) {
+        s = do_gen_prepass(p, A, lda, B, ldb, ws, st);
+        return s != LCMA_OK ? s : do_gen_products(p, C, ldc, ws, st);
+    }
     s = do_prepass(p, A, lda, B, ldb, ws, st);
     if (s != LCMA_OK)
         return s;
@@ -746,6 +887,8 @@ lcma_status lcma_prepass(lcma_plan_t p, const void* A, int64_t lda, const void* 
     lcma_status s = check_lcma_call(p, A, lda, B, ldb, nullptr, 0, ws, ws_bytes, false, &io);
     if (s != LCMA_OK)
         return s;
+    if (p->unfused)
+        return do_gen_prepass(p, A, lda, B, ldb, ws, (hipStream_t)stream);
     return do_prepass(p, A, lda, B, ldb, ws, (hipStream_t)stream);
 }
 
@@ -758,6 +901,8 @@ lcma_status lcma_fused(lcma_plan_t p, const void* A, int64_t lda, const void* B,
     lcma_status s = check_lcma_call(p, A, lda, B, ldb, C, ldc, ws, ws_bytes, true, &io);
     if (s != LCMA_OK)
         return s;
+    if (p->unfused)
+        return do_gen_products(p, C, ldc, ws, (hipStream_t)stream);
     return do_fused(p, A, lda, B, ldb, C, ldc, io, ws, (hipStream_t)stream);
 }
 

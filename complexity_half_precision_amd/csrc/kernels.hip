@@ -33,6 +33,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <utility>
 
 #include "kernels.hpp"
@@ -1083,6 +1084,89 @@ k_classic_q4(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, 
         store_c<C, BF, false>(acc, Cm + (int64_t)m0 * ldc + n0, ldc, M - m0, N - n0, wm, wn, lane);
 }
 
+// One product of the unfused path: the same engine, with an epilogue that
+// adds w[t] * H into fp32 targets (read-modify-write, 16 bytes per lane)
+// instead of storing H.  Products run one after another on the stream, so
+// no two launches touch a target at the same time.
+struct GenTargets {
+    float* tgt[kGenMaxBlocks];
+    float w[kGenMaxBlocks];
+    int ntgt;
+    int64_t ldt;
+};
+
+template <class C, bool BF>
+__global__ void __launch_bounds__(C::NT, 1)
+k_gen_product(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb, int M, int N, int K,
+              int gy, int gx, int P, const GenTargets tg)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    int p, q;
+    tile_coords((int32_t)blockIdx.x, gy, gx, P, 8, &p, &q);
+    const int m0 = p * C::BM, n0 = q * C::BN;
+    const u16* Ab = A + (int64_t)m0 * lda;
+    const u16* Bb = B + n0;
+    const int nk = (K + C::BK - 1) / C::BK;
+    f32x16 acc[C::FM][C::FN];
+    zero_acc<C>(acc);
+    auto src = [&](int t) {
+        return tiles::TileSrc{Ab, (int)lda, M - m0, Bb, (int)ldb, N - n0, t * C::BK, K};
+    };
+    const q4::Addr<C> ad = q4::frag_addr<C>(wm, wn, lane);
+    auto none = [](int) {};
+    const bool inside = (m0 + C::BM <= M) & (n0 + C::BN <= N) & (K % C::BK == 0);
+    if (inside)
+        q4::run_tile<C, BF, false, true>(smem, nk, src, none, wave, lane, ad, acc);
+    else
+        q4::run_tile<C, BF, true, false>(smem, nk, src, none, wave, lane, ad, acc);
+    // lane l of MFMA tile (i, j) holds row (l % 32) and, per group g of 4
+    // accumulators, columns 8 g + 4 (l / 32) .. + 3
+    const int ld = (int)tg.ldt;
+    const int r = lane & 31, hi = lane >> 5;
+    for (int t = 0; t < tg.ntgt; ++t) {
+        const rsrc_t rt = make_rsrc(tg.tgt[t] + (int64_t)m0 * tg.ldt + n0);
+        const float wt = tg.w[t];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int m = wm * C::WTM + i * 32 + r, n = wn * C::WTN + j * 32 + 8 * g + 4 * hi;
+                    const u32 off = (m < M - m0 && n < N - n0) ? (u32)(m * ld + n) * 4u : kOob;
+                    f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0));
+                    v.x += wt * acc[i][j][4 * g];
+                    v.y += wt * acc[i][j][4 * g + 1];
+                    v.z += wt * acc[i][j][4 * g + 2];
+                    v.w += wt * acc[i][j][4 * g + 3];
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), rt, off, 0, 0);
+                }
+    }
+}
+
+template <class C, bool BF>
+hipError_t launch_gen_product_t(const GenProductLaunch& L, hipStream_t st)
+{
+    const int gy = (L.M + C::BM - 1) / C::BM, gx = (L.N + C::BN - 1) / C::BN;
+    const long tiles = (long)gy * gx;
+    if (tiles == 0)
+        return hipSuccess;
+    GenTargets tg{};
+    for (int t = 0; t < L.ntgt; ++t) {
+        tg.tgt[t] = L.tgt[t];
+        tg.w[t] = L.w[t];
+    }
+    tg.ntgt = L.ntgt;
+    tg.ldt = L.ldt;
+    hipLaunchKernelGGL((k_gen_product<C, BF>), dim3((unsigned)tiles), dim3(C::NT), 0, st, (const u16*)L.A, L.lda,
+                       (const u16*)L.B, L.ldb, L.M, L.N, L.K, gy, gx, L.P, tg);
+    return hipGetLastError();
+}
+
 template <class C, bool BF>
 hipError_t launch_classic_q4_t(const ClassicLaunch& L, hipStream_t st)
 {
@@ -1281,6 +1365,93 @@ hipError_t launch_skinny_t(const ClassicLaunch& L, hipStream_t st)
     hipLaunchKernelGGL((k_skinny<C, BF>), dim3((unsigned)gx), dim3(C::NT), 0, st, (const u16*)L.A, L.lda,
                        (const u16*)L.B, L.ldb, (u16*)L.C, L.ldc, L.M, L.N, L.K, L.vec4);
     return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ unfused path helpers
+
+// Runtime-coefficient pre-pass: one thread per 8-element chunk position of
+// one product's combined operand; it sums the chunk of every block with a
+// non-zero coefficient in fp32 (the coefficients are uniform) and rounds once.
+struct GenPrepassParams {
+    const u16* X;
+    int64_t ldx;
+    int rows, cols, bcols, nblocks, rank;
+    int8_t coef[kGenMaxRank * kGenMaxBlocks];
+    u16* out;
+    int64_t ldo, stride;
+};
+
+template <bool IBF, bool OBF>
+__global__ void __launch_bounds__(256) k_gen_prepass(const GenPrepassParams gp)
+{
+    const int r = blockIdx.y;                          // product
+    const int cpr = gp.cols / 8;                       // chunks per row
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= (int64_t)gp.rows * cpr)
+        return;
+    const int row = (int)(c / cpr), col = (int)(c % cpr) * 8;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int b = 0; b < gp.nblocks; ++b) {
+        const int w = gp.coef[r * kGenMaxBlocks + b];
+        if (w == 0)
+            continue;
+        const int br = b / gp.bcols, bc = b % gp.bcols;
+        const u16* src = gp.X + (int64_t)(br * gp.rows + row) * gp.ldx + (int64_t)bc * gp.cols + col;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+        const float fw = (float)w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += fw * h2f<IBF>((u16)(v[e] & 0xffffu));
+            acc[2 * e + 1] += fw * h2f<IBF>((u16)(v[e] >> 16));
+        }
+    }
+    const u32x4 o{pack2<OBF>(acc[0], acc[1]), pack2<OBF>(acc[2], acc[3]), pack2<OBF>(acc[4], acc[5]),
+                  pack2<OBF>(acc[6], acc[7])};
+    *reinterpret_cast<u32x4*>(gp.out + (int64_t)r * gp.stride + (int64_t)row * gp.ldo + col) = o;
+}
+
+template <bool IBF, bool OBF>
+hipError_t launch_gen_prepass_t(const GenPrepassLaunch& L, hipStream_t st)
+{
+    const int64_t chunks = (int64_t)L.rows * (L.cols / 8);
+    if (chunks == 0 || L.rank == 0)
+        return hipSuccess;
+    GenPrepassParams gp;
+    gp.X = (const u16*)L.X;
+    gp.ldx = L.ldx;
+    gp.rows = L.rows;
+    gp.cols = L.cols;
+    gp.bcols = L.bcols;
+    gp.nblocks = L.nblocks;
+    gp.rank = L.rank;
+    for (int i = 0; i < kGenMaxRank * kGenMaxBlocks; ++i)
+        gp.coef[i] = L.coef[i];
+    gp.out = (u16*)L.out;
+    gp.ldo = L.ldo;
+    gp.stride = L.stride;
+    hipLaunchKernelGGL((k_gen_prepass<IBF, OBF>), dim3((unsigned)((chunks + 255) / 256), (unsigned)L.rank), dim3(256),
+                       0, st, gp);
+    return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) k_fill_f32(float* __restrict__ p, int64_t n, float v)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        p[i] = v;
+}
+
+template <bool BF>
+__global__ void __launch_bounds__(256) k_gen_cast(const float* __restrict__ src, int rows, int cols, int bcols,
+                                                  int nblocks, u16* __restrict__ C, int64_t ldc)
+{
+    const int64_t per = (int64_t)rows * cols;
+    const int64_t n = per * nblocks;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int b = (int)(i / per);
+        const int64_t e = i % per;
+        const int row = (int)(e / cols), col = (int)(e % cols);
+        C[(int64_t)((b / bcols) * rows + row) * ldc + (int64_t)(b % bcols) * cols + col] = f2h<BF>(src[i]);
+    }
 }
 
 // ------------------------------------------------------------------ fused group kernel
@@ -1636,6 +1807,45 @@ hipError_t launch_fused(const FusedLaunch& L, hipStream_t st)
     if (L.out_bf16)
         return L.op_bf16 ? launch_fused_t<2, true, true>(L, st) : launch_fused_t<2, false, true>(L, st);
     return launch_fused_t<2, false, false>(L, st);
+}
+
+hipError_t launch_gen_prepass(const GenPrepassLaunch& L, hipStream_t st)
+{
+    if (L.in_bf16)
+        return L.op_bf16 ? launch_gen_prepass_t<true, true>(L, st) : launch_gen_prepass_t<true, false>(L, st);
+    return L.op_bf16 ? launch_gen_prepass_t<false, true>(L, st) : launch_gen_prepass_t<false, false>(L, st);
+}
+
+hipError_t launch_gen_product(const GenProductLaunch& L, hipStream_t st)
+{
+    const int64_t t256 = (int64_t)((L.M + 255) / 256) * ((L.N + 255) / 256);
+    if (t256 >= L.P)
+        return L.op_bf16 ? launch_gen_product_t<QC256, true>(L, st) : launch_gen_product_t<QC256, false>(L, st);
+    return L.op_bf16 ? launch_gen_product_t<QC128, true>(L, st) : launch_gen_product_t<QC128, false>(L, st);
+}
+
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st)
+{
+    if (n <= 0)
+        return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)blocks), dim3(256), 0, st, p, n, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_gen_cast(const GenCastLaunch& L, hipStream_t st)
+{
+    const int64_t n = (int64_t)L.rows * L.cols * L.nblocks;
+    if (n <= 0)
+        return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
+    if (L.out_bf16)
+        hipLaunchKernelGGL(k_gen_cast<true>, dim3((unsigned)blocks), dim3(256), 0, st, L.src, L.rows, L.cols, L.bcols,
+                           L.nblocks, (u16*)L.C, L.ldc);
+    else
+        hipLaunchKernelGGL(k_gen_cast<false>, dim3((unsigned)blocks), dim3(256), 0, st, L.src, L.rows, L.cols,
+                           L.bcols, L.nblocks, (u16*)L.C, L.ldc);
+    return hipGetLastError();
 }
 
 }  // namespace lcma

@@ -68,6 +68,41 @@ struct FusedLaunch {
     int32_t grid;
 };
 // Workgroup tile edge of the fused kernel for a level (1: 128, 2: 64).
+// ---- unfused path for any valid description (one level of it)
+constexpr int kGenMaxRank = 64;     // products
+constexpr int kGenMaxBlocks = 16;   // blocks per side (ms*ks, ks*ns, ms*ns)
+
+// Combined operands of one side: out_r = sum_b coef[r][b] * X_b (fp32 sum,
+// one rounding), for every product r.  Block b of X sits at block row
+// b / bcols, block column b % bcols, each rows x cols.
+struct GenPrepassLaunch {
+    const void* X; int64_t ldx;
+    int32_t rows, cols, bcols, nblocks, rank;
+    int8_t coef[kGenMaxRank * kGenMaxBlocks];
+    void* out; int64_t ldo, stride;        // out_r at out + r * stride (elements)
+    int32_t in_bf16, op_bf16;
+};
+hipError_t launch_gen_prepass(const GenPrepassLaunch& L, hipStream_t stream);
+
+// One product H = Ahat * Bhat (M x N x K) whose epilogue adds w[t] * H into
+// fp32 targets t (each M x N, leading dimension ldt), in place of storing H.
+struct GenProductLaunch {
+    const void* A; int64_t lda;
+    const void* B; int64_t ldb;
+    int32_t M, N, K, op_bf16, P;
+    float* tgt[kGenMaxBlocks]; float w[kGenMaxBlocks]; int32_t ntgt; int64_t ldt;
+};
+hipError_t launch_gen_product(const GenProductLaunch& L, hipStream_t stream);
+
+// fp32 fill, and the final cast: block t (row t / bcols, column t % bcols) of
+// nblocks fp32 blocks (rows x cols, ld = cols) to C in the storage type.
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
+struct GenCastLaunch {
+    const float* src; int32_t rows, cols, bcols, nblocks;
+    void* C; int64_t ldc; int32_t out_bf16;
+};
+hipError_t launch_gen_cast(const GenCastLaunch& L, hipStream_t stream);
+
 int32_t fused_tile(int32_t levels);
 // Bytes of one split partial (all output blocks of one group, fp32).
 int64_t fused_partial_bytes(int32_t levels);

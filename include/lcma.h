@@ -79,7 +79,12 @@ typedef enum {
 typedef enum {
     LCMA_COMBINE_AUTO = 0,
     LCMA_COMBINE_PREPASS = 1, /* a separate bandwidth-bound pass writes each combined operand to the workspace */
-    LCMA_COMBINE_AT_LOAD = 2  /* the fused kernel forms the combinations while staging tiles (one-level only) */
+    LCMA_COMBINE_AT_LOAD = 2, /* the fused kernel forms the combinations while staging tiles (one-level only) */
+    LCMA_COMBINE_UNFUSED = 3  /* one level only: every combined operand is written, each product runs as its own
+                                 GEMM whose epilogue adds W[r][i,j] * H_r into fp32 output blocks in the
+                                 workspace (H_r is never stored), and a final pass rounds them into C.  The path
+                                 for descriptions that are not a built-in scheme, and the unfused ablation of
+                                 the fused path for the built-in one */
 } lcma_combine;
 
 /*
@@ -135,8 +140,12 @@ lcma_status lcma_desc_validate(const lcma_desc* desc);
 /* Plans C = A * B for an M x N x K product of storage type dt.
  *   desc:  NULL = built-in Strassen schemes; otherwise validated
  *          (LCMA_E_BAD_DESCRIPTOR) and deep-copied.  A description that is
- *          not one of the built-in schemes is LCMA_E_UNSUPPORTED when an
- *          LCMA path is forced, and is ignored by LCMA_ALGO_AUTO.
+ *          not one of the built-in schemes runs one level of itself through
+ *          the unfused path (LCMA_COMBINE_UNFUSED) when LCMA_ALGO_L1 is
+ *          forced (up to 64 products and 16 blocks per side; larger ones are
+ *          LCMA_E_UNSUPPORTED); LCMA_ALGO_AUTO picks classic for it, and
+ *          LCMA_ALGO_L2 is LCMA_E_UNSUPPORTED.  One level of a description
+ *          (ms, ks, ns) needs M, K, N divisible by ms, ks, ns.
  *   force: LCMA_ALGO_AUTO lets the roofline cost model pick among the
  *          admissible algorithms (ties go to classic);
  *          a forced L1/L2 on a shape it cannot split returns
@@ -198,7 +207,8 @@ lcma_status lcma_plan_operand(lcma_plan_t plan, int32_t side, int32_t r, int64_t
  * end product position (in the kernel's product order), split slot (-1 for
  * a whole group).  *count receives the total number of items (call with
  * cap = 0 to size).  *order (if not NULL, `rank` entries) receives the
- * kernel's product order.  LCMA_E_INVALID for a classic plan. */
+ * kernel's product order.  LCMA_E_INVALID for a classic plan and for an
+ * unfused one (it has no persistent schedule). */
 lcma_status lcma_plan_schedule(lcma_plan_t plan, int32_t* items, int64_t cap, int64_t* count,
                                int32_t* order);
 

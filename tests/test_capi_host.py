@@ -15,6 +15,7 @@ import pytest
 
 import complexity_half_precision_amd as L
 import oracle
+import descriptors as D
 import seeded_inputs as si
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -71,15 +72,59 @@ def test_validator_agrees_with_oracle_brent_on_corruptions():
     assert L.lcma_desc_validate(L.Desc(2, 2, 2, bad, V, W)) == L.E_BAD_DESCRIPTOR
 
 
-def test_naive_descriptor_validates_but_is_not_a_fused_scheme():
+def test_non_builtin_descriptors_plan_the_unfused_path():
+    # a valid description that is not a built-in scheme: one level of it, unfused
     d = oracle.naive()
     desc = L.Desc(2, 2, 2, d.U, d.V, d.W)
     assert L.lcma_desc_validate(desc) == L.OK
-    with pytest.raises(L.LcmaError) as e:
-        L.lcma_plan_ex(512, 512, 512, "f16", desc=desc, force="l1", num_cus=CUS)
-    assert e.value.status == L.E_UNSUPPORTED
+    p = L.lcma_plan_ex(512, 512, 768, "f16", desc=desc, force="l1", num_cus=CUS)
+    algo, ws, est = L.lcma_plan_info(p)
+    assert algo == "l1" and est > 0
+    # every combined operand written (8 per side), then 4 fp32 output blocks
+    Mb, Nb, Kb = 256, 256, 384
+    off_a, ld_a, _ = L.lcma_plan_operand(p, 0, 3)
+    off_b, ld_b, _ = L.lcma_plan_operand(p, 1, 0)
+    assert (off_a, ld_a) == (3 * Mb * Kb * 2, Kb) and ld_b == Nb and off_b == 8 * Mb * Kb * 2
+    assert ws == 8 * Mb * Kb * 2 + 8 * Kb * Nb * 2 + 4 * Mb * Nb * 4
+    with pytest.raises(L.LcmaError):
+        L.lcma_plan_schedule(p)
+    # automatic planning never picks it; two levels of it are not built
     p = L.lcma_plan_ex(512, 512, 512, "f16", desc=desc, force="auto", num_cus=CUS)
     assert L.lcma_plan_info(p)[0] == "classic"
+    with pytest.raises(L.LcmaError) as e:
+        L.lcma_plan_ex(512, 512, 512, "f16", desc=desc, force="l2", num_cus=CUS)
+    assert e.value.status == L.E_UNSUPPORTED
+    # more blocks per side than the unfused path takes
+    big = oracle.naive(4, 4, 5)
+    with pytest.raises(L.LcmaError) as e:
+        L.lcma_plan_ex(512, 640, 512, "f16", desc=L.Desc(4, 4, 5, big.U, big.V, big.W), force="l1", num_cus=CUS)
+    assert e.value.status == L.E_UNSUPPORTED
+
+
+def test_winograd_variant_validates_in_library_and_oracle():
+    d = oracle.Desc(2, 2, 2, D.WINOGRAD_U, D.WINOGRAD_V, D.WINOGRAD_W)
+    assert oracle.brent_violations(d) == 0
+    desc = L.Desc(2, 2, 2, D.WINOGRAD_U, D.WINOGRAD_V, D.WINOGRAD_W)
+    assert L.lcma_desc_validate(desc) == L.OK
+    # every single-entry change breaks it, in both checkers
+    for T in range(3):
+        for x in range(28):
+            tabs = [D.WINOGRAD_U.copy(), D.WINOGRAD_V.copy(), D.WINOGRAD_W.copy()]
+            t = tabs[T].reshape(-1)
+            t[x] = (int(t[x]) + 2) % 3 - 1 if t[x] != 0 else 1
+            bad_o = oracle.Desc(2, 2, 2, *tabs)
+            assert oracle.brent_violations(bad_o) > 0
+            assert L.lcma_desc_validate(L.Desc(2, 2, 2, *tabs)) == L.E_BAD_DESCRIPTOR
+    p = L.lcma_plan_ex(1024, 1024, 1024, "bf16", desc=desc, force="l1", num_cus=CUS)
+    assert L.lcma_plan_info(p)[0] == "l1"
+
+
+def test_builtin_scheme_can_be_forced_unfused():
+    p = L.lcma_plan_ex(1024, 1024, 1024, "bf16", force="l1", combine="unfused", num_cus=CUS)
+    algo, ws, _ = L.lcma_plan_info(p)
+    assert algo == "l1" and ws == 7 * 512 * 512 * 2 * 2 + 4 * 512 * 512 * 4
+    with pytest.raises(L.LcmaError):
+        L.lcma_plan_ex(1024, 1024, 1024, "bf16", force="l2", combine="unfused", num_cus=CUS)
 
 
 def test_plan_rejects_bad_descriptor():

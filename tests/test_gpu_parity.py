@@ -14,6 +14,7 @@ import torch
 import complexity_half_precision_amd as L
 import oracle
 import seeded_inputs as si
+import descriptors as D
 from oracle import metrics
 
 pytestmark = pytest.mark.gpu
@@ -273,6 +274,61 @@ def test_l1_tail_split_shapes(n):
     ref = np.stack([oracle.gemm_rows(A64, B64, r, r + 1)[0] for r in rows])
     assert metrics.e_rel(C[rows], ref) <= 4 * metrics.UNIT_ROUNDOFF["bf16"]
     assert metrics.freivalds(C, A64, B64) <= 4 * metrics.UNIT_ROUNDOFF["bf16"]
+
+
+# ---------------------------------------------------------------- unfused path (any valid description)
+
+def winograd():
+    return L.Desc(2, 2, 2, D.WINOGRAD_U, D.WINOGRAD_V, D.WINOGRAD_W)
+
+
+def planned_desc(A, B, desc, **kw):
+    M, K = A.shape
+    N = B.shape[1]
+    plan = L.lcma_plan_ex(M, N, K, A.dtype, desc=desc, force="l1", **kw)
+    assert L.lcma_plan_info(plan)[0] == "l1"
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    C = torch.full((M, N), 5.0, dtype=A.dtype, device=DEV)
+    ws = L.workspace_for(plan)
+    L.lcma_gemm(plan, Ad, Bd, C, ws)
+    torch.cuda.synchronize()
+    return C.cpu()
+
+
+@pytest.mark.parametrize("M,N,K,dtype", [(1024, 1024, 1024, "bf16"), (512, 768, 640, "f16"), (400, 272, 144, "f16")])
+def test_unfused_winograd_variant_matches_oracle(M, N, K, dtype):
+    say("unfused winograd", M, N, K, dtype)
+    dist = "uniform" if dtype == "f16" else "normal_sqrtk"
+    A, B, A64, B64 = gen(M, N, K, dtype, dist, seed=31)
+    C_ref = oracle.gemm(A64, B64)
+    e_c = check_float(classic(A, B), A64, B64, dtype, C_ref)
+    e_w = check_float(planned_desc(A, B, winograd()), A64, B64, dtype, C_ref, blocks=2)
+    assert e_w <= 4 * e_c, (e_w, e_c)
+    # against the oracle's evaluation of the same description with operands
+    # rounded to the operand type: only the fp32 order and the final rounding differ
+    dw = oracle.Desc(2, 2, 2, D.WINOGRAD_U, D.WINOGRAD_V, D.WINOGRAD_W)
+    C_sh, n = oracle.lcma(A64, B64, dw, 1, round_operands=dtype)
+    assert n == 7
+    assert metrics.e_rel(si.f64(planned_desc(A, B, winograd())), C_sh) <= 2 * metrics.UNIT_ROUNDOFF[dtype]
+    idist = "int2" if dtype == "f16" else "int1"
+    A, B, A64, B64 = gen(M, N, min(K, 256), dtype, idist, seed=32)
+    check_exact(planned_desc(A, B, winograd()), A64, B64, dtype)
+
+
+def test_unfused_builtin_and_naive_descriptions():
+    say("unfused builtin / naive")
+    A, B, A64, B64 = gen(768, 512, 1024, "bf16", "normal_sqrtk", seed=33)
+    C_ref = oracle.gemm(A64, B64)
+    e_c = check_float(classic(A, B), A64, B64, "bf16", C_ref)
+    e_f = check_float(planned(A, B, "l1"), A64, B64, "bf16", C_ref, blocks=2)
+    e_u = check_float(planned(A, B, "l1", combine="unfused"), A64, B64, "bf16", C_ref, blocks=2)
+    assert e_u <= 4 * e_c and e_f <= 4 * e_c
+    d8 = oracle.naive()
+    e_n = check_float(planned_desc(A, B, L.Desc(2, 2, 2, d8.U, d8.V, d8.W)), A64, B64, "bf16", C_ref, blocks=2)
+    assert e_n <= 2 * e_c
+    A, B, A64, B64 = gen(512, 512, 256, "f16", "int2", seed=34)
+    check_exact(planned(A, B, "l1", combine="unfused"), A64, B64, "f16")
+    check_exact(planned_desc(A, B, L.Desc(2, 2, 2, d8.U, d8.V, d8.W)), A64, B64, "f16")
 
 
 # ---------------------------------------------------------------- two levels

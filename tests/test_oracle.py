@@ -12,6 +12,7 @@ import torch
 
 import oracle
 from oracle import metrics
+import descriptors as D
 
 
 # ----------------------------------------------------------------------------- encodings
@@ -315,3 +316,21 @@ def test_freivalds_detects_one_wrong_entry():
     assert metrics.freivalds(C, A, B) < 1e-13
     C[17, 3] += 1.0
     assert metrics.freivalds(C, A, B) > 1e-3
+
+
+def test_winograd_variant_evaluates_exactly_and_differs_from_strassen():
+    # a second rank-7 description: Brent-valid, 7 block products, exact on
+    # integers at one and two levels, and not the same table as Strassen's
+    d = oracle.Desc(2, 2, 2, D.WINOGRAD_U, D.WINOGRAD_V, D.WINOGRAD_W)
+    assert oracle.brent_violations(d) == 0
+    s = oracle.strassen()
+    assert not (np.array_equal(d.U, s.U) and np.array_equal(d.V, s.V) and np.array_equal(d.W, s.W))
+    rng = np.random.default_rng(4)
+    A = rng.integers(-3, 4, (12, 20)).astype(np.float64)
+    B = rng.integers(-3, 4, (20, 8)).astype(np.float64)
+    C, n = oracle.lcma(A, B, d, 1)
+    assert n == 7 and np.array_equal(C, A @ B)
+    A = rng.integers(-2, 3, (16, 16)).astype(np.float64)
+    B = rng.integers(-2, 3, (16, 16)).astype(np.float64)
+    C, n = oracle.lcma(A, B, d, 2)
+    assert n == 49 and np.array_equal(C, A @ B)
