@@ -138,11 +138,14 @@ def main():
     detail = {}
     only = set(a for a in args.only.split(",") if a)
     plans = {}
-    for algo in ("classic", "l1", "l2"):
+    for algo in ("classic", "l1", "l2", "l1_unfused"):
         if only and algo not in only:
             continue
         try:
-            p = L.lcma_plan_ex(M, N, K, dtype, force=algo)
+            if algo == "l1_unfused":
+                p = L.lcma_plan_ex(M, N, K, dtype, force="l1", combine="unfused")
+            else:
+                p = L.lcma_plan_ex(M, N, K, dtype, force=algo)
         except L.LcmaError:
             continue
         plans[algo] = (p, L.workspace_for(p))
@@ -155,8 +158,8 @@ def main():
             t_pre = time_calls(lambda: L.lcma_prepass(p, Ad, Bd, ws), reps, args.warmup)
             L.lcma_prepass(p, Ad, Bd, ws)
             t_fu = time_calls(lambda: L.lcma_fused(p, Ad, Bd, C, ws), reps, args.warmup)
-            R = 7 if algo == "l1" else 49
-            S = 2 if algo == "l1" else 4
+            R = 49 if algo == "l2" else 7
+            S = 4 if algo == "l2" else 2
             mfma_flops = 2.0 * R * (M // S) * (N // S) * (K // S)
             # bytes the pre-pass must move: read A and B once, write the combined operands
             written = sum(1 for r in range(R) if L.lcma_plan_operand(p, 0, r)[0] >= 0) * (M // S) * (K // S) \
@@ -224,6 +227,9 @@ def main():
     }
     if "l1" in detail and "classic" in detail:
         out["l1_over_classic"] = round(detail["classic"]["ms"] / detail["l1"]["ms"], 4)
+    if "l1" in detail and "l1_unfused" in detail:
+        # the fusion gain: same scheme, products folded on chip vs through fp32 blocks in HBM
+        out["fused_over_unfused"] = round(detail["l1_unfused"]["ms"] / detail["l1"]["ms"], 4)
 
     if not args.no_extra and not args.size:
         del Ad, Bd, C, plans
