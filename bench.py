@@ -200,7 +200,7 @@ def main():
     if chosen == "classic":
         t_k = detail["classic"]["ms"]
         achieved = flops / (t_k * 1e-3) / 1e12
-        kname, kprefix = "k_classic_q4 (256x256 tile, 2MNK flops per launch)", "k_classic_q4"
+        kname, kprefix = "k_classic_m16 (256x256 tile, 8 waves, 16x16x32 MFMA; 2MNK flops per launch)", "k_classic_m16"
     else:
         t_k = detail[chosen]["fused_ms"]
         achieved = detail[chosen]["fused_mfma_tflop"] * 1e12 / (t_k * 1e-3) / 1e12

@@ -1045,6 +1045,309 @@ __device__ __forceinline__ void store_c_staged(const f32x16 (&acc)[C::FM][C::FN]
 
 }  // namespace q4
 
+// ------------------------------------------------------------------ 16x16 engine
+//
+// The direct-to-LDS engine on v_mfma_f32_16x16x32: on random bf16 data
+// 16x16x32 MFMAs sustain about 15% more flops than 32x32x16 (the chip holds
+// a higher clock).  Eight waves, two per SIMD, each own 128 x 64 of a
+// 256 x 256 tile: 32 accumulator tiles (128 registers) per wave, which the
+// compiler keeps in place (64 tiles per wave it does not).  A k-tile of 32
+// is one MFMA k-step, so fragments are double-buffered across k-tiles: the
+// reads of tile t+1 are slotted among tile t's MFMAs, and the other wave of
+// the SIMD covers their latency.
+
+namespace m16 {
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, BK = 32, WM = WM_, WN = WN_, MT = 16;
+    static constexpr int NSTAGE = 4, AHEAD = 3;
+    static constexpr int NW = WM * WN;
+    static constexpr int NT = NW * 64;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int FM = WTM / 16, FN = WTN / 16;
+    using acc_t = f32x4;
+    static constexpr int NACC = 4;
+    static constexpr int AROW = BK * 2;
+    static constexpr int BROW = BN * 2;
+    static constexpr int A_BYTES = BM * AROW;
+    static constexpr int B_BYTES = BK * BROW;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int LDS = NSTAGE * STAGE;
+    static constexpr int LOADERS = NW;
+    static constexpr int A_PER = A_BYTES / 1024 / LOADERS;
+    static constexpr int B_PER = B_BYTES / 1024 / LOADERS;
+    static constexpr int PER = A_PER + B_PER;
+    static constexpr int SROW = WTN * 2 + 8;
+    static constexpr int EPI = NW * WTM * SROW;
+    static constexpr int LDS_ALLOC = LDS > EPI ? LDS : EPI;
+    static_assert(A_BYTES % (1024 * LOADERS) == 0 && B_BYTES % (1024 * LOADERS) == 0, "DMA split");
+    static_assert(BROW % 256 == 0 && FM >= 1 && FN >= 1, "tile shape");
+    static_assert(LDS <= 160 * 1024 && EPI <= 160 * 1024, "LDS budget");
+    static_assert(PER * (AHEAD - 1) < 64, "vmcnt range");
+    static_assert(WTN % 128 == 0 || WTN == 64, "staged output rows of 8-column chunks");
+};
+
+// Per-lane LDS offsets of a wave's fragments within a stage.  A fragment i:
+// row wm*WTM + 16 i + (lane % 16), 8 k from chunk lane / 16 (chunks XOR-
+// swizzled by row).  B fragment j, half h: a transposed read whose source
+// lane s (of each 16-lane group g) points at k row 8g + 4h + s/4, column
+// wn*WTN + 16 j + 4 (s % 4); lane l then holds B[8g+4h .. +3][16 j + l % 16].
+template <class C>
+struct Addr {
+    u32 a0;
+    u32 b[C::FN];
+};
+
+template <class C>
+__device__ __forceinline__ Addr<C> frag_addr(int wm, int wn, int lane)
+{
+    Addr<C> ad;
+    const u32 m = wm * C::WTM + (lane & 15);
+    ad.a0 = m * (u32)C::AROW + ((((u32)lane >> 4) ^ tiles::a_swz(m)) << 4);
+    const int g = lane >> 4, s = lane & 15;
+    const u32 kr = 8 * g + (s >> 2);
+    const u32 xb = tiles::b_swz(kr);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+        const u32 n = wn * C::WTN + j * 16 + 4 * (s & 3);
+        ad.b[j] = C::A_BYTES + kr * C::BROW + (((n >> 3) ^ xb) << 4) + (n & 7) * 2;
+    }
+    return ad;
+}
+
+template <class C>
+__device__ __forceinline__ void read_a(const char* stage, const Addr<C>& ad, int i, u32x4& a)
+{
+    a = *reinterpret_cast<const u32x4*>(stage + ad.a0 + i * 16 * C::AROW);
+}
+
+// Both halves of B fragment j, straight into its register quad.
+template <class C>
+__device__ __forceinline__ void read_b(const char* stage, const Addr<C>& ad, int j, u32x4& b)
+{
+    const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) tiles::s16x4*)(stage + ad.b[j])));
+    const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) tiles::s16x4*)(stage + ad.b[j] + 4 * C::BROW)));
+    b = u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
+// One k-tile: MFMA (i, j) = A fragment i x B fragment j, i outer.  A is
+// single-buffered: the next tile's A fragment i is read right after the
+// last MFMA that uses the current one.  B is double-buffered (Bc -> Bn), its
+// reads slotted after the first FN MFMAs.  With PRE the loads of tile t+3
+// follow in later slots.
+template <class C, bool BF, bool NEXT, bool PRE, bool EDGE, bool GROUPED>
+__device__ __forceinline__ void ktile(u32x4 (&Af)[C::FM], const u32x4 (&Bc)[C::FN], u32x4 (&Bn)[C::FN],
+                                      const char* nxt, char* pre, const tiles::TileSrc& ps, const q4::Group<C>& go,
+                                      const Addr<C>& ad, int wave, int lane, f32x4 (&acc)[C::FM][C::FN])
+{
+    constexpr int NMF = C::FM * C::FN;
+    constexpr int L0 = C::FN + 1;                   // first load slot
+    static_assert(L0 + 2 * (C::PER - 1) < NMF, "load slots");
+#pragma unroll
+    for (int x = 0; x < NMF; ++x) {
+        const int i = x / C::FN, j = x % C::FN;
+        acc[i][j] = mfma<BF>(Bc[j], Af[i], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (NEXT) {
+            if (x < C::FN)
+                read_b<C>(nxt, ad, x, Bn[x]);
+            if (j == C::FN - 1)
+                read_a<C>(nxt, ad, i, Af[i]);
+        }
+        if constexpr (PRE) {
+            const int y = x - L0;
+            if (y >= 0 && (y & 1) == 0 && y / 2 < C::PER) {
+                const int k = y / 2;
+                if constexpr (GROUPED) {
+                    if (k == 0)
+                        q4::dma_group<C>(pre, ps, go, wave, 0);
+                    else if (k == C::PER / 2)
+                        q4::dma_group<C>(pre, ps, go, wave, 1);
+                } else {
+                    q4::dma_one<C, EDGE>(pre, ps, wave, lane, k);
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// K loop of one output tile (same contract as q4::run_tile).
+template <class C, bool BF, bool EDGE, bool GROUPED, class SrcFn, class AfterFn>
+__device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, AfterFn after, int wave, int lane,
+                                         const Addr<C>& ad, f32x4 (&acc)[C::FM][C::FN])
+{
+    static_assert(C::AHEAD == 3 && C::NSTAGE == 4, "stage reuse below assumes a 4-stage ring, 3 ahead");
+    static_assert(!(GROUPED && EDGE), "grouped loads carry no bounds");
+    u32x4 Af[C::FM], B0[C::FN], B1[C::FN];
+    q4::Group<C> go;
+    if constexpr (GROUPED)
+        go = q4::group_offsets<C>(src(0), wave, lane);
+#pragma unroll
+    for (int t = 0; t < C::AHEAD; ++t) {
+        if (t < nk) {
+            if constexpr (GROUPED) {
+                q4::dma_group<C>(smem + t * C::STAGE, src(t), go, wave, 0);
+                q4::dma_group<C>(smem + t * C::STAGE, src(t), go, wave, 1);
+            } else {
+                q4::dma_tile<C, EDGE>(smem + t * C::STAGE, src(t), wave, lane);
+            }
+        }
+    }
+    q4::wait_tiles<C>(min(nk, C::AHEAD) - 1);
+    tiles::bar();
+    if (nk > 0) {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+            read_a<C>(smem, ad, i, Af[i]);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+            read_b<C>(smem, ad, j, B0[j]);
+    }
+    // Top of k-tile t: tile t+1 has landed and every wave has finished with
+    // tile t-1's stage, which then takes tile t+3.
+    auto steady = [&](int t, const u32x4 (&Bc)[C::FN], u32x4 (&Bn)[C::FN]) {
+        q4::wait_vm<C::PER>();
+        tiles::wait_lgkm0();
+        tiles::bar();
+        __builtin_amdgcn_sched_barrier(0);
+        const tiles::TileSrc ps = src(t + C::AHEAD);
+        ktile<C, BF, true, true, EDGE, GROUPED>(Af, Bc, Bn, smem + ((t + 1) % C::NSTAGE) * C::STAGE,
+                                                smem + ((t + C::AHEAD) % C::NSTAGE) * C::STAGE, ps, go, ad, wave,
+                                                lane, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        after(t);
+    };
+    int t = 0;
+    // Steady state, two k-tiles per trip so the B buffers alternate without
+    // copies; both tiles have a successor and a tile to prefetch.
+    for (; t + 1 + C::AHEAD < nk; t += 2) {
+        steady(t, B0, B1);
+        steady(t + 1, B1, B0);
+    }
+    // At most AHEAD + 1 k-tiles remain; Af and B0 hold tile t's fragments.
+    // Plain order: the MFMAs, then the next tile's reads (not overlapped).
+    for (; t < nk; ++t) {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                acc[i][j] = mfma<BF>(B0[j], Af[i], acc[i][j]);
+        after(t);
+        if (t + 1 < nk) {
+            // issued so far: tiles up to min(t+2, nk-1); tile t+1 must have landed
+            q4::wait_tiles<C>(min(nk - 2 - t, 1));
+            tiles::wait_lgkm0();
+            tiles::bar();
+            if (t + C::AHEAD < nk) {
+                const tiles::TileSrc ps = src(t + C::AHEAD);
+                char* pre = smem + ((t + C::AHEAD) % C::NSTAGE) * C::STAGE;
+                if constexpr (GROUPED) {
+                    q4::dma_group<C>(pre, ps, go, wave, 0);
+                    q4::dma_group<C>(pre, ps, go, wave, 1);
+                } else {
+                    q4::dma_tile<C, EDGE>(pre, ps, wave, lane);
+                }
+            }
+            const char* nxt = smem + ((t + 1) % C::NSTAGE) * C::STAGE;
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+                read_a<C>(nxt, ad, i, Af[i]);
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                read_b<C>(nxt, ad, j, B0[j]);
+        }
+    }
+}
+
+// Output tile store through LDS (16x16 accumulator layout: lane l of tile
+// (i, j) holds row 16 i + l % 16, columns 16 j + 4 (l / 16) .. + 3).
+template <class C, bool BF>
+__device__ __forceinline__ void store_c_staged(const f32x4 (&acc)[C::FM][C::FN], char* smem, u16* Cp, int64_t ldc,
+                                               int rows, int cols, int wave, int wm, int wn, int lane)
+{
+    char* reg = smem + wave * C::WTM * C::SROW;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+            const int row = i * 16 + (lane & 15), col = j * 16 + 4 * (lane >> 4);
+            const u32x2 v{pack2<BF>(acc[i][j][0], acc[i][j][1]), pack2<BF>(acc[i][j][2], acc[i][j][3])};
+            *reinterpret_cast<u32x2*>(reg + row * C::SROW + col * 2) = v;
+        }
+    tiles::wait_lgkm0();
+    const rsrc_t rc = make_rsrc(Cp);
+    const int ld = (int)ldc;
+    constexpr int CHUNKS = C::WTN / 8;
+    constexpr int RPI = 64 / CHUNKS;
+#pragma unroll
+    for (int r0 = 0; r0 < C::WTM; r0 += RPI) {
+        const int row = r0 + lane / CHUNKS, ch = lane % CHUNKS;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(reg + row * C::SROW + ch * 16);
+        const int m = wm * C::WTM + row, n = wn * C::WTN + ch * 8;
+        const u32 off = (m < rows && n < cols) ? (u32)(m * ld + n) * 2u : kOob;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v),
+                                               rc, off, 0, 0);
+    }
+}
+
+}  // namespace m16
+
+using MC256 = m16::Cfg<256, 256, 2, 4>;   // 8 waves (2 per SIMD) of 128 x 64, 16x16x32 MFMAs
+
+template <class C, bool BF>
+__global__ void __launch_bounds__(C::NT, 1)
+k_classic_m16(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb, u16* __restrict__ Cm,
+              int64_t ldc, int M, int N, int K, int gy, int gx, int P, int vec4, int vec8)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_ALLOC];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    int p, q;
+    tile_coords((int32_t)blockIdx.x, gy, gx, P, 8, &p, &q);
+    const int m0 = p * C::BM, n0 = q * C::BN;
+    const u16* Ab = A + (int64_t)m0 * lda;
+    const u16* Bb = B + n0;
+    const int nk = (K + C::BK - 1) / C::BK;
+    f32x4 acc[C::FM][C::FN];
+    zero_acc<C>(acc);
+    auto src = [&](int t) {
+        return tiles::TileSrc{Ab, (int)lda, M - m0, Bb, (int)ldb, N - n0, t * C::BK, K};
+    };
+    const m16::Addr<C> ad = m16::frag_addr<C>(wm, wn, lane);
+    const bool inside = (m0 + C::BM <= M) & (n0 + C::BN <= N) & (K % C::BK == 0);
+    auto none = [](int) {};
+    if (inside)
+        m16::run_tile<C, BF, false, true>(smem, nk, src, none, wave, lane, ad, acc);
+    else
+        m16::run_tile<C, BF, true, false>(smem, nk, src, none, wave, lane, ad, acc);
+    if (vec8) {
+        __syncthreads();
+        m16::store_c_staged<C, BF>(acc, smem, Cm + (int64_t)m0 * ldc + n0, ldc, M - m0, N - n0, wave, wm, wn, lane);
+    } else if (vec4)
+        store_c<C, BF, true>(acc, Cm + (int64_t)m0 * ldc + n0, ldc, M - m0, N - n0, wm, wn, lane);
+    else
+        store_c<C, BF, false>(acc, Cm + (int64_t)m0 * ldc + n0, ldc, M - m0, N - n0, wm, wn, lane);
+}
+
+template <class C, bool BF>
+hipError_t launch_classic_m16_t(const ClassicLaunch& L, hipStream_t st)
+{
+    const int gy = (L.M + C::BM - 1) / C::BM, gx = (L.N + C::BN - 1) / C::BN;
+    const long tiles = (long)gy * gx;
+    if (tiles == 0)
+        return hipSuccess;
+    const int vec8 = L.vec4 && ((uintptr_t)L.C % 16 == 0) && (L.ldc % 8 == 0) && (L.N % 8 == 0);
+    hipLaunchKernelGGL((k_classic_m16<C, BF>), dim3((unsigned)tiles), dim3(C::NT), 0, st,
+                       (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, (u16*)L.C, L.ldc, L.M, L.N, L.K,
+                       gy, gx, L.P, L.vec4, vec8);
+    return hipGetLastError();
+}
+
 using QC256 = q4::QCfg<256, 256>;   // 4 waves of 128 x 128
 using QC128 = q4::QCfg<128, 128>;   // 4 waves of 64 x 64
 
@@ -1738,7 +2041,7 @@ hipError_t launch_classic(const ClassicLaunch& L, hipStream_t st)
     switch (L.tile) {
     case kTile256:
         if (L.vec)
-            return L.bf16 ? launch_classic_q4_t<QC256, true>(L, st) : launch_classic_q4_t<QC256, false>(L, st);
+            return L.bf16 ? launch_classic_m16_t<MC256, true>(L, st) : launch_classic_m16_t<MC256, false>(L, st);
         return launch_classic_c<Cfg256>(L, st);
     case kTile128:
         if (L.vec)
