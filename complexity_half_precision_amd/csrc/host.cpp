@@ -387,11 +387,11 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     m.l2bw = 8.0 * 2048.0 * 2.4e9;
     m.launch = 4e-6;
     // Sustained fractions of the MFMA peak measured on MI355X (256 CUs) for
-    // the kernels as they stand: classic 256x256 tiles 0.45-0.53 over
-    // 4096^3..16384^3; fused one-level group kernel about 0.175; fused
+    // the kernels as they stand: classic 256x256 tiles 0.50-0.55 over
+    // 4096^3..16384^3; fused one-level group kernel about 0.31; fused
     // two-level kernel about 0.037.
-    m.eta_mfma = o.classic_eff > 0 ? o.classic_eff : 0.48;
-    m.eta_fused1 = o.fused_eff > 0 ? o.fused_eff : 0.175;
+    m.eta_mfma = o.classic_eff > 0 ? o.classic_eff : 0.52;
+    m.eta_fused1 = o.fused_eff > 0 ? o.fused_eff : 0.31;
     m.eta_fused2 = o.fused_eff > 0 ? o.fused_eff : 0.037;
     m.eta_bw = 0.8;
     if (o.num_cus > 0) {

@@ -1,14 +1,16 @@
 // kernels.hip -- gfx950 (MI355X) kernels of the half-precision GEMM library.
 //
-//  * k_classic_q4 -- classic GEMM, C = A * B (fp32 accumulate, one RNE cast),
-//                    256 x 256 tiles on the four-wave engine (one wave per
-//                    SIMD, 128 x 128 per wave, direct-to-LDS loads).
+//  * k_classic_m16 -- classic GEMM, C = A * B (fp32 accumulate, one RNE
+//                    cast), 256 x 256 tiles, 8 waves of 128 x 64 on 16x16x32
+//                    MFMAs, direct-to-LDS loads.
+//  * k_classic_q4 -- the same for 128 x 128 tiles: 4 waves (one per SIMD) of
+//                    64 x 64 on 32x32x16 MFMAs.
 //  * k_skinny     -- M <= 64 products, built to stream B from HBM.
 //  * k_classic    -- register-staged tiles for the other shapes and for
 //                    operands that are not 16-byte aligned.
 //  * k_prepass    -- combine-A/B pass: every combined operand of an LCMA scheme,
 //                    summed in fp32 and rounded once to the operand type.
-//  * k_fused1_q4  -- persistent one-level group kernel on the four-wave engine:
+//  * k_fused1_m16 -- persistent one-level group kernel on the 16x16x32 engine:
 //                    the 7 products of one output coordinate accumulate into
 //                    the 4 output tiles in registers (fp32), no product is
 //                    written to memory; tail groups may be split over two
@@ -649,7 +651,7 @@ struct QCfg {
     static_assert(BROW % 256 == 0 && FM >= 1 && FN >= 1, "tile shape");
     static_assert(LDS <= 160 * 1024 && EPI <= 160 * 1024, "LDS budget");
     static_assert(PER * (AHEAD - 1) < 64, "outstanding DMA count fits the 6-bit vmcnt");
-    static_assert(WTN % 128 == 0 || WTN == 64, "staged output rows of 8-column chunks");
+    static_assert(WTN % 8 == 0 && 64 % (WTN / 8) == 0 || WTN % 512 == 0, "staged output rows of 8-column chunks");
 };
 
 // Fragments of one k-step (16 k) of a wave tile.
@@ -745,7 +747,7 @@ struct Group {
 template <class C>
 __device__ __forceinline__ Group<C> group_offsets(const tiles::TileSrc& s, int xw, int lane)
 {
-    static_assert(C::A_PER == C::B_PER && (C::A_PER == 2 || C::A_PER == 4), "loads per group");
+    static_assert(C::A_PER == C::B_PER && (C::A_PER == 1 || C::A_PER == 2 || C::A_PER == 4), "loads per group");
     Group<C> g;
 #pragma unroll
     for (int i = 0; i < C::A_PER; ++i) {
@@ -768,8 +770,10 @@ __device__ __forceinline__ Group<C> group_offsets(const tiles::TileSrc& s, int x
 template <int N>
 __device__ __forceinline__ void dma16xN(u32x4 rs, const u32 (&off)[N], u32 lds)
 {
-    static_assert(N == 2 || N == 4, "group size");
-    if constexpr (N == 4)
+    static_assert(N == 1 || N == 2 || N == 4, "group size");
+    if constexpr (N == 1)
+        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(off[0]), "s"(rs), "{m0}"(lds) : "memory");
+    else if constexpr (N == 4)
         asm volatile("s_nop 0\n\t"
                      "buffer_load_dwordx4 %0, %4, 0 offen lds\n\t"
                      "buffer_load_dwordx4 %1, %4, 0 offen offset:1024 lds\n\t"
@@ -1085,7 +1089,7 @@ struct Cfg {
     static_assert(BROW % 256 == 0 && FM >= 1 && FN >= 1, "tile shape");
     static_assert(LDS <= 160 * 1024 && EPI <= 160 * 1024, "LDS budget");
     static_assert(PER * (AHEAD - 1) < 64, "vmcnt range");
-    static_assert(WTN % 128 == 0 || WTN == 64, "staged output rows of 8-column chunks");
+    static_assert(WTN % 8 == 0 && 64 % (WTN / 8) == 0 || WTN % 512 == 0, "staged output rows of 8-column chunks");
 };
 
 // Per-lane LDS offsets of a wave's fragments within a stage.  A fragment i:
@@ -1926,16 +1930,18 @@ __global__ void __launch_bounds__(FusedCfg<LEVELS>::C::NT) k_fused(const FusedPa
 // back through the DMA ring; after each product's last k-tile every wave folds
 // its H sub-tile into its four output sub-tiles.
 
-using QCF1 = QC128;                 // fused one-level group tile
+using MCF1 = m16::Cfg<128, 128, 2, 4>;   // fused one-level group tile: 8 waves of 64 x 32
 
-// Fused one-level group kernel on the four-wave engine: the products of a
-// work item stream back to back through the same LDS ring (the prefetch runs
-// across product boundaries); at each product's last k-tile every wave folds
-// H into its four fp32 output sub-tiles.
+// Fused one-level group kernel on the 16x16x32 engine: 8 waves (two per
+// SIMD) of 64 x 32, each holding four fp32 output sub-tiles plus H (160
+// accumulator registers).  The products of a work item stream back to back
+// through the same LDS ring (the prefetch runs across product boundaries);
+// at each product's last k-tile every wave folds H into its four output
+// sub-tiles.
 template <bool OBF, bool CBF>
-__global__ void __launch_bounds__(QCF1::NT, 1) k_fused1_q4(const FusedParams fp)
+__global__ void __launch_bounds__(MCF1::NT, 1) k_fused1_m16(const FusedParams fp)
 {
-    using C = QCF1;
+    using C = MCF1;
     constexpr int NOUT = 4;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
     __shared__ int sh_old;
@@ -1954,11 +1960,11 @@ __global__ void __launch_bounds__(QCF1::NT, 1) k_fused1_q4(const FusedParams fp)
         int p, q;
         tile_coords(item.g, fp.sp.gy, fp.sp.gx, fp.sp.P, fp.sp.raster, &p, &q);
         const int m0 = p * C::BM, n0 = q * C::BN;
-        f32x16 Cacc[NOUT][C::FM][C::FN];
+        f32x4 Cacc[NOUT][C::FM][C::FN];
 #pragma unroll
         for (int o = 0; o < NOUT; ++o)
             zero_acc<C>(Cacc[o]);
-        f32x16 H[C::FM][C::FN];
+        f32x4 H[C::FM][C::FN];
         zero_acc<C>(H);
         const int nprod = item.pos1 - item.pos0;
         const int ntiles = nprod * nk;
@@ -1992,12 +1998,12 @@ __global__ void __launch_bounds__(QCF1::NT, 1) k_fused1_q4(const FusedParams fp)
                 ++aj;
             }
         };
-        const q4::Addr<C> ad = q4::frag_addr<C>(wm, wn, lane);
+        const m16::Addr<C> ad = m16::frag_addr<C>(wm, wn, lane);
         const bool inside = (m0 + C::BM <= fp.Mb) & (n0 + C::BN <= fp.Nb) & (fp.Kb % C::BK == 0);
         if (inside)
-            q4::run_tile<C, OBF, false, false>(smem, ntiles, src, after, wave, lane, ad, H);
+            m16::run_tile<C, OBF, false, false>(smem, ntiles, src, after, wave, lane, ad, H);
         else
-            q4::run_tile<C, OBF, true, false>(smem, ntiles, src, after, wave, lane, ad, H);
+            m16::run_tile<C, OBF, true, false>(smem, ntiles, src, after, wave, lane, ad, H);
         __syncthreads();
         fused_epilogue<NOUT, C, CBF>(fp, item, m0, n0, Cacc, tid, wm, wn, lane, &sh_old);
         __syncthreads();
@@ -2005,11 +2011,11 @@ __global__ void __launch_bounds__(QCF1::NT, 1) k_fused1_q4(const FusedParams fp)
 }
 
 template <bool OBF, bool CBF>
-hipError_t launch_fused1_q4(const FusedLaunch& L, hipStream_t st)
+hipError_t launch_fused1_m16(const FusedLaunch& L, hipStream_t st)
 {
     if (L.grid <= 0)
         return hipSuccess;
-    hipLaunchKernelGGL((k_fused1_q4<OBF, CBF>), dim3(L.grid), dim3(QCF1::NT), 0, st, L.p);
+    hipLaunchKernelGGL((k_fused1_m16<OBF, CBF>), dim3(L.grid), dim3(MCF1::NT), 0, st, L.p);
     return hipGetLastError();
 }
 
@@ -2072,15 +2078,15 @@ hipError_t launch_prepass(const PrepassLaunch& L, hipStream_t st)
     return launch_prepass_t<2, false, false, false>(L, st);
 }
 
-int32_t fused_tile(int32_t levels) { return levels == 1 ? QCF1::BM : FusedCfg<2>::C::BM; }
-static_assert(QCF1::BM == QCF1::BN, "fused tiles are square");
+int32_t fused_tile(int32_t levels) { return levels == 1 ? MCF1::BM : FusedCfg<2>::C::BM; }
+static_assert(MCF1::BM == MCF1::BN, "fused tiles are square");
 static_assert(FusedCfg<1>::C::BM == FusedCfg<1>::C::BN && FusedCfg<2>::C::BM == FusedCfg<2>::C::BN,
               "fused tiles are square");
 
 int64_t fused_partial_bytes(int32_t levels)
 {
     if (levels == 1)
-        return (int64_t)4 * QCF1::BM * QCF1::BN * 4;
+        return (int64_t)4 * MCF1::BM * MCF1::BN * 4;
     using C = FusedCfg<2>::C;
     return (int64_t)16 * C::BM * C::BN * 4;
 }
@@ -2104,8 +2110,8 @@ hipError_t launch_fused(const FusedLaunch& L, hipStream_t st)
 {
     if (L.levels == 1) {
         if (L.out_bf16)
-            return L.op_bf16 ? launch_fused1_q4<true, true>(L, st) : launch_fused1_q4<false, true>(L, st);
-        return launch_fused1_q4<false, false>(L, st);
+            return L.op_bf16 ? launch_fused1_m16<true, true>(L, st) : launch_fused1_m16<false, true>(L, st);
+        return launch_fused1_m16<false, false>(L, st);
     }
     if (L.out_bf16)
         return L.op_bf16 ? launch_fused_t<2, true, true>(L, st) : launch_fused_t<2, false, true>(L, st);

@@ -118,9 +118,9 @@ typedef struct {
     double peak_tflops;     /* 0 = 2516 (dense fp16/bf16 MFMA: 256 CUs x 4096 FLOP/clk x 2.4 GHz) */
     double hbm_gbps;        /* 0 = 8000 */
     double classic_eff;     /* fraction of peak_tflops the classic kernel sustains when compute-bound;
-                               0 = 0.48 (measured on MI355X at 4096^3 .. 16384^3) */
+                               0 = 0.52 (measured on MI355X at 4096^3 .. 16384^3) */
     double fused_eff;       /* the same for the fused group kernel (both levels);
-                               0 = 0.175 for one level, 0.037 for two levels (measured) */
+                               0 = 0.31 for one level, 0.037 for two levels (measured) */
 } lcma_options;
 
 typedef struct lcma_plan_s* lcma_plan_t;
