@@ -62,6 +62,12 @@ def parse():
                     help="only the decode-shape bandwidth measurement (one JSON line), for profiling runs")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the decode-shape bandwidth and 24-shape sweep measurements")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time every kernel with the caches flushed before each call (writes a 512 MiB "
+                         "buffer between calls, outside the timed region)")
+    ap.add_argument("--server", action="store_true",
+                    help="also time every algorithm in server mode: single calls separated by seeded random "
+                         "host-side gaps of 0.2-2 ms (mean and median of the per-call event times)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="first run 3 device copies of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -135,6 +141,43 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
+
+    def time_cold(fn, reps):
+        """Mean ms of fn with L2 and the last-level cache flushed before each call:
+        a 512 MiB write (twice the MI355X last-level cache) between calls; only fn
+        is inside the events."""
+        tot = 0.0
+        for _ in range(reps):
+            flush_buf.fill_(1)
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            tot += e0.elapsed_time(e1)
+        return tot / reps
+
+    def time_gapped(fn, reps, seed=1234):
+        """Per-call event times of fn, each call issued after the device went idle and
+        the host slept a seeded random gap of 0.2-2 ms: the clock and cache state a
+        server sees between requests, rather than back-to-back."""
+        import random
+        import time as _time
+        rng = random.Random(seed)
+        ts = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            _time.sleep(rng.uniform(0.2e-3, 2e-3))
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        return sum(ts) / len(ts), ts[len(ts) // 2]
+
     detail = {}
     only = set(a for a in args.only.split(",") if a)
     plans = {}
@@ -168,6 +211,14 @@ def main():
             d.update({"prepass_ms": t_pre, "fused_ms": t_fu, "fused_mfma_tflop": mfma_flops / 1e12,
                       "fused_tflops_actual": mfma_flops / (t_fu * 1e-3) / 1e12,
                       "prepass_bytes": pre_bytes, "prepass_gbps": pre_bytes / (t_pre * 1e-3) / 1e9})
+        if args.cold:
+            reps_c = min(reps, 20)
+            d["cold_ms"] = time_cold(lambda: L.lcma_gemm(p, Ad, Bd, C, ws), reps_c)
+            if algo != "classic":
+                t_pre_c = time_cold(lambda: L.lcma_prepass(p, Ad, Bd, ws), reps_c)
+                d.update({"cold_prepass_ms": t_pre_c, "cold_prepass_gbps": d["prepass_bytes"] / (t_pre_c * 1e-3) / 1e9})
+        if args.server:
+            d["server_mean_ms"], d["server_p50_ms"] = time_gapped(lambda: L.lcma_gemm(p, Ad, Bd, C, ws), 50)
         detail[algo] = d
 
     # ---- the step: plan + planned product on the workload
