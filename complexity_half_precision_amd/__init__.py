@@ -20,6 +20,12 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build it with `python {os.path.join(_HERE, 'build.py')}` "
         "(there is no fallback implementation)")
 
+# torch first: its wheel carries its own HIP runtime, and the library must bind
+# to that one.  Loaded before torch, the library would pull in the system HIP
+# runtime as a second copy in the process, which then finds no device and
+# cannot use torch's allocations.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ---------------------------------------------------------------- constants (lcma.h)

@@ -101,18 +101,28 @@ int builtin_kind(const lcma_desc* d)
 
 // ---------------------------------------------------------------- device facts
 
+bool log_enabled();
+
 int query_cus(int* out)
 {
     static std::mutex mu;
     static int cached[64] = {0};
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= 64) {
+        if (log_enabled())
+            fprintf(stderr, "lcma: hipGetDevice: %s (device %d)\n", hipGetErrorName(e), dev);
         return -1;
+    }
     std::lock_guard<std::mutex> lock(mu);
     if (!cached[dev]) {
         int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+        e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess || v <= 0) {
+            if (log_enabled())
+                fprintf(stderr, "lcma: hipDeviceGetAttribute(CU count): %s (%d)\n", hipGetErrorName(e), v);
             return -1;
+        }
         cached[dev] = v;
     }
     *out = cached[dev];
@@ -127,6 +137,17 @@ bool log_enabled()
         v = (e && *e && *e != '0') ? 1 : 0;
     }
     return v == 1;
+}
+
+// A HIP call's result as a library status; with LCMA_LOG set, a failure
+// prints the HIP error name and the call that returned it.
+lcma_status hip_status(hipError_t e, const char* what)
+{
+    if (e == hipSuccess)
+        return LCMA_OK;
+    if (log_enabled())
+        fprintf(stderr, "lcma: %s: %s (%s)\n", what, hipGetErrorName(e), hipGetErrorString(e));
+    return LCMA_E_HIP;
 }
 
 // ---------------------------------------------------------------- cost model
@@ -685,7 +706,7 @@ lcma_status run_classic(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const vo
     L.A = A; L.lda = lda; L.B = B; L.ldb = ldb; L.C = C; L.ldc = ldc;
     L.M = (int32_t)M; L.N = (int32_t)N; L.K = (int32_t)K;
     L.bf16 = dt == LCMA_BF16; L.vec = io.vec; L.vec4 = io.vec4; L.tile = tile; L.P = P;
-    return launch_classic(L, st) == hipSuccess ? LCMA_OK : LCMA_E_HIP;
+    return hip_status(launch_classic(L, st), "launch_classic");
 }
 
 lcma_status check_ws(const lcma_plan_s* p, void* ws, size_t ws_bytes)
@@ -713,7 +734,7 @@ lcma_status do_prepass(const lcma_plan_s* p, const void* A, int64_t lda, const v
     L.write_all = p->write_all;
     L.counters = (int32_t*)((char*)ws + p->offCtr);
     L.n_counters = p->n_slots;
-    return launch_prepass(L, st) == hipSuccess ? LCMA_OK : LCMA_E_HIP;
+    return hip_status(launch_prepass(L, st), "launch_prepass");
 }
 
 lcma_status do_fused(const lcma_plan_s* p, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
@@ -755,7 +776,7 @@ lcma_status do_fused(const lcma_plan_s* p, const void* A, int64_t lda, const voi
     L.op_bf16 = p->op_bf16;
     L.out_bf16 = p->dt == LCMA_BF16;
     L.grid = p->grid;
-    return launch_fused(L, st) == hipSuccess ? LCMA_OK : LCMA_E_HIP;
+    return hip_status(launch_fused(L, st), "launch_fused");
 }
 
 // Unfused path, pre-pass half: every combined operand of both sides.
@@ -772,14 +793,14 @@ lcma_status do_gen_prepass(const lcma_plan_s* p, const void* A, int64_t lda, con
     L.nblocks = p->gms * p->gks;
     memcpy(L.coef, p->gU, sizeof L.coef);
     L.out = (char*)ws + p->offGA; L.ldo = p->gKb; L.stride = p->gMb * p->gKb;
-    if (launch_gen_prepass(L, st) != hipSuccess)
+    if (hip_status(launch_gen_prepass(L, st), "launch_gen_prepass") != LCMA_OK)
         return LCMA_E_HIP;
     // side B: blocks (k, j) of Kb x Nb
     L.X = B; L.ldx = ldb; L.rows = (int32_t)p->gKb; L.cols = (int32_t)p->gNb; L.bcols = p->gns;
     L.nblocks = p->gks * p->gns;
     memcpy(L.coef, p->gV, sizeof L.coef);
     L.out = (char*)ws + p->offGB; L.ldo = p->gNb; L.stride = p->gKb * p->gNb;
-    return launch_gen_prepass(L, st) == hipSuccess ? LCMA_OK : LCMA_E_HIP;
+    return hip_status(launch_gen_prepass(L, st), "launch_gen_prepass");
 }
 
 // Unfused path, product half: clear the fp32 output blocks, one GEMM per
@@ -788,7 +809,7 @@ lcma_status do_gen_products(const lcma_plan_s* p, void* C, int64_t ldc, void* ws
 {
     float* acc = (float*)((char*)ws + p->offGC);
     const int nout = p->gms * p->gns;
-    if (launch_fill_f32(acc, (int64_t)nout * p->gMb * p->gNb, 0.0f, st) != hipSuccess)
+    if (hip_status(launch_fill_f32(acc, (int64_t)nout * p->gMb * p->gNb, 0.0f, st), "launch_fill_f32") != LCMA_OK)
         return LCMA_E_HIP;
     for (int r = 0; r < p->gR; ++r) {
         GenProductLaunch L;
@@ -807,13 +828,13 @@ lcma_status do_gen_products(const lcma_plan_s* p, void* C, int64_t ldc, void* ws
         }
         if (L.ntgt == 0)
             continue;
-        if (launch_gen_product(L, st) != hipSuccess)
+        if (hip_status(launch_gen_product(L, st), "launch_gen_product") != LCMA_OK)
             return LCMA_E_HIP;
     }
     GenCastLaunch L;
     L.src = acc; L.rows = (int32_t)p->gMb; L.cols = (int32_t)p->gNb; L.bcols = p->gns; L.nblocks = nout;
     L.C = C; L.ldc = ldc; L.out_bf16 = p->dt == LCMA_BF16;
-    return launch_gen_cast(L, st) == hipSuccess ? LCMA_OK : LCMA_E_HIP;
+    return hip_status(launch_gen_cast(L, st), "launch_gen_cast");
 }
 
 lcma_status check_lcma_call(const lcma_plan_s* p, const void* A, int64_t lda, const void* B, int64_t ldb,

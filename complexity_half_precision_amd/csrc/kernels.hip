@@ -652,6 +652,10 @@ struct QCfg {
     static_assert(LDS <= 160 * 1024 && EPI <= 160 * 1024, "LDS budget");
     static_assert(PER * (AHEAD - 1) < 64, "outstanding DMA count fits the 6-bit vmcnt");
     static_assert(WTN % 8 == 0 && 64 % (WTN / 8) == 0 || WTN % 512 == 0, "staged output rows of 8-column chunks");
+    // LDS swizzles (XOR on the 16-byte chunk index of a row): the 32x32x16
+    // fragment reads below hit distinct banks with these.
+    __device__ static u32 a_swz(u32 m) { return tiles::a_swz(m); }
+    __device__ static u32 b_swz(u32 k) { return tiles::b_swz(k); }
 };
 
 // Fragments of one k-step (16 k) of a wave tile.
@@ -709,7 +713,7 @@ __device__ __forceinline__ void dma_one(char* stage, const tiles::TileSrc& s, in
     if (i < C::A_PER) {
         const int ins = xw * C::A_PER + i;
         const int r = ins * 16 + (lane >> 2);
-        const int k = ((lane & 3) ^ (int)tiles::a_swz(r)) * 8;
+        const int k = ((lane & 3) ^ (int)C::a_swz(r)) * 8;
         const u32 off0 = (u32)(r * s.lda + k) * 2u;
         const u32 off = !EDGE || ((r < s.a_rows) & (k < kleft)) ? off0 : kOob;
         dma16(rsrc_words(s.a + s.k0), off, base + ins * 1024);
@@ -717,7 +721,7 @@ __device__ __forceinline__ void dma_one(char* stage, const tiles::TileSrc& s, in
         const int ins = xw * C::B_PER + (i - C::A_PER);
         const int byte = ins * 1024 + lane * 16;
         const int r = byte / C::BROW;
-        const int n = (((byte % C::BROW) >> 4) ^ (int)tiles::b_swz(r)) * 8;
+        const int n = (((byte % C::BROW) >> 4) ^ (int)C::b_swz(r)) * 8;
         const u32 off0 = (u32)(r * s.ldb + n) * 2u;
         const u32 off = !EDGE || ((r < kleft) & (n < s.b_cols)) ? off0 : kOob;
         dma16(rsrc_words(s.b + (int64_t)s.k0 * s.ldb), off, base + C::A_BYTES + ins * 1024);
@@ -753,7 +757,7 @@ __device__ __forceinline__ Group<C> group_offsets(const tiles::TileSrc& s, int x
     for (int i = 0; i < C::A_PER; ++i) {
         const int ins = xw * C::A_PER + i;
         const int r = ins * 16 + (lane >> 2);
-        const int k = ((lane & 3) ^ (int)tiles::a_swz(r)) * 8;
+        const int k = ((lane & 3) ^ (int)C::a_swz(r)) * 8;
         g.a[i] = (u32)(r * s.lda + k) * 2u - 1024u * i;
     }
 #pragma unroll
@@ -761,7 +765,7 @@ __device__ __forceinline__ Group<C> group_offsets(const tiles::TileSrc& s, int x
         const int ins = xw * C::B_PER + i;
         const int byte = ins * 1024 + lane * 16;
         const int r = byte / C::BROW;
-        const int n = (((byte % C::BROW) >> 4) ^ (int)tiles::b_swz(r)) * 8;
+        const int n = (((byte % C::BROW) >> 4) ^ (int)C::b_swz(r)) * 8;
         g.b[i] = (u32)(r * s.ldb + n) * 2u - 1024u * i;
     }
     return g;
@@ -842,11 +846,11 @@ __device__ __forceinline__ Addr<C> frag_addr(int wm, int wn, int lane)
 {
     Addr<C> ad;
     const u32 m = wm * C::WTM + (lane & 31);
-    const u32 f = tiles::a_swz(m);
+    const u32 f = C::a_swz(m);
     ad.a0 = m * (u32)C::AROW + ((((lane >> 5) ^ f) & 1u) << 4) + ((f & 2u) << 4);
     const int g = lane >> 4, s = lane & 15;
     const u32 kr = 8 * (g >> 1) + (s >> 2);
-    const u32 xb = tiles::b_swz(kr);
+    const u32 xb = C::b_swz(kr);
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
         const u32 n = wn * C::WTN + j * 32 + 16 * (g & 1) + 4 * (s & 3);
@@ -1090,6 +1094,15 @@ struct Cfg {
     static_assert(LDS <= 160 * 1024 && EPI <= 160 * 1024, "LDS budget");
     static_assert(PER * (AHEAD - 1) < 64, "vmcnt range");
     static_assert(WTN % 8 == 0 && 64 % (WTN / 8) == 0 || WTN % 512 == 0, "staged output rows of 8-column chunks");
+    // LDS swizzles (XOR on the 16-byte chunk index of a row), both measured
+    // conflict-free on gfx950 for the fragment reads below.  A: the 16-byte
+    // read of rows 0..15 x chunks 0..3 runs at the full 256 B/clk with chunk
+    // (lane/16) ^ ((m >> 1) & 3); the (m >> 2) & 3 that suits the 32x32
+    // reads reaches only 58% of it.  B: a transposed read pairs k rows r and
+    // r + 8 in one access, so bit 3 of the row joins the swizzle (without it
+    // the read runs at 3/4 rate).
+    __device__ static u32 a_swz(u32 m) { return (m >> 1) & 3u; }
+    __device__ static u32 b_swz(u32 k) { return (4u * (k & 3u)) ^ (2u * ((k >> 3) & 1u)); }
 };
 
 // Per-lane LDS offsets of a wave's fragments within a stage.  A fragment i:
@@ -1108,10 +1121,10 @@ __device__ __forceinline__ Addr<C> frag_addr(int wm, int wn, int lane)
 {
     Addr<C> ad;
     const u32 m = wm * C::WTM + (lane & 15);
-    ad.a0 = m * (u32)C::AROW + ((((u32)lane >> 4) ^ tiles::a_swz(m)) << 4);
+    ad.a0 = m * (u32)C::AROW + ((((u32)lane >> 4) ^ C::a_swz(m)) << 4);
     const int g = lane >> 4, s = lane & 15;
     const u32 kr = 8 * g + (s >> 2);
-    const u32 xb = tiles::b_swz(kr);
+    const u32 xb = C::b_swz(kr);
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
         const u32 n = wn * C::WTN + j * 16 + 4 * (s & 3);

@@ -30,6 +30,18 @@ def _declared_functions():
     return sorted({n for n in names if n not in keywords and (n.startswith("lcma_") or n.startswith("gemm_"))})
 
 
+def test_library_binds_to_the_one_hip_runtime_in_the_process():
+    # Imported before anything else, the binding must not pull in a second HIP
+    # runtime beside torch's (that copy sees no device on a GPU host).
+    import subprocess
+    import sys
+    code = ("import complexity_half_precision_amd, torch; "
+            "print(len({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == "1"
+
+
 def test_every_declared_symbol_is_exported():
     declared = _declared_functions()
     assert len(declared) >= 14
