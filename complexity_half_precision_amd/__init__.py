@@ -32,12 +32,13 @@ _lib = ctypes.CDLL(LIB_PATH)
 F16, BF16 = 0, 1
 ALGO_AUTO, ALGO_CLASSIC, ALGO_L1, ALGO_L2 = 0, 1, 2, 3
 SPLIT_AUTO, SPLIT_NONE, SPLIT_ALL = 0, 1, 2
-COMBINE_AUTO, COMBINE_PREPASS, COMBINE_AT_LOAD, COMBINE_UNFUSED = 0, 1, 2, 3
+COMBINE_AUTO, COMBINE_PREPASS, COMBINE_AT_LOAD, COMBINE_UNFUSED, COMBINE_L2_ON_CHIP = 0, 1, 2, 3, 4
 OK, E_INVALID, E_UNSUPPORTED, E_BAD_DESCRIPTOR, E_WORKSPACE, E_HIP, E_NOMEM = range(7)
 ALGO_NAMES = {ALGO_CLASSIC: "classic", ALGO_L1: "l1", ALGO_L2: "l2"}
 _ALGO = {"auto": ALGO_AUTO, "classic": ALGO_CLASSIC, "l1": ALGO_L1, "l2": ALGO_L2}
 _SPLIT = {"auto": SPLIT_AUTO, "none": SPLIT_NONE, "all": SPLIT_ALL}
-_COMBINE = {"auto": COMBINE_AUTO, "prepass": COMBINE_PREPASS, "at_load": COMBINE_AT_LOAD, "unfused": COMBINE_UNFUSED}
+_COMBINE = {"auto": COMBINE_AUTO, "prepass": COMBINE_PREPASS, "at_load": COMBINE_AT_LOAD, "unfused": COMBINE_UNFUSED,
+            "l2_on_chip": COMBINE_L2_ON_CHIP}
 
 _i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
 

@@ -257,10 +257,29 @@ void written_counts(int levels, bool write_all, int* nA, int* nB)
     }
 }
 
-double est_lcma(int64_t M, int64_t N, int64_t K, int levels, int split_req, bool write_all, const Machine& m)
+// Tiles of the group kernel that runs a plan's products: the one-level
+// kernel's (128) for one level and for two levels with the outer level in
+// memory (7 launches over the M/4 x N/4 blocks), the on-chip two-level
+// kernel's (64) otherwise.
+Geo sched_geo(const Geo& g, bool outer)
+{
+    Geo s = g;
+    if (outer) {
+        s.tile = fused_tile(1);
+        s.R = 7;
+        s.gy = (int)((g.Mb + s.tile - 1) / s.tile);
+        s.gx = (int)((g.Nb + s.tile - 1) / s.tile);
+        s.G = s.gy * s.gx;
+    }
+    return s;
+}
+
+double est_lcma(int64_t M, int64_t N, int64_t K, int levels, int split_req, bool write_all, bool outer,
+                const Machine& m)
 {
     const double s = 2.0;
     const Geo g = lcma_geo(M, N, K, levels);
+    const Geo sg = sched_geo(g, levels == 2 && outer);
     int nA, nB;
     written_counts(levels, write_all, &nA, &nB);
     // pre-pass: read A and B once, write the combined operands
@@ -269,16 +288,24 @@ double est_lcma(int64_t M, int64_t N, int64_t K, int levels, int split_req, bool
     const double t_pre = Bpre / (m.eta_bw * m.bw) + m.launch;
     // fused: R products of Mb x Nb x Kb
     const double F = 2.0 * g.R * (double)g.Mb * g.Nb * g.Kb;
-    const double Bf = s * g.R * ((double)g.Mb * g.Kb + (double)g.Kb * g.Nb) + s * (double)M * N;
-    const int mode = split_mode_for((lcma_split)split_req, g.G, m.P);
+    double Bf = s * g.R * ((double)g.Mb * g.Kb + (double)g.Kb * g.Nb) + s * (double)M * N;
+    const bool out2 = levels == 2 && outer;
+    // Outer level in memory: per element of the four M/2 x N/2 outer
+    // outputs, 4 bytes stored by the first contributor, 8 read and written by
+    // each middle one, 4 read by the last (which writes C): 8c - 6 bytes for
+    // c contributors (4, 2, 2, 4 for Strassen), 18 MN bytes in all.
+    if (out2)
+        Bf += 18.0 * (double)M * N - s * (double)M * N;
+    const int mode = split_mode_for((lcma_split)split_req, sg.G, m.P);
     double q;
     if (mode == kSplitTail) {
-        const double rounds = (double)(g.G / m.P) + 0.5;
-        q = ((double)g.G / m.P) / rounds;
+        const double rounds = (double)(sg.G / m.P) + 0.5;
+        q = ((double)sg.G / m.P) / rounds;
     } else {
-        q = quant(g.G, m.P);
+        q = quant(sg.G, m.P);
     }
-    const double t_f = kernel_time(F, Bf, g.tile / 2.0, q, levels == 1 ? m.eta_fused1 : m.eta_fused2, m);
+    const double eta = (levels == 1 || out2) ? m.eta_fused1 : m.eta_fused2;
+    const double t_f = kernel_time(F, Bf, sg.tile / 2.0, q, eta, m) + (out2 ? 6 * m.launch : 0.0);
     return t_pre + t_f;
 }
 
@@ -301,6 +328,9 @@ struct lcma_plan_s {
     int8_t order[kMaxRank];
     int n_slots;
     int64_t offA, offB, offPart, offCtr;
+    int outer;             // two levels: inner level fused, outer level accumulated in fp32 memory
+    int8_t order1[7];      // outer level: order of the 7 launches (outer products)
+    int64_t offAcc;        // outer level: fp32 output blocks
     int64_t slotA[kMaxRank], slotB[kMaxRank];   // index among written operands, -1 = in place
     int blockA[kMaxRank], blockB[kMaxRank];     // block index of an in-place operand
     size_t ws_bytes;
@@ -368,7 +398,7 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     if (opts)
         o = *opts;
     if (o.split < LCMA_SPLIT_AUTO || o.split > LCMA_SPLIT_ALL || o.combine < LCMA_COMBINE_AUTO ||
-        o.combine > LCMA_COMBINE_UNFUSED || o.num_cus < 0 || o.peak_tflops < 0 || o.hbm_gbps < 0 ||
+        o.combine > LCMA_COMBINE_L2_ON_CHIP || o.num_cus < 0 || o.peak_tflops < 0 || o.hbm_gbps < 0 ||
         o.bf16_ops_f16 < -1 || o.bf16_ops_f16 > 1 || !(o.classic_eff >= 0 && o.classic_eff <= 1) ||
         !(o.fused_eff >= 0 && o.fused_eff <= 1))
         return LCMA_E_INVALID;
@@ -399,6 +429,9 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     const bool unfused = generic || o.combine == LCMA_COMBINE_UNFUSED;
     if (o.combine == LCMA_COMBINE_AT_LOAD)
         return LCMA_E_UNSUPPORTED;   // not built yet
+    // Two levels: the outer level goes through memory unless all 49 products
+    // are to accumulate on chip.
+    const bool outer2 = o.combine != LCMA_COMBINE_L2_ON_CHIP;
     if (generic && force == LCMA_ALGO_L2)
         return LCMA_E_UNSUPPORTED;
 
@@ -409,8 +442,9 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     m.launch = 4e-6;
     // Sustained fractions of the MFMA peak measured on MI355X (256 CUs) for
     // the kernels as they stand: classic 256x256 tiles 0.50-0.55 over
-    // 4096^3..16384^3; fused one-level group kernel about 0.31; fused
-    // two-level kernel about 0.037.
+    // 4096^3..16384^3; fused one-level group kernel about 0.31 (also the
+    // inner level of the default two-level path); the on-chip two-level
+    // kernel about 0.037.
     m.eta_mfma = o.classic_eff > 0 ? o.classic_eff : 0.52;
     m.eta_fused1 = o.fused_eff > 0 ? o.fused_eff : 0.31;
     m.eta_fused2 = o.fused_eff > 0 ? o.fused_eff : 0.037;
@@ -464,10 +498,10 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         const double comb = 8.0 * nnzW * (double)Mb * Nb + 6.0 * (double)M * N;
         est[LCMA_ALGO_L1] = (pre + comb) / (m.eta_bw * m.bw) + gen.rank * est_classic(Mb, Nb, Kb, m) + 3 * m.launch;
     } else if (ok1) {
-        est[LCMA_ALGO_L1] = est_lcma(M, N, K, 1, o.split, op_bf16_for(1) != (dt == LCMA_BF16), m);
+        est[LCMA_ALGO_L1] = est_lcma(M, N, K, 1, o.split, op_bf16_for(1) != (dt == LCMA_BF16), false, m);
     }
     if (ok2)
-        est[LCMA_ALGO_L2] = est_lcma(M, N, K, 2, o.split, op_bf16_for(2) != (dt == LCMA_BF16), m);
+        est[LCMA_ALGO_L2] = est_lcma(M, N, K, 2, o.split, op_bf16_for(2) != (dt == LCMA_BF16), outer2, m);
 
     lcma_algo chosen = force;
     if (force == LCMA_ALGO_L1 && !ok1)
@@ -530,23 +564,26 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         const int L = p->levels;
         p->op_bf16 = op_bf16_for(L);
         p->write_all = p->op_bf16 != (dt == LCMA_BF16 ? 1 : 0);
+        p->outer = L == 2 && outer2;
         p->geo = lcma_geo(M, N, K, L);
         const Geo& g = p->geo;
+        const Geo sg = sched_geo(g, p->outer);
         SchedParams& sp = p->sp;
-        sp.G = g.G; sp.gy = g.gy; sp.gx = g.gx; sp.R = g.R; sp.P = m.P;
-        sp.mode = split_mode_for(o.split, g.G, m.P);
-        sp.h = (g.R + 1) / 2;
+        sp.G = sg.G; sp.gy = sg.gy; sp.gx = sg.gx; sp.R = sg.R; sp.P = m.P;
+        sp.mode = split_mode_for(o.split, sg.G, m.P);
+        sp.h = (sg.R + 1) / 2;
         sp.raster = 8;
         if (sp.mode == kSplitTail) {
-            p->n_slots = g.G % m.P;
-            p->grid = g.G / m.P > 0 ? m.P : 2 * (g.G % m.P);
+            p->n_slots = sg.G % m.P;
+            p->grid = sg.G / m.P > 0 ? m.P : 2 * (sg.G % m.P);
         } else if (sp.mode == kSplitAll) {
-            p->n_slots = g.G;
-            p->grid = std::min(2 * g.G, m.P);
+            p->n_slots = sg.G;
+            p->grid = std::min(2 * sg.G, m.P);
         } else {
-            p->grid = std::min(g.G, m.P);
+            p->grid = std::min(sg.G, m.P);
         }
-        fused_order(L, p->order);
+        fused_order(p->outer ? 1 : L, p->order);
+        fused_order(1, p->order1);
         // workspace layout
         std::call_once(g_tables_once, init_tables);
         const int SS = g.S * g.S;
@@ -575,9 +612,12 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         p->offB = off;
         off = align_up(off + (int64_t)nB * g.Kb * g.Nb * 2, 256);
         p->offPart = off;
-        off = align_up(off + (int64_t)p->n_slots * 2 * fused_partial_bytes(L), 256);
+        off = align_up(off + (int64_t)p->n_slots * 2 * fused_partial_bytes(p->outer ? 1 : L), 256);
         p->offCtr = off;
         off = align_up(off + (int64_t)p->n_slots * 4, 256);
+        p->offAcc = off;
+        if (p->outer)
+            off = align_up(off + (int64_t)16 * g.Mb * g.Nb * 4, 256);
         p->ws_bytes = (size_t)off;
     }
     if (log_enabled())
@@ -659,7 +699,7 @@ lcma_status lcma_plan_schedule(lcma_plan_t p, int32_t* items, int64_t cap, int64
     }
     *count = n;
     if (order)
-        for (int r = 0; r < p->geo.R; ++r)
+        for (int r = 0; r < p->sp.R; ++r)
             order[r] = p->order[r];
     return LCMA_OK;
 }
@@ -737,34 +777,36 @@ lcma_status do_prepass(const lcma_plan_s* p, const void* A, int64_t lda, const v
     return hip_status(launch_prepass(L, st), "launch_prepass");
 }
 
+// Operand pointers of canonical product r into position j of the kernel
+// arguments: the pre-pass output, or the block of A / B read in place.
+void set_operands(const lcma_plan_s* p, const void* A, int64_t lda, const void* B, int64_t ldb, void* ws, int r,
+                  int j, FusedParams& fp)
+{
+    const Geo& g = p->geo;
+    if (p->slotA[r] >= 0) {
+        fp.a[j] = (const uint16_t*)((char*)ws + p->offA) + p->slotA[r] * g.Mb * g.Kb;
+        fp.lda[j] = g.Kb;
+    } else {
+        const int bi = p->blockA[r] / g.S, bk = p->blockA[r] % g.S;
+        fp.a[j] = (const uint16_t*)A + bi * g.Mb * lda + bk * g.Kb;
+        fp.lda[j] = lda;
+    }
+    if (p->slotB[r] >= 0) {
+        fp.b[j] = (const uint16_t*)((char*)ws + p->offB) + p->slotB[r] * g.Kb * g.Nb;
+        fp.ldb[j] = g.Nb;
+    } else {
+        const int bk = p->blockB[r] / g.S, bj = p->blockB[r] % g.S;
+        fp.b[j] = (const uint16_t*)B + bk * g.Kb * ldb + bj * g.Nb;
+        fp.ldb[j] = ldb;
+    }
+}
+
 lcma_status do_fused(const lcma_plan_s* p, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                      int64_t ldc, const Io& io, void* ws, hipStream_t st)
 {
     FusedLaunch L;
     memset(&L, 0, sizeof L);
     const Geo& g = p->geo;
-    for (int r = 0; r < g.R; ++r) {
-        if (p->slotA[r] >= 0) {
-            L.p.a[r] = (const uint16_t*)((char*)ws + p->offA) + p->slotA[r] * g.Mb * g.Kb;
-            L.p.lda[r] = g.Kb;
-        } else {
-            const int bi = p->blockA[r] / g.S, bk = p->blockA[r] % g.S;
-            L.p.a[r] = (const uint16_t*)A + bi * g.Mb * lda + bk * g.Kb;
-            L.p.lda[r] = lda;
-        }
-        if (p->slotB[r] >= 0) {
-            L.p.b[r] = (const uint16_t*)((char*)ws + p->offB) + p->slotB[r] * g.Kb * g.Nb;
-            L.p.ldb[r] = g.Nb;
-        } else {
-            const int bk = p->blockB[r] / g.S, bj = p->blockB[r] % g.S;
-            L.p.b[r] = (const uint16_t*)B + bk * g.Kb * ldb + bj * g.Nb;
-            L.p.ldb[r] = ldb;
-        }
-        L.p.order[r] = p->order[r];
-        const int8_t* W = p->levels == 1 ? g_W1 : g_W2;
-        for (int o = 0; o < g.S * g.S; ++o)
-            L.p.w[r][o] = W[r * g.S * g.S + o];
-    }
     L.p.C = (uint16_t*)C;
     L.p.ldc = ldc;
     L.p.Mb = (int32_t)g.Mb; L.p.Nb = (int32_t)g.Nb; L.p.Kb = (int32_t)g.Kb;
@@ -776,7 +818,57 @@ lcma_status do_fused(const lcma_plan_s* p, const void* A, int64_t lda, const voi
     L.op_bf16 = p->op_bf16;
     L.out_bf16 = p->dt == LCMA_BF16;
     L.grid = p->grid;
-    return hip_status(launch_fused(L, st), "launch_fused");
+    if (!p->outer) {
+        const int8_t* W = p->levels == 1 ? g_W1 : g_W2;
+        for (int r = 0; r < g.R; ++r) {
+            set_operands(p, A, lda, B, ldb, ws, r, r, L.p);
+            L.p.order[r] = p->order[r];
+            for (int o = 0; o < g.S * g.S; ++o)
+                L.p.w[r][o] = W[r * g.S * g.S + o];
+        }
+        return hip_status(launch_fused(L, st), "launch_fused");
+    }
+    // Two levels, outer level in memory: one launch per outer product r1 (in
+    // the order order1), each running the inner products (r1, r2) = r1*7 + r2
+    // of the flattened scheme.  Outer output (i1, j1) is fed by every r1 with
+    // W1[r1][i1, j1] != 0: the first in launch order stores its fp32 blocks,
+    // the last adds and rounds into C.
+    L.outer = 1;
+    L.p.acc = (float*)((char*)ws + p->offAcc);
+    int first[4], last[4], uses[4];
+    for (int o = 0; o < 4; ++o) {
+        first[o] = last[o] = -1;
+        uses[o] = 0;
+        for (int k = 0; k < 7; ++k)
+            if (g_W1[p->order1[k] * 4 + o] != 0) {
+                if (first[o] < 0)
+                    first[o] = k;
+                last[o] = k;
+                ++uses[o];
+            }
+    }
+    for (int r2 = 0; r2 < 7; ++r2) {
+        L.p.order[r2] = p->order[r2];
+        for (int o = 0; o < 4; ++o)
+            L.p.w[r2][o] = g_W1[r2 * 4 + o];
+    }
+    for (int k = 0; k < 7; ++k) {
+        const int r1 = p->order1[k];
+        for (int r2 = 0; r2 < 7; ++r2)
+            set_operands(p, A, lda, B, ldb, ws, r1 * 7 + r2, r2, L.p);
+        for (int o = 0; o < 4; ++o) {
+            const int c = g_W1[r1 * 4 + o];
+            L.p.ow[o] = (float)c;
+            L.p.omode[o] = c == 0             ? kOuterNone
+                           : uses[o] == 1     ? kOuterOnly
+                           : k == first[o]    ? kOuterStore
+                           : k == last[o]     ? kOuterFinish
+                                              : kOuterAdd;
+        }
+        if (hip_status(launch_fused(L, st), "launch_fused (outer level)") != LCMA_OK)
+            return LCMA_E_HIP;
+    }
+    return LCMA_OK;
 }
 
 // Unfused path, pre-pass half: every combined operand of both sides.

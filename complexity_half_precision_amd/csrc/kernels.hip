@@ -14,8 +14,13 @@
 //                    the 7 products of one output coordinate accumulate into
 //                    the 4 output tiles in registers (fp32), no product is
 //                    written to memory; tail groups may be split over two
-//                    workgroups with a last-arriver fp32 fix-up.
-//  * k_fused<2>   -- the same for two levels (49 products, 16 outputs) on the
+//                    workgroups with a last-arriver fp32 fix-up.  Its OUTER
+//                    variant runs one outer product of the two-level scheme
+//                    (7 inner products on M/4 x N/4 blocks, fused the same
+//                    way) and folds the 4 inner outputs into fp32 output
+//                    blocks in memory, rounding into C at the last touch.
+//  * k_fused<2>   -- all 49 products of one output coordinate on one
+//                    workgroup (16 outputs on chip, 64 x 64 tiles) on the
 //                    register-staged path.
 //
 // Sources: "FalconGEMM: Surpassing Hardware Peaks with Lower-Complexity
@@ -816,19 +821,18 @@ __device__ __forceinline__ void wait_vm()
 }
 
 // Wait until at most n k-tiles of this wave's loads are in flight
-// (0 <= n < AHEAD; n < 0 waits for all).
-template <class C>
+// (n is capped at AHEAD - 1; n <= 0 waits for all).
+template <class C, int K = C::AHEAD - 1>
 __device__ __forceinline__ void wait_tiles(int n)
 {
-    static_assert(C::AHEAD <= 4, "cases below");
-    if (n >= 3)
-        wait_vm<3 * C::PER>();
-    else if (n == 2)
-        wait_vm<2 * C::PER>();
-    else if (n == 1)
-        wait_vm<C::PER>();
-    else
+    if constexpr (K <= 0) {
         tiles::wait_vm0();
+    } else {
+        if (n >= K)
+            wait_vm<K * C::PER>();
+        else
+            wait_tiles<C, K - 1>(n);
+    }
 }
 
 
@@ -1066,10 +1070,10 @@ __device__ __forceinline__ void store_c_staged(const f32x16 (&acc)[C::FM][C::FN]
 
 namespace m16 {
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int AHEAD_ = 3>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = 32, WM = WM_, WN = WN_, MT = 16;
-    static constexpr int NSTAGE = 4, AHEAD = 3;
+    static constexpr int AHEAD = AHEAD_, NSTAGE = AHEAD_ + 1;   // k-tiles loaded ahead; LDS ring stages
     static constexpr int NW = WM * WN;
     static constexpr int NT = NW * 64;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -1192,23 +1196,41 @@ __device__ __forceinline__ void ktile(u32x4 (&Af)[C::FM], const u32x4 (&Bc)[C::F
     }
 }
 
-// K loop of one output tile (same contract as q4::run_tile).
-template <class C, bool BF, bool EDGE, bool GROUPED, class SrcFn, class AfterFn>
+// K loop of one output tile (same contract as q4::run_tile).  RESTRIDE: the
+// sources may change their leading dimensions between k-tiles (the products
+// of a fused group: combined blocks and singleton operands differ), so the
+// grouped-load offsets are recomputed whenever a source's strides differ from
+// the last ones (a uniform branch, taken once per product switch at most),
+// and src(0) is not called ahead of the k-tiles (cursor sources may be used).
+template <class C, bool BF, bool EDGE, bool GROUPED, bool RESTRIDE = false, class SrcFn, class AfterFn>
 __device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, AfterFn after, int wave, int lane,
                                          const Addr<C>& ad, f32x4 (&acc)[C::FM][C::FN])
 {
-    static_assert(C::AHEAD == 3 && C::NSTAGE == 4, "stage reuse below assumes a 4-stage ring, 3 ahead");
+    static_assert(C::AHEAD >= 3 && C::NSTAGE == C::AHEAD + 1, "stage reuse below: tile t + AHEAD goes where tile t - 1 was");
     static_assert(!(GROUPED && EDGE), "grouped loads carry no bounds");
+    static_assert(!RESTRIDE || GROUPED, "restriding applies to grouped loads");
     u32x4 Af[C::FM], B0[C::FN], B1[C::FN];
     q4::Group<C> go;
-    if constexpr (GROUPED)
+    int go_lda = -1, go_ldb = -1;
+    auto regroup = [&](const tiles::TileSrc& ps) {
+        if constexpr (RESTRIDE) {
+            if (ps.lda != go_lda || ps.ldb != go_ldb) {
+                go = q4::group_offsets<C>(ps, wave, lane);
+                go_lda = ps.lda;
+                go_ldb = ps.ldb;
+            }
+        }
+    };
+    if constexpr (GROUPED && !RESTRIDE)
         go = q4::group_offsets<C>(src(0), wave, lane);
 #pragma unroll
     for (int t = 0; t < C::AHEAD; ++t) {
         if (t < nk) {
             if constexpr (GROUPED) {
-                q4::dma_group<C>(smem + t * C::STAGE, src(t), go, wave, 0);
-                q4::dma_group<C>(smem + t * C::STAGE, src(t), go, wave, 1);
+                const tiles::TileSrc ps = src(t);
+                regroup(ps);
+                q4::dma_group<C>(smem + t * C::STAGE, ps, go, wave, 0);
+                q4::dma_group<C>(smem + t * C::STAGE, ps, go, wave, 1);
             } else {
                 q4::dma_tile<C, EDGE>(smem + t * C::STAGE, src(t), wave, lane);
             }
@@ -1225,13 +1247,17 @@ __device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, AfterFn 
             read_b<C>(smem, ad, j, B0[j]);
     }
     // Top of k-tile t: tile t+1 has landed and every wave has finished with
-    // tile t-1's stage, which then takes tile t+3.
+    // tile t-1's stage, which then takes tile t+3.  No LDS-read wait here:
+    // reads still in flight target stage t+1 (the fragments of tile t+1),
+    // which nothing overwrites before the next barrier, and the reads of
+    // stage t-1 were consumed by tile t-1's MFMAs (the compiler waits for
+    // each fragment before its first use).
     auto steady = [&](int t, const u32x4 (&Bc)[C::FN], u32x4 (&Bn)[C::FN]) {
-        q4::wait_vm<C::PER>();
-        tiles::wait_lgkm0();
+        q4::wait_vm<(C::AHEAD - 2) * C::PER>();   // tiles t+2 .. t+AHEAD-1 may be in flight
         tiles::bar();
         __builtin_amdgcn_sched_barrier(0);
         const tiles::TileSrc ps = src(t + C::AHEAD);
+        regroup(ps);
         ktile<C, BF, true, true, EDGE, GROUPED>(Af, Bc, Bn, smem + ((t + 1) % C::NSTAGE) * C::STAGE,
                                                 smem + ((t + C::AHEAD) % C::NSTAGE) * C::STAGE, ps, go, ad, wave,
                                                 lane, acc);
@@ -1255,14 +1281,15 @@ __device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, AfterFn 
                 acc[i][j] = mfma<BF>(B0[j], Af[i], acc[i][j]);
         after(t);
         if (t + 1 < nk) {
-            // issued so far: tiles up to min(t+2, nk-1); tile t+1 must have landed
-            q4::wait_tiles<C>(min(nk - 2 - t, 1));
+            // issued so far: tiles up to min(t+AHEAD-1, nk-1); tile t+1 must have landed
+            q4::wait_tiles<C>(min(nk - 2 - t, C::AHEAD - 2));
             tiles::wait_lgkm0();
             tiles::bar();
             if (t + C::AHEAD < nk) {
                 const tiles::TileSrc ps = src(t + C::AHEAD);
                 char* pre = smem + ((t + C::AHEAD) % C::NSTAGE) * C::STAGE;
                 if constexpr (GROUPED) {
+                    regroup(ps);
                     q4::dma_group<C>(pre, ps, go, wave, 0);
                     q4::dma_group<C>(pre, ps, go, wave, 1);
                 } else {
@@ -1803,11 +1830,57 @@ __device__ __forceinline__ void combine_h(const int8_t* w, const typename C::acc
     }
 }
 
+// Outer level of the two-level path: the finished inner outputs of this
+// group tile go, scaled by W1[r1][i1, j1], into the fp32 blocks of every
+// outer output (i1, j1) that outer product r1 feeds (mode per output: store,
+// add, add and round into C, or round into C).  Rows past the block edge get
+// an out-of-range offset (loads read zero, stores are dropped); columns come
+// in fours and Nb is a multiple of 8.
+template <class C, bool CBF>
+__device__ __forceinline__ void outer_update(const FusedParams& fp, int m0, int n0,
+                                             const f32x4 (&Cacc)[4][C::FM][C::FN], int wm, int wn, int lane)
+{
+    const int rows = fp.Mb - m0, cols = fp.Nb - n0, ld = fp.Nb;
+#pragma unroll
+    for (int o1 = 0; o1 < 4; ++o1) {
+        const int mode = fp.omode[o1];
+        if (mode == kOuterNone)
+            continue;
+        const float w = fp.ow[o1];
+        const int i1 = o1 >> 1, j1 = o1 & 1;
+#pragma unroll
+        for (int o2 = 0; o2 < 4; ++o2) {
+            const int bi = 2 * i1 + (o2 >> 1), bj = 2 * j1 + (o2 & 1);
+            const rsrc_t ra = make_rsrc(fp.acc + (int64_t)(bi * 4 + bj) * fp.Mb * fp.Nb + (int64_t)m0 * ld + n0);
+            f32x4 t[C::FM][C::FN];
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j) {
+                    const int m = wm * C::WTM + i * 16 + (lane & 15);
+                    const int n = wn * C::WTN + j * 16 + 4 * (lane >> 4);
+                    const u32 off = (m < rows && n < cols) ? (u32)(m * ld + n) * 4u : kOob;
+                    f32x4 v = Cacc[o2][i][j] * w;
+                    if (mode == kOuterAdd || mode == kOuterFinish)
+                        v += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
+                    if (mode == kOuterStore || mode == kOuterAdd)
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), ra, off, 0, 0);
+                    t[i][j] = v;
+                }
+            if (mode == kOuterFinish || mode == kOuterOnly)
+                store_c<C, CBF, true>(t, fp.C + (int64_t)(bi * fp.Mb + m0) * fp.ldc + bj * fp.Nb + n0, fp.ldc, rows,
+                                      cols, wm, wn, lane);
+        }
+    }
+}
+
 // Writes a group's output blocks.  A split piece first publishes its fp32
 // partial; the second piece to arrive (agent-scope acquire/release through a
 // per-slot counter) adds the other partial, writes C and resets the counter.
 // fp32 addition commutes, so the result does not depend on arrival order.
-template <int NOUT, class C, bool CBF>
+// OUTER: the outputs go through outer_update instead of straight into C.
+template <int NOUT, class C, bool CBF, bool OUTER = false>
 __device__ __forceinline__ void fused_epilogue(const FusedParams& fp, const Item& item, int m0, int n0,
                                                typename C::acc_t (&Cacc)[NOUT][C::FM][C::FN], int tid, int wm,
                                                int wn, int lane, int* sh_old)
@@ -1865,11 +1938,16 @@ __device__ __forceinline__ void fused_epilogue(const FusedParams& fp, const Item
         }
     }
     if (store) {
+        if constexpr (OUTER) {
+            static_assert(NOUT == 4, "the outer level runs the one-level kernel");
+            outer_update<C, CBF>(fp, m0, n0, Cacc, wm, wn, lane);
+        } else {
 #pragma unroll
-        for (int o = 0; o < NOUT; ++o) {
-            const int bi = o / S, bj = o % S;
-            store_c<C, CBF, true>(Cacc[o], fp.C + (int64_t)(bi * fp.Mb + m0) * fp.ldc + bj * fp.Nb + n0, fp.ldc,
-                                  fp.Mb - m0, fp.Nb - n0, wm, wn, lane);
+            for (int o = 0; o < NOUT; ++o) {
+                const int bi = o / S, bj = o % S;
+                store_c<C, CBF, true>(Cacc[o], fp.C + (int64_t)(bi * fp.Mb + m0) * fp.ldc + bj * fp.Nb + n0, fp.ldc,
+                                      fp.Mb - m0, fp.Nb - n0, wm, wn, lane);
+            }
         }
     }
 }
@@ -1943,7 +2021,10 @@ __global__ void __launch_bounds__(FusedCfg<LEVELS>::C::NT) k_fused(const FusedPa
 // back through the DMA ring; after each product's last k-tile every wave folds
 // its H sub-tile into its four output sub-tiles.
 
-using MCF1 = m16::Cfg<128, 128, 2, 4>;   // fused one-level group tile: 8 waves of 64 x 32
+// Fused one-level group tile: 8 waves of 64 x 32.  A k-tile holds only 8
+// MFMAs per wave, so loads run 7 tiles ahead (8-stage ring, 128 KiB) to
+// cover the latency of operands that miss L2.
+using MCF1 = m16::Cfg<128, 128, 2, 4, 7>;
 
 // Fused one-level group kernel on the 16x16x32 engine: 8 waves (two per
 // SIMD) of 64 x 32, each holding four fp32 output sub-tiles plus H (160
@@ -1951,7 +2032,7 @@ using MCF1 = m16::Cfg<128, 128, 2, 4>;   // fused one-level group tile: 8 waves 
 // through the same LDS ring (the prefetch runs across product boundaries);
 // at each product's last k-tile every wave folds H into its four output
 // sub-tiles.
-template <bool OBF, bool CBF>
+template <bool OBF, bool CBF, bool OUTER>
 __global__ void __launch_bounds__(MCF1::NT, 1) k_fused1_m16(const FusedParams fp)
 {
     using C = MCF1;
@@ -1964,6 +2045,12 @@ __global__ void __launch_bounds__(MCF1::NT, 1) k_fused1_m16(const FusedParams fp
     const int w = blockIdx.x;
     const int n_items = sched_count(fp.sp, w);
     const int nk = (fp.Kb + C::BK - 1) / C::BK;
+    // The 7 order entries as one scalar word: indexing the argument array
+    // directly compiles to a vector load, whose wait drains the in-flight
+    // tile loads at every product switch.
+    uint64_t ordw;
+    __builtin_memcpy(&ordw, fp.order, sizeof ordw);
+    auto order_at = [&](int pos) { return (int)(int8_t)(ordw >> (8 * pos)); };
     for (int it = 0; it < n_items; ++it) {
         // Opaque per item: keeps lane-derived addresses from being hoisted out
         // of the item loop and held in registers across the whole kernel.
@@ -1986,7 +2073,7 @@ __global__ void __launch_bounds__(MCF1::NT, 1) k_fused1_m16(const FusedParams fp
         // argument arrays, read through scalar loads) are fetched only when
         // the product changes.
         auto prod_src = [&](int j) {
-            const int r = fp.order[item.pos0 + j];
+            const int r = order_at(item.pos0 + j);
             return tiles::TileSrc{fp.a[r] + (int64_t)m0 * fp.lda[r], (int)fp.lda[r], fp.Mb - m0,
                                   fp.b[r] + n0, (int)fp.ldb[r], fp.Nb - n0, 0, fp.Kb};
         };
@@ -2006,19 +2093,22 @@ __global__ void __launch_bounds__(MCF1::NT, 1) k_fused1_m16(const FusedParams fp
         auto after = [&](int) {
             if (++akt == nk) {
                 akt = 0;
-                combine_h<NOUT, C>(fp.w[fp.order[item.pos0 + aj]], H, Cacc);
+                combine_h<NOUT, C>(fp.w[order_at(item.pos0 + aj)], H, Cacc);
                 zero_acc<C>(H);
                 ++aj;
             }
         };
         const m16::Addr<C> ad = m16::frag_addr<C>(wm, wn, lane);
         const bool inside = (m0 + C::BM <= fp.Mb) & (n0 + C::BN <= fp.Nb) & (fp.Kb % C::BK == 0);
+        // Interior items load through grouped loads; the singleton operands
+        // (read in place, with the full matrices' strides) and the combined
+        // blocks differ in stride, hence the restriding variant.
         if (inside)
-            m16::run_tile<C, OBF, false, false>(smem, ntiles, src, after, wave, lane, ad, H);
+            m16::run_tile<C, OBF, false, true, true>(smem, ntiles, src, after, wave, lane, ad, H);
         else
             m16::run_tile<C, OBF, true, false>(smem, ntiles, src, after, wave, lane, ad, H);
         __syncthreads();
-        fused_epilogue<NOUT, C, CBF>(fp, item, m0, n0, Cacc, tid, wm, wn, lane, &sh_old);
+        fused_epilogue<NOUT, C, CBF, OUTER>(fp, item, m0, n0, Cacc, tid, wm, wn, lane, &sh_old);
         __syncthreads();
     }
 }
@@ -2028,7 +2118,10 @@ hipError_t launch_fused1_m16(const FusedLaunch& L, hipStream_t st)
 {
     if (L.grid <= 0)
         return hipSuccess;
-    hipLaunchKernelGGL((k_fused1_m16<OBF, CBF>), dim3(L.grid), dim3(MCF1::NT), 0, st, L.p);
+    if (L.outer)
+        hipLaunchKernelGGL((k_fused1_m16<OBF, CBF, true>), dim3(L.grid), dim3(MCF1::NT), 0, st, L.p);
+    else
+        hipLaunchKernelGGL((k_fused1_m16<OBF, CBF, false>), dim3(L.grid), dim3(MCF1::NT), 0, st, L.p);
     return hipGetLastError();
 }
 
@@ -2121,7 +2214,7 @@ void fused_order(int32_t levels, int8_t* order)
 
 hipError_t launch_fused(const FusedLaunch& L, hipStream_t st)
 {
-    if (L.levels == 1) {
+    if (L.levels == 1 || L.outer) {
         if (L.out_bf16)
             return L.op_bf16 ? launch_fused1_m16<true, true>(L, st) : launch_fused1_m16<false, true>(L, st);
         return launch_fused1_m16<false, false>(L, st);

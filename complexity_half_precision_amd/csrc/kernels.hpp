@@ -59,13 +59,26 @@ struct FusedParams {
     int8_t w[kMaxRank][16];        // W[r][output block] (output blocks row-major)
     float* partial;                // split fix-up partials
     int32_t* counters;             // split fix-up arrival counters
+    // Two levels with the outer level in memory: this launch runs the 7 inner
+    // products of one outer product r1 over blocks of M/4 x N/4; its inner
+    // output (i2, j2) feeds output block (2 i1 + i2, 2 j1 + j2) of every outer
+    // output (i1, j1) with omode != kOuterNone, scaled by ow = W1[r1][i1, j1].
+    float* acc;                    // fp32 output blocks, 16 of Mb x Nb, block-major (block 4 bi + bj)
+    int8_t omode[4];               // OuterMode per outer output (i1, j1), row-major
+    float ow[4];
 };
+
+// What one outer product does to an outer output's fp32 blocks: the first
+// contributor stores, later ones add, the last adds and rounds into C; an
+// output fed by one product only is rounded straight into C.
+enum OuterMode : int8_t { kOuterNone = 0, kOuterStore = 1, kOuterAdd = 2, kOuterFinish = 3, kOuterOnly = 4 };
 
 struct FusedLaunch {
     FusedParams p;
     int32_t levels;
     int32_t op_bf16, out_bf16;
     int32_t grid;
+    int32_t outer;                 // levels == 2: 1 = one launch of the outer level (one-level kernel + acc)
 };
 // Workgroup tile edge of the fused kernel for a level (1: 128, 2: 64).
 // ---- unfused path for any valid description (one level of it)

@@ -75,16 +75,25 @@ typedef enum {
     LCMA_SPLIT_ALL = 2    /* split every group (testing the fix-up path) */
 } lcma_split;
 
-/* How the combined operands reach the fused kernel. */
+/* How the combined operands reach the fused kernel, and (two levels) where
+ * the products of one output coordinate accumulate. */
 typedef enum {
     LCMA_COMBINE_AUTO = 0,
-    LCMA_COMBINE_PREPASS = 1, /* a separate bandwidth-bound pass writes each combined operand to the workspace */
+    LCMA_COMBINE_PREPASS = 1, /* a separate bandwidth-bound pass writes each combined operand to the workspace.
+                                 Two levels: the 7 inner products of each outer product run fused as one
+                                 level (their 4 outputs accumulate on chip), one launch per outer product,
+                                 and each launch folds W1[r1][i1,j1] * (its inner outputs) into fp32 output
+                                 blocks in the workspace; the last contributor to an output rounds it into C */
     LCMA_COMBINE_AT_LOAD = 2, /* the fused kernel forms the combinations while staging tiles (one-level only) */
-    LCMA_COMBINE_UNFUSED = 3  /* one level only: every combined operand is written, each product runs as its own
+    LCMA_COMBINE_UNFUSED = 3, /* one level only: every combined operand is written, each product runs as its own
                                  GEMM whose epilogue adds W[r][i,j] * H_r into fp32 output blocks in the
                                  workspace (H_r is never stored), and a final pass rounds them into C.  The path
                                  for descriptions that are not a built-in scheme, and the unfused ablation of
                                  the fused path for the built-in one */
+    LCMA_COMBINE_L2_ON_CHIP = 4 /* two levels only (pre-pass as above): all 49 products of an output coordinate
+                                 run in one group on one workgroup and the 16 outputs accumulate on chip.  The
+                                 register file holds 17 accumulator tiles only at 64 x 64 group tiles, so this
+                                 runs far below the default; kept as the literal form of the fused group */
 } lcma_combine;
 
 /*
@@ -120,7 +129,8 @@ typedef struct {
     double classic_eff;     /* fraction of peak_tflops the classic kernel sustains when compute-bound;
                                0 = 0.52 (measured on MI355X at 4096^3 .. 16384^3) */
     double fused_eff;       /* the same for the fused group kernel (both levels);
-                               0 = 0.31 for one level, 0.037 for two levels (measured) */
+                               0 = 0.31 for one level and for two levels with the outer level in
+                               memory, 0.037 for LCMA_COMBINE_L2_ON_CHIP (measured) */
 } lcma_options;
 
 typedef struct lcma_plan_s* lcma_plan_t;

@@ -313,8 +313,15 @@ def test_schedule_covers_every_product_once(M, cus):
 def test_forced_split_modes(split):
     p = L.lcma_plan_ex(1024, 1024, 1024, "f16", force="l1", split=split, num_cus=256)
     _check_schedule(p, 7, split)
+    # two levels: the schedule of one outer launch (7 inner products per
+    # group tile over the M/4 x N/4 blocks), shared by all 7 launches
     p2 = L.lcma_plan_ex(1024, 1024, 1024, "bf16", force="l2", split=split, num_cus=256)
-    _check_schedule(p2, 49, split)
+    _, G2, _ = _check_schedule(p2, 7, split)
+    assert G2 == (256 // 128) ** 2
+    # all 49 products in one group on chip
+    p3 = L.lcma_plan_ex(1024, 1024, 1024, "bf16", force="l2", split=split, combine="l2_on_chip", num_cus=256)
+    _, G3, _ = _check_schedule(p3, 49, split)
+    assert G3 == (256 // 64) ** 2
 
 
 def test_split_pieces_of_a_group_sit_on_adjacent_workers():

@@ -188,13 +188,13 @@ def test_l1_square_512_f16_matches_oracle_and_ratio():
     assert metrics.e_rel(si.f64(C1), C_sh) <= 2 * metrics.UNIT_ROUNDOFF["f16"]
 
 
-@pytest.mark.parametrize("algo", ["l1", "l2"])
-def test_lcma_integer_inputs_are_exact(algo):
-    say("exact", algo)
+@pytest.mark.parametrize("algo,combine", [("l1", "auto"), ("l2", "auto"), ("l2", "l2_on_chip")])
+def test_lcma_integer_inputs_are_exact(algo, combine):
+    say("exact", algo, combine)
     A, B, A64, B64 = gen(**si.SQUARE_512_F16_INT)
-    check_exact(planned(A, B, algo), A64, B64, "f16")
+    check_exact(planned(A, B, algo, combine=combine), A64, B64, "f16")
     A, B, A64, B64 = gen(256, 512, 384, "bf16", "int1", seed=2)
-    check_exact(planned(A, B, algo), A64, B64, "bf16")
+    check_exact(planned(A, B, algo, combine=combine), A64, B64, "bf16")
 
 
 @pytest.mark.parametrize("ops", [-1, 1])
@@ -344,6 +344,33 @@ def test_l2_bf16_matches_oracle_and_ratio():
     C_sh, n = oracle.lcma(A64, B64, oracle.strassen2(), 1, round_operands="f16")
     assert n == 49
     assert metrics.e_rel(si.f64(C2), C_sh) <= 2 * metrics.UNIT_ROUNDOFF["bf16"]
+
+
+def test_l2_on_chip_matches_oracle():
+    say("l2 on chip bf16")
+    A, B, A64, B64 = gen(1024, 1024, 1024, "bf16", "normal_sqrtk", seed=17)
+    C_ref = oracle.gemm(A64, B64)
+    e_c = check_float(classic(A, B), A64, B64, "bf16", C_ref)
+    C2 = planned(A, B, "l2", combine="l2_on_chip")
+    e_2 = check_float(C2, A64, B64, "bf16", C_ref, blocks=4)
+    assert e_2 <= 4 * e_c
+    say("l2 on chip f16 split")
+    A, B, A64, B64 = gen(512, 768, 1024, "f16", "uniform", seed=19)
+    check_float(planned(A, B, "l2", combine="l2_on_chip", split="all"), A64, B64, "f16", blocks=4)
+
+
+@pytest.mark.parametrize("split", ["auto", "none", "all"])
+def test_l2_outer_level_ragged_blocks(split):
+    # blocks of 272 x 136 x 264: the 128-row group tiles end ragged in M and
+    # N, k-tiles ragged in K; every split mode of the outer launches
+    say("l2 ragged", split)
+    A, B, A64, B64 = gen(1088, 1056, 544, "bf16", "normal_sqrtk", seed=23)
+    C_ref = oracle.gemm(A64, B64)
+    e_c = check_float(classic(A, B), A64, B64, "bf16", C_ref)
+    C2 = planned(A, B, "l2", split=split)
+    e_2 = check_float(C2, A64, B64, "bf16", C_ref, blocks=4)
+    assert e_2 <= 4 * e_c
+    assert np.array_equal(si.bits(C2), si.bits(planned(A, B, "l2", split=split)))
 
 
 def test_l2_f16_and_split_all():
