@@ -495,8 +495,11 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         for (int x = 0; x < gen.rank * gen.ms * gen.ns; ++x)
             nnzW += gen.W[x] != 0;
         const double pre = 2.0 * ((double)M * K + (double)K * N) + 2.0 * gen.rank * ((double)Mb * Kb + (double)Kb * Nb);
-        const double comb = 8.0 * nnzW * (double)Mb * Nb + 6.0 * (double)M * N;
-        est[LCMA_ALGO_L1] = (pre + comb) / (m.eta_bw * m.bw) + gen.rank * est_classic(Mb, Nb, Kb, m) + 3 * m.launch;
+        // fold traffic per element of an output block fed by c products:
+        // 4 bytes stored by the first, 8 read and written by each middle one,
+        // 4 read by the last (which writes 2 bytes of C): 8c - 6
+        const double comb = (8.0 * nnzW - 6.0 * gen.ms * gen.ns) * (double)Mb * Nb;
+        est[LCMA_ALGO_L1] = (pre + comb) / (m.eta_bw * m.bw) + gen.rank * est_classic(Mb, Nb, Kb, m) + 2 * m.launch;
     } else if (ok1) {
         est[LCMA_ALGO_L1] = est_lcma(M, N, K, 1, o.split, op_bf16_for(1) != (dt == LCMA_BF16), false, m);
     }
@@ -895,14 +898,30 @@ lcma_status do_gen_prepass(const lcma_plan_s* p, const void* A, int64_t lda, con
     return hip_status(launch_gen_prepass(L, st), "launch_gen_prepass");
 }
 
-// Unfused path, product half: clear the fp32 output blocks, one GEMM per
-// product adding W[r][i,j] * H_r into them, then round into C.
+// Unfused path, product half: one GEMM per product, whose epilogue folds
+// W[r][i,j] * H_r into output block (i, j).  The first product feeding a
+// block stores its fp32 sum in the workspace, later ones add, and the last
+// one rounds it into C (a block fed by one product goes straight to C), so
+// no fill or final rounding pass is needed.  Brent's identity gives every
+// output block at least one product.
 lcma_status do_gen_products(const lcma_plan_s* p, void* C, int64_t ldc, void* ws, hipStream_t st)
 {
     float* acc = (float*)((char*)ws + p->offGC);
     const int nout = p->gms * p->gns;
-    if (hip_status(launch_fill_f32(acc, (int64_t)nout * p->gMb * p->gNb, 0.0f, st), "launch_fill_f32") != LCMA_OK)
-        return LCMA_E_HIP;
+    int first[kGenMaxBlocks], last[kGenMaxBlocks], uses[kGenMaxBlocks];
+    for (int o = 0; o < nout; ++o) {
+        first[o] = last[o] = -1;
+        uses[o] = 0;
+        for (int r = 0; r < p->gR; ++r)
+            if (p->gW[r * kGenMaxBlocks + o] != 0) {
+                if (first[o] < 0)
+                    first[o] = r;
+                last[o] = r;
+                ++uses[o];
+            }
+        if (uses[o] == 0)
+            return LCMA_E_BAD_DESCRIPTOR;
+    }
     for (int r = 0; r < p->gR; ++r) {
         GenProductLaunch L;
         memset(&L, 0, sizeof L);
@@ -910,11 +929,18 @@ lcma_status do_gen_products(const lcma_plan_s* p, void* C, int64_t ldc, void* ws
         L.B = (const char*)ws + p->offGB + (int64_t)r * p->gKb * p->gNb * 2; L.ldb = p->gNb;
         L.M = (int32_t)p->gMb; L.N = (int32_t)p->gNb; L.K = (int32_t)p->gKb;
         L.op_bf16 = p->op_bf16; L.P = p->P; L.ldt = p->gNb;
+        L.ldc = ldc; L.out_bf16 = p->dt == LCMA_BF16;
         for (int o = 0; o < nout; ++o) {
             const int w = p->gW[r * kGenMaxBlocks + o];
             if (w != 0) {
+                const int bi = o / p->gns, bj = o % p->gns;
                 L.tgt[L.ntgt] = acc + (int64_t)o * p->gMb * p->gNb;
+                L.cdst[L.ntgt] = (uint16_t*)C + bi * p->gMb * ldc + bj * p->gNb;
                 L.w[L.ntgt] = (float)w;
+                L.mode[L.ntgt] = uses[o] == 1 ? kOuterOnly
+                                 : r == first[o] ? kOuterStore
+                                 : r == last[o]  ? kOuterFinish
+                                                 : kOuterAdd;
                 ++L.ntgt;
             }
         }
@@ -923,10 +949,7 @@ lcma_status do_gen_products(const lcma_plan_s* p, void* C, int64_t ldc, void* ws
         if (hip_status(launch_gen_product(L, st), "launch_gen_product") != LCMA_OK)
             return LCMA_E_HIP;
     }
-    GenCastLaunch L;
-    L.src = acc; L.rows = (int32_t)p->gMb; L.cols = (int32_t)p->gNb; L.bcols = p->gns; L.nblocks = nout;
-    L.C = C; L.ldc = ldc; L.out_bf16 = p->dt == LCMA_BF16;
-    return hip_status(launch_gen_cast(L, st), "launch_gen_cast");
+    return LCMA_OK;
 }
 
 lcma_status check_lcma_call(const lcma_plan_s* p, const void* A, int64_t lda, const void* B, int64_t ldb,

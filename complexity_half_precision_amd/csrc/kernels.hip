@@ -19,6 +19,13 @@
 //                    (7 inner products on M/4 x N/4 blocks, fused the same
 //                    way) and folds the 4 inner outputs into fp32 output
 //                    blocks in memory, rounding into C at the last touch.
+//  * k_gen_prepass, k_gen_product(_m16) -- the unfused path for any valid
+//                    description: a runtime-coefficient combination pass, then
+//                    one GEMM per product (256 x 256 tiles on the 16x16x32
+//                    engine when they fill the chip, 128 x 128 on the
+//                    four-wave engine otherwise) whose epilogue folds W * H
+//                    into fp32 output blocks and rounds into C at the last
+//                    product feeding each block.
 //  * k_fused<2>   -- all 49 products of one output coordinate on one
 //                    workgroup (16 outputs on chip, 64 x 64 tiles) on the
 //                    register-staged path.
@@ -1431,18 +1438,54 @@ k_classic_q4(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, 
         store_c<C, BF, false>(acc, Cm + (int64_t)m0 * ldc + n0, ldc, M - m0, N - n0, wm, wn, lane);
 }
 
-// One product of the unfused path: the same engine, with an epilogue that
-// adds w[t] * H into fp32 targets (read-modify-write, 16 bytes per lane)
-// instead of storing H.  Products run one after another on the stream, so
-// no two launches touch a target at the same time.
+// One product of the unfused path, with an epilogue that folds w[t] * H into
+// output targets instead of storing H (modes as in the two-level outer
+// level: store, add, add and round into C, round into C).  Products run one
+// after another on the stream, so no two launches touch a target at the same
+// time.
 struct GenTargets {
     float* tgt[kGenMaxBlocks];
+    u16* cdst[kGenMaxBlocks];
     float w[kGenMaxBlocks];
+    int8_t mode[kGenMaxBlocks];
     int ntgt;
-    int64_t ldt;
+    int64_t ldt, ldc;
 };
 
-template <class C, bool BF>
+// `each(f)` calls f(m, n, h) for every 4-column group h of the wave's
+// accumulators (m, n relative to the tile origin m0, n0).  N is a multiple of
+// 8 on this path, so a group is wholly inside the columns or wholly out.
+template <bool CBF, class Each>
+__device__ __forceinline__ void gen_fold(const GenTargets& tg, int m0, int n0, int rows, int cols, Each each)
+{
+    const int ld = (int)tg.ldt, ldc = (int)tg.ldc;
+    for (int t = 0; t < tg.ntgt; ++t) {
+        const int mode = tg.mode[t];
+        const float wt = tg.w[t];
+        const rsrc_t rt = make_rsrc(tg.tgt[t] + (int64_t)m0 * tg.ldt + n0);
+        const rsrc_t rc = make_rsrc(tg.cdst[t] + (int64_t)m0 * tg.ldc + n0);
+        each([&](int m, int n, const f32x4& h) {
+            const bool ok = m < rows && n < cols;
+            const u32 off = ok ? (u32)(m * ld + n) * 4u : kOob;
+            f32x4 v = h * wt;
+            if (mode == kOuterAdd || mode == kOuterFinish)
+                v += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0));
+            if (mode == kOuterStore || mode == kOuterAdd) {
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), rt, off, 0, 0);
+            } else {
+                const u32 oc = ok ? (u32)(m * ldc + n) * 2u : kOob;
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
+                                       u32x2{pack2<CBF>(v.x, v.y), pack2<CBF>(v.z, v.w)}),
+                    rc, oc, 0, 0);
+            }
+        });
+    }
+}
+
+// On the four-wave 32x32 engine (128 x 128 tiles; shapes with few tiles).
+template <class C, bool BF, bool CBF>
 __global__ void __launch_bounds__(C::NT, 1)
 k_gen_product(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb, int M, int N, int K,
               int gy, int gx, int P, const GenTargets tg)
@@ -1471,31 +1514,59 @@ k_gen_product(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B,
         q4::run_tile<C, BF, true, false>(smem, nk, src, none, wave, lane, ad, acc);
     // lane l of MFMA tile (i, j) holds row (l % 32) and, per group g of 4
     // accumulators, columns 8 g + 4 (l / 32) .. + 3
-    const int ld = (int)tg.ldt;
     const int r = lane & 31, hi = lane >> 5;
-    for (int t = 0; t < tg.ntgt; ++t) {
-        const rsrc_t rt = make_rsrc(tg.tgt[t] + (int64_t)m0 * tg.ldt + n0);
-        const float wt = tg.w[t];
+    gen_fold<CBF>(tg, m0, n0, M - m0, N - n0, [&](auto f) {
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
             for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int m = wm * C::WTM + i * 32 + r, n = wn * C::WTN + j * 32 + 8 * g + 4 * hi;
-                    const u32 off = (m < M - m0 && n < N - n0) ? (u32)(m * ld + n) * 4u : kOob;
-                    f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0));
-                    v.x += wt * acc[i][j][4 * g];
-                    v.y += wt * acc[i][j][4 * g + 1];
-                    v.z += wt * acc[i][j][4 * g + 2];
-                    v.w += wt * acc[i][j][4 * g + 3];
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), rt, off, 0, 0);
-                }
-    }
+                for (int g = 0; g < 4; ++g)
+                    f(wm * C::WTM + i * 32 + r, wn * C::WTN + j * 32 + 8 * g + 4 * hi,
+                      f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]});
+    });
 }
 
-template <class C, bool BF>
+// On the 8-wave 16x16x32 engine with 256 x 256 tiles (the classic kernel's),
+// for products with at least one full round of tiles.
+template <class C, bool BF, bool CBF>
+__global__ void __launch_bounds__(C::NT, 1)
+k_gen_product_m16(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb, int M, int N,
+                  int K, int gy, int gx, int P, const GenTargets tg)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_ALLOC];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    int p, q;
+    tile_coords((int32_t)blockIdx.x, gy, gx, P, 8, &p, &q);
+    const int m0 = p * C::BM, n0 = q * C::BN;
+    const u16* Ab = A + (int64_t)m0 * lda;
+    const u16* Bb = B + n0;
+    const int nk = (K + C::BK - 1) / C::BK;
+    f32x4 acc[C::FM][C::FN];
+    zero_acc<C>(acc);
+    auto src = [&](int t) {
+        return tiles::TileSrc{Ab, (int)lda, M - m0, Bb, (int)ldb, N - n0, t * C::BK, K};
+    };
+    const m16::Addr<C> ad = m16::frag_addr<C>(wm, wn, lane);
+    auto none = [](int) {};
+    const bool inside = (m0 + C::BM <= M) & (n0 + C::BN <= N) & (K % C::BK == 0);
+    if (inside)
+        m16::run_tile<C, BF, false, true>(smem, nk, src, none, wave, lane, ad, acc);
+    else
+        m16::run_tile<C, BF, true, false>(smem, nk, src, none, wave, lane, ad, acc);
+    // lane l of MFMA tile (i, j) holds row 16 i + l % 16, columns 16 j + 4 (l / 16) .. + 3
+    gen_fold<CBF>(tg, m0, n0, M - m0, N - n0, [&](auto f) {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                f(wm * C::WTM + i * 16 + (lane & 15), wn * C::WTN + j * 16 + 4 * (lane >> 4), acc[i][j]);
+    });
+}
+
+template <class C, bool BF, bool CBF, bool M16>
 hipError_t launch_gen_product_t(const GenProductLaunch& L, hipStream_t st)
 {
     const int gy = (L.M + C::BM - 1) / C::BM, gx = (L.N + C::BN - 1) / C::BN;
@@ -1505,12 +1576,19 @@ hipError_t launch_gen_product_t(const GenProductLaunch& L, hipStream_t st)
     GenTargets tg{};
     for (int t = 0; t < L.ntgt; ++t) {
         tg.tgt[t] = L.tgt[t];
+        tg.cdst[t] = (u16*)L.cdst[t];
         tg.w[t] = L.w[t];
+        tg.mode[t] = L.mode[t];
     }
     tg.ntgt = L.ntgt;
     tg.ldt = L.ldt;
-    hipLaunchKernelGGL((k_gen_product<C, BF>), dim3((unsigned)tiles), dim3(C::NT), 0, st, (const u16*)L.A, L.lda,
-                       (const u16*)L.B, L.ldb, L.M, L.N, L.K, gy, gx, L.P, tg);
+    tg.ldc = L.ldc;
+    if constexpr (M16)
+        hipLaunchKernelGGL((k_gen_product_m16<C, BF, CBF>), dim3((unsigned)tiles), dim3(C::NT), 0, st,
+                           (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, L.M, L.N, L.K, gy, gx, L.P, tg);
+    else
+        hipLaunchKernelGGL((k_gen_product<C, BF, CBF>), dim3((unsigned)tiles), dim3(C::NT), 0, st,
+                           (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, L.M, L.N, L.K, gy, gx, L.P, tg);
     return hipGetLastError();
 }
 
@@ -1779,26 +1857,6 @@ hipError_t launch_gen_prepass_t(const GenPrepassLaunch& L, hipStream_t st)
     hipLaunchKernelGGL((k_gen_prepass<IBF, OBF>), dim3((unsigned)((chunks + 255) / 256), (unsigned)L.rank), dim3(256),
                        0, st, gp);
     return hipGetLastError();
-}
-
-__global__ void __launch_bounds__(256) k_fill_f32(float* __restrict__ p, int64_t n, float v)
-{
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-        p[i] = v;
-}
-
-template <bool BF>
-__global__ void __launch_bounds__(256) k_gen_cast(const float* __restrict__ src, int rows, int cols, int bcols,
-                                                  int nblocks, u16* __restrict__ C, int64_t ldc)
-{
-    const int64_t per = (int64_t)rows * cols;
-    const int64_t n = per * nblocks;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-        const int b = (int)(i / per);
-        const int64_t e = i % per;
-        const int row = (int)(e / cols), col = (int)(e % cols);
-        C[(int64_t)((b / bcols) * rows + row) * ldc + (int64_t)(b % bcols) * cols + col] = f2h<BF>(src[i]);
-    }
 }
 
 // ------------------------------------------------------------------ fused group kernel
@@ -2233,34 +2291,19 @@ hipError_t launch_gen_prepass(const GenPrepassLaunch& L, hipStream_t st)
 
 hipError_t launch_gen_product(const GenProductLaunch& L, hipStream_t st)
 {
+    // 256 x 256 tiles on the 16x16x32 engine once they fill a round of the
+    // compute units; 128 x 128 tiles on the four-wave engine below that.
     const int64_t t256 = (int64_t)((L.M + 255) / 256) * ((L.N + 255) / 256);
-    if (t256 >= L.P)
-        return L.op_bf16 ? launch_gen_product_t<QC256, true>(L, st) : launch_gen_product_t<QC256, false>(L, st);
-    return L.op_bf16 ? launch_gen_product_t<QC128, true>(L, st) : launch_gen_product_t<QC128, false>(L, st);
-}
-
-hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st)
-{
-    if (n <= 0)
-        return hipSuccess;
-    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
-    hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)blocks), dim3(256), 0, st, p, n, v);
-    return hipGetLastError();
-}
-
-hipError_t launch_gen_cast(const GenCastLaunch& L, hipStream_t st)
-{
-    const int64_t n = (int64_t)L.rows * L.cols * L.nblocks;
-    if (n <= 0)
-        return hipSuccess;
-    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
+    if (t256 >= L.P) {
+        if (L.out_bf16)
+            return L.op_bf16 ? launch_gen_product_t<MC256, true, true, true>(L, st)
+                             : launch_gen_product_t<MC256, false, true, true>(L, st);
+        return launch_gen_product_t<MC256, false, false, true>(L, st);
+    }
     if (L.out_bf16)
-        hipLaunchKernelGGL(k_gen_cast<true>, dim3((unsigned)blocks), dim3(256), 0, st, L.src, L.rows, L.cols, L.bcols,
-                           L.nblocks, (u16*)L.C, L.ldc);
-    else
-        hipLaunchKernelGGL(k_gen_cast<false>, dim3((unsigned)blocks), dim3(256), 0, st, L.src, L.rows, L.cols,
-                           L.bcols, L.nblocks, (u16*)L.C, L.ldc);
-    return hipGetLastError();
+        return L.op_bf16 ? launch_gen_product_t<QC128, true, true, false>(L, st)
+                         : launch_gen_product_t<QC128, false, true, false>(L, st);
+    return launch_gen_product_t<QC128, false, false, false>(L, st);
 }
 
 }  // namespace lcma

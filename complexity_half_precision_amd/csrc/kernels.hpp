@@ -97,24 +97,21 @@ struct GenPrepassLaunch {
 };
 hipError_t launch_gen_prepass(const GenPrepassLaunch& L, hipStream_t stream);
 
-// One product H = Ahat * Bhat (M x N x K) whose epilogue adds w[t] * H into
-// fp32 targets t (each M x N, leading dimension ldt), in place of storing H.
+// One product H = Ahat * Bhat (M x N x K) whose epilogue folds w[t] * H into
+// targets t (each M x N) in place of storing H: the first product feeding an
+// output stores its fp32 block, later ones add, the last adds and rounds into
+// C, and an output fed once is rounded straight into C.
 struct GenProductLaunch {
     const void* A; int64_t lda;
     const void* B; int64_t ldb;
     int32_t M, N, K, op_bf16, P;
-    float* tgt[kGenMaxBlocks]; float w[kGenMaxBlocks]; int32_t ntgt; int64_t ldt;
+    // Targets: fp32 output blocks (ld = ldt) folded with w[t] * H in mode[t]
+    // (an OuterMode); the finishing modes round into cdst[t] (ld = ldc) of
+    // the storage type (out_bf16).
+    float* tgt[kGenMaxBlocks]; float w[kGenMaxBlocks]; int8_t mode[kGenMaxBlocks]; int32_t ntgt; int64_t ldt;
+    void* cdst[kGenMaxBlocks]; int64_t ldc; int32_t out_bf16;
 };
 hipError_t launch_gen_product(const GenProductLaunch& L, hipStream_t stream);
-
-// fp32 fill, and the final cast: block t (row t / bcols, column t % bcols) of
-// nblocks fp32 blocks (rows x cols, ld = cols) to C in the storage type.
-hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
-struct GenCastLaunch {
-    const float* src; int32_t rows, cols, bcols, nblocks;
-    void* C; int64_t ldc; int32_t out_bf16;
-};
-hipError_t launch_gen_cast(const GenCastLaunch& L, hipStream_t stream);
 
 int32_t fused_tile(int32_t levels);
 // Bytes of one split partial (all output blocks of one group, fp32).
