@@ -1806,33 +1806,47 @@ struct GenPrepassParams {
     int64_t ldo, stride;
 };
 
+// One thread per 8-element chunk position of a block: it reads that chunk of
+// every block once (at most kGenMaxBlocks, held in registers), then writes
+// the chunk of every combined operand, each summed in fp32 and rounded once.
 template <bool IBF, bool OBF>
 __global__ void __launch_bounds__(256) k_gen_prepass(const GenPrepassParams gp)
 {
-    const int r = blockIdx.y;                          // product
     const int cpr = gp.cols / 8;                       // chunks per row
     const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (c >= (int64_t)gp.rows * cpr)
         return;
     const int row = (int)(c / cpr), col = (int)(c % cpr) * 8;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int b = 0; b < gp.nblocks; ++b) {
-        const int w = gp.coef[r * kGenMaxBlocks + b];
-        if (w == 0)
-            continue;
-        const int br = b / gp.bcols, bc = b % gp.bcols;
-        const u16* src = gp.X + (int64_t)(br * gp.rows + row) * gp.ldx + (int64_t)bc * gp.cols + col;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
-        const float fw = (float)w;
+    u32x4 v[kGenMaxBlocks];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc[2 * e] += fw * h2f<IBF>((u16)(v[e] & 0xffffu));
-            acc[2 * e + 1] += fw * h2f<IBF>((u16)(v[e] >> 16));
+    for (int b = 0; b < kGenMaxBlocks; ++b) {
+        if (b < gp.nblocks) {
+            const int br = b / gp.bcols, bc = b % gp.bcols;
+            v[b] = *reinterpret_cast<const u32x4*>(gp.X + (int64_t)(br * gp.rows + row) * gp.ldx +
+                                                   (int64_t)bc * gp.cols + col);
         }
     }
-    const u32x4 o{pack2<OBF>(acc[0], acc[1]), pack2<OBF>(acc[2], acc[3]), pack2<OBF>(acc[4], acc[5]),
+    u16* out = gp.out + (int64_t)row * gp.ldo + col;
+    for (int r = 0; r < gp.rank; ++r) {
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int b = 0; b < kGenMaxBlocks; ++b) {
+            if (b < gp.nblocks) {
+                const int w = gp.coef[r * kGenMaxBlocks + b];
+                if (w != 0) {
+                    const float fw = (float)w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[2 * e] += fw * h2f<IBF>((u16)(v[b][e] & 0xffffu));
+                        acc[2 * e + 1] += fw * h2f<IBF>((u16)(v[b][e] >> 16));
+                    }
+                }
+            }
+        }
+        *reinterpret_cast<u32x4*>(out + (int64_t)r * gp.stride) =
+            u32x4{pack2<OBF>(acc[0], acc[1]), pack2<OBF>(acc[2], acc[3]), pack2<OBF>(acc[4], acc[5]),
                   pack2<OBF>(acc[6], acc[7])};
-    *reinterpret_cast<u32x4*>(gp.out + (int64_t)r * gp.stride + (int64_t)row * gp.ldo + col) = o;
+    }
 }
 
 template <bool IBF, bool OBF>
@@ -1854,8 +1868,7 @@ hipError_t launch_gen_prepass_t(const GenPrepassLaunch& L, hipStream_t st)
     gp.out = (u16*)L.out;
     gp.ldo = L.ldo;
     gp.stride = L.stride;
-    hipLaunchKernelGGL((k_gen_prepass<IBF, OBF>), dim3((unsigned)((chunks + 255) / 256), (unsigned)L.rank), dim3(256),
-                       0, st, gp);
+    hipLaunchKernelGGL((k_gen_prepass<IBF, OBF>), dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, gp);
     return hipGetLastError();
 }
 
