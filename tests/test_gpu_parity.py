@@ -359,6 +359,20 @@ def test_l2_on_chip_matches_oracle():
     check_float(planned(A, B, "l2", combine="l2_on_chip", split="all"), A64, B64, "f16", blocks=4)
 
 
+@pytest.mark.parametrize("combine", ["auto", "l2_on_chip"])
+def test_l2_bf16_operands_match_the_oracle_with_the_same_rounding(combine):
+    # bfloat16 combined operands (not the default for two levels): the GPU
+    # result must equal the oracle's evaluation of the same scheme with the
+    # same operand rounding up to fp32 accumulation order and the final cast
+    say("l2 bf16 operands", combine)
+    A, B, A64, B64 = gen(512, 1024, 768, "bf16", "normal_sqrtk", seed=29)
+    C2 = planned(A, B, "l2", combine=combine, bf16_ops_f16=-1)
+    check_float(C2, A64, B64, "bf16", blocks=4)
+    C_sh, n = oracle.lcma(A64, B64, oracle.strassen2(), 1, round_operands="bf16")
+    assert n == 49
+    assert metrics.e_rel(si.f64(C2), C_sh) <= 2 * metrics.UNIT_ROUNDOFF["bf16"]
+
+
 @pytest.mark.parametrize("split", ["auto", "none", "all"])
 def test_l2_outer_level_ragged_blocks(split):
     # blocks of 272 x 136 x 264: the 128-row group tiles end ragged in M and
