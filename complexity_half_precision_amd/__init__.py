@@ -130,10 +130,18 @@ def _ld(t, default):
     return t.stride(0)
 
 
+def _current_stream():
+    # torch's raw handle of the current stream (one C call; building a
+    # torch.cuda.Stream object costs ~3 us per library call)
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
+
+
 def _stream(stream):
     if stream is None:
-        import torch
-        return torch.cuda.current_stream().cuda_stream
+        return _current_stream()
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
@@ -174,10 +182,12 @@ class Plan:
         self.handle = handle
         self.M, self.N, self.K, self.dtype = M, N, K, dtype
 
-    def __del__(self):
+    def __del__(self, _destroy=_lib_plan_destroy):
+        # the library function is bound at definition time: module globals may
+        # already be cleared when a plan dies at interpreter exit
         h, self.handle = getattr(self, "handle", None), None
         if h:
-            _lib_plan_destroy(h)
+            _destroy(h)
 
     @property
     def info(self):

@@ -455,3 +455,42 @@ def test_square_16384_bf16_sampled():
         assert metrics.freivalds(C, A64, B64, seeds=(11,)) <= 4 * u
         del C
     assert res["l1"] <= 4 * res["classic"] and res["l2"] <= 4 * res["classic"]
+
+
+# ---------------------------------------------------------------- graph capture
+
+@pytest.mark.parametrize("algo,kw", [("classic", {}), ("l1", {"split": "all"}), ("l2", {})])
+def test_graph_capture_replays_match_eager(algo, kw):
+    # Every path launches only kernels (the split counters are cleared by the
+    # pre-pass kernel, not a memset), so a call can be captured into a HIP
+    # graph; each replay, with eager work and synchronisation in between,
+    # must reproduce the eager result bit for bit.
+    say("graph", algo, kw)
+    M = N = K = 1024
+    A, B, _, _ = gen(M, N, K, "bf16", "normal_sqrtk", seed=31)
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    plan = L.lcma_plan_ex(M, N, K, "bf16", force=algo, **kw)
+    ws = L.workspace_for(plan)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    L.lcma_gemm(plan, Ad, Bd, C, ws)
+    torch.cuda.synchronize()
+    eager = C.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        L.lcma_gemm(plan, Ad, Bd, C, ws)      # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.lcma_gemm(plan, Ad, Bd, C, ws)
+    for rep in range(4):
+        C.fill_(float(rep + 1))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C, eager), rep
+        # eager work on the same buffers between replays
+        L.lcma_gemm(plan, Ad, Bd, C, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(C, eager), rep
