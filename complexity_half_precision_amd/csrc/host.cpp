@@ -204,9 +204,13 @@ double est_classic(int64_t M, int64_t N, int64_t K, const Machine& m)
     const double F = 2.0 * M * N * K;
     const double B = s * ((double)M * K + (double)K * N + (double)M * N);
     int bm, bn;
-    classic_tile_dims(classic_tile_for(M, N, m.P), &bm, &bn);
+    const int tile = classic_tile_for(M, N, m.P);
+    classic_tile_dims(tile, &bm, &bn);
     const double tiles = (double)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-    return kernel_time(F, B, (double)bm * bn / (bm + bn), quant(tiles, m.P), m.eta_mfma, m);
+    // the 128 x 128 kernel sustains less than the 256 x 256 one (measured
+    // 0.34-0.40 of peak against 0.50-0.55)
+    const double eta = tile == kTile128 ? m.eta_mfma * 0.7 : m.eta_mfma;
+    return kernel_time(F, B, (double)bm * bn / (bm + bn), quant(tiles, m.P), eta, m);
 }
 
 // Geometry of an LCMA plan at `levels`.
