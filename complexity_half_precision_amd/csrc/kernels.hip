@@ -37,13 +37,16 @@
 // combination, one final cast); "CUDA-L2 ..." section "核心贡献与发现的技术"
 // (multi-stage staging, wide epilogue stores, block swizzling).
 //
-// MFMA: v_mfma_f32_32x32x16_{f16,bf16} (16x16x32 in the two-level kernel).
-// Operands are fed swapped (the B fragment as the A operand), so the
-// accumulator of lane l holds 4 consecutive output columns of output row
-// (l % 32) per group of 4 registers, which the epilogue stores as one 8-byte
-// write.  The register-staged path stores B transposed in LDS (rows padded to
-// 144 bytes); the direct-to-LDS engines keep B row-major as in memory,
-// XOR-swizzled, and read it with ds_read_b64_tr_b16.
+// MFMA: v_mfma_f32_16x16x32_{f16,bf16} on the 16x16x32 engine (classic
+// 256 x 256 tiles, the fused one-level kernel, the unfused 256 x 256
+// products, the on-chip two-level kernel) and v_mfma_f32_32x32x16 on the
+// four-wave engine (128 x 128 tiles), the streaming kernel and the
+// register-staged fallback.  Operands are fed swapped (the B fragment as the
+// A operand), so each lane's accumulators hold 4 consecutive output columns
+// of one output row, stored as one 8-byte write (or staged through LDS for
+// 16-byte row segments).  The register-staged path stores B transposed in LDS
+// (rows padded to 144 bytes); the direct-to-LDS engines keep B row-major as
+// in memory, XOR-swizzled, and read it with ds_read_b64_tr_b16.
 
 #include <hip/hip_runtime.h>
 
@@ -161,7 +164,6 @@ struct Cfg {
 using Cfg256 = Cfg<256, 256, 2, 2, 32, 8>;   // classic: 4 waves of 128 x 128
 using Cfg128 = Cfg<128, 128, 2, 2, 32, 4>;   // classic: 4 waves of 64 x 64
 using Cfg32 = Cfg<32, 64, 1, 2, 32, 4>;      // classic skinny: 2 waves of 32 x 32
-using CfgF1 = Cfg<128, 128, 2, 4, 32, 2>;    // fused one-level: 8 waves of 64 x 32
 using CfgF2 = Cfg<64, 64, 4, 2, 16, 2>;      // fused two-level: 8 waves of 16 x 32 (16x16x32 MFMA)
 
 // Buffer resources: global loads and stores go through a buffer descriptor
@@ -627,12 +629,14 @@ struct TileSrc {
 
 // ------------------------------------------------------------------ four-wave engine
 //
-// One wave per SIMD, each owning a 128 x 128 output tile (16 MFMA tiles,
-// 256 accumulator registers): per byte read from LDS this does 1.5x the
-// MFMA work of a 128 x 64 wave tile.  k-tiles of 32 stream through a
-// 4-stage LDS ring by direct-to-LDS loads issued 3 tiles ahead; fragments
-// are double-buffered in registers by k-step, so the LDS reads of one k-step
-// run under the MFMAs of the other.  One barrier per k-tile.
+// One wave per SIMD on v_mfma_f32_32x32x16, a 2 x 2 grid of wave tiles
+// (here 128 x 128 workgroup tiles: 64 x 64 per wave, 4 MFMA tiles, 64
+// accumulator registers).  k-tiles of 32 stream through a 4-stage LDS ring
+// by direct-to-LDS loads issued 3 tiles ahead; fragments are double-buffered
+// in registers by k-step, so the LDS reads of one k-step run under the MFMAs
+// of the other.  One barrier per k-tile.  Used for classic products whose
+// 256 x 256 tiles would not fill the compute units, and for the unfused
+// path's products of that size.
 
 namespace q4 {
 
@@ -1399,7 +1403,6 @@ hipError_t launch_classic_m16_t(const ClassicLaunch& L, hipStream_t st)
     return hipGetLastError();
 }
 
-using QC256 = q4::QCfg<256, 256>;   // 4 waves of 128 x 128
 using QC128 = q4::QCfg<128, 128>;   // 4 waves of 64 x 64
 
 template <class C, bool BF>
@@ -1877,9 +1880,7 @@ hipError_t launch_gen_prepass_t(const GenPrepassLaunch& L, hipStream_t st)
 template <int LEVELS>
 struct FusedCfg;
 template <>
-struct FusedCfg<1> { using C = CfgF1; };
-template <>
-struct FusedCfg<2> { using C = CfgF2; };
+struct FusedCfg<2> { using C = CfgF2; };   // the on-chip two-level kernel
 
 // C_o += W[r][o] * H for every output block o.  The coefficients are
 // uniform kernel arguments; zero ones are skipped by a scalar branch.
@@ -2257,7 +2258,7 @@ hipError_t launch_prepass(const PrepassLaunch& L, hipStream_t st)
 
 int32_t fused_tile(int32_t levels) { return levels == 1 ? MCF1::BM : FusedCfg<2>::C::BM; }
 static_assert(MCF1::BM == MCF1::BN, "fused tiles are square");
-static_assert(FusedCfg<1>::C::BM == FusedCfg<1>::C::BN && FusedCfg<2>::C::BM == FusedCfg<2>::C::BN,
+static_assert(FusedCfg<2>::C::BM == FusedCfg<2>::C::BN,
               "fused tiles are square");
 
 int64_t fused_partial_bytes(int32_t levels)
