@@ -926,6 +926,31 @@ lcma_status do_gen_products(const lcma_plan_s* p, void* C, int64_t ldc, void* ws
         if (uses[o] == 0)
             return LCMA_E_BAD_DESCRIPTOR;
     }
+    // Enough 256 x 256 output positions for a round of the compute units:
+    // every product in one persistent launch, each position owned by one
+    // workgroup throughout.
+    const int64_t pos256 = ((p->gMb + 255) / 256) * ((p->gNb + 255) / 256);
+    if (pos256 >= p->P) {
+        GenGroupLaunch G;
+        memset(&G, 0, sizeof G);
+        G.A0 = (const char*)ws + p->offGA; G.strideA = p->gMb * p->gKb;
+        G.B0 = (const char*)ws + p->offGB; G.strideB = p->gKb * p->gNb;
+        G.M = (int32_t)p->gMb; G.N = (int32_t)p->gNb; G.K = (int32_t)p->gKb; G.R = p->gR;
+        G.op_bf16 = p->op_bf16; G.out_bf16 = p->dt == LCMA_BF16; G.P = p->P;
+        G.nout = nout; G.ncols = p->gns;
+        G.acc = acc; G.C = C; G.ldc = ldc;
+        for (int r = 0; r < p->gR; ++r)
+            for (int o = 0; o < nout; ++o) {
+                const int w = p->gW[r * kGenMaxBlocks + o];
+                G.w[r * kGenMaxBlocks + o] = (int8_t)w;
+                G.mode[r * kGenMaxBlocks + o] = w == 0           ? kOuterNone
+                                                : uses[o] == 1   ? kOuterOnly
+                                                : r == first[o]  ? kOuterStore
+                                                : r == last[o]   ? kOuterFinish
+                                                                 : kOuterAdd;
+            }
+        return hip_status(launch_gen_group(G, st), "launch_gen_group");
+    }
     for (int r = 0; r < p->gR; ++r) {
         GenProductLaunch L;
         memset(&L, 0, sizeof L);

@@ -19,13 +19,14 @@
 //                    (7 inner products on M/4 x N/4 blocks, fused the same
 //                    way) and folds the 4 inner outputs into fp32 output
 //                    blocks in memory, rounding into C at the last touch.
-//  * k_gen_prepass, k_gen_product(_m16) -- the unfused path for any valid
-//                    description: a runtime-coefficient combination pass, then
-//                    one GEMM per product (256 x 256 tiles on the 16x16x32
-//                    engine when they fill the chip, 128 x 128 on the
-//                    four-wave engine otherwise) whose epilogue folds W * H
-//                    into fp32 output blocks and rounds into C at the last
-//                    product feeding each block.
+//  * k_gen_prepass, k_gen_group_m16, k_gen_product(_m16) -- the unfused
+//                    path for any valid description: a runtime-coefficient
+//                    combination pass, then the products, each folding W * H
+//                    into fp32 output blocks and rounding into C at the last
+//                    product feeding a block.  With a round of 256 x 256
+//                    positions, one persistent launch runs every product per
+//                    position (k_gen_group_m16); otherwise one GEMM launch per
+//                    product (128 x 128 tiles on the four-wave engine).
 //  * k_fused<2>   -- all 49 products of one output coordinate on one
 //                    workgroup (16 outputs on chip, 64 x 64 tiles) on the
 //                    register-staged path.
@@ -1458,33 +1459,38 @@ struct GenTargets {
 // `each(f)` calls f(m, n, h) for every 4-column group h of the wave's
 // accumulators (m, n relative to the tile origin m0, n0).  N is a multiple of
 // 8 on this path, so a group is wholly inside the columns or wholly out.
+// One target of a fold: rt is the target's fp32 block and rc its C block,
+// both at the tile origin (ld, ldc elements per row).
+template <bool CBF, class Each>
+__device__ __forceinline__ void fold_target(rsrc_t rt, rsrc_t rc, int ld, int ldc, int mode, float wt, int rows,
+                                            int cols, Each each)
+{
+    each([&](int m, int n, const f32x4& h) {
+        const bool ok = m < rows && n < cols;
+        const u32 off = ok ? (u32)(m * ld + n) * 4u : kOob;
+        f32x4 v = h * wt;
+        if (mode == kOuterAdd || mode == kOuterFinish)
+            v += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0));
+        if (mode == kOuterStore || mode == kOuterAdd) {
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), rt, off, 0, 0);
+        } else {
+            const u32 oc = ok ? (u32)(m * ldc + n) * 2u : kOob;
+            __builtin_amdgcn_raw_buffer_store_b64(
+                __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
+                                   u32x2{pack2<CBF>(v.x, v.y), pack2<CBF>(v.z, v.w)}),
+                rc, oc, 0, 0);
+        }
+    });
+}
+
 template <bool CBF, class Each>
 __device__ __forceinline__ void gen_fold(const GenTargets& tg, int m0, int n0, int rows, int cols, Each each)
 {
-    const int ld = (int)tg.ldt, ldc = (int)tg.ldc;
-    for (int t = 0; t < tg.ntgt; ++t) {
-        const int mode = tg.mode[t];
-        const float wt = tg.w[t];
-        const rsrc_t rt = make_rsrc(tg.tgt[t] + (int64_t)m0 * tg.ldt + n0);
-        const rsrc_t rc = make_rsrc(tg.cdst[t] + (int64_t)m0 * tg.ldc + n0);
-        each([&](int m, int n, const f32x4& h) {
-            const bool ok = m < rows && n < cols;
-            const u32 off = ok ? (u32)(m * ld + n) * 4u : kOob;
-            f32x4 v = h * wt;
-            if (mode == kOuterAdd || mode == kOuterFinish)
-                v += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0));
-            if (mode == kOuterStore || mode == kOuterAdd) {
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), rt, off, 0, 0);
-            } else {
-                const u32 oc = ok ? (u32)(m * ldc + n) * 2u : kOob;
-                __builtin_amdgcn_raw_buffer_store_b64(
-                    __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
-                                       u32x2{pack2<CBF>(v.x, v.y), pack2<CBF>(v.z, v.w)}),
-                    rc, oc, 0, 0);
-            }
-        });
-    }
+    for (int t = 0; t < tg.ntgt; ++t)
+        fold_target<CBF>(make_rsrc(tg.tgt[t] + (int64_t)m0 * tg.ldt + n0),
+                         make_rsrc(tg.cdst[t] + (int64_t)m0 * tg.ldc + n0), (int)tg.ldt, (int)tg.ldc, tg.mode[t],
+                         tg.w[t], rows, cols, each);
 }
 
 // On the four-wave 32x32 engine (128 x 128 tiles; shapes with few tiles).
@@ -1567,6 +1573,101 @@ k_gen_product_m16(const u16* __restrict__ A, int64_t lda, const u16* __restrict_
             for (int j = 0; j < C::FN; ++j)
                 f(wm * C::WTM + i * 16 + (lane & 15), wn * C::WTN + j * 16 + 4 * (lane >> 4), acc[i][j]);
     });
+}
+
+// All products of the unfused path in one persistent launch: each workgroup
+// owns 256 x 256 output positions (round-robin) and, for each, runs every
+// product's K loop in turn and folds it into that position's blocks, so the
+// read-modify-write of a block is never shared between workgroups and the
+// folds of different workgroups fall at different times.
+struct GenGroupParams {
+    const u16* A0; int64_t strideA;    // combined A operand r at A0 + r * strideA (M x K, ld K)
+    const u16* B0; int64_t strideB;    // combined B operand r at B0 + r * strideB (K x N, ld N)
+    int M, N, K, R, P, nout, ncols;
+    float* acc;                        // fp32 block o at acc + o * M * N (ld N)
+    u16* C; int64_t ldc;               // block o of C at row (o / ncols) * M, column (o % ncols) * N
+    int8_t w[kGenMaxRank * kGenMaxBlocks];
+    int8_t mode[kGenMaxRank * kGenMaxBlocks];   // OuterMode per (product, block)
+};
+
+// EDGE: some position is a partial tile or K is not a multiple of 32 (then
+// every position takes the bounds-checked loads: one K-loop form per kernel
+// keeps the persistent loops within the register budget).
+template <class C, bool BF, bool CBF, bool EDGE>
+__global__ void __launch_bounds__(C::NT, 1) k_gen_group_m16(const GenGroupParams gp)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_ALLOC];
+    const int tid = threadIdx.x, lane0 = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int gy = (gp.M + C::BM - 1) / C::BM, gx = (gp.N + C::BN - 1) / C::BN;
+    const int nk = (gp.K + C::BK - 1) / C::BK;
+    auto none = [](int) {};
+    for (int item = blockIdx.x; item < gy * gx; item += gridDim.x) {
+        int p, q;
+        tile_coords(item, gy, gx, gp.P, 8, &p, &q);
+        const int m0 = p * C::BM, n0 = q * C::BN, rows = gp.M - m0, cols = gp.N - n0;
+        for (int r = 0; r < gp.R; ++r) {
+            // Opaque per product: keeps lane-derived addresses (fold offsets,
+            // fragment offsets) from being hoisted out of the loops and held
+            // in registers through every K loop.
+            int lane = lane0;
+            asm volatile("" : "+v"(lane));
+            const m16::Addr<C> ad = m16::frag_addr<C>(wm, wn, lane);
+            const u16* Ab = gp.A0 + r * gp.strideA + (int64_t)m0 * gp.K;
+            const u16* Bb = gp.B0 + r * gp.strideB + n0;
+            auto src = [&](int t) {
+                return tiles::TileSrc{Ab, gp.K, rows, Bb, gp.N, cols, t * C::BK, gp.K};
+            };
+            f32x4 acc[C::FM][C::FN];
+            zero_acc<C>(acc);
+            __syncthreads();   // every wave is done reading the ring of the previous product
+            m16::run_tile<C, BF, EDGE, !EDGE>(smem, nk, src, none, wave, lane, ad, acc);
+            for (int o = 0; o < gp.nout; ++o) {
+                const int mode = gp.mode[r * kGenMaxBlocks + o];
+                if (mode == kOuterNone)
+                    continue;
+                const int bi = o / gp.ncols, bj = o % gp.ncols;
+                fold_target<CBF>(make_rsrc(gp.acc + (int64_t)o * gp.M * gp.N + (int64_t)m0 * gp.N + n0),
+                                 make_rsrc(gp.C + (int64_t)(bi * gp.M + m0) * gp.ldc + bj * gp.N + n0), gp.N,
+                                 (int)gp.ldc, mode, (float)gp.w[r * kGenMaxBlocks + o], rows, cols,
+                                 [&](auto f) {
+#pragma unroll
+                                     for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                                         for (int j = 0; j < C::FN; ++j)
+                                             f(wm * C::WTM + i * 16 + (lane & 15),
+                                               wn * C::WTN + j * 16 + 4 * (lane >> 4), acc[i][j]);
+                                 });
+            }
+        }
+    }
+}
+
+template <bool BF, bool CBF>
+hipError_t launch_gen_group_t(const GenGroupLaunch& L, hipStream_t st)
+{
+    using C = MC256;
+    const int items = ((L.M + C::BM - 1) / C::BM) * ((L.N + C::BN - 1) / C::BN);
+    if (items == 0 || L.R == 0)
+        return hipSuccess;
+    GenGroupParams gp;
+    gp.A0 = (const u16*)L.A0; gp.strideA = L.strideA;
+    gp.B0 = (const u16*)L.B0; gp.strideB = L.strideB;
+    gp.M = L.M; gp.N = L.N; gp.K = L.K; gp.R = L.R; gp.P = L.P; gp.nout = L.nout; gp.ncols = L.ncols;
+    gp.acc = L.acc;
+    gp.C = (u16*)L.C; gp.ldc = L.ldc;
+    for (int i = 0; i < kGenMaxRank * kGenMaxBlocks; ++i) {
+        gp.w[i] = L.w[i];
+        gp.mode[i] = L.mode[i];
+    }
+    const bool edge = L.M % C::BM != 0 || L.N % C::BN != 0 || L.K % C::BK != 0;
+    const dim3 grid((unsigned)std::min(items, L.P));
+    if (edge)
+        hipLaunchKernelGGL((k_gen_group_m16<C, BF, CBF, true>), grid, dim3(C::NT), 0, st, gp);
+    else
+        hipLaunchKernelGGL((k_gen_group_m16<C, BF, CBF, false>), grid, dim3(C::NT), 0, st, gp);
+    return hipGetLastError();
 }
 
 template <class C, bool BF, bool CBF, bool M16>
@@ -2301,6 +2402,13 @@ hipError_t launch_gen_prepass(const GenPrepassLaunch& L, hipStream_t st)
     if (L.in_bf16)
         return L.op_bf16 ? launch_gen_prepass_t<true, true>(L, st) : launch_gen_prepass_t<true, false>(L, st);
     return L.op_bf16 ? launch_gen_prepass_t<false, true>(L, st) : launch_gen_prepass_t<false, false>(L, st);
+}
+
+hipError_t launch_gen_group(const GenGroupLaunch& L, hipStream_t st)
+{
+    if (L.out_bf16)
+        return L.op_bf16 ? launch_gen_group_t<true, true>(L, st) : launch_gen_group_t<false, true>(L, st);
+    return launch_gen_group_t<false, false>(L, st);
 }
 
 hipError_t launch_gen_product(const GenProductLaunch& L, hipStream_t st)

@@ -113,6 +113,22 @@ struct GenProductLaunch {
 };
 hipError_t launch_gen_product(const GenProductLaunch& L, hipStream_t stream);
 
+// All products of the unfused path in one persistent launch (256 x 256
+// positions, one workgroup per position for every product; same fold modes
+// per (product, block)).  Combined operand r: A0 + r * strideA (M x K, ld K),
+// B0 + r * strideB (K x N, ld N); fp32 block o at acc + o * M * N (ld N);
+// block o of C at row (o / ncols) * M, column (o % ncols) * N.
+struct GenGroupLaunch {
+    const void* A0; int64_t strideA;
+    const void* B0; int64_t strideB;
+    int32_t M, N, K, R, op_bf16, out_bf16, P, nout, ncols;
+    float* acc;
+    void* C; int64_t ldc;
+    int8_t w[kGenMaxRank * kGenMaxBlocks];
+    int8_t mode[kGenMaxRank * kGenMaxBlocks];
+};
+hipError_t launch_gen_group(const GenGroupLaunch& L, hipStream_t stream);
+
 int32_t fused_tile(int32_t levels);
 // Bytes of one split partial (all output blocks of one group, fp32).
 int64_t fused_partial_bytes(int32_t levels);

@@ -295,6 +295,26 @@ def planned_desc(A, B, desc, **kw):
     return C.cpu()
 
 
+@pytest.mark.parametrize("M,N,K,dtype,scheme", [(8192, 8192, 512, "bf16", "builtin"),
+                                                (8208, 8192, 528, "f16", "winograd")])
+def test_unfused_group_kernel_matches_oracle(M, N, K, dtype, scheme):
+    # blocks of at least 4096 x 4096: one persistent launch runs every product
+    # per 256 x 256 position (interior tiles, then ragged rows and K)
+    say("unfused group", M, N, K, dtype, scheme)
+    dist = "uniform" if dtype == "f16" else "normal_sqrtk"
+    A, B, A64, B64 = gen(M, N, K, dtype, dist, seed=37)
+    C_ref = oracle.gemm(A64, B64)
+    if scheme == "builtin":
+        C = planned(A, B, "l1", combine="unfused")
+        C_sh, _ = oracle.lcma(A64, B64, oracle.strassen(), 1, round_operands=dtype)
+    else:
+        C = planned_desc(A, B, winograd())
+        dw = oracle.Desc(2, 2, 2, D.WINOGRAD_U, D.WINOGRAD_V, D.WINOGRAD_W)
+        C_sh, _ = oracle.lcma(A64, B64, dw, 1, round_operands=dtype)
+    check_float(C, A64, B64, dtype, C_ref, blocks=2)
+    assert metrics.e_rel(si.f64(C), C_sh) <= 2 * metrics.UNIT_ROUNDOFF[dtype]
+
+
 @pytest.mark.parametrize("M,N,K,dtype", [(1024, 1024, 1024, "bf16"), (512, 768, 640, "f16"), (400, 272, 144, "f16")])
 def test_unfused_winograd_variant_matches_oracle(M, N, K, dtype):
     say("unfused winograd", M, N, K, dtype)
