@@ -19,7 +19,7 @@
 //                    (7 inner products on M/4 x N/4 blocks, fused the same
 //                    way) and folds the 4 inner outputs into fp32 output
 //                    blocks in memory, rounding into C at the last touch.
-//  * k_gen_prepass, k_gen_group_m16, k_gen_product(_m16) -- the unfused
+//  * k_gen_prepass, k_gen_group_m16, k_gen_product -- the unfused
 //                    path for any valid description: a runtime-coefficient
 //                    combination pass, then the products, each folding W * H
 //                    into fp32 output blocks and rounding into C at the last
@@ -1536,45 +1536,6 @@ k_gen_product(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B,
     });
 }
 
-// On the 8-wave 16x16x32 engine with 256 x 256 tiles (the classic kernel's),
-// for products with at least one full round of tiles.
-template <class C, bool BF, bool CBF>
-__global__ void __launch_bounds__(C::NT, 1)
-k_gen_product_m16(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb, int M, int N,
-                  int K, int gy, int gx, int P, const GenTargets tg)
-{
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_ALLOC];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / C::WN, wn = wave % C::WN;
-    int p, q;
-    tile_coords((int32_t)blockIdx.x, gy, gx, P, 8, &p, &q);
-    const int m0 = p * C::BM, n0 = q * C::BN;
-    const u16* Ab = A + (int64_t)m0 * lda;
-    const u16* Bb = B + n0;
-    const int nk = (K + C::BK - 1) / C::BK;
-    f32x4 acc[C::FM][C::FN];
-    zero_acc<C>(acc);
-    auto src = [&](int t) {
-        return tiles::TileSrc{Ab, (int)lda, M - m0, Bb, (int)ldb, N - n0, t * C::BK, K};
-    };
-    const m16::Addr<C> ad = m16::frag_addr<C>(wm, wn, lane);
-    auto none = [](int) {};
-    const bool inside = (m0 + C::BM <= M) & (n0 + C::BN <= N) & (K % C::BK == 0);
-    if (inside)
-        m16::run_tile<C, BF, false, true>(smem, nk, src, none, wave, lane, ad, acc);
-    else
-        m16::run_tile<C, BF, true, false>(smem, nk, src, none, wave, lane, ad, acc);
-    // lane l of MFMA tile (i, j) holds row 16 i + l % 16, columns 16 j + 4 (l / 16) .. + 3
-    gen_fold<CBF>(tg, m0, n0, M - m0, N - n0, [&](auto f) {
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j)
-                f(wm * C::WTM + i * 16 + (lane & 15), wn * C::WTN + j * 16 + 4 * (lane >> 4), acc[i][j]);
-    });
-}
-
 // All products of the unfused path in one persistent launch: each workgroup
 // owns 256 x 256 output positions (round-robin) and, for each, runs every
 // product's K loop in turn and folds it into that position's blocks, so the
@@ -1670,7 +1631,7 @@ hipError_t launch_gen_group_t(const GenGroupLaunch& L, hipStream_t st)
     return hipGetLastError();
 }
 
-template <class C, bool BF, bool CBF, bool M16>
+template <class C, bool BF, bool CBF>
 hipError_t launch_gen_product_t(const GenProductLaunch& L, hipStream_t st)
 {
     const int gy = (L.M + C::BM - 1) / C::BM, gx = (L.N + C::BN - 1) / C::BN;
@@ -1687,12 +1648,8 @@ hipError_t launch_gen_product_t(const GenProductLaunch& L, hipStream_t st)
     tg.ntgt = L.ntgt;
     tg.ldt = L.ldt;
     tg.ldc = L.ldc;
-    if constexpr (M16)
-        hipLaunchKernelGGL((k_gen_product_m16<C, BF, CBF>), dim3((unsigned)tiles), dim3(C::NT), 0, st,
-                           (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, L.M, L.N, L.K, gy, gx, L.P, tg);
-    else
-        hipLaunchKernelGGL((k_gen_product<C, BF, CBF>), dim3((unsigned)tiles), dim3(C::NT), 0, st,
-                           (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, L.M, L.N, L.K, gy, gx, L.P, tg);
+    hipLaunchKernelGGL((k_gen_product<C, BF, CBF>), dim3((unsigned)tiles), dim3(C::NT), 0, st,
+                       (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, L.M, L.N, L.K, gy, gx, L.P, tg);
     return hipGetLastError();
 }
 
@@ -2413,19 +2370,12 @@ hipError_t launch_gen_group(const GenGroupLaunch& L, hipStream_t st)
 
 hipError_t launch_gen_product(const GenProductLaunch& L, hipStream_t st)
 {
-    // 256 x 256 tiles on the 16x16x32 engine once they fill a round of the
-    // compute units; 128 x 128 tiles on the four-wave engine below that.
-    const int64_t t256 = (int64_t)((L.M + 255) / 256) * ((L.N + 255) / 256);
-    if (t256 >= L.P) {
-        if (L.out_bf16)
-            return L.op_bf16 ? launch_gen_product_t<MC256, true, true, true>(L, st)
-                             : launch_gen_product_t<MC256, false, true, true>(L, st);
-        return launch_gen_product_t<MC256, false, false, true>(L, st);
-    }
+    // Products whose 256 x 256 tiles fill the compute units go through the
+    // persistent group kernel instead; these use 128 x 128 tiles.
     if (L.out_bf16)
-        return L.op_bf16 ? launch_gen_product_t<QC128, true, true, false>(L, st)
-                         : launch_gen_product_t<QC128, false, true, false>(L, st);
-    return launch_gen_product_t<QC128, false, false, false>(L, st);
+        return L.op_bf16 ? launch_gen_product_t<QC128, true, true>(L, st)
+                         : launch_gen_product_t<QC128, false, true>(L, st);
+    return launch_gen_product_t<QC128, false, false>(L, st);
 }
 
 }  // namespace lcma
