@@ -68,6 +68,11 @@ def parse():
     ap.add_argument("--server", action="store_true",
                     help="also time every algorithm in server mode: single calls separated by seeded random "
                          "host-side gaps of 0.2-2 ms (mean and median of the per-call event times)")
+    ap.add_argument("--study", action="store_true",
+                    help="only the schedule ablation of the one-level fused kernel (one JSON line): tail split "
+                         "none/auto and locality/plain order on a tail shape, an all-split shape and 4096^3")
+    ap.add_argument("--study-case", default="",
+                    help="with --study: run only the case named 'MxNxK:split:order' (for counter runs)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="first run 3 device copies of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -96,6 +101,22 @@ def main():
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / reps
         print(json.dumps({"decode": decode_bandwidth(L, si, torch, tc)}), flush=True)
+        return
+
+    if args.study:
+        def tc(fn, reps, warm):
+            for _ in range(warm):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+        print(json.dumps({"schedule_study": schedule_study(L, si, torch, tc, args.study_case,
+                                                           max(args.steps, 10), args.warmup)}), flush=True)
         return
 
     wl = dict(si.SQUARE_4096_BF16)
@@ -380,6 +401,75 @@ def sweep_picks(L, si, torch, time_calls):
         del Ad, Bd, Cd
     torch.cuda.empty_cache()
     return {"agreement": round(agree / len(rows), 3), "shapes": rows}
+
+
+STUDY_SHAPES = ((4096, 5120, 4096), (2560, 2560, 2560), (4096, 4096, 4096))
+
+
+def schedule_mix(L, plan):
+    """From the planned schedule: split groups, the makespan in products, and the
+    fraction of XCDs (worker w runs on XCD w % 8) whose workers run both halves
+    of split groups at once (product-type mixing in one L2)."""
+    items, _ = L.lcma_plan_schedule(plan)
+    load, halves = {}, {}
+    split = set()
+    for (w, g, p0, p1, slot) in items:
+        load[w] = load.get(w, 0) + (p1 - p0)
+        if slot >= 0:
+            split.add(g)
+            halves.setdefault(w % 8, set()).add(p0 == 0)
+    mixed = sum(1 for h in halves.values() if len(h) == 2)
+    return {"split_groups": len(split), "makespan_products": max(load.values()),
+            "xcds_mixing_halves": round(mixed / 8, 3)}
+
+
+def schedule_study(L, si, torch, time_calls, case, reps, warm):
+    """Schedule ablation of the one-level fused kernel on bfloat16 N(0,1)/sqrt(K)
+    inputs: tail split (none / auto) x order (locality / plain), timed kernel by
+    kernel (the pre-pass is identical across variants and excluded), with the
+    classic product of the same shape beside it.  4096 x 5120 x 4096 has 320
+    groups of 128 x 128 (one full round plus a tail of 64 on 256 compute units);
+    2560^3 has 100 groups, all split; 4096^3 has 256, no tail."""
+    res = []
+    for (M, N, K) in STUDY_SHAPES:
+        shape = f"{M}x{N}x{K}"
+        variants = [(sp, od) for sp in ("none", "auto") for od in ("auto", "plain")]
+        variants = [v for v in variants if not case or case == f"{shape}:{v[0]}:{v[1]}"]
+        if not variants:
+            continue
+        A, B = si.gen(M, N, K, "bf16", "normal_sqrtk", 0)
+        Ad, Bd = A.to("cuda"), B.to("cuda")
+        Cd = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        row = {"shape": [M, N, K]}
+        calls = {}
+        if not case:
+            pc = L.lcma_plan_ex(M, N, K, "bf16", force="classic")
+            calls["classic"] = (None, lambda pc=pc: L.lcma_gemm(pc, Ad, Bd, Cd, None))
+        for sp, od in variants:
+            p = L.lcma_plan_ex(M, N, K, "bf16", force="l1", split=sp, order=od)
+            ws = L.workspace_for(p)
+            L.lcma_prepass(p, Ad, Bd, ws)
+            calls[f"split={sp},order={od}"] = (p, lambda p=p, ws=ws: L.lcma_fused(p, Ad, Bd, Cd, ws))
+        # rounds in rotated order, median per variant: clock drift over the
+        # run then favours no variant
+        names = list(calls)
+        times = {n: [] for n in names}
+        for rnd in range(5):
+            for i in range(len(names)):
+                n = names[(i + rnd) % len(names)]
+                times[n].append(time_calls(calls[n][1], reps, warm))
+        flops = 2.0 * 7 * (M // 2) * (N // 2) * (K // 2)
+        for n in names:
+            t = sorted(times[n])[len(times[n]) // 2]
+            if n == "classic":
+                row["classic_ms"] = round(t, 4)
+            else:
+                row[n] = dict(schedule_mix(L, calls[n][0]), fused_ms=round(t, 4),
+                              fused_tflops_actual=round(flops / (t * 1e-3) / 1e12, 1))
+        res.append(row)
+        del Ad, Bd, Cd
+        torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(A, B, target_s):

@@ -37,6 +37,8 @@ OK, E_INVALID, E_UNSUPPORTED, E_BAD_DESCRIPTOR, E_WORKSPACE, E_HIP, E_NOMEM = ra
 ALGO_NAMES = {ALGO_CLASSIC: "classic", ALGO_L1: "l1", ALGO_L2: "l2"}
 _ALGO = {"auto": ALGO_AUTO, "classic": ALGO_CLASSIC, "l1": ALGO_L1, "l2": ALGO_L2}
 _SPLIT = {"auto": SPLIT_AUTO, "none": SPLIT_NONE, "all": SPLIT_ALL}
+ORDER_AUTO, ORDER_PLAIN = 0, 1
+_ORDER = {"auto": ORDER_AUTO, "plain": ORDER_PLAIN}
 _COMBINE = {"auto": COMBINE_AUTO, "prepass": COMBINE_PREPASS, "at_load": COMBINE_AT_LOAD, "unfused": COMBINE_UNFUSED,
             "l2_on_chip": COMBINE_L2_ON_CHIP}
 
@@ -52,7 +54,7 @@ class lcma_desc(ctypes.Structure):
 class lcma_options(ctypes.Structure):
     _fields_ = [("split", _i32), ("combine", _i32), ("bf16_ops_f16", _i32), ("num_cus", _i32),
                 ("peak_tflops", ctypes.c_double), ("hbm_gbps", ctypes.c_double),
-                ("classic_eff", ctypes.c_double), ("fused_eff", ctypes.c_double)]
+                ("classic_eff", ctypes.c_double), ("fused_eff", ctypes.c_double), ("order", _i32)]
 
 
 def _sig(name, res, args):
@@ -196,10 +198,11 @@ class Plan:
 
 def lcma_plan_ex(M, N, K, dtype, desc: Desc | None = None, force="auto", split="auto", combine="auto",
                  bf16_ops_f16=0, num_cus=0, peak_tflops=0.0, hbm_gbps=0.0, classic_eff=0.0,
-                 fused_eff=0.0) -> Plan:
+                 fused_eff=0.0, order="auto") -> Plan:
     opts = lcma_options(_SPLIT[split] if isinstance(split, str) else split,
                         _COMBINE[combine] if isinstance(combine, str) else combine,
-                        bf16_ops_f16, num_cus, peak_tflops, hbm_gbps, classic_eff, fused_eff)
+                        bf16_ops_f16, num_cus, peak_tflops, hbm_gbps, classic_eff, fused_eff,
+                        _ORDER[order] if isinstance(order, str) else order)
     h = _vp()
     st = _lib_plan_ex(M, N, K, _dt(dtype), ctypes.byref(desc.c) if desc is not None else None,
                       _ALGO[force] if isinstance(force, str) else force, ctypes.byref(opts), ctypes.byref(h))

@@ -401,7 +401,8 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     lcma_options o{};
     if (opts)
         o = *opts;
-    if (o.split < LCMA_SPLIT_AUTO || o.split > LCMA_SPLIT_ALL || o.combine < LCMA_COMBINE_AUTO ||
+    if (o.split < LCMA_SPLIT_AUTO || o.split > LCMA_SPLIT_ALL || o.order < LCMA_ORDER_AUTO ||
+        o.order > LCMA_ORDER_PLAIN || o.combine < LCMA_COMBINE_AUTO ||
         o.combine > LCMA_COMBINE_L2_ON_CHIP || o.num_cus < 0 || o.peak_tflops < 0 || o.hbm_gbps < 0 ||
         o.bf16_ops_f16 < -1 || o.bf16_ops_f16 > 1 || !(o.classic_eff >= 0 && o.classic_eff <= 1) ||
         !(o.fused_eff >= 0 && o.fused_eff <= 1))
@@ -579,7 +580,7 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         sp.G = sg.G; sp.gy = sg.gy; sp.gx = sg.gx; sp.R = sg.R; sp.P = m.P;
         sp.mode = split_mode_for(o.split, sg.G, m.P);
         sp.h = (sg.R + 1) / 2;
-        sp.raster = 8;
+        sp.raster = o.order == LCMA_ORDER_PLAIN ? 0 : 8;
         if (sp.mode == kSplitTail) {
             p->n_slots = sg.G % m.P;
             p->grid = sg.G / m.P > 0 ? m.P : 2 * (sg.G % m.P);

@@ -2006,8 +2006,9 @@ __device__ __forceinline__ void outer_update(const FusedParams& fp, int m0, int 
 }
 
 // Writes a group's output blocks.  A split piece first publishes its fp32
-// partial; the second piece to arrive (agent-scope acquire/release through a
-// per-slot counter) adds the other partial, writes C and resets the counter.
+// partial; the second piece to arrive (one agent-scope acquire/release atomic
+// per workgroup on a per-slot counter) adds the other partial, writes C and
+// resets the counter.
 // fp32 addition commutes, so the result does not depend on arrival order.
 // OUTER: the outputs go through outer_update instead of straight into C.
 template <int NOUT, class C, bool CBF, bool OUTER = false>
@@ -2036,14 +2037,21 @@ __device__ __forceinline__ void fused_epilogue(const FusedParams& fp, const Item
                             f32x4{Cacc[o][i][j][4 * g], Cacc[o][i][j][4 * g + 1],
                                   Cacc[o][i][j][4 * g + 2], Cacc[o][i][j][4 * g + 3]};
                     }
-        __threadfence();
+        // Each wave waits until its own partial stores have reached the L2 of
+        // its XCD.  Thread 0's agent-scope acquire-release atomic then writes
+        // that L2 back to memory once for the whole workgroup (and, on the
+        // second arrival, invalidates it before the other piece's partial is
+        // read).  A per-thread agent-scope fence here made every wave write
+        // back and invalidate the whole L2 of its XCD, which cost more than
+        // the split saved.
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tid == 0)
             *sh_old = __hip_atomic_fetch_add(fp.counters + item.slot, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         store = *sh_old == 1;
         if (store) {
-            __threadfence();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 #pragma unroll
             for (int o = 0; o < NOUT; ++o) {
                 // One output block at a time keeps the partial loads from all

@@ -36,7 +36,8 @@ struct SchedParams {
     int32_t P;      // workers (one per compute unit)
     int32_t mode;   // SplitMode actually used
     int32_t h;      // products in the first piece of a split group
-    int32_t raster; // rows of tiles per raster band
+    int32_t raster; // rows of tiles per raster band; 0 = plain order (row-major tiles,
+                    // split pieces not paired by XCD), the baseline the ordering is measured against
 };
 
 struct Item {
@@ -69,7 +70,8 @@ LCMA_HD inline Item sched_item(const SchedParams& s, int32_t w, int32_t i)
         if (i < FR) {
             it.g = i * s.P + w; it.pos0 = 0; it.pos1 = s.R; it.slot = -1;
         } else {
-            const int32_t which = w & 1, t = w >> 1;
+            const int32_t T = s.G % s.P;
+            const int32_t which = s.raster ? (w & 1) : (w >= T), t = s.raster ? (w >> 1) : w - (w >= T) * T;
             it.g = FR * s.P + t;
             it.pos0 = which ? s.h : 0;
             it.pos1 = which ? s.R : s.h;
@@ -79,7 +81,7 @@ LCMA_HD inline Item sched_item(const SchedParams& s, int32_t w, int32_t i)
     }
     if (s.mode == kSplitAll) {
         const int32_t piece = w + i * s.P;
-        const int32_t which = piece & 1, t = piece >> 1;
+        const int32_t which = s.raster ? (piece & 1) : (piece >= s.G), t = s.raster ? (piece >> 1) : piece % s.G;
         it.g = t; it.pos0 = which ? s.h : 0; it.pos1 = which ? s.R : s.h; it.slot = t;
         return it;
     }
@@ -91,10 +93,16 @@ LCMA_HD inline Item sched_item(const SchedParams& s, int32_t w, int32_t i)
 // by P workers.  Within each complete round of P indices the workers of one
 // XCD (w % 8) receive consecutive virtual indices; virtual indices then walk
 // a raster of bands `raster` tiles tall, column by column inside a band.
+// raster = 0 gives the plain row-major order instead.
 LCMA_HD inline void tile_coords(int32_t g, int32_t gy, int32_t gx, int32_t P, int32_t raster,
                                 int32_t* p, int32_t* q)
 {
     const int32_t G = gy * gx;
+    if (raster == 0) {
+        *p = g / gx;
+        *q = g % gx;
+        return;
+    }
     int32_t v = g;
     if (P % 8 == 0 && P >= 8) {
         const int32_t k = g / P, w = g % P;

@@ -75,6 +75,18 @@ typedef enum {
     LCMA_SPLIT_ALL = 2    /* split every group (testing the fix-up path) */
 } lcma_split;
 
+/* Order in which the persistent LCMA kernel deals output groups and split
+ * pieces to compute units ([FG] "从 LCMA 到 FalconGEMM": tiles of one product
+ * type run together, which keeps the cache hit rate and the clock up). */
+typedef enum {
+    LCMA_ORDER_AUTO = 0,  /* locality order: the compute units of one XCD (own L2) take a compact
+                             block of output groups; the two pieces of a split group go to adjacent
+                             workers, so even XCDs run first halves and odd XCDs second halves */
+    LCMA_ORDER_PLAIN = 1  /* row-major groups; first halves of split groups on workers 0..T-1,
+                             second halves on T..2T-1 (every XCD mixes both halves): the baseline
+                             the locality order is measured against */
+} lcma_order;
+
 /* How the combined operands reach the fused kernel, and (two levels) where
  * the products of one output coordinate accumulate. */
 typedef enum {
@@ -131,6 +143,7 @@ typedef struct {
     double fused_eff;       /* the same for the fused group kernel (both levels);
                                0 = 0.31 for one level and for two levels with the outer level in
                                memory, 0.037 for LCMA_COMBINE_L2_ON_CHIP (measured) */
+    lcma_order order;       /* persistent fused kernel's work order (LCMA_ORDER_AUTO by default) */
 } lcma_options;
 
 typedef struct lcma_plan_s* lcma_plan_t;

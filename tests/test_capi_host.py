@@ -337,6 +337,43 @@ def test_split_pieces_of_a_group_sit_on_adjacent_workers():
         assert a == 0 and w1 == w0 + 1 and w0 % 2 == 0   # first half on even, second on odd worker
 
 
+def _xcd_halves(items):
+    halves = {}
+    for (w, g, p0, p1, slot) in items:
+        if slot >= 0:
+            halves.setdefault(w % 8, set()).add(p0 == 0)
+    return halves
+
+
+@pytest.mark.parametrize("M,N", [(2560, 2560), (4096, 5120)])
+def test_plain_order_is_a_valid_schedule_that_mixes_halves(M, N):
+    # 2560^2: 100 groups, all split; 4096 x 5120: 320 groups, a split tail of 64
+    pa = L.lcma_plan_ex(M, N, 1024, "bf16", force="l1", num_cus=256)
+    pp = L.lcma_plan_ex(M, N, 1024, "bf16", force="l1", num_cus=256, order="plain")
+    ia, Ga, na = _check_schedule(pa, 7, None)
+    ip, Gp, nq = _check_schedule(pp, 7, None)
+    assert (Ga, na) == (Gp, nq) and na > 0
+    T = na
+    # same pieces, only placed differently
+    assert sorted(x[1:4] for x in ia) == sorted(x[1:4] for x in ip)
+    # locality order: every XCD runs one kind of half; plain: every XCD runs both
+    assert all(len(h) == 1 for h in _xcd_halves(ia).values())
+    assert len(_xcd_halves(ip)) == 8 and all(len(h) == 2 for h in _xcd_halves(ip).values())
+    # plain placement: first halves of tail group t on worker t, second on T + t
+    for (w, g, p0, p1, slot) in ip:
+        if slot >= 0:
+            assert w == (slot if p0 == 0 else T + slot)
+    # plain order of whole groups: row-major, worker w takes groups w, w + P, ...
+    for (w, g, p0, p1, slot) in ip:
+        if slot < 0:
+            assert g % 256 == w
+
+
+def test_invalid_order_is_rejected():
+    with pytest.raises(L.LcmaError):
+        L.lcma_plan_ex(1024, 1024, 1024, "f16", force="l1", num_cus=256, order=2)
+
+
 # ---------------------------------------------------------------- call validation (no device work)
 
 def test_invalid_calls_fail_before_touching_the_device():

@@ -276,6 +276,30 @@ def test_l1_tail_split_shapes(n):
     assert metrics.freivalds(C, A64, B64) <= 4 * metrics.UNIT_ROUNDOFF["bf16"]
 
 
+@pytest.mark.parametrize("M,N,split", [(2560, 2560, "auto"), (4096, 5120, "none"), (4096, 5120, "all"),
+                                       (4096, 5120, "auto")])
+def test_l1_plain_order_equals_locality_order(M, N, split):
+    # The order moves groups and split pieces between compute units.  When the
+    # same groups are split under both orders (none, all; 2560^2 splits all
+    # 100 groups) each group's arithmetic (product order, split point,
+    # commutative fix-up add) is the same, so the results are bitwise equal.
+    # With a partial tail (4096 x 5120: 64 of 320 groups) the two orders put
+    # different output tiles in the tail, whose split sums associate
+    # differently: then both must meet the oracle's gates.
+    say("l1 order", M, N, split)
+    A, B, A64, B64 = gen(M, N, 256, "bf16", "normal_sqrtk", seed=M + N)
+    C0 = planned(A, B, "l1", split=split)
+    C1 = planned(A, B, "l1", split=split, order="plain")
+    tail = split == "auto" and (M // 256) * (N // 256) % 256 != 0
+    if not tail:
+        assert np.array_equal(si.bits(C0), si.bits(C1))
+    rows = np.random.default_rng(2).choice(M, 16, replace=False)
+    ref = np.stack([oracle.gemm_rows(A64, B64, r, r + 1)[0] for r in rows])
+    for C in (C0, C1):
+        assert metrics.e_rel(si.f64(C)[rows], ref) <= 4 * metrics.UNIT_ROUNDOFF["bf16"]
+    assert metrics.freivalds(si.f64(C1), A64, B64) <= 4 * metrics.UNIT_ROUNDOFF["bf16"]
+
+
 # ---------------------------------------------------------------- unfused path (any valid description)
 
 def winograd():
