@@ -1456,41 +1456,76 @@ struct GenTargets {
     int64_t ldt, ldc;
 };
 
-// `each(f)` calls f(m, n, h) for every 4-column group h of the wave's
-// accumulators (m, n relative to the tile origin m0, n0).  N is a multiple of
-// 8 on this path, so a group is wholly inside the columns or wholly out.
 // One target of a fold: rt is the target's fp32 block and rc its C block,
-// both at the tile origin (ld, ldc elements per row).
-template <bool CBF, class Each>
+// both at the tile origin (ld, ldc elements per row).  get(e, m, n, h) gives
+// the e-th (0 <= e < NE) 4-column group h of the wave's accumulators at
+// (m, n) relative to the tile origin; N is a multiple of 8 on this path, so a
+// group is wholly inside the columns or wholly out.  The mode is uniform, so
+// it is tested once; the read-modify-write modes issue CH loads before the
+// first use, so a fold waits for NE / CH round trips instead of NE.
+template <bool CBF, int NE, int CH, class Get>
 __device__ __forceinline__ void fold_target(rsrc_t rt, rsrc_t rc, int ld, int ldc, int mode, float wt, int rows,
-                                            int cols, Each each)
+                                            int cols, Get get)
 {
-    each([&](int m, int n, const f32x4& h) {
-        const bool ok = m < rows && n < cols;
-        const u32 off = ok ? (u32)(m * ld + n) * 4u : kOob;
-        f32x4 v = h * wt;
-        if (mode == kOuterAdd || mode == kOuterFinish)
-            v += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0));
-        if (mode == kOuterStore || mode == kOuterAdd) {
-            __builtin_amdgcn_raw_buffer_store_b128(
-                __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), rt, off, 0, 0);
-        } else {
-            const u32 oc = ok ? (u32)(m * ldc + n) * 2u : kOob;
-            __builtin_amdgcn_raw_buffer_store_b64(
-                __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
-                                   u32x2{pack2<CBF>(v.x, v.y), pack2<CBF>(v.z, v.w)}),
-                rc, oc, 0, 0);
+    static_assert(NE % CH == 0, "fold chunks");
+    if (mode == kOuterNone)
+        return;
+    auto off_t = [&](int m, int n) { return (m < rows && n < cols) ? (u32)(m * ld + n) * 4u : kOob; };
+    auto put_c = [&](int m, int n, const f32x4& v) {
+        const u32 oc = (m < rows && n < cols) ? (u32)(m * ldc + n) * 2u : kOob;
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
+                               u32x2{pack2<CBF>(v.x, v.y), pack2<CBF>(v.z, v.w)}),
+            rc, oc, 0, 0);
+    };
+    auto put_t = [&](int m, int n, const f32x4& v) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v),
+                                               rt, off_t(m, n), 0, 0);
+    };
+    if (mode == kOuterStore || mode == kOuterOnly) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            int m, n;
+            f32x4 h;
+            get(e, m, n, h);
+            if (mode == kOuterStore)
+                put_t(m, n, h * wt);
+            else
+                put_c(m, n, h * wt);
         }
-    });
+        return;
+    }
+#pragma unroll
+    for (int e0 = 0; e0 < NE; e0 += CH) {
+        f32x4 old[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            int m, n;
+            f32x4 h;
+            get(e0 + c, m, n, h);
+            old[c] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, off_t(m, n), 0, 0));
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            int m, n;
+            f32x4 h;
+            get(e0 + c, m, n, h);
+            const f32x4 v = h * wt + old[c];
+            if (mode == kOuterAdd)
+                put_t(m, n, v);
+            else
+                put_c(m, n, v);
+        }
+    }
 }
 
-template <bool CBF, class Each>
-__device__ __forceinline__ void gen_fold(const GenTargets& tg, int m0, int n0, int rows, int cols, Each each)
+template <bool CBF, int NE, int CH, class Get>
+__device__ __forceinline__ void gen_fold(const GenTargets& tg, int m0, int n0, int rows, int cols, Get get)
 {
     for (int t = 0; t < tg.ntgt; ++t)
-        fold_target<CBF>(make_rsrc(tg.tgt[t] + (int64_t)m0 * tg.ldt + n0),
-                         make_rsrc(tg.cdst[t] + (int64_t)m0 * tg.ldc + n0), (int)tg.ldt, (int)tg.ldc, tg.mode[t],
-                         tg.w[t], rows, cols, each);
+        fold_target<CBF, NE, CH>(make_rsrc(tg.tgt[t] + (int64_t)m0 * tg.ldt + n0),
+                                 make_rsrc(tg.cdst[t] + (int64_t)m0 * tg.ldc + n0), (int)tg.ldt, (int)tg.ldc,
+                                 tg.mode[t], tg.w[t], rows, cols, get);
 }
 
 // On the four-wave 32x32 engine (128 x 128 tiles; shapes with few tiles).
@@ -1524,15 +1559,12 @@ k_gen_product(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B,
     // lane l of MFMA tile (i, j) holds row (l % 32) and, per group g of 4
     // accumulators, columns 8 g + 4 (l / 32) .. + 3
     const int r = lane & 31, hi = lane >> 5;
-    gen_fold<CBF>(tg, m0, n0, M - m0, N - n0, [&](auto f) {
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    f(wm * C::WTM + i * 32 + r, wn * C::WTN + j * 32 + 8 * g + 4 * hi,
-                      f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]});
+    constexpr int NE = C::FM * C::FN * 4;
+    gen_fold<CBF, NE, 16>(tg, m0, n0, M - m0, N - n0, [&](int e, int& m, int& n, f32x4& h) {
+        const int i = e / (C::FN * 4), j = (e / 4) % C::FN, g = e % 4;
+        m = wm * C::WTM + i * 32 + r;
+        n = wn * C::WTN + j * 32 + 8 * g + 4 * hi;
+        h = f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
     });
 }
 
@@ -1589,17 +1621,15 @@ __global__ void __launch_bounds__(C::NT, 1) k_gen_group_m16(const GenGroupParams
                 if (mode == kOuterNone)
                     continue;
                 const int bi = o / gp.ncols, bj = o % gp.ncols;
-                fold_target<CBF>(make_rsrc(gp.acc + (int64_t)o * gp.M * gp.N + (int64_t)m0 * gp.N + n0),
-                                 make_rsrc(gp.C + (int64_t)(bi * gp.M + m0) * gp.ldc + bj * gp.N + n0), gp.N,
-                                 (int)gp.ldc, mode, (float)gp.w[r * kGenMaxBlocks + o], rows, cols,
-                                 [&](auto f) {
-#pragma unroll
-                                     for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-                                         for (int j = 0; j < C::FN; ++j)
-                                             f(wm * C::WTM + i * 16 + (lane & 15),
-                                               wn * C::WTN + j * 16 + 4 * (lane >> 4), acc[i][j]);
-                                 });
+                fold_target<CBF, C::FM * C::FN, 8>(
+                    make_rsrc(gp.acc + (int64_t)o * gp.M * gp.N + (int64_t)m0 * gp.N + n0),
+                    make_rsrc(gp.C + (int64_t)(bi * gp.M + m0) * gp.ldc + bj * gp.N + n0), gp.N, (int)gp.ldc, mode,
+                    (float)gp.w[r * kGenMaxBlocks + o], rows, cols, [&](int e, int& m, int& n, f32x4& h) {
+                        const int i = e / C::FN, j = e % C::FN;
+                        m = wm * C::WTM + i * 16 + (lane & 15);
+                        n = wn * C::WTN + j * 16 + 4 * (lane >> 4);
+                        h = acc[i][j];
+                    });
             }
         }
     }
@@ -1982,22 +2012,41 @@ __device__ __forceinline__ void outer_update(const FusedParams& fp, int m0, int 
         for (int o2 = 0; o2 < 4; ++o2) {
             const int bi = 2 * i1 + (o2 >> 1), bj = 2 * j1 + (o2 & 1);
             const rsrc_t ra = make_rsrc(fp.acc + (int64_t)(bi * 4 + bj) * fp.Mb * fp.Nb + (int64_t)m0 * ld + n0);
+            // The mode is uniform: the read-modify-write modes issue all of
+            // the block's loads before the first use (one round trip).
+            auto off_of = [&](int i, int j) {
+                const int m = wm * C::WTM + i * 16 + (lane & 15);
+                const int n = wn * C::WTN + j * 16 + 4 * (lane >> 4);
+                return (m < rows && n < cols) ? (u32)(m * ld + n) * 4u : kOob;
+            };
             f32x4 t[C::FM][C::FN];
+            if (mode == kOuterAdd || mode == kOuterFinish) {
 #pragma unroll
-            for (int i = 0; i < C::FM; ++i)
+                for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-                for (int j = 0; j < C::FN; ++j) {
-                    const int m = wm * C::WTM + i * 16 + (lane & 15);
-                    const int n = wn * C::WTN + j * 16 + 4 * (lane >> 4);
-                    const u32 off = (m < rows && n < cols) ? (u32)(m * ld + n) * 4u : kOob;
-                    f32x4 v = Cacc[o2][i][j] * w;
-                    if (mode == kOuterAdd || mode == kOuterFinish)
-                        v += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
-                    if (mode == kOuterStore || mode == kOuterAdd)
+                    for (int j = 0; j < C::FN; ++j)
+                        t[i][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off_of(i, j), 0, 0));
+#pragma unroll
+                for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::FN; ++j)
+                        t[i][j] = Cacc[o2][i][j] * w + t[i][j];
+            } else {
+#pragma unroll
+                for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::FN; ++j)
+                        t[i][j] = Cacc[o2][i][j] * w;
+            }
+            if (mode == kOuterStore || mode == kOuterAdd) {
+#pragma unroll
+                for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::FN; ++j)
                         __builtin_amdgcn_raw_buffer_store_b128(
-                            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), ra, off, 0, 0);
-                    t[i][j] = v;
-                }
+                            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, t[i][j]), ra,
+                            off_of(i, j), 0, 0);
+            }
             if (mode == kOuterFinish || mode == kOuterOnly)
                 store_c<C, CBF, true>(t, fp.C + (int64_t)(bi * fp.Mb + m0) * fp.ldc + bj * fp.Nb + n0, fp.ldc, rows,
                                       cols, wm, wn, lane);
