@@ -202,12 +202,16 @@ def main():
     detail = {}
     only = set(a for a in args.only.split(",") if a)
     plans = {}
-    for algo in ("classic", "l1", "l2", "l1_unfused"):
+    for algo in ("classic", "l1", "l2", "l2_bf16_operands", "l1_unfused"):
         if only and algo not in only:
             continue
         try:
             if algo == "l1_unfused":
                 p = L.lcma_plan_ex(M, N, K, dtype, force="l1", combine="unfused")
+            elif algo == "l2_bf16_operands":
+                # two levels with the combined operands rounded to bfloat16
+                # (the default rounds them to binary16 for bfloat16 inputs)
+                p = L.lcma_plan_ex(M, N, K, dtype, force="l2", bf16_ops_f16=-1)
             else:
                 p = L.lcma_plan_ex(M, N, K, dtype, force=algo)
         except L.LcmaError:
@@ -222,8 +226,8 @@ def main():
             t_pre = time_calls(lambda: L.lcma_prepass(p, Ad, Bd, ws), reps, args.warmup)
             L.lcma_prepass(p, Ad, Bd, ws)
             t_fu = time_calls(lambda: L.lcma_fused(p, Ad, Bd, C, ws), reps, args.warmup)
-            R = 49 if algo == "l2" else 7
-            S = 4 if algo == "l2" else 2
+            R = 49 if algo.startswith("l2") else 7
+            S = 4 if algo.startswith("l2") else 2
             mfma_flops = 2.0 * R * (M // S) * (N // S) * (K // S)
             # bytes the pre-pass must move: read A and B once, write the combined operands
             written = sum(1 for r in range(R) if L.lcma_plan_operand(p, 0, r)[0] >= 0) * (M // S) * (K // S) \
@@ -327,11 +331,31 @@ def main():
         del Ad, Bd, C, plans
         torch.cuda.empty_cache()
         out["machine"] = hbm_copy_rate(torch, time_calls)
+        out["square_512_f16"] = small_square(L, si, torch, time_calls)
         out["decode"] = decode_bandwidth(L, si, torch, time_calls)
         out["sweep"] = sweep_picks(L, si, torch, time_calls)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(A, B, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def small_square(L, si, torch, time_calls):
+    """512^3 binary16 product, A, B ~ U(-1, 1): classic against one level (7
+    products of 256^3 blocks).  Launch- and latency-bound: the operands sit in
+    the caches and the MFMA work is a fraction of a microsecond."""
+    A, B = si.gen(512, 512, 512, "f16", "uniform", 0)
+    Ad, Bd = A.to("cuda"), B.to("cuda")
+    Cd = torch.empty((512, 512), dtype=torch.float16, device="cuda")
+    res = {}
+    for algo in ("classic", "l1"):
+        p = L.lcma_plan_ex(512, 512, 512, "f16", force=algo)
+        ws = L.workspace_for(p)
+        t = time_calls(lambda: L.lcma_gemm(p, Ad, Bd, Cd, ws), 200, 20)
+        res[algo] = {"us": round(t * 1e3, 2), "eff_tflops": round(2.0 * 512 ** 3 / (t * 1e-3) / 1e12, 1)}
+    res["pick"] = L.lcma_plan_info(L.lcma_plan(512, 512, 512, "f16"))[0]
+    del Ad, Bd, Cd
+    torch.cuda.empty_cache()
+    return res
 
 
 def hbm_copy_rate(torch, time_calls):
