@@ -508,6 +508,23 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     } else if (ok1) {
         est[LCMA_ALGO_L1] = est_lcma(M, N, K, 1, o.split, op_bf16_for(1) != (dt == LCMA_BF16), false, m);
     }
+    // One level of the built-in scheme, combine left to the planner: the
+    // unfused path when it is estimated faster.  Its products run on the
+    // classic kernel's tiles, which wins once the blocks are large (measured
+    // at 8192^3 and 16384^3); the fused group kernel wins below.  A split or
+    // order request asks for the fused kernel's schedule, so it keeps it.
+    bool l1_unfused_auto = false;
+    if (ok1 && !unfused && o.combine == LCMA_COMBINE_AUTO && o.split == LCMA_SPLIT_AUTO &&
+        o.order == LCMA_ORDER_AUTO && admissible_unfused()) {
+        const int64_t Mb = M / 2, Nb = N / 2, Kb = K / 2;
+        const double pre = 2.0 * ((double)M * K + (double)K * N) + 2.0 * 7 * ((double)Mb * Kb + (double)Kb * Nb);
+        const double comb = (8.0 * 12 - 6.0 * 4) * (double)Mb * Nb;
+        const double t_unf = (pre + comb) / (m.eta_bw * m.bw) + 7 * est_classic(Mb, Nb, Kb, m) + 2 * m.launch;
+        if (t_unf < 0.98 * est[LCMA_ALGO_L1]) {
+            est[LCMA_ALGO_L1] = t_unf;
+            l1_unfused_auto = true;
+        }
+    }
     if (ok2)
         est[LCMA_ALGO_L2] = est_lcma(M, N, K, 2, o.split, op_bf16_for(2) != (dt == LCMA_BF16), outer2, m);
 
@@ -542,7 +559,7 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     p->levels = chosen == LCMA_ALGO_L1 ? 1 : chosen == LCMA_ALGO_L2 ? 2 : 0;
     p->ws_bytes = 0;
     p->n_slots = 0;
-    p->unfused = p->levels == 1 && unfused;
+    p->unfused = p->levels == 1 && (unfused || l1_unfused_auto);
     if (p->unfused) {
         p->op_bf16 = op_bf16_for(1);
         p->gms = gen.ms; p->gks = gen.ks; p->gns = gen.ns; p->gR = gen.rank;

@@ -90,18 +90,23 @@ typedef enum {
 /* How the combined operands reach the fused kernel, and (two levels) where
  * the products of one output coordinate accumulate. */
 typedef enum {
-    LCMA_COMBINE_AUTO = 0,
+    LCMA_COMBINE_AUTO = 0,    /* one level of a built-in scheme: PREPASS, or UNFUSED when the cost model
+                                 estimates it at least 2% faster (large blocks) and split and order are left
+                                 at their defaults; two levels: PREPASS */
     LCMA_COMBINE_PREPASS = 1, /* a separate bandwidth-bound pass writes each combined operand to the workspace.
                                  Two levels: the 7 inner products of each outer product run fused as one
                                  level (their 4 outputs accumulate on chip), one launch per outer product,
                                  and each launch folds W1[r1][i1,j1] * (its inner outputs) into fp32 output
                                  blocks in the workspace; the last contributor to an output rounds it into C */
-    LCMA_COMBINE_AT_LOAD = 2, /* the fused kernel forms the combinations while staging tiles (one-level only) */
-    LCMA_COMBINE_UNFUSED = 3, /* one level only: every combined operand is written, each product runs as its own
-                                 GEMM whose epilogue adds W[r][i,j] * H_r into fp32 output blocks in the
-                                 workspace (H_r is never stored), and a final pass rounds them into C.  The path
-                                 for descriptions that are not a built-in scheme, and the unfused ablation of
-                                 the fused path for the built-in one */
+    LCMA_COMBINE_AT_LOAD = 2, /* the fused kernel would form the combinations while staging tiles (one level).
+                                 Not built: lcma_plan_ex returns LCMA_E_UNSUPPORTED */
+    LCMA_COMBINE_UNFUSED = 3, /* one level only: every combined operand is written; each product's epilogue adds
+                                 W[r][i,j] * H_r into fp32 output blocks in the workspace (H_r is never stored)
+                                 and the last contributor to a block rounds it into C.  Blocks with enough
+                                 256 x 256 positions for every compute unit run all products in one persistent
+                                 launch (each position owned by one workgroup); smaller ones run one launch
+                                 per product.  The path for descriptions that are not a built-in scheme, and
+                                 the unfused form of the built-in one */
     LCMA_COMBINE_L2_ON_CHIP = 4 /* two levels only (pre-pass as above): all 49 products of an output coordinate
                                  run in one group on one workgroup and the 16 outputs accumulate on chip.  The
                                  register file holds 17 accumulator tiles only at 64 x 64 group tiles, so this

@@ -369,6 +369,29 @@ def test_plain_order_is_a_valid_schedule_that_mixes_halves(M, N):
             assert g % 256 == w
 
 
+def test_one_level_combine_follows_the_cost_model():
+    # Left to the planner, one level of the built-in scheme runs the unfused
+    # path where its estimate is lower (large blocks) and the fused group
+    # kernel below; an explicit split or order keeps the fused kernel.
+    def fused(plan):
+        try:
+            L.lcma_plan_schedule(plan)
+            return True
+        except L.LcmaError:
+            return False
+    for n, want_fused in ((4096, True), (6144, True), (8192, False), (16384, False)):
+        p = L.lcma_plan_ex(n, n, n, "bf16", force="l1", num_cus=256)
+        assert fused(p) == want_fused, n
+        pf = L.lcma_plan_ex(n, n, n, "bf16", force="l1", combine="prepass", num_cus=256)
+        pu = L.lcma_plan_ex(n, n, n, "bf16", force="l1", combine="unfused", num_cus=256)
+        assert fused(pf) and not fused(pu)
+        assert L.lcma_plan_info(p)[2] == min(L.lcma_plan_info(pf)[2], L.lcma_plan_info(pu)[2]) or want_fused
+    p = L.lcma_plan_ex(16384, 16384, 16384, "bf16", force="l1", split="none", num_cus=256)
+    assert fused(p)
+    p = L.lcma_plan_ex(16384, 16384, 16384, "bf16", force="l1", order="plain", num_cus=256)
+    assert fused(p)
+
+
 def test_invalid_order_is_rejected():
     with pytest.raises(L.LcmaError):
         L.lcma_plan_ex(1024, 1024, 1024, "f16", force="l1", num_cus=256, order=2)

@@ -491,14 +491,17 @@ def test_square_16384_bf16_sampled():
     ref = np.stack([oracle.gemm_rows(A64, B64, r, r + 1)[0] for r in rows])
     u = metrics.UNIT_ROUNDOFF["bf16"]
     res = {}
-    for algo in ("classic", "l1", "l2"):
-        say("16384", algo)
-        C = si.f64(planned(A, B, algo))
-        res[algo] = metrics.e_rel(C[rows], ref)
-        assert res[algo] <= 4 * u, (algo, res[algo])
+    # one level: the planner's choice at this size (the unfused path) and the
+    # fused group kernel after a pre-pass
+    for name, algo, kw in (("classic", "classic", {}), ("l1", "l1", {}), ("l1_fused", "l1", {"combine": "prepass"}),
+                           ("l2", "l2", {})):
+        say("16384", name)
+        C = si.f64(planned(A, B, algo, **kw))
+        res[name] = metrics.e_rel(C[rows], ref)
+        assert res[name] <= 4 * u, (name, res[name])
         assert metrics.freivalds(C, A64, B64, seeds=(11,)) <= 4 * u
         del C
-    assert res["l1"] <= 4 * res["classic"] and res["l2"] <= 4 * res["classic"]
+    assert max(res["l1"], res["l1_fused"], res["l2"]) <= 4 * res["classic"]
 
 
 # ---------------------------------------------------------------- graph capture
