@@ -1405,6 +1405,12 @@ hipError_t launch_classic_m16_t(const ClassicLaunch& L, hipStream_t st)
 }
 
 using QC128 = q4::QCfg<128, 128>;   // 4 waves of 64 x 64
+// 8 waves (2 per SIMD) of 64 x 32, 16x16x32 MFMAs, 7 k-tiles in flight: for
+// long K on 128 x 128 tiles (measured 10-24% faster than the four-wave
+// kernel from K = 2048, 11-15% slower at K <= 1024, where its deeper
+// prologue and epilogue weigh more than the K loop).
+using MC128 = m16::Cfg<128, 128, 2, 4, 7>;
+constexpr int kLongK128 = 2048;
 
 template <class C, bool BF>
 __global__ void __launch_bounds__(C::NT, 1)
@@ -2343,6 +2349,8 @@ hipError_t launch_classic(const ClassicLaunch& L, hipStream_t st)
             return L.bf16 ? launch_classic_m16_t<MC256, true>(L, st) : launch_classic_m16_t<MC256, false>(L, st);
         return launch_classic_c<Cfg256>(L, st);
     case kTile128:
+        if (L.vec && L.K >= kLongK128)
+            return L.bf16 ? launch_classic_m16_t<MC128, true>(L, st) : launch_classic_m16_t<MC128, false>(L, st);
         if (L.vec)
             return L.bf16 ? launch_classic_q4_t<QC128, true>(L, st) : launch_classic_q4_t<QC128, false>(L, st);
         return launch_classic_c<Cfg128>(L, st);

@@ -12,9 +12,9 @@ constexpr int kMaxRank = 49;
 
 // Tile shapes of the classic kernel.
 enum ClassicTile : int32_t {
-    kTile256 = 0,  // 256 x 256 workgroup tile, 4 waves of 128 x 128
-    kTile128 = 1,  // 128 x 128, 4 waves of 64 x 64
-    kTile32 = 2    // 32 x 64, 2 waves of 32 x 32 (skinny products)
+    kTile256 = 0,  // 256 x 256 workgroup tile, 8 waves of 128 x 64
+    kTile128 = 1,  // 128 x 128: 4 waves of 64 x 64, or 8 waves of 64 x 32 for K >= 2048
+    kTile32 = 2    // M <= 64: the streaming kernel (32- or 64-row A, 64-column strips of B)
 };
 
 struct ClassicLaunch {

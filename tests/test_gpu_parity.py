@@ -79,8 +79,10 @@ CLASSIC_SHAPES = [
     (1, 8, 8), (7, 13, 5), (3, 1, 9), (33, 40, 24), (64, 64, 64), (65, 72, 136),
     (100, 200, 304), (257, 136, 72), (300, 520, 1000), (513, 264, 520),
     (4100, 4104, 72),          # 256 x 256 tiles with ragged tails in M and N
-    (1000, 1064, 256),         # 128 x 128 four-wave tiles: interior (grouped loads) and edge tiles
-    (640, 384, 4096),          # 128 x 128 four-wave tiles, all interior, long K
+    (1000, 1064, 256),         # 128 x 128 four-wave tiles (short K): interior (grouped loads) and edge tiles
+    (640, 384, 4096),          # 128 x 128 tiles, long K (eight-wave kernel): all interior
+    (1000, 1064, 2056),        # 128 x 128 tiles, long K (eight-wave kernel): edge tiles, K tail
+    (1000, 1064, 2040),        # 128 x 128 tiles just below the long-K switch (four-wave kernel)
     (17, 1000, 520),           # streaming kernel (32-row A), N and K tails
     (60, 2056, 1000),          # streaming kernel (64-row A), N and K tails
 ]
