@@ -143,10 +143,11 @@ def main():
     def warm_clocks(seconds=0.5):
         # Bring clocks and power state to steady load before any timing.
         p = L.lcma_plan_ex(M, N, K, dtype, force="classic")
+        ws = L.workspace_for(p)
         t_end = time.perf_counter() + seconds
         while time.perf_counter() < t_end:
             for _ in range(20):
-                L.lcma_gemm(p, Ad, Bd, C, None)
+                L.lcma_gemm(p, Ad, Bd, C, ws)
             torch.cuda.synchronize()
 
     def time_calls(fn, reps, warm):
@@ -473,7 +474,8 @@ def schedule_study(L, si, torch, time_calls, case, reps, warm):
         calls = {}
         if not case:
             pc = L.lcma_plan_ex(M, N, K, "bf16", force="classic")
-            calls["classic"] = (None, lambda pc=pc: L.lcma_gemm(pc, Ad, Bd, Cd, None))
+            wsc = L.workspace_for(pc)
+            calls["classic"] = (None, lambda pc=pc, wsc=wsc: L.lcma_gemm(pc, Ad, Bd, Cd, wsc))
         for sp, od in variants:
             p = L.lcma_plan_ex(M, N, K, "bf16", force="l1", split=sp, order=od)
             ws = L.workspace_for(p)

@@ -345,9 +345,44 @@ struct lcma_plan_s {
     int64_t gMb, gKb, gNb;
     int8_t gU[kGenMaxRank * kGenMaxBlocks], gV[kGenMaxRank * kGenMaxBlocks], gW[kGenMaxRank * kGenMaxBlocks];
     int64_t offGA, offGB, offGC;
+    // padded plan: a forced LCMA on a shape that does not split evenly runs
+    // `inner` on zero-padded Mp x Kp and Kp x Np copies of A and B in the
+    // workspace and crops its Mp x Np product into C
+    lcma_plan_s* inner = nullptr;
+    int64_t Mp, Np, Kp;
+    int64_t offPA, offPB, offPC, offIn;
 };
 
 static int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Wraps `in`, planned for the Mp x Np x Kp product, into a plan for M x N x K
+// that copies A and B into zero-padded buffers in the workspace, runs `in`
+// there and crops its product into C.  extra_s: estimated seconds of the
+// copies.  Takes ownership of `in`.
+static lcma_status wrap_padded(lcma_plan_s* in, int64_t M, int64_t N, int64_t K, lcma_dtype dt, lcma_algo chosen,
+                               int64_t Mp, int64_t Np, int64_t Kp, const double* est, double extra_s,
+                               lcma_plan_s** out)
+{
+    lcma_plan_s* p = new (std::nothrow) lcma_plan_s();
+    if (!p) {
+        lcma_plan_destroy(in);
+        return LCMA_E_NOMEM;
+    }
+    p->M = M; p->N = N; p->K = K; p->dt = dt; p->chosen = chosen; p->P = in->P;
+    p->levels = in->levels; p->unfused = in->unfused; p->geo = in->geo; p->classic_tile = in->classic_tile;
+    p->inner = in;
+    p->Mp = Mp; p->Np = Np; p->Kp = Kp;
+    p->offPA = 0;
+    p->offPB = align_up(p->offPA + Mp * Kp * 2, 256);
+    p->offPC = align_up(p->offPB + Kp * Np * 2, 256);
+    p->offIn = align_up(p->offPC + Mp * Np * 2, 256);
+    p->ws_bytes = (size_t)(p->offIn + (int64_t)in->ws_bytes);
+    for (int a = 0; a < 4; ++a)
+        p->est[a] = est[a];
+    p->est[chosen] = in->est[chosen] + extra_s;
+    *out = p;
+    return LCMA_OK;
+}
 
 extern "C" {
 
@@ -528,6 +563,38 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     if (ok2)
         est[LCMA_ALGO_L2] = est_lcma(M, N, K, 2, o.split, op_bf16_for(2) != (dt == LCMA_BF16), outer2, m);
 
+    // A forced level of the built-in scheme on a shape that does not split
+    // evenly: zero-pad M, N, K to multiples of (blocks per side) x 16, plan
+    // the padded product and crop it into C.  The zero rows and columns add
+    // nothing to the product; the padding traffic is part of the estimate.
+    const bool forced_lcma = force == LCMA_ALGO_L1 || force == LCMA_ALGO_L2;
+    const int64_t pad_g = (force == LCMA_ALGO_L1 ? 2 : 4) * 16;
+    auto pad_up = [&](int64_t x) { return (x + pad_g - 1) / pad_g * pad_g; };
+    // Padding only changes the shape: an algorithm that is not built for
+    // this description or combine mode stays unsupported, and a shape that
+    // is already a multiple is never padded (so the padded plan below is
+    // always planned without padding).
+    if (forced_lcma && !(force == LCMA_ALGO_L1 ? ok1 : ok2) && !generic &&
+        (force == LCMA_ALGO_L1 ? allow_l1 : allow_l2 && !unfused) && M > 0 && N > 0 && K > 0 &&
+        (pad_up(M) != M || pad_up(N) != N || pad_up(K) != K)) {
+        const int64_t Mp = pad_up(M), Np = pad_up(N), Kp = pad_up(K);
+        if (Mp > INT32_MAX || Np > INT32_MAX || Kp > INT32_MAX)
+            return LCMA_E_UNSUPPORTED;
+        lcma_plan_s* in = nullptr;
+        lcma_status s = lcma_plan_ex(Mp, Np, Kp, dt, desc, force, opts, &in);
+        if (s != LCMA_OK)
+            return s;
+        if (in->inner) {   // cannot happen: the padded shape splits evenly
+            lcma_plan_destroy(in);
+            return LCMA_E_UNSUPPORTED;
+        }
+        // read A, B; write the padded copies; read the padded C window; write C
+        const double pad_bytes = 2.0 * ((double)M * K + (double)K * N + (double)Mp * Kp + (double)Kp * Np) +
+                                 4.0 * (double)M * N;
+        return wrap_padded(in, M, N, K, dt, force, Mp, Np, Kp, est, pad_bytes / (m.eta_bw * m.bw) + 3 * m.launch,
+                           out);
+    }
+
     lcma_algo chosen = force;
     if (force == LCMA_ALGO_L1 && !ok1)
         return LCMA_E_UNSUPPORTED;
@@ -547,6 +614,25 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
             chosen = LCMA_ALGO_L2;
             best = est[LCMA_ALGO_L2];
         }
+    }
+
+    // A classic product whose K or N is not a multiple of 8 cannot use the
+    // 16-byte-load kernels.  A plan has a workspace, so it copies A and B
+    // into zero-padded buffers with K and N rounded up to 8, runs the fast
+    // kernels there and crops C (gemm_classic, which has no workspace, runs
+    // the element-load kernel instead).
+    if (chosen == LCMA_ALGO_CLASSIC && M > 0 && N > 0 && K > 0 && (K % 8 || N % 8)) {
+        const int64_t Np = (N + 7) / 8 * 8, Kp = (K + 7) / 8 * 8;
+        if (Np > INT32_MAX || Kp > INT32_MAX)
+            return LCMA_E_UNSUPPORTED;
+        lcma_plan_s* in = nullptr;
+        lcma_status s = lcma_plan_ex(M, Np, Kp, dt, nullptr, LCMA_ALGO_CLASSIC, &o, &in);
+        if (s != LCMA_OK)
+            return s;
+        const double pad_bytes = 2.0 * ((double)M * K + (double)K * N + (double)M * Kp + (double)Kp * Np) +
+                                 2.0 * (2.0 * (double)M * Np + (double)M * N);
+        return wrap_padded(in, M, N, K, dt, LCMA_ALGO_CLASSIC, M, Np, Kp, est,
+                           pad_bytes / (m.eta_bw * m.bw) + 3 * m.launch, out);
     }
 
     lcma_plan_s* p = new (std::nothrow) lcma_plan_s();
@@ -686,6 +772,12 @@ lcma_status lcma_plan_operand(lcma_plan_t p, int32_t side, int32_t r, int64_t* o
 {
     if (!p || p->levels == 0 || side < 0 || side > 1 || r < 0 || r >= p->geo.R)
         return LCMA_E_INVALID;
+    if (p->inner) {
+        const lcma_status s = lcma_plan_operand(p->inner, side, r, offset, ld, dtype);
+        if (s == LCMA_OK && offset && *offset >= 0)
+            *offset += p->offIn;
+        return s;
+    }
     if (p->unfused) {
         if (offset)
             *offset = side == 0 ? p->offGA + (int64_t)r * p->gMb * p->gKb * 2 : p->offGB + (int64_t)r * p->gKb * p->gNb * 2;
@@ -709,6 +801,8 @@ lcma_status lcma_plan_operand(lcma_plan_t p, int32_t side, int32_t r, int64_t* o
 
 lcma_status lcma_plan_schedule(lcma_plan_t p, int32_t* items, int64_t cap, int64_t* count, int32_t* order)
 {
+    if (p && p->inner)
+        return lcma_plan_schedule(p->inner, items, cap, count, order);
     if (!p || p->levels == 0 || p->unfused || !count || (cap > 0 && !items))
         return LCMA_E_INVALID;
     int64_t n = 0;
@@ -729,7 +823,12 @@ lcma_status lcma_plan_schedule(lcma_plan_t p, int32_t* items, int64_t cap, int64
     return LCMA_OK;
 }
 
-void lcma_plan_destroy(lcma_plan_t p) { delete p; }
+void lcma_plan_destroy(lcma_plan_t p)
+{
+    if (p)
+        lcma_plan_destroy(p->inner);
+    delete p;
+}
 
 }  // extern "C"
 
@@ -781,6 +880,31 @@ lcma_status check_ws(const lcma_plan_s* p, void* ws, size_t ws_bytes)
     if (!ws || ws_bytes < p->ws_bytes || ((uintptr_t)ws % 256) != 0)
         return LCMA_E_WORKSPACE;
     return LCMA_OK;
+}
+
+// Padded plans.  The element-wise pad and crop kernels take any alignment,
+// so only the arguments' validity and the workspace are checked here.
+lcma_status check_padded_call(const lcma_plan_s* p, const void* A, int64_t lda, const void* B, int64_t ldb,
+                              const void* C, int64_t ldc, void* ws, size_t ws_bytes, bool need_c)
+{
+    Io io;
+    const lcma_status s = check_io(p->M, p->N, p->K, A, lda, B, ldb, C, ldc, &io, need_c);
+    return s != LCMA_OK ? s : check_ws(p, ws, ws_bytes);
+}
+
+lcma_status pad_operands(const lcma_plan_s* p, const void* A, int64_t lda, const void* B, int64_t ldb, void* ws,
+                         hipStream_t st)
+{
+    char* w = (char*)ws;
+    if (hip_status(launch_pad_copy(A, lda, p->M, p->K, w + p->offPA, p->Kp, p->Mp, p->Kp, st), "pad A") != LCMA_OK ||
+        hip_status(launch_pad_copy(B, ldb, p->K, p->N, w + p->offPB, p->Np, p->Kp, p->Np, st), "pad B") != LCMA_OK)
+        return LCMA_E_HIP;
+    return LCMA_OK;
+}
+
+lcma_status crop_output(const lcma_plan_s* p, void* C, int64_t ldc, void* ws, hipStream_t st)
+{
+    return hip_status(launch_pad_copy((char*)ws + p->offPC, p->Np, p->M, p->N, C, ldc, p->M, p->N, st), "crop C");
 }
 
 lcma_status do_prepass(const lcma_plan_s* p, const void* A, int64_t lda, const void* B, int64_t ldb, void* ws,
@@ -1040,6 +1164,17 @@ lcma_status lcma_gemm(lcma_plan_t p, const void* A, int64_t lda, const void* B, 
     if (!p)
         return LCMA_E_INVALID;
     hipStream_t st = (hipStream_t)stream;
+    if (p->inner) {
+        lcma_status s = check_padded_call(p, A, lda, B, ldb, C, ldc, ws, ws_bytes, true);
+        if (s != LCMA_OK)
+            return s;
+        char* w = (char*)ws;
+        s = pad_operands(p, A, lda, B, ldb, ws, st);
+        if (s == LCMA_OK)
+            s = lcma_gemm(p->inner, w + p->offPA, p->Kp, w + p->offPB, p->Np, w + p->offPC, p->Np, w + p->offIn,
+                          p->inner->ws_bytes, stream);
+        return s != LCMA_OK ? s : crop_output(p, C, ldc, ws, st);
+    }
     if (p->levels == 0) {
         Io io;
         lcma_status s = check_io(p->M, p->N, p->K, A, lda, B, ldb, C, ldc, &io);
@@ -1066,6 +1201,15 @@ lcma_status lcma_prepass(lcma_plan_t p, const void* A, int64_t lda, const void* 
 {
     if (!p || p->levels == 0)
         return LCMA_E_INVALID;
+    if (p->inner) {
+        lcma_status s = check_padded_call(p, A, lda, B, ldb, nullptr, 0, ws, ws_bytes, false);
+        if (s == LCMA_OK)
+            s = pad_operands(p, A, lda, B, ldb, ws, (hipStream_t)stream);
+        char* w = (char*)ws;
+        return s != LCMA_OK ? s
+                            : lcma_prepass(p->inner, w + p->offPA, p->Kp, w + p->offPB, p->Np, w + p->offIn,
+                                           p->inner->ws_bytes, stream);
+    }
     Io io;
     lcma_status s = check_lcma_call(p, A, lda, B, ldb, nullptr, 0, ws, ws_bytes, false, &io);
     if (s != LCMA_OK)
@@ -1080,6 +1224,15 @@ lcma_status lcma_fused(lcma_plan_t p, const void* A, int64_t lda, const void* B,
 {
     if (!p || p->levels == 0)
         return LCMA_E_INVALID;
+    if (p->inner) {
+        // the padded operands were written by lcma_prepass on this workspace
+        lcma_status s = check_padded_call(p, A, lda, B, ldb, C, ldc, ws, ws_bytes, true);
+        char* w = (char*)ws;
+        if (s == LCMA_OK)
+            s = lcma_fused(p->inner, w + p->offPA, p->Kp, w + p->offPB, p->Np, w + p->offPC, p->Np, w + p->offIn,
+                           p->inner->ws_bytes, stream);
+        return s != LCMA_OK ? s : crop_output(p, C, ldc, ws, (hipStream_t)stream);
+    }
     Io io;
     lcma_status s = check_lcma_call(p, A, lda, B, ldb, C, ldc, ws, ws_bytes, true, &io);
     if (s != LCMA_OK)

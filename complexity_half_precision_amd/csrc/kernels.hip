@@ -2328,7 +2328,43 @@ hipError_t launch_fused_t(const FusedLaunch& L, hipStream_t st)
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ padding
+//
+// Zero-padding of operands to a shape that splits evenly, and the crop of
+// the padded product back into C.  Each thread moves 8 consecutive elements
+// of one row; rows beyond the grid's y extent are taken in strides.
+
+__global__ void __launch_bounds__(256) k_pad_copy(const u16* __restrict__ src, int64_t lds, int64_t rows,
+                                                  int64_t cols, u16* __restrict__ dst, int64_t ldd, int64_t prows,
+                                                  int64_t pcols)
+{
+    const int64_t j0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (j0 >= pcols)
+        return;
+    for (int64_t i = blockIdx.y; i < prows; i += gridDim.y) {
+        u16* d = dst + i * ldd;
+        const u16* sr = src + i * lds;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int64_t j = j0 + t;
+            if (j < pcols)
+                d[j] = (i < rows && j < cols) ? sr[j] : (u16)0;
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_pad_copy(const void* src, int64_t lds, int64_t rows, int64_t cols, void* dst, int64_t ldd,
+                           int64_t prows, int64_t pcols, hipStream_t st)
+{
+    if (prows <= 0 || pcols <= 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)((pcols + 2047) / 2048), (unsigned)std::min<int64_t>(prows, 65535));
+    hipLaunchKernelGGL(k_pad_copy, grid, dim3(256), 0, st, (const u16*)src, lds, rows, cols, (u16*)dst, ldd, prows,
+                       pcols);
+    return hipGetLastError();
+}
 
 // ------------------------------------------------------------------ host entry points
 

@@ -46,6 +46,12 @@ struct PrepassLaunch {
 };
 hipError_t launch_prepass(const PrepassLaunch& L, hipStream_t stream);
 
+// Copies the rows x cols window of src (16-bit elements, ld lds) into the
+// top-left of the prows x pcols matrix dst (ld ldd) and writes zeros in the
+// rest of dst (prows >= rows and pcols >= cols pad; equal sizes crop).
+hipError_t launch_pad_copy(const void* src, int64_t lds, int64_t rows, int64_t cols, void* dst, int64_t ldd,
+                           int64_t prows, int64_t pcols, hipStream_t stream);
+
 struct FusedParams {
     const uint16_t* a[kMaxRank];   // operand origin (block row 0, col 0) per canonical product
     const uint16_t* b[kMaxRank];

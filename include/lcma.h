@@ -175,8 +175,14 @@ lcma_status lcma_desc_validate(const lcma_desc* desc);
  *          LCMA_ALGO_L2 is LCMA_E_UNSUPPORTED.  One level of a description
  *          (ms, ks, ns) needs M, K, N divisible by ms, ks, ns.
  *   force: LCMA_ALGO_AUTO lets the roofline cost model pick among the
- *          admissible algorithms (ties go to classic);
- *          a forced L1/L2 on a shape it cannot split returns
+ *          admissible algorithms (ties go to classic); shapes that do not
+ *          split evenly are left to classic.
+ *          A forced L1/L2 of the built-in scheme on a shape that does not
+ *          split evenly is zero-padded: M, N, K are rounded up to multiples
+ *          of 32 (L1) or 64 (L2), A and B are copied into zero-padded
+ *          buffers in the workspace, the padded product runs there and its
+ *          M x N window is copied into C (any alignment and leading
+ *          dimensions).  Other forced combinations that do not fit return
  *          LCMA_E_UNSUPPORTED.
  * Sizes: M, N, K >= 0 (negative: LCMA_E_INVALID).  Zero-sized products are
  * valid (K = 0 writes C = 0).  Performs no device work; the only HIP call
@@ -200,7 +206,8 @@ lcma_status lcma_plan_estimate(lcma_plan_t plan, lcma_algo algo, double* est_sec
 
 /* Runs the planned product on `stream`.  A, B, C: device pointers as above.
  * Fast path: pointers 16-byte aligned and lda, ldb multiples of 8; classic
- * accepts any alignment (slower element loads), LCMA paths require it
+ * and padded LCMA plans accept any alignment (slower element loads, resp.
+ * element-wise padding copies), other LCMA plans require it
  * (LCMA_E_UNSUPPORTED otherwise).  workspace: device memory of at least
  * the planned size (may be NULL when that size is 0); it must not be used
  * by two calls that can overlap.
@@ -214,8 +221,11 @@ lcma_status lcma_gemm(lcma_plan_t plan, const void* A, int64_t lda, const void* 
  * so each kernel can be checked and timed on its own: lcma_prepass writes
  * the combined operands (and clears the split counters) in the workspace;
  * lcma_fused then runs the persistent group kernel from them.  Calling
- * lcma_prepass then lcma_fused on one stream equals lcma_gemm.  For other
- * plans: LCMA_E_INVALID. */
+ * lcma_prepass then lcma_fused on one stream equals lcma_gemm.  Unfused
+ * plans: lcma_prepass writes every combined operand, lcma_fused runs the
+ * products and their folds.  Padded plans: lcma_prepass also writes the
+ * zero-padded copies of A and B, lcma_fused also crops the padded product
+ * into C.  Classic plans: LCMA_E_INVALID. */
 lcma_status lcma_prepass(lcma_plan_t plan, const void* A, int64_t lda, const void* B, int64_t ldb,
                          void* workspace, size_t workspace_bytes, void* stream);
 lcma_status lcma_fused(lcma_plan_t plan, const void* A, int64_t lda, const void* B, int64_t ldb,
@@ -226,7 +236,9 @@ lcma_status lcma_fused(lcma_plan_t plan, const void* A, int64_t lda, const void*
  * workspace: side 0 = A (an (M/ms) x (K/ks) matrix), side 1 = B (a (K/ks) x
  * (N/ns) matrix).  *offset_bytes receives its byte offset and *ld its
  * leading dimension; *offset_bytes = -1 when the operand is a single input
- * block read in place (not copied).  *dtype receives the operand type. */
+ * block read in place (not copied).  *dtype receives the operand type.
+ * A padded plan reports the operands of its padded product (blocks of the
+ * padded shape). */
 lcma_status lcma_plan_operand(lcma_plan_t plan, int32_t side, int32_t r, int64_t* offset_bytes,
                               int64_t* ld, lcma_dtype* dtype);
 
@@ -236,7 +248,8 @@ lcma_status lcma_plan_operand(lcma_plan_t plan, int32_t side, int32_t r, int64_t
  * a whole group).  *count receives the total number of items (call with
  * cap = 0 to size).  *order (if not NULL, `rank` entries) receives the
  * kernel's product order.  LCMA_E_INVALID for a classic plan and for an
- * unfused one (it has no persistent schedule). */
+ * unfused one (it has no persistent schedule).  A padded plan reports the
+ * schedule of its padded product. */
 lcma_status lcma_plan_schedule(lcma_plan_t plan, int32_t* items, int64_t cap, int64_t* count,
                                int32_t* order);
 

@@ -137,6 +137,10 @@ def test_builtin_scheme_can_be_forced_unfused():
     assert algo == "l1" and ws == 7 * 512 * 512 * 2 * 2 + 4 * 512 * 512 * 4
     with pytest.raises(L.LcmaError):
         L.lcma_plan_ex(1024, 1024, 1024, "bf16", force="l2", combine="unfused", num_cus=CUS)
+    # padding changes only the shape: two levels stay unsupported unfused
+    with pytest.raises(L.LcmaError) as e:
+        L.lcma_plan_ex(1000, 1000, 1000, "bf16", force="l2", combine="unfused", num_cus=CUS)
+    assert e.value.status == L.E_UNSUPPORTED
 
 
 def test_plan_rejects_bad_descriptor():
@@ -168,10 +172,56 @@ def test_plan_rejects_bad_enums():
 
 
 @pytest.mark.parametrize("M,N,K,algo", [(511, 512, 512, "l1"), (512, 512, 8, "l1"), (512, 12, 512, "l1"),
-                                        (512, 512, 100, "l2"), (1, 4096, 4096, "l1")])
-def test_forced_lcma_on_unsplittable_shape_is_unsupported(M, N, K, algo):
+                                        (512, 512, 100, "l2"), (1, 4096, 4096, "l1"), (1000, 1032, 520, "l2")])
+def test_forced_lcma_on_unsplittable_shape_is_padded(M, N, K, algo):
+    # zero-padded to multiples of (blocks per side) x 16, planned as that
+    # product, cropped into C; the workspace holds the padded copies and the
+    # padded plan's own workspace
+    g = (2 if algo == "l1" else 4) * 16
+    up = lambda x: -(-x // g) * g
+    Mp, Np, Kp = up(M), up(N), up(K)
+    p = L.lcma_plan_ex(M, N, K, "f16", force=algo, num_cus=CUS)
+    chosen, ws, est = L.lcma_plan_info(p)
+    inner = L.lcma_plan_ex(Mp, Np, Kp, "f16", force=algo, num_cus=CUS)
+    _, ws_in, est_in = L.lcma_plan_info(inner)
+    assert chosen == algo
+    assert ws >= 2 * (Mp * Kp + Kp * Np + Mp * Np) + ws_in
+    assert est > est_in
+    # the schedule and operands are the padded plan's
+    if L.lcma_plan_info(inner)[0] == algo:
+        try:
+            assert L.lcma_plan_schedule(p)[0] == L.lcma_plan_schedule(inner)[0]
+        except L.LcmaError:
+            pass
+    # a workspace smaller than reported fails before any device work
+    assert L._lib_gemm(p.handle, 4096, K, 4096, N, 8192, N, 1 << 20, ws - 1, None) == L.E_WORKSPACE
+    # automatic planning keeps classic for shapes that do not split
+    assert L.lcma_plan_info(L.lcma_plan_ex(M, N, K, "f16", num_cus=CUS))[0] == "classic"
+
+
+@pytest.mark.parametrize("M,N,K", [(100, 200, 300), (257, 13, 64), (1, 14337, 4096), (4100, 4100, 4100)])
+def test_classic_plan_pads_k_and_n_to_multiples_of_8(M, N, K):
+    p = L.lcma_plan_ex(M, N, K, "bf16", num_cus=CUS)
+    chosen, ws, est = L.lcma_plan_info(p)
+    assert chosen == "classic"
+    Np, Kp = -(-N // 8) * 8, -(-K // 8) * 8
+    inner = L.lcma_plan_ex(M, Np, Kp, "bf16", force="classic", num_cus=CUS)
+    assert L.lcma_plan_info(inner)[1] == 0
+    assert ws >= 2 * (M * Kp + Kp * Np + M * Np)
+    assert est > L.lcma_plan_info(inner)[2]
+    # aligned shapes need no workspace
+    assert L.lcma_plan_info(L.lcma_plan_ex(M, Np, Kp, "bf16", num_cus=CUS))[1] == 0
+    # the two halves are for LCMA plans only
+    assert L._lib_prepass(p.handle, 4096, K, 4096, N, 1 << 20, ws, None) == L.E_INVALID
+
+
+def test_padding_is_only_for_the_built_in_schemes():
+    # a description that is not built in runs one level of itself unfused and
+    # needs M, K, N divisible by its block counts
+    d = oracle.naive(2, 2, 2)
+    desc = L.Desc(2, 2, 2, d.U, d.V, d.W)
     with pytest.raises(L.LcmaError) as e:
-        L.lcma_plan_ex(M, N, K, "f16", force=algo, num_cus=CUS)
+        L.lcma_plan_ex(511, 512, 512, "f16", desc=desc, force="l1", num_cus=CUS)
     assert e.value.status == L.E_UNSUPPORTED
 
 

@@ -302,6 +302,70 @@ def test_l1_plain_order_equals_locality_order(M, N, split):
     assert metrics.freivalds(si.f64(C1), A64, B64) <= 4 * metrics.UNIT_ROUNDOFF["bf16"]
 
 
+# ---------------------------------------------------------------- padded shapes
+
+@pytest.mark.parametrize("algo,M,N,K,dtype,dist", [
+    ("l1", 511, 520, 500, "f16", "int2"),            # integer inputs: exact
+    ("l2", 300, 200, 250, "f16", "int2"),
+    ("l1", 1000, 1032, 520, "bf16", "normal_sqrtk"),
+    ("l2", 1000, 1032, 520, "bf16", "normal_sqrtk"),
+    ("l1", 1, 4096, 4096, "bf16", "normal_sqrtk"),   # one row, padded to 32
+])
+def test_padded_lcma_matches_oracle(algo, M, N, K, dtype, dist):
+    # a forced level on a shape that does not split evenly runs on zero-padded
+    # copies of A and B and crops the padded product into C
+    say("padded", algo, M, N, K, dtype)
+    A, B, A64, B64 = gen(M, N, K, dtype, dist, seed=M + 2 * N + 3 * K)
+    C = planned(A, B, algo)
+    if dist.startswith("int"):
+        check_exact(C, A64, B64, dtype)
+    else:
+        check_float(C, A64, B64, dtype)
+
+
+@pytest.mark.parametrize("M,N,K,dtype,dist", [(300, 522, 1000, "f16", "uniform"), (257, 13, 64, "bf16", "normal_sqrtk"),
+                                              (1, 14337, 4096, "bf16", "decode"), (1000, 1064, 2050, "bf16", "normal_sqrtk"),
+                                              (513, 264, 519, "f16", "int2")])
+def test_classic_plan_with_ragged_k_or_n(M, N, K, dtype, dist):
+    # a classic plan pads K and N to multiples of 8 in its workspace, runs the
+    # 16-byte-load kernels and crops C; gemm_classic takes the element-load
+    # kernel on the same inputs
+    say("classic ragged plan", M, N, K, dtype)
+    A, B, A64, B64 = gen(M, N, K, dtype, dist, seed=M + N + K + 1)
+    plan = L.lcma_plan_ex(M, N, K, dtype)
+    assert L.lcma_plan_info(plan)[0] == "classic" and L.lcma_plan_info(plan)[1] > 0
+    C = planned(A, B, "classic")
+    if dist.startswith("int"):
+        check_exact(C, A64, B64, dtype)
+        check_exact(classic(A, B), A64, B64, dtype)
+    else:
+        check_float(C, A64, B64, dtype)
+        check_float(classic(A, B), A64, B64, dtype)
+
+
+def test_padded_lcma_strided_and_split_calls():
+    # strided, unaligned operands; lcma_prepass + lcma_fused equal lcma_gemm;
+    # nothing is written outside C
+    say("padded strided")
+    M, N, K = 333, 250, 210
+    Abig, Bbig, _, _ = gen(M, N + 3, K + 5, "f16", "uniform", seed=5)
+    A, B = Abig[:, :K], Bbig[:K, :N]
+    A64, B64 = si.f64(A), si.f64(B)
+    Ad, Bd = Abig.to(DEV)[:, :K], Bbig.to(DEV)[:K, :N]
+    plan = L.lcma_plan_ex(M, N, K, "f16", force="l1")
+    ws = L.workspace_for(plan)
+    Cbig = torch.full((M, N + 7), 7.0, dtype=torch.float16, device=DEV)
+    C = Cbig[:, :N]
+    L.lcma_gemm(plan, Ad, Bd, C, ws)
+    C2 = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    L.lcma_prepass(plan, Ad, Bd, ws)
+    L.lcma_fused(plan, Ad, Bd, C2, ws)
+    torch.cuda.synchronize()
+    check_float(C.cpu(), A64, B64, "f16")
+    assert torch.equal(C.cpu(), C2.cpu())
+    assert torch.all(Cbig[:, N:].cpu() == 7.0)
+
+
 # ---------------------------------------------------------------- unfused path (any valid description)
 
 def winograd():
