@@ -565,8 +565,11 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
 
     // A forced level of the built-in scheme on a shape that does not split
     // evenly: zero-pad M, N, K to multiples of (blocks per side) x 16, plan
-    // the padded product and crop it into C.  The zero rows and columns add
-    // nothing to the product; the padding traffic is part of the estimate.
+    // the padded product and crop it into C (zero-padding non-divisible
+    // dimensions to reach an efficient blocking: "CUDA-L2: Surpassing cuBLAS
+    // Performance for Matrix Multiplication through Reinforcement Learning",
+    // section "核心贡献与发现的技术").  The zero rows and columns add nothing
+    // to the product; the padding traffic is part of the estimate.
     const bool forced_lcma = force == LCMA_ALGO_L1 || force == LCMA_ALGO_L2;
     const int64_t pad_g = (force == LCMA_ALGO_L1 ? 2 : 4) * 16;
     auto pad_up = [&](int64_t x) { return (x + pad_g - 1) / pad_g * pad_g; };
