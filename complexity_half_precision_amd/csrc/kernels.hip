@@ -1345,8 +1345,10 @@ __device__ __forceinline__ void store_c_staged(const f32x4 (&acc)[C::FM][C::FN],
         const u32x4 v = *reinterpret_cast<const u32x4*>(reg + row * C::SROW + ch * 16);
         const int m = wm * C::WTM + row, n = wn * C::WTN + ch * 8;
         const u32 off = (m < rows && n < cols) ? (u32)(m * ld + n) * 2u : kOob;
+        // non-temporal (aux bit 1): C is not read back by the kernel; measured
+        // 1-1.5% faster at 4096^3 and within noise elsewhere
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v),
-                                               rc, off, 0, 0);
+                                               rc, off, 0, 2);
     }
 }
 
