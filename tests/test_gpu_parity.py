@@ -366,6 +366,32 @@ def test_padded_lcma_strided_and_split_calls():
     assert torch.all(Cbig[:, N:].cpu() == 7.0)
 
 
+def _random_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        M, N, K = (int(x) for x in rng.integers(1, 700, size=3))
+        algo = ["classic", "l1", "l2", "auto"][i % 4]
+        dtype = ["f16", "bf16"][(i // 4) % 2]
+        cases.append((i, M, N, K, algo, dtype))
+    return cases
+
+
+@pytest.mark.parametrize("i,M,N,K,algo,dtype", _random_cases(32, 2024))
+def test_random_shapes_every_path(i, M, N, K, algo, dtype):
+    # seeded random shapes (1..699 per dimension, mostly ragged): classic plans
+    # (padded when K or N is not a multiple of 8), forced one and two levels
+    # (zero-padded when the shape does not split), and the planner's choice
+    say("random", i, M, N, K, algo, dtype)
+    A, B, A64, B64 = gen(M, N, K, dtype, "uniform", seed=7000 + i)
+    plan = L.lcma_plan_ex(M, N, K, dtype, force=algo)
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    C = torch.empty((M, N), dtype=A.dtype, device=DEV)
+    L.lcma_gemm(plan, Ad, Bd, C, L.workspace_for(plan))
+    torch.cuda.synchronize()
+    check_float(C.cpu(), A64, B64, dtype)
+
+
 # ---------------------------------------------------------------- unfused path (any valid description)
 
 def winograd():
