@@ -24,6 +24,9 @@
  *            cast.
  *   [KP] "Kernel 与性能" notes page, section "Roofline" (I = FLOPs / bytes,
  *        F <= min(F_max, I * B_max)).
+ *   [CL2] "CUDA-L2: Surpassing cuBLAS Performance for Matrix Multiplication
+ *        through Reinforcement Learning", section "核心贡献与发现的技术" --
+ *            zero-padding of dimensions that do not divide the blocking.
  *
  * Memory ownership: the caller owns A, B, C and the workspace (device
  * memory).  The library never allocates device memory.  A plan owns only
