@@ -1058,6 +1058,80 @@ lcma_status do_gen_prepass(const lcma_plan_s* p, const void* A, int64_t lda, con
 // one rounds it into C (a block fed by one product goes straight to C), so
 // no fill or final rounding pass is needed.  Brent's identity gives every
 // output block at least one product.
+// Run order and folds of the persistent unfused kernel.  A product that
+// feeds a single output block o with coefficient +-1 runs right after a
+// product that also feeds o with coefficient +-1 and continues its
+// accumulators: the first run folds its other blocks from the accumulators
+// (which then hold its product alone) and carries o; the second starts from
+// them (negated when the two coefficients differ in sign) and folds the sum,
+// so o takes one fp32 round trip less.  The remaining products follow in
+// their own order.  Fold modes (store, add, finish, only) are then those of
+// the run sequence.
+void gen_group_runs(const lcma_plan_s* p, int nout, GenGroupLaunch* G)
+{
+    const int R = p->gR;
+    auto W = [&](int r, int o) { return (int)p->gW[r * kGenMaxBlocks + o]; };
+    auto single = [&](int r, int* o_out) {
+        int n = 0, o1 = -1;
+        for (int o = 0; o < nout; ++o)
+            if (W(r, o) != 0) {
+                ++n;
+                o1 = o;
+            }
+        *o_out = o1;
+        return n == 1 && (W(r, o1) == 1 || W(r, o1) == -1);
+    };
+    bool used[kGenMaxRank] = {};
+    int seq[kGenMaxRank], carried[kGenMaxRank], n = 0;   // carried: block a run hands to the next, or -1
+    for (int q = 0; q < R; ++q) {
+        int o;
+        if (used[q] || !single(q, &o))
+            continue;
+        for (int r = 0; r < R; ++r) {
+            if (r == q || used[r] || (W(r, o) != 1 && W(r, o) != -1))
+                continue;
+            used[r] = used[q] = true;
+            seq[n] = r; carried[n] = o; ++n;
+            seq[n] = q; carried[n] = -1; ++n;
+            break;
+        }
+    }
+    for (int r = 0; r < R; ++r)
+        if (!used[r]) {
+            seq[n] = r; carried[n] = -1; ++n;
+        }
+    // Fold coefficient of run j into block o (0 = no fold): the head of a
+    // chain does not fold the carried block; the tail folds it with its own
+    // coefficient (its accumulators hold that sign times the partial sum).
+    int fw[kGenMaxRank][kGenMaxBlocks];
+    for (int j = 0; j < R; ++j) {
+        const int r = seq[j];
+        G->prod[j] = (int8_t)r;
+        const bool tail = j > 0 && carried[j - 1] >= 0;
+        G->carry[j] = !tail ? 0 : (W(r, carried[j - 1]) == W(seq[j - 1], carried[j - 1]) ? 1 : 2);
+        for (int o = 0; o < nout; ++o)
+            fw[j][o] = o == carried[j] ? 0 : W(r, o);
+    }
+    for (int o = 0; o < nout; ++o) {
+        int f = -1, l = -1, c = 0;
+        for (int j = 0; j < R; ++j)
+            if (fw[j][o] != 0) {
+                f = f < 0 ? j : f;
+                l = j;
+                ++c;
+            }
+        for (int j = 0; j < R; ++j) {
+            const int w = fw[j][o];
+            G->w[j * kGenMaxBlocks + o] = (int8_t)w;
+            G->mode[j * kGenMaxBlocks + o] = w == 0  ? kOuterNone
+                                             : c == 1 ? kOuterOnly
+                                             : j == f ? kOuterStore
+                                             : j == l ? kOuterFinish
+                                                      : kOuterAdd;
+        }
+    }
+}
+
 lcma_status do_gen_products(const lcma_plan_s* p, void* C, int64_t ldc, void* ws, hipStream_t st)
 {
     float* acc = (float*)((char*)ws + p->offGC);
@@ -1089,16 +1163,7 @@ lcma_status do_gen_products(const lcma_plan_s* p, void* C, int64_t ldc, void* ws
         G.op_bf16 = p->op_bf16; G.out_bf16 = p->dt == LCMA_BF16; G.P = p->P;
         G.nout = nout; G.ncols = p->gns;
         G.acc = acc; G.C = C; G.ldc = ldc;
-        for (int r = 0; r < p->gR; ++r)
-            for (int o = 0; o < nout; ++o) {
-                const int w = p->gW[r * kGenMaxBlocks + o];
-                G.w[r * kGenMaxBlocks + o] = (int8_t)w;
-                G.mode[r * kGenMaxBlocks + o] = w == 0           ? kOuterNone
-                                                : uses[o] == 1   ? kOuterOnly
-                                                : r == first[o]  ? kOuterStore
-                                                : r == last[o]   ? kOuterFinish
-                                                                 : kOuterAdd;
-            }
+        gen_group_runs(p, nout, &G);
         return hip_status(launch_gen_group(G, st), "launch_gen_group");
     }
     for (int r = 0; r < p->gR; ++r) {

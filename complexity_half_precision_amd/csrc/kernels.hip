@@ -1587,9 +1587,12 @@ struct GenGroupParams {
     int M, N, K, R, P, nout, ncols;
     float* acc;                        // fp32 block o at acc + o * M * N (ld N)
     u16* C; int64_t ldc;               // block o of C at row (o / ncols) * M, column (o % ncols) * N
-    int8_t w[kGenMaxRank * kGenMaxBlocks];
-    int8_t mode[kGenMaxRank * kGenMaxBlocks];   // OuterMode per (product, block)
+    int8_t w[kGenMaxRank * kGenMaxBlocks];      // fold coefficient per (run, block)
+    int8_t mode[kGenMaxRank * kGenMaxBlocks];   // OuterMode per (run, block)
+    int8_t prod[kGenMaxRank];                    // product of run j
+    int8_t carry[kGenMaxRank];                   // 0: zero accumulators, 1: keep, 2: negate
 };
+static_assert(sizeof(GenGroupParams) <= 4096, "kernel argument segment");
 
 // EDGE: some position is a partial tile or K is not a multiple of 32 (then
 // every position takes the bounds-checked loads: one K-loop form per kernel
@@ -1608,7 +1611,9 @@ __global__ void __launch_bounds__(C::NT, 1) k_gen_group_m16(const GenGroupParams
         int p, q;
         tile_coords(item, gy, gx, gp.P, 8, &p, &q);
         const int m0 = p * C::BM, n0 = q * C::BN, rows = gp.M - m0, cols = gp.N - n0;
-        for (int r = 0; r < gp.R; ++r) {
+        f32x4 acc[C::FM][C::FN];
+        for (int run = 0; run < gp.R; ++run) {
+            const int r = gp.prod[run], cy = gp.carry[run];
             // Opaque per product: keeps lane-derived addresses (fold offsets,
             // fragment offsets) from being hoisted out of the loops and held
             // in registers through every K loop.
@@ -1620,19 +1625,26 @@ __global__ void __launch_bounds__(C::NT, 1) k_gen_group_m16(const GenGroupParams
             auto src = [&](int t) {
                 return tiles::TileSrc{Ab, gp.K, rows, Bb, gp.N, cols, t * C::BK, gp.K};
             };
-            f32x4 acc[C::FM][C::FN];
-            zero_acc<C>(acc);
+            if (cy == 0) {
+                zero_acc<C>(acc);
+            } else if (cy == 2) {
+#pragma unroll
+                for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::FN; ++j)
+                        acc[i][j] = -acc[i][j];
+            }
             __syncthreads();   // every wave is done reading the ring of the previous product
             m16::run_tile<C, BF, EDGE, !EDGE>(smem, nk, src, none, wave, lane, ad, acc);
             for (int o = 0; o < gp.nout; ++o) {
-                const int mode = gp.mode[r * kGenMaxBlocks + o];
+                const int mode = gp.mode[run * kGenMaxBlocks + o];
                 if (mode == kOuterNone)
                     continue;
                 const int bi = o / gp.ncols, bj = o % gp.ncols;
                 fold_target<CBF, C::FM * C::FN, 8>(
                     make_rsrc(gp.acc + (int64_t)o * gp.M * gp.N + (int64_t)m0 * gp.N + n0),
                     make_rsrc(gp.C + (int64_t)(bi * gp.M + m0) * gp.ldc + bj * gp.N + n0), gp.N, (int)gp.ldc, mode,
-                    (float)gp.w[r * kGenMaxBlocks + o], rows, cols, [&](int e, int& m, int& n, f32x4& h) {
+                    (float)gp.w[run * kGenMaxBlocks + o], rows, cols, [&](int e, int& m, int& n, f32x4& h) {
                         const int i = e / C::FN, j = e % C::FN;
                         m = wm * C::WTM + i * 16 + (lane & 15);
                         n = wn * C::WTN + j * 16 + 4 * (lane >> 4);
@@ -1659,6 +1671,10 @@ hipError_t launch_gen_group_t(const GenGroupLaunch& L, hipStream_t st)
     for (int i = 0; i < kGenMaxRank * kGenMaxBlocks; ++i) {
         gp.w[i] = L.w[i];
         gp.mode[i] = L.mode[i];
+    }
+    for (int i = 0; i < kGenMaxRank; ++i) {
+        gp.prod[i] = L.prod[i];
+        gp.carry[i] = L.carry[i];
     }
     const bool edge = L.M % C::BM != 0 || L.N % C::BN != 0 || L.K % C::BK != 0;
     const dim3 grid((unsigned)std::min(items, L.P));

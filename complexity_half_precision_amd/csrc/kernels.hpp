@@ -130,8 +130,15 @@ struct GenGroupLaunch {
     int32_t M, N, K, R, op_bf16, out_bf16, P, nout, ncols;
     float* acc;
     void* C; int64_t ldc;
+    // Per run j (the products in the order they run): prod[j] is the
+    // product, w / mode[j * kGenMaxBlocks + o] its fold into block o, and
+    // carry[j] how its accumulators start: 0 = zero, 1 = as the previous
+    // run left them, 2 = negated (a chained run continues the partial sum of
+    // the one output block it shares with the run before it).
     int8_t w[kGenMaxRank * kGenMaxBlocks];
     int8_t mode[kGenMaxRank * kGenMaxBlocks];
+    int8_t prod[kGenMaxRank];
+    int8_t carry[kGenMaxRank];
 };
 hipError_t launch_gen_group(const GenGroupLaunch& L, hipStream_t stream);
 
