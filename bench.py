@@ -203,12 +203,15 @@ def main():
     detail = {}
     only = set(a for a in args.only.split(",") if a)
     plans = {}
-    for algo in ("classic", "l1", "l2", "l2_bf16_operands", "l1_unfused"):
+    for algo in ("classic", "l1", "l2", "l2_bf16_operands", "l1_unfused", "l1_at_load"):
         if only and algo not in only:
             continue
         try:
             if algo == "l1_unfused":
                 p = L.lcma_plan_ex(M, N, K, dtype, force="l1", combine="unfused")
+            elif algo == "l1_at_load":
+                # one launch: the group kernel combines the input blocks itself
+                p = L.lcma_plan_ex(M, N, K, dtype, force="l1", combine="at_load")
             elif algo == "l1":
                 # the fused group kernel after a pre-pass (the planner itself
                 # takes the unfused path for large blocks)
@@ -227,7 +230,10 @@ def main():
     for algo, (p, ws) in plans.items():
         t_all = time_calls(lambda: L.lcma_gemm(p, Ad, Bd, C, ws), reps, args.warmup)
         d = {"ms": t_all, "eff_tflops": flops / (t_all * 1e-3) / 1e12, "est_ms": L.lcma_plan_info(p)[2] * 1e3}
-        if algo != "classic":
+        if algo == "l1_at_load":
+            mfma_flops = 2.0 * 7 * (M // 2) * (N // 2) * (K // 2)
+            d.update({"fused_mfma_tflop": mfma_flops / 1e12, "fused_tflops_actual": mfma_flops / (t_all * 1e-3) / 1e12})
+        elif algo != "classic":
             t_pre = time_calls(lambda: L.lcma_prepass(p, Ad, Bd, ws), reps, args.warmup)
             L.lcma_prepass(p, Ad, Bd, ws)
             t_fu = time_calls(lambda: L.lcma_fused(p, Ad, Bd, C, ws), reps, args.warmup)
@@ -244,7 +250,7 @@ def main():
         if args.cold:
             reps_c = min(reps, 20)
             d["cold_ms"] = time_cold(lambda: L.lcma_gemm(p, Ad, Bd, C, ws), reps_c)
-            if algo != "classic":
+            if algo not in ("classic", "l1_at_load"):
                 t_pre_c = time_cold(lambda: L.lcma_prepass(p, Ad, Bd, ws), reps_c)
                 d.update({"cold_prepass_ms": t_pre_c, "cold_prepass_gbps": d["prepass_bytes"] / (t_pre_c * 1e-3) / 1e9})
         if args.server:
@@ -329,6 +335,8 @@ def main():
     }
     if "l1" in detail and "classic" in detail:
         out["l1_over_classic"] = round(detail["classic"]["ms"] / detail["l1"]["ms"], 4)
+    if "l1_at_load" in detail and "classic" in detail:
+        out["l1_at_load_over_classic"] = round(detail["classic"]["ms"] / detail["l1_at_load"]["ms"], 4)
     if "l1" in detail and "l1_unfused" in detail:
         # the fusion gain: same scheme, products folded on chip vs through fp32 blocks in HBM
         out["fused_over_unfused"] = round(detail["l1_unfused"]["ms"] / detail["l1"]["ms"], 4)

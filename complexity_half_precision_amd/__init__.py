@@ -255,14 +255,18 @@ def lcma_gemm(plan: Plan, A, B, C, workspace=None, workspace_bytes=None, stream=
                      ldc or _ld(C, plan.N), _ptr(workspace), ws_bytes, _stream(stream)), "lcma_gemm")
 
 
+def _ws_bytes(workspace):
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
 def lcma_prepass(plan: Plan, A, B, workspace, stream=None, lda=None, ldb=None) -> None:
-    ws_bytes = workspace.numel() * workspace.element_size()
+    ws_bytes = _ws_bytes(workspace)
     _check(_lib_prepass(plan.handle, _ptr(A), lda or _ld(A, plan.K), _ptr(B), ldb or _ld(B, plan.N),
                         _ptr(workspace), ws_bytes, _stream(stream)), "lcma_prepass")
 
 
 def lcma_fused(plan: Plan, A, B, C, workspace, stream=None, lda=None, ldb=None, ldc=None) -> None:
-    ws_bytes = workspace.numel() * workspace.element_size()
+    ws_bytes = _ws_bytes(workspace)
     _check(_lib_fused(plan.handle, _ptr(A), lda or _ld(A, plan.K), _ptr(B), ldb or _ld(B, plan.N), _ptr(C),
                       ldc or _ld(C, plan.N), _ptr(workspace), ws_bytes, _stream(stream)), "lcma_fused")
 

@@ -167,7 +167,7 @@ lcma_status hip_status(hipError_t e, const char* what)
 
 struct Machine {
     double peak, bw, l2bw, launch;
-    double eta_mfma, eta_fused1, eta_fused2, eta_bw;
+    double eta_mfma, eta_fused1, eta_fused2, eta_cal, eta_bw;
     int P;
 };
 
@@ -284,7 +284,7 @@ Geo sched_geo(const Geo& g, bool outer)
 }
 
 double est_lcma(int64_t M, int64_t N, int64_t K, int levels, int split_req, bool write_all, bool outer,
-                const Machine& m)
+                const Machine& m, bool at_load = false)
 {
     const double s = 2.0;
     const Geo g = lcma_geo(M, N, K, levels);
@@ -294,10 +294,19 @@ double est_lcma(int64_t M, int64_t N, int64_t K, int levels, int split_req, bool
     // pre-pass: read A and B once, write the combined operands
     const double Bpre = s * ((double)M * K + (double)K * N) +
                         s * (nA * (double)g.Mb * g.Kb + nB * (double)g.Kb * g.Nb);
-    const double t_pre = Bpre / (m.eta_bw * m.bw) + m.launch;
-    // fused: R products of Mb x Nb x Kb
+    const double t_pre = at_load ? 0.0 : Bpre / (m.eta_bw * m.bw) + m.launch;
+    // fused: R products of Mb x Nb x Kb; combining at load reads every
+    // nonzero block of U and V instead of one operand per product
     const double F = 2.0 * g.R * (double)g.Mb * g.Nb * g.Kb;
-    double Bf = s * g.R * ((double)g.Mb * g.Kb + (double)g.Kb * g.Nb) + s * (double)M * N;
+    double rdA = g.R, rdB = g.R;
+    if (at_load) {
+        rdA = rdB = 0;
+        for (int x = 0; x < 7 * 4; ++x) {
+            rdA += g_U1[x] != 0;
+            rdB += g_V1[x] != 0;
+        }
+    }
+    double Bf = s * (rdA * (double)g.Mb * g.Kb + rdB * (double)g.Kb * g.Nb) + s * (double)M * N;
     const bool out2 = levels == 2 && outer;
     // Outer level in memory: per element of the four M/2 x N/2 outer
     // outputs, 4 bytes stored by the first contributor, 8 read and written by
@@ -313,7 +322,7 @@ double est_lcma(int64_t M, int64_t N, int64_t K, int levels, int split_req, bool
     } else {
         q = quant(sg.G, m.P);
     }
-    const double eta = (levels == 1 || out2) ? m.eta_fused1 : m.eta_fused2;
+    const double eta = at_load ? m.eta_cal : (levels == 1 || out2) ? m.eta_fused1 : m.eta_fused2;
     const double t_f = kernel_time(F, Bf, sg.tile / 2.0, q, eta, m) + (out2 ? 6 * m.launch : 0.0);
     return t_pre + t_f;
 }
@@ -338,6 +347,7 @@ struct lcma_plan_s {
     int n_slots;
     int64_t offA, offB, offPart, offCtr;
     int outer;             // two levels: inner level fused, outer level accumulated in fp32 memory
+    int at_load;           // one level: the group kernel combines the input blocks itself (no pre-pass)
     int8_t order1[7];      // outer level: order of the 7 launches (outer products)
     int64_t offAcc;        // outer level: fp32 output blocks
     int64_t slotA[kMaxRank], slotB[kMaxRank];   // index among written operands, -1 = in place
@@ -472,8 +482,12 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     }
     const bool generic = desc && builtin_kind(desc) == 0;
     const bool unfused = generic || o.combine == LCMA_COMBINE_UNFUSED;
-    if (o.combine == LCMA_COMBINE_AT_LOAD)
-        return LCMA_E_UNSUPPORTED;   // not built yet
+    // Combining at load: one level of the built-in scheme, operands of the
+    // storage type, no split (nothing would clear the fix-up counters).
+    const bool at_load = o.combine == LCMA_COMBINE_AT_LOAD;
+    if (at_load && (generic || force == LCMA_ALGO_L2 || o.split == LCMA_SPLIT_ALL ||
+                    (dt == LCMA_BF16 && o.bf16_ops_f16 == 1)))
+        return LCMA_E_UNSUPPORTED;
     // Two levels: the outer level goes through memory unless all 49 products
     // are to accumulate on chip.
     const bool outer2 = o.combine != LCMA_COMBINE_L2_ON_CHIP;
@@ -493,6 +507,7 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     m.eta_mfma = o.classic_eff > 0 ? o.classic_eff : 0.52;
     m.eta_fused1 = o.fused_eff > 0 ? o.fused_eff : 0.31;
     m.eta_fused2 = o.fused_eff > 0 ? o.fused_eff : 0.037;
+    m.eta_cal = o.fused_eff > 0 ? o.fused_eff : 0.2;
     m.eta_bw = 0.8;
     if (o.num_cus > 0) {
         m.P = o.num_cus;
@@ -531,7 +546,7 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     double est[4] = {-1, -1, -1, -1};
     est[LCMA_ALGO_CLASSIC] = est_classic(M, N, K, m);
     bool ok1 = allow_l1 && (unfused ? admissible_unfused() : admissible(1));
-    bool ok2 = allow_l2 && !unfused && admissible(2);
+    bool ok2 = allow_l2 && !unfused && !at_load && admissible(2);
     if (ok1 && unfused) {
         // pre-pass (every operand written), one GEMM per product, fp32
         // read-modify-write of the touched output blocks, final cast
@@ -545,6 +560,8 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         // 4 read by the last (which writes 2 bytes of C): 8c - 6
         const double comb = (8.0 * nnzW - 6.0 * gen.ms * gen.ns) * (double)Mb * Nb;
         est[LCMA_ALGO_L1] = (pre + comb) / (m.eta_bw * m.bw) + gen.rank * est_classic(Mb, Nb, Kb, m) + 2 * m.launch;
+    } else if (ok1 && at_load) {
+        est[LCMA_ALGO_L1] = est_lcma(M, N, K, 1, LCMA_SPLIT_NONE, false, false, m, true);
     } else if (ok1) {
         est[LCMA_ALGO_L1] = est_lcma(M, N, K, 1, o.split, op_bf16_for(1) != (dt == LCMA_BF16), false, m);
     }
@@ -684,12 +701,13 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         p->op_bf16 = op_bf16_for(L);
         p->write_all = p->op_bf16 != (dt == LCMA_BF16 ? 1 : 0);
         p->outer = L == 2 && outer2;
+        p->at_load = L == 1 && at_load;
         p->geo = lcma_geo(M, N, K, L);
         const Geo& g = p->geo;
         const Geo sg = sched_geo(g, p->outer);
         SchedParams& sp = p->sp;
         sp.G = sg.G; sp.gy = sg.gy; sp.gx = sg.gx; sp.R = sg.R; sp.P = m.P;
-        sp.mode = split_mode_for(o.split, sg.G, m.P);
+        sp.mode = p->at_load ? kSplitNone : split_mode_for(o.split, sg.G, m.P);
         sp.h = (sg.R + 1) / 2;
         sp.raster = o.order == LCMA_ORDER_PLAIN ? 0 : 8;
         if (sp.mode == kSplitTail) {
@@ -718,8 +736,8 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
             // Same rule as the pre-pass kernel: a single-block operand is read
             // in place (the built-in schemes give it coefficient +1).
             (void)ca; (void)cb;
-            const bool wa = p->write_all || na > 1;
-            const bool wb = p->write_all || nb > 1;
+            const bool wa = !p->at_load && (p->write_all || na > 1);
+            const bool wb = !p->at_load && (p->write_all || nb > 1);
             p->slotA[r] = wa ? nA++ : -1;
             p->slotB[r] = wb ? nB++ : -1;
             p->blockA[r] = ba;
@@ -780,6 +798,8 @@ lcma_status lcma_plan_operand(lcma_plan_t p, int32_t side, int32_t r, int64_t* o
 {
     if (!p || p->levels == 0 || side < 0 || side > 1 || r < 0 || r >= p->geo.R)
         return LCMA_E_INVALID;
+    if (p->at_load)
+        return LCMA_E_INVALID;   // no combined operand is ever written
     if (p->inner) {
         const lcma_status s = lcma_plan_operand(p->inner, side, r, offset, ld, dtype);
         if (s == LCMA_OK && offset && *offset >= 0)
@@ -975,6 +995,37 @@ lcma_status do_fused(const lcma_plan_s* p, const void* A, int64_t lda, const voi
     L.op_bf16 = p->op_bf16;
     L.out_bf16 = p->dt == LCMA_BF16;
     L.grid = p->grid;
+    if (p->at_load) {
+        // Each operand is one or two input blocks (block order), read in
+        // place with the inputs' leading dimensions; a coefficient of -1
+        // becomes a sign mask on the loaded halves.
+        L.at_load = 1;
+        for (int r = 0; r < 7; ++r) {
+            int na = 0, nb = 0;
+            for (int x = 0; x < 4; ++x) {
+                const int bi = x / 2, bk = x % 2;
+                if (g_U1[r * 4 + x]) {
+                    const uint16_t* ptr = (const uint16_t*)A + bi * g.Mb * lda + bk * g.Kb;
+                    (na == 0 ? L.p.a[r] : L.p.a2[r]) = ptr;
+                    L.p.sa[r][na++] = g_U1[r * 4 + x] < 0 ? 0x80008000u : 0u;
+                }
+                const int kb = x / 2, bj = x % 2;
+                if (g_V1[r * 4 + x]) {
+                    const uint16_t* ptr = (const uint16_t*)B + kb * g.Kb * ldb + bj * g.Nb;
+                    (nb == 0 ? L.p.b[r] : L.p.b2[r]) = ptr;
+                    L.p.sb[r][nb++] = g_V1[r * 4 + x] < 0 ? 0x80008000u : 0u;
+                }
+            }
+            if (na < 1 || na > 2 || nb < 1 || nb > 2)
+                return LCMA_E_UNSUPPORTED;   // not a Strassen-shaped row
+            L.p.lda[r] = lda;
+            L.p.ldb[r] = ldb;
+            L.p.order[r] = p->order[r];
+            for (int o = 0; o < 4; ++o)
+                L.p.w[r][o] = g_W1[r * 4 + o];
+        }
+        return hip_status(launch_fused(L, st), "launch_fused (combine at load)");
+    }
     if (!p->outer) {
         const int8_t* W = p->levels == 1 ? g_W1 : g_W2;
         for (int r = 0; r < g.R; ++r) {
@@ -1263,9 +1314,11 @@ lcma_status lcma_gemm(lcma_plan_t p, const void* A, int64_t lda, const void* B, 
         s = do_gen_prepass(p, A, lda, B, ldb, ws, st);
         return s != LCMA_OK ? s : do_gen_products(p, C, ldc, ws, st);
     }
-    s = do_prepass(p, A, lda, B, ldb, ws, st);
-    if (s != LCMA_OK)
-        return s;
+    if (!p->at_load) {
+        s = do_prepass(p, A, lda, B, ldb, ws, st);
+        if (s != LCMA_OK)
+            return s;
+    }
     return do_fused(p, A, lda, B, ldb, C, ldc, io, ws, st);
 }
 
@@ -1289,6 +1342,8 @@ lcma_status lcma_prepass(lcma_plan_t p, const void* A, int64_t lda, const void* 
         return s;
     if (p->unfused)
         return do_gen_prepass(p, A, lda, B, ldb, ws, (hipStream_t)stream);
+    if (p->at_load)
+        return LCMA_OK;   // the group kernel combines the blocks itself
     return do_prepass(p, A, lda, B, ldb, ws, (hipStream_t)stream);
 }
 

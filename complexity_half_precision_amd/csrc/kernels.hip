@@ -226,17 +226,27 @@ __device__ __forceinline__ u32x4 load_row8(const rsrc_t& r, int ld, int row, int
     }
 }
 
+// The A chunks of one k-tile: `a` is the tile's first row (column 0).
 template <class C, bool VEC>
-__device__ __forceinline__ void load_tile(Regs<C>& R, const Src& s, int k0, int tid)
+__device__ __forceinline__ void load_a(u32x4 (&ra8)[C::A_CH], const u16* a, int lda, int a_rows, int k0, int K,
+                                       int tid)
 {
-    const rsrc_t ra = make_rsrc(s.a + k0);
-    const rsrc_t rb = make_rsrc(s.b + (int64_t)k0 * s.ldb);
-    const int kleft = s.K - k0;
+    const rsrc_t ra = make_rsrc(a + k0);
+    const int kleft = K - k0;
 #pragma unroll
     for (int i = 0; i < C::A_CH; ++i) {
         const int c = tid + i * C::NT;
-        R.a[i] = load_row8<VEC>(ra, s.lda, c >> 3, (c & 7) * 8, s.a_rows, kleft);
+        ra8[i] = load_row8<VEC>(ra, lda, c >> 3, (c & 7) * 8, a_rows, kleft);
     }
+}
+
+// The B blocks of one k-tile: `b` is the tile's first column (row 0).
+template <class C, bool VEC>
+__device__ __forceinline__ void load_b(u32x4 (&rb8)[C::B_PER][C::BKB], const u16* b, int ldb, int b_cols, int k0,
+                                       int K, int tid)
+{
+    const rsrc_t rb = make_rsrc(b + (int64_t)k0 * ldb);
+    const int kleft = K - k0;
 #pragma unroll
     for (int i = 0; i < C::B_PER; ++i) {
         const int blk = tid + i * C::NT;
@@ -244,9 +254,16 @@ __device__ __forceinline__ void load_tile(Regs<C>& R, const Src& s, int k0, int 
             const int kb = blk % (C::BK / C::BKB), n = (blk / (C::BK / C::BKB)) * 8;
 #pragma unroll
             for (int r = 0; r < C::BKB; ++r)
-                R.b[i][r] = load_row8<VEC>(rb, s.ldb, kb * C::BKB + r, n, kleft, s.b_cols);
+                rb8[i][r] = load_row8<VEC>(rb, ldb, kb * C::BKB + r, n, kleft, b_cols);
         }
     }
+}
+
+template <class C, bool VEC>
+__device__ __forceinline__ void load_tile(Regs<C>& R, const Src& s, int k0, int tid)
+{
+    load_a<C, VEC>(R.a, s.a, s.lda, s.a_rows, k0, s.K, tid);
+    load_b<C, VEC>(R.b, s.b, s.ldb, s.b_cols, k0, s.K, tid);
 }
 
 // Registers -> LDS stage.  A chunks go straight to their swizzled slot.  Each
@@ -2227,6 +2244,155 @@ __global__ void __launch_bounds__(FusedCfg<LEVELS>::C::NT) k_fused(const FusedPa
     }
 }
 
+// ------------------------------------------------------------------ combine at load
+//
+// One-level group kernel that forms the combined operands while it stages
+// k-tiles, so no pre-pass runs and no combined operand reaches memory
+// ("FalconGEMM ...", section "从 LCMA 到 FalconGEMM", combine A/B; here moved
+// into the tile loads).  Each operand of a one-level product is one or two
+// input blocks with coefficients +-1: the 8-element chunks of both blocks are
+// loaded, the second is added after the sign flips, and the sum is rounded
+// once to the operand type.  Adding two bfloat16 values goes through fp32
+// (4 unpacks, 2 adds, one packed RNE conversion per 32-bit word);
+// two binary16 values add with one packed instruction, whose single
+// rounding of the exact sum equals rounding their fp32 sum (the fp32 sum of
+// two binary16 values is inexact only when the smaller is below a quarter
+// unit of the larger's last binary16 place, and then both give the larger).
+// Register-staged engine: 4 waves of 64 x 64 on a 128 x 128 group tile, so
+// the combination is done once per workgroup, not once per wave.
+using CfgCal = Cfg<128, 128, 2, 4, 32, 2>;
+
+template <bool BF>
+__device__ __forceinline__ u32 add_h2(u32 x, u32 y)
+{
+    if constexpr (BF) {
+        using v2 = __bf16 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(u32, __builtin_bit_cast(v2, x) + __builtin_bit_cast(v2, y));
+    } else {
+        using v2 = _Float16 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(u32, __builtin_bit_cast(v2, x) + __builtin_bit_cast(v2, y));
+    }
+}
+
+// Terms of the tile held in registers: sign masks and which sides have a
+// second block (loaded into the second register set).
+struct CalTerms {
+    u32 sa1, sa2, sb1, sb2;
+    bool a2, b2;
+};
+
+template <class C, bool BF>
+__device__ __forceinline__ void combine_regs(Regs<C>& R, const Regs<C>& R2, const CalTerms& t)
+{
+#pragma unroll
+    for (int i = 0; i < C::A_CH; ++i)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const u32 x = R.a[i][d] ^ t.sa1;
+            R.a[i][d] = t.a2 ? add_h2<BF>(x, R2.a[i][d] ^ t.sa2) : x;
+        }
+#pragma unroll
+    for (int i = 0; i < C::B_PER; ++i)
+#pragma unroll
+        for (int r = 0; r < C::BKB; ++r)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const u32 x = R.b[i][r][d] ^ t.sb1;
+                R.b[i][r][d] = t.b2 ? add_h2<BF>(x, R2.b[i][r][d] ^ t.sb2) : x;
+            }
+}
+
+// ktile with the staged registers combined right before they are written to
+// the next stage (their loads have had the whole k-tile to land).
+template <class C, bool BF, bool MORE>
+__device__ __forceinline__ void ktile_cal(const char* cur, char* nxt, Regs<C>& R, const Regs<C>& R2,
+                                          const CalTerms& tm, typename C::acc_t (&acc)[C::FM][C::FN], int wm,
+                                          int wn, int lane, int tid)
+{
+    constexpr int KSTEPS = C::BK / Mma<C::MT>::KSTEP;
+    u32x4 af[2][C::FM], bf[2][C::FN];
+    read_frags<C>(cur, 0, af[0], bf[0], wm, wn, lane);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+        if (s + 1 < KSTEPS)
+            read_frags<C>(cur, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1], wm, wn, lane);
+        if (MORE && s == KSTEPS - 1) {
+            combine_regs<C, BF>(R, R2, tm);
+            store_tile<C>(nxt, R, tid);
+        }
+        mma_step<C, BF>(af[s & 1], bf[s & 1], acc);
+    }
+}
+
+template <bool BF>
+__global__ void __launch_bounds__(CfgCal::NT) k_fused_cal(const FusedParams fp)
+{
+    using C = CfgCal;
+    constexpr int NOUT = 4;
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    __shared__ int sh_old;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int w = blockIdx.x;
+    const int n_items = sched_count(fp.sp, w);
+    const int nk = (fp.Kb + C::BK - 1) / C::BK;
+
+    for (int it = 0; it < n_items; ++it) {
+        const Item item = sched_item(fp.sp, w, it);
+        int p, q;
+        tile_coords(item.g, fp.sp.gy, fp.sp.gx, fp.sp.P, fp.sp.raster, &p, &q);
+        const int m0 = p * C::BM, n0 = q * C::BN;
+        const int a_rows = fp.Mb - m0, b_cols = fp.Nb - n0;
+
+        typename C::acc_t Cacc[NOUT][C::FM][C::FN];
+#pragma unroll
+        for (int o = 0; o < NOUT; ++o)
+            zero_acc<C>(Cacc[o]);
+        typename C::acc_t H[C::FM][C::FN];
+        zero_acc<C>(H);
+
+        // Loads k-tile k0 of the product at position pos into R (first
+        // blocks) and R2 (second blocks) and returns its terms.
+        Regs<C> R, R2;
+        auto load = [&](int pos, int k0) {
+            const int r = fp.order[pos];
+            const int64_t lda = fp.lda[r], ldb = fp.ldb[r];
+            CalTerms t{fp.sa[r][0], fp.sa[r][1], fp.sb[r][0], fp.sb[r][1], fp.a2[r] != nullptr,
+                       fp.b2[r] != nullptr};
+            load_a<C, true>(R.a, fp.a[r] + m0 * lda, (int)lda, a_rows, k0, fp.Kb, tid);
+            load_b<C, true>(R.b, fp.b[r] + n0, (int)ldb, b_cols, k0, fp.Kb, tid);
+            if (t.a2)
+                load_a<C, true>(R2.a, fp.a2[r] + m0 * lda, (int)lda, a_rows, k0, fp.Kb, tid);
+            if (t.b2)
+                load_b<C, true>(R2.b, fp.b2[r] + n0, (int)ldb, b_cols, k0, fp.Kb, tid);
+            return t;
+        };
+        const int ntiles = (item.pos1 - item.pos0) * nk;
+        CalTerms tm = load(item.pos0, 0);
+        combine_regs<C, BF>(R, R2, tm);
+        store_tile<C>(smem, R, tid);
+        __syncthreads();
+        for (int t = 0; t < ntiles; ++t) {
+            const int t1 = t + 1;
+            const char* cur = smem + (t & 1) * C::STAGE;
+            if (t1 < ntiles) {
+                tm = load(item.pos0 + t1 / nk, (t1 % nk) * C::BK);
+                ktile_cal<C, BF, true>(cur, smem + (t1 & 1) * C::STAGE, R, R2, tm, H, wm, wn, lane, tid);
+            } else {
+                ktile_cal<C, BF, false>(cur, nullptr, R, R2, tm, H, wm, wn, lane, tid);
+            }
+            if (t % nk == nk - 1) {
+                combine_h<NOUT, C>(fp.w[fp.order[item.pos0 + t / nk]], H, Cacc);
+                zero_acc<C>(H);
+            }
+            __syncthreads();
+        }
+
+        fused_epilogue<NOUT, C, BF>(fp, item, m0, n0, Cacc, tid, wm, wn, lane, &sh_old);
+        __syncthreads();
+    }
+}
+
 // One-level fused group kernel on the ping-pong engine (8 waves, 128 x 128
 // group tile, 64 x 32 per wave): the product tiles of an item run back to
 // back through the DMA ring; after each product's last k-tile every wave folds
@@ -2435,6 +2601,9 @@ hipError_t launch_prepass(const PrepassLaunch& L, hipStream_t st)
 
 int32_t fused_tile(int32_t levels) { return levels == 1 ? MCF1::BM : FusedCfg<2>::C::BM; }
 static_assert(MCF1::BM == MCF1::BN, "fused tiles are square");
+static_assert(CfgCal::BM == MCF1::BM && CfgCal::BN == MCF1::BN,
+              "the combine-at-load kernel shares the one-level group geometry");
+static_assert(sizeof(FusedParams) <= 4096, "kernel arguments");
 static_assert(FusedCfg<2>::C::BM == FusedCfg<2>::C::BN,
               "fused tiles are square");
 
@@ -2463,6 +2632,17 @@ void fused_order(int32_t levels, int8_t* order)
 
 hipError_t launch_fused(const FusedLaunch& L, hipStream_t st)
 {
+    if (L.at_load) {
+        if (L.levels != 1 || L.outer || L.op_bf16 != L.out_bf16)
+            return hipErrorInvalidValue;
+        if (L.grid <= 0)
+            return hipSuccess;
+        if (L.out_bf16)
+            hipLaunchKernelGGL((k_fused_cal<true>), dim3(L.grid), dim3(CfgCal::NT), 0, st, L.p);
+        else
+            hipLaunchKernelGGL((k_fused_cal<false>), dim3(L.grid), dim3(CfgCal::NT), 0, st, L.p);
+        return hipGetLastError();
+    }
     if (L.levels == 1 || L.outer) {
         if (L.out_bf16)
             return L.op_bf16 ? launch_fused1_m16<true, true>(L, st) : launch_fused1_m16<false, true>(L, st);

@@ -72,6 +72,14 @@ struct FusedParams {
     float* acc;                    // fp32 output blocks, 16 of Mb x Nb, block-major (block 4 bi + bj)
     int8_t omode[4];               // OuterMode per outer output (i1, j1), row-major
     float ow[4];
+    // Combine at load (one level): a[r] / b[r] are product r's first input
+    // block, a2[r] / b2[r] its second (null for a single block, same leading
+    // dimension), and sa[r] / sb[r] the sign masks of the two terms
+    // (0x80008000 negates both halves of a 32-bit word, 0 keeps them).
+    const uint16_t* a2[7];
+    const uint16_t* b2[7];
+    uint32_t sa[7][2];
+    uint32_t sb[7][2];
 };
 
 // What one outer product does to an outer output's fp32 blocks: the first
@@ -85,6 +93,7 @@ struct FusedLaunch {
     int32_t op_bf16, out_bf16;
     int32_t grid;
     int32_t outer;                 // levels == 2: 1 = one launch of the outer level (one-level kernel + acc)
+    int32_t at_load;               // levels == 1: combine the input blocks while staging tiles (no pre-pass)
 };
 // Workgroup tile edge of the fused kernel for a level (1: 128, 2: 64).
 // ---- unfused path for any valid description (one level of it)

@@ -101,8 +101,15 @@ typedef enum {
                                  level (their 4 outputs accumulate on chip), one launch per outer product,
                                  and each launch folds W1[r1][i1,j1] * (its inner outputs) into fp32 output
                                  blocks in the workspace; the last contributor to an output rounds it into C */
-    LCMA_COMBINE_AT_LOAD = 2, /* the fused kernel would form the combinations while staging tiles (one level).
-                                 Not built: lcma_plan_ex returns LCMA_E_UNSUPPORTED */
+    LCMA_COMBINE_AT_LOAD = 2, /* one level of the built-in scheme: no pre-pass; the group kernel loads the one
+                                 or two input blocks of each operand, adds them in fp32 (binary16: one packed
+                                 add, the same single rounding) and rounds once to the operand type while
+                                 staging each k-tile, so no combined operand is written and the workspace is
+                                 empty.  Runs on the register-staged four-wave engine.  Operands keep the
+                                 storage type and groups are never split: with LCMA_ALGO_L2, a generic
+                                 description, LCMA_SPLIT_ALL or bf16_ops_f16 = 1 on bfloat16 inputs,
+                                 lcma_plan_ex returns LCMA_E_UNSUPPORTED.  lcma_prepass does nothing and
+                                 lcma_fused runs the whole product; lcma_plan_operand is LCMA_E_INVALID */
     LCMA_COMBINE_UNFUSED = 3, /* one level only: every combined operand is written; each product's epilogue adds
                                  W[r][i,j] * H_r into fp32 output blocks in the workspace (H_r is never stored)
                                  and the last contributor to a block rounds it into C.  Blocks with enough
@@ -150,7 +157,8 @@ typedef struct {
                                0 = 0.52 (measured on MI355X at 4096^3 .. 16384^3) */
     double fused_eff;       /* the same for the fused group kernel (both levels);
                                0 = 0.31 for one level and for two levels with the outer level in
-                               memory, 0.037 for LCMA_COMBINE_L2_ON_CHIP (measured) */
+                               memory, 0.037 for LCMA_COMBINE_L2_ON_CHIP (measured), 0.2 for
+                               LCMA_COMBINE_AT_LOAD */
     lcma_order order;       /* persistent fused kernel's work order (LCMA_ORDER_AUTO by default) */
 } lcma_options;
 
@@ -241,7 +249,8 @@ lcma_status lcma_fused(lcma_plan_t plan, const void* A, int64_t lda, const void*
  * leading dimension; *offset_bytes = -1 when the operand is a single input
  * block read in place (not copied).  *dtype receives the operand type.
  * A padded plan reports the operands of its padded product (blocks of the
- * padded shape). */
+ * padded shape).  LCMA_E_INVALID for a plan that combines at load (it
+ * writes no combined operand). */
 lcma_status lcma_plan_operand(lcma_plan_t plan, int32_t side, int32_t r, int64_t* offset_bytes,
                               int64_t* ld, lcma_dtype* dtype);
 

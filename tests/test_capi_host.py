@@ -476,3 +476,50 @@ def test_invalid_calls_fail_before_touching_the_device():
     pc = L.lcma_plan_ex(512, 512, 512, "f16", force="classic", num_cus=CUS)
     assert L._lib_prepass(pc.handle, 4096, 512, 4096, 512, 1 << 20, 0, None) == L.E_INVALID
     assert L._lib_plan_operand(pc.handle, 0, 0, None, None, None) == L.E_INVALID
+
+
+# ---------------------------------------------------------------- combine at load
+
+def test_combine_at_load_plans_one_level_without_a_workspace():
+    p = L.lcma_plan_ex(1024, 1024, 1024, "bf16", force="l1", combine="at_load", num_cus=CUS)
+    chosen, ws, est = L.lcma_plan_info(p)
+    assert chosen == "l1" and ws == 0 and est > 0
+    # no combined operand is ever written
+    with pytest.raises(L.LcmaError) as e:
+        L.lcma_plan_operand(p, 0, 0)
+    assert e.value.status == L.E_INVALID
+    # whole groups only, each on one worker, every group once
+    items, order = L.lcma_plan_schedule(p)
+    assert all(it[4] == -1 and (it[2], it[3]) == (0, 7) for it in items)
+    assert sorted(it[1] for it in items) == list(range(len(items)))
+    assert sorted(order[:7]) == list(range(7))
+    # the same in binary16, and a forced padded shape wraps it like any L1 plan
+    p = L.lcma_plan_ex(512, 512, 512, "f16", force="l1", combine="at_load", num_cus=CUS)
+    assert L.lcma_plan_info(p)[:2] == ("l1", 0)
+    p = L.lcma_plan_ex(500, 520, 260, "f16", force="l1", combine="at_load", num_cus=CUS)
+    assert L.lcma_plan_info(p)[0] == "l1"
+    with pytest.raises(L.LcmaError):
+        L.lcma_plan_operand(p, 0, 0)
+
+
+def test_combine_at_load_rejects_what_it_does_not_build():
+    for kw in (dict(force="l2"), dict(force="l1", split="all"), dict(force="l1", bf16_ops_f16=1)):
+        with pytest.raises(L.LcmaError) as e:
+            L.lcma_plan_ex(1024, 1024, 1024, "bf16", combine="at_load", num_cus=CUS, **kw)
+        assert e.value.status == L.E_UNSUPPORTED, kw
+    d = oracle.naive(2, 2, 2)
+    with pytest.raises(L.LcmaError) as e:
+        L.lcma_plan_ex(512, 512, 512, "f16", desc=L.Desc(2, 2, 2, d.U, d.V, d.W), force="l1", combine="at_load",
+                       num_cus=CUS)
+    assert e.value.status == L.E_UNSUPPORTED
+    # binary16 inputs have binary16 operands either way
+    p = L.lcma_plan_ex(512, 512, 512, "f16", force="l1", combine="at_load", bf16_ops_f16=1, num_cus=CUS)
+    assert L.lcma_plan_info(p)[0] == "l1"
+
+
+def test_combine_at_load_estimate_has_no_prepass():
+    n = 4096
+    pa = L.lcma_plan_ex(n, n, n, "bf16", force="l1", combine="at_load", num_cus=256, fused_eff=0.31)
+    pp = L.lcma_plan_ex(n, n, n, "bf16", force="l1", combine="prepass", num_cus=256, fused_eff=0.31)
+    # same kernel efficiency: dropping the pre-pass can only shorten the estimate
+    assert L.lcma_plan_info(pa)[2] < L.lcma_plan_info(pp)[2]

@@ -534,6 +534,72 @@ def test_l2_f16_and_split_all():
     assert np.array_equal(si.bits(C1), si.bits(planned(A, B, "l2", split="all")))
 
 
+# ---------------------------------------------------------------- combine at load
+
+def test_at_load_integer_inputs_are_exact():
+    say("at_load exact")
+    A, B, A64, B64 = gen(**si.SQUARE_512_F16_INT)
+    check_exact(planned(A, B, "l1", combine="at_load"), A64, B64, "f16")
+    A, B, A64, B64 = gen(256, 512, 384, "bf16", "int1", seed=2)
+    check_exact(planned(A, B, "l1", combine="at_load"), A64, B64, "bf16")
+
+
+# 512^3 and 1024^3: whole group tiles; 400 x 272 x 144 and 600 x 528 x 512:
+# ragged group tiles (blocks of 200 x 136 x 72 and 300 x 264 x 256);
+# 500 x 520 x 260: padded to 512 x 544 x 288
+@pytest.mark.parametrize("M,N,K,dtype,dist", [(512, 512, 512, "f16", "uniform"),
+                                              (1024, 1024, 1024, "bf16", "normal_sqrtk"),
+                                              (400, 272, 144, "f16", "uniform"),
+                                              (600, 528, 512, "bf16", "normal_sqrtk"),
+                                              (500, 520, 260, "f16", "uniform")])
+def test_at_load_matches_oracle(M, N, K, dtype, dist):
+    say("at_load", M, N, K, dtype)
+    A, B, A64, B64 = gen(M, N, K, dtype, dist, seed=21)
+    C_ref = oracle.gemm(A64, B64)
+    e_c = check_float(classic(A, B), A64, B64, dtype, C_ref)
+    C = planned(A, B, "l1", combine="at_load")
+    e = check_float(C, A64, B64, dtype, C_ref, blocks=2)
+    assert e <= 4 * e_c, (e, e_c)
+    if (M, N, K) != (500, 520, 260):
+        # against the oracle's evaluation with each combined operand rounded
+        # once to the operand type: only the fp32 accumulation order and the
+        # final rounding differ
+        C_sh, n = oracle.lcma(A64, B64, oracle.strassen(), 1, round_operands=dtype)
+        assert n == 7
+        assert metrics.e_rel(si.f64(C), C_sh) <= 2 * metrics.UNIT_ROUNDOFF[dtype]
+
+
+def test_at_load_halves_strides_and_repeats():
+    say("at_load halves")
+    M, N, K = 768, 640, 1024
+    A, B, A64, B64 = gen(M, N, K, "bf16", "normal_sqrtk", seed=23)
+    plan = L.lcma_plan_ex(M, N, K, "bf16", force="l1", combine="at_load")
+    assert L.lcma_plan_info(plan)[:2] == ("l1", 0)
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    C0 = torch.empty((M, N), dtype=A.dtype, device=DEV)
+    L.lcma_gemm(plan, Ad, Bd, C0, None)
+    # the two halves: the pre-pass half has nothing to do
+    C1 = torch.full((M, N), 3.0, dtype=A.dtype, device=DEV)
+    L.lcma_prepass(plan, Ad, Bd, None)
+    L.lcma_fused(plan, Ad, Bd, C1, None)
+    # strided operands and output
+    As = torch.zeros((M, K + 24), dtype=A.dtype, device=DEV)
+    Bs = torch.zeros((K, N + 40), dtype=A.dtype, device=DEV)
+    Cs = torch.full((M, N + 8), 7.0, dtype=A.dtype, device=DEV)
+    As[:, :K] = Ad
+    Bs[:, :N] = Bd
+    L.lcma_gemm(plan, As, Bs, Cs, None, lda=K + 24, ldb=N + 40, ldc=N + 8)
+    C2 = torch.empty((M, N), dtype=A.dtype, device=DEV)
+    L.lcma_gemm(plan, Ad, Bd, C2, None)
+    torch.cuda.synchronize()
+    ref = si.bits(C0.cpu())
+    assert np.array_equal(si.bits(C1.cpu()), ref)
+    assert np.array_equal(si.bits(Cs[:, :N].cpu()), ref)
+    assert np.all(Cs[:, N:].cpu().float().numpy() == 7.0)
+    assert np.array_equal(si.bits(C2.cpu()), ref)
+    check_float(C0.cpu(), A64, B64, "bf16", blocks=2)
+
+
 # ---------------------------------------------------------------- full-size workloads
 
 def test_square_4096_bf16_classic_and_one_level():
@@ -546,6 +612,11 @@ def test_square_4096_bf16_classic_and_one_level():
         e_1 = check_float(C1, A64, B64, "bf16", C_ref, blocks=2)
         assert e_1 <= 4 * e_c, (ops, e_1, e_c)
         assert metrics.freivalds(si.f64(C1), A64, B64) <= 4 * metrics.UNIT_ROUNDOFF["bf16"]
+    # the same product with the combination done while staging tiles
+    C1 = planned(A, B, "l1", combine="at_load")
+    e_1 = check_float(C1, A64, B64, "bf16", C_ref, blocks=2)
+    assert e_1 <= 4 * e_c, ("at_load", e_1, e_c)
+    assert metrics.freivalds(si.f64(C1), A64, B64) <= 4 * metrics.UNIT_ROUNDOFF["bf16"]
 
 
 @pytest.mark.parametrize("m", si.DECODE_MS)
