@@ -503,11 +503,11 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     // the kernels as they stand: classic 256x256 tiles 0.50-0.55 over
     // 4096^3..16384^3; fused one-level group kernel about 0.31 (also the
     // inner level of the default two-level path); the on-chip two-level
-    // kernel about 0.037.
+    // kernel about 0.037; the combine-at-load group kernel about 0.13.
     m.eta_mfma = o.classic_eff > 0 ? o.classic_eff : 0.52;
     m.eta_fused1 = o.fused_eff > 0 ? o.fused_eff : 0.31;
     m.eta_fused2 = o.fused_eff > 0 ? o.fused_eff : 0.037;
-    m.eta_cal = o.fused_eff > 0 ? o.fused_eff : 0.2;
+    m.eta_cal = o.fused_eff > 0 ? o.fused_eff : 0.13;
     m.eta_bw = 0.8;
     if (o.num_cus > 0) {
         m.P = o.num_cus;

@@ -19,6 +19,9 @@
 //                    (7 inner products on M/4 x N/4 blocks, fused the same
 //                    way) and folds the 4 inner outputs into fp32 output
 //                    blocks in memory, rounding into C at the last touch.
+//  * k_fused_cal_m16 -- the one-level group kernel without a pre-pass: it
+//                    loads both input blocks of every combined operand and
+//                    adds them in LDS while staging each k-tile.
 //  * k_gen_prepass, k_gen_group_m16, k_gen_product -- the unfused
 //                    path for any valid description: a runtime-coefficient
 //                    combination pass, then the products, each folding W * H
@@ -1336,6 +1339,87 @@ __device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, AfterFn 
     }
 }
 
+// K loop of one output tile whose operands are sums of two input tiles
+// (combine at load).  A ring stage holds both terms of a k-tile: the first
+// term's A and B at the usual offsets, the second's one stage size further.
+// Every k-tile moves both terms by direct-to-LDS loads (a term that is
+// absent reads as zero: its bounds are empty), so the wait counts are fixed.
+// Iteration t, after one barrier: the fragment reads of k-tile t (folded in
+// iteration t - 1), comb(t + 1, stage) folding the second terms of k-tile
+// t + 1 into its first terms in place (its loads have landed), the loads of
+// k-tile t + AHEAD into the stage of k-tile t - 1, and the MFMAs of k-tile
+// t.  (Issuing the MFMAs before the fold measured 3-8% slower.)
+template <class C, bool BF, class SrcFn, class CombFn, class AfterFn>
+__device__ __forceinline__ void run_tile_cal(char* smem, int nk, SrcFn src, CombFn comb, AfterFn after, int wave,
+                                             int lane, const Addr<C>& ad, f32x4 (&acc)[C::FM][C::FN])
+{
+    constexpr int ST = 2 * C::STAGE;
+    constexpr int P2 = 2 * C::PER;
+    static_assert(C::AHEAD >= 2 && C::AHEAD <= 4 && C::NSTAGE == C::AHEAD + 1,
+                  "stage reuse (k-tile t + AHEAD goes where k-tile t - 1 was) and wait counts below");
+    static_assert(C::NSTAGE * ST <= 160 * 1024, "LDS budget");
+    static_assert(P2 * (C::AHEAD - 1) < 64, "vmcnt range");
+    auto issue = [&](int t) {
+        tiles::TileSrc s1, s2;
+        src(t, &s1, &s2);
+        char* stage = smem + (t % C::NSTAGE) * ST;
+        q4::dma_tile<C, true>(stage, s1, wave, lane);
+        q4::dma_tile<C, true>(stage + C::STAGE, s2, wave, lane);
+    };
+    if (nk <= 0)
+        return;
+#pragma unroll
+    for (int t = 0; t < C::AHEAD; ++t)
+        if (t < nk)
+            issue(t);
+    // k-tile 0 landed (up to AHEAD - 1 later k-tiles in flight), then folded
+    const int later0 = min(nk - 1, C::AHEAD - 1);
+    if (later0 >= 3)
+        q4::wait_vm<3 * P2>();
+    else if (later0 == 2)
+        q4::wait_vm<2 * P2>();
+    else if (later0 == 1)
+        q4::wait_vm<P2>();
+    else
+        tiles::wait_vm0();
+    tiles::bar();
+    comb(0, smem);
+    tiles::wait_lgkm0();
+    for (int t = 0; t < nk; ++t) {
+        // k-tile t + 1 must have landed: loads issued after it cover
+        // min(nk - 2 - t, AHEAD - 2) k-tiles
+        if (t + 1 < nk) {
+            const int later = min(nk - 2 - t, C::AHEAD - 2);
+            if (later >= 2)
+                q4::wait_vm<2 * P2>();
+            else if (later == 1)
+                q4::wait_vm<P2>();
+            else
+                tiles::wait_vm0();
+        }
+        tiles::bar();
+        char* stage = smem + (t % C::NSTAGE) * ST;
+        u32x4 Af[C::FM], Bf[C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+            read_a<C>(stage, ad, i, Af[i]);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+            read_b<C>(stage, ad, j, Bf[j]);
+        if (t + 1 < nk)
+            comb(t + 1, smem + ((t + 1) % C::NSTAGE) * ST);
+        if (t + C::AHEAD < nk)
+            issue(t + C::AHEAD);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                acc[i][j] = mfma<BF>(Bf[j], Af[i], acc[i][j]);
+        after(t);
+        tiles::wait_lgkm0();
+    }
+}
+
 // Output tile store through LDS (16x16 accumulator layout: lane l of tile
 // (i, j) holds row 16 i + l % 16, columns 16 j + 4 (l / 16) .. + 3).
 template <class C, bool BF>
@@ -2250,17 +2334,16 @@ __global__ void __launch_bounds__(FusedCfg<LEVELS>::C::NT) k_fused(const FusedPa
 // k-tiles, so no pre-pass runs and no combined operand reaches memory
 // ("FalconGEMM ...", section "从 LCMA 到 FalconGEMM", combine A/B; here moved
 // into the tile loads).  Each operand of a one-level product is one or two
-// input blocks with coefficients +-1: the 8-element chunks of both blocks are
-// loaded, the second is added after the sign flips, and the sum is rounded
-// once to the operand type.  Adding two bfloat16 values goes through fp32
-// (4 unpacks, 2 adds, one packed RNE conversion per 32-bit word);
-// two binary16 values add with one packed instruction, whose single
-// rounding of the exact sum equals rounding their fp32 sum (the fp32 sum of
-// two binary16 values is inexact only when the smaller is below a quarter
-// unit of the larger's last binary16 place, and then both give the larger).
-// Register-staged engine: 4 waves of 64 x 64 on a 128 x 128 group tile, so
-// the combination is done once per workgroup, not once per wave.
-using CfgCal = Cfg<128, 128, 2, 4, 32, 2>;
+// input blocks with coefficients +-1.  Both blocks' tiles go global -> LDS
+// by direct-to-LDS loads three k-tiles ahead (128 KiB ring; four ahead, the
+// whole 160 KiB, measured no faster); all threads then fold the second term into the first
+// in LDS, one 16-byte chunk of A and one of B per thread and k-tile, before
+// the fragment reads.  Adding two bfloat16 values goes through fp32 (4
+// unpacks, 2 adds, one packed RNE conversion per 32-bit word); two binary16
+// values add with one packed instruction, whose single rounding of the exact
+// sum equals rounding their fp32 sum (the fp32 sum of two binary16 values
+// is inexact only when the smaller is below a quarter unit of the larger's
+// last binary16 place, and then both give the larger).
 
 template <bool BF>
 __device__ __forceinline__ u32 add_h2(u32 x, u32 y)
@@ -2274,121 +2357,120 @@ __device__ __forceinline__ u32 add_h2(u32 x, u32 y)
     }
 }
 
-// Terms of the tile held in registers: sign masks and which sides have a
-// second block (loaded into the second register set).
-struct CalTerms {
-    u32 sa1, sa2, sb1, sb2;
-    bool a2, b2;
-};
-
-template <class C, bool BF>
-__device__ __forceinline__ void combine_regs(Regs<C>& R, const Regs<C>& R2, const CalTerms& t)
-{
-#pragma unroll
-    for (int i = 0; i < C::A_CH; ++i)
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const u32 x = R.a[i][d] ^ t.sa1;
-            R.a[i][d] = t.a2 ? add_h2<BF>(x, R2.a[i][d] ^ t.sa2) : x;
-        }
-#pragma unroll
-    for (int i = 0; i < C::B_PER; ++i)
-#pragma unroll
-        for (int r = 0; r < C::BKB; ++r)
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const u32 x = R.b[i][r][d] ^ t.sb1;
-                R.b[i][r][d] = t.b2 ? add_h2<BF>(x, R2.b[i][r][d] ^ t.sb2) : x;
-            }
-}
-
-// ktile with the staged registers combined right before they are written to
-// the next stage (their loads have had the whole k-tile to land).
-template <class C, bool BF, bool MORE>
-__device__ __forceinline__ void ktile_cal(const char* cur, char* nxt, Regs<C>& R, const Regs<C>& R2,
-                                          const CalTerms& tm, typename C::acc_t (&acc)[C::FM][C::FN], int wm,
-                                          int wn, int lane, int tid)
-{
-    constexpr int KSTEPS = C::BK / Mma<C::MT>::KSTEP;
-    u32x4 af[2][C::FM], bf[2][C::FN];
-    read_frags<C>(cur, 0, af[0], bf[0], wm, wn, lane);
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-        if (s + 1 < KSTEPS)
-            read_frags<C>(cur, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1], wm, wn, lane);
-        if (MORE && s == KSTEPS - 1) {
-            combine_regs<C, BF>(R, R2, tm);
-            store_tile<C>(nxt, R, tid);
-        }
-        mma_step<C, BF>(af[s & 1], bf[s & 1], acc);
-    }
-}
+// 8 waves of 64 x 32 on the 16x16x32 engine, 128 x 128 group tiles.
+using MCFC = m16::Cfg<128, 128, 2, 4, 3>;
 
 template <bool BF>
-__global__ void __launch_bounds__(CfgCal::NT) k_fused_cal(const FusedParams fp)
+__global__ void __launch_bounds__(MCFC::NT, 1) k_fused_cal_m16(const FusedParams fp)
 {
-    using C = CfgCal;
+    using C = MCFC;
     constexpr int NOUT = 4;
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-    __shared__ int sh_old;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the fix-up word of the epilogue (no split here, so never touched)
+    // reuses the ring after the K loop
+    __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * 2 * C::STAGE];
+    const int tid = threadIdx.x, lane0 = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int w = blockIdx.x;
     const int n_items = sched_count(fp.sp, w);
     const int nk = (fp.Kb + C::BK - 1) / C::BK;
-
+    uint64_t ordw;
+    __builtin_memcpy(&ordw, fp.order, sizeof ordw);
+    auto order_at = [&](int pos) { return (int)(int8_t)(ordw >> (8 * pos)); };
     for (int it = 0; it < n_items; ++it) {
+        // opaque per item: keeps lane-derived addresses from being held in
+        // registers across the whole kernel
+        int lane = lane0;
+        asm volatile("" : "+v"(lane));
         const Item item = sched_item(fp.sp, w, it);
         int p, q;
         tile_coords(item.g, fp.sp.gy, fp.sp.gx, fp.sp.P, fp.sp.raster, &p, &q);
         const int m0 = p * C::BM, n0 = q * C::BN;
-        const int a_rows = fp.Mb - m0, b_cols = fp.Nb - n0;
-
-        typename C::acc_t Cacc[NOUT][C::FM][C::FN];
+        f32x4 Cacc[NOUT][C::FM][C::FN];
 #pragma unroll
         for (int o = 0; o < NOUT; ++o)
             zero_acc<C>(Cacc[o]);
-        typename C::acc_t H[C::FM][C::FN];
+        f32x4 H[C::FM][C::FN];
         zero_acc<C>(H);
-
-        // Loads k-tile k0 of the product at position pos into R (first
-        // blocks) and R2 (second blocks) and returns its terms.
-        Regs<C> R, R2;
-        auto load = [&](int pos, int k0) {
-            const int r = fp.order[pos];
-            const int64_t lda = fp.lda[r], ldb = fp.ldb[r];
-            CalTerms t{fp.sa[r][0], fp.sa[r][1], fp.sb[r][0], fp.sb[r][1], fp.a2[r] != nullptr,
-                       fp.b2[r] != nullptr};
-            load_a<C, true>(R.a, fp.a[r] + m0 * lda, (int)lda, a_rows, k0, fp.Kb, tid);
-            load_b<C, true>(R.b, fp.b[r] + n0, (int)ldb, b_cols, k0, fp.Kb, tid);
-            if (t.a2)
-                load_a<C, true>(R2.a, fp.a2[r] + m0 * lda, (int)lda, a_rows, k0, fp.Kb, tid);
-            if (t.b2)
-                load_b<C, true>(R2.b, fp.b2[r] + n0, (int)ldb, b_cols, k0, fp.Kb, tid);
-            return t;
+        const int nprod = item.pos1 - item.pos0;
+        const int ntiles = nprod * nk;
+        // The engine asks for k-tile sources, folds and finished k-tiles in
+        // increasing order, so each walks a cursor and reads a product's
+        // parameters (kernel argument arrays) only when the product changes:
+        // a dynamically indexed argument read waits for every load in
+        // flight, which must not happen once per k-tile.
+        struct Prod {
+            const u16 *a, *b, *a2, *b2;
+            int lda, ldb;
+            u32 sa1, sa2, sb1, sb2;
         };
-        const int ntiles = (item.pos1 - item.pos0) * nk;
-        CalTerms tm = load(item.pos0, 0);
-        combine_regs<C, BF>(R, R2, tm);
-        store_tile<C>(smem, R, tid);
-        __syncthreads();
-        for (int t = 0; t < ntiles; ++t) {
-            const int t1 = t + 1;
-            const char* cur = smem + (t & 1) * C::STAGE;
-            if (t1 < ntiles) {
-                tm = load(item.pos0 + t1 / nk, (t1 % nk) * C::BK);
-                ktile_cal<C, BF, true>(cur, smem + (t1 & 1) * C::STAGE, R, R2, tm, H, wm, wn, lane, tid);
-            } else {
-                ktile_cal<C, BF, false>(cur, nullptr, R, R2, tm, H, wm, wn, lane, tid);
+        auto prod = [&](int j) {
+            const int r = order_at(item.pos0 + j);
+            return Prod{fp.a[r], fp.b[r], fp.a2[r], fp.b2[r], (int)fp.lda[r], (int)fp.ldb[r],
+                        fp.sa[r][0], fp.sa[r][1], fp.sb[r][0], fp.sb[r][1]};
+        };
+        int sj = 0, skt = 0;
+        Prod ps = prod(0);
+        auto src = [&](int, tiles::TileSrc* s1, tiles::TileSrc* s2) {
+            *s1 = tiles::TileSrc{ps.a + (int64_t)m0 * ps.lda, ps.lda, fp.Mb - m0, ps.b + n0, ps.ldb, fp.Nb - n0,
+                                 skt * C::BK, fp.Kb};
+            *s2 = *s1;
+            if (ps.a2)
+                s2->a = ps.a2 + (int64_t)m0 * ps.lda;
+            else
+                s2->a_rows = 0;
+            if (ps.b2)
+                s2->b = ps.b2 + n0;
+            else
+                s2->b_cols = 0;
+            if (++skt == nk) {
+                skt = 0;
+                if (++sj < nprod)
+                    ps = prod(sj);
             }
-            if (t % nk == nk - 1) {
-                combine_h<NOUT, C>(fp.w[fp.order[item.pos0 + t / nk]], H, Cacc);
+        };
+        auto fold = [&](char* x, int bytes, bool two, u32 s1, u32 s2) {
+            for (int c = tid; c < bytes / 16; c += C::NT) {
+                u32x4 v = *reinterpret_cast<const u32x4*>(x + c * 16);
+                if (two) {
+                    const u32x4 y = *reinterpret_cast<const u32x4*>(x + C::STAGE + c * 16);
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        v[d] = add_h2<BF>(v[d] ^ s1, y[d] ^ s2);
+                } else {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        v[d] ^= s1;
+                }
+                *reinterpret_cast<u32x4*>(x + c * 16) = v;
+            }
+        };
+        int cj = 0, ckt = 0;
+        Prod pc = ps;
+        auto comb = [&](int, char* stage) {
+            if (pc.a2 || pc.sa1)
+                fold(stage, C::A_BYTES, pc.a2 != nullptr, pc.sa1, pc.sa2);
+            if (pc.b2 || pc.sb1)
+                fold(stage + C::A_BYTES, C::B_BYTES, pc.b2 != nullptr, pc.sb1, pc.sb2);
+            if (++ckt == nk) {
+                ckt = 0;
+                if (++cj < nprod)
+                    pc = prod(cj);
+            }
+        };
+        int aj = 0, akt = 0;
+        auto after = [&](int) {
+            if (++akt == nk) {
+                akt = 0;
+                combine_h<NOUT, C>(fp.w[order_at(item.pos0 + aj)], H, Cacc);
                 zero_acc<C>(H);
+                ++aj;
             }
-            __syncthreads();
-        }
-
-        fused_epilogue<NOUT, C, BF>(fp, item, m0, n0, Cacc, tid, wm, wn, lane, &sh_old);
+        };
+        const m16::Addr<C> ad = m16::frag_addr<C>(wm, wn, lane);
+        m16::run_tile_cal<C, BF>(smem, ntiles, src, comb, after, wave, lane, ad, H);
+        __syncthreads();
+        fused_epilogue<NOUT, C, BF>(fp, item, m0, n0, Cacc, tid, wm, wn, lane, reinterpret_cast<int*>(smem));
         __syncthreads();
     }
 }
@@ -2601,7 +2683,7 @@ hipError_t launch_prepass(const PrepassLaunch& L, hipStream_t st)
 
 int32_t fused_tile(int32_t levels) { return levels == 1 ? MCF1::BM : FusedCfg<2>::C::BM; }
 static_assert(MCF1::BM == MCF1::BN, "fused tiles are square");
-static_assert(CfgCal::BM == MCF1::BM && CfgCal::BN == MCF1::BN,
+static_assert(MCFC::BM == MCF1::BM && MCFC::BN == MCF1::BN,
               "the combine-at-load kernel shares the one-level group geometry");
 static_assert(sizeof(FusedParams) <= 4096, "kernel arguments");
 static_assert(FusedCfg<2>::C::BM == FusedCfg<2>::C::BN,
@@ -2638,9 +2720,9 @@ hipError_t launch_fused(const FusedLaunch& L, hipStream_t st)
         if (L.grid <= 0)
             return hipSuccess;
         if (L.out_bf16)
-            hipLaunchKernelGGL((k_fused_cal<true>), dim3(L.grid), dim3(CfgCal::NT), 0, st, L.p);
+            hipLaunchKernelGGL((k_fused_cal_m16<true>), dim3(L.grid), dim3(MCFC::NT), 0, st, L.p);
         else
-            hipLaunchKernelGGL((k_fused_cal<false>), dim3(L.grid), dim3(CfgCal::NT), 0, st, L.p);
+            hipLaunchKernelGGL((k_fused_cal_m16<false>), dim3(L.grid), dim3(MCFC::NT), 0, st, L.p);
         return hipGetLastError();
     }
     if (L.levels == 1 || L.outer) {

@@ -104,9 +104,9 @@ typedef enum {
     LCMA_COMBINE_AT_LOAD = 2, /* one level of the built-in scheme: no pre-pass; the group kernel loads the one
                                  or two input blocks of each operand, adds them in fp32 (binary16: one packed
                                  add, the same single rounding) and rounds once to the operand type while
-                                 staging each k-tile, so no combined operand is written and the workspace is
-                                 empty.  Runs on the register-staged four-wave engine.  Operands keep the
-                                 storage type and groups are never split: with LCMA_ALGO_L2, a generic
+                                 staging each k-tile (both blocks go to LDS, then all threads fold them in
+                                 place), so no combined operand is written and the workspace is empty.
+                                 Operands keep the storage type and groups are never split: with LCMA_ALGO_L2, a generic
                                  description, LCMA_SPLIT_ALL or bf16_ops_f16 = 1 on bfloat16 inputs,
                                  lcma_plan_ex returns LCMA_E_UNSUPPORTED.  lcma_prepass does nothing and
                                  lcma_fused runs the whole product; lcma_plan_operand is LCMA_E_INVALID */
@@ -157,8 +157,8 @@ typedef struct {
                                0 = 0.52 (measured on MI355X at 4096^3 .. 16384^3) */
     double fused_eff;       /* the same for the fused group kernel (both levels);
                                0 = 0.31 for one level and for two levels with the outer level in
-                               memory, 0.037 for LCMA_COMBINE_L2_ON_CHIP (measured), 0.2 for
-                               LCMA_COMBINE_AT_LOAD */
+                               memory, 0.037 for LCMA_COMBINE_L2_ON_CHIP, 0.13 for
+                               LCMA_COMBINE_AT_LOAD (measured) */
     lcma_order order;       /* persistent fused kernel's work order (LCMA_ORDER_AUTO by default) */
 } lcma_options;
 
