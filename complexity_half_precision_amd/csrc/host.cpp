@@ -483,10 +483,9 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     const bool generic = desc && builtin_kind(desc) == 0;
     const bool unfused = generic || o.combine == LCMA_COMBINE_UNFUSED;
     // Combining at load: one level of the built-in scheme, operands of the
-    // storage type, no split (nothing would clear the fix-up counters).
+    // storage type.
     const bool at_load = o.combine == LCMA_COMBINE_AT_LOAD;
-    if (at_load && (generic || force == LCMA_ALGO_L2 || o.split == LCMA_SPLIT_ALL ||
-                    (dt == LCMA_BF16 && o.bf16_ops_f16 == 1)))
+    if (at_load && (generic || force == LCMA_ALGO_L2 || (dt == LCMA_BF16 && o.bf16_ops_f16 == 1)))
         return LCMA_E_UNSUPPORTED;
     // Two levels: the outer level goes through memory unless all 49 products
     // are to accumulate on chip.
@@ -561,7 +560,7 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         const double comb = (8.0 * nnzW - 6.0 * gen.ms * gen.ns) * (double)Mb * Nb;
         est[LCMA_ALGO_L1] = (pre + comb) / (m.eta_bw * m.bw) + gen.rank * est_classic(Mb, Nb, Kb, m) + 2 * m.launch;
     } else if (ok1 && at_load) {
-        est[LCMA_ALGO_L1] = est_lcma(M, N, K, 1, LCMA_SPLIT_NONE, false, false, m, true);
+        est[LCMA_ALGO_L1] = est_lcma(M, N, K, 1, o.split, false, false, m, true);
     } else if (ok1) {
         est[LCMA_ALGO_L1] = est_lcma(M, N, K, 1, o.split, op_bf16_for(1) != (dt == LCMA_BF16), false, m);
     }
@@ -707,7 +706,7 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         const Geo sg = sched_geo(g, p->outer);
         SchedParams& sp = p->sp;
         sp.G = sg.G; sp.gy = sg.gy; sp.gx = sg.gx; sp.R = sg.R; sp.P = m.P;
-        sp.mode = p->at_load ? kSplitNone : split_mode_for(o.split, sg.G, m.P);
+        sp.mode = split_mode_for(o.split, sg.G, m.P);
         sp.h = (sg.R + 1) / 2;
         sp.raster = o.order == LCMA_ORDER_PLAIN ? 0 : 8;
         if (sp.mode == kSplitTail) {
@@ -1000,6 +999,12 @@ lcma_status do_fused(const lcma_plan_s* p, const void* A, int64_t lda, const voi
         // place with the inputs' leading dimensions; a coefficient of -1
         // becomes a sign mask on the loaded halves.
         L.at_load = 1;
+        // no pre-pass clears the split fix-up counters here: a fill kernel
+        // does (no memset node, so the call stays capturable)
+        if (p->n_slots > 0 &&
+            hip_status(launch_pad_copy(L.p.counters, 0, 0, 0, L.p.counters, 2 * p->n_slots, 1, 2 * p->n_slots, st),
+                       "launch_pad_copy (split counters)") != LCMA_OK)
+            return LCMA_E_HIP;
         for (int r = 0; r < 7; ++r) {
             int na = 0, nb = 0;
             for (int x = 0; x < 4; ++x) {

@@ -2365,9 +2365,8 @@ __global__ void __launch_bounds__(MCFC::NT, 1) k_fused_cal_m16(const FusedParams
 {
     using C = MCFC;
     constexpr int NOUT = 4;
-    // the fix-up word of the epilogue (no split here, so never touched)
-    // reuses the ring after the K loop
     __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * 2 * C::STAGE];
+    __shared__ int sh_old;
     const int tid = threadIdx.x, lane0 = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN;
@@ -2470,7 +2469,7 @@ __global__ void __launch_bounds__(MCFC::NT, 1) k_fused_cal_m16(const FusedParams
         const m16::Addr<C> ad = m16::frag_addr<C>(wm, wn, lane);
         m16::run_tile_cal<C, BF>(smem, ntiles, src, comb, after, wave, lane, ad, H);
         __syncthreads();
-        fused_epilogue<NOUT, C, BF>(fp, item, m0, n0, Cacc, tid, wm, wn, lane, reinterpret_cast<int*>(smem));
+        fused_epilogue<NOUT, C, BF>(fp, item, m0, n0, Cacc, tid, wm, wn, lane, &sh_old);
         __syncthreads();
     }
 }

@@ -106,10 +106,12 @@ typedef enum {
                                  add, the same single rounding) and rounds once to the operand type while
                                  staging each k-tile (both blocks go to LDS, then all threads fold them in
                                  place), so no combined operand is written and the workspace is empty.
-                                 Operands keep the storage type and groups are never split: with LCMA_ALGO_L2, a generic
-                                 description, LCMA_SPLIT_ALL or bf16_ops_f16 = 1 on bfloat16 inputs,
-                                 lcma_plan_ex returns LCMA_E_UNSUPPORTED.  lcma_prepass does nothing and
-                                 lcma_fused runs the whole product; lcma_plan_operand is LCMA_E_INVALID */
+                                 Operands keep the storage type: with LCMA_ALGO_L2, a generic description
+                                 or bf16_ops_f16 = 1 on bfloat16 inputs, lcma_plan_ex returns
+                                 LCMA_E_UNSUPPORTED.  The workspace holds only the split fix-up partials and
+                                 counters (none without a split).  lcma_prepass does nothing and lcma_fused
+                                 runs the whole product (it clears the counters first); lcma_plan_operand is
+                                 LCMA_E_INVALID */
     LCMA_COMBINE_UNFUSED = 3, /* one level only: every combined operand is written; each product's epilogue adds
                                  W[r][i,j] * H_r into fp32 output blocks in the workspace (H_r is never stored)
                                  and the last contributor to a block rounds it into C.  Blocks with enough

@@ -481,7 +481,7 @@ def test_invalid_calls_fail_before_touching_the_device():
 # ---------------------------------------------------------------- combine at load
 
 def test_combine_at_load_plans_one_level_without_a_workspace():
-    p = L.lcma_plan_ex(1024, 1024, 1024, "bf16", force="l1", combine="at_load", num_cus=CUS)
+    p = L.lcma_plan_ex(1024, 1024, 1024, "bf16", force="l1", combine="at_load", split="none", num_cus=CUS)
     chosen, ws, est = L.lcma_plan_info(p)
     assert chosen == "l1" and ws == 0 and est > 0
     # no combined operand is ever written
@@ -494,8 +494,17 @@ def test_combine_at_load_plans_one_level_without_a_workspace():
     assert sorted(it[1] for it in items) == list(range(len(items)))
     assert sorted(order[:7]) == list(range(7))
     # the same in binary16, and a forced padded shape wraps it like any L1 plan
-    p = L.lcma_plan_ex(512, 512, 512, "f16", force="l1", combine="at_load", num_cus=CUS)
+    p = L.lcma_plan_ex(512, 512, 512, "f16", force="l1", combine="at_load", split="none", num_cus=CUS)
     assert L.lcma_plan_info(p)[:2] == ("l1", 0)
+    # a partial last round is split like the pre-pass path's: two pieces per
+    # tail group, partials and counters in the workspace
+    pa = L.lcma_plan_ex(2560, 2560, 2560, "bf16", force="l1", combine="at_load", num_cus=256)
+    pp = L.lcma_plan_ex(2560, 2560, 2560, "bf16", force="l1", combine="prepass", num_cus=256)
+    items_a, _ = L.lcma_plan_schedule(pa)
+    items_p, _ = L.lcma_plan_schedule(pp)
+    assert items_a == items_p and any(it[4] >= 0 for it in items_a)
+    ws_a, ws_p = L.lcma_plan_info(pa)[1], L.lcma_plan_info(pp)[1]
+    assert 0 < ws_a < ws_p
     p = L.lcma_plan_ex(500, 520, 260, "f16", force="l1", combine="at_load", num_cus=CUS)
     assert L.lcma_plan_info(p)[0] == "l1"
     with pytest.raises(L.LcmaError):
@@ -503,7 +512,7 @@ def test_combine_at_load_plans_one_level_without_a_workspace():
 
 
 def test_combine_at_load_rejects_what_it_does_not_build():
-    for kw in (dict(force="l2"), dict(force="l1", split="all"), dict(force="l1", bf16_ops_f16=1)):
+    for kw in (dict(force="l2"), dict(force="l1", bf16_ops_f16=1)):
         with pytest.raises(L.LcmaError) as e:
             L.lcma_plan_ex(1024, 1024, 1024, "bf16", combine="at_load", num_cus=CUS, **kw)
         assert e.value.status == L.E_UNSUPPORTED, kw

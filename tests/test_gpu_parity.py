@@ -573,7 +573,8 @@ def test_at_load_halves_strides_and_repeats():
     say("at_load halves")
     M, N, K = 768, 640, 1024
     A, B, A64, B64 = gen(M, N, K, "bf16", "normal_sqrtk", seed=23)
-    plan = L.lcma_plan_ex(M, N, K, "bf16", force="l1", combine="at_load")
+    # without a split the plan needs no workspace at all
+    plan = L.lcma_plan_ex(M, N, K, "bf16", force="l1", combine="at_load", split="none")
     assert L.lcma_plan_info(plan)[:2] == ("l1", 0)
     Ad, Bd = A.to(DEV), B.to(DEV)
     C0 = torch.empty((M, N), dtype=A.dtype, device=DEV)
@@ -598,6 +599,34 @@ def test_at_load_halves_strides_and_repeats():
     assert np.all(Cs[:, N:].cpu().float().numpy() == 7.0)
     assert np.array_equal(si.bits(C2.cpu()), ref)
     check_float(C0.cpu(), A64, B64, "bf16", blocks=2)
+
+
+# 2560 x 2560 x 1024: 100 groups on 256 workers, the tail split by default;
+# 1024^3 and 600 x 528 x 512 (ragged tiles): every group split
+@pytest.mark.parametrize("M,N,K,split", [(2560, 2560, 1024, "auto"), (1024, 1024, 1024, "all"),
+                                         (600, 528, 512, "all")])
+def test_at_load_split_groups(M, N, K, split):
+    say("at_load split", M, N, K, split)
+    A, B, A64, B64 = gen(M, N, K, "bf16", "normal_sqrtk", seed=25)
+    plan = L.lcma_plan_ex(M, N, K, "bf16", force="l1", combine="at_load", split=split)
+    items, _ = L.lcma_plan_schedule(plan)
+    assert any(it[4] >= 0 for it in items)
+    ws = L.workspace_for(plan)
+    # stale fix-up counters: the call must clear them itself
+    ws.fill_(0x7F)
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    outs = []
+    for _ in range(2):
+        C = torch.full((M, N), 9.0, dtype=A.dtype, device=DEV)
+        L.lcma_gemm(plan, Ad, Bd, C, ws)
+        torch.cuda.synchronize()
+        outs.append(C.cpu())
+    # fp32 addition of the two pieces' partials commutes: repeats are bitwise equal
+    assert np.array_equal(si.bits(outs[0]), si.bits(outs[1]))
+    C_ref = oracle.gemm(A64, B64)
+    e_c = check_float(classic(A, B), A64, B64, "bf16", C_ref)
+    e = check_float(outs[0], A64, B64, "bf16", C_ref, blocks=2)
+    assert e <= 4 * e_c, (e, e_c)
 
 
 # ---------------------------------------------------------------- full-size workloads
