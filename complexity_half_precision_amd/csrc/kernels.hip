@@ -1349,9 +1349,13 @@ __device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, AfterFn 
 // t + 1 into its first terms in place (its loads have landed), the loads of
 // k-tile t + AHEAD into the stage of k-tile t - 1, and the MFMAs of k-tile
 // t.  (Issuing the MFMAs before the fold measured 3-8% slower.)
-template <class C, bool BF, class SrcFn, class CombFn, class AfterFn>
+// GROUPED (interior tiles, K a multiple of 32): grouped loads with the
+// per-lane offsets `go` of the inputs' strides, shared by both terms; an
+// absent second term then loads the first term again (not folded).
+template <class C, bool BF, bool GROUPED, class SrcFn, class CombFn, class AfterFn>
 __device__ __forceinline__ void run_tile_cal(char* smem, int nk, SrcFn src, CombFn comb, AfterFn after, int wave,
-                                             int lane, const Addr<C>& ad, f32x4 (&acc)[C::FM][C::FN])
+                                             int lane, const Addr<C>& ad, const q4::Group<C>& go,
+                                             f32x4 (&acc)[C::FM][C::FN])
 {
     constexpr int ST = 2 * C::STAGE;
     constexpr int P2 = 2 * C::PER;
@@ -1363,8 +1367,19 @@ __device__ __forceinline__ void run_tile_cal(char* smem, int nk, SrcFn src, Comb
         tiles::TileSrc s1, s2;
         src(t, &s1, &s2);
         char* stage = smem + (t % C::NSTAGE) * ST;
-        q4::dma_tile<C, true>(stage, s1, wave, lane);
-        q4::dma_tile<C, true>(stage + C::STAGE, s2, wave, lane);
+        if constexpr (GROUPED) {
+            if (s2.a_rows == 0)
+                s2.a = s1.a;
+            if (s2.b_cols == 0)
+                s2.b = s1.b;
+            q4::dma_group<C>(stage, s1, go, wave, 0);
+            q4::dma_group<C>(stage, s1, go, wave, 1);
+            q4::dma_group<C>(stage + C::STAGE, s2, go, wave, 0);
+            q4::dma_group<C>(stage + C::STAGE, s2, go, wave, 1);
+        } else {
+            q4::dma_tile<C, true>(stage, s1, wave, lane);
+            q4::dma_tile<C, true>(stage + C::STAGE, s2, wave, lane);
+        }
     };
     if (nk <= 0)
         return;
@@ -2467,7 +2482,15 @@ __global__ void __launch_bounds__(MCFC::NT, 1) k_fused_cal_m16(const FusedParams
             }
         };
         const m16::Addr<C> ad = m16::frag_addr<C>(wm, wn, lane);
-        m16::run_tile_cal<C, BF>(smem, ntiles, src, comb, after, wave, lane, ad, H);
+        // every term is a block of A or B: one set of grouped-load offsets
+        const bool inside = (m0 + C::BM <= fp.Mb) & (n0 + C::BN <= fp.Nb) & (fp.Kb % C::BK == 0);
+        if (inside) {
+            const tiles::TileSrc st{nullptr, ps.lda, C::BM, nullptr, ps.ldb, C::BN, 0, fp.Kb};
+            const q4::Group<C> go = q4::group_offsets<C>(st, wave, lane);
+            m16::run_tile_cal<C, BF, true>(smem, ntiles, src, comb, after, wave, lane, ad, go, H);
+        } else {
+            m16::run_tile_cal<C, BF, false>(smem, ntiles, src, comb, after, wave, lane, ad, q4::Group<C>{}, H);
+        }
         __syncthreads();
         fused_epilogue<NOUT, C, BF>(fp, item, m0, n0, Cacc, tid, wm, wn, lane, &sh_old);
         __syncthreads();
