@@ -54,7 +54,8 @@ class lcma_desc(ctypes.Structure):
 class lcma_options(ctypes.Structure):
     _fields_ = [("split", _i32), ("combine", _i32), ("bf16_ops_f16", _i32), ("num_cus", _i32),
                 ("peak_tflops", ctypes.c_double), ("hbm_gbps", ctypes.c_double),
-                ("classic_eff", ctypes.c_double), ("fused_eff", ctypes.c_double), ("order", _i32)]
+                ("classic_eff", ctypes.c_double), ("fused_eff", ctypes.c_double), ("order", _i32),
+                ("accuracy_optin", _i32)]
 
 
 def _sig(name, res, args):
@@ -132,6 +133,67 @@ def _ld(t, default):
     return t.stride(0)
 
 
+_TORCH_DT = {F16: torch.float16, BF16: torch.bfloat16}
+
+
+def _device_of_stream(stream, *tensors):
+    """Device the call runs on (the stream's, else the current one), after
+    checking that every tensor argument is a device tensor at all."""
+    for what, t in tensors:
+        if isinstance(t, torch.Tensor) and not t.is_cuda:
+            raise ValueError(f"{what} must be a device tensor (got {t.device})")
+    return torch.cuda.current_device() if stream is None or isinstance(stream, int) else stream.device.index
+
+
+def _check_matrix(t, rows, cols, ld, dtype, what, device):
+    """Checks a tensor argument against the extent the library will address:
+    rows x cols elements at leading dimension ld from its data pointer, on the
+    plan's device and of the plan's storage type.  Raw integer addresses (and
+    None) pass unchecked: the C ABI cannot see buffer sizes, this layer can."""
+    if t is None or isinstance(t, int):
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch tensor or a device address, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor (got {t.device})")
+    if t.device.index != device:
+        raise ValueError(f"{what} is on {t.device}, the call runs on cuda:{device}")
+    if dtype is not None and t.dtype != _TORCH_DT[dtype]:
+        raise ValueError(f"{what} has dtype {t.dtype}, the plan's storage type is {_TORCH_DT[dtype]}")
+    if rows <= 0 or cols <= 0:
+        return
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{what} must be 2-D with unit column stride (row-major)")
+    if t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError(f"{what} has shape {tuple(t.shape)}, the call addresses {rows} x {cols}")
+    if ld < cols:
+        raise ValueError(f"{what}: leading dimension {ld} < {cols} columns")
+    need = t.storage_offset() + (rows - 1) * ld + cols
+    have = t.untyped_storage().nbytes() // t.element_size()
+    if need > have:
+        raise ValueError(f"{what}: {rows} rows at leading dimension {ld} need {need} elements of storage, "
+                         f"the tensor's storage holds {have}")
+
+
+def _check_workspace(ws, nbytes, device):
+    if ws is None or isinstance(ws, int):
+        return
+    if not ws.is_cuda or ws.device.index != device:
+        raise ValueError(f"workspace must be a device tensor on cuda:{device} (got {ws.device})")
+    have = ws.untyped_storage().nbytes() - ws.storage_offset() * ws.element_size()
+    if not ws.is_contiguous() or have < nbytes:
+        raise ValueError(f"workspace: a contiguous buffer of at least {nbytes} bytes is needed")
+
+
+def _check_call(plan, A, lda, B, ldb, C, ldc, stream, need_c=True, workspace=None):
+    dev = _device_of_stream(stream, ("A", A), ("B", B), ("C", C if need_c else None), ("workspace", workspace))
+    _check_matrix(A, plan.M, plan.K, lda, plan.dtype, "A", dev)
+    _check_matrix(B, plan.K, plan.N, ldb, plan.dtype, "B", dev)
+    if need_c:
+        _check_matrix(C, plan.M, plan.N, ldc, plan.dtype, "C", dev)
+    return dev
+
+
 def _current_stream():
     # torch's raw handle of the current stream (one C call; building a
     # torch.cuda.Stream object costs ~3 us per library call)
@@ -198,11 +260,11 @@ class Plan:
 
 def lcma_plan_ex(M, N, K, dtype, desc: Desc | None = None, force="auto", split="auto", combine="auto",
                  bf16_ops_f16=0, num_cus=0, peak_tflops=0.0, hbm_gbps=0.0, classic_eff=0.0,
-                 fused_eff=0.0, order="auto") -> Plan:
+                 fused_eff=0.0, order="auto", accuracy_optin=0) -> Plan:
     opts = lcma_options(_SPLIT[split] if isinstance(split, str) else split,
                         _COMBINE[combine] if isinstance(combine, str) else combine,
                         bf16_ops_f16, num_cus, peak_tflops, hbm_gbps, classic_eff, fused_eff,
-                        _ORDER[order] if isinstance(order, str) else order)
+                        _ORDER[order] if isinstance(order, str) else order, int(accuracy_optin))
     h = _vp()
     st = _lib_plan_ex(M, N, K, _dt(dtype), ctypes.byref(desc.c) if desc is not None else None,
                       _ALGO[force] if isinstance(force, str) else force, ctypes.byref(opts), ctypes.byref(h))
@@ -251,8 +313,11 @@ def lcma_gemm(plan: Plan, A, B, C, workspace=None, workspace_bytes=None, stream=
               ldc=None) -> None:
     ws_bytes = workspace_bytes if workspace_bytes is not None else (
         0 if workspace is None or isinstance(workspace, int) else workspace.numel() * workspace.element_size())
-    _check(_lib_gemm(plan.handle, _ptr(A), lda or _ld(A, plan.K), _ptr(B), ldb or _ld(B, plan.N), _ptr(C),
-                     ldc or _ld(C, plan.N), _ptr(workspace), ws_bytes, _stream(stream)), "lcma_gemm")
+    lda, ldb, ldc = lda or _ld(A, plan.K), ldb or _ld(B, plan.N), ldc or _ld(C, plan.N)
+    dev = _check_call(plan, A, lda, B, ldb, C, ldc, stream, workspace=workspace)
+    _check_workspace(workspace, ws_bytes, dev)
+    _check(_lib_gemm(plan.handle, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(workspace), ws_bytes,
+                     _stream(stream)), "lcma_gemm")
 
 
 def _ws_bytes(workspace):
@@ -261,14 +326,20 @@ def _ws_bytes(workspace):
 
 def lcma_prepass(plan: Plan, A, B, workspace, stream=None, lda=None, ldb=None) -> None:
     ws_bytes = _ws_bytes(workspace)
-    _check(_lib_prepass(plan.handle, _ptr(A), lda or _ld(A, plan.K), _ptr(B), ldb or _ld(B, plan.N),
-                        _ptr(workspace), ws_bytes, _stream(stream)), "lcma_prepass")
+    lda, ldb = lda or _ld(A, plan.K), ldb or _ld(B, plan.N)
+    dev = _check_call(plan, A, lda, B, ldb, None, 0, stream, need_c=False, workspace=workspace)
+    _check_workspace(workspace, ws_bytes, dev)
+    _check(_lib_prepass(plan.handle, _ptr(A), lda, _ptr(B), ldb, _ptr(workspace), ws_bytes, _stream(stream)),
+           "lcma_prepass")
 
 
 def lcma_fused(plan: Plan, A, B, C, workspace, stream=None, lda=None, ldb=None, ldc=None) -> None:
     ws_bytes = _ws_bytes(workspace)
-    _check(_lib_fused(plan.handle, _ptr(A), lda or _ld(A, plan.K), _ptr(B), ldb or _ld(B, plan.N), _ptr(C),
-                      ldc or _ld(C, plan.N), _ptr(workspace), ws_bytes, _stream(stream)), "lcma_fused")
+    lda, ldb, ldc = lda or _ld(A, plan.K), ldb or _ld(B, plan.N), ldc or _ld(C, plan.N)
+    dev = _check_call(plan, A, lda, B, ldb, C, ldc, stream, workspace=workspace)
+    _check_workspace(workspace, ws_bytes, dev)
+    _check(_lib_fused(plan.handle, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(workspace), ws_bytes,
+                      _stream(stream)), "lcma_fused")
 
 
 def gemm_classic(A, B, C, stream=None, M=None, N=None, K=None, dtype=None, lda=None, ldb=None, ldc=None) -> None:
@@ -276,8 +347,12 @@ def gemm_classic(A, B, C, stream=None, M=None, N=None, K=None, dtype=None, lda=N
     K = K if K is not None else A.shape[1]
     N = N if N is not None else B.shape[1]
     dt = _dt(dtype if dtype is not None else A.dtype)
-    _check(_lib_classic(M, N, K, dt, _ptr(A), lda or _ld(A, K), _ptr(B), ldb or _ld(B, N), _ptr(C),
-                        ldc or _ld(C, N), _stream(stream)), "gemm_classic")
+    lda, ldb, ldc = lda or _ld(A, K), ldb or _ld(B, N), ldc or _ld(C, N)
+    dev = _device_of_stream(stream, ("A", A), ("B", B), ("C", C))
+    _check_matrix(A, M, K, lda, dt, "A", dev)
+    _check_matrix(B, K, N, ldb, dt, "B", dev)
+    _check_matrix(C, M, N, ldc, dt, "C", dev)
+    _check(_lib_classic(M, N, K, dt, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _stream(stream)), "gemm_classic")
 
 
 def workspace_for(plan: Plan, device="cuda"):

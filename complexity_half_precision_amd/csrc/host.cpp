@@ -370,6 +370,10 @@ struct lcma_plan_s {
 
 static int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
+// Kernels address rows through 32-bit buffer offsets re-based at every
+// k-tile: a tile spans at most 256 rows of a leading dimension below 2^21.
+static constexpr int64_t kMaxLd = (int64_t)1 << 21;
+
 // Wraps `in`, planned for the Mp x Np x Kp product, into a plan for M x N x K
 // that copies A and B into zero-padded buffers in the workspace, runs `in`
 // there and crops its product into C.  extra_s: estimated seconds of the
@@ -448,6 +452,10 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         return LCMA_E_INVALID;
     if (force < LCMA_ALGO_AUTO || force > LCMA_ALGO_L2)
         return LCMA_E_INVALID;
+    // lda >= K and ldb, ldc >= N: no call of such a plan could pass the
+    // leading-dimension limit of the kernels
+    if (M > 0 && N > 0 && K > 0 && (K >= kMaxLd || N >= kMaxLd))
+        return LCMA_E_UNSUPPORTED;
     lcma_options o{};
     if (opts)
         o = *opts;
@@ -455,7 +463,7 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         o.order > LCMA_ORDER_PLAIN || o.combine < LCMA_COMBINE_AUTO ||
         o.combine > LCMA_COMBINE_L2_ON_CHIP || o.num_cus < 0 || o.peak_tflops < 0 || o.hbm_gbps < 0 ||
         o.bf16_ops_f16 < -1 || o.bf16_ops_f16 > 1 || !(o.classic_eff >= 0 && o.classic_eff <= 1) ||
-        !(o.fused_eff >= 0 && o.fused_eff <= 1))
+        !(o.fused_eff >= 0 && o.fused_eff <= 1) || o.accuracy_optin < 0 || o.accuracy_optin > 1)
         return LCMA_E_INVALID;
 
     // Which LCMA levels the description allows.  A description that is not
@@ -494,7 +502,7 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         return LCMA_E_UNSUPPORTED;
 
     Machine m;
-    m.peak = (o.peak_tflops > 0 ? o.peak_tflops : 2516.0) * 1e12;
+    m.peak = (o.peak_tflops > 0 ? o.peak_tflops : 2500.0) * 1e12;
     m.bw = (o.hbm_gbps > 0 ? o.hbm_gbps : 8000.0) * 1e9;
     m.l2bw = 8.0 * 2048.0 * 2.4e9;
     m.launch = 4e-6;
@@ -530,7 +538,7 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         if (M % S || N % S || K % S)
             return false;
         const int64_t Mb = M / S, Nb = N / S, Kb = K / S;
-        return Mb >= 1 && Nb >= 8 && Kb >= 8 && Nb % 8 == 0 && Kb % 8 == 0;
+        return Mb >= 1 && Nb >= 8 && Kb >= 8 && Nb % 8 == 0 && Kb % 8 == 0 && Nb < kMaxLd && Kb < kMaxLd;
     };
 
     // One level of the description on the unfused path: even block split,
@@ -539,7 +547,8 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         if (M % gen.ms || N % gen.ns || K % gen.ks)
             return false;
         const int64_t Mb = M / gen.ms, Nb = N / gen.ns, Kb = K / gen.ks;
-        return Mb >= 1 && Nb >= 8 && Kb >= 8 && Nb % 8 == 0 && Kb % 8 == 0 && Nb <= ((int64_t)1 << 19);
+        return Mb >= 1 && Nb >= 8 && Kb >= 8 && Nb % 8 == 0 && Kb % 8 == 0 && Nb <= ((int64_t)1 << 19) &&
+               Kb < kMaxLd;
     };
 
     double est[4] = {-1, -1, -1, -1};
@@ -602,7 +611,8 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         (force == LCMA_ALGO_L1 ? allow_l1 : allow_l2 && !unfused) && M > 0 && N > 0 && K > 0 &&
         (pad_up(M) != M || pad_up(N) != N || pad_up(K) != K)) {
         const int64_t Mp = pad_up(M), Np = pad_up(N), Kp = pad_up(K);
-        if (Mp > INT32_MAX || Np > INT32_MAX || Kp > INT32_MAX)
+        // the padded copies are addressed with leading dimensions Kp and Np
+        if (Mp > INT32_MAX || Np >= kMaxLd || Kp >= kMaxLd)
             return LCMA_E_UNSUPPORTED;
         lcma_plan_s* in = nullptr;
         lcma_status s = lcma_plan_ex(Mp, Np, Kp, dt, desc, force, opts, &in);
@@ -623,6 +633,13 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     if (force == LCMA_ALGO_L1 && !ok1)
         return LCMA_E_UNSUPPORTED;
     if (force == LCMA_ALGO_L2 && !ok2)
+        return LCMA_E_UNSUPPORTED;
+    // Accuracy: two levels with combined operands rounded to binary16 from
+    // binary16 inputs, or to bfloat16 from bfloat16 inputs, carry about 5.8x
+    // the classic kernel's normwise error (fp64 evaluation of the scheme with
+    // rounded operands), beyond the 4x this library promises.  Such plans
+    // need an explicit opt-in.
+    if (force == LCMA_ALGO_L2 && !o.accuracy_optin && (dt == LCMA_F16 || op_bf16_for(2) == 1))
         return LCMA_E_UNSUPPORTED;
     if (force == LCMA_ALGO_AUTO) {
         // Ties (within 2%) go to classic, then to fewer levels.  Two levels
@@ -647,7 +664,7 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     // the element-load kernel instead).
     if (chosen == LCMA_ALGO_CLASSIC && M > 0 && N > 0 && K > 0 && (K % 8 || N % 8)) {
         const int64_t Np = (N + 7) / 8 * 8, Kp = (K + 7) / 8 * 8;
-        if (Np > INT32_MAX || Kp > INT32_MAX)
+        if (Np >= kMaxLd || Kp >= kMaxLd)
             return LCMA_E_UNSUPPORTED;
         lcma_plan_s* in = nullptr;
         lcma_status s = lcma_plan_ex(M, Np, Kp, dt, nullptr, LCMA_ALGO_CLASSIC, &o, &in);
@@ -879,7 +896,6 @@ lcma_status check_io(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
             return LCMA_E_INVALID;
     }
     // 32-bit buffer offsets: a tile spans at most 256 rows of a leading dimension.
-    const int64_t kMaxLd = (int64_t)1 << 21;
     if (lda >= kMaxLd || ldb >= kMaxLd || (check_c && ldc >= kMaxLd))
         return LCMA_E_UNSUPPORTED;
     const auto al = [](const void* x, uintptr_t a) { return ((uintptr_t)x % a) == 0; };

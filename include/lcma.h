@@ -153,7 +153,7 @@ typedef struct {
                                -1 = always bfloat16 operands */
     int32_t num_cus;        /* 0 = query the current device; >0 = plan for that many compute units
                                (host-only planning and tests) */
-    double peak_tflops;     /* 0 = 2516 (dense fp16/bf16 MFMA: 256 CUs x 4096 FLOP/clk x 2.4 GHz) */
+    double peak_tflops;     /* 0 = 2500 (published dense fp16/bf16 MFMA peak of MI355X) */
     double hbm_gbps;        /* 0 = 8000 */
     double classic_eff;     /* fraction of peak_tflops the classic kernel sustains when compute-bound;
                                0 = 0.52 (measured on MI355X at 4096^3 .. 16384^3) */
@@ -162,6 +162,9 @@ typedef struct {
                                memory, 0.037 for LCMA_COMBINE_L2_ON_CHIP, 0.13 for
                                LCMA_COMBINE_AT_LOAD (measured) */
     lcma_order order;       /* persistent fused kernel's work order (LCMA_ORDER_AUTO by default) */
+    int32_t accuracy_optin; /* 1 = accept a forced algorithm whose error exceeds 4x the classic kernel's
+                               on the same inputs (see "Accuracy" at lcma_plan); 0 = refuse it with
+                               LCMA_E_UNSUPPORTED */
 } lcma_options;
 
 typedef struct lcma_plan_s* lcma_plan_t;
@@ -169,16 +172,25 @@ typedef struct lcma_plan_s* lcma_plan_t;
 /* Built-in Strassen schemes: levels = 1 (2x2x2, rank 7) or 2 (4x4x4, rank
  * 49, the Kronecker square of the one-level scheme).  The tables are static
  * storage owned by the library (do not free).
- * Errors: LCMA_E_INVALID (levels not 1 or 2, out == NULL). */
+ * Errors: LCMA_E_INVALID (levels not 1 or 2, out == NULL).
+ * Source: [FG] "从 Strassen 出发" (Strassen's 7 products of a 2x2 block split;
+ * applied twice, 49 products instead of 64; the U/V/W description). */
 lcma_status lcma_desc_builtin(int32_t levels, lcma_desc* out);
 
 /* Checks a description: positive sizes, coefficients in [-8, 8], and
  * Brent's identity sum_r U[r][i,k] V[r][k',j] W[r][i',j'] =
  * [k==k'][i==i'][j==j'] (exact integers).  LCMA_OK or LCMA_E_BAD_DESCRIPTOR
- * (LCMA_E_INVALID for NULL). */
+ * (LCMA_E_INVALID for NULL).
+ * Source: [FG] "从 Strassen 出发" (a scheme is a set of coefficient tables that
+ * must reproduce the exact product); the identity itself is the textbook
+ * condition for such tables. */
 lcma_status lcma_desc_validate(const lcma_desc* desc);
 
 /* Plans C = A * B for an M x N x K product of storage type dt.
+ * Source: [FG] "从缓存重排到 Cost Model" (a roofline-like cost model from
+ * FLOPs, bytes and the device's peak and bandwidth picks the algorithm per
+ * shape; it aims to pick, not to predict) and [KP] "Roofline"; the product
+ * forms come from [FG] "从 LCMA 到 FalconGEMM".
  *   desc:  NULL = built-in Strassen schemes; otherwise validated
  *          (LCMA_E_BAD_DESCRIPTOR) and deep-copied.  A description that is
  *          not one of the built-in schemes runs one level of itself through
@@ -197,6 +209,22 @@ lcma_status lcma_desc_validate(const lcma_desc* desc);
  *          M x N window is copied into C (any alignment and leading
  *          dimensions).  Other forced combinations that do not fit return
  *          LCMA_E_UNSUPPORTED.
+ * Accuracy: an LCMA result may carry at most 4x the error of the classic
+ * kernel on the same inputs (e_nw = ||C - C_ref||_F / (||A||_F ||B||_F)).
+ * Measured by evaluating the schemes with rounded combined operands in fp64
+ * (uniform / normal inputs, 512..1024 per side): one level 2.8x; two levels
+ * with combined operands of the input type 5.8-5.9x; two levels of bfloat16
+ * inputs with binary16 operands (the default) 1.1x.  So LCMA_ALGO_L2 on
+ * binary16 inputs, and on bfloat16 inputs with bf16_ops_f16 = -1, returns
+ * LCMA_E_UNSUPPORTED unless opts->accuracy_optin = 1 (AUTO never picks them).
+ * Two levels with binary16 operands need every combination of up to four
+ * bfloat16 input entries to stay below 65520 in magnitude: a larger sum
+ * rounds to +-Inf, which then propagates into C as IEEE arithmetic makes it
+ * (nothing is checked on the device).
+ * Leading dimensions: every buffer the plan addresses (the inputs, the
+ * combined operands and, for padded plans, the zero-padded copies) must have
+ * a leading dimension below 2^21 elements; a plan that would need a larger
+ * one returns LCMA_E_UNSUPPORTED (AUTO falls back to classic when it can).
  * Sizes: M, N, K >= 0 (negative: LCMA_E_INVALID).  Zero-sized products are
  * valid (K = 0 writes C = 0).  Performs no device work; the only HIP call
  * is a device-property query when opts->num_cus is 0.
@@ -209,15 +237,25 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt,
 
 /* What the plan chose: algorithm, workspace bytes the caller must pass to
  * lcma_gemm, and the cost model's time estimate in seconds (any output
- * pointer may be NULL). */
+ * pointer may be NULL).  LCMA_E_INVALID for a NULL plan.
+ * Source: [FG] "从缓存重排到 Cost Model" (the algorithm picked per shape). */
 lcma_status lcma_plan_info(lcma_plan_t plan, lcma_algo* chosen, size_t* workspace_bytes,
                            double* est_seconds);
 
 /* Cost-model estimate (seconds) the plan computed for one algorithm;
- * a negative value means the algorithm was not admissible for the shape. */
+ * a negative value means the algorithm was not admissible for the shape.
+ * Per kernel the model takes max(F / (eta * peak * q), B / (0.8 * bw),
+ * F / (I_tile * bw_L2 * q)) + 4 us, with bw_L2 = 8 * 2048 B * 2.4 GHz,
+ * I_tile = BM * BN / (BM + BN), q the wave-quantisation efficiency and eta
+ * the kernel's sustained fraction of the peak.
+ * Source: [FG] "从缓存重排到 Cost Model"; [KP] "Roofline". */
 lcma_status lcma_plan_estimate(lcma_plan_t plan, lcma_algo algo, double* est_seconds);
 
 /* Runs the planned product on `stream`.  A, B, C: device pointers as above.
+ * Source: [FG] "从 LCMA 到 FalconGEMM" (combine A/B, the block products,
+ * combine H accumulated in fp32 on chip, one final cast) for LCMA plans;
+ * [CL2] "核心贡献与发现的技术" (staged, coalesced tile loads) for classic
+ * plans.
  * Fast path: pointers 16-byte aligned and lda, ldb multiples of 8; classic
  * and padded LCMA plans accept any alignment (slower element loads, resp.
  * element-wise padding copies), other LCMA plans require it
@@ -230,7 +268,9 @@ lcma_status lcma_gemm(lcma_plan_t plan, const void* A, int64_t lda, const void* 
                       void* C, int64_t ldc, void* workspace, size_t workspace_bytes,
                       void* stream);
 
-/* The two halves of lcma_gemm for an LCMA plan using the pre-pass, exposed
+/* Source: [FG] "从 LCMA 到 FalconGEMM" (the combine-A/B pass and the
+ * persistent group kernel as two stages of the pipeline).
+ * The two halves of lcma_gemm for an LCMA plan using the pre-pass, exposed
  * so each kernel can be checked and timed on its own: lcma_prepass writes
  * the combined operands (and clears the split counters) in the workspace;
  * lcma_fused then runs the persistent group kernel from them.  Calling
@@ -245,7 +285,8 @@ lcma_status lcma_fused(lcma_plan_t plan, const void* A, int64_t lda, const void*
                        void* C, int64_t ldc, void* workspace, size_t workspace_bytes,
                        void* stream);
 
-/* Where the pre-pass puts the combined operand of product r (0-based) in the
+/* Source: [FG] "从 LCMA 到 FalconGEMM" (combined operands of the products).
+ * Where the pre-pass puts the combined operand of product r (0-based) in the
  * workspace: side 0 = A (an (M/ms) x (K/ks) matrix), side 1 = B (a (K/ks) x
  * (N/ns) matrix).  *offset_bytes receives its byte offset and *ld its
  * leading dimension; *offset_bytes = -1 when the operand is a single input
@@ -256,7 +297,9 @@ lcma_status lcma_fused(lcma_plan_t plan, const void* A, int64_t lda, const void*
 lcma_status lcma_plan_operand(lcma_plan_t plan, int32_t side, int32_t r, int64_t* offset_bytes,
                               int64_t* ld, lcma_dtype* dtype);
 
-/* Schedule of the persistent kernel, for host-side checking.  Fills up to
+/* Source: [FG] "从 LCMA 到 FalconGEMM" (groups on compute units, the split of
+ * a group over two compute units, locality-aware ordering).
+ * Schedule of the persistent kernel, for host-side checking.  Fills up to
  * `cap` work items, 5 int32 each: worker, group, first product position,
  * end product position (in the kernel's product order), split slot (-1 for
  * a whole group).  *count receives the total number of items (call with
@@ -268,13 +311,20 @@ lcma_status lcma_plan_schedule(lcma_plan_t plan, int32_t* items, int64_t cap, in
                                int32_t* order);
 
 /* Classic MFMA GEMM without a plan (enqueues one kernel on `stream`).
- * Same layout, alignment and error rules as lcma_gemm. */
+ * Same layout, alignment and error rules as lcma_gemm; K or N not a
+ * multiple of 8, or unaligned operands, take the element-load kernel.
+ * Source: [CL2] "核心贡献与发现的技术" (multi-stage staging of A/B tiles,
+ * wide epilogue stores, block swizzling); [KP] "Roofline" (compute-bound
+ * when FLOPs per byte exceed the ridge point). */
 lcma_status gemm_classic(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const void* A, int64_t lda,
                          const void* B, int64_t ldb, void* C, int64_t ldc, void* stream);
 
+/* Frees a plan (NULL is a no-op).  Plans own host memory only.
+ * Source: none on the pages (plan lifetime is this library's interface). */
 void lcma_plan_destroy(lcma_plan_t plan);
 
-/* Static text for a status code. */
+/* Static text for a status code.
+ * Source: none on the pages (error reporting is this library's interface). */
 const char* lcma_status_str(lcma_status s);
 
 #ifdef __cplusplus

@@ -191,6 +191,14 @@ def strassen2() -> Desc:
     return kron(s, s)
 
 
+def magnitude(d: Desc) -> Desc:
+    """The scheme with every coefficient replaced by its absolute value.  Its
+    exact evaluation on |A|, |B| is sum_r |W_r| (sum |U_r| |A|)(sum |V_r| |B|),
+    the magnitude that bounds the rounding errors of an evaluation of ``d``
+    (not a valid scheme itself: it does not satisfy Brent's identity)."""
+    return Desc(d.ms, d.ks, d.ns, np.abs(d.U), np.abs(d.V), np.abs(d.W))
+
+
 def brent_violations(d: Desc) -> int:
     """Number of index tuples violating Brent's identity (0 = a valid scheme)."""
     return int(lib().oracle_brent_violations(d.ms, d.ks, d.ns, d.rank, _p(d.U), _p(d.V), _p(d.W)))

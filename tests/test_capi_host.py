@@ -180,9 +180,11 @@ def test_forced_lcma_on_unsplittable_shape_is_padded(M, N, K, algo):
     g = (2 if algo == "l1" else 4) * 16
     up = lambda x: -(-x // g) * g
     Mp, Np, Kp = up(M), up(N), up(K)
-    p = L.lcma_plan_ex(M, N, K, "f16", force=algo, num_cus=CUS)
+    # two levels on binary16 inputs exceed the 4x accuracy gate: opt in
+    opt = int(algo == "l2")
+    p = L.lcma_plan_ex(M, N, K, "f16", force=algo, num_cus=CUS, accuracy_optin=opt)
     chosen, ws, est = L.lcma_plan_info(p)
-    inner = L.lcma_plan_ex(Mp, Np, Kp, "f16", force=algo, num_cus=CUS)
+    inner = L.lcma_plan_ex(Mp, Np, Kp, "f16", force=algo, num_cus=CUS, accuracy_optin=opt)
     _, ws_in, est_in = L.lcma_plan_info(inner)
     assert chosen == algo
     assert ws >= 2 * (Mp * Kp + Kp * Np + Mp * Np) + ws_in
@@ -532,3 +534,89 @@ def test_combine_at_load_estimate_has_no_prepass():
     pp = L.lcma_plan_ex(n, n, n, "bf16", force="l1", combine="prepass", num_cus=256, fused_eff=0.31)
     # same kernel efficiency: dropping the pre-pass can only shorten the estimate
     assert L.lcma_plan_info(pa)[2] < L.lcma_plan_info(pp)[2]
+
+
+# ---------------------------------------------------------------- accuracy gate, limits, header
+
+def test_two_level_plans_beyond_the_accuracy_gate_need_an_opt_in():
+    # Two levels with combined operands rounded to the input type carry about
+    # 5.8-5.9x the classic kernel's normwise error (see
+    # test_oracle.py::test_two_level_error_ratios_from_the_scheme_evaluation),
+    # beyond the 4x the library promises: refused unless opted in.
+    for kw in (dict(), dict(combine="l2_on_chip")):
+        with pytest.raises(L.LcmaError) as e:
+            L.lcma_plan_ex(1024, 1024, 1024, "f16", force="l2", num_cus=CUS, **kw)
+        assert e.value.status == L.E_UNSUPPORTED, kw
+        p = L.lcma_plan_ex(1024, 1024, 1024, "f16", force="l2", num_cus=CUS, accuracy_optin=1, **kw)
+        assert L.lcma_plan_info(p)[0] == "l2"
+    # a shape that is padded first is refused the same way
+    with pytest.raises(L.LcmaError) as e:
+        L.lcma_plan_ex(1000, 1032, 520, "f16", force="l2", num_cus=CUS)
+    assert e.value.status == L.E_UNSUPPORTED
+    # bfloat16 inputs: bfloat16 operands need the opt-in, binary16 operands (the default) do not
+    with pytest.raises(L.LcmaError) as e:
+        L.lcma_plan_ex(1024, 1024, 1024, "bf16", force="l2", bf16_ops_f16=-1, num_cus=CUS)
+    assert e.value.status == L.E_UNSUPPORTED
+    for kw in (dict(bf16_ops_f16=-1, accuracy_optin=1), dict(), dict(bf16_ops_f16=1)):
+        assert L.lcma_plan_info(L.lcma_plan_ex(1024, 1024, 1024, "bf16", force="l2", num_cus=CUS, **kw))[0] == "l2"
+    # one level (about 2.8x) never needs it
+    for dt in ("f16", "bf16"):
+        for ops in (-1, 0, 1):
+            assert L.lcma_plan_info(L.lcma_plan_ex(1024, 1024, 1024, dt, force="l1", bf16_ops_f16=ops,
+                                                   num_cus=CUS))[0] == "l1"
+    with pytest.raises(L.LcmaError) as e:
+        L.lcma_plan_ex(64, 64, 64, "f16", num_cus=CUS, accuracy_optin=2)
+    assert e.value.status == L.E_INVALID
+    # the planner never picks a gated form by itself, even when it estimates it fastest
+    for (M, N, K) in si.sweep_shapes() + [(16384, 16384, 16384)]:
+        p = L.lcma_plan_ex(M, N, K, "f16", num_cus=CUS, classic_eff=0.01)
+        assert L.lcma_plan_info(p)[0] != "l2", (M, N, K)
+
+
+def test_leading_dimension_limits_are_refused_at_plan_time():
+    big = 1 << 21
+    for (M, N, K, algo) in [(8, big, 64, "auto"), (8, 64, big, "classic"),     # lda >= K, ldb >= N
+                            (8, big - 3, 64, "auto"), (8, 64, big - 5, "auto"),  # classic padding to 8
+                            (64, 64, big - 1, "l1"), (64, big - 30, 64, "l1"),    # L1 padding to 32
+                            (64, 64, big - 60, "l2")]:                           # L2 padding to 64
+        with pytest.raises(L.LcmaError) as e:
+            L.lcma_plan_ex(M, N, K, "bf16", force=algo, num_cus=CUS)
+        assert e.value.status == L.E_UNSUPPORTED, (M, N, K, algo)
+    assert L.lcma_plan_info(L.lcma_plan_ex(8, big - 8, 64, "bf16", num_cus=CUS))[0] == "classic"
+    # a split block's leading dimension must stay below the limit too: AUTO keeps classic
+    p = L.lcma_plan_ex(1 << 20, 64, big - 64, "bf16", num_cus=CUS)
+    assert L.lcma_plan_info(p)[0] == "classic"
+
+
+# The calls the boundary exports and the passage each is defined by.
+SOURCED = ["lcma_desc_builtin", "lcma_desc_validate", "lcma_plan", "lcma_plan_info", "lcma_plan_estimate",
+           "lcma_gemm", "lcma_prepass", "lcma_plan_operand", "lcma_plan_schedule", "gemm_classic",
+           "lcma_plan_destroy", "lcma_status_str"]
+
+
+def test_each_boundary_declaration_cites_its_source():
+    text = open(os.path.join(ROOT, "include", "lcma.h")).read()
+    for name in SOURCED:
+        m = re.search(r"^[a-z_ ]+\*?\s*\b" + name + r"\(", text, flags=re.M)
+        assert m, name
+        # the comment block that ends right above the declaration (or above its group)
+        before = text[:m.start()]
+        end = before.rfind("*/")
+        start = before.rfind("/*", 0, end)
+        between = before[end + 2:]
+        assert between.count(";") <= 1, (name, "comment is not next to the declaration")
+        block = before[start:end]
+        src = re.search(r"Source:(.*)", block, flags=re.S)
+        assert src, name
+        cited = src.group(1)
+        assert re.search(r"\[(FG|CL2|KP)\] \"[^\"]+\"", cited) or "none on the pages" in cited, name
+
+
+def test_binding_refuses_host_tensors_and_short_buffers():
+    import torch
+    p = L.lcma_plan_ex(64, 64, 64, "f16", force="classic", num_cus=CUS)
+    A = torch.zeros((64, 64), dtype=torch.float16)
+    with pytest.raises(ValueError, match="device tensor"):
+        L.lcma_gemm(p, A, A, A)
+    with pytest.raises(ValueError, match="device tensor"):
+        L.gemm_classic(A, A, A)

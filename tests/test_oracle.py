@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+import seeded_inputs as si
 from oracle import metrics
 import descriptors as D
 
@@ -334,3 +335,27 @@ def test_winograd_variant_evaluates_exactly_and_differs_from_strassen():
     B = rng.integers(-2, 3, (16, 16)).astype(np.float64)
     C, n = oracle.lcma(A, B, d, 2)
     assert n == 49 and np.array_equal(C, A @ B)
+
+
+@pytest.mark.parametrize("dtype,dist,levels,ops,lo,hi", [
+    ("f16", "uniform", 1, "f16", 2.5, 3.2),
+    ("bf16", "normal_sqrtk", 1, "bf16", 2.5, 3.2),
+    ("f16", "uniform", 2, "f16", 5.3, 6.5),             # beyond the 4x gate: opt-in only
+    ("bf16", "normal_sqrtk", 2, "bf16", 5.3, 6.5),      # beyond the 4x gate: opt-in only
+    ("bf16", "normal_sqrtk", 2, "f16", 0.9, 1.4),       # the default for two levels of bfloat16
+])
+def test_two_level_error_ratios_from_the_scheme_evaluation(dtype, dist, levels, ops, lo, hi):
+    # The error of a scheme evaluated with combined operands rounded to `ops`
+    # (then the result rounded once to the output type), over the error of the
+    # exact product rounded once: the basis of the library's accuracy gate
+    # (at most 4x, else an explicit opt-in).  Casts are the error source the
+    # FalconGEMM write-up names (section "从缓存重排到 Cost Model").
+    A, B = si.gen(512, 768, 640, dtype, dist, 4)
+    A64, B64 = si.f64(A), si.f64(B)
+    ref = oracle.gemm(A64, B64)
+    e_c = metrics.e_nw(oracle.round_to(dtype, ref), ref, A64, B64)
+    d = oracle.strassen() if levels == 1 else oracle.strassen2()
+    C, n = oracle.lcma(A64, B64, d, 1, round_operands=ops)
+    assert n == d.rank
+    e = metrics.e_nw(oracle.round_to(dtype, C), ref, A64, B64)
+    assert lo <= e / e_c <= hi, e / e_c
