@@ -74,6 +74,7 @@ _lib_plan_info = _sig("lcma_plan_info", _i32, [_vp, ctypes.POINTER(_i32), ctypes
                                                ctypes.POINTER(ctypes.c_double)])
 _lib_plan_estimate = _sig("lcma_plan_estimate", _i32, [_vp, _i32, ctypes.POINTER(ctypes.c_double)])
 _lib_gemm = _sig("lcma_gemm", _i32, [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp])
+_lib_gemm_noalloc = _sig("lcma_gemm_noalloc", _i32, [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp])
 _lib_prepass = _sig("lcma_prepass", _i32, [_vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp])
 _lib_fused = _sig("lcma_fused", _i32, [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp])
 _lib_plan_operand = _sig("lcma_plan_operand", _i32, [_vp, _i32, _i32, ctypes.POINTER(_i64),
@@ -85,7 +86,8 @@ _lib_plan_destroy = _sig("lcma_plan_destroy", None, [_vp])
 
 EXPORTED = ["lcma_status_str", "lcma_desc_builtin", "lcma_desc_validate", "lcma_plan", "lcma_plan_ex",
             "lcma_plan_info", "lcma_plan_estimate", "lcma_gemm", "lcma_prepass", "lcma_fused",
-            "lcma_plan_operand", "lcma_plan_schedule", "gemm_classic", "lcma_plan_destroy"]
+            "lcma_plan_operand", "lcma_plan_schedule", "gemm_classic", "lcma_plan_destroy", "lcma_gemm_noalloc"]
+SCRATCH_BYTES = 64 << 20   # LCMA_SCRATCH_BYTES
 
 
 class LcmaError(RuntimeError):
@@ -318,6 +320,15 @@ def lcma_gemm(plan: Plan, A, B, C, workspace=None, workspace_bytes=None, stream=
     _check_workspace(workspace, ws_bytes, dev)
     _check(_lib_gemm(plan.handle, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(workspace), ws_bytes,
                      _stream(stream)), "lcma_gemm")
+
+
+def lcma_gemm_noalloc(plan: Plan, A, B, C, stream=None, lda=None, ldb=None, ldc=None) -> None:
+    """lcma_gemm with the workspace taken from the library's static device scratch
+    array (no allocation; plans with a workspace above SCRATCH_BYTES are refused)."""
+    lda, ldb, ldc = lda or _ld(A, plan.K), ldb or _ld(B, plan.N), ldc or _ld(C, plan.N)
+    _check_call(plan, A, lda, B, ldb, C, ldc, stream)
+    _check(_lib_gemm_noalloc(plan.handle, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _stream(stream)),
+           "lcma_gemm_noalloc")
 
 
 def _ws_bytes(workspace):

@@ -1343,6 +1343,24 @@ lcma_status lcma_gemm(lcma_plan_t p, const void* A, int64_t lda, const void* B, 
     return do_fused(p, A, lda, B, ldb, C, ldc, io, ws, st);
 }
 
+lcma_status lcma_gemm_noalloc(lcma_plan_t p, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                              int64_t ldc, void* stream)
+{
+    static_assert(kScratchBytes == LCMA_SCRATCH_BYTES, "scratch size in lcma.h and kernels.hpp");
+    if (!p)
+        return LCMA_E_INVALID;
+    if (p->ws_bytes > kScratchBytes) {
+        if (log_enabled())
+            fprintf(stderr, "lcma: lcma_gemm_noalloc: the plan needs %zu workspace bytes, more than the %zu of the "
+                            "static scratch array\n", p->ws_bytes, kScratchBytes);
+        return LCMA_E_WORKSPACE;
+    }
+    void* ws = nullptr;
+    if (p->ws_bytes > 0 && hip_status(scratch_address(&ws), "hipGetSymbolAddress(scratch)") != LCMA_OK)
+        return LCMA_E_HIP;
+    return lcma_gemm(p, A, lda, B, ldb, C, ldc, ws, p->ws_bytes, stream);
+}
+
 lcma_status lcma_prepass(lcma_plan_t p, const void* A, int64_t lda, const void* B, int64_t ldb, void* ws,
                          size_t ws_bytes, void* stream)
 {

@@ -55,6 +55,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <utility>
 
 #include "kernels.hpp"
@@ -2769,6 +2770,38 @@ hipError_t launch_gen_group(const GenGroupLaunch& L, hipStream_t st)
     if (L.out_bf16)
         return L.op_bf16 ? launch_gen_group_t<true, true>(L, st) : launch_gen_group_t<false, true>(L, st);
     return launch_gen_group_t<false, false>(L, st);
+}
+
+// Allocation-free calls: a file-scope device array stands in for the
+// caller's workspace.  Each GPU the library runs on holds its own copy until
+// the process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory, so only the address returned by hipGetSymbolAddress (looked
+// up once per device, with that device current) is ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(void** out)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (!p || ((uintptr_t)p % 256) != 0)
+            return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_gen_product(const GenProductLaunch& L, hipStream_t st)

@@ -159,4 +159,11 @@ hipError_t launch_fused(const FusedLaunch& L, hipStream_t stream);
 // Kernel product order used by the fused kernel (position -> product).
 void fused_order(int32_t levels, int8_t* order);
 
+// Size of the device-resident scratch array of the allocation-free entry
+// point (equal to LCMA_SCRATCH_BYTES in lcma.h).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+// Device address of the current device's scratch array, looked up once per
+// device with that device current and cached.
+hipError_t scratch_address(void** out);
+
 }  // namespace lcma

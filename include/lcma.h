@@ -268,6 +268,23 @@ lcma_status lcma_gemm(lcma_plan_t plan, const void* A, int64_t lda, const void* 
                       void* C, int64_t ldc, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): lcma_gemm
+ * with the workspace taken from a static device array of LCMA_SCRATCH_BYTES
+ * that the library holds on each GPU it runs on until the process ends.
+ * The first call on a device looks the array's address up (once per device,
+ * with that device current); no call allocates or frees device memory.
+ * The caller still passes A, B and C.  Every call on one GPU shares that
+ * GPU's array and finds the last call's contents there (the kernels clear
+ * what must start at zero), so calls that can overlap on one GPU -- on two
+ * streams, or from two threads -- race and must not be issued.
+ * Errors: LCMA_E_WORKSPACE when the plan's workspace (lcma_plan_info) is
+ * larger than LCMA_SCRATCH_BYTES; LCMA_E_HIP if the address lookup fails;
+ * otherwise those of lcma_gemm. */
+#define LCMA_SCRATCH_BYTES ((size_t)64 << 20)
+lcma_status lcma_gemm_noalloc(lcma_plan_t plan, const void* A, int64_t lda, const void* B, int64_t ldb,
+                              void* C, int64_t ldc, void* stream);
+
 /* Source: [FG] "从 LCMA 到 FalconGEMM" (the combine-A/B pass and the
  * persistent group kernel as two stages of the pipeline).
  * The two halves of lcma_gemm for an LCMA plan using the pre-pass, exposed

@@ -588,6 +588,16 @@ def test_leading_dimension_limits_are_refused_at_plan_time():
     assert L.lcma_plan_info(p)[0] == "classic"
 
 
+def test_noalloc_entry_point_refuses_before_any_device_call():
+    assert L._lib_gemm_noalloc(None, 4096, 64, 4096, 64, 4096, 64, None) == L.E_INVALID
+    p = L.lcma_plan_ex(8192, 8192, 8192, "bf16", force="l1", combine="prepass", num_cus=CUS)
+    assert L.lcma_plan_info(p)[1] > L.SCRATCH_BYTES
+    # fake addresses: the call must return before touching them
+    assert L._lib_gemm_noalloc(p.handle, 4096, 8192, 8192, 8192, 16384, 8192, None) == L.E_WORKSPACE
+    text = open(os.path.join(ROOT, "include", "lcma.h")).read()
+    assert re.search(r"#define LCMA_SCRATCH_BYTES \(\(size_t\)64 << 20\)", text) and L.SCRATCH_BYTES == 64 << 20
+
+
 # The calls the boundary exports and the passage each is defined by.
 SOURCED = ["lcma_desc_builtin", "lcma_desc_validate", "lcma_plan", "lcma_plan_info", "lcma_plan_estimate",
            "lcma_gemm", "lcma_prepass", "lcma_plan_operand", "lcma_plan_schedule", "gemm_classic",
@@ -620,3 +630,5 @@ def test_binding_refuses_host_tensors_and_short_buffers():
         L.lcma_gemm(p, A, A, A)
     with pytest.raises(ValueError, match="device tensor"):
         L.gemm_classic(A, A, A)
+    with pytest.raises(ValueError, match="device tensor"):
+        L.lcma_gemm_noalloc(p, A, A, A)
