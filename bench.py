@@ -12,6 +12,12 @@ on the stream the kernels run on, so the JSON line also reports the classic
 and LCMA rates, the pre-pass bandwidth, the roofline of the dominant kernel
 and the CPU oracle's rate on a bounded sample.
 
+Also in the default line: the measured machine references (an MFMA loop
+and an HBM stream kernel of the library), the 16384^3 comparison of classic,
+one level (unfused and fused) and two levels, cold-cache and server-mode
+timings, the cold pre-pass bandwidth, and the build's targets with whether
+they are met.
+
 Prints ONE JSON line.  Single GPU only.
 """
 from __future__ import annotations
@@ -61,7 +67,8 @@ def parse():
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode-shape bandwidth measurement (one JSON line), for profiling runs")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the decode-shape bandwidth and 24-shape sweep measurements")
+                    help="skip the decode-shape bandwidth, 24-shape sweep, 16384^3 and machine measurements")
+    ap.add_argument("--no-large", action="store_true", help="skip the 16384^3 comparison")
     ap.add_argument("--cold", action="store_true",
                     help="also time every kernel with the caches flushed before each call (writes a 512 MiB "
                          "buffer between calls, outside the timed region)")
@@ -163,7 +170,7 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
     def time_cold(fn, reps):
         """Mean ms of fn with L2 and the last-level cache flushed before each call:
@@ -247,13 +254,13 @@ def main():
             d.update({"prepass_ms": t_pre, "fused_ms": t_fu, "fused_mfma_tflop": mfma_flops / 1e12,
                       "fused_tflops_actual": mfma_flops / (t_fu * 1e-3) / 1e12,
                       "prepass_bytes": pre_bytes, "prepass_gbps": pre_bytes / (t_pre * 1e-3) / 1e9})
-        if args.cold:
+        if args.cold or algo in ("classic", "l1", "l2", "l1_unfused"):
             reps_c = min(reps, 20)
             d["cold_ms"] = time_cold(lambda: L.lcma_gemm(p, Ad, Bd, C, ws), reps_c)
             if algo not in ("classic", "l1_at_load"):
                 t_pre_c = time_cold(lambda: L.lcma_prepass(p, Ad, Bd, ws), reps_c)
                 d.update({"cold_prepass_ms": t_pre_c, "cold_prepass_gbps": d["prepass_bytes"] / (t_pre_c * 1e-3) / 1e9})
-        if args.server:
+        if args.server or algo in ("classic", "l1", "l2", "l1_unfused"):
             d["server_mean_ms"], d["server_p50_ms"] = time_gapped(lambda: L.lcma_gemm(p, Ad, Bd, C, ws), 50)
         detail[algo] = d
 
@@ -337,20 +344,116 @@ def main():
         out["l1_over_classic"] = round(detail["classic"]["ms"] / detail["l1"]["ms"], 4)
     if "l1_at_load" in detail and "classic" in detail:
         out["l1_at_load_over_classic"] = round(detail["classic"]["ms"] / detail["l1_at_load"]["ms"], 4)
+    if "l1_unfused" in detail and "classic" in detail:
+        out["l1_unfused_over_classic"] = round(detail["classic"]["ms"] / detail["l1_unfused"]["ms"], 4)
     if "l1" in detail and "l1_unfused" in detail:
         # the fusion gain: same scheme, products folded on chip vs through fp32 blocks in HBM
         out["fused_over_unfused"] = round(detail["l1_unfused"]["ms"] / detail["l1"]["ms"], 4)
 
+    out["modes"] = {a: {k: round(d[k], 4) for k in ("ms", "cold_ms", "server_p50_ms", "server_mean_ms") if k in d}
+                    for a, d in detail.items() if "cold_ms" in d}
     if not args.no_extra and not args.size:
         del Ad, Bd, C, plans
         torch.cuda.empty_cache()
-        out["machine"] = hbm_copy_rate(torch, time_calls)
+        out["machine"] = machine_refs(L, torch, time_calls)
+        roofline["measured_peak_tflops"] = out["machine"]["mfma_bf16_tflops"]
+        roofline["frac_of_measured_peak"] = round(roofline["achieved"] / out["machine"]["mfma_bf16_tflops"], 4)
+        if not args.no_large:
+            out["large"] = large_square(L, si, torch, time_calls, time_cold)
         out["square_512_f16"] = small_square(L, si, torch, time_calls)
         out["decode"] = decode_bandwidth(L, si, torch, time_calls)
         out["sweep"] = sweep_picks(L, si, torch, time_calls)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(A, B, args.cpu_seconds)
+        out["cpu_baseline"]["one_core"] = cpu_baseline_one_core(A, B, args.cpu_seconds)
+    out["targets"] = targets(out)
     print(json.dumps(out), flush=True)
+
+
+def targets(out):
+    """The build's throughput targets against what this run measured (reported
+    as they stand, met or not)."""
+    t = {"classic_frac_of_peak": {"target": 0.70, "measured": out["roofline"]["frac"]}}
+    if "l1_over_classic" in out:
+        best = max(out.get("l1_over_classic", 0), out.get("l1_at_load_over_classic", 0),
+                   out.get("l1_unfused_over_classic", 0))
+        t["lcma_over_classic_4096"] = {"target": 1.08, "measured": round(best, 4)}
+    if "large" in out:
+        lg = out["large"]
+        t["lcma_over_classic_16384"] = {"target": 1.08, "measured": max(
+            lg[a]["over_classic"] for a in ("l1", "l1_fused", "l2") if a in lg)}
+    for v in t.values():
+        v["met"] = v["measured"] >= v["target"]
+    return t
+
+
+def machine_refs(L, torch, time_calls):
+    """Measured references beside the published peaks: the library's MFMA loop
+    (16x16x32, random operands, 2 workgroups of 8 waves per compute unit) and
+    its HBM stream kernel (1 GiB copied, read + write counted), plus torch's
+    device copy of the same buffers."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    res = {}
+    wg, iters = 2 * cus, 20000
+    out = torch.empty(wg * 512, dtype=torch.float32, device="cuda")
+    for dt in ("bf16", "f16"):
+        flops = [0.0]
+
+        def call():
+            flops[0] = L.lcma_measure_mfma(out, wg, iters, dt)
+        t = time_calls(call, 5, 2)
+        res[f"mfma_{dt}_tflops"] = round(flops[0] / (t * 1e-3) / 1e12, 1)
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    t = time_calls(lambda: L.lcma_measure_copy(src, dst), 10, 3)
+    res["hbm_stream_gbps"] = round(2.0 * n / (t * 1e-3) / 1e9, 1)
+    t = time_calls(lambda: dst.copy_(src), 10, 3)
+    res["torch_copy_gbps"] = round(2.0 * n / (t * 1e-3) / 1e9, 1)
+    res["note"] = ("mfma: %d workgroups x 8 waves x %d x 16 MFMAs per launch; stream: %d bytes read and written"
+                   % (wg, iters, n))
+    del out, src, dst
+    torch.cuda.empty_cache()
+    return res
+
+
+def large_square(L, si, torch, time_calls, time_cold):
+    """16384^3 bfloat16, A, B ~ N(0,1)/sqrt(K): classic against one level (the
+    planner's unfused form and the fused group kernel after a pre-pass) and
+    two levels (binary16 combined operands, the default for bfloat16), each
+    timed back to back on resident inputs; effective TFLOP/s = 2 n^3 / t."""
+    w = si.SQUARE_16384_BF16
+    n = w["M"]
+    A, B = si.gen(**w)
+    Ad, Bd = A.to("cuda"), B.to("cuda")
+    del A, B
+    C = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    flops = 2.0 * n ** 3
+    res = {"workload": f"square GEMM M=N=K={n}, bf16 A,B ~ N(0,1)/sqrt(K), fp32 accumulate, bf16 out"}
+    for name, kw in (("classic", dict(force="classic")), ("l1", dict(force="l1")),
+                     ("l1_fused", dict(force="l1", combine="prepass")), ("l2", dict(force="l2"))):
+        p = L.lcma_plan_ex(n, n, n, "bf16", **kw)
+        ws = L.workspace_for(p)
+        t = time_calls(lambda: L.lcma_gemm(p, Ad, Bd, C, ws), 6, 2)
+        d = {"ms": round(t, 4), "eff_tflops": round(flops / (t * 1e-3) / 1e12, 1)}
+        if name != "classic":
+            t_pre = time_calls(lambda: L.lcma_prepass(p, Ad, Bd, ws), 6, 1)
+            R = 49 if name == "l2" else 7
+            S = 4 if name == "l2" else 2
+            nw = sum(1 for r in range(R) for side in (0, 1) if L.lcma_plan_operand(p, side, r)[0] >= 0)
+            pre_bytes = 2.0 * 2 * n * n + 2.0 * nw * (n // S) ** 2
+            d.update({"prepass_ms": round(t_pre, 4), "prepass_gbps": round(pre_bytes / (t_pre * 1e-3) / 1e9, 1),
+                      "cold_prepass_gbps": round(pre_bytes / (time_cold(lambda: L.lcma_prepass(p, Ad, Bd, ws), 3)
+                                                              * 1e-3) / 1e9, 1),
+                      "mfma_tflop": round(2.0 * R * (n // S) ** 3 / 1e12, 3)})
+        res[name] = d
+        del ws
+        torch.cuda.empty_cache()
+    for name in ("l1", "l1_fused", "l2"):
+        res[name]["over_classic"] = round(res["classic"]["ms"] / res[name]["ms"], 4)
+    del Ad, Bd, C
+    torch.cuda.empty_cache()
+    return res
 
 
 def small_square(L, si, torch, time_calls):
@@ -519,19 +622,46 @@ def cpu_baseline(A, B, target_s):
     A64, B64 = si.f64(A), si.f64(B)
     M, K = A64.shape
     N = B64.shape[1]
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    cores = oracle.max_threads()
     rows = 64
     t0 = time.perf_counter()
     oracle.gemm_rows(A64, B64, 0, rows)
     dt = time.perf_counter() - t0
     rows = int(min(M, max(64, rows * target_s / max(dt, 1e-6))))
+    # the whole product may take less than the target: repeat it
+    reps = max(1, int(target_s / max(dt * rows / 64, 1e-6))) if rows == M else 1
     t0 = time.perf_counter()
-    oracle.gemm_rows(A64, B64, 0, rows)
+    for _ in range(reps):
+        oracle.gemm_rows(A64, B64, 0, rows)
     dt = time.perf_counter() - t0
-    tflops = 2.0 * rows * N * K / dt / 1e12
+    tflops = 2.0 * reps * rows * N * K / dt / 1e12
     return {"value": round(tflops, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"rows 0..{rows} of the {M}x{N}x{K} product (fp64, k ascending), {dt:.1f} s"}
+            "sample": f"rows 0..{rows} of the {M}x{N}x{K} product (fp64, k ascending), {reps} time(s), {dt:.1f} s"}
 
+
+def cpu_baseline_one_core(A, B, target_s):
+    """The same oracle on one host thread, on a row slice of the same workload
+    sized for about a third of target_s."""
+    import oracle
+    import seeded_inputs as si
+    A64, B64 = si.f64(A), si.f64(B)
+    M, K = A64.shape
+    N = B64.shape[1]
+    before = oracle.max_threads()
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.gemm_rows(A64, B64, 0, 8)
+        dt = time.perf_counter() - t0
+        rows = int(min(M, max(8, 8 * (target_s / 3) / max(dt, 1e-6))))
+        t0 = time.perf_counter()
+        oracle.gemm_rows(A64, B64, 0, rows)
+        dt = time.perf_counter() - t0
+        used = oracle.max_threads()
+    finally:
+        oracle.set_threads(before)
+    return {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TFLOP/s", "cores": used, "kind": "oracle",
+            "sample": f"rows 0..{rows} of the {M}x{N}x{K} product (fp64, k ascending), {dt:.1f} s"}
 
 if __name__ == "__main__":
     main()

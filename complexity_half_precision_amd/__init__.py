@@ -13,7 +13,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblcma.so")
+# LCMA_LIBRARY may name another build of the same library (the host
+# sanitizer build the CPU tests run against); the default is the in-tree one.
+LIB_PATH = os.environ.get("LCMA_LIBRARY") or os.path.join(_HERE, "liblcma.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -74,6 +76,8 @@ _lib_plan_info = _sig("lcma_plan_info", _i32, [_vp, ctypes.POINTER(_i32), ctypes
                                                ctypes.POINTER(ctypes.c_double)])
 _lib_plan_estimate = _sig("lcma_plan_estimate", _i32, [_vp, _i32, ctypes.POINTER(ctypes.c_double)])
 _lib_gemm = _sig("lcma_gemm", _i32, [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp])
+_lib_measure_mfma = _sig("lcma_measure_mfma", _i32, [_vp, _i32, _i32, _i32, _vp])
+_lib_measure_copy = _sig("lcma_measure_copy", _i32, [_vp, _vp, _sz, _vp])
 _lib_gemm_noalloc = _sig("lcma_gemm_noalloc", _i32, [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp])
 _lib_prepass = _sig("lcma_prepass", _i32, [_vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp])
 _lib_fused = _sig("lcma_fused", _i32, [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp])
@@ -86,7 +90,8 @@ _lib_plan_destroy = _sig("lcma_plan_destroy", None, [_vp])
 
 EXPORTED = ["lcma_status_str", "lcma_desc_builtin", "lcma_desc_validate", "lcma_plan", "lcma_plan_ex",
             "lcma_plan_info", "lcma_plan_estimate", "lcma_gemm", "lcma_prepass", "lcma_fused",
-            "lcma_plan_operand", "lcma_plan_schedule", "gemm_classic", "lcma_plan_destroy", "lcma_gemm_noalloc"]
+            "lcma_plan_operand", "lcma_plan_schedule", "gemm_classic", "lcma_plan_destroy", "lcma_gemm_noalloc",
+            "lcma_measure_mfma", "lcma_measure_copy"]
 SCRATCH_BYTES = 64 << 20   # LCMA_SCRATCH_BYTES
 
 
@@ -329,6 +334,22 @@ def lcma_gemm_noalloc(plan: Plan, A, B, C, stream=None, lda=None, ldb=None, ldc=
     _check_call(plan, A, lda, B, ldb, C, ldc, stream)
     _check(_lib_gemm_noalloc(plan.handle, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _stream(stream)),
            "lcma_gemm_noalloc")
+
+
+def lcma_measure_mfma(out, workgroups: int, iters: int, dtype="bf16", stream=None) -> float:
+    """Enqueues the MFMA reference loop; returns the flops it performs."""
+    if out.numel() < workgroups * 512 or out.dtype != torch.float32 or not out.is_cuda:
+        raise ValueError("out: a float32 device tensor of workgroups * 512 elements is needed")
+    _check(_lib_measure_mfma(_ptr(out), workgroups, iters, _dt(dtype), _stream(stream)), "lcma_measure_mfma")
+    return float(workgroups) * 8 * iters * 16 * 16384
+
+
+def lcma_measure_copy(src, dst, stream=None) -> None:
+    """Enqueues the HBM stream reference: dst = src (same byte size)."""
+    n = src.numel() * src.element_size()
+    if not (src.is_cuda and dst.is_cuda) or dst.numel() * dst.element_size() < n:
+        raise ValueError("src, dst: device tensors, dst at least as large as src")
+    _check(_lib_measure_copy(_ptr(src), _ptr(dst), n, _stream(stream)), "lcma_measure_copy")
 
 
 def _ws_bytes(workspace):

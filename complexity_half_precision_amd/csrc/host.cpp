@@ -370,6 +370,18 @@ struct lcma_plan_s {
 
 static int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
+// The integer a caller passed for an enum argument.  C callers may pass any
+// int; reading an out-of-range value through the enum type is undefined in
+// C++, so entry points validate the bytes before using the enum.
+template <class E>
+static int32_t enum_bits(const E* e)
+{
+    static_assert(sizeof(E) == sizeof(int32_t), "enums of the ABI are 32-bit");
+    int32_t v;
+    memcpy(&v, e, sizeof v);
+    return v;
+}
+
 // Kernels address rows through 32-bit buffer offsets re-based at every
 // k-tile: a tile spans at most 256 rows of a leading dimension below 2^21.
 static constexpr int64_t kMaxLd = (int64_t)1 << 21;
@@ -407,7 +419,7 @@ extern "C" {
 
 const char* lcma_status_str(lcma_status s)
 {
-    switch (s) {
+    switch (enum_bits(&s)) {
     case LCMA_OK: return "ok";
     case LCMA_E_INVALID: return "invalid argument";
     case LCMA_E_UNSUPPORTED: return "unsupported shape, alignment or algorithm";
@@ -448,9 +460,9 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     *out = nullptr;
     if (M < 0 || N < 0 || K < 0 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
         return LCMA_E_INVALID;
-    if (dt != LCMA_F16 && dt != LCMA_BF16)
+    if (enum_bits(&dt) != LCMA_F16 && enum_bits(&dt) != LCMA_BF16)
         return LCMA_E_INVALID;
-    if (force < LCMA_ALGO_AUTO || force > LCMA_ALGO_L2)
+    if (enum_bits(&force) < LCMA_ALGO_AUTO || enum_bits(&force) > LCMA_ALGO_L2)
         return LCMA_E_INVALID;
     // lda >= K and ldb, ldc >= N: no call of such a plan could pass the
     // leading-dimension limit of the kernels
@@ -459,9 +471,9 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     lcma_options o{};
     if (opts)
         o = *opts;
-    if (o.split < LCMA_SPLIT_AUTO || o.split > LCMA_SPLIT_ALL || o.order < LCMA_ORDER_AUTO ||
-        o.order > LCMA_ORDER_PLAIN || o.combine < LCMA_COMBINE_AUTO ||
-        o.combine > LCMA_COMBINE_L2_ON_CHIP || o.num_cus < 0 || o.peak_tflops < 0 || o.hbm_gbps < 0 ||
+    if (enum_bits(&o.split) < LCMA_SPLIT_AUTO || enum_bits(&o.split) > LCMA_SPLIT_ALL ||
+        enum_bits(&o.order) < LCMA_ORDER_AUTO || enum_bits(&o.order) > LCMA_ORDER_PLAIN ||
+        enum_bits(&o.combine) < LCMA_COMBINE_AUTO || enum_bits(&o.combine) > LCMA_COMBINE_L2_ON_CHIP || o.num_cus < 0 || o.peak_tflops < 0 || o.hbm_gbps < 0 ||
         o.bf16_ops_f16 < -1 || o.bf16_ops_f16 > 1 || !(o.classic_eff >= 0 && o.classic_eff <= 1) ||
         !(o.fused_eff >= 0 && o.fused_eff <= 1) || o.accuracy_optin < 0 || o.accuracy_optin > 1)
         return LCMA_E_INVALID;
@@ -803,7 +815,7 @@ lcma_status lcma_plan_info(lcma_plan_t p, lcma_algo* chosen, size_t* ws, double*
 
 lcma_status lcma_plan_estimate(lcma_plan_t p, lcma_algo algo, double* est)
 {
-    if (!p || !est || algo < LCMA_ALGO_CLASSIC || algo > LCMA_ALGO_L2)
+    if (!p || !est || enum_bits(&algo) < LCMA_ALGO_CLASSIC || enum_bits(&algo) > LCMA_ALGO_L2)
         return LCMA_E_INVALID;
     *est = p->est[algo];
     return LCMA_OK;
@@ -1287,7 +1299,7 @@ extern "C" {
 lcma_status gemm_classic(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const void* A, int64_t lda, const void* B,
                          int64_t ldb, void* C, int64_t ldc, void* stream)
 {
-    if (dt != LCMA_F16 && dt != LCMA_BF16)
+    if (enum_bits(&dt) != LCMA_F16 && enum_bits(&dt) != LCMA_BF16)
         return LCMA_E_INVALID;
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
         return LCMA_E_INVALID;
@@ -1341,6 +1353,29 @@ lcma_status lcma_gemm(lcma_plan_t p, const void* A, int64_t lda, const void* B, 
             return s;
     }
     return do_fused(p, A, lda, B, ldb, C, ldc, io, ws, st);
+}
+
+lcma_status lcma_measure_mfma(float* out, int32_t workgroups, int32_t iters, lcma_dtype dt, void* stream)
+{
+    if (!out || workgroups < 1 || workgroups > (1 << 16) || iters < 1 || iters > (1 << 24) ||
+        (enum_bits(&dt) != LCMA_F16 && enum_bits(&dt) != LCMA_BF16))
+        return LCMA_E_INVALID;
+    return hip_status(launch_ref_mfma(out, workgroups, iters, dt == LCMA_BF16, (hipStream_t)stream), "launch_ref_mfma");
+}
+
+lcma_status lcma_measure_copy(const void* src, void* dst, size_t bytes, void* stream)
+{
+    if (bytes == 0)
+        return LCMA_OK;
+    if (!src || !dst)
+        return LCMA_E_INVALID;
+    if ((uintptr_t)src % 16 || (uintptr_t)dst % 16 || bytes % 16)
+        return LCMA_E_UNSUPPORTED;
+    int P = 0;
+    if (query_cus(&P) != 0)
+        return LCMA_E_HIP;
+    // 64 workgroups per compute unit (measured best of 4..64 on MI355X)
+    return hip_status(launch_ref_copy(src, dst, (int64_t)(bytes / 16), 64 * P, (hipStream_t)stream), "launch_ref_copy");
 }
 
 lcma_status lcma_gemm_noalloc(lcma_plan_t p, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,

@@ -2642,7 +2642,92 @@ __global__ void __launch_bounds__(256) k_pad_copy(const u16* __restrict__ src, i
     }
 }
 
+// ------------------------------------------------------------------ machine references
+//
+// Measured ceilings the kernels above are compared against (the published
+// peaks are not what the chip holds under load): an MFMA loop and an HBM
+// stream copy.
+
+// Random half-precision operands in +-[0.5, 1): random sign and fraction,
+// fixed exponent (two values per 32-bit word).
+template <bool BF>
+__device__ __forceinline__ u32 ref_operand(u32& h)
+{
+    h ^= h << 13;
+    h ^= h >> 17;
+    h ^= h << 5;
+    return BF ? ((h & 0x807F807Fu) | 0x3F003F00u) : ((h & 0x83FF83FFu) | 0x38003800u);
+}
+
+// Eight waves per workgroup, each issuing `iters` rounds of 16 independent
+// 16x16x32 MFMAs on operands held in registers; one fp32 sum per thread is
+// written so nothing is optimised away.
+template <bool BF>
+__global__ void __launch_bounds__(512) k_ref_mfma(float* __restrict__ out, int iters)
+{
+    const u32 gid = blockIdx.x * 512u + threadIdx.x;
+    u32 h = gid * 2654435761u + 12345u;
+    u32x4 a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i] = u32x4{ref_operand<BF>(h), ref_operand<BF>(h), ref_operand<BF>(h), ref_operand<BF>(h)};
+        b[i] = u32x4{ref_operand<BF>(h), ref_operand<BF>(h), ref_operand<BF>(h), ref_operand<BF>(h)};
+    }
+    f32x4 acc[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            acc[j] = mfma<BF>(a[j & 3], b[j >> 2], acc[j]);
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        sum += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+    out[gid] = sum;
+}
+
+// dst = src: each workgroup copies one contiguous chunk of `per` 16-byte
+// chunks, four accesses in flight per lane, non-temporal stores (the copy is
+// not read back).  Measured faster than grid-stride loops and than torch's
+// device copy on MI355X.
+__global__ void __launch_bounds__(256) k_ref_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t n,
+                                                  int64_t per)
+{
+    const int64_t b = (int64_t)blockIdx.x * per;
+    const int64_t e = b + per < n ? b + per : n;
+    for (int64_t i = b + threadIdx.x; i < e; i += 4 * 256) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i + u * 256 < e)
+                v[u] = src[i + u * 256];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i + u * 256 < e)
+                __builtin_nontemporal_store(v[u], dst + i + u * 256);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_ref_mfma(float* out, int32_t workgroups, int32_t iters, int32_t bf16, hipStream_t st)
+{
+    if (bf16)
+        hipLaunchKernelGGL((k_ref_mfma<true>), dim3(workgroups), dim3(512), 0, st, out, iters);
+    else
+        hipLaunchKernelGGL((k_ref_mfma<false>), dim3(workgroups), dim3(512), 0, st, out, iters);
+    return hipGetLastError();
+}
+
+hipError_t launch_ref_copy(const void* src, void* dst, int64_t chunks, int32_t workgroups, hipStream_t st)
+{
+    const int64_t per = (chunks + workgroups - 1) / workgroups;
+    hipLaunchKernelGGL(k_ref_copy, dim3(workgroups), dim3(256), 0, st, (const u32x4*)src, (u32x4*)dst, chunks, per);
+    return hipGetLastError();
+}
 
 hipError_t launch_pad_copy(const void* src, int64_t lds, int64_t rows, int64_t cols, void* dst, int64_t ldd,
                            int64_t prows, int64_t pcols, hipStream_t st)

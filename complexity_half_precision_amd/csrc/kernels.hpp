@@ -159,6 +159,12 @@ hipError_t launch_fused(const FusedLaunch& L, hipStream_t stream);
 // Kernel product order used by the fused kernel (position -> product).
 void fused_order(int32_t levels, int8_t* order);
 
+// Machine references: `workgroups` x 8 waves each issuing iters x 16 MFMAs
+// (16x16x32, random operands) and writing one float per thread to out; a
+// copy of `chunks` 16-byte chunks from src to dst.
+hipError_t launch_ref_mfma(float* out, int32_t workgroups, int32_t iters, int32_t bf16, hipStream_t stream);
+hipError_t launch_ref_copy(const void* src, void* dst, int64_t chunks, int32_t workgroups, hipStream_t stream);
+
 // Size of the device-resident scratch array of the allocation-free entry
 // point (equal to LCMA_SCRATCH_BYTES in lcma.h).
 constexpr size_t kScratchBytes = (size_t)64 << 20;

@@ -336,6 +336,23 @@ lcma_status lcma_plan_schedule(lcma_plan_t plan, int32_t* items, int64_t cap, in
 lcma_status gemm_classic(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const void* A, int64_t lda,
                          const void* B, int64_t ldb, void* C, int64_t ldc, void* stream);
 
+/* Measured machine references, the ceilings the kernels are compared with
+ * beside the published peaks.
+ * lcma_measure_mfma: `workgroups` workgroups of 8 waves, each wave issuing
+ *   iters x 16 independent 16x16x32 MFMAs (dt operands, random values held
+ *   in registers, fp32 accumulate); out receives one float per thread
+ *   (workgroups * 512 floats, device memory).  Work per launch:
+ *   workgroups * 8 * iters * 16 * 16384 flops.  LCMA_E_INVALID for a NULL
+ *   out, workgroups outside 1..65536 or iters outside 1..2^24.
+ * lcma_measure_copy: dst = src over `bytes` (device memory, 16-byte aligned,
+ *   a multiple of 16 bytes: else LCMA_E_UNSUPPORTED); reads and writes each
+ *   byte once, so HBM traffic is 2 * bytes when both exceed the caches.
+ * Both only enqueue on `stream`.
+ * Source: [KP] "Roofline" (F <= min(F_max, I * B_max): the peaks the
+ * roofline is drawn against) and "Benchmark 纪律" (measure, do not assume). */
+lcma_status lcma_measure_mfma(float* out, int32_t workgroups, int32_t iters, lcma_dtype dt, void* stream);
+lcma_status lcma_measure_copy(const void* src, void* dst, size_t bytes, void* stream);
+
 /* Frees a plan (NULL is a no-op).  Plans own host memory only.
  * Source: none on the pages (plan lifetime is this library's interface). */
 void lcma_plan_destroy(lcma_plan_t plan);

@@ -52,9 +52,13 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-            build()
-        L = ctypes.CDLL(_LIB_PATH)
+        # ORACLE_LIBRARY may name another build of oracle.c (the sanitizer build)
+        path = os.environ.get("ORACLE_LIBRARY")
+        if not path:
+            path = _LIB_PATH
+            if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+                build()
+        L = ctypes.CDLL(path)
         i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
         L.oracle_f16_to_f64.restype = ctypes.c_double
         L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
@@ -81,6 +85,8 @@ def lib():
         L.oracle_lcma_eval.restype = i32
         L.oracle_combine_block.argtypes = [i32, i32, vp, i64, i64, vp, i64, vp, i32]
         L.oracle_combine_block.restype = i32
+        L.oracle_set_threads.argtypes = [i32]
+        L.oracle_max_threads.restype = i32
         _lib = L
     return _lib
 
@@ -91,6 +97,15 @@ def _p(a: np.ndarray):
 
 def _f64(a) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def set_threads(n: int) -> None:
+    """Host threads of the product loops (results do not depend on it)."""
+    lib().oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().oracle_max_threads())
 
 
 # --------------------------------------------------------------------------- encodings

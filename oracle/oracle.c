@@ -28,9 +28,23 @@
  * product counts).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Host threads the product loops use (timing the oracle on a given number of
+ * cores; no effect on any result: each element's summation order is fixed). */
+void oracle_set_threads(int n)
+{
+    if (n > 0)
+        omp_set_num_threads(n);
+}
+
+int oracle_max_threads(void)
+{
+    return omp_get_max_threads();
+}
 
 /* ------------------------------------------------------------------------ */
 /* Half-precision encodings, written from the format definitions.            */

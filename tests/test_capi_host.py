@@ -632,3 +632,14 @@ def test_binding_refuses_host_tensors_and_short_buffers():
         L.gemm_classic(A, A, A)
     with pytest.raises(ValueError, match="device tensor"):
         L.lcma_gemm_noalloc(p, A, A, A)
+
+
+def test_measurement_entry_points_check_arguments_first():
+    assert L._lib_measure_mfma(None, 1, 1, L.BF16, None) == L.E_INVALID
+    assert L._lib_measure_mfma(4096, 0, 1, L.BF16, None) == L.E_INVALID
+    assert L._lib_measure_mfma(4096, 1, 0, L.BF16, None) == L.E_INVALID
+    assert L._lib_measure_mfma(4096, 1, 1, 7, None) == L.E_INVALID
+    assert L._lib_measure_copy(None, None, 0, None) == L.OK            # nothing to copy
+    assert L._lib_measure_copy(None, 4096, 16, None) == L.E_INVALID
+    assert L._lib_measure_copy(4104, 8192, 16, None) == L.E_UNSUPPORTED   # misaligned source
+    assert L._lib_measure_copy(4096, 8192, 24, None) == L.E_UNSUPPORTED   # not a multiple of 16 bytes

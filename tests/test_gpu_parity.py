@@ -930,3 +930,19 @@ def test_graph_capture_replays_match_eager(algo, kw):
         L.lcma_gemm(plan, Ad, Bd, C, ws)
         torch.cuda.synchronize()
         assert torch.equal(C, eager), rep
+
+
+# ---------------------------------------------------------------- measurement references
+
+def test_measurement_references_run_and_copy_exactly():
+    say("measurement references")
+    n = (64 << 20) + 48                       # not a multiple of the chunking
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, device=DEV)
+    dst = torch.zeros_like(src)
+    L.lcma_measure_copy(src, dst)
+    out = torch.full((2 * 512,), float("nan"), dtype=torch.float32, device=DEV)
+    flops = L.lcma_measure_mfma(out, 2, 10, "bf16")
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    assert flops == 2 * 8 * 10 * 16 * 16384
+    assert torch.all(torch.isfinite(out))
