@@ -169,7 +169,9 @@ CLASSIC_SHAPES = [
     (1000, 1064, 2056),        # 128 x 128 tiles, long K (eight-wave kernel): edge tiles, K tail
     (1000, 1064, 2040),        # 128 x 128 tiles just below the long-K switch (four-wave kernel)
     (17, 1000, 520),           # streaming kernel (32-row A), N and K tails
-    (60, 2056, 1000),          # streaming kernel (64-row A), N and K tails
+    (60, 2056, 1000),          # streaming kernel (64-row A, 64-k stages), N and K tails
+    (33, 4104, 4104),          # 64-k stages: an odd stage count per wave and a k tail of 8
+    (64, 136, 72),             # one stage per wave at most, ragged N
 ]
 
 
@@ -183,7 +185,8 @@ def test_classic_matches_oracle(M, N, K, dtype):
 
 @pytest.mark.parametrize("dtype,dist", [("f16", "int2"), ("bf16", "int1")])
 @pytest.mark.parametrize("M,N,K", [(33, 40, 24), (130, 200, 96), (257, 136, 120), (512, 512, 256), (4100, 264, 64),
-                                   (1000, 1064, 256), (4096, 4104, 96), (48, 1000, 200)])
+                                   (1000, 1064, 256), (4096, 4104, 96), (48, 1000, 200), (64, 14336, 256),
+                                   (40, 1032, 248)])
 def test_classic_integer_inputs_are_exact(M, N, K, dtype, dist):
     say("classic exact", M, N, K, dtype)
     A, B, A64, B64 = gen(M, N, K, dtype, dist, seed=7)
