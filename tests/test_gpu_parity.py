@@ -171,6 +171,7 @@ CLASSIC_SHAPES = [
     (17, 1000, 520),           # streaming kernel (32-row A), N and K tails
     (60, 2056, 1000),          # streaming kernel (64-row A, 64-k stages), N and K tails
     (33, 4104, 4104),          # 64-k stages: an odd stage count per wave and a k tail of 8
+    (20, 1032, 1032),          # up to 32 rows, long K: 64-k stages on two waves, k tail of 8
     (64, 136, 72),             # one stage per wave at most, ragged N
 ]
 
