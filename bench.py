@@ -95,6 +95,15 @@ def main():
     import complexity_half_precision_amd as L
     import seeded_inputs as si
 
+    if args.copy_calib_mib:
+        # reference for the HBM byte counters: device copies of known size
+        src = torch.ones(args.copy_calib_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     if args.decode_only:
         def tc(fn, reps, warm):
             for _ in range(warm):
@@ -136,13 +145,6 @@ def main():
     C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
     flops = 2.0 * M * N * K
-    if args.copy_calib_mib:
-        src = torch.ones(args.copy_calib_mib << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
