@@ -412,9 +412,17 @@ def machine_refs(L, torch, time_calls):
     res["hbm_stream_gbps"] = round(2.0 * n / (t * 1e-3) / 1e9, 1)
     t = time_calls(lambda: dst.copy_(src), 10, 3)
     res["torch_copy_gbps"] = round(2.0 * n / (t * 1e-3) / 1e9, 1)
-    res["note"] = ("mfma: %d workgroups x 8 waves x %d x 16 MFMAs per launch; stream: %d bytes read and written"
-                   % (wg, iters, n))
-    del out, src, dst
+    del src, dst
+    # the vendor library's GEMM on the headline shape, as context for the classic kernel
+    g = torch.Generator(device="cuda").manual_seed(7)
+    a = (torch.randn(4096, 4096, device="cuda", generator=g) / 64).to(torch.bfloat16)
+    b = (torch.randn(4096, 4096, device="cuda", generator=g) / 64).to(torch.bfloat16)
+    c = torch.empty(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    t = time_calls(lambda: torch.matmul(a, b, out=c), 50, 10)
+    res["torch_matmul_4096_bf16_tflops"] = round(2.0 * 4096 ** 3 / (t * 1e-3) / 1e12, 1)
+    res["note"] = ("mfma: %d workgroups x 8 waves x %d x 16 MFMAs per launch; stream: %d bytes read and written; "
+                   "torch.matmul: the vendor BLAS on 4096^3 bfloat16, context only" % (wg, iters, n))
+    del out, a, b, c
     torch.cuda.empty_cache()
     return res
 

@@ -1921,12 +1921,14 @@ __device__ __forceinline__ void wait_tiles(int n)
         tiles::wait_vm0();
 }
 
-// All fragments of one stage (KSTEPS k-steps) and their MFMAs.
+// All fragments of one stage (KSTEPS k-steps) and their MFMAs, for the wave
+// tile whose origin is (row0, col0) in the stage (row0 a multiple of 32).
 template <class C, bool BF>
-__device__ __forceinline__ void ktile(const char* stage, int lane, f32x16 (&acc)[C::FM][C::FN])
+__device__ __forceinline__ void ktile(const char* stage, int lane, f32x16 (&acc)[C::FM][C::FN], u32 row0 = 0,
+                                      u32 col0 = 0)
 {
-    const char* sA = stage;
-    const char* sB = stage + C::A_BYTES;
+    const char* sA = stage + row0 * (u32)C::AROW;
+    const char* sB = stage + C::A_BYTES + col0 * 2u;
     const u32 m = lane & 31;
     const int g = lane >> 4, s = lane & 15;
     const u32 kr = 8 * (g >> 1) + (s >> 2);
@@ -1960,7 +1962,117 @@ __device__ __forceinline__ void ktile(const char* stage, int lane, f32x16 (&acc)
                 acc[i][j] = mfma<BF>(b[st][j], a[st][i], acc[i][j]);
 }
 
+// Shared-ring variant for 33..64 rows: the four waves load each 64-k stage
+// together (a quarter of its A rows and of its B rows each) into one ring of
+// NST stages, NST - 1 ahead, and after one barrier per stage each wave
+// multiplies its quarter of the 64 x BN output tile.  The MFMAs spread over
+// the four SIMDs, and a stage holds one copy of A's rows for all four waves.
+template <int NST_ = 5, int BN_ = 64>
+struct CCfg {
+    static constexpr int BM = 64, BN = BN_, BK = 64, MT = 32, NW = 4, NT = 256;
+    static constexpr int WM = 2, WN = 2, WTM = 32, WTN = BN / 2;   // wave w: rows 32 (w % 2), columns BN/2 (w / 2)
+    static constexpr int FM = 1, FN = WTN / 32;
+    static constexpr int KSTEPS = BK / 16;
+    using acc_t = f32x16;
+    static constexpr int NACC = 16;
+    static constexpr int NSTAGE = NST_, AHEAD = NST_ - 1;
+    static constexpr int AROW = BK * 2, BROW = BN * 2;
+    static constexpr int LPR = AROW / 16;
+    static constexpr int A_BYTES = BM * AROW, B_BYTES = BK * BROW;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int LDS = NSTAGE * STAGE;
+    static constexpr int A_PER = A_BYTES / 1024 / NW, B_PER = B_BYTES / 1024 / NW;   // per wave
+    static constexpr int PER = A_PER + B_PER;
+    static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "DMA granularity");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(PER * AHEAD < 64, "every load in flight stays within the 6-bit vmcnt");
+    static_assert(AHEAD >= 1, "prefetch depth");
+    __device__ static u32 a_swz(u32 m) { return (m >> 1) & 7u; }
+};
+
+// Wave `wave`'s share of the loads of k-tile s.k0 into `stage`: A rows
+// 16 wave .. 16 wave + 15 and B k-rows 16 wave .. 16 wave + 15 (rows, columns
+// and k beyond the operands read as zero).
+template <class C>
+__device__ __forceinline__ void dma_ktile_shared(char* stage, const tiles::TileSrc& s, int wave, int lane)
+{
+    const u32x4 ra = q4::rsrc_words(s.a + s.k0);
+    const u32x4 rb = q4::rsrc_words(s.b + (int64_t)s.k0 * s.ldb);
+    const int kleft = s.K - s.k0;
+    const u32 base = q4::lds_addr(stage);
+#pragma unroll
+    for (int i = 0; i < C::A_PER; ++i) {
+        const int ins = wave * C::A_PER + i;
+        const int r = ins * (64 / C::LPR) + lane / C::LPR;
+        const int k = ((lane % C::LPR) ^ (int)C::a_swz(r)) * 8;
+        const u32 off = ((r < s.a_rows) & (k < kleft)) ? (u32)(r * s.lda + k) * 2u : kOob;
+        q4::dma16(ra, off, base + ins * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_PER; ++i) {
+        const int ins = wave * C::B_PER + i;
+        const int byte = ins * 1024 + lane * 16;
+        const int r = byte / C::BROW;
+        const int n = ((byte % C::BROW) >> 4) * 8;
+        const u32 off = ((r < kleft) & (n < s.b_cols)) ? (u32)(r * s.ldb + n) * 2u : kOob;
+        q4::dma16(rb, off, base + C::A_BYTES + ins * 1024);
+    }
+}
+
 }  // namespace sk
+
+template <class C, bool BF>
+__global__ void __launch_bounds__(C::NT, 1)
+k_skinny_shared(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb, u16* __restrict__ Cm,
+                int64_t ldc, int M, int N, int K, int vec4)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % C::WM, wn = wave / C::WM;
+    const int n0 = blockIdx.x * C::BN;
+    const u16* Bb = B + n0;
+    const int nk = (K + C::BK - 1) / C::BK;
+    auto src = [&](int t) { return tiles::TileSrc{A, (int)lda, M, Bb, (int)ldb, N - n0, t * C::BK, K}; };
+    f32x16 acc[C::FM][C::FN];
+    zero_acc<C>(acc);
+#pragma unroll
+    for (int u = 0; u < C::AHEAD; ++u)
+        if (u < nk)
+            sk::dma_ktile_shared<C>(smem + u * C::STAGE, src(u), wave, lane);
+    // stage offsets of tile t (read) and of tile t + AHEAD (written), advanced
+    // by one stage per k-tile with wrap-around
+    int rd = 0, wr = C::AHEAD * C::STAGE;
+    for (int t = 0; t < nk; ++t) {
+        // this wave's loads of tile t landed (tiles up to min(t + AHEAD - 1,
+        // nk - 1) were issued); its fragment reads of tile t - 1 completed
+        q4::wait_tiles<C>(min(nk - 1 - t, C::AHEAD - 1));
+        tiles::wait_lgkm0();
+        // every wave's loads of tile t landed, and every wave is done with
+        // tile t - 1's stage, which takes tile t + AHEAD
+        tiles::bar();
+        if (t + C::AHEAD < nk)
+            sk::dma_ktile_shared<C>(smem + wr, src(t + C::AHEAD), wave, lane);
+        sk::ktile<C, BF>(smem + rd, lane, acc, (u32)(wm * C::WTM), (u32)(wn * C::WTN));
+        rd = rd + C::STAGE == C::LDS ? 0 : rd + C::STAGE;
+        wr = wr + C::STAGE == C::LDS ? 0 : wr + C::STAGE;
+    }
+    if (vec4)
+        store_c<C, BF, true>(acc, Cm + n0, ldc, M, N - n0, wm, wn, lane);
+    else
+        store_c<C, BF, false>(acc, Cm + n0, ldc, M, N - n0, wm, wn, lane);
+}
+
+template <class C, bool BF>
+hipError_t launch_skinny_shared_t(const ClassicLaunch& L, hipStream_t st)
+{
+    const int gx = (L.N + C::BN - 1) / C::BN;
+    if (gx == 0 || L.M == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((k_skinny_shared<C, BF>), dim3((unsigned)gx), dim3(C::NT), 0, st, (const u16*)L.A, L.lda,
+                       (const u16*)L.B, L.ldb, (u16*)L.C, L.ldc, L.M, L.N, L.K, L.vec4);
+    return hipGetLastError();
+}
 
 template <class C, bool BF>
 __global__ void __launch_bounds__(C::NT, 1)
@@ -2786,12 +2898,13 @@ hipError_t launch_classic(const ClassicLaunch& L, hipStream_t st)
         if (L.vec && L.M <= 32)
             return L.bf16 ? launch_skinny_t<sk::SCfg<32>, true>(L, st) : launch_skinny_t<sk::SCfg<32>, false>(L, st);
         // 33..64 rows: 64-k stages (A rows of 128 bytes, half the L2 requests
-        // per byte of A of 32-k stages) on two waves, 3 stages ahead each
-        // (16 loads per stage; the 6-bit vmcnt bounds the depth): measured
-        // 29.3 us against 35.8 us at 64 x 14336 x 4096
+        // per byte of A of 32-k stages) in one 5-stage ring shared by the four
+        // waves: measured 28.4 us at 64 x 14336 x 4096 against 29.3 us for a
+        // private 4-stage ring per wave on two waves; rings of 3, 6..10 stages
+        // and 128-column strips (112 workgroups, 37 us) were slower
         if (L.vec && L.M <= 64)
-            return L.bf16 ? launch_skinny_t<sk::SCfg<64, 64, 2, 4>, true>(L, st)
-                          : launch_skinny_t<sk::SCfg<64, 64, 2, 4>, false>(L, st);
+            return L.bf16 ? launch_skinny_shared_t<sk::CCfg<>, true>(L, st)
+                          : launch_skinny_shared_t<sk::CCfg<>, false>(L, st);
         return launch_classic_c<Cfg32>(L, st);
     }
 }
