@@ -247,24 +247,6 @@ def test_lcma_rejects_uneven_split():
         oracle.lcma(A, B, oracle.strassen(), 1)
 
 
-def test_operand_rounding_worked_example():
-    """Hand-worked 2x2 scalar case of Strassen with binary16 combined operands.
-
-    A = diag(1, 2^-11), B = I.  Exact: C = diag(1, 2^-11).  The only combined
-    operand that is not representable is A11 + A22 = 1 + 2^-11, the midpoint
-    between 1 and 1 + 2^-10, which rounds to even, i.e. to 1.  Then
-    P1 = 1 * 2 = 2, P2 = 2^-11, P3 = -1, P4 = -2^-11, P5 = 1, P6 = -1,
-    P7 = -2^-11, so C11 = P1 + P4 - P5 + P7 = 1 - 2^-10, C12 = P3 + P5 = 0,
-    C21 = P2 + P4 = 0, C22 = P1 - P2 + P3 + P6 = -2^-11.
-    """
-    A = np.array([[1.0, 0.0], [0.0, 2.0 ** -11]])
-    B = np.eye(2)
-    C, _ = oracle.lcma(A, B, oracle.strassen(), 1, round_operands="f16")
-    assert C.tolist() == [[1 - 2.0 ** -10, 0.0], [0.0, -2.0 ** -11]]
-    Ce, _ = oracle.lcma(A, B, oracle.strassen(), 1)
-    assert Ce.tolist() == [[1.0, 0.0], [0.0, 2.0 ** -11]]
-
-
 def test_operand_rounding_is_identity_when_combinations_are_representable():
     rng = np.random.default_rng(9)
     A = rng.integers(-2, 3, (16, 24)).astype(np.float64)
