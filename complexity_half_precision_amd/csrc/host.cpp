@@ -360,6 +360,8 @@ struct lcma_plan_s {
     int64_t gMb, gKb, gNb;
     int8_t gU[kGenMaxRank * kGenMaxBlocks], gV[kGenMaxRank * kGenMaxBlocks], gW[kGenMaxRank * kGenMaxBlocks];
     int64_t offGA, offGB, offGC;
+    int gGroup;            // all products in one persistent launch (enough 256 x 256 positions)
+    int gPackA;            // ... with the combined A operands tile-packed (whole 256 x 256 tiles)
     // padded plan: a forced LCMA on a shape that does not split evenly runs
     // `inner` on zero-padded Mp x Kp and Kp x Np copies of A and B in the
     // workspace and crops its Mp x Np product into C
@@ -724,6 +726,11 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         p->offGC = off;
         off = align_up(off + (int64_t)gen.ms * gen.ns * p->gMb * p->gNb * 4, 256);
         p->ws_bytes = (size_t)off;
+        // Enough 256 x 256 output positions for a round of the compute units:
+        // every product in one persistent launch.  Whole tiles there: the
+        // pre-pass writes the A operands in the engine's stage layout.
+        p->gGroup = ((p->gMb + 255) / 256) * ((p->gNb + 255) / 256) >= p->P;
+        p->gPackA = p->gGroup && p->gMb % kPackRows == 0 && p->gNb % 256 == 0 && p->gKb % kPackCols == 0;
     } else if (p->levels > 0) {
         const int L = p->levels;
         p->op_bf16 = op_bf16_for(L);
@@ -838,7 +845,7 @@ lcma_status lcma_plan_operand(lcma_plan_t p, int32_t side, int32_t r, int64_t* o
         if (offset)
             *offset = side == 0 ? p->offGA + (int64_t)r * p->gMb * p->gKb * 2 : p->offGB + (int64_t)r * p->gKb * p->gNb * 2;
         if (ld)
-            *ld = side == 0 ? p->gKb : p->gNb;
+            *ld = side == 0 ? (p->gPackA ? 0 : p->gKb) : p->gNb;
         if (dtype)
             *dtype = p->op_bf16 ? LCMA_BF16 : LCMA_F16;
         return LCMA_OK;
@@ -1126,8 +1133,10 @@ lcma_status do_gen_prepass(const lcma_plan_s* p, const void* A, int64_t lda, con
     L.nblocks = p->gms * p->gks;
     memcpy(L.coef, p->gU, sizeof L.coef);
     L.out = (char*)ws + p->offGA; L.ldo = p->gKb; L.stride = p->gMb * p->gKb;
+    L.packed = p->gPackA;
     if (hip_status(launch_gen_prepass(L, st), "launch_gen_prepass") != LCMA_OK)
         return LCMA_E_HIP;
+    L.packed = 0;
     // side B: blocks (k, j) of Kb x Nb
     L.X = B; L.ldx = ldb; L.rows = (int32_t)p->gKb; L.cols = (int32_t)p->gNb; L.bcols = p->gns;
     L.nblocks = p->gks * p->gns;
@@ -1234,11 +1243,9 @@ lcma_status do_gen_products(const lcma_plan_s* p, void* C, int64_t ldc, void* ws
         if (uses[o] == 0)
             return LCMA_E_BAD_DESCRIPTOR;
     }
-    // Enough 256 x 256 output positions for a round of the compute units:
-    // every product in one persistent launch, each position owned by one
+    // Every product in one persistent launch, each position owned by one
     // workgroup throughout.
-    const int64_t pos256 = ((p->gMb + 255) / 256) * ((p->gNb + 255) / 256);
-    if (pos256 >= p->P) {
+    if (p->gGroup) {
         GenGroupLaunch G;
         memset(&G, 0, sizeof G);
         G.A0 = (const char*)ws + p->offGA; G.strideA = p->gMb * p->gKb;
@@ -1247,6 +1254,7 @@ lcma_status do_gen_products(const lcma_plan_s* p, void* C, int64_t ldc, void* ws
         G.op_bf16 = p->op_bf16; G.out_bf16 = p->dt == LCMA_BF16; G.P = p->P;
         G.nout = nout; G.ncols = p->gns;
         G.acc = acc; G.C = C; G.ldc = ldc;
+        G.packed_a = p->gPackA;
         gen_group_runs(p, nout, &G);
         return hip_status(launch_gen_group(G, st), "launch_gen_group");
     }

@@ -786,17 +786,23 @@ struct Group {
     u32 b[C::B_PER];
 };
 
-template <class C>
+// PK: A is tile-packed (see dma_group), so a wave's A loads read its
+// A_PER kilobytes of the k-tile's block in order, lane l at 16 l.
+template <class C, bool PK = false>
 __device__ __forceinline__ Group<C> group_offsets(const tiles::TileSrc& s, int xw, int lane)
 {
     static_assert(C::A_PER == C::B_PER && (C::A_PER == 1 || C::A_PER == 2 || C::A_PER == 4), "loads per group");
     Group<C> g;
 #pragma unroll
     for (int i = 0; i < C::A_PER; ++i) {
-        const int ins = xw * C::A_PER + i;
-        const int r = ins * 16 + (lane >> 2);
-        const int k = ((lane & 3) ^ (int)C::a_swz(r)) * 8;
-        g.a[i] = (u32)(r * s.lda + k) * 2u - 1024u * i;
+        if constexpr (PK) {
+            g.a[i] = (u32)(xw * C::A_PER * 1024 + lane * 16);
+        } else {
+            const int ins = xw * C::A_PER + i;
+            const int r = ins * 16 + (lane >> 2);
+            const int k = ((lane & 3) ^ (int)C::a_swz(r)) * 8;
+            g.a[i] = (u32)(r * s.lda + k) * 2u - 1024u * i;
+        }
     }
 #pragma unroll
     for (int i = 0; i < C::B_PER; ++i) {
@@ -834,12 +840,16 @@ __device__ __forceinline__ void dma16xN(u32x4 rs, const u32 (&off)[N], u32 lds)
 }
 
 // Wave xw's A loads (side 0) or B loads (side 1) of k-tile source s into `stage`.
-template <class C>
+// PK: A is tile-packed: s.a is the first row of a BM-row tile row, whose
+// k-tile t is one contiguous block of BM x BK elements at s.a + t BK BM, laid
+// out byte for byte as the stage's A part (rows of BK elements, 16-byte
+// chunks XOR-swizzled by row), so every load reads whole cache lines.
+template <class C, bool PK = false>
 __device__ __forceinline__ void dma_group(char* stage, const tiles::TileSrc& s, const Group<C>& g, int xw, int side)
 {
     const u32 base = lds_addr(stage);
     if (side == 0)
-        dma16xN<C::A_PER>(rsrc_words(s.a + s.k0), g.a, base + xw * C::A_PER * 1024);
+        dma16xN<C::A_PER>(rsrc_words(PK ? s.a + (int64_t)s.k0 * C::BM : s.a + s.k0), g.a, base + xw * C::A_PER * 1024);
     else
         dma16xN<C::B_PER>(rsrc_words(s.b + (int64_t)s.k0 * s.ldb), g.b, base + C::A_BYTES + xw * C::B_PER * 1024);
 }
@@ -1192,7 +1202,7 @@ __device__ __forceinline__ void read_b(const char* stage, const Addr<C>& ad, int
 // last MFMA that uses the current one.  B is double-buffered (Bc -> Bn), its
 // reads slotted after the first FN MFMAs.  With PRE the loads of tile t+3
 // follow in later slots.
-template <class C, bool BF, bool NEXT, bool PRE, bool EDGE, bool GROUPED>
+template <class C, bool BF, bool NEXT, bool PRE, bool EDGE, bool GROUPED, bool PK = false>
 __device__ __forceinline__ void ktile(u32x4 (&Af)[C::FM], const u32x4 (&Bc)[C::FN], u32x4 (&Bn)[C::FN],
                                       const char* nxt, char* pre, const tiles::TileSrc& ps, const q4::Group<C>& go,
                                       const Addr<C>& ad, int wave, int lane, f32x4 (&acc)[C::FM][C::FN])
@@ -1217,9 +1227,9 @@ __device__ __forceinline__ void ktile(u32x4 (&Af)[C::FM], const u32x4 (&Bc)[C::F
                 const int k = y / 2;
                 if constexpr (GROUPED) {
                     if (k == 0)
-                        q4::dma_group<C>(pre, ps, go, wave, 0);
+                        q4::dma_group<C, PK>(pre, ps, go, wave, 0);
                     else if (k == C::PER / 2)
-                        q4::dma_group<C>(pre, ps, go, wave, 1);
+                        q4::dma_group<C, PK>(pre, ps, go, wave, 1);
                 } else {
                     q4::dma_one<C, EDGE>(pre, ps, wave, lane, k);
                 }
@@ -1235,35 +1245,38 @@ __device__ __forceinline__ void ktile(u32x4 (&Af)[C::FM], const u32x4 (&Bc)[C::F
 // grouped-load offsets are recomputed whenever a source's strides differ from
 // the last ones (a uniform branch, taken once per product switch at most),
 // and src(0) is not called ahead of the k-tiles (cursor sources may be used).
-template <class C, bool BF, bool EDGE, bool GROUPED, bool RESTRIDE = false, class SrcFn, class AfterFn>
+// PK: A is tile-packed (q4::dma_group); grouped loads only.
+template <class C, bool BF, bool EDGE, bool GROUPED, bool RESTRIDE = false, bool PK = false, class SrcFn,
+          class AfterFn>
 __device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, AfterFn after, int wave, int lane,
                                          const Addr<C>& ad, f32x4 (&acc)[C::FM][C::FN])
 {
     static_assert(C::AHEAD >= 3 && C::NSTAGE == C::AHEAD + 1, "stage reuse below: tile t + AHEAD goes where tile t - 1 was");
     static_assert(!(GROUPED && EDGE), "grouped loads carry no bounds");
     static_assert(!RESTRIDE || GROUPED, "restriding applies to grouped loads");
+    static_assert(!PK || (GROUPED && !RESTRIDE), "packed A takes the grouped loads of one stride");
     u32x4 Af[C::FM], B0[C::FN], B1[C::FN];
     q4::Group<C> go;
     int go_lda = -1, go_ldb = -1;
     auto regroup = [&](const tiles::TileSrc& ps) {
         if constexpr (RESTRIDE) {
             if (ps.lda != go_lda || ps.ldb != go_ldb) {
-                go = q4::group_offsets<C>(ps, wave, lane);
+                go = q4::group_offsets<C, PK>(ps, wave, lane);
                 go_lda = ps.lda;
                 go_ldb = ps.ldb;
             }
         }
     };
     if constexpr (GROUPED && !RESTRIDE)
-        go = q4::group_offsets<C>(src(0), wave, lane);
+        go = q4::group_offsets<C, PK>(src(0), wave, lane);
 #pragma unroll
     for (int t = 0; t < C::AHEAD; ++t) {
         if (t < nk) {
             if constexpr (GROUPED) {
                 const tiles::TileSrc ps = src(t);
                 regroup(ps);
-                q4::dma_group<C>(smem + t * C::STAGE, ps, go, wave, 0);
-                q4::dma_group<C>(smem + t * C::STAGE, ps, go, wave, 1);
+                q4::dma_group<C, PK>(smem + t * C::STAGE, ps, go, wave, 0);
+                q4::dma_group<C, PK>(smem + t * C::STAGE, ps, go, wave, 1);
             } else {
                 q4::dma_tile<C, EDGE>(smem + t * C::STAGE, src(t), wave, lane);
             }
@@ -1291,7 +1304,7 @@ __device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, AfterFn 
         __builtin_amdgcn_sched_barrier(0);
         const tiles::TileSrc ps = src(t + C::AHEAD);
         regroup(ps);
-        ktile<C, BF, true, true, EDGE, GROUPED>(Af, Bc, Bn, smem + ((t + 1) % C::NSTAGE) * C::STAGE,
+        ktile<C, BF, true, true, EDGE, GROUPED, PK>(Af, Bc, Bn, smem + ((t + 1) % C::NSTAGE) * C::STAGE,
                                                 smem + ((t + C::AHEAD) % C::NSTAGE) * C::STAGE, ps, go, ad, wave,
                                                 lane, acc);
         __builtin_amdgcn_sched_barrier(0);
@@ -1323,8 +1336,8 @@ __device__ __forceinline__ void run_tile(char* smem, int nk, SrcFn src, AfterFn 
                 char* pre = smem + ((t + C::AHEAD) % C::NSTAGE) * C::STAGE;
                 if constexpr (GROUPED) {
                     regroup(ps);
-                    q4::dma_group<C>(pre, ps, go, wave, 0);
-                    q4::dma_group<C>(pre, ps, go, wave, 1);
+                    q4::dma_group<C, PK>(pre, ps, go, wave, 0);
+                    q4::dma_group<C, PK>(pre, ps, go, wave, 1);
                 } else {
                     q4::dma_tile<C, EDGE>(pre, ps, wave, lane);
                 }
@@ -1713,10 +1726,12 @@ static_assert(sizeof(GenGroupParams) <= 4096, "kernel argument segment");
 
 // EDGE: some position is a partial tile or K is not a multiple of 32 (then
 // every position takes the bounds-checked loads: one K-loop form per kernel
-// keeps the persistent loops within the register budget).
-template <class C, bool BF, bool CBF, bool EDGE>
+// keeps the persistent loops within the register budget).  PK: the combined
+// A operands are tile-packed by the pre-pass (q4::dma_group); interior only.
+template <class C, bool BF, bool CBF, bool EDGE, bool PK>
 __global__ void __launch_bounds__(C::NT, 1) k_gen_group_m16(const GenGroupParams gp)
 {
+    static_assert(!(PK && EDGE), "packed operands cover whole tiles");
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_ALLOC];
     const int tid = threadIdx.x, lane0 = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1752,7 +1767,7 @@ __global__ void __launch_bounds__(C::NT, 1) k_gen_group_m16(const GenGroupParams
                         acc[i][j] = -acc[i][j];
             }
             __syncthreads();   // every wave is done reading the ring of the previous product
-            m16::run_tile<C, BF, EDGE, !EDGE>(smem, nk, src, none, wave, lane, ad, acc);
+            m16::run_tile<C, BF, EDGE, !EDGE, false, PK>(smem, nk, src, none, wave, lane, ad, acc);
             for (int o = 0; o < gp.nout; ++o) {
                 const int mode = gp.mode[run * kGenMaxBlocks + o];
                 if (mode == kOuterNone)
@@ -1794,11 +1809,15 @@ hipError_t launch_gen_group_t(const GenGroupLaunch& L, hipStream_t st)
         gp.carry[i] = L.carry[i];
     }
     const bool edge = L.M % C::BM != 0 || L.N % C::BN != 0 || L.K % C::BK != 0;
+    if (L.packed_a && (edge || C::BM != kPackRows || C::BK != kPackCols))
+        return hipErrorInvalidValue;    // the packed layout needs whole tiles of this shape
     const dim3 grid((unsigned)std::min(items, L.P));
     if (edge)
-        hipLaunchKernelGGL((k_gen_group_m16<C, BF, CBF, true>), grid, dim3(C::NT), 0, st, gp);
+        hipLaunchKernelGGL((k_gen_group_m16<C, BF, CBF, true, false>), grid, dim3(C::NT), 0, st, gp);
+    else if (L.packed_a)
+        hipLaunchKernelGGL((k_gen_group_m16<C, BF, CBF, false, true>), grid, dim3(C::NT), 0, st, gp);
     else
-        hipLaunchKernelGGL((k_gen_group_m16<C, BF, CBF, false>), grid, dim3(C::NT), 0, st, gp);
+        hipLaunchKernelGGL((k_gen_group_m16<C, BF, CBF, false, false>), grid, dim3(C::NT), 0, st, gp);
     return hipGetLastError();
 }
 
@@ -2164,7 +2183,8 @@ struct GenPrepassParams {
 // One thread per 8-element chunk position of a block: it reads that chunk of
 // every block once (at most kGenMaxBlocks, held in registers), then writes
 // the chunk of every combined operand, each summed in fp32 and rounded once.
-template <bool IBF, bool OBF>
+// PK: the operands are written tile-packed (GenPrepassLaunch::packed).
+template <bool IBF, bool OBF, bool PK>
 __global__ void __launch_bounds__(256) k_gen_prepass(const GenPrepassParams gp)
 {
     const int cpr = gp.cols / 8;                       // chunks per row
@@ -2181,7 +2201,16 @@ __global__ void __launch_bounds__(256) k_gen_prepass(const GenPrepassParams gp)
                                                    (int64_t)bc * gp.cols + col);
         }
     }
-    u16* out = gp.out + (int64_t)row * gp.ldo + col;
+    u16* out;
+    if constexpr (PK) {
+        // tile row row / 256, k-tile col / 32, row in the tile rr, chunk
+        // (col / 8) % 4 at position chunk ^ ((rr >> 1) & 3) of its row
+        const int rr = row % kPackRows, ch = (col / 8) % 4;
+        out = gp.out + ((int64_t)(row / kPackRows) * gp.cols + (col / kPackCols) * kPackCols) * kPackRows +
+              rr * kPackCols + (ch ^ ((rr >> 1) & 3)) * 8;
+    } else {
+        out = gp.out + (int64_t)row * gp.ldo + col;
+    }
     for (int r = 0; r < gp.rank; ++r) {
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
@@ -2223,7 +2252,14 @@ hipError_t launch_gen_prepass_t(const GenPrepassLaunch& L, hipStream_t st)
     gp.out = (u16*)L.out;
     gp.ldo = L.ldo;
     gp.stride = L.stride;
-    hipLaunchKernelGGL((k_gen_prepass<IBF, OBF>), dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, gp);
+    const dim3 grid((unsigned)((chunks + 255) / 256));
+    if (L.packed) {
+        if (L.rows % kPackRows != 0 || L.cols % kPackCols != 0)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_gen_prepass<IBF, OBF, true>), grid, dim3(256), 0, st, gp);
+    } else {
+        hipLaunchKernelGGL((k_gen_prepass<IBF, OBF, false>), grid, dim3(256), 0, st, gp);
+    }
     return hipGetLastError();
 }
 

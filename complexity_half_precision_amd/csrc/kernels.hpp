@@ -103,12 +103,21 @@ constexpr int kGenMaxBlocks = 16;   // blocks per side (ms*ks, ks*ns, ms*ns)
 // Combined operands of one side: out_r = sum_b coef[r][b] * X_b (fp32 sum,
 // one rounding), for every product r.  Block b of X sits at block row
 // b / bcols, block column b % bcols, each rows x cols.
+// Tile-packed operand layout (packed = 1; rows a multiple of kPackRows,
+// cols of kPackCols; ldo unused): tile row tr and k-tile t form one
+// contiguous block of kPackRows x kPackCols elements at element
+// (tr * cols + t * kPackCols) * kPackRows; row rr of the block holds its four
+// 8-element chunks c at positions c ^ ((rr >> 1) & 3).  That is the A part of
+// an LDS stage of the 256 x 256 engine byte for byte, so the persistent
+// product kernel reads it with whole-cache-line loads.
+constexpr int kPackRows = 256, kPackCols = 32;
 struct GenPrepassLaunch {
     const void* X; int64_t ldx;
     int32_t rows, cols, bcols, nblocks, rank;
     int8_t coef[kGenMaxRank * kGenMaxBlocks];
     void* out; int64_t ldo, stride;        // out_r at out + r * stride (elements)
     int32_t in_bf16, op_bf16;
+    int32_t packed;                        // 1: write out_r tile-packed (above)
 };
 hipError_t launch_gen_prepass(const GenPrepassLaunch& L, hipStream_t stream);
 
@@ -134,7 +143,7 @@ hipError_t launch_gen_product(const GenProductLaunch& L, hipStream_t stream);
 // B0 + r * strideB (K x N, ld N); fp32 block o at acc + o * M * N (ld N);
 // block o of C at row (o / ncols) * M, column (o % ncols) * N.
 struct GenGroupLaunch {
-    const void* A0; int64_t strideA;
+    const void* A0; int64_t strideA;       // packed_a = 1: the A operands are tile-packed (GenPrepassLaunch)
     const void* B0; int64_t strideB;
     int32_t M, N, K, R, op_bf16, out_bf16, P, nout, ncols;
     float* acc;
@@ -148,6 +157,7 @@ struct GenGroupLaunch {
     int8_t mode[kGenMaxRank * kGenMaxBlocks];
     int8_t prod[kGenMaxRank];
     int8_t carry[kGenMaxRank];
+    int32_t packed_a;
 };
 hipError_t launch_gen_group(const GenGroupLaunch& L, hipStream_t stream);
 

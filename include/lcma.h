@@ -116,8 +116,9 @@ typedef enum {
                                  W[r][i,j] * H_r into fp32 output blocks in the workspace (H_r is never stored)
                                  and the last contributor to a block rounds it into C.  Blocks with enough
                                  256 x 256 positions for every compute unit run all products in one persistent
-                                 launch (each position owned by one workgroup); smaller ones run one launch
-                                 per product.  The path for descriptions that are not a built-in scheme, and
+                                 launch (each position owned by one workgroup; on whole tiles the pre-pass
+                                 writes the A operands tile-packed, see lcma_plan_operand); smaller ones run
+                                 one launch per product.  The path for descriptions that are not a built-in scheme, and
                                  the unfused form of the built-in one */
     LCMA_COMBINE_L2_ON_CHIP = 4 /* two levels only (pre-pass as above): all 49 products of an output coordinate
                                  run in one group on one workgroup and the 16 outputs accumulate on chip.  The
@@ -308,6 +309,12 @@ lcma_status lcma_fused(lcma_plan_t plan, const void* A, int64_t lda, const void*
  * (N/ns) matrix).  *offset_bytes receives its byte offset and *ld its
  * leading dimension; *offset_bytes = -1 when the operand is a single input
  * block read in place (not copied).  *dtype receives the operand type.
+ * *ld = 0 marks a tile-packed A operand: an unfused plan whose products run
+ * in one persistent launch on whole 256 x 256 tiles (Mb and Nb multiples of
+ * 256, Kb of 32) stores each combined A operand as consecutive blocks of
+ * 256 rows x 32 columns, block (tr, t) (rows 256 tr.., columns 32 t..) at
+ * element (tr * Kb + 32 t) * 256; row rr of a block is 32 elements whose four
+ * 8-element chunks c sit at positions c ^ ((rr >> 1) & 3).
  * A padded plan reports the operands of its padded product (blocks of the
  * padded shape).  LCMA_E_INVALID for a plan that combines at load (it
  * writes no combined operand). */

@@ -310,6 +310,21 @@ def test_workspace_layout_of_one_level_plan():
     assert all(b - a >= blk for a, b in zip(starts, starts[1:]))
 
 
+def test_unfused_plan_packs_its_a_operands_only_on_whole_tiles():
+    # one persistent launch on whole 256 x 256 tiles: every combined A operand
+    # is tile-packed (ld 0), the B operands stay row-major
+    for (M, N, K), packed in (((8192, 8192, 512), True), ((8192, 8192, 528), False), ((8192, 8000, 512), False),
+                              ((2048, 2048, 512), False)):
+        p = L.lcma_plan_ex(M, N, K, "bf16", force="l1", combine="unfused", num_cus=CUS)
+        assert L.lcma_plan_info(p)[0] == "l1"
+        for r in range(7):
+            off_a, ld_a, _ = L.lcma_plan_operand(p, 0, r)
+            off_b, ld_b, _ = L.lcma_plan_operand(p, 1, r)
+            assert off_a >= 0 and off_b >= 0
+            assert ld_a == (0 if packed else K // 2), (M, N, K, ld_a)
+            assert ld_b == N // 2
+
+
 def test_bf16_two_level_writes_every_operand_in_binary16():
     p = L.lcma_plan_ex(4096, 4096, 4096, "bf16", force="l2", num_cus=CUS)
     for r in range(49):

@@ -333,6 +333,45 @@ def test_prepass_operands_are_rne_of_the_exact_combination():
                 assert fp32_exact.mean() > 0.99
 
 
+def _unpack_a(x, rows, cols):
+    """Row-major view of a tile-packed A operand (the layout lcma_plan_operand
+    states for ld 0): block (tr, t) of 256 rows x 32 columns at element
+    (tr * cols + 32 t) * 256, chunk c of block row rr at position c ^ ((rr >> 1) & 3)."""
+    t = x.reshape(rows // 256, cols // 32, 256, 4, 8)
+    rr = np.arange(256)[:, None]
+    pos = np.arange(4)[None, :]
+    out = np.empty_like(t)
+    out[:, :, rr, pos ^ ((rr >> 1) & 3), :] = t[:, :, rr, pos, :]
+    return out.transpose(0, 2, 1, 3, 4).reshape(rows, cols)
+
+
+def test_unfused_prepass_writes_tile_packed_a_operands():
+    # blocks of 4096 x 4096 on whole 256 x 256 tiles: the A operands are
+    # tile-packed (ld 0), the B operands row-major; both are the RNE of the
+    # exact combination, bit for bit where the fp32 sum is exact
+    say("unfused packed operands")
+    M, N, K = 8192, 8192, 512
+    A, B, A64, B64 = gen(M, N, K, "bf16", "normal_sqrtk", seed=12)
+    plan = L.lcma_plan_ex(M, N, K, "bf16", force="l1", combine="unfused")
+    ws = L.workspace_for(plan)
+    L.lcma_prepass(plan, A.to(DEV), B.to(DEV), ws)
+    torch.cuda.synchronize()
+    d = oracle.strassen()
+    for side, X, T in ((0, A64, d.U), (1, B64, d.V)):
+        rows, cols = (M // 2, K // 2) if side == 0 else (K // 2, N // 2)
+        for r in range(7):
+            off, ld, odt = L.lcma_plan_operand(plan, side, r)
+            assert off >= 0 and ld == (0 if side == 0 else cols)
+            odt = "f16" if odt == L.F16 else "bf16"
+            got = ws[off:off + rows * cols * 2].cpu().view(torch.int16).numpy().view(np.uint16)
+            got = _unpack_a(got, rows, cols) if side == 0 else got.reshape(rows, cols)
+            exact = oracle.combine_block(X, T[r], 2, 2)
+            want = oracle.encode(odt, exact)
+            fp32_exact = np.float32(exact).astype(np.float64) == exact
+            assert np.array_equal(got[fp32_exact], want[fp32_exact]), (side, r)
+            assert fp32_exact.mean() > 0.99
+
+
 @pytest.mark.parametrize("M,N,K,dtype", [(400, 272, 144, "f16"), (600, 528, 512, "bf16")])
 def test_l1_ragged_group_tiles(M, N, K, dtype):
     # quadrants that do not fill whole 128 x 128 group tiles (and a k tail in
