@@ -5,7 +5,9 @@
 //                    MFMAs, direct-to-LDS loads.
 //  * k_classic_q4 -- the same for 128 x 128 tiles: 4 waves (one per SIMD) of
 //                    64 x 64 on 32x32x16 MFMAs.
-//  * k_skinny     -- M <= 64 products, built to stream B from HBM.
+//  * k_skinny     -- M <= 32 products, built to stream B from HBM (private
+//                    direct-to-LDS rings per wave, no barrier in the K loop).
+//  * k_skinny_shared -- 33 <= M <= 64: one ring shared by four waves.
 //  * k_classic    -- register-staged tiles for the other shapes and for
 //                    operands that are not 16-byte aligned.
 //  * k_prepass    -- combine-A/B pass: every combined operand of an LCMA scheme,
@@ -28,8 +30,9 @@
 //                    into fp32 output blocks and rounding into C at the last
 //                    product feeding a block.  With a round of 256 x 256
 //                    positions, one persistent launch runs every product per
-//                    position (k_gen_group_m16); otherwise one GEMM launch per
-//                    product (128 x 128 tiles on the four-wave engine).
+//                    position (k_gen_group_m16, reading tile-packed A operands
+//                    on whole tiles); otherwise one GEMM launch per product
+//                    (128 x 128 tiles on the four-wave engine).
 //  * k_fused<2>   -- all 49 products of one output coordinate on one
 //                    workgroup (16 outputs on chip, 64 x 64 tiles) on the
 //                    register-staged path.
