@@ -7,7 +7,9 @@
 //                    64 x 64 on 32x32x16 MFMAs.
 //  * k_skinny     -- M <= 32 products, built to stream B from HBM (private
 //                    direct-to-LDS rings per wave, no barrier in the K loop).
-//  * k_skinny_shared -- 33 <= M <= 64: one ring shared by four waves.
+//  * k_skinny_shared -- M <= 64 products: one ring shared by the waves of a
+//                    workgroup (33..64 rows; up to 32 rows when B has many
+//                    column strips).
 //  * k_classic    -- register-staged tiles for the other shapes and for
 //                    operands that are not 16-byte aligned.
 //  * k_prepass    -- combine-A/B pass: every combined operand of an LCMA scheme,
@@ -1984,16 +1986,18 @@ __device__ __forceinline__ void ktile(const char* stage, int lane, f32x16 (&acc)
                 acc[i][j] = mfma<BF>(b[st][j], a[st][i], acc[i][j]);
 }
 
-// Shared-ring variant for 33..64 rows: the four waves load each 64-k stage
-// together (a quarter of its A rows and of its B rows each) into one ring of
-// NST stages, NST - 1 ahead, and after one barrier per stage each wave
-// multiplies its quarter of the 64 x BN output tile.  The MFMAs spread over
-// the four SIMDs, and a stage holds one copy of A's rows for all four waves.
-template <int NST_ = 5, int BN_ = 64>
+// Shared-ring variant: the waves (four for 64 rows, two for 32) load each
+// 64-k stage together (an equal share of its A rows and of its B rows each)
+// into one ring of NST stages, NST - 1 ahead, and after one barrier per stage
+// each wave multiplies its 32 x BN/2 part of the BM x BN output tile.  The
+// MFMAs spread over the SIMDs, and a stage holds one copy of A's rows for all
+// the waves.
+template <int NST_ = 5, int BN_ = 64, int BM_ = 64>
 struct CCfg {
-    static constexpr int BM = 64, BN = BN_, BK = 64, MT = 32, NW = 4, NT = 256;
-    static constexpr int WM = 2, WN = 2, WTM = 32, WTN = BN / 2;   // wave w: rows 32 (w % 2), columns BN/2 (w / 2)
+    static constexpr int BM = BM_, BN = BN_, BK = 64, MT = 32, WM = BM / 32, NW = 2 * WM, NT = NW * 64;
+    static constexpr int WN = 2, WTM = 32, WTN = BN / 2;   // wave w: rows 32 (w % WM), columns BN/2 (w / WM)
     static constexpr int FM = 1, FN = WTN / 32;
+    static_assert(BM == 32 || BM == 64, "one or two 32-row wave tiles");
     static constexpr int KSTEPS = BK / 16;
     using acc_t = f32x16;
     static constexpr int NACC = 16;
@@ -2927,10 +2931,16 @@ hipError_t launch_classic(const ClassicLaunch& L, hipStream_t st)
             return L.bf16 ? launch_classic_q4_t<QC128, true>(L, st) : launch_classic_q4_t<QC128, false>(L, st);
         return launch_classic_c<Cfg128>(L, st);
     default:
-        // M <= 64 with 16-byte aligned operands: the streaming kernel
-        // up to 32 rows: 64-k stages on two waves, 4 ahead, for long K (decode
-        // shapes: 1 x 14336 x 4096 bf16 25.2 -> 23.0 us, 32 rows 28.7 -> 25.4 us);
-        // 32-k stages on four waves for short K (fewer stages to share out)
+        // M <= 64 with 16-byte aligned operands: the streaming kernels.
+        // Up to 32 rows and long K: 64-k stages on two waves.  With more than
+        // 128 column strips the waves share one 5-stage ring (1 x 14336 x 4096
+        // bf16: 23.1 -> 21.5 us, 16 rows 24.0 -> 22.9 us, 2-7% faster from 160
+        // strips up); with fewer strips each compute unit streams more of B and
+        // a private 5-stage ring per wave, 4 ahead, keeps more in flight (2-7%
+        // faster up to 128 strips).  Short K: 32-k stages on four waves.
+        if (L.vec && L.M <= 32 && L.K >= 1024 && (L.N + 63) / 64 > 128)
+            return L.bf16 ? launch_skinny_shared_t<sk::CCfg<5, 64, 32>, true>(L, st)
+                          : launch_skinny_shared_t<sk::CCfg<5, 64, 32>, false>(L, st);
         if (L.vec && L.M <= 32 && L.K >= 1024)
             return L.bf16 ? launch_skinny_t<sk::SCfg<32, 64, 2, 5>, true>(L, st)
                           : launch_skinny_t<sk::SCfg<32, 64, 2, 5>, false>(L, st);

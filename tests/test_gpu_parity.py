@@ -181,6 +181,7 @@ CLASSIC_SHAPES = [
     (33, 4104, 4104),          # 64-k stages: an odd stage count per wave and a k tail of 8
     (20, 1032, 1032),          # up to 32 rows, long K: 64-k stages on two waves, k tail of 8
     (64, 136, 72),             # one stage per wave at most, ragged N
+    (17, 8264, 1032),          # up to 32 rows, more than 128 column strips: the shared ring, all tails ragged
 ]
 
 
@@ -274,6 +275,7 @@ def test_classic_is_deterministic():
     (4096, 4096, 512, "int2"),      # 256 x 256 tiles, interior grouped loads, 16 k-tiles: the steady-state loop
     (1024, 1024, 2048, "int1"),     # 128 x 128 eight-wave kernel for long K (7 k-tiles in flight), interior
     (1000, 1064, 2048, "int1"),     # the same with edge tiles
+    (24, 8200, 1024, "int1"),       # streaming kernel with a ring shared by its waves (more than 128 strips)
 ])
 def test_classic_integer_inputs_exact_through_the_full_size_loops(M, N, K, dist):
     # |C| <= 2048 (2 * 2 * 512, or 2048 * 1): every partial sum and the result
