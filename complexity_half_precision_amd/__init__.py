@@ -327,6 +327,28 @@ def lcma_gemm(plan: Plan, A, B, C, workspace=None, workspace_bytes=None, stream=
                      _stream(stream)), "lcma_gemm")
 
 
+def lcma_gemm_prepared(plan: Plan, A, B, C, workspace=None, workspace_bytes=None, stream=None, lda=None, ldb=None,
+                       ldc=None):
+    """Checks the arguments of one lcma_gemm call once and returns a function
+    that enqueues exactly that call (same buffers, leading dimensions,
+    workspace and stream, the current one at preparation when `stream` is
+    None) with no per-call checks: for loops that repeat a call on fixed
+    buffers, where the checks would take as long as a short kernel.  The
+    returned function holds references to the tensors."""
+    ws_bytes = workspace_bytes if workspace_bytes is not None else (
+        0 if workspace is None or isinstance(workspace, int) else workspace.numel() * workspace.element_size())
+    lda, ldb, ldc = lda or _ld(A, plan.K), ldb or _ld(B, plan.N), ldc or _ld(C, plan.N)
+    dev = _check_call(plan, A, lda, B, ldb, C, ldc, stream, workspace=workspace)
+    _check_workspace(workspace, ws_bytes, dev)
+    args = (plan.handle, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(workspace), ws_bytes, _stream(stream))
+    held = (plan, A, B, C, workspace)
+
+    def call() -> None:
+        _check(_lib_gemm(*args), "lcma_gemm")
+    call.held = held
+    return call
+
+
 def lcma_gemm_noalloc(plan: Plan, A, B, C, stream=None, lda=None, ldb=None, ldc=None) -> None:
     """lcma_gemm with the workspace taken from the library's static device scratch
     array (no allocation; plans with a workspace above SCRATCH_BYTES are refused)."""

@@ -647,6 +647,8 @@ def test_binding_refuses_host_tensors_and_short_buffers():
         L.gemm_classic(A, A, A)
     with pytest.raises(ValueError, match="device tensor"):
         L.lcma_gemm_noalloc(p, A, A, A)
+    with pytest.raises(ValueError, match="device tensor"):
+        L.lcma_gemm_prepared(p, A, A, A)        # checked once, when the call is prepared
 
 
 def test_measurement_entry_points_check_arguments_first():

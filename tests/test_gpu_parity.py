@@ -946,6 +946,26 @@ def test_square_16384_bf16_sampled():
     assert max(res["l1"], res["l1_fused"], res["l2"]) <= 4 * res["classic"]
 
 
+def test_prepared_calls_equal_lcma_gemm():
+    # a call prepared once (arguments checked once) enqueues the same work as
+    # lcma_gemm: bitwise equal results, repeatable, for a streaming-kernel plan
+    # and a one-level plan with a workspace
+    say("prepared calls")
+    for (M, N, K, algo) in ((16, 14336, 4096, "classic"), (512, 512, 512, "l1")):
+        A, B, A64, B64 = gen(M, N, K, "bf16", "normal_sqrtk", seed=44)
+        Ad, Bd = A.to(DEV), B.to(DEV)
+        plan = L.lcma_plan_ex(M, N, K, "bf16", force=algo)
+        ws = L.workspace_for(plan)
+        C1 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        C2 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+        L.lcma_gemm(plan, Ad, Bd, C1, ws)
+        call = L.lcma_gemm_prepared(plan, Ad, Bd, C2, ws)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        assert torch.equal(C1, C2), (M, N, K, algo)
+
+
 # ---------------------------------------------------------------- graph capture
 
 @pytest.mark.parametrize("algo,kw", [("classic", {}), ("l1", {"split": "all"}), ("l2", {})])
