@@ -13,7 +13,9 @@ and LCMA rates, the pre-pass bandwidth, the roofline of the dominant kernel
 and the CPU oracle's rate on a bounded sample.
 
 Also in the default line: the measured machine references (an MFMA loop
-and an HBM stream kernel of the library), the 16384^3 comparison of classic,
+and an HBM stream kernel of the library; socket power and the shader clock
+held while the classic kernel, the MFMA loop and the vendor GEMM each run
+back to back, from amd-smi), the 16384^3 comparison of classic,
 one level (unfused and fused) and two levels, cold-cache and server-mode
 timings, the cold pre-pass bandwidth, and the build's targets with whether
 they are met.
@@ -360,6 +362,12 @@ def main():
         out["machine"] = machine_refs(L, torch, time_calls)
         roofline["measured_peak_tflops"] = out["machine"]["mfma_bf16_tflops"]
         roofline["frac_of_measured_peak"] = round(roofline["achieved"] / out["machine"]["mfma_bf16_tflops"], 4)
+        out["machine"]["power"] = power_and_clock(L, torch)
+        held = out["machine"]["power"].get("classic_4096_bf16", {})
+        if "gfx_clock_mhz" in held:
+            roofline["held_clock_mhz"] = held["gfx_clock_mhz"]
+            roofline["socket_power_w"] = held["socket_power_w"]
+            roofline["frac_at_held_clock"] = round(roofline["achieved"] / held["peak_at_clock_tflops"], 4)
         if not args.no_large:
             out["large"] = large_square(L, si, torch, time_calls, time_cold)
         out["square_512_f16"] = small_square(L, si, torch, time_calls)
@@ -418,11 +426,89 @@ def machine_refs(L, torch, time_calls):
     a = (torch.randn(4096, 4096, device="cuda", generator=g) / 64).to(torch.bfloat16)
     b = (torch.randn(4096, 4096, device="cuda", generator=g) / 64).to(torch.bfloat16)
     c = torch.empty(4096, 4096, device="cuda", dtype=torch.bfloat16)
-    t = time_calls(lambda: torch.matmul(a, b, out=c), 50, 10)
+    t = time_calls(lambda: torch.matmul(a, b, out=c), 200, 200)     # its first calls run slower: warm it up well
     res["torch_matmul_4096_bf16_tflops"] = round(2.0 * 4096 ** 3 / (t * 1e-3) / 1e12, 1)
     res["note"] = ("mfma: %d workgroups x 8 waves x %d x 16 MFMAs per launch; stream: %d bytes read and written; "
                    "torch.matmul: the vendor BLAS on 4096^3 bfloat16, context only" % (wg, iters, n))
     del out, a, b, c
+    torch.cuda.empty_cache()
+    return res
+
+
+def power_and_clock(L, torch, seconds=2.0):
+    """Socket power and shader clock while one workload at a time runs back to
+    back for `seconds`: the classic kernel on a 4096^3 bfloat16 product, the
+    library's MFMA loop and the vendor GEMM.  amd-smi (a child process)
+    samples every ~0.1 s; the medians over the second half of each run are
+    reported (its readings update about once a second).  peak_at_clock =
+    1024 SIMDs x 1024 flop/clk x the clock held; frac_at_clock = achieved /
+    peak_at_clock."""
+    import shutil
+    import subprocess
+    import threading
+    import time
+    smi = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    if not os.path.exists(smi):
+        return {"note": "amd-smi not found"}
+
+    def sample():
+        r = subprocess.run([smi, "metric", "-p", "-c", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)["gpu_data"][0]
+        clk = [v["clk"]["value"] for k, v in d["clock"].items() if k.startswith("gfx_")]
+        return float(d["power"]["socket_power"]["value"]), sum(clk) / len(clk)
+
+    def run(fn, flops_per_call, batch):
+        samples, stop = [], threading.Event()
+
+        def loop():
+            while not stop.is_set():
+                try:
+                    samples.append((time.time(),) + sample())
+                except (OSError, ValueError, KeyError, IndexError, subprocess.SubprocessError):
+                    time.sleep(0.1)
+        for _ in range(batch):
+            fn()
+        torch.cuda.synchronize()
+        th = threading.Thread(target=loop, daemon=True)
+        t0 = time.time()
+        th.start()
+        calls = 0
+        while time.time() - t0 < seconds:
+            for _ in range(batch):
+                fn()
+            calls += batch
+            torch.cuda.synchronize()
+        el = time.time() - t0
+        stop.set()
+        th.join()
+        late = sorted(x for x in samples if x[0] >= t0 + seconds / 2) or samples
+        if not late:
+            return {"note": "no amd-smi samples"}
+        pw = sorted(x[1] for x in late)[len(late) // 2]
+        ck = sorted(x[2] for x in late)[len(late) // 2]
+        achieved = calls * flops_per_call / el / 1e12
+        peak = 1024 * 1024 * ck * 1e6 / 1e12
+        return {"tflops": round(achieved, 1), "socket_power_w": pw, "gfx_clock_mhz": round(ck, 1),
+                "peak_at_clock_tflops": round(peak, 1), "frac_at_clock": round(achieved / peak, 4),
+                "samples": len(late)}
+
+    n = 4096
+    g = torch.Generator(device="cuda").manual_seed(7)
+    a = (torch.randn(n, n, device="cuda", generator=g) / 64).to(torch.bfloat16)
+    b = (torch.randn(n, n, device="cuda", generator=g) / 64).to(torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    plan = L.lcma_plan(n, n, n, "bf16")
+    res = {"classic_4096_bf16": run(L.lcma_gemm_prepared(plan, a, b, c, L.workspace_for(plan)), 2.0 * n ** 3, 100)}
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(2 * cus * 512, dtype=torch.float32, device="cuda")
+    mflops = [0.0]
+
+    def mfma():
+        mflops[0] = L.lcma_measure_mfma(out, 2 * cus, 2000, "bf16")
+    mfma()
+    res["mfma_loop_bf16"] = run(mfma, mflops[0], 2)
+    res["torch_matmul_4096_bf16"] = run(lambda: torch.matmul(a, b, out=c), 2.0 * n ** 3, 100)
+    del a, b, c, out
     torch.cuda.empty_cache()
     return res
 
