@@ -11,12 +11,15 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
+#include <random>
 #include <vector>
 
 #include "kernels.hpp"
@@ -339,6 +342,7 @@ struct lcma_plan_s {
     int op_bf16;           // combined-operand type (LCMA)
     int write_all;         // pre-pass copies single-block operands too
     int classic_tile;
+    int split;             // classic, split_pays(M, N, K): K split over two workgroups per strip
     int P;
     Geo geo;
     SchedParams sp;
@@ -700,6 +704,10 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     p->levels = chosen == LCMA_ALGO_L1 ? 1 : chosen == LCMA_ALGO_L2 ? 2 : 0;
     p->ws_bytes = 0;
     p->n_slots = 0;
+    // decode-shaped classic plans: the workspace of the K-split streaming kernel
+    p->split = p->levels == 0 && split_pays(M, N, K);
+    if (p->split)
+        p->ws_bytes = (size_t)split_ws_bytes(N);
     p->unfused = p->levels == 1 && (unfused || l1_unfused_auto);
     if (p->unfused) {
         p->op_bf16 = op_bf16_for(1);
@@ -923,8 +931,28 @@ lcma_status check_io(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     return LCMA_OK;
 }
 
+// Identifier of one call of the K-split kernel: even, non-zero and never
+// repeated within the process; a random per-process offset keeps it from
+// matching a tag that another process may have left in reused memory.
+uint64_t next_call_id()
+{
+    static const uint64_t salt = [] {
+        uint64_t x = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+        try {
+            std::random_device rd;
+            x ^= ((uint64_t)rd() << 32) ^ (uint64_t)rd();
+        } catch (...) {
+        }
+        return x;
+    }();
+    static std::atomic<uint64_t> n{0};
+    const uint64_t id = (salt + 2 * n.fetch_add(1, std::memory_order_relaxed)) & ~(uint64_t)1;
+    return id != 0 ? id : 2;
+}
+
 lcma_status run_classic(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const void* A, int64_t lda, const void* B,
-                        int64_t ldb, void* C, int64_t ldc, const Io& io, int tile, int P, hipStream_t st)
+                        int64_t ldb, void* C, int64_t ldc, const Io& io, int tile, int P, hipStream_t st,
+                        void* split_ws = nullptr)
 {
     if (M == 0 || N == 0)
         return LCMA_OK;
@@ -932,6 +960,8 @@ lcma_status run_classic(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const vo
     L.A = A; L.lda = lda; L.B = B; L.ldb = ldb; L.C = C; L.ldc = ldc;
     L.M = (int32_t)M; L.N = (int32_t)N; L.K = (int32_t)K;
     L.bf16 = dt == LCMA_BF16; L.vec = io.vec; L.vec4 = io.vec4; L.tile = tile; L.P = P;
+    L.split_ws = split_ws;
+    L.split_id = split_ws ? next_call_id() : 0;
     return hip_status(launch_classic(L, st), "launch_classic");
 }
 
@@ -1343,9 +1373,12 @@ lcma_status lcma_gemm(lcma_plan_t p, const void* A, int64_t lda, const void* B, 
     if (p->levels == 0) {
         Io io;
         lcma_status s = check_io(p->M, p->N, p->K, A, lda, B, ldb, C, ldc, &io);
+        if (s == LCMA_OK)
+            s = check_ws(p, ws, ws_bytes);
         if (s != LCMA_OK)
             return s;
-        return run_classic(p->M, p->N, p->K, p->dt, A, lda, B, ldb, C, ldc, io, p->classic_tile, p->P, st);
+        return run_classic(p->M, p->N, p->K, p->dt, A, lda, B, ldb, C, ldc, io, p->classic_tile, p->P, st,
+                           p->split ? ws : nullptr);
     }
     Io io;
     lcma_status s = check_lcma_call(p, A, lda, B, ldb, C, ldc, ws, ws_bytes, true, &io);

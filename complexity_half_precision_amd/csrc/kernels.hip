@@ -2100,6 +2100,120 @@ hipError_t launch_skinny_shared_t(const ClassicLaunch& L, hipStream_t st)
     return hipGetLastError();
 }
 
+// K split for 33..64 rows: the two workgroups of a 128-column strip take one
+// half of K each (on one XCD: blocks 16 (s / 8) + s % 8 and that + 8), so
+// each reads half as many bytes of A per byte of B as the unsplit 64-column
+// kernel, whose time grows with the A bytes re-read by every workgroup.  The
+// K loop is k_skinny_shared's.  Each half then writes its fp32 partial tile
+// to the workspace, and thread 0 swaps the strip's 64-bit arrival tag for its
+// own (call id | half) with one agent-scope acquire-release atomic.  Finding
+// the other half's tag of the same call means the other partial is complete:
+// this workgroup adds it, clears the tag and rounds the sum into C.  A stale
+// tag (an earlier call, or whatever a fresh workspace holds) never carries
+// this call's id, and the cleared tag lets a replayed graph (same id) start
+// clean.  fp32 addition commutes, so the result does not depend on which
+// half arrives last.
+template <class C, bool BF>
+__global__ void __launch_bounds__(C::NT, 1)
+k_skinny_split(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb, u16* __restrict__ Cm,
+               int64_t ldc, int M, int N, int K, int kh, int vec4, float* __restrict__ part, uint64_t* tags,
+               uint64_t id)
+{
+    static_assert(C::BN == kSplitCols && C::BM == 64, "strip shape of the workspace layout");
+    constexpr int PF4 = C::FM * C::FN * (C::NACC / 4);     // float4 per thread in a partial tile
+    static_assert((int64_t)PF4 * C::NT * 16 == kSplitPartBytes, "partial tile size");
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+    __shared__ int sh_last;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % C::WM, wn = wave / C::WM;
+    const int b = blockIdx.x;
+    const int strip = (b / 16) * 8 + b % 8, half = (b / 8) % 2;
+    const int n0 = strip * C::BN;
+    if (n0 >= N)
+        return;                     // the grid covers whole groups of 8 strips
+    const int kb = half * kh, klen = max(0, min(K - kb, kh));
+    const u16* Ah = A + kb;
+    const u16* Bh = B + (int64_t)kb * ldb + n0;
+    const int nk = (klen + C::BK - 1) / C::BK;
+    auto src = [&](int t) { return tiles::TileSrc{Ah, (int)lda, M, Bh, (int)ldb, N - n0, t * C::BK, klen}; };
+    f32x16 acc[C::FM][C::FN];
+    zero_acc<C>(acc);
+#pragma unroll
+    for (int u = 0; u < C::AHEAD; ++u)
+        if (u < nk)
+            sk::dma_ktile_shared<C>(smem + u * C::STAGE, src(u), wave, lane);
+    int rd = 0, wr = C::AHEAD * C::STAGE;
+    for (int t = 0; t < nk; ++t) {
+        q4::wait_tiles<C>(min(nk - 1 - t, C::AHEAD - 1));
+        tiles::wait_lgkm0();
+        tiles::bar();
+        if (t + C::AHEAD < nk)
+            sk::dma_ktile_shared<C>(smem + wr, src(t + C::AHEAD), wave, lane);
+        sk::ktile<C, BF>(smem + rd, lane, acc, (u32)(wm * C::WTM), (u32)(wn * C::WTN));
+        rd = rd + C::STAGE == C::LDS ? 0 : rd + C::STAGE;
+        wr = wr + C::STAGE == C::LDS ? 0 : wr + C::STAGE;
+    }
+    f32x4* mine = reinterpret_cast<f32x4*>(part) + (int64_t)(strip * 2 + half) * PF4 * C::NT;
+    const f32x4* other = reinterpret_cast<const f32x4*>(part) + (int64_t)(strip * 2 + 1 - half) * PF4 * C::NT;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int g = 0; g < C::NACC / 4; ++g)
+                mine[(int64_t)((i * C::FN + j) * (C::NACC / 4) + g) * C::NT + tid] =
+                    f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+    // Every wave's partial stores have reached the L2 of its XCD; thread 0's
+    // agent-scope acquire-release swap writes it back once for the workgroup
+    // (and, for the second half to arrive, invalidates before the reads).
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const uint64_t old = __hip_atomic_exchange(tags + strip, id | (uint64_t)half, __ATOMIC_ACQ_REL,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+        sh_last = old == (id | (uint64_t)(1 - half));
+    }
+    __syncthreads();
+    if (!sh_last)
+        return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int g = 0; g < C::NACC / 4; ++g) {
+                const f32x4 v = __builtin_nontemporal_load(other + (int64_t)((i * C::FN + j) * (C::NACC / 4) + g) * C::NT + tid);
+                acc[i][j][4 * g] += v.x;
+                acc[i][j][4 * g + 1] += v.y;
+                acc[i][j][4 * g + 2] += v.z;
+                acc[i][j][4 * g + 3] += v.w;
+            }
+    if (tid == 0)
+        __hip_atomic_store(tags + strip, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (vec4)
+        store_c<C, BF, true>(acc, Cm + n0, ldc, M, N - n0, wm, wn, lane);
+    else
+        store_c<C, BF, false>(acc, Cm + n0, ldc, M, N - n0, wm, wn, lane);
+}
+
+template <class C, bool BF>
+hipError_t launch_skinny_split_t(const ClassicLaunch& L, hipStream_t st)
+{
+    const int strips = (L.N + C::BN - 1) / C::BN;
+    if (strips == 0 || L.M == 0)
+        return hipSuccess;
+    if (L.split_id == 0 || (L.split_id & 1) != 0 || ((uintptr_t)L.split_ws % 256) != 0)
+        return hipErrorInvalidValue;
+    const int kh = ((L.K + 1) / 2 + C::BK - 1) / C::BK * C::BK;
+    char* ws = (char*)L.split_ws;
+    hipLaunchKernelGGL((k_skinny_split<C, BF>), dim3((unsigned)((strips + 7) / 8 * 16)), dim3(C::NT), 0, st,
+                       (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, (u16*)L.C, L.ldc, L.M, L.N, L.K, kh, L.vec4,
+                       (float*)ws, (uint64_t*)(ws + split_tag_offset(L.N)), L.split_id);
+    return hipGetLastError();
+}
+
 template <class C, bool BF>
 __global__ void __launch_bounds__(C::NT, 1)
 k_skinny(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb, u16* __restrict__ Cm,
@@ -2946,6 +3060,11 @@ hipError_t launch_classic(const ClassicLaunch& L, hipStream_t st)
                           : launch_skinny_t<sk::SCfg<32, 64, 2, 5>, false>(L, st);
         if (L.vec && L.M <= 32)
             return L.bf16 ? launch_skinny_t<sk::SCfg<32>, true>(L, st) : launch_skinny_t<sk::SCfg<32>, false>(L, st);
+        // 33..64 rows with a workspace for the K split (classic plans):
+        // 128-column strips, one half of K per workgroup
+        if (L.vec && L.M > 32 && L.M <= 64 && L.split_ws)
+            return L.bf16 ? launch_skinny_split_t<sk::CCfg<5, kSplitCols>, true>(L, st)
+                          : launch_skinny_split_t<sk::CCfg<5, kSplitCols>, false>(L, st);
         // 33..64 rows: 64-k stages (A rows of 128 bytes, half the L2 requests
         // per byte of A of 32-k stages) in one 5-stage ring shared by the four
         // waves: measured 28.4 us at 64 x 14336 x 4096 against 29.3 us for a

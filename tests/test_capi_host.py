@@ -325,6 +325,22 @@ def test_unfused_plan_packs_its_a_operands_only_on_whole_tiles():
             assert ld_b == N // 2
 
 
+def test_decode_shaped_classic_plans_take_the_k_split_workspace():
+    # 33..64 rows with long K (K >= 8192 and N <= 8192, or K >= 10240): two
+    # workgroups per 128-column strip, each an fp32 partial tile of 64 x 128
+    # (32 KiB), then one 8-byte tag per strip
+    for (M, N, K), strips in (((64, 4096, 14336), 32), ((33, 8192, 8192), 64), ((48, 104, 8200), 1),
+                              ((64, 14336, 10240), 112)):
+        p = L.lcma_plan_ex(M, N, K, "bf16", force="classic", num_cus=CUS)
+        algo, ws, _ = L.lcma_plan_info(p)
+        assert algo == "classic"
+        assert ws == -(-(strips * 2 * 32768 + strips * 8) // 256) * 256, (M, N, K, ws)
+    for M, N, K in ((32, 4096, 14336), (65, 4096, 14336), (64, 14336, 4096), (64, 8200, 8192), (64, 4096, 8184),
+                    (1, 8, 8)):
+        p = L.lcma_plan_ex(M, N, K, "bf16", force="classic", num_cus=CUS)
+        assert L.lcma_plan_info(p)[1] == 0, (M, N, K)
+
+
 def test_bf16_two_level_writes_every_operand_in_binary16():
     p = L.lcma_plan_ex(4096, 4096, 4096, "bf16", force="l2", num_cus=CUS)
     for r in range(49):

@@ -468,6 +468,84 @@ def test_padded_lcma_matches_oracle(algo, M, N, K, dtype, dist):
         check_scheme(C, A64, B64, dtype, algo, e_c, C_ref)
 
 
+@pytest.mark.parametrize("M,N,K,dtype", [(64, 4096, 14336, "bf16"), (33, 8200, 10248, "f16"), (48, 1032, 8192, "bf16"),
+                                       (57, 136, 8200, "f16")])
+def test_decode_k_split_matches_oracle(M, N, K, dtype):
+    # classic plans of 33..64 rows with long K: two workgroups per 128-column
+    # strip, one half of K each, partials exchanged through the workspace
+    # (ragged rows, columns and k; one strip and many)
+    say("decode K split", M, N, K, dtype)
+    A, B, A64, B64 = gen(M, N, K, dtype, "uniform" if dtype == "f16" else "normal_sqrtk", seed=61)
+    plan = L.lcma_plan_ex(M, N, K, dtype, force="classic")
+    assert L.lcma_plan_info(plan)[1] > 0
+    check_float(planned(A, B, "classic"), A64, B64, dtype)
+
+
+def test_decode_k_split_integer_inputs_are_exact():
+    # {-1, 0, 1} inputs: every partial sum is an exact fp32 integer, and the
+    # products stay within binary16's exact integers (checked below)
+    say("decode K split exact")
+    A, B, A64, B64 = gen(64, 4104, 8200, "f16", "int1", seed=62)
+    assert np.abs(oracle.gemm(A64, B64)).max() <= 2048
+    check_exact(planned(A, B, "classic"), A64, B64, "f16")
+
+
+def test_decode_k_split_any_workspace_contents_and_repeated_calls():
+    # the exchange needs no cleared workspace: random initial bytes, then
+    # calls with other inputs on the same workspace, then the first inputs
+    # again (bit for bit the first result)
+    say("decode K split workspace reuse")
+    M, N, K = 64, 4104, 8192
+    plan = L.lcma_plan_ex(M, N, K, "bf16", force="classic")
+    ws = L.workspace_for(plan)
+    ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device=DEV))
+    outs = []
+    for seed in (71, 72, 71):
+        A, B, A64, B64 = gen(M, N, K, "bf16", "normal_sqrtk", seed=seed)
+        C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+        L.lcma_gemm(plan, A.to(DEV), B.to(DEV), C, ws)
+        torch.cuda.synchronize()
+        check_float(C.cpu(), A64, B64, "bf16")
+        outs.append(si.bits(C.cpu()))
+    assert np.array_equal(outs[0], outs[2])
+
+
+def test_decode_k_split_graph_replays_with_new_inputs():
+    # a captured call keeps its call identifier; the second arrival clears
+    # each strip's tag, so every replay pairs its own halves: each replay,
+    # after the inputs change in place, equals the eager product
+    say("decode K split graph")
+    M, N, K = 48, 4104, 8200
+    plan = L.lcma_plan_ex(M, N, K, "bf16", force="classic")
+    ws = L.workspace_for(plan)
+    Ad = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    Bd = torch.empty((K, N), dtype=torch.bfloat16, device=DEV)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    A, B, _, _ = gen(M, N, K, "bf16", "normal_sqrtk", seed=80)
+    Ad.copy_(A.to(DEV)); Bd.copy_(B.to(DEV))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        L.lcma_gemm(plan, Ad, Bd, C, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.lcma_gemm(plan, Ad, Bd, C, ws)
+    for seed in (81, 82, 83):
+        A, B, A64, B64 = gen(M, N, K, "bf16", "normal_sqrtk", seed=seed)
+        Ad.copy_(A.to(DEV)); Bd.copy_(B.to(DEV))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = si.bits(C.cpu())
+        C2 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        L.lcma_gemm(plan, Ad, Bd, C2, L.workspace_for(plan))
+        torch.cuda.synchronize()
+        assert np.array_equal(got, si.bits(C2.cpu())), seed
+        check_float(C.cpu(), A64, B64, "bf16")
+
+
 @pytest.mark.parametrize("M,N,K,dtype,dist", [(300, 522, 1000, "f16", "uniform"), (257, 13, 64, "bf16", "normal_sqrtk"),
                                               (1, 14337, 4096, "bf16", "decode"), (1000, 1064, 2050, "bf16", "normal_sqrtk"),
                                               (513, 264, 519, "f16", "int2")])

@@ -22,6 +22,7 @@ CASES = [
     ("l2", (1024, 1024, 1024), (512, 512, 512), "bf16", dict(force="l2")),
     ("l1 unfused", (1024, 1024, 1024), (512, 512, 256), "f16", dict(force="l1", combine="unfused")),
     ("l1 padded", (1000, 1032, 520), (333, 250, 210), "f16", dict(force="l1")),
+    ("classic, K split", (64, 4096, 14336), (40, 4104, 8200), "bf16", dict(force="classic")),
 ]
 
 
