@@ -342,7 +342,7 @@ struct lcma_plan_s {
     int op_bf16;           // combined-operand type (LCMA)
     int write_all;         // pre-pass copies single-block operands too
     int classic_tile;
-    int split;             // classic, split_pays(M, N, K): K split over two workgroups per strip
+    int split_s;           // classic: workgroups per strip of the K-split kernel (0: none), split_pieces()
     int P;
     Geo geo;
     SchedParams sp;
@@ -457,6 +457,30 @@ lcma_status lcma_desc_validate(const lcma_desc* d)
         return LCMA_E_BAD_DESCRIPTOR;
     return LCMA_OK;
 }
+
+namespace {
+
+// Workgroups per 128-column strip of the K-split kernel for 33..64 rows, 0
+// for none.  Measured on MI355X (64 rows, bfloat16, S in 0, 2, 4, 8): each
+// split workgroup writes its XCD's L2 back once for the exchange, which costs
+// more the more workgroups split, so S = 4 pays only with few strips and
+// S = 8 never (64 x 4096 x 14336: 80.1 us unsplit, 62.5 with S = 2, 45.6
+// with 4, 57.0 with 8; 64 x 14336 x 4096: 28.0 unsplit, 35.5 with S = 2).
+int split_pieces(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 32 || M > 64)
+        return 0;
+    const int64_t strips = split_strips(N);
+    if (strips <= 16)
+        return K >= 4096 ? 4 : 0;
+    if (strips <= 32)
+        return K >= 8192 ? 4 : 0;
+    if (strips <= 64)
+        return K >= 14336 ? 4 : K >= 8192 ? 2 : 0;
+    return K >= 10240 ? 2 : 0;
+}
+
+}  // namespace
 
 lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const lcma_desc* desc,
                          lcma_algo force, const lcma_options* opts, lcma_plan_t* out)
@@ -705,9 +729,9 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     p->ws_bytes = 0;
     p->n_slots = 0;
     // decode-shaped classic plans: the workspace of the K-split streaming kernel
-    p->split = p->levels == 0 && split_pays(M, N, K);
-    if (p->split)
-        p->ws_bytes = (size_t)split_ws_bytes(N);
+    p->split_s = p->levels == 0 ? split_pieces(M, N, K) : 0;
+    if (p->split_s)
+        p->ws_bytes = (size_t)split_ws_bytes(N, p->split_s);
     p->unfused = p->levels == 1 && (unfused || l1_unfused_auto);
     if (p->unfused) {
         p->op_bf16 = op_bf16_for(1);
@@ -931,9 +955,10 @@ lcma_status check_io(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     return LCMA_OK;
 }
 
-// Identifier of one call of the K-split kernel: even, non-zero and never
-// repeated within the process; a random per-process offset keeps it from
-// matching a tag that another process may have left in reused memory.
+// Identifier of one call of the K-split kernel: a non-zero multiple of 16
+// (the low bits count arrivals), never repeated within the process; a random
+// per-process offset keeps it from matching a slot that another process may
+// have left in reused memory.
 uint64_t next_call_id()
 {
     static const uint64_t salt = [] {
@@ -946,13 +971,13 @@ uint64_t next_call_id()
         return x;
     }();
     static std::atomic<uint64_t> n{0};
-    const uint64_t id = (salt + 2 * n.fetch_add(1, std::memory_order_relaxed)) & ~(uint64_t)1;
-    return id != 0 ? id : 2;
+    const uint64_t id = (salt + 16 * n.fetch_add(1, std::memory_order_relaxed)) & ~(uint64_t)15;
+    return id != 0 ? id : 16;
 }
 
 lcma_status run_classic(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const void* A, int64_t lda, const void* B,
                         int64_t ldb, void* C, int64_t ldc, const Io& io, int tile, int P, hipStream_t st,
-                        void* split_ws = nullptr)
+                        void* split_ws = nullptr, int split_s = 0)
 {
     if (M == 0 || N == 0)
         return LCMA_OK;
@@ -960,8 +985,9 @@ lcma_status run_classic(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const vo
     L.A = A; L.lda = lda; L.B = B; L.ldb = ldb; L.C = C; L.ldc = ldc;
     L.M = (int32_t)M; L.N = (int32_t)N; L.K = (int32_t)K;
     L.bf16 = dt == LCMA_BF16; L.vec = io.vec; L.vec4 = io.vec4; L.tile = tile; L.P = P;
-    L.split_ws = split_ws;
-    L.split_id = split_ws ? next_call_id() : 0;
+    L.split_ws = split_s ? split_ws : nullptr;
+    L.split_s = split_s;
+    L.split_id = split_s ? next_call_id() : 0;
     return hip_status(launch_classic(L, st), "launch_classic");
 }
 
@@ -1377,8 +1403,8 @@ lcma_status lcma_gemm(lcma_plan_t p, const void* A, int64_t lda, const void* B, 
             s = check_ws(p, ws, ws_bytes);
         if (s != LCMA_OK)
             return s;
-        return run_classic(p->M, p->N, p->K, p->dt, A, lda, B, ldb, C, ldc, io, p->classic_tile, p->P, st,
-                           p->split ? ws : nullptr);
+        return run_classic(p->M, p->N, p->K, p->dt, A, lda, B, ldb, C, ldc, io, p->classic_tile, p->P, st, ws,
+                           p->split_s);
     }
     Io io;
     lcma_status s = check_lcma_call(p, A, lda, B, ldb, C, ldc, ws, ws_bytes, true, &io);

@@ -2100,23 +2100,24 @@ hipError_t launch_skinny_shared_t(const ClassicLaunch& L, hipStream_t st)
     return hipGetLastError();
 }
 
-// K split for 33..64 rows: the two workgroups of a 128-column strip take one
-// half of K each (on one XCD: blocks 16 (s / 8) + s % 8 and that + 8), so
-// each reads half as many bytes of A per byte of B as the unsplit 64-column
-// kernel, whose time grows with the A bytes re-read by every workgroup.  The
-// K loop is k_skinny_shared's.  Each half then writes its fp32 partial tile
-// to the workspace, and thread 0 swaps the strip's 64-bit arrival tag for its
-// own (call id | half) with one agent-scope acquire-release atomic.  Finding
-// the other half's tag of the same call means the other partial is complete:
-// this workgroup adds it, clears the tag and rounds the sum into C.  A stale
-// tag (an earlier call, or whatever a fresh workspace holds) never carries
-// this call's id, and the cleared tag lets a replayed graph (same id) start
-// clean.  fp32 addition commutes, so the result does not depend on which
-// half arrives last.
+// K split for 33..64 rows: the S workgroups of a 128-column strip (S = 2, 4
+// or 8; blocks 8 S (s / 8) + 8 q + s % 8 for piece q, all on one XCD) each
+// take one S-th of K, so each reads S times fewer bytes of A per byte of B
+// than an unsplit 64-column kernel, whose time grows with the A bytes every
+// workgroup re-reads, and few strips still fill the chip.  The K loop is
+// k_skinny_shared's.  Each piece then writes its fp32 partial tile to the
+// workspace, and thread 0 counts its arrival in the strip's 64-bit slot with
+// one agent-scope acquire-release compare-and-swap: the slot holds the
+// call's identifier (a multiple of 16) plus the arrivals so far, and a slot
+// holding another identifier (an earlier call, or whatever a fresh
+// workspace holds) counts as none.  Each failed swap means another piece's
+// swap succeeded, so the loop ends.  The S-th arrival adds the S partials
+// in piece order (the same sum whatever the arrival order), clears the slot
+// (so a replayed graph, same identifier, starts clean) and rounds into C.
 template <class C, bool BF>
 __global__ void __launch_bounds__(C::NT, 1)
 k_skinny_split(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb, u16* __restrict__ Cm,
-               int64_t ldc, int M, int N, int K, int kh, int vec4, float* __restrict__ part, uint64_t* tags,
+               int64_t ldc, int M, int N, int K, int S, int kh, int vec4, float* __restrict__ part, uint64_t* tags,
                uint64_t id)
 {
     static_assert(C::BN == kSplitCols && C::BM == 64, "strip shape of the workspace layout");
@@ -2127,12 +2128,12 @@ k_skinny_split(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % C::WM, wn = wave / C::WM;
-    const int b = blockIdx.x;
-    const int strip = (b / 16) * 8 + b % 8, half = (b / 8) % 2;
+    const int b = blockIdx.x, r = b % (8 * S);
+    const int strip = (b / (8 * S)) * 8 + r % 8, piece = r / 8;
     const int n0 = strip * C::BN;
     if (n0 >= N)
         return;                     // the grid covers whole groups of 8 strips
-    const int kb = half * kh, klen = max(0, min(K - kb, kh));
+    const int kb = piece * kh, klen = max(0, min(K - kb, kh));
     const u16* Ah = A + kb;
     const u16* Bh = B + (int64_t)kb * ldb + n0;
     const int nk = (klen + C::BK - 1) / C::BK;
@@ -2154,63 +2155,77 @@ k_skinny_split(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B
         rd = rd + C::STAGE == C::LDS ? 0 : rd + C::STAGE;
         wr = wr + C::STAGE == C::LDS ? 0 : wr + C::STAGE;
     }
-    f32x4* mine = reinterpret_cast<f32x4*>(part) + (int64_t)(strip * 2 + half) * PF4 * C::NT;
-    const f32x4* other = reinterpret_cast<const f32x4*>(part) + (int64_t)(strip * 2 + 1 - half) * PF4 * C::NT;
+    f32x4* slots = reinterpret_cast<f32x4*>(part) + (int64_t)strip * S * PF4 * C::NT;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
 #pragma unroll
             for (int g = 0; g < C::NACC / 4; ++g)
-                mine[(int64_t)((i * C::FN + j) * (C::NACC / 4) + g) * C::NT + tid] =
+                slots[((int64_t)piece * PF4 + (i * C::FN + j) * (C::NACC / 4) + g) * C::NT + tid] =
                     f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
     // Every wave's partial stores have reached the L2 of its XCD; thread 0's
     // agent-scope acquire-release swap writes it back once for the workgroup
-    // (and, for the second half to arrive, invalidates before the reads).
+    // (and, for the last piece to arrive, invalidates before the reads).
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-        const uint64_t old = __hip_atomic_exchange(tags + strip, id | (uint64_t)half, __ATOMIC_ACQ_REL,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-        sh_last = old == (id | (uint64_t)(1 - half));
+        uint64_t* slot = tags + strip;
+        uint64_t old = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), now;
+        do {
+            now = (old & ~(uint64_t)15) == id ? old + 1 : (id | 1);
+        } while (!__hip_atomic_compare_exchange_strong(slot, &old, now, __ATOMIC_ACQ_REL, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT));
+        sh_last = (int)(now & 15) == S;
     }
     __syncthreads();
     if (!sh_last)
         return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    f32x16 sum[C::FM][C::FN];
+    zero_acc<C>(sum);
+    for (int q = 0; q < S; ++q) {
+        asm volatile("" ::: "memory");     // one piece at a time: its loads are not all hoisted ahead
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+        for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j)
+            for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-            for (int g = 0; g < C::NACC / 4; ++g) {
-                const f32x4 v = __builtin_nontemporal_load(other + (int64_t)((i * C::FN + j) * (C::NACC / 4) + g) * C::NT + tid);
-                acc[i][j][4 * g] += v.x;
-                acc[i][j][4 * g + 1] += v.y;
-                acc[i][j][4 * g + 2] += v.z;
-                acc[i][j][4 * g + 3] += v.w;
-            }
+                for (int g = 0; g < C::NACC / 4; ++g) {
+                    f32x4 v;
+                    if (q == piece)
+                        v = f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    else
+                        v = __builtin_nontemporal_load(
+                            slots + ((int64_t)q * PF4 + (i * C::FN + j) * (C::NACC / 4) + g) * C::NT + tid);
+                    sum[i][j][4 * g] += v.x;
+                    sum[i][j][4 * g + 1] += v.y;
+                    sum[i][j][4 * g + 2] += v.z;
+                    sum[i][j][4 * g + 3] += v.w;
+                }
+    }
     if (tid == 0)
         __hip_atomic_store(tags + strip, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (vec4)
-        store_c<C, BF, true>(acc, Cm + n0, ldc, M, N - n0, wm, wn, lane);
+        store_c<C, BF, true>(sum, Cm + n0, ldc, M, N - n0, wm, wn, lane);
     else
-        store_c<C, BF, false>(acc, Cm + n0, ldc, M, N - n0, wm, wn, lane);
+        store_c<C, BF, false>(sum, Cm + n0, ldc, M, N - n0, wm, wn, lane);
 }
 
 template <class C, bool BF>
 hipError_t launch_skinny_split_t(const ClassicLaunch& L, hipStream_t st)
 {
-    const int strips = (L.N + C::BN - 1) / C::BN;
+    const int strips = (L.N + C::BN - 1) / C::BN, S = L.split_s;
     if (strips == 0 || L.M == 0)
         return hipSuccess;
-    if (L.split_id == 0 || (L.split_id & 1) != 0 || ((uintptr_t)L.split_ws % 256) != 0)
+    if ((S != 2 && S != 4 && S != 8) || L.split_id == 0 || (L.split_id & 15) != 0 ||
+        ((uintptr_t)L.split_ws % 256) != 0)
         return hipErrorInvalidValue;
-    const int kh = ((L.K + 1) / 2 + C::BK - 1) / C::BK * C::BK;
+    const int kh = ((L.K + S - 1) / S + C::BK - 1) / C::BK * C::BK;
     char* ws = (char*)L.split_ws;
-    hipLaunchKernelGGL((k_skinny_split<C, BF>), dim3((unsigned)((strips + 7) / 8 * 16)), dim3(C::NT), 0, st,
-                       (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, (u16*)L.C, L.ldc, L.M, L.N, L.K, kh, L.vec4,
-                       (float*)ws, (uint64_t*)(ws + split_tag_offset(L.N)), L.split_id);
+    hipLaunchKernelGGL((k_skinny_split<C, BF>), dim3((unsigned)((strips + 7) / 8 * 8 * S)), dim3(C::NT), 0, st,
+                       (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, (u16*)L.C, L.ldc, L.M, L.N, L.K, S, kh,
+                       L.vec4, (float*)ws, (uint64_t*)(ws + split_tag_offset(L.N, S)), L.split_id);
     return hipGetLastError();
 }
 

@@ -27,24 +27,21 @@ struct ClassicLaunch {
     int32_t vec4;      // 8-byte C stores allowed
     int32_t tile;      // ClassicTile
     int32_t P;         // compute units (for the XCD-aware tile order)
-    // 33..64 rows: K split over the two workgroups of each kSplitCols-column
-    // strip (null: no split).  split_ws holds split_ws_bytes(N) bytes (256-byte
-    // aligned); split_id identifies the call (even, non-zero, never reused).
-    void* split_ws; uint64_t split_id;
+    // 33..64 rows: K split over split_s (2, 4 or 8) workgroups of each
+    // kSplitCols-column strip (split_ws null: no split).  split_ws holds
+    // split_ws_bytes(N, split_s) bytes (256-byte aligned); split_id identifies
+    // the call (a non-zero multiple of 16, never reused in the process).
+    void* split_ws; uint64_t split_id; int32_t split_s;
 };
 constexpr int kSplitCols = 128;
-// When the K split pays (measured at 33..64 rows): long K with few column
-// strips, or very long K (at 64 x 14336 x 4096 it loses 17%: every workgroup
-// writes back its XCD's L2 once for the exchange).
-inline bool split_pays(int64_t M, int64_t N, int64_t K)
-{
-    return M > 32 && M <= 64 && ((K >= 8192 && N <= 8192) || K >= 10240);
-}
 constexpr int64_t kSplitPartBytes = 64 * kSplitCols * 4;    // one workgroup's fp32 partial tile
 inline int64_t split_strips(int64_t N) { return (N + kSplitCols - 1) / kSplitCols; }
-// Partials (two per strip), then one 64-bit arrival tag per strip.
-inline int64_t split_tag_offset(int64_t N) { return split_strips(N) * 2 * kSplitPartBytes; }
-inline int64_t split_ws_bytes(int64_t N) { return (split_tag_offset(N) + split_strips(N) * 8 + 255) / 256 * 256; }
+// Partials (S per strip), then one 64-bit arrival counter per strip.
+inline int64_t split_tag_offset(int64_t N, int S) { return split_strips(N) * S * kSplitPartBytes; }
+inline int64_t split_ws_bytes(int64_t N, int S)
+{
+    return (split_tag_offset(N, S) + split_strips(N) * 8 + 255) / 256 * 256;
+}
 
 // Tile edge (rows, cols) of a classic tile shape.
 void classic_tile_dims(int32_t tile, int32_t* bm, int32_t* bn);
