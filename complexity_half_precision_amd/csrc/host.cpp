@@ -460,24 +460,30 @@ lcma_status lcma_desc_validate(const lcma_desc* d)
 
 namespace {
 
-// Workgroups per 128-column strip of the K-split kernel for 33..64 rows, 0
-// for none.  Measured on MI355X (64 rows, bfloat16, S in 0, 2, 4, 8): each
-// split workgroup writes its XCD's L2 back once for the exchange, which costs
-// more the more workgroups split, so S = 4 pays only with few strips and
-// S = 8 never (64 x 4096 x 14336: 80.1 us unsplit, 62.5 with S = 2, 45.6
-// with 4, 57.0 with 8; 64 x 14336 x 4096: 28.0 unsplit, 35.5 with S = 2).
+// Workgroups per 128-column strip of the K-split kernel for classic plans of
+// up to 64 rows, 0 for none.  Measured on MI355X (bfloat16; 1, 16, 32 and 64
+// rows; S in 0, 2, 4, 8): the split pays where few strips would leave most
+// compute units idle over a long K.  Each split workgroup adds a partial
+// tile's round trip, an L2 write-back for the exchange and a shorter K loop,
+// so with many strips it loses (1 x 1024 x 14336: 58.6 us unsplit, 24.7 with
+// S = 8; 1 x 4096 x 14336: 59.1 unsplit, 35.2 with S = 4; 64 x 4096 x 14336:
+// 80.1 unsplit, 44.2 with S = 4; 1 x 14336 x 4096: 21.4 unsplit, 31.8 with
+// S = 2).
 int split_pieces(int64_t M, int64_t N, int64_t K)
 {
-    if (M <= 32 || M > 64)
+    if (M < 1 || M > 64)
         return 0;
     const int64_t strips = split_strips(N);
-    if (strips <= 16)
-        return K >= 4096 ? 4 : 0;
+    if (strips <= 8 && K >= 12288)
+        return 8;
     if (strips <= 32)
-        return K >= 8192 ? 4 : 0;
-    if (strips <= 64)
+        return K >= 4096 ? 4 : 0;
+    if (strips <= 64) {
+        if (M <= 32)
+            return K >= 14336 || (K >= 8192 && M > 8) ? 2 : 0;
         return K >= 14336 ? 4 : K >= 8192 ? 2 : 0;
-    return K >= 10240 ? 2 : 0;
+    }
+    return M > 32 && K >= 10240 ? 2 : 0;
 }
 
 }  // namespace
@@ -731,7 +737,7 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     // decode-shaped classic plans: the workspace of the K-split streaming kernel
     p->split_s = p->levels == 0 ? split_pieces(M, N, K) : 0;
     if (p->split_s)
-        p->ws_bytes = (size_t)split_ws_bytes(N, p->split_s);
+        p->ws_bytes = (size_t)split_ws_bytes(N, p->split_s, split_rows(M));
     p->unfused = p->levels == 1 && (unfused || l1_unfused_auto);
     if (p->unfused) {
         p->op_bf16 = op_bf16_for(1);

@@ -10,6 +10,10 @@
 //  * k_skinny_shared -- M <= 64 products: one ring shared by the waves of a
 //                    workgroup (33..64 rows; up to 32 rows when B has many
 //                    column strips).
+//  * k_skinny_split -- M <= 64 products with K long against the column
+//                    strips: the K loop of k_skinny_shared over one part of
+//                    K per workgroup, fp32 partials exchanged through the
+//                    workspace, summed in a fixed order by the last arrival.
 //  * k_classic    -- register-staged tiles for the other shapes and for
 //                    operands that are not 16-byte aligned.
 //  * k_prepass    -- combine-A/B pass: every combined operand of an LCMA scheme,
@@ -2100,8 +2104,9 @@ hipError_t launch_skinny_shared_t(const ClassicLaunch& L, hipStream_t st)
     return hipGetLastError();
 }
 
-// K split for 33..64 rows: the S workgroups of a 128-column strip (S = 2, 4
-// or 8; blocks 8 S (s / 8) + 8 q + s % 8 for piece q, all on one XCD) each
+// K split for up to 64 rows (tiles of 32 rows on two waves or 64 rows on
+// four): the S workgroups of a 128-column strip (S = 2, 4 or 8; blocks
+// 8 S (s / 8) + 8 q + s % 8 for piece q, all on one XCD) each
 // take one S-th of K, so each reads S times fewer bytes of A per byte of B
 // than an unsplit 64-column kernel, whose time grows with the A bytes every
 // workgroup re-reads, and few strips still fill the chip.  The K loop is
@@ -2120,9 +2125,9 @@ k_skinny_split(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B
                int64_t ldc, int M, int N, int K, int S, int kh, int vec4, float* __restrict__ part, uint64_t* tags,
                uint64_t id)
 {
-    static_assert(C::BN == kSplitCols && C::BM == 64, "strip shape of the workspace layout");
+    static_assert(C::BN == kSplitCols, "strip width of the workspace layout");
     constexpr int PF4 = C::FM * C::FN * (C::NACC / 4);     // float4 per thread in a partial tile
-    static_assert((int64_t)PF4 * C::NT * 16 == kSplitPartBytes, "partial tile size");
+    static_assert((int64_t)PF4 * C::NT * 16 == (int64_t)C::BM * C::BN * 4, "partial tile size");
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
     __shared__ int sh_last;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -2165,8 +2170,12 @@ k_skinny_split(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B
                 slots[((int64_t)piece * PF4 + (i * C::FN + j) * (C::NACC / 4) + g) * C::NT + tid] =
                     f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
     // Every wave's partial stores have reached the L2 of its XCD; thread 0's
-    // agent-scope acquire-release swap writes it back once for the workgroup
-    // (and, for the last piece to arrive, invalidates before the reads).
+    // agent-scope release swap writes it back once for the workgroup.  Only
+    // the last piece to arrive takes the agent-scope acquire (an L2
+    // invalidate): the swaps on the slot form one release sequence, so that
+    // one acquire sees every piece's partial.  An acquire-release swap in
+    // every piece (an L2 invalidate each) measured 4-16% slower with 256 to
+    // 1800 pieces.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
@@ -2174,35 +2183,50 @@ k_skinny_split(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B
         uint64_t old = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), now;
         do {
             now = (old & ~(uint64_t)15) == id ? old + 1 : (id | 1);
-        } while (!__hip_atomic_compare_exchange_strong(slot, &old, now, __ATOMIC_ACQ_REL, __ATOMIC_RELAXED,
+        } while (!__hip_atomic_compare_exchange_strong(slot, &old, now, __ATOMIC_RELEASE, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT));
         sh_last = (int)(now & 15) == S;
+        if (sh_last)
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
     if (!sh_last)
         return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // The other pieces' partials are loaded QB at a time, so one batch costs
+    // one memory round trip (up to 8 partial tiles in flight per thread),
+    // and added in piece order.
+    constexpr int QB = 4;
     f32x16 sum[C::FM][C::FN];
     zero_acc<C>(sum);
-    for (int q = 0; q < S; ++q) {
-        asm volatile("" ::: "memory");     // one piece at a time: its loads are not all hoisted ahead
+    for (int q0 = 0; q0 < S; q0 += QB) {
+        asm volatile("" ::: "memory");     // at most QB partial tiles in registers
+        f32x4 v[QB][PF4];
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
+        for (int u = 0; u < QB; ++u)
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j)
+            for (int e = 0; e < PF4; ++e)
+                if (q0 + u < S && q0 + u != piece)
+                    v[u][e] = __builtin_nontemporal_load(slots + ((int64_t)(q0 + u) * PF4 + e) * C::NT + tid);
 #pragma unroll
-                for (int g = 0; g < C::NACC / 4; ++g) {
-                    f32x4 v;
-                    if (q == piece)
-                        v = f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                    else
-                        v = __builtin_nontemporal_load(
-                            slots + ((int64_t)q * PF4 + (i * C::FN + j) * (C::NACC / 4) + g) * C::NT + tid);
-                    sum[i][j][4 * g] += v.x;
-                    sum[i][j][4 * g + 1] += v.y;
-                    sum[i][j][4 * g + 2] += v.z;
-                    sum[i][j][4 * g + 3] += v.w;
-                }
+        for (int u = 0; u < QB; ++u) {
+            if (q0 + u >= S)
+                break;
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                    for (int g = 0; g < C::NACC / 4; ++g) {
+                        const int e = (i * C::FN + j) * (C::NACC / 4) + g;
+                        const f32x4 w = q0 + u == piece ? f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1],
+                                                                acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]}
+                                                        : v[u][e];
+                        sum[i][j][4 * g] += w.x;
+                        sum[i][j][4 * g + 1] += w.y;
+                        sum[i][j][4 * g + 2] += w.z;
+                        sum[i][j][4 * g + 3] += w.w;
+                    }
+        }
     }
     if (tid == 0)
         __hip_atomic_store(tags + strip, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2225,7 +2249,7 @@ hipError_t launch_skinny_split_t(const ClassicLaunch& L, hipStream_t st)
     char* ws = (char*)L.split_ws;
     hipLaunchKernelGGL((k_skinny_split<C, BF>), dim3((unsigned)((strips + 7) / 8 * 8 * S)), dim3(C::NT), 0, st,
                        (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, (u16*)L.C, L.ldc, L.M, L.N, L.K, S, kh,
-                       L.vec4, (float*)ws, (uint64_t*)(ws + split_tag_offset(L.N, S)), L.split_id);
+                       L.vec4, (float*)ws, (uint64_t*)(ws + split_tag_offset(L.N, S, C::BM)), L.split_id);
     return hipGetLastError();
 }
 
@@ -3060,6 +3084,14 @@ hipError_t launch_classic(const ClassicLaunch& L, hipStream_t st)
             return L.bf16 ? launch_classic_q4_t<QC128, true>(L, st) : launch_classic_q4_t<QC128, false>(L, st);
         return launch_classic_c<Cfg128>(L, st);
     default:
+        // with a workspace for the K split (classic plans): 128-column
+        // strips, one part of K per workgroup
+        if (L.vec && L.M <= 32 && L.split_ws)
+            return L.bf16 ? launch_skinny_split_t<sk::CCfg<5, kSplitCols, 32>, true>(L, st)
+                          : launch_skinny_split_t<sk::CCfg<5, kSplitCols, 32>, false>(L, st);
+        if (L.vec && L.M <= 64 && L.split_ws)
+            return L.bf16 ? launch_skinny_split_t<sk::CCfg<5, kSplitCols>, true>(L, st)
+                          : launch_skinny_split_t<sk::CCfg<5, kSplitCols>, false>(L, st);
         // M <= 64 with 16-byte aligned operands: the streaming kernels.
         // Up to 32 rows and long K: 64-k stages on two waves.  With more than
         // 128 column strips the waves share one 5-stage ring (1 x 14336 x 4096
@@ -3075,11 +3107,6 @@ hipError_t launch_classic(const ClassicLaunch& L, hipStream_t st)
                           : launch_skinny_t<sk::SCfg<32, 64, 2, 5>, false>(L, st);
         if (L.vec && L.M <= 32)
             return L.bf16 ? launch_skinny_t<sk::SCfg<32>, true>(L, st) : launch_skinny_t<sk::SCfg<32>, false>(L, st);
-        // 33..64 rows with a workspace for the K split (classic plans):
-        // 128-column strips, one half of K per workgroup
-        if (L.vec && L.M > 32 && L.M <= 64 && L.split_ws)
-            return L.bf16 ? launch_skinny_split_t<sk::CCfg<5, kSplitCols>, true>(L, st)
-                          : launch_skinny_split_t<sk::CCfg<5, kSplitCols>, false>(L, st);
         // 33..64 rows: 64-k stages (A rows of 128 bytes, half the L2 requests
         // per byte of A of 32-k stages) in one 5-stage ring shared by the four
         // waves: measured 28.4 us at 64 x 14336 x 4096 against 29.3 us for a

@@ -469,11 +469,14 @@ def test_padded_lcma_matches_oracle(algo, M, N, K, dtype, dist):
 
 
 @pytest.mark.parametrize("M,N,K,dtype", [(64, 4096, 14336, "bf16"), (33, 8200, 10248, "f16"), (48, 1032, 8192, "bf16"),
-                                       (57, 136, 8200, "f16")])
+                                       (57, 136, 8200, "f16"), (1, 1024, 14336, "bf16"), (1, 1032, 12296, "f16"),
+                                       (13, 4104, 8200, "bf16"), (32, 136, 8200, "f16"), (8, 8064, 14336, "bf16"),
+                                       (29, 1000, 12344, "bf16")])
 def test_decode_k_split_matches_oracle(M, N, K, dtype):
-    # classic plans of 33..64 rows with long K: 2 or 4 workgroups per
+    # classic plans of up to 64 rows with long K: 2, 4 or 8 workgroups per
     # 128-column strip, one part of K each, partials exchanged through the
-    # workspace (ragged rows, columns and k; one strip and many)
+    # workspace (32- and 64-row tiles; ragged rows, columns and k; one strip
+    # and many)
     say("decode K split", M, N, K, dtype)
     A, B, A64, B64 = gen(M, N, K, dtype, "uniform" if dtype == "f16" else "normal_sqrtk", seed=61)
     plan = L.lcma_plan_ex(M, N, K, dtype, force="classic")
@@ -481,21 +484,22 @@ def test_decode_k_split_matches_oracle(M, N, K, dtype):
     check_float(planned(A, B, "classic"), A64, B64, dtype)
 
 
-def test_decode_k_split_integer_inputs_are_exact():
+@pytest.mark.parametrize("M,N,K", [(64, 4104, 8200), (24, 1032, 14344), (5, 1024, 14336)])
+def test_decode_k_split_integer_inputs_are_exact(M, N, K):
     # {-1, 0, 1} inputs: every partial sum is an exact fp32 integer, and the
     # products stay within binary16's exact integers (checked below)
-    say("decode K split exact")
-    A, B, A64, B64 = gen(64, 4104, 8200, "f16", "int1", seed=62)
+    say("decode K split exact", M, N, K)
+    A, B, A64, B64 = gen(M, N, K, "f16", "int1", seed=62)
     assert np.abs(oracle.gemm(A64, B64)).max() <= 2048
     check_exact(planned(A, B, "classic"), A64, B64, "f16")
 
 
-def test_decode_k_split_any_workspace_contents_and_repeated_calls():
+@pytest.mark.parametrize("M,N,K", [(64, 2056, 8192), (16, 1024, 14336)])
+def test_decode_k_split_any_workspace_contents_and_repeated_calls(M, N, K):
     # the exchange needs no cleared workspace: random initial bytes, then
     # calls with other inputs on the same workspace, then the first inputs
     # again (bit for bit the first result)
-    say("decode K split workspace reuse")
-    M, N, K = 64, 2056, 8192
+    say("decode K split workspace reuse", M, N, K)
     plan = L.lcma_plan_ex(M, N, K, "bf16", force="classic")
     ws = L.workspace_for(plan)
     ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device=DEV))
@@ -510,12 +514,12 @@ def test_decode_k_split_any_workspace_contents_and_repeated_calls():
     assert np.array_equal(outs[0], outs[2])
 
 
-def test_decode_k_split_graph_replays_with_new_inputs():
-    # a captured call keeps its call identifier; the second arrival clears
-    # each strip's tag, so every replay pairs its own halves: each replay,
+@pytest.mark.parametrize("M,N,K", [(48, 4104, 8200), (8, 4104, 14336)])
+def test_decode_k_split_graph_replays_with_new_inputs(M, N, K):
+    # a captured call keeps its call identifier; the last arrival clears
+    # each strip's tag, so every replay pairs its own pieces: each replay,
     # after the inputs change in place, equals the eager product
-    say("decode K split graph")
-    M, N, K = 48, 4104, 8200
+    say("decode K split graph", M, N, K)
     plan = L.lcma_plan_ex(M, N, K, "bf16", force="classic")
     ws = L.workspace_for(plan)
     Ad = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)

@@ -7,8 +7,9 @@ k-tiles ahead, PER loads per wave and k-tile).  These models replay each
 kernel's issue and wait sequence for every k-tile count up to 300 and check
 that (1) every load of a k-tile has completed, in every wave, before any
 wave reads that k-tile's stage, and (2) a stage is refilled only after every
-read of its previous k-tile.  The sequences follow k_skinny_shared,
-k_skinny and the steady state of the 256 x 256 engine in kernels.hip.
+read of its previous k-tile.  The sequences follow k_skinny_shared
+(and k_skinny_split, whose K loop it shares), k_skinny and the steady state
+of the 256 x 256 engine in kernels.hip.
 """
 import pytest
 
@@ -105,9 +106,10 @@ def engine_steady(nk, ahead, per, waves=8):
                 w.issue(t + ahead, per)
 
 
-@pytest.mark.parametrize("ahead,per,waves", [(4, 4, 4), (4, 6, 2), (2, 4, 4), (9, 4, 4)])
+@pytest.mark.parametrize("ahead,per,waves", [(4, 4, 4), (4, 6, 2), (4, 6, 4), (4, 10, 2), (2, 4, 4), (9, 4, 4)])
 def test_shared_ring_schedule(ahead, per, waves):
-    # (4, 4, 4): 64 rows, 5-stage ring; (4, 6, 2): 32 rows; 3 and 10 stages: the depths measured around it
+    # (4, 4, 4): 64 rows, 5-stage ring; (4, 6, 2): 32 rows; (4, 6, 4) and (4, 10, 2): the K-split
+    # kernel's 128-column strips of 64 and 32 rows; 3 and 10 stages: the depths measured around it
     for nk in range(0, 301):
         shared_ring(nk, ahead, per, waves)
 
