@@ -16,9 +16,10 @@ Also in the default line: the measured machine references (an MFMA loop
 and an HBM stream kernel of the library; socket power and the shader clock
 held while the classic kernel, the MFMA loop and the vendor GEMM each run
 back to back, from amd-smi), the 16384^3 comparison of classic,
-one level (unfused and fused) and two levels, cold-cache and server-mode
-timings, the cold pre-pass bandwidth, and the build's targets with whether
-they are met.
+one level (unfused and fused) and two levels, decode-shaped products (M = 1
+to 64 against N = 14336, K = 4096 and against N = 4096, K = 14336), cold-cache
+and server-mode timings, the cold pre-pass bandwidth, and the performance
+targets with whether each is met.
 
 Prints ONE JSON line.  Single GPU only.
 """
@@ -118,7 +119,8 @@ def main():
             e1.record()
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / reps
-        print(json.dumps({"decode": decode_bandwidth(L, si, torch, tc)}), flush=True)
+        print(json.dumps({"decode": decode_bandwidth(L, si, torch, tc),
+                          "decode_long_k": decode_bandwidth(L, si, torch, tc, si.decode_long_k_shape)}), flush=True)
         return
 
     if args.study:
@@ -372,6 +374,7 @@ def main():
             out["large"] = large_square(L, si, torch, time_calls, time_cold)
         out["square_512_f16"] = small_square(L, si, torch, time_calls)
         out["decode"] = decode_bandwidth(L, si, torch, time_calls)
+        out["decode_long_k"] = decode_bandwidth(L, si, torch, time_calls, si.decode_long_k_shape)
         out["sweep"] = sweep_picks(L, si, torch, time_calls)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(A, B, args.cpu_seconds)
@@ -381,7 +384,7 @@ def main():
 
 
 def targets(out):
-    """The build's throughput targets against what this run measured (reported
+    """The throughput targets against what this run measured (reported
     as they stand, met or not)."""
     t = {"classic_frac_of_peak": {"target": 0.70, "measured": out["roofline"]["frac"]}}
     if "l1_over_classic" in out:
@@ -583,15 +586,17 @@ def hbm_copy_rate(torch, time_calls):
     return {"hbm_copy_gbps": round(2.0 * n / (t * 1e-3) / 1e9, 1), "copy_bytes": n}
 
 
-def decode_bandwidth(L, si, torch, time_calls):
-    """Decode-shaped products (M in 1, 4, 16, 64; K=4096, N=14336, bfloat16): the
-    planned path (the cost model must pick classic), HBM GB/s of the algorithmic
-    bytes 2(MK + KN + MN).  B rotates over 4 resident copies (470 MB, more than
-    the 256 MB last-level cache), so every call streams its B from HBM.  The
-    calls are prepared once (lcma_gemm_prepared) and issued back to back."""
+def decode_bandwidth(L, si, torch, time_calls, shape=None):
+    """Decode-shaped products (M in 1, 4, 16, 64, bfloat16; K=4096, N=14336 by
+    default, or `shape(m)`, e.g. K=14336, N=4096, which the K split serves):
+    the planned path (the cost model must pick classic), HBM GB/s of the
+    algorithmic bytes 2(MK + KN + MN).  B rotates over 4 resident copies (470
+    MB, more than the 256 MB last-level cache), so every call streams its B
+    from HBM.  The calls are prepared once (lcma_gemm_prepared) and issued
+    back to back."""
     res = {}
     for m in si.DECODE_MS:
-        w = si.decode_shape(m)
+        w = (shape or si.decode_shape)(m)
         A, B = si.gen(**w)
         Ad = A.to("cuda")
         Bs = [B.to("cuda")] + [None] * 3
@@ -602,7 +607,7 @@ def decode_bandwidth(L, si, torch, time_calls):
         algo = L.lcma_plan_info(p)[0]
         # arguments checked once per B copy: the per-call checks of the binding
         # take about as long as these kernels run
-        ws = L.workspace_for(p)      # none for these shapes (the K split pays only for longer K)
+        ws = L.workspace_for(p)      # the K split's partials, if the plan splits
         calls = [L.lcma_gemm_prepared(p, Ad, Bs[i], Cd, ws) for i in range(4)]
         k = [0]
 

@@ -94,6 +94,11 @@ def decode_shape(m: int):
     return dict(M=m, N=14336, K=4096, dtype="bf16", dist="decode", seed=0)
 
 
+def decode_long_k_shape(m: int):
+    """The same layer's product with N and K exchanged: few column strips over a long K."""
+    return dict(M=m, N=4096, K=14336, dtype="bf16", dist="decode", seed=0)
+
+
 def sweep_workloads():
     return [dict(M=M, N=N, K=K, dtype="f16", dist="uniform", seed=1000 + i)
             for i, (M, N, K) in enumerate(sweep_shapes())]
