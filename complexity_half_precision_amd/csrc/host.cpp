@@ -461,28 +461,27 @@ lcma_status lcma_desc_validate(const lcma_desc* d)
 namespace {
 
 // Workgroups per 128-column strip of the K-split kernel for classic plans of
-// up to 64 rows, 0 for none.  Measured on MI355X (bfloat16; 1, 16, 32 and 64
-// rows; S in 0, 2, 4, 8): the split pays where few strips would leave most
-// compute units idle over a long K.  Each split workgroup adds a partial
-// tile's round trip, an L2 write-back for the exchange and a shorter K loop,
-// so with many strips it loses (1 x 1024 x 14336: 58.6 us unsplit, 24.7 with
-// S = 8; 1 x 4096 x 14336: 59.1 unsplit, 35.2 with S = 4; 64 x 4096 x 14336:
-// 80.1 unsplit, 44.2 with S = 4; 1 x 14336 x 4096: 21.4 unsplit, 31.8 with
-// S = 2).
+// up to 64 rows, 0 for none.  Measured on MI355X (bfloat16; 1, 8, 32 and 64
+// rows; 15 shapes each; S in 0, 2, 4, 8): the split pays where few strips
+// would leave most compute units idle over a long K.  Each split workgroup
+// adds an exchange (partial tile, L2 write-back, arrival) and a shorter K
+// loop, so with many strips it loses (1 x 1024 x 14336: 58.4 us unsplit,
+// 20.1 with S = 8; 1 x 4096 x 14336: 59.0 unsplit, 32.3 with S = 4;
+// 64 x 4096 x 14336: 79.9 unsplit, 36.2 with S = 8; 1 x 14336 x 4096: 21.4
+// unsplit, 29.1 with S = 2).
 int split_pieces(int64_t M, int64_t N, int64_t K)
 {
     if (M < 1 || M > 64)
         return 0;
     const int64_t strips = split_strips(N);
-    if (strips <= 8 && K >= 12288)
-        return 8;
+    if (strips <= 8)
+        return K >= 4096 ? 8 : K >= 2048 ? 4 : 0;
+    if (strips <= 16)
+        return K >= 8192 ? 8 : K >= 2048 ? 4 : 0;
     if (strips <= 32)
-        return K >= 4096 ? 4 : 0;
-    if (strips <= 64) {
-        if (M <= 32)
-            return K >= 14336 || (K >= 8192 && M > 8) ? 2 : 0;
-        return K >= 14336 ? 4 : K >= 8192 ? 2 : 0;
-    }
+        return M > 32 && K >= 12288 ? 8 : K >= 4096 ? 4 : 0;
+    if (strips <= 64)
+        return K >= 12288 ? 4 : K >= 8192 ? (M > 32 ? 4 : 2) : 0;
     return M > 32 && K >= 10240 ? 2 : 0;
 }
 

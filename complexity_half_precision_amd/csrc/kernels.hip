@@ -2106,28 +2106,31 @@ hipError_t launch_skinny_shared_t(const ClassicLaunch& L, hipStream_t st)
 
 // K split for up to 64 rows (tiles of 32 rows on two waves or 64 rows on
 // four): the S workgroups of a 128-column strip (S = 2, 4 or 8; blocks
-// 8 S (s / 8) + 8 q + s % 8 for piece q, all on one XCD) each
-// take one S-th of K, so each reads S times fewer bytes of A per byte of B
-// than an unsplit 64-column kernel, whose time grows with the A bytes every
-// workgroup re-reads, and few strips still fill the chip.  The K loop is
-// k_skinny_shared's.  Each piece then writes its fp32 partial tile to the
-// workspace, and thread 0 counts its arrival in the strip's 64-bit slot with
-// one agent-scope acquire-release compare-and-swap: the slot holds the
-// call's identifier (a multiple of 16) plus the arrivals so far, and a slot
-// holding another identifier (an earlier call, or whatever a fresh
-// workspace holds) counts as none.  Each failed swap means another piece's
-// swap succeeded, so the loop ends.  The S-th arrival adds the S partials
-// in piece order (the same sum whatever the arrival order), clears the slot
-// (so a replayed graph, same identifier, starts clean) and rounds into C.
+// 8 S (s / 8) + 8 q + s % 8 for piece q, all on one XCD) each take one S-th
+// of K, so each reads S times fewer bytes of A per byte of B than an unsplit
+// 64-column kernel, whose time grows with the A bytes every workgroup
+// re-reads, and few strips still fill the chip.  The K loop is
+// k_skinny_shared's.
+//
+// Exchange.  Each piece writes the rows below M of its fp32 partial tile to
+// the workspace, row-major through LDS (one row of a one-row product is 512
+// contiguous bytes), and thread 0 counts the arrival in the strip's 64-bit slot: the
+// slot holds the call's identifier (a multiple of 16) plus the arrivals so
+// far.  A slot holding another identifier (an earlier call, or whatever a
+// fresh workspace holds) counts as none: the first piece to arrive swaps it
+// for (identifier, 1); every later one finds the identifier and adds 1.
+// Either is a release at agent scope.  Only the S-th arrival takes the
+// agent-scope acquire (the swap and the adds form one release sequence),
+// adds the S partials in piece order (the same sum whatever the arrival
+// order), clears the slot (so a replayed graph, same identifier, starts
+// clean) and rounds into C.
 template <class C, bool BF>
 __global__ void __launch_bounds__(C::NT, 1)
 k_skinny_split(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb, u16* __restrict__ Cm,
                int64_t ldc, int M, int N, int K, int S, int kh, int vec4, float* __restrict__ part, uint64_t* tags,
                uint64_t id)
 {
-    static_assert(C::BN == kSplitCols, "strip width of the workspace layout");
-    constexpr int PF4 = C::FM * C::FN * (C::NACC / 4);     // float4 per thread in a partial tile
-    static_assert((int64_t)PF4 * C::NT * 16 == (int64_t)C::BM * C::BN * 4, "partial tile size");
+    static_assert(C::BN == kSplitCols && C::MT == 32 && C::FM == 1, "strip and tile shape of the workspace layout");
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
     __shared__ int sh_last;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -2160,80 +2163,117 @@ k_skinny_split(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B
         rd = rd + C::STAGE == C::LDS ? 0 : rd + C::STAGE;
         wr = wr + C::STAGE == C::LDS ? 0 : wr + C::STAGE;
     }
-    f32x4* slots = reinterpret_cast<f32x4*>(part) + (int64_t)strip * S * PF4 * C::NT;
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+    // The partial tile goes through LDS (the ring is free now) so that its
+    // rows below M leave as contiguous 16-byte chunks: chunk c of the tile is
+    // row c / 32, columns 4 (c % 32) .. + 3, and thread t holds chunks
+    // t + k NT.  Staging rows are padded by 16 bytes against bank conflicts.
+    constexpr int SROW = C::BN * 4 + 16, CPR = C::BN / 4, CPT = C::BM * CPR / C::NT;
+    static_assert(C::BM * SROW <= C::LDS && C::BM * CPR % C::NT == 0, "staging");
+    tiles::bar();                                      // every wave is done reading the ring
+    {
+        const int m = wm * C::WTM + (lane & 31), hi = lane >> 5;
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
 #pragma unroll
             for (int g = 0; g < C::NACC / 4; ++g)
-                slots[((int64_t)piece * PF4 + (i * C::FN + j) * (C::NACC / 4) + g) * C::NT + tid] =
-                    f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                *reinterpret_cast<f32x4*>(smem + m * SROW + (wn * C::WTN + j * 32 + 8 * g + 4 * hi) * 4) =
+                    f32x4{acc[0][j][4 * g], acc[0][j][4 * g + 1], acc[0][j][4 * g + 2], acc[0][j][4 * g + 3]};
+    }
+    tiles::wait_lgkm0();
+    tiles::bar();
+    f32x4* tile = reinterpret_cast<f32x4*>(part) + (int64_t)strip * S * C::BM * CPR;   // the strip's S partials
+    f32x4 own[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int c = tid + k * C::NT;
+        own[k] = *reinterpret_cast<const f32x4*>(smem + (c / CPR) * SROW + (c % CPR) * 16);
+        if (c / CPR < M)
+            tile[(int64_t)piece * C::BM * CPR + c] = own[k];
+    }
     // Every wave's partial stores have reached the L2 of its XCD; thread 0's
-    // agent-scope release swap writes it back once for the workgroup.  Only
-    // the last piece to arrive takes the agent-scope acquire (an L2
-    // invalidate): the swaps on the slot form one release sequence, so that
-    // one acquire sees every piece's partial.  An acquire-release swap in
-    // every piece (an L2 invalidate each) measured 4-16% slower with 256 to
-    // 1800 pieces.
+    // agent-scope release writes it back once for the workgroup.  An
+    // acquire-release swap in every piece (an L2 invalidate each) measured
+    // 4-16% slower with 256 to 1800 pieces; a swap retried until it succeeds
+    // (one round trip per piece arriving at the same time) up to 1.3x slower
+    // than a load and an add; and reading the slot at the start instead of
+    // here up to 1.13x slower (every piece then swaps).
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
         uint64_t* slot = tags + strip;
-        uint64_t old = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), now;
-        do {
-            now = (old & ~(uint64_t)15) == id ? old + 1 : (id | 1);
-        } while (!__hip_atomic_compare_exchange_strong(slot, &old, now, __ATOMIC_RELEASE, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT));
-        sh_last = (int)(now & 15) == S;
+        uint64_t old = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), prev;
+        for (;;) {
+            if ((old & ~(uint64_t)15) == id) {
+                prev = __hip_atomic_fetch_add(slot, (uint64_t)1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            // a failed swap returns the slot's value: another piece's swap, so
+            // the next pass adds
+            if (__hip_atomic_compare_exchange_strong(slot, &old, id | 1, __ATOMIC_RELEASE, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT)) {
+                prev = id;
+                break;
+            }
+        }
+        sh_last = (int)(prev & 15) == S - 1;
         if (sh_last)
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
     if (!sh_last)
         return;
-    // The other pieces' partials are loaded QB at a time, so one batch costs
-    // one memory round trip (up to 8 partial tiles in flight per thread),
-    // and added in piece order.
+    // The other pieces' chunks are loaded QB pieces at a time, so one batch
+    // costs one memory round trip, and added in piece order.
     constexpr int QB = 4;
-    f32x16 sum[C::FM][C::FN];
-    zero_acc<C>(sum);
+    f32x4 sum[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k)
+        sum[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int q0 = 0; q0 < S; q0 += QB) {
-        asm volatile("" ::: "memory");     // at most QB partial tiles in registers
-        f32x4 v[QB][PF4];
+        asm volatile("" ::: "memory");     // at most QB pieces' chunks in registers
+        f32x4 v[QB][CPT];
 #pragma unroll
         for (int u = 0; u < QB; ++u)
 #pragma unroll
-            for (int e = 0; e < PF4; ++e)
-                if (q0 + u < S && q0 + u != piece)
-                    v[u][e] = __builtin_nontemporal_load(slots + ((int64_t)(q0 + u) * PF4 + e) * C::NT + tid);
+            for (int k = 0; k < CPT; ++k) {
+                const int c = tid + k * C::NT;
+                v[u][k] = c / CPR < M && q0 + u < S && q0 + u != piece
+                              ? __builtin_nontemporal_load(tile + (int64_t)(q0 + u) * C::BM * CPR + c)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
         for (int u = 0; u < QB; ++u) {
             if (q0 + u >= S)
                 break;
 #pragma unroll
-            for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-                    for (int g = 0; g < C::NACC / 4; ++g) {
-                        const int e = (i * C::FN + j) * (C::NACC / 4) + g;
-                        const f32x4 w = q0 + u == piece ? f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1],
-                                                                acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]}
-                                                        : v[u][e];
-                        sum[i][j][4 * g] += w.x;
-                        sum[i][j][4 * g + 1] += w.y;
-                        sum[i][j][4 * g + 2] += w.z;
-                        sum[i][j][4 * g + 3] += w.w;
-                    }
+            for (int k = 0; k < CPT; ++k)
+                sum[k] += q0 + u == piece ? own[k] : v[u][k];
         }
     }
     if (tid == 0)
         __hip_atomic_store(tags + strip, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (vec4)
-        store_c<C, BF, true>(sum, Cm + n0, ldc, M, N - n0, wm, wn, lane);
-    else
-        store_c<C, BF, false>(sum, Cm + n0, ldc, M, N - n0, wm, wn, lane);
+    // C: each chunk is 4 consecutive columns of one row
+    const rsrc_t rc = make_rsrc(Cm + n0);
+    const int ld = (int)ldc, cols = N - n0;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int c = tid + k * C::NT, row = c / CPR, col = (c % CPR) * 4;
+        if (vec4) {
+            // cols is a multiple of 4 here, so the 4 columns are all valid or all not
+            const u32 off = (row < M && col < cols) ? (u32)(row * ld + col) * 2u : kOob;
+            __builtin_amdgcn_raw_buffer_store_b64(
+                __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
+                                   u32x2{pack2<BF>(sum[k].x, sum[k].y), pack2<BF>(sum[k].z, sum[k].w)}),
+                rc, off, 0, 0);
+        } else {
+            const float xs[4] = {sum[k].x, sum[k].y, sum[k].z, sum[k].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const u32 off = (row < M && col + e < cols) ? (u32)(row * ld + col + e) * 2u : kOob;
+                __builtin_amdgcn_raw_buffer_store_b16(f2h<BF>(xs[e]), rc, off, 0, 0);
+            }
+        }
+    }
 }
 
 template <class C, bool BF>

@@ -264,9 +264,8 @@ lcma_status lcma_plan_estimate(lcma_plan_t plan, lcma_algo algo, double* est_sec
  * the planned size (may be NULL when that size is 0), 256-byte aligned; it
  * must not be used by two calls that can overlap.  Classic plans of up to
  * 64 rows whose K is long against their number of 128-column strips
- * (N <= 4096: K >= 4096; N <= 8192: K >= 8192 for more than 8 rows,
- * K >= 14336 otherwise; wider N, 33..64 rows only: K >= 10240) have a
- * workspace: 2, 4 or 8 workgroups per strip each take a
+ * (N <= 2048: K >= 2048; N <= 4096: K >= 4096; N <= 8192: K >= 8192;
+ * wider N, 33..64 rows only: K >= 10240) have a workspace: 2, 4 or 8 workgroups per strip each take a
  * part of K and exchange fp32 partial tiles (32 or 64 rows x 128 columns)
  * through it ([KP] "GEMM 形状": such products stream B; the split cuts the
  * bytes of A each workgroup re-reads and fills the chip when the strips are

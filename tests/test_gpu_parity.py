@@ -471,7 +471,7 @@ def test_padded_lcma_matches_oracle(algo, M, N, K, dtype, dist):
 @pytest.mark.parametrize("M,N,K,dtype", [(64, 4096, 14336, "bf16"), (33, 8200, 10248, "f16"), (48, 1032, 8192, "bf16"),
                                        (57, 136, 8200, "f16"), (1, 1024, 14336, "bf16"), (1, 1032, 12296, "f16"),
                                        (13, 4104, 8200, "bf16"), (32, 136, 8200, "f16"), (8, 8064, 14336, "bf16"),
-                                       (29, 1000, 12344, "bf16")])
+                                       (29, 1000, 12344, "bf16"), (40, 2056, 4104, "f16"), (3, 3976, 6152, "bf16")])
 def test_decode_k_split_matches_oracle(M, N, K, dtype):
     # classic plans of up to 64 rows with long K: 2, 4 or 8 workgroups per
     # 128-column strip, one part of K each, partials exchanged through the
