@@ -11,15 +11,12 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
-#include <chrono>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
-#include <random>
 #include <vector>
 
 #include "kernels.hpp"
@@ -462,27 +459,29 @@ namespace {
 
 // Workgroups per 128-column strip of the K-split kernel for classic plans of
 // up to 64 rows, 0 for none.  Measured on MI355X (bfloat16; 1, 8, 32 and 64
-// rows; 15 shapes each; S in 0, 2, 4, 8): the split pays where few strips
-// would leave most compute units idle over a long K.  Each split workgroup
-// adds an exchange (partial tile, L2 write-back, arrival) and a shorter K
-// loop, so with many strips it loses (1 x 1024 x 14336: 58.4 us unsplit,
-// 20.1 with S = 8; 1 x 4096 x 14336: 59.0 unsplit, 32.3 with S = 4;
-// 64 x 4096 x 14336: 79.9 unsplit, 36.2 with S = 8; 1 x 14336 x 4096: 21.4
-// unsplit, 29.1 with S = 2).
+// rows; 18 shapes each; S in 0, 2, 4, 8): the split pays where few strips
+// would leave most compute units idle over a long K, and with many strips
+// only for 17 rows and more over a long K, where it halves the A bytes each
+// workgroup re-reads.  It costs a second launch and a partial tile per
+// piece (1 x 1024 x 14336: 58.5 us unsplit, 18.9 with S = 8; 1 x 4096 x
+// 14336: 59.1 unsplit, 26.0 with S = 8; 64 x 14336 x 14336: 93.4 unsplit,
+// 81.5 with S = 2; 1 x 14336 x 4096: 21.5 unsplit, 24.5 with S = 2).
 int split_pieces(int64_t M, int64_t N, int64_t K)
 {
     if (M < 1 || M > 64)
         return 0;
     const int64_t strips = split_strips(N);
     if (strips <= 8)
-        return K >= 4096 ? 8 : K >= 2048 ? 4 : 0;
+        return K >= 2048 ? 8 : 0;
     if (strips <= 16)
-        return K >= 8192 ? 8 : K >= 2048 ? 4 : 0;
+        return K >= 4096 ? 8 : K >= 2048 ? (M > 32 ? 4 : 8) : 0;
     if (strips <= 32)
-        return M > 32 && K >= 12288 ? 8 : K >= 4096 ? 4 : 0;
+        return K >= 4096 ? 8 : K >= 2048 ? 4 : 0;
     if (strips <= 64)
-        return K >= 12288 ? 4 : K >= 8192 ? (M > 32 ? 4 : 2) : 0;
-    return M > 32 && K >= 10240 ? 2 : 0;
+        return K >= 4096 ? 4 : 0;
+    if (M > 32)
+        return K >= 8192 || (strips > 128 && K >= 4096) ? 2 : 0;
+    return M > 16 && K >= 12288 ? 2 : 0;
 }
 
 }  // namespace
@@ -960,26 +959,6 @@ lcma_status check_io(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     return LCMA_OK;
 }
 
-// Identifier of one call of the K-split kernel: a non-zero multiple of 16
-// (the low bits count arrivals), never repeated within the process; a random
-// per-process offset keeps it from matching a slot that another process may
-// have left in reused memory.
-uint64_t next_call_id()
-{
-    static const uint64_t salt = [] {
-        uint64_t x = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
-        try {
-            std::random_device rd;
-            x ^= ((uint64_t)rd() << 32) ^ (uint64_t)rd();
-        } catch (...) {
-        }
-        return x;
-    }();
-    static std::atomic<uint64_t> n{0};
-    const uint64_t id = (salt + 16 * n.fetch_add(1, std::memory_order_relaxed)) & ~(uint64_t)15;
-    return id != 0 ? id : 16;
-}
-
 lcma_status run_classic(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const void* A, int64_t lda, const void* B,
                         int64_t ldb, void* C, int64_t ldc, const Io& io, int tile, int P, hipStream_t st,
                         void* split_ws = nullptr, int split_s = 0)
@@ -992,7 +971,6 @@ lcma_status run_classic(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const vo
     L.bf16 = dt == LCMA_BF16; L.vec = io.vec; L.vec4 = io.vec4; L.tile = tile; L.P = P;
     L.split_ws = split_s ? split_ws : nullptr;
     L.split_s = split_s;
-    L.split_id = split_s ? next_call_id() : 0;
     return hip_status(launch_classic(L, st), "launch_classic");
 }
 

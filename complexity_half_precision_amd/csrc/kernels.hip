@@ -10,10 +10,11 @@
 //  * k_skinny_shared -- M <= 64 products: one ring shared by the waves of a
 //                    workgroup (33..64 rows; up to 32 rows when B has many
 //                    column strips).
-//  * k_skinny_split -- M <= 64 products with K long against the column
-//                    strips: the K loop of k_skinny_shared over one part of
-//                    K per workgroup, fp32 partials exchanged through the
-//                    workspace, summed in a fixed order by the last arrival.
+//  * k_skinny_split, k_split_reduce -- M <= 64 products with K long
+//                    against the column strips: the K loop of
+//                    k_skinny_shared over one part of K per workgroup, fp32
+//                    partials in the workspace, then a second launch adds
+//                    them in a fixed order and rounds into C.
 //  * k_classic    -- register-staged tiles for the other shapes and for
 //                    operands that are not 16-byte aligned.
 //  * k_prepass    -- combine-A/B pass: every combined operand of an LCMA scheme,
@@ -2110,29 +2111,23 @@ hipError_t launch_skinny_shared_t(const ClassicLaunch& L, hipStream_t st)
 // of K, so each reads S times fewer bytes of A per byte of B than an unsplit
 // 64-column kernel, whose time grows with the A bytes every workgroup
 // re-reads, and few strips still fill the chip.  The K loop is
-// k_skinny_shared's.
-//
-// Exchange.  Each piece writes the rows below M of its fp32 partial tile to
-// the workspace, row-major through LDS (one row of a one-row product is 512
-// contiguous bytes), and thread 0 counts the arrival in the strip's 64-bit slot: the
-// slot holds the call's identifier (a multiple of 16) plus the arrivals so
-// far.  A slot holding another identifier (an earlier call, or whatever a
-// fresh workspace holds) counts as none: the first piece to arrive swaps it
-// for (identifier, 1); every later one finds the identifier and adds 1.
-// Either is a release at agent scope.  Only the S-th arrival takes the
-// agent-scope acquire (the swap and the adds form one release sequence),
-// adds the S partials in piece order (the same sum whatever the arrival
-// order), clears the slot (so a replayed graph, same identifier, starts
-// clean) and rounds into C.
+// k_skinny_shared's.  Each piece writes the rows below M of its fp32 partial
+// tile to the workspace, row-major through LDS (one row of a one-row product
+// is 512 contiguous bytes); k_split_reduce, the next launch on the stream,
+// adds the S partials in piece order and rounds into C.  The stream orders
+// the two kernels, so the workspace needs no clearing and no counters, and
+// any call or graph replay finds it ready.  An in-kernel exchange (the last
+// of the S pieces to count its arrival in an agent-scope atomic adds the
+// partials) measured 1.06-1.5x slower: every piece's release writes its
+// XCD's L2 back, and the count, the acquire and the partial loads are
+// round trips in series at the end of the kernel.
 template <class C, bool BF>
 __global__ void __launch_bounds__(C::NT, 1)
-k_skinny_split(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb, u16* __restrict__ Cm,
-               int64_t ldc, int M, int N, int K, int S, int kh, int vec4, float* __restrict__ part, uint64_t* tags,
-               uint64_t id)
+k_skinny_split(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb, int M, int N, int K,
+               int S, int kh, float* __restrict__ part)
 {
     static_assert(C::BN == kSplitCols && C::MT == 32 && C::FM == 1, "strip and tile shape of the workspace layout");
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
-    __shared__ int sh_last;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % C::WM, wn = wave / C::WM;
@@ -2165,7 +2160,7 @@ k_skinny_split(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B
     }
     // The partial tile goes through LDS (the ring is free now) so that its
     // rows below M leave as contiguous 16-byte chunks: chunk c of the tile is
-    // row c / 32, columns 4 (c % 32) .. + 3, and thread t holds chunks
+    // row c / 32, columns 4 (c % 32) .. + 3, and thread t writes chunks
     // t + k NT.  Staging rows are padded by 16 bytes against bank conflicts.
     constexpr int SROW = C::BN * 4 + 16, CPR = C::BN / 4, CPT = C::BM * CPR / C::NT;
     static_assert(C::BM * SROW <= C::LDS && C::BM * CPR % C::NT == 0, "staging");
@@ -2181,98 +2176,46 @@ k_skinny_split(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B
     }
     tiles::wait_lgkm0();
     tiles::bar();
-    f32x4* tile = reinterpret_cast<f32x4*>(part) + (int64_t)strip * S * C::BM * CPR;   // the strip's S partials
-    f32x4 own[CPT];
+    f32x4* tile = reinterpret_cast<f32x4*>(part) + ((int64_t)strip * S + piece) * C::BM * CPR;
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
         const int c = tid + k * C::NT;
-        own[k] = *reinterpret_cast<const f32x4*>(smem + (c / CPR) * SROW + (c % CPR) * 16);
         if (c / CPR < M)
-            tile[(int64_t)piece * C::BM * CPR + c] = own[k];
+            tile[c] = *reinterpret_cast<const f32x4*>(smem + (c / CPR) * SROW + (c % CPR) * 16);
     }
-    // Every wave's partial stores have reached the L2 of its XCD; thread 0's
-    // agent-scope release writes it back once for the workgroup.  An
-    // acquire-release swap in every piece (an L2 invalidate each) measured
-    // 4-16% slower with 256 to 1800 pieces; a swap retried until it succeeds
-    // (one round trip per piece arriving at the same time) up to 1.3x slower
-    // than a load and an add; and reading the slot at the start instead of
-    // here up to 1.13x slower (every piece then swaps).
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-        uint64_t* slot = tags + strip;
-        uint64_t old = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), prev;
-        for (;;) {
-            if ((old & ~(uint64_t)15) == id) {
-                prev = __hip_atomic_fetch_add(slot, (uint64_t)1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-            // a failed swap returns the slot's value: another piece's swap, so
-            // the next pass adds
-            if (__hip_atomic_compare_exchange_strong(slot, &old, id | 1, __ATOMIC_RELEASE, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT)) {
-                prev = id;
-                break;
-            }
-        }
-        sh_last = (int)(prev & 15) == S - 1;
-        if (sh_last)
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    }
-    __syncthreads();
-    if (!sh_last)
+}
+
+// C = the sum of the S partial tiles of each strip, in piece order, rounded
+// once: one thread per 4 consecutive columns of one row (consecutive threads
+// read consecutive 16-byte chunks of a partial row).
+template <bool BF>
+__global__ void __launch_bounds__(256) k_split_reduce(const f32x4* __restrict__ part, int S, int rows_per_tile,
+                                                      u16* __restrict__ Cm, int64_t ldc, int M, int N, int vec4)
+{
+    constexpr int CPR = kSplitCols / 4;
+    const int cpr = (N + 3) / 4;
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= M * cpr)
         return;
-    // The other pieces' chunks are loaded QB pieces at a time, so one batch
-    // costs one memory round trip, and added in piece order.
-    constexpr int QB = 4;
-    f32x4 sum[CPT];
+    const int row = c / cpr, col = (c % cpr) * 4;
+    const f32x4* p = part + (int64_t)(col / kSplitCols) * S * rows_per_tile * CPR + row * CPR + (col % kSplitCols) / 4;
+    f32x4 sum = __builtin_nontemporal_load(p);
+    for (int q = 1; q < S; ++q)
+        sum += __builtin_nontemporal_load(p + (int64_t)q * rows_per_tile * CPR);
+    const rsrc_t rc = make_rsrc(Cm);
+    const u32 base = (u32)(row * (int)ldc + col) * 2u;
+    if (vec4) {
+        // N is a multiple of 4 here, so the 4 columns are all valid
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
+                               u32x2{pack2<BF>(sum.x, sum.y), pack2<BF>(sum.z, sum.w)}),
+            rc, base, 0, 0);
+    } else {
+        const float xs[4] = {sum.x, sum.y, sum.z, sum.w};
 #pragma unroll
-    for (int k = 0; k < CPT; ++k)
-        sum[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int q0 = 0; q0 < S; q0 += QB) {
-        asm volatile("" ::: "memory");     // at most QB pieces' chunks in registers
-        f32x4 v[QB][CPT];
-#pragma unroll
-        for (int u = 0; u < QB; ++u)
-#pragma unroll
-            for (int k = 0; k < CPT; ++k) {
-                const int c = tid + k * C::NT;
-                v[u][k] = c / CPR < M && q0 + u < S && q0 + u != piece
-                              ? __builtin_nontemporal_load(tile + (int64_t)(q0 + u) * C::BM * CPR + c)
-                              : f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-        for (int u = 0; u < QB; ++u) {
-            if (q0 + u >= S)
-                break;
-#pragma unroll
-            for (int k = 0; k < CPT; ++k)
-                sum[k] += q0 + u == piece ? own[k] : v[u][k];
-        }
-    }
-    if (tid == 0)
-        __hip_atomic_store(tags + strip, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // C: each chunk is 4 consecutive columns of one row
-    const rsrc_t rc = make_rsrc(Cm + n0);
-    const int ld = (int)ldc, cols = N - n0;
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-        const int c = tid + k * C::NT, row = c / CPR, col = (c % CPR) * 4;
-        if (vec4) {
-            // cols is a multiple of 4 here, so the 4 columns are all valid or all not
-            const u32 off = (row < M && col < cols) ? (u32)(row * ld + col) * 2u : kOob;
-            __builtin_amdgcn_raw_buffer_store_b64(
-                __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
-                                   u32x2{pack2<BF>(sum[k].x, sum[k].y), pack2<BF>(sum[k].z, sum[k].w)}),
-                rc, off, 0, 0);
-        } else {
-            const float xs[4] = {sum[k].x, sum[k].y, sum[k].z, sum[k].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const u32 off = (row < M && col + e < cols) ? (u32)(row * ld + col + e) * 2u : kOob;
-                __builtin_amdgcn_raw_buffer_store_b16(f2h<BF>(xs[e]), rc, off, 0, 0);
-            }
-        }
+        for (int e = 0; e < 4; ++e)
+            if (col + e < N)
+                __builtin_amdgcn_raw_buffer_store_b16(f2h<BF>(xs[e]), rc, base + 2u * e, 0, 0);
     }
 }
 
@@ -2282,14 +2225,17 @@ hipError_t launch_skinny_split_t(const ClassicLaunch& L, hipStream_t st)
     const int strips = (L.N + C::BN - 1) / C::BN, S = L.split_s;
     if (strips == 0 || L.M == 0)
         return hipSuccess;
-    if ((S != 2 && S != 4 && S != 8) || L.split_id == 0 || (L.split_id & 15) != 0 ||
-        ((uintptr_t)L.split_ws % 256) != 0)
+    if ((S != 2 && S != 4 && S != 8) || L.M > C::BM || ((uintptr_t)L.split_ws % 256) != 0)
         return hipErrorInvalidValue;
     const int kh = ((L.K + S - 1) / S + C::BK - 1) / C::BK * C::BK;
-    char* ws = (char*)L.split_ws;
     hipLaunchKernelGGL((k_skinny_split<C, BF>), dim3((unsigned)((strips + 7) / 8 * 8 * S)), dim3(C::NT), 0, st,
-                       (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, (u16*)L.C, L.ldc, L.M, L.N, L.K, S, kh,
-                       L.vec4, (float*)ws, (uint64_t*)(ws + split_tag_offset(L.N, S, C::BM)), L.split_id);
+                       (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, L.M, L.N, L.K, S, kh, (float*)L.split_ws);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t chunks = (int64_t)L.M * ((L.N + 3) / 4);
+    hipLaunchKernelGGL((k_split_reduce<BF>), dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st,
+                       (const f32x4*)L.split_ws, S, C::BM, (u16*)L.C, L.ldc, L.M, L.N, L.vec4);
     return hipGetLastError();
 }
 

@@ -29,20 +29,17 @@ struct ClassicLaunch {
     int32_t P;         // compute units (for the XCD-aware tile order)
     // M <= 64: K split over split_s (2, 4 or 8) workgroups of each
     // kSplitCols-column strip (split_ws null: no split).  split_ws holds
-    // split_ws_bytes(N, split_s, split_rows(M)) bytes (256-byte aligned);
-    // split_id identifies the call (a non-zero multiple of 16, never reused
-    // in the process).
-    void* split_ws; uint64_t split_id; int32_t split_s;
+    // split_ws_bytes(N, split_s, split_rows(M)) bytes (256-byte aligned).
+    void* split_ws; int32_t split_s;
 };
 constexpr int kSplitCols = 128;
 inline int split_rows(int64_t M) { return M <= 32 ? 32 : 64; }                 // rows of the tile
 inline int64_t split_part_bytes(int rows) { return (int64_t)rows * kSplitCols * 4; }   // one fp32 partial tile
 inline int64_t split_strips(int64_t N) { return (N + kSplitCols - 1) / kSplitCols; }
-// Partials (S per strip), then one 64-bit arrival counter per strip.
-inline int64_t split_tag_offset(int64_t N, int S, int rows) { return split_strips(N) * S * split_part_bytes(rows); }
+// S partial tiles per strip.
 inline int64_t split_ws_bytes(int64_t N, int S, int rows)
 {
-    return (split_tag_offset(N, S, rows) + split_strips(N) * 8 + 255) / 256 * 256;
+    return (split_strips(N) * S * split_part_bytes(rows) + 255) / 256 * 256;
 }
 
 // Tile edge (rows, cols) of a classic tile shape.

@@ -264,16 +264,16 @@ lcma_status lcma_plan_estimate(lcma_plan_t plan, lcma_algo algo, double* est_sec
  * the planned size (may be NULL when that size is 0), 256-byte aligned; it
  * must not be used by two calls that can overlap.  Classic plans of up to
  * 64 rows whose K is long against their number of 128-column strips
- * (N <= 2048: K >= 2048; N <= 4096: K >= 4096; N <= 8192: K >= 8192;
- * wider N, 33..64 rows only: K >= 10240) have a workspace: 2, 4 or 8 workgroups per strip each take a
- * part of K and exchange fp32 partial tiles (32 or 64 rows x 128 columns)
- * through it ([KP] "GEMM 形状": such products stream B; the split cuts the
- * bytes of A each workgroup re-reads and fills the chip when the strips are
- * few).  The exchange needs no clearing: each call tags its arrivals with its
- * own identifier and the last arrival clears the tag, so any initial
- * contents, earlier calls and replays of a captured graph are handled; the
- * last arrival adds the partials in a fixed order.  Without 16-byte
- * alignment the unsplit kernels run instead.
+ * (N <= 4096: K >= 2048; N <= 8192: K >= 4096; wider N: 33..64 rows with
+ * K >= 8192, or K >= 4096 when N > 16384, and 17..32 rows with K >= 12288)
+ * have a workspace: 2, 4 or 8
+ * workgroups per strip each take a part of K and write an fp32 partial tile
+ * (the rows below M of 32 or 64 x 128) there, and a second kernel on the
+ * same stream adds the partials in a fixed order and rounds into C ([KP]
+ * "GEMM 形状": such products stream B; the split cuts the bytes of A each
+ * workgroup re-reads and fills the chip when the strips are few).  The
+ * workspace needs no clearing and keeps nothing between calls.  Without
+ * 16-byte alignment the unsplit kernels run instead.
  * Errors: LCMA_E_INVALID (NULL pointers with nonzero sizes, ld too small),
  * LCMA_E_WORKSPACE, LCMA_E_UNSUPPORTED, LCMA_E_HIP. */
 lcma_status lcma_gemm(lcma_plan_t plan, const void* A, int64_t lda, const void* B, int64_t ldb,

@@ -328,24 +328,25 @@ def test_unfused_plan_packs_its_a_operands_only_on_whole_tiles():
 def test_decode_shaped_classic_plans_take_the_k_split_workspace():
     # up to 64 rows with K long against the number of 128-column strips:
     # S = 2, 4 or 8 workgroups per strip, each an fp32 partial tile of 64 x
-    # 128 (32 KiB; 32 x 128, 16 KiB, up to 32 rows), then one 8-byte arrival
-    # counter per strip
+    # 128 (32 KiB; 32 x 128, 16 KiB, up to 32 rows)
     for (M, N, K), strips, S in (((64, 4096, 14336), 32, 8), ((33, 8192, 8192), 64, 4), ((48, 104, 8200), 1, 8),
-                                 ((64, 14336, 10240), 112, 2), ((40, 8192, 14336), 64, 4), ((64, 2048, 4096), 16, 4),
+                                 ((64, 14336, 10240), 112, 2), ((40, 8192, 14336), 64, 4), ((64, 2048, 4096), 16, 8),
                                  ((64, 1024, 14336), 8, 8), ((1, 1024, 14336), 8, 8), ((32, 1024, 12288), 8, 8),
-                                 ((1, 4096, 14336), 32, 4), ((16, 8192, 8192), 64, 2), ((8, 8192, 14336), 64, 4),
-                                 ((32, 2048, 4096), 16, 4), ((17, 1032, 12288), 9, 8), ((1, 1024, 8192), 8, 8),
-                                 ((32, 4096, 4096), 32, 4), ((64, 4096, 8184), 32, 4), ((1, 1024, 2048), 8, 4),
-                                 ((64, 1024, 4088), 8, 4), ((8, 8192, 8192), 64, 2), ((1, 2048, 4096), 16, 4),
-                                 ((40, 4096, 12280), 32, 4)):
+                                 ((1, 4096, 14336), 32, 8), ((16, 8192, 8192), 64, 4), ((8, 8192, 14336), 64, 4),
+                                 ((32, 2048, 4096), 16, 8), ((17, 1032, 12288), 9, 8), ((1, 1024, 8192), 8, 8),
+                                 ((32, 4096, 4096), 32, 8), ((64, 4096, 8184), 32, 8), ((1, 1024, 2048), 8, 8),
+                                 ((64, 1024, 4088), 8, 8), ((8, 8192, 8192), 64, 4), ((1, 2048, 4096), 16, 8),
+                                 ((40, 4096, 12280), 32, 8), ((64, 2048, 2048), 16, 4), ((1, 4096, 2048), 32, 4),
+                                 ((1, 8192, 4096), 64, 4), ((64, 28672, 4096), 224, 2), ((32, 14336, 14336), 112, 2),
+                                 ((48, 9000, 8192), 71, 2)):
         p = L.lcma_plan_ex(M, N, K, "bf16", force="classic", num_cus=CUS)
         algo, ws, _ = L.lcma_plan_info(p)
         assert algo == "classic"
         part = 32768 if M > 32 else 16384
-        assert ws == -(-(strips * S * part + strips * 8) // 256) * 256, (M, N, K, ws)
-    for M, N, K in ((65, 4096, 14336), (64, 14336, 4096), (64, 8200, 8192), (64, 4096, 4088), (64, 1024, 2040),
-                    (1, 8, 8), (8, 8192, 8184), (32, 8320, 14336), (1, 14336, 4096), (32, 4104, 4096),
-                    (1, 1024, 2040), (1, 28672, 14336), (64, 2048, 2040)):
+        assert ws == -(-(strips * S * part) // 256) * 256, (M, N, K, ws)
+    for M, N, K in ((65, 4096, 14336), (64, 14336, 4096), (64, 8200, 4096), (64, 4096, 2040), (64, 1024, 2040),
+                    (1, 8, 8), (8, 8192, 4088), (16, 8320, 14336), (1, 14336, 4096), (32, 4104, 4088),
+                    (1, 1024, 2040), (1, 28672, 14336), (64, 2048, 2040), (32, 14336, 8192), (64, 16384, 4096)):
         p = L.lcma_plan_ex(M, N, K, "bf16", force="classic", num_cus=CUS)
         assert L.lcma_plan_info(p)[1] == 0, (M, N, K)
 

@@ -471,12 +471,13 @@ def test_padded_lcma_matches_oracle(algo, M, N, K, dtype, dist):
 @pytest.mark.parametrize("M,N,K,dtype", [(64, 4096, 14336, "bf16"), (33, 8200, 10248, "f16"), (48, 1032, 8192, "bf16"),
                                        (57, 136, 8200, "f16"), (1, 1024, 14336, "bf16"), (1, 1032, 12296, "f16"),
                                        (13, 4104, 8200, "bf16"), (32, 136, 8200, "f16"), (8, 8064, 14336, "bf16"),
-                                       (29, 1000, 12344, "bf16"), (40, 2056, 4104, "f16"), (3, 3976, 6152, "bf16")])
+                                       (29, 1000, 12344, "bf16"), (40, 2056, 4104, "f16"), (3, 3976, 6152, "bf16"),
+                                       (48, 28680, 4104, "bf16"), (20, 14336, 12296, "f16")])
 def test_decode_k_split_matches_oracle(M, N, K, dtype):
     # classic plans of up to 64 rows with long K: 2, 4 or 8 workgroups per
-    # 128-column strip, one part of K each, partials exchanged through the
-    # workspace (32- and 64-row tiles; ragged rows, columns and k; one strip
-    # and many)
+    # 128-column strip, one part of K each, partials through the workspace
+    # and a second kernel that adds them (32- and 64-row tiles; ragged rows,
+    # columns and k; one strip and many)
     say("decode K split", M, N, K, dtype)
     A, B, A64, B64 = gen(M, N, K, dtype, "uniform" if dtype == "f16" else "normal_sqrtk", seed=61)
     plan = L.lcma_plan_ex(M, N, K, dtype, force="classic")
@@ -496,9 +497,9 @@ def test_decode_k_split_integer_inputs_are_exact(M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(64, 2056, 8192), (16, 1024, 14336)])
 def test_decode_k_split_any_workspace_contents_and_repeated_calls(M, N, K):
-    # the exchange needs no cleared workspace: random initial bytes, then
-    # calls with other inputs on the same workspace, then the first inputs
-    # again (bit for bit the first result)
+    # the split needs no cleared workspace: random initial bytes, then calls
+    # with other inputs on the same workspace, then the first inputs again
+    # (bit for bit the first result)
     say("decode K split workspace reuse", M, N, K)
     plan = L.lcma_plan_ex(M, N, K, "bf16", force="classic")
     ws = L.workspace_for(plan)
@@ -516,9 +517,9 @@ def test_decode_k_split_any_workspace_contents_and_repeated_calls(M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(48, 4104, 8200), (8, 4104, 14336)])
 def test_decode_k_split_graph_replays_with_new_inputs(M, N, K):
-    # a captured call keeps its call identifier; the last arrival clears
-    # each strip's tag, so every replay pairs its own pieces: each replay,
-    # after the inputs change in place, equals the eager product
+    # a captured call (the split kernel and the kernel that adds its
+    # partials) replays with the inputs changed in place: each replay equals
+    # the eager product, bit for bit
     say("decode K split graph", M, N, K)
     plan = L.lcma_plan_ex(M, N, K, "bf16", force="classic")
     ws = L.workspace_for(plan)
