@@ -515,6 +515,26 @@ def test_decode_k_split_any_workspace_contents_and_repeated_calls(M, N, K):
     assert np.array_equal(outs[0], outs[2])
 
 
+@pytest.mark.parametrize("M,N,K,ldc_pad", [(5, 1032, 8192, 3), (40, 2056, 4104, 16)])
+def test_decode_k_split_strided_operands_and_output(M, N, K, ldc_pad):
+    # leading dimensions beyond the extents (lda, ldb multiples of 8, so the
+    # split runs); ldc = N + 3 takes the reduction's 2-byte C stores, N + 16
+    # its 8-byte stores; nothing outside C is written
+    say("decode K split strided", M, N, K, ldc_pad)
+    Abig, Bbig, _, _ = gen(M, N + 24, K + 40, "bf16", "normal_sqrtk", seed=90)
+    A, B = Abig[:, :K], Bbig[:K, :N]
+    A64, B64 = si.f64(A), si.f64(B)
+    Ad, Bd = Abig.to(DEV)[:, :K], Bbig.to(DEV)[:K, :N]
+    plan = L.lcma_plan_ex(M, N, K, "bf16", force="classic")
+    assert L.lcma_plan_info(plan)[1] > 0
+    Cbig = torch.full((M, N + ldc_pad), 7.0, dtype=torch.bfloat16, device=DEV)
+    C = Cbig[:, :N]
+    L.lcma_gemm(plan, Ad, Bd, C, L.workspace_for(plan))
+    torch.cuda.synchronize()
+    check_float(C.cpu(), A64, B64, "bf16")
+    assert torch.all(Cbig[:, N:].cpu() == 7.0)
+
+
 @pytest.mark.parametrize("M,N,K", [(48, 4104, 8200), (8, 4104, 14336)])
 def test_decode_k_split_graph_replays_with_new_inputs(M, N, K):
     # a captured call (the split kernel and the kernel that adds its
