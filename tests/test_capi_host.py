@@ -351,6 +351,19 @@ def test_decode_shaped_classic_plans_take_the_k_split_workspace():
         assert L.lcma_plan_info(p)[1] == 0, (M, N, K)
 
 
+def test_ragged_decode_plans_pad_then_split():
+    # K or N not a multiple of 8: the plan pads A, B and C into its workspace
+    # and runs the padded product's plan after them, here a K split
+    up = lambda x: -(-x // 256) * 256
+    for (M, N, K), S in (((3, 1030, 14330), 8), ((50, 2050, 6150), 8)):
+        Np, Kp = -(-N // 8) * 8, -(-K // 8) * 8
+        strips = -(-Np // 128)
+        inner = L.lcma_plan_info(L.lcma_plan_ex(M, Np, Kp, "bf16", force="classic", num_cus=CUS))[1]
+        assert inner == up(strips * S * (16384 if M <= 32 else 32768))
+        ws = L.lcma_plan_info(L.lcma_plan_ex(M, N, K, "bf16", force="classic", num_cus=CUS))[1]
+        assert ws == up(up(up(M * Kp * 2) + Kp * Np * 2) + M * Np * 2) + inner, (M, N, K, ws)
+
+
 def test_bf16_two_level_writes_every_operand_in_binary16():
     p = L.lcma_plan_ex(4096, 4096, 4096, "bf16", force="l2", num_cus=CUS)
     for r in range(49):

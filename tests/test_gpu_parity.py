@@ -472,12 +472,14 @@ def test_padded_lcma_matches_oracle(algo, M, N, K, dtype, dist):
                                        (57, 136, 8200, "f16"), (1, 1024, 14336, "bf16"), (1, 1032, 12296, "f16"),
                                        (13, 4104, 8200, "bf16"), (32, 136, 8200, "f16"), (8, 8064, 14336, "bf16"),
                                        (29, 1000, 12344, "bf16"), (40, 2056, 4104, "f16"), (3, 3976, 6152, "bf16"),
-                                       (48, 28680, 4104, "bf16"), (20, 14336, 12296, "f16")])
+                                       (48, 28680, 4104, "bf16"), (20, 14336, 12296, "f16"), (3, 1030, 14330, "f16"),
+                                       (50, 2050, 6150, "bf16")])
 def test_decode_k_split_matches_oracle(M, N, K, dtype):
     # classic plans of up to 64 rows with long K: 2, 4 or 8 workgroups per
     # 128-column strip, one part of K each, partials through the workspace
     # and a second kernel that adds them (32- and 64-row tiles; ragged rows,
-    # columns and k; one strip and many)
+    # columns and k; one strip and many; K and N not multiples of 8, where
+    # the plan pads into its workspace and splits the padded product)
     say("decode K split", M, N, K, dtype)
     A, B, A64, B64 = gen(M, N, K, dtype, "uniform" if dtype == "f16" else "normal_sqrtk", seed=61)
     plan = L.lcma_plan_ex(M, N, K, dtype, force="classic")
