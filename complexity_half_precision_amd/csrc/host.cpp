@@ -484,6 +484,26 @@ int split_pieces(int64_t M, int64_t N, int64_t K)
     return M > 16 && K >= 12288 ? 2 : 0;
 }
 
+// Pieces of K for the classic kernel beyond 64 rows (128 x 128 tiles): when
+// its tiles fill at most half the compute units and K is long, S pieces of K
+// per tile write fp32 planes that a second launch adds; S is the largest of
+// 2, 4, 8 that keeps tiles x S within the compute units and 2048 of K per
+// piece.  0 for none.  Measured on MI355X (bfloat16, 15 shapes, S in 0, 2,
+// 4, 8): the rule picks the fastest S on all of them (4096 x 256 x 8192:
+// 52.9 us unsplit, 26.9 with S = 4; 256 x 8192 x 14336: 169.6, 105.2 with
+// S = 2; 256 x 256 x 16384: 103.6, 22.4 with S = 8; 2048 x 2048 x 8192,
+// 256 tiles: 63.9 unsplit, 75.8 with S = 2).
+int classic_split_pieces(int64_t M, int64_t N, int64_t K, int P)
+{
+    if (M <= 64 || N % 8 != 0 || K % 8 != 0)
+        return 0;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    int S = 1;
+    while (S < 8 && tiles * S * 2 <= P && K / (S * 2) >= 2048)
+        S *= 2;
+    return S > 1 ? S : 0;
+}
+
 }  // namespace
 
 lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const lcma_desc* desc,
@@ -736,6 +756,11 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     p->split_s = p->levels == 0 ? split_pieces(M, N, K) : 0;
     if (p->split_s)
         p->ws_bytes = (size_t)split_ws_bytes(N, p->split_s, split_rows(M));
+    // classic plans beyond 64 rows with few tiles: K split on 128 x 128 tiles
+    if (p->levels == 0 && M > 64 && (p->split_s = classic_split_pieces(M, N, K, m.P)) != 0) {
+        p->classic_tile = kTile128;
+        p->ws_bytes = (size_t)((p->split_s * M * N * 4 + 255) / 256 * 256);
+    }
     p->unfused = p->levels == 1 && (unfused || l1_unfused_auto);
     if (p->unfused) {
         p->op_bf16 = op_bf16_for(1);

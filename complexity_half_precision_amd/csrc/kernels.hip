@@ -1496,33 +1496,57 @@ __device__ __forceinline__ void store_c_staged(const f32x4 (&acc)[C::FM][C::FN],
 
 using MC256 = m16::Cfg<256, 256, 2, 4>;   // 8 waves (2 per SIMD) of 128 x 64, 16x16x32 MFMAs
 
-template <class C, bool BF>
+template <class C, bool BF, bool PART = false>
 __global__ void __launch_bounds__(C::NT, 1)
 k_classic_m16(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb, u16* __restrict__ Cm,
-              int64_t ldc, int M, int N, int K, int gy, int gx, int P, int vec4, int vec8)
+              int64_t ldc, int M, int N, int K, int gy, int gx, int P, int vec4, int vec8, int kh,
+              float* __restrict__ part)
 {
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_ALLOC];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN;
+    // PART: block b is piece b / tiles (k in [piece kh, piece kh + kh)) of
+    // tile b % tiles, which writes an fp32 partial tile of plane `piece`.
+    const int tiles = gy * gx;
+    const int piece = PART ? (int)blockIdx.x / tiles : 0;
     int p, q;
-    tile_coords((int32_t)blockIdx.x, gy, gx, P, 8, &p, &q);
+    tile_coords(PART ? (int32_t)blockIdx.x % tiles : (int32_t)blockIdx.x, gy, gx, P, 8, &p, &q);
     const int m0 = p * C::BM, n0 = q * C::BN;
-    const u16* Ab = A + (int64_t)m0 * lda;
-    const u16* Bb = B + n0;
-    const int nk = (K + C::BK - 1) / C::BK;
+    const int kb = piece * kh, klen = PART ? max(0, min(K - kb, kh)) : K;
+    const u16* Ab = A + (int64_t)m0 * lda + kb;
+    const u16* Bb = B + (int64_t)kb * ldb + n0;
+    const int nk = (klen + C::BK - 1) / C::BK;
     f32x4 acc[C::FM][C::FN];
     zero_acc<C>(acc);
     auto src = [&](int t) {
-        return tiles::TileSrc{Ab, (int)lda, M - m0, Bb, (int)ldb, N - n0, t * C::BK, K};
+        return tiles::TileSrc{Ab, (int)lda, M - m0, Bb, (int)ldb, N - n0, t * C::BK, klen};
     };
     const m16::Addr<C> ad = m16::frag_addr<C>(wm, wn, lane);
-    const bool inside = (m0 + C::BM <= M) & (n0 + C::BN <= N) & (K % C::BK == 0);
+    const bool inside = (m0 + C::BM <= M) & (n0 + C::BN <= N) & (klen % C::BK == 0);
     auto none = [](int) {};
-    if (inside)
-        m16::run_tile<C, BF, false, true>(smem, nk, src, none, wave, lane, ad, acc);
-    else
-        m16::run_tile<C, BF, true, false>(smem, nk, src, none, wave, lane, ad, acc);
+    if (!PART || nk > 0) {
+        if (inside)
+            m16::run_tile<C, BF, false, true>(smem, nk, src, none, wave, lane, ad, acc);
+        else
+            m16::run_tile<C, BF, true, false>(smem, nk, src, none, wave, lane, ad, acc);
+    }
+    if constexpr (PART) {
+        // lane l of accumulator tile (i, j): row 16 i + l % 16, columns
+        // 16 j + 4 (l / 16) .. + 3 of the wave's tile; N is a multiple of 8
+        // on this path, so each 4-column group is wholly inside or out
+        const rsrc_t rp = make_rsrc(part + (int64_t)piece * M * N + (int64_t)m0 * N + n0);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) {
+                const int m = wm * C::WTM + i * 16 + (lane & 15), n = wn * C::WTN + j * 16 + 4 * (lane >> 4);
+                const u32 off = (m < M - m0 && n < N - n0) ? (u32)(m * N + n) * 4u : kOob;
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, acc[i][j]), rp, off, 0, 0);
+            }
+        return;
+    }
     if (vec8) {
         __syncthreads();
         m16::store_c_staged<C, BF>(acc, smem, Cm + (int64_t)m0 * ldc + n0, ldc, M - m0, N - n0, wave, wm, wn, lane);
@@ -1542,7 +1566,7 @@ hipError_t launch_classic_m16_t(const ClassicLaunch& L, hipStream_t st)
     const int vec8 = L.vec4 && ((uintptr_t)L.C % 16 == 0) && (L.ldc % 8 == 0) && (L.N % 8 == 0);
     hipLaunchKernelGGL((k_classic_m16<C, BF>), dim3((unsigned)tiles), dim3(C::NT), 0, st,
                        (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, (u16*)L.C, L.ldc, L.M, L.N, L.K,
-                       gy, gx, L.P, L.vec4, vec8);
+                       gy, gx, L.P, L.vec4, vec8, L.K, nullptr);
     return hipGetLastError();
 }
 
@@ -2185,38 +2209,50 @@ k_skinny_split(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B
     }
 }
 
-// C = the sum of the S partial tiles of each strip, in piece order, rounded
-// once: one thread per 4 consecutive columns of one row (consecutive threads
-// read consecutive 16-byte chunks of a partial row).
+// C = the sum of the S partials of each output element, in piece order,
+// rounded once.  The partials are tiles of `rows` x W fp32 per strip of W
+// columns, the S pieces of a strip one after another (W = 128, rows = the
+// streaming kernel's tile rows; or W = N, rows = M: S full planes).  One
+// thread per 4 consecutive columns of one row, so consecutive threads read
+// consecutive 16-byte chunks of a partial row.
 template <bool BF>
-__global__ void __launch_bounds__(256) k_split_reduce(const f32x4* __restrict__ part, int S, int rows_per_tile,
+__global__ void __launch_bounds__(256) k_split_reduce(const f32x4* __restrict__ part, int S, int rows, int W,
                                                       u16* __restrict__ Cm, int64_t ldc, int M, int N, int vec4)
 {
-    constexpr int CPR = kSplitCols / 4;
-    const int cpr = (N + 3) / 4;
-    const int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= M * cpr)
+    const int64_t cpr = (N + 3) / 4;
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= (int64_t)M * cpr)
         return;
-    const int row = c / cpr, col = (c % cpr) * 4;
-    const f32x4* p = part + (int64_t)(col / kSplitCols) * S * rows_per_tile * CPR + row * CPR + (col % kSplitCols) / 4;
+    const int row = (int)(c / cpr), col = (int)(c % cpr) * 4;
+    const int64_t cpw = W / 4, tile = (int64_t)rows * cpw;
+    const f32x4* p = part + (int64_t)(col / W) * S * tile + (int64_t)row * cpw + (col % W) / 4;
     f32x4 sum = __builtin_nontemporal_load(p);
     for (int q = 1; q < S; ++q)
-        sum += __builtin_nontemporal_load(p + (int64_t)q * rows_per_tile * CPR);
-    const rsrc_t rc = make_rsrc(Cm);
-    const u32 base = (u32)(row * (int)ldc + col) * 2u;
+        sum += __builtin_nontemporal_load(p + q * tile);
+    u16* out = Cm + (int64_t)row * ldc + col;
     if (vec4) {
-        // N is a multiple of 4 here, so the 4 columns are all valid
-        __builtin_amdgcn_raw_buffer_store_b64(
-            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
-                               u32x2{pack2<BF>(sum.x, sum.y), pack2<BF>(sum.z, sum.w)}),
-            rc, base, 0, 0);
+        // C 8-byte aligned, ldc and N multiples of 4: the 4 columns are all valid
+        *reinterpret_cast<u32x2*>(out) = u32x2{pack2<BF>(sum.x, sum.y), pack2<BF>(sum.z, sum.w)};
     } else {
         const float xs[4] = {sum.x, sum.y, sum.z, sum.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             if (col + e < N)
-                __builtin_amdgcn_raw_buffer_store_b16(f2h<BF>(xs[e]), rc, base + 2u * e, 0, 0);
+                out[e] = f2h<BF>(xs[e]);
     }
+}
+
+// The reduction launch after a K-split kernel.
+template <bool BF>
+hipError_t launch_split_reduce(const ClassicLaunch& L, int rows, int W, hipStream_t st)
+{
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t chunks = (int64_t)L.M * ((L.N + 3) / 4);
+    hipLaunchKernelGGL((k_split_reduce<BF>), dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st,
+                       (const f32x4*)L.split_ws, L.split_s, rows, W, (u16*)L.C, L.ldc, L.M, L.N, L.vec4);
+    return hipGetLastError();
 }
 
 template <class C, bool BF>
@@ -2230,13 +2266,25 @@ hipError_t launch_skinny_split_t(const ClassicLaunch& L, hipStream_t st)
     const int kh = ((L.K + S - 1) / S + C::BK - 1) / C::BK * C::BK;
     hipLaunchKernelGGL((k_skinny_split<C, BF>), dim3((unsigned)((strips + 7) / 8 * 8 * S)), dim3(C::NT), 0, st,
                        (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, L.M, L.N, L.K, S, kh, (float*)L.split_ws);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    const int64_t chunks = (int64_t)L.M * ((L.N + 3) / 4);
-    hipLaunchKernelGGL((k_split_reduce<BF>), dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st,
-                       (const f32x4*)L.split_ws, S, C::BM, (u16*)L.C, L.ldc, L.M, L.N, L.vec4);
-    return hipGetLastError();
+    return launch_split_reduce<BF>(L, C::BM, kSplitCols, st);
+}
+
+// K split of the 256-row-and-up classic kernel (128 x 128 tiles, long K):
+// S pieces of K per tile write S fp32 planes of M x N, then the reduction.
+template <class C, bool BF>
+hipError_t launch_classic_m16_split_t(const ClassicLaunch& L, hipStream_t st)
+{
+    const int gy = (L.M + C::BM - 1) / C::BM, gx = (L.N + C::BN - 1) / C::BN, S = L.split_s;
+    const long tiles = (long)gy * gx;
+    if (tiles == 0)
+        return hipSuccess;
+    if ((S != 2 && S != 4 && S != 8) || L.N % 4 != 0 || ((uintptr_t)L.split_ws % 256) != 0)
+        return hipErrorInvalidValue;
+    const int kh = ((L.K + S - 1) / S + C::BK - 1) / C::BK * C::BK;
+    hipLaunchKernelGGL((k_classic_m16<C, BF, true>), dim3((unsigned)(tiles * S)), dim3(C::NT), 0, st,
+                       (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, (u16*)L.C, L.ldc, L.M, L.N, L.K,
+                       gy, gx, L.P, 0, 0, kh, (float*)L.split_ws);
+    return launch_split_reduce<BF>(L, L.M, L.N, st);
 }
 
 template <class C, bool BF>
@@ -3064,6 +3112,9 @@ hipError_t launch_classic(const ClassicLaunch& L, hipStream_t st)
             return L.bf16 ? launch_classic_m16_t<MC256, true>(L, st) : launch_classic_m16_t<MC256, false>(L, st);
         return launch_classic_c<Cfg256>(L, st);
     case kTile128:
+        if (L.vec && L.split_ws)
+            return L.bf16 ? launch_classic_m16_split_t<MC128, true>(L, st)
+                          : launch_classic_m16_split_t<MC128, false>(L, st);
         if (L.vec && L.K >= kLongK128)
             return L.bf16 ? launch_classic_m16_t<MC128, true>(L, st) : launch_classic_m16_t<MC128, false>(L, st);
         if (L.vec)

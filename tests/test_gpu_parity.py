@@ -497,7 +497,7 @@ def test_decode_k_split_integer_inputs_are_exact(M, N, K):
     check_exact(planned(A, B, "classic"), A64, B64, "f16")
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 2056, 8192), (16, 1024, 14336)])
+@pytest.mark.parametrize("M,N,K", [(64, 2056, 8192), (16, 1024, 14336), (2048, 512, 8192)])
 def test_decode_k_split_any_workspace_contents_and_repeated_calls(M, N, K):
     # the split needs no cleared workspace: random initial bytes, then calls
     # with other inputs on the same workspace, then the first inputs again
@@ -515,6 +515,43 @@ def test_decode_k_split_any_workspace_contents_and_repeated_calls(M, N, K):
         check_float(C.cpu(), A64, B64, "bf16")
         outs.append(si.bits(C.cpu()))
     assert np.array_equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("M,N,K,dtype", [(4096, 256, 8192, "bf16"), (256, 8192, 4096, "f16"), (1000, 264, 8200, "bf16"),
+                                       (300, 136, 16392, "f16"), (128, 14336, 4096, "bf16"), (65, 128, 4104, "bf16")])
+def test_classic_k_split_matches_oracle(M, N, K, dtype):
+    # classic plans beyond 64 rows with few 128 x 128 tiles and long K: S
+    # pieces of K per tile write fp32 planes, a second kernel adds them in
+    # piece order (ragged rows, columns and k; S = 2, 4, 8)
+    say("classic K split", M, N, K, dtype)
+    A, B, A64, B64 = gen(M, N, K, dtype, "uniform" if dtype == "f16" else "normal_sqrtk", seed=63)
+    plan = L.lcma_plan_ex(M, N, K, dtype, force="classic")
+    assert L.lcma_plan_info(plan)[1] > 0
+    check_float(planned(A, B, "classic"), A64, B64, dtype)
+
+
+def test_classic_k_split_integer_inputs_are_exact():
+    say("classic K split exact")
+    A, B, A64, B64 = gen(2048, 512, 8192, "f16", "int1", seed=64)
+    assert np.abs(oracle.gemm(A64, B64)).max() <= 2048
+    check_exact(planned(A, B, "classic"), A64, B64, "f16")
+
+
+@pytest.mark.parametrize("M,N,K,ldc_pad", [(1024, 1024, 8192, 3), (4096, 256, 8192, 16)])
+def test_classic_k_split_strided_operands_and_output(M, N, K, ldc_pad):
+    say("classic K split strided", M, N, K, ldc_pad)
+    Abig, Bbig, _, _ = gen(M, N + 24, K + 40, "bf16", "normal_sqrtk", seed=91)
+    A, B = Abig[:, :K], Bbig[:K, :N]
+    A64, B64 = si.f64(A), si.f64(B)
+    Ad, Bd = Abig.to(DEV)[:, :K], Bbig.to(DEV)[:K, :N]
+    plan = L.lcma_plan_ex(M, N, K, "bf16", force="classic")
+    assert L.lcma_plan_info(plan)[1] > 0
+    Cbig = torch.full((M, N + ldc_pad), 7.0, dtype=torch.bfloat16, device=DEV)
+    C = Cbig[:, :N]
+    L.lcma_gemm(plan, Ad, Bd, C, L.workspace_for(plan))
+    torch.cuda.synchronize()
+    check_float(C.cpu(), A64, B64, "bf16")
+    assert torch.all(Cbig[:, N:].cpu() == 7.0)
 
 
 @pytest.mark.parametrize("M,N,K,ldc_pad", [(5, 1032, 8192, 3), (40, 2056, 4104, 16)])
@@ -537,7 +574,7 @@ def test_decode_k_split_strided_operands_and_output(M, N, K, ldc_pad):
     assert torch.all(Cbig[:, N:].cpu() == 7.0)
 
 
-@pytest.mark.parametrize("M,N,K", [(48, 4104, 8200), (8, 4104, 14336)])
+@pytest.mark.parametrize("M,N,K", [(48, 4104, 8200), (8, 4104, 14336), (1024, 1024, 8192)])
 def test_decode_k_split_graph_replays_with_new_inputs(M, N, K):
     # a captured call (the split kernel and the kernel that adds its
     # partials) replays with the inputs changed in place: each replay equals
