@@ -272,8 +272,11 @@ lcma_status lcma_plan_estimate(lcma_plan_t plan, lcma_algo algo, double* est_sec
  * same stream adds the partials in a fixed order and rounds into C ([KP]
  * "GEMM 形状": such products stream B; the split cuts the bytes of A each
  * workgroup re-reads and fills the chip when the strips are few).  The
- * workspace needs no clearing and keeps nothing between calls.  Without
- * 16-byte alignment the unsplit kernels run instead.
+ * workspace needs no clearing and keeps nothing between calls.  Classic
+ * plans beyond 64 rows whose 128 x 128 tiles fill at most half the compute
+ * units, with K >= 4096, split K the same way into S fp32 planes of M x N
+ * (S = 2, 4 or 8).  Without 16-byte alignment the unsplit kernels run
+ * instead.
  * Errors: LCMA_E_INVALID (NULL pointers with nonzero sizes, ld too small),
  * LCMA_E_WORKSPACE, LCMA_E_UNSUPPORTED, LCMA_E_HIP. */
 lcma_status lcma_gemm(lcma_plan_t plan, const void* A, int64_t lda, const void* B, int64_t ldb,
