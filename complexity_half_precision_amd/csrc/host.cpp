@@ -487,19 +487,23 @@ int split_pieces(int64_t M, int64_t N, int64_t K)
 // Pieces of K for the classic kernel beyond 64 rows (128 x 128 tiles): when
 // its tiles fill at most half the compute units and K is long, S pieces of K
 // per tile write fp32 planes that a second launch adds; S is the largest of
-// 2, 4, 8 that keeps tiles x S within the compute units and 2048 of K per
-// piece.  0 for none.  Measured on MI355X (bfloat16, 15 shapes, S in 0, 2,
-// 4, 8): the rule picks the fastest S on all of them (4096 x 256 x 8192:
-// 52.9 us unsplit, 26.9 with S = 4; 256 x 8192 x 14336: 169.6, 105.2 with
-// S = 2; 256 x 256 x 16384: 103.6, 22.4 with S = 8; 2048 x 2048 x 8192,
-// 256 tiles: 63.9 unsplit, 75.8 with S = 2).
+// 2, 4, 8 that keeps tiles x S within the compute units and 768 of K per
+// piece.  0 for none.  Measured on MI355X (bfloat16, S in 0, 2, 4, 8): on
+// the 26 shapes with K >= 4096 the rule picks the fastest S (4096 x 256 x
+// 8192: 52.9 us unsplit, 26.9 with S = 4; 256 x 8192 x 14336: 169.6, 105.2
+// with S = 2; 256 x 256 x 16384: 103.6, 22.4 with S = 8; 1024 x 512 x 6144:
+// 49.8, 20.8 with S = 8; 2048 x 2048 x 8192, 256 tiles: 63.9 unsplit, 75.8
+// with S = 2).  K = 2048 stays unsplit: the split gained up to 11% at
+// 1024 x 1024 x 2048 and lost at 4096 x 256 x 2048.
 int classic_split_pieces(int64_t M, int64_t N, int64_t K, int P)
 {
     if (M <= 64 || N % 8 != 0 || K % 8 != 0)
         return 0;
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
     int S = 1;
-    while (S < 8 && tiles * S * 2 <= P && K / (S * 2) >= 2048)
+    if (K < 4096)
+        return 0;
+    while (S < 8 && tiles * S * 2 <= P && K / (S * 2) >= 768)
         S *= 2;
     return S > 1 ? S : 0;
 }

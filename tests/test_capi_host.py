@@ -353,17 +353,18 @@ def test_decode_shaped_classic_plans_take_the_k_split_workspace():
 
 def test_few_tile_classic_plans_split_k_into_fp32_planes():
     # beyond 64 rows, 128 x 128 tiles filling at most half the compute
-    # units with K >= 4096: S planes of M x N fp32 (tiles x S <= CUs, 2048 of
+    # units with K >= 4096: S planes of M x N fp32 (tiles x S <= CUs, 768 of
     # K per piece at least)
     for (M, N, K), S in (((4096, 256, 8192), 4), ((256, 8192, 4096), 2), ((256, 256, 16384), 8),
-                         ((128, 14336, 4096), 2), ((1000, 264, 8200), 4), ((300, 136, 16392), 8),
-                         ((1024, 1024, 8192), 4), ((65, 128, 4096), 2)):
+                         ((128, 14336, 4096), 2), ((1000, 264, 8200), 8), ((300, 136, 16392), 8),
+                         ((1024, 1024, 8192), 4), ((65, 128, 4096), 4), ((4096, 256, 4096), 4),
+                         ((1024, 512, 6144), 8), ((512, 1024, 4096), 4)):
         p = L.lcma_plan_ex(M, N, K, "bf16", force="classic", num_cus=CUS)
         algo, ws, _ = L.lcma_plan_info(p)
         assert algo == "classic"
         assert ws == -(-(S * M * N * 4) // 256) * 256, (M, N, K, ws)
     # full rounds of tiles, short K, or not multiples of 8 (those pad first)
-    for M, N, K in ((2048, 2048, 8192), (4096, 4096, 4096), (4096, 256, 2048), (1024, 1024, 4088),
+    for M, N, K in ((2048, 2048, 8192), (4096, 4096, 4096), (4096, 256, 2048), (1024, 1024, 4088), (1024, 1024, 4080),
                     (8192, 8192, 8192)):
         p = L.lcma_plan_ex(M, N, K, "bf16", force="classic", num_cus=CUS)
         assert L.lcma_plan_info(p)[1] == 0, (M, N, K)
