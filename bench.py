@@ -639,8 +639,9 @@ def sweep_picks(L, si, torch, time_calls):
                 p = L.lcma_plan_ex(M, N, K, "f16", force=algo)
             except L.LcmaError:
                 continue
-            ws = L.workspace_for(p)
-            times[algo] = time_calls(lambda: L.lcma_gemm(p, Ad, Bd, Cd, ws), 20, 3)
+            # prepared once: the per-call argument checks of the binding would
+            # otherwise set the pace for the small shapes
+            times[algo] = time_calls(L.lcma_gemm_prepared(p, Ad, Bd, Cd, L.workspace_for(p)), 20, 3)
         best = min(times, key=times.get)
         agree += pick == best
         rows.append({"shape": [M, N, K], "pick": pick, "best": best,
