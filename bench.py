@@ -375,6 +375,9 @@ def main():
         out["square_512_f16"] = small_square(L, si, torch, time_calls)
         out["decode"] = decode_bandwidth(L, si, torch, time_calls)
         out["decode_long_k"] = decode_bandwidth(L, si, torch, time_calls, si.decode_long_k_shape)
+        for leg in (out["decode"], out["decode_long_k"]):       # against the measured read-only stream
+            for v in leg.values():
+                v["frac_of_read_ref"] = round(v["hbm_gbps"] / out["machine"]["hbm_read_gbps"], 3)
         out["sweep"] = sweep_picks(L, si, torch, time_calls)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(A, B, args.cpu_seconds)
@@ -402,9 +405,9 @@ def targets(out):
 
 def machine_refs(L, torch, time_calls):
     """Measured references beside the published peaks: the library's MFMA loop
-    (16x16x32, random operands, 2 workgroups of 8 waves per compute unit) and
-    its HBM stream kernel (1 GiB copied, read + write counted), plus torch's
-    device copy of the same buffers."""
+    (16x16x32, random operands, 2 workgroups of 8 waves per compute unit), its
+    HBM stream kernels (1 GiB copied, read + write counted; 1 GiB read), plus
+    torch's device copy of the same buffers."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     res = {}
     wg, iters = 2 * cus, 20000
@@ -423,7 +426,10 @@ def machine_refs(L, torch, time_calls):
     res["hbm_stream_gbps"] = round(2.0 * n / (t * 1e-3) / 1e9, 1)
     t = time_calls(lambda: dst.copy_(src), 10, 3)
     res["torch_copy_gbps"] = round(2.0 * n / (t * 1e-3) / 1e9, 1)
-    del src, dst
+    word = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t = time_calls(lambda: L.lcma_measure_read(src, word), 10, 3)
+    res["hbm_read_gbps"] = round(n / (t * 1e-3) / 1e9, 1)
+    del src, dst, word
     # the vendor library's GEMM on the headline shape, as context for the classic kernel
     g = torch.Generator(device="cuda").manual_seed(7)
     a = (torch.randn(4096, 4096, device="cuda", generator=g) / 64).to(torch.bfloat16)
@@ -431,7 +437,8 @@ def machine_refs(L, torch, time_calls):
     c = torch.empty(4096, 4096, device="cuda", dtype=torch.bfloat16)
     t = time_calls(lambda: torch.matmul(a, b, out=c), 200, 200)     # its first calls run slower: warm it up well
     res["torch_matmul_4096_bf16_tflops"] = round(2.0 * 4096 ** 3 / (t * 1e-3) / 1e12, 1)
-    res["note"] = ("mfma: %d workgroups x 8 waves x %d x 16 MFMAs per launch; stream: %d bytes read and written; "
+    res["note"] = ("mfma: %d workgroups x 8 waves x %d x 16 MFMAs per launch; stream: %d bytes read and written "
+                   "(copy) or read (read); "
                    "torch.matmul: the vendor BLAS on 4096^3 bfloat16, context only" % (wg, iters, n))
     del out, a, b, c
     torch.cuda.empty_cache()

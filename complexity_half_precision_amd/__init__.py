@@ -78,6 +78,7 @@ _lib_plan_estimate = _sig("lcma_plan_estimate", _i32, [_vp, _i32, ctypes.POINTER
 _lib_gemm = _sig("lcma_gemm", _i32, [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp])
 _lib_measure_mfma = _sig("lcma_measure_mfma", _i32, [_vp, _i32, _i32, _i32, _vp])
 _lib_measure_copy = _sig("lcma_measure_copy", _i32, [_vp, _vp, _sz, _vp])
+_lib_measure_read = _sig("lcma_measure_read", _i32, [_vp, _sz, _vp, _vp])
 _lib_gemm_noalloc = _sig("lcma_gemm_noalloc", _i32, [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp])
 _lib_prepass = _sig("lcma_prepass", _i32, [_vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp])
 _lib_fused = _sig("lcma_fused", _i32, [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp])
@@ -91,7 +92,7 @@ _lib_plan_destroy = _sig("lcma_plan_destroy", None, [_vp])
 EXPORTED = ["lcma_status_str", "lcma_desc_builtin", "lcma_desc_validate", "lcma_plan", "lcma_plan_ex",
             "lcma_plan_info", "lcma_plan_estimate", "lcma_gemm", "lcma_prepass", "lcma_fused",
             "lcma_plan_operand", "lcma_plan_schedule", "gemm_classic", "lcma_plan_destroy", "lcma_gemm_noalloc",
-            "lcma_measure_mfma", "lcma_measure_copy"]
+            "lcma_measure_mfma", "lcma_measure_copy", "lcma_measure_read"]
 SCRATCH_BYTES = 64 << 20   # LCMA_SCRATCH_BYTES
 
 
@@ -372,6 +373,15 @@ def lcma_measure_copy(src, dst, stream=None) -> None:
     if not (src.is_cuda and dst.is_cuda) or dst.numel() * dst.element_size() < n:
         raise ValueError("src, dst: device tensors, dst at least as large as src")
     _check(_lib_measure_copy(_ptr(src), _ptr(dst), n, _stream(stream)), "lcma_measure_copy")
+
+
+def lcma_measure_read(src, out, stream=None) -> None:
+    """Enqueues the read-only HBM stream reference over src; out is a device
+    tensor of at least 4 bytes that the kernel may write (value unspecified)."""
+    n = src.numel() * src.element_size()
+    if not (src.is_cuda and out.is_cuda) or out.numel() * out.element_size() < 4:
+        raise ValueError("src, out: device tensors, out at least 4 bytes")
+    _check(_lib_measure_read(_ptr(src), n, _ptr(out), _stream(stream)), "lcma_measure_read")
 
 
 def _ws_bytes(workspace):

@@ -1457,6 +1457,22 @@ lcma_status lcma_measure_copy(const void* src, void* dst, size_t bytes, void* st
     return hip_status(launch_ref_copy(src, dst, (int64_t)(bytes / 16), 64 * P, (hipStream_t)stream), "launch_ref_copy");
 }
 
+lcma_status lcma_measure_read(const void* src, size_t bytes, uint32_t* out, void* stream)
+{
+    if (bytes == 0)
+        return LCMA_OK;
+    if (!src || !out)
+        return LCMA_E_INVALID;
+    if ((uintptr_t)src % 16 || bytes % 16)
+        return LCMA_E_UNSUPPORTED;
+    int P = 0;
+    if (query_cus(&P) != 0)
+        return LCMA_E_HIP;
+    // 16 workgroups per compute unit: eight 16-byte loads in flight per lane
+    return hip_status(launch_ref_read(src, (int64_t)(bytes / 16), 16 * P, 0x9e3779b9u, out, (hipStream_t)stream),
+                      "launch_ref_read");
+}
+
 lcma_status lcma_gemm_noalloc(lcma_plan_t p, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                               int64_t ldc, void* stream)
 {

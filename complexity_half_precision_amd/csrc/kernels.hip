@@ -3064,7 +3064,38 @@ __global__ void __launch_bounds__(256) k_ref_copy(const u32x4* __restrict__ src,
     }
 }
 
+// Reads src once: each workgroup one contiguous chunk of `per` 16-byte
+// chunks, eight loads in flight per lane, folded into one word per lane that
+// is stored only when it equals `never` (so the loads stay live and nothing
+// is written in practice).
+__global__ void __launch_bounds__(256) k_ref_read(const u32x4* __restrict__ src, int64_t n, int64_t per, u32 never,
+                                                  u32* __restrict__ out)
+{
+    const int64_t b = (int64_t)blockIdx.x * per;
+    const int64_t e = b + per < n ? b + per : n;
+    u32 acc = 0;
+    for (int64_t i = b + threadIdx.x; i < e; i += 8 * 256) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = i + u * 256 < e ? __builtin_nontemporal_load(src + i + u * 256) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    if (acc == never)
+        *out = acc;
+}
+
 }  // namespace
+
+hipError_t launch_ref_read(const void* src, int64_t chunks, int32_t workgroups, uint32_t never, uint32_t* out,
+                           hipStream_t st)
+{
+    const int64_t per = (chunks + workgroups - 1) / workgroups;
+    hipLaunchKernelGGL(k_ref_read, dim3(workgroups), dim3(256), 0, st, (const u32x4*)src, chunks, per, never, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_ref_mfma(float* out, int32_t workgroups, int32_t iters, int32_t bf16, hipStream_t st)
 {

@@ -187,6 +187,8 @@ void fused_order(int32_t levels, int8_t* order);
 // copy of `chunks` 16-byte chunks from src to dst.
 hipError_t launch_ref_mfma(float* out, int32_t workgroups, int32_t iters, int32_t bf16, hipStream_t stream);
 hipError_t launch_ref_copy(const void* src, void* dst, int64_t chunks, int32_t workgroups, hipStream_t stream);
+hipError_t launch_ref_read(const void* src, int64_t chunks, int32_t workgroups, uint32_t never, uint32_t* out,
+                           hipStream_t stream);
 
 // Size of the device-resident scratch array of the allocation-free entry
 // point (equal to LCMA_SCRATCH_BYTES in lcma.h).

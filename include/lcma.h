@@ -368,11 +368,16 @@ lcma_status gemm_classic(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const v
  * lcma_measure_copy: dst = src over `bytes` (device memory, 16-byte aligned,
  *   a multiple of 16 bytes: else LCMA_E_UNSUPPORTED); reads and writes each
  *   byte once, so HBM traffic is 2 * bytes when both exceed the caches.
- * Both only enqueue on `stream`.
+ * lcma_measure_read: reads `bytes` of src once (same alignment rules), the
+ *   ceiling of read-dominated kernels such as decode products; out is one
+ *   device uint32 that the kernel may write (its value is unspecified).
+ *   LCMA_E_INVALID for a NULL src or out with nonzero bytes.
+ * All only enqueue on `stream`.
  * Source: [KP] "Roofline" (F <= min(F_max, I * B_max): the peaks the
  * roofline is drawn against) and "Benchmark 纪律" (measure, do not assume). */
 lcma_status lcma_measure_mfma(float* out, int32_t workgroups, int32_t iters, lcma_dtype dt, void* stream);
 lcma_status lcma_measure_copy(const void* src, void* dst, size_t bytes, void* stream);
+lcma_status lcma_measure_read(const void* src, size_t bytes, uint32_t* out, void* stream);
 
 /* Frees a plan (NULL is a no-op).  Plans own host memory only.
  * Source: none on the pages (plan lifetime is this library's interface). */

@@ -718,3 +718,11 @@ def test_measurement_entry_points_check_arguments_first():
     assert L._lib_measure_copy(None, 4096, 16, None) == L.E_INVALID
     assert L._lib_measure_copy(4104, 8192, 16, None) == L.E_UNSUPPORTED   # misaligned source
     assert L._lib_measure_copy(4096, 8192, 24, None) == L.E_UNSUPPORTED   # not a multiple of 16 bytes
+    assert L._lib_measure_read(None, 0, None, None) == L.OK               # nothing to read
+    assert L._lib_measure_read(None, 16, 4096, None) == L.E_INVALID
+    assert L._lib_measure_read(4096, 16, None, None) == L.E_INVALID
+    assert L._lib_measure_read(4104, 16, 4096, None) == L.E_UNSUPPORTED   # misaligned source
+    assert L._lib_measure_read(4096, 24, 4096, None) == L.E_UNSUPPORTED   # not a multiple of 16 bytes
+    import torch
+    with pytest.raises(ValueError, match="device tensors"):
+        L.lcma_measure_read(torch.zeros(16, dtype=torch.uint8), torch.zeros(1, dtype=torch.int32))

@@ -1155,9 +1155,11 @@ def test_measurement_references_run_and_copy_exactly():
     src = torch.randint(0, 256, (n,), dtype=torch.uint8, device=DEV)
     dst = torch.zeros_like(src)
     L.lcma_measure_copy(src, dst)
+    word = torch.zeros(2, dtype=torch.int32, device=DEV)
+    L.lcma_measure_read(src, word[:1])       # reads src; may write word[0] only
     out = torch.full((2 * 512,), float("nan"), dtype=torch.float32, device=DEV)
     flops = L.lcma_measure_mfma(out, 2, 10, "bf16")
     torch.cuda.synchronize()
-    assert torch.equal(src, dst)
+    assert torch.equal(src, dst) and int(word[1]) == 0
     assert flops == 2 * 8 * 10 * 16 * 16384
     assert torch.all(torch.isfinite(out))
