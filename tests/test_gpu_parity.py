@@ -554,6 +554,22 @@ def test_classic_k_split_strided_operands_and_output(M, N, K, ldc_pad):
     assert torch.all(Cbig[:, N:].cpu() == 7.0)
 
 
+@pytest.mark.parametrize("M,N,K", [(8, 1024, 8192), (256, 512, 8192)])
+def test_k_split_plans_run_unsplit_on_unaligned_operands(M, N, K):
+    # a plan with a K-split workspace, called with A 2 bytes off 16-byte
+    # alignment: the element-load kernels run instead (same result bound)
+    say("K split plan, unaligned A", M, N, K)
+    A, B, A64, B64 = gen(M, N, K, "bf16", "normal_sqrtk", seed=92)
+    plan = L.lcma_plan_ex(M, N, K, "bf16", force="classic")
+    assert L.lcma_plan_info(plan)[1] > 0
+    flat = torch.zeros(M * K + 1, dtype=torch.bfloat16, device=DEV)
+    flat[1:] = A.reshape(-1).to(DEV)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    L.lcma_gemm(plan, flat[1:].view(M, K), B.to(DEV), C, L.workspace_for(plan))
+    torch.cuda.synchronize()
+    check_float(C.cpu(), A64, B64, "bf16")
+
+
 @pytest.mark.parametrize("M,N,K,ldc_pad", [(5, 1032, 8192, 3), (40, 2056, 4104, 16)])
 def test_decode_k_split_strided_operands_and_output(M, N, K, ldc_pad):
     # leading dimensions beyond the extents (lda, ldb multiples of 8, so the
