@@ -508,6 +508,29 @@ int classic_split_pieces(int64_t M, int64_t N, int64_t K, int P)
     return S > 1 ? S : 0;
 }
 
+// Pieces of K for the last, partial round of a multi-round classic grid on
+// 256 x 256 tiles: its T tiles run as S pieces of K each (T S workgroups
+// within one round, at least 1024 of K per piece), writing compact fp32
+// partial tiles that a third launch adds.  0 for none.  Measured on MI355X
+// (bfloat16, S in 0, 2, 4, 8): the tail round runs faster than a full one,
+// so the split pays with one full round before it (3328 x 5120 x 8192,
+// T = 4: 324.6 us unsplit, 239.0 with S = 8; 4104^3, T = 33: 187.4, 162.3
+// with S = 4), with a small tail (7168^3, T = 16: 614.7, 554.8), or with
+// long K (6144 x 6144 x 12288, T = 64: 769.4, 706.0); not with T = 64 after
+// six rounds at K = 4096 (10240 x 10240 x 4096: 658.5, 662.6).
+int tail_split_pieces(int64_t M, int64_t N, int64_t K, int P)
+{
+    if (M <= 64 || N % 8 != 0 || K % 8 != 0 || K < 4096)
+        return 0;
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256), R = tiles / P, T = tiles % P;
+    if (R == 0 || T == 0 || T > 64 || (R > 1 && T > 32 && K < 8192))
+        return 0;
+    int S = 1;
+    while (S < 8 && T * S * 2 <= P && K / (S * 2) >= 1024)
+        S *= 2;
+    return S > 1 ? S : 0;
+}
+
 }  // namespace
 
 lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const lcma_desc* desc,
@@ -756,14 +779,22 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     p->levels = chosen == LCMA_ALGO_L1 ? 1 : chosen == LCMA_ALGO_L2 ? 2 : 0;
     p->ws_bytes = 0;
     p->n_slots = 0;
-    // decode-shaped classic plans: the workspace of the K-split streaming kernel
-    p->split_s = p->levels == 0 ? split_pieces(M, N, K) : 0;
+    // K splits of classic plans (none with LCMA_SPLIT_NONE, which keeps
+    // classic plans free of workspace): decode shapes on the streaming
+    // kernels; beyond 64 rows, few tiles on 128 x 128 tiles, or the last,
+    // partial round of a multi-round 256 x 256 grid
+    const bool ksplit = p->levels == 0 && o.split != LCMA_SPLIT_NONE;
+    p->split_s = ksplit ? split_pieces(M, N, K) : 0;
     if (p->split_s)
         p->ws_bytes = (size_t)split_ws_bytes(N, p->split_s, split_rows(M));
-    // classic plans beyond 64 rows with few tiles: K split on 128 x 128 tiles
-    if (p->levels == 0 && M > 64 && (p->split_s = classic_split_pieces(M, N, K, m.P)) != 0) {
-        p->classic_tile = kTile128;
-        p->ws_bytes = (size_t)((p->split_s * M * N * 4 + 255) / 256 * 256);
+    if (ksplit && M > 64) {
+        if ((p->split_s = classic_split_pieces(M, N, K, m.P)) != 0) {
+            p->classic_tile = kTile128;
+            p->ws_bytes = (size_t)((p->split_s * M * N * 4 + 255) / 256 * 256);
+        } else if (p->classic_tile == kTile256 && (p->split_s = tail_split_pieces(M, N, K, m.P)) != 0) {
+            const int64_t T = ((M + 255) / 256) * ((N + 255) / 256) % m.P;
+            p->ws_bytes = (size_t)((p->split_s * T * 256 * 256 * 4 + 255) / 256 * 256);
+        }
     }
     p->unfused = p->levels == 1 && (unfused || l1_unfused_auto);
     if (p->unfused) {

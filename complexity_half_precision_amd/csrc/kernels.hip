@@ -1499,19 +1499,21 @@ using MC256 = m16::Cfg<256, 256, 2, 4>;   // 8 waves (2 per SIMD) of 128 x 64, 1
 template <class C, bool BF, bool PART = false>
 __global__ void __launch_bounds__(C::NT, 1)
 k_classic_m16(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B, int64_t ldb, u16* __restrict__ Cm,
-              int64_t ldc, int M, int N, int K, int gy, int gx, int P, int vec4, int vec8, int kh,
-              float* __restrict__ part)
+              int64_t ldc, int M, int N, int K, int gy, int gx, int P, int vec4, int vec8, int tile0, int kh,
+              int tcount, int compact, float* __restrict__ part)
 {
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_ALLOC];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN;
-    // PART: block b is piece b / tiles (k in [piece kh, piece kh + kh)) of
-    // tile b % tiles, which writes an fp32 partial tile of plane `piece`.
-    const int tiles = gy * gx;
-    const int piece = PART ? (int)blockIdx.x / tiles : 0;
+    // Block b works tile tile0 + b.  PART: block b is piece b / tcount (k in
+    // [piece kh, piece kh + kh)) of tile tile0 + b % tcount and writes an fp32
+    // partial tile: into plane `piece` of M x N (row stride N), or, compact,
+    // into slot piece * tcount + b % tcount of BM x BN tiles (row stride BN).
+    const int idx = PART ? (int)blockIdx.x % tcount : (int)blockIdx.x;
+    const int piece = PART ? (int)blockIdx.x / tcount : 0;
     int p, q;
-    tile_coords(PART ? (int32_t)blockIdx.x % tiles : (int32_t)blockIdx.x, gy, gx, P, 8, &p, &q);
+    tile_coords((int32_t)(tile0 + idx), gy, gx, P, 8, &p, &q);
     const int m0 = p * C::BM, n0 = q * C::BN;
     const int kb = piece * kh, klen = PART ? max(0, min(K - kb, kh)) : K;
     const u16* Ab = A + (int64_t)m0 * lda + kb;
@@ -1535,13 +1537,15 @@ k_classic_m16(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B,
         // lane l of accumulator tile (i, j): row 16 i + l % 16, columns
         // 16 j + 4 (l / 16) .. + 3 of the wave's tile; N is a multiple of 8
         // on this path, so each 4-column group is wholly inside or out
-        const rsrc_t rp = make_rsrc(part + (int64_t)piece * M * N + (int64_t)m0 * N + n0);
+        const int pld = compact ? C::BN : N;
+        const rsrc_t rp = make_rsrc(compact ? part + ((int64_t)piece * tcount + idx) * (C::BM * C::BN)
+                                            : part + (int64_t)piece * M * N + (int64_t)m0 * N + n0);
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
             for (int j = 0; j < C::FN; ++j) {
                 const int m = wm * C::WTM + i * 16 + (lane & 15), n = wn * C::WTN + j * 16 + 4 * (lane >> 4);
-                const u32 off = (m < M - m0 && n < N - n0) ? (u32)(m * N + n) * 4u : kOob;
+                const u32 off = (m < M - m0 && n < N - n0) ? (u32)(m * pld + n) * 4u : kOob;
                 __builtin_amdgcn_raw_buffer_store_b128(
                     __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, acc[i][j]), rp, off, 0, 0);
             }
@@ -1566,7 +1570,7 @@ hipError_t launch_classic_m16_t(const ClassicLaunch& L, hipStream_t st)
     const int vec8 = L.vec4 && ((uintptr_t)L.C % 16 == 0) && (L.ldc % 8 == 0) && (L.N % 8 == 0);
     hipLaunchKernelGGL((k_classic_m16<C, BF>), dim3((unsigned)tiles), dim3(C::NT), 0, st,
                        (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, (u16*)L.C, L.ldc, L.M, L.N, L.K,
-                       gy, gx, L.P, L.vec4, vec8, L.K, nullptr);
+                       gy, gx, L.P, L.vec4, vec8, 0, L.K, 1, 0, nullptr);
     return hipGetLastError();
 }
 
@@ -2283,8 +2287,79 @@ hipError_t launch_classic_m16_split_t(const ClassicLaunch& L, hipStream_t st)
     const int kh = ((L.K + S - 1) / S + C::BK - 1) / C::BK * C::BK;
     hipLaunchKernelGGL((k_classic_m16<C, BF, true>), dim3((unsigned)(tiles * S)), dim3(C::NT), 0, st,
                        (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, (u16*)L.C, L.ldc, L.M, L.N, L.K,
-                       gy, gx, L.P, 0, 0, kh, (float*)L.split_ws);
+                       gy, gx, L.P, 0, 0, 0, kh, (int)tiles, 0, (float*)L.split_ws);
     return launch_split_reduce<BF>(L, L.M, L.N, st);
+}
+
+// C over the tail tiles tile0 .. tile0 + T - 1 (tile_coords order) = the sum
+// of their S compact partial tiles (slot piece * T + i, BM x BN fp32 each),
+// in piece order, rounded once.  One thread per 4 consecutive columns of a
+// tile row.
+template <int BM, int BN, bool BF>
+__global__ void __launch_bounds__(256) k_tail_reduce(const f32x4* __restrict__ part, int S, int T, int tile0, int gy,
+                                                     int gx, int P, u16* __restrict__ Cm, int64_t ldc, int M, int N,
+                                                     int vec4)
+{
+    constexpr int CPR = BN / 4, CPT = BM * CPR;
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= (int64_t)T * CPT)
+        return;
+    const int i = (int)(c / CPT), r = (int)(c % CPT) / CPR, c4 = (int)(c % CPR);
+    int p, q;
+    tile_coords((int32_t)(tile0 + i), gy, gx, P, 8, &p, &q);
+    const int m = p * BM + r, n = q * BN + c4 * 4;
+    if (m >= M || n >= N)
+        return;
+    const f32x4* src = part + (int64_t)i * CPT + r * CPR + c4;
+    f32x4 sum = __builtin_nontemporal_load(src);
+    for (int k = 1; k < S; ++k)
+        sum += __builtin_nontemporal_load(src + (int64_t)k * T * CPT);
+    u16* out = Cm + (int64_t)m * ldc + n;
+    if (vec4) {
+        // C 8-byte aligned, ldc and N multiples of 4: the 4 columns are all valid
+        *reinterpret_cast<u32x2*>(out) = u32x2{pack2<BF>(sum.x, sum.y), pack2<BF>(sum.z, sum.w)};
+    } else {
+        const float xs[4] = {sum.x, sum.y, sum.z, sum.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (n + e < N)
+                out[e] = f2h<BF>(xs[e]);
+    }
+}
+
+// The last, partial round of a multi-round classic grid split along K: the
+// full rounds run as usual, then the T tail tiles run as S pieces of K each
+// (T S workgroups, at most one round) writing compact fp32 partial tiles,
+// then k_tail_reduce adds them into C.
+template <class C, bool BF>
+hipError_t launch_classic_m16_tail_t(const ClassicLaunch& L, hipStream_t st)
+{
+    const int gy = (L.M + C::BM - 1) / C::BM, gx = (L.N + C::BN - 1) / C::BN, S = L.split_s;
+    const long tiles = (long)gy * gx;
+    const long full = tiles / L.P * L.P, T = tiles - full;
+    if (tiles == 0)
+        return hipSuccess;
+    if ((S != 2 && S != 4 && S != 8) || full == 0 || T == 0 || T * S > L.P || ((uintptr_t)L.split_ws % 256) != 0)
+        return hipErrorInvalidValue;
+    const int vec8 = L.vec4 && ((uintptr_t)L.C % 16 == 0) && (L.ldc % 8 == 0) && (L.N % 8 == 0);
+    hipLaunchKernelGGL((k_classic_m16<C, BF>), dim3((unsigned)full), dim3(C::NT), 0, st,
+                       (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, (u16*)L.C, L.ldc, L.M, L.N, L.K,
+                       gy, gx, L.P, L.vec4, vec8, 0, L.K, 1, 0, nullptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int kh = ((L.K + S - 1) / S + C::BK - 1) / C::BK * C::BK;
+    hipLaunchKernelGGL((k_classic_m16<C, BF, true>), dim3((unsigned)(T * S)), dim3(C::NT), 0, st,
+                       (const u16*)L.A, L.lda, (const u16*)L.B, L.ldb, (u16*)L.C, L.ldc, L.M, L.N, L.K,
+                       gy, gx, L.P, 0, 0, (int)full, kh, (int)T, 1, (float*)L.split_ws);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t chunks = T * (C::BM * C::BN / 4);
+    hipLaunchKernelGGL((k_tail_reduce<C::BM, C::BN, BF>), dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st,
+                       (const f32x4*)L.split_ws, S, (int)T, (int)full, gy, gx, L.P, (u16*)L.C, L.ldc, L.M, L.N,
+                       L.vec4);
+    return hipGetLastError();
 }
 
 template <class C, bool BF>
@@ -3139,6 +3214,9 @@ hipError_t launch_classic(const ClassicLaunch& L, hipStream_t st)
 {
     switch (L.tile) {
     case kTile256:
+        if (L.vec && L.split_ws)
+            return L.bf16 ? launch_classic_m16_tail_t<MC256, true>(L, st)
+                          : launch_classic_m16_tail_t<MC256, false>(L, st);
         if (L.vec)
             return L.bf16 ? launch_classic_m16_t<MC256, true>(L, st) : launch_classic_m16_t<MC256, false>(L, st);
         return launch_classic_c<Cfg256>(L, st);

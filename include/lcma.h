@@ -74,7 +74,7 @@ typedef enum {
  * FalconGEMM": a group is split over two compute units when needed). */
 typedef enum {
     LCMA_SPLIT_AUTO = 0,  /* split the last, partial round of groups when that shortens it */
-    LCMA_SPLIT_NONE = 1,  /* never split */
+    LCMA_SPLIT_NONE = 1,  /* never split (nor split K in classic plans) */
     LCMA_SPLIT_ALL = 2    /* split every group (testing the fix-up path) */
 } lcma_split;
 
@@ -275,8 +275,11 @@ lcma_status lcma_plan_estimate(lcma_plan_t plan, lcma_algo algo, double* est_sec
  * workspace needs no clearing and keeps nothing between calls.  Classic
  * plans beyond 64 rows whose 128 x 128 tiles fill at most half the compute
  * units, with K >= 4096, split K the same way into S fp32 planes of M x N
- * (S = 2, 4 or 8).  Without 16-byte alignment the unsplit kernels run
- * instead.
+ * (S = 2, 4 or 8); multi-round plans on 256 x 256 tiles split the K of the
+ * last round's T tiles (up to 64) into S compact 256 x 256 fp32 tiles each
+ * (S * T * 256 KiB, at most 64 MiB).  LCMA_SPLIT_NONE in lcma_options turns
+ * every K split off (classic plans then need no workspace).  Without 16-byte
+ * alignment the unsplit kernels run instead.
  * Errors: LCMA_E_INVALID (NULL pointers with nonzero sizes, ld too small),
  * LCMA_E_WORKSPACE, LCMA_E_UNSUPPORTED, LCMA_E_HIP. */
 lcma_status lcma_gemm(lcma_plan_t plan, const void* A, int64_t lda, const void* B, int64_t ldb,

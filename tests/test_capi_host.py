@@ -208,11 +208,12 @@ def test_classic_plan_pads_k_and_n_to_multiples_of_8(M, N, K):
     assert chosen == "classic"
     Np, Kp = -(-N // 8) * 8, -(-K // 8) * 8
     inner = L.lcma_plan_ex(M, Np, Kp, "bf16", force="classic", num_cus=CUS)
-    assert L.lcma_plan_info(inner)[1] == 0
-    assert ws >= 2 * (M * Kp + Kp * Np + M * Np)
+    inner_ws = L.lcma_plan_info(inner)[1]                # a K split of the padded product, if any
+    assert ws >= 2 * (M * Kp + Kp * Np + M * Np) + inner_ws
     assert est > L.lcma_plan_info(inner)[2]
-    # aligned shapes need no workspace
-    assert L.lcma_plan_info(L.lcma_plan_ex(M, Np, Kp, "bf16", num_cus=CUS))[1] == 0
+    # aligned shapes need no workspace beyond a K split's, none with split="none"
+    assert L.lcma_plan_info(L.lcma_plan_ex(M, Np, Kp, "bf16", num_cus=CUS))[1] == inner_ws
+    assert L.lcma_plan_info(L.lcma_plan_ex(M, Np, Kp, "bf16", split="none", num_cus=CUS))[1] == 0
     # the two halves are for LCMA plans only
     assert L._lib_prepass(p.handle, 4096, K, 4096, N, 1 << 20, ws, None) == L.E_INVALID
 
@@ -368,6 +369,22 @@ def test_few_tile_classic_plans_split_k_into_fp32_planes():
                     (8192, 8192, 8192)):
         p = L.lcma_plan_ex(M, N, K, "bf16", force="classic", num_cus=CUS)
         assert L.lcma_plan_info(p)[1] == 0, (M, N, K)
+
+
+def test_multi_round_classic_plans_split_the_tail_round():
+    # 256 x 256 grids of more than one round: the T tiles of the last round
+    # split K into S compact fp32 tiles each (S * T * 256 KiB)
+    for (M, N, K), T, S in (((4104, 4104, 4104), 33, 4), ((3328, 5120, 8192), 4, 8), ((7168, 7168, 7168), 16, 4),
+                            ((6144, 6144, 12288), 64, 4), ((2304, 7424, 4096), 5, 4)):
+        p = L.lcma_plan_ex(M, N, K, "bf16", force="classic", num_cus=CUS)
+        assert L.lcma_plan_info(p)[1] == S * T * 256 * 256 * 4, (M, N, K)
+    for M, N, K in ((4096, 4096, 4096), (16384, 16384, 16384), (10240, 10240, 4096), (6144, 6144, 6144),
+                    (5120, 5120, 8192), (4104, 4104, 2048)):
+        p = L.lcma_plan_ex(M, N, K, "bf16", force="classic", num_cus=CUS)
+        assert L.lcma_plan_info(p)[1] == 0, (M, N, K)
+    # split="none": no K split, no workspace
+    for M, N, K in ((3328, 5120, 8192), (4096, 256, 8192), (1, 4096, 14336)):
+        assert L.lcma_plan_info(L.lcma_plan_ex(M, N, K, "bf16", force="classic", split="none", num_cus=CUS))[1] == 0
 
 
 def test_ragged_decode_plans_pad_then_split():

@@ -530,6 +530,25 @@ def test_classic_k_split_matches_oracle(M, N, K, dtype):
     check_float(planned(A, B, "classic"), A64, B64, dtype)
 
 
+def test_classic_tail_round_k_split_matches_oracle():
+    # 17 x 17 tiles of 256 on 256 compute units: one full round, then 33
+    # tail tiles split into 4 pieces of K (ragged edge tiles and k)
+    say("classic tail split")
+    M = N = K = 4104
+    A, B, A64, B64 = gen(M, N, K, "bf16", "normal_sqrtk", seed=65)
+    plan = L.lcma_plan_ex(M, N, K, "bf16", force="classic")
+    assert L.lcma_plan_info(plan)[1] > 0
+    check_float(planned(A, B, "classic"), A64, B64, "bf16")
+
+
+def test_classic_tail_round_k_split_integer_inputs_are_exact():
+    say("classic tail split exact")
+    A, B, A64, B64 = gen(2304, 7424, 4096, "f16", "int1", seed=66)
+    assert L.lcma_plan_info(L.lcma_plan_ex(2304, 7424, 4096, "f16", force="classic"))[1] > 0
+    assert np.abs(oracle.gemm(A64, B64)).max() <= 2048
+    check_exact(planned(A, B, "classic"), A64, B64, "f16")
+
+
 def test_classic_k_split_integer_inputs_are_exact():
     say("classic K split exact")
     A, B, A64, B64 = gen(2048, 512, 8192, "f16", "int1", seed=64)

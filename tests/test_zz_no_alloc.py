@@ -25,6 +25,7 @@ CASES = [
     ("classic, K split", (64, 4096, 14336), (40, 4104, 8200), "bf16", dict(force="classic")),
     ("classic, K split, 32-row tiles", (1, 1024, 14336), (16, 2056, 8192), "bf16", dict(force="classic")),
     ("classic, K split, 128 x 128 tiles", (4096, 256, 8192), (1024, 1024, 8192), "bf16", dict(force="classic")),
+    ("classic, tail round K split", (4104, 4104, 4104), (2304, 7424, 4096), "bf16", dict(force="classic")),
 ]
 
 
