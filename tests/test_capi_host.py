@@ -382,6 +382,11 @@ def test_multi_round_classic_plans_split_the_tail_round():
                     (5120, 5120, 8192), (4104, 4104, 2048)):
         p = L.lcma_plan_ex(M, N, K, "bf16", force="classic", num_cus=CUS)
         assert L.lcma_plan_info(p)[1] == 0, (M, N, K)
+    # the cost model (which models the unsplit classic kernels) keeps classic
+    # on these shapes, where classic runs the tail split and LCMA is slower
+    for M, N, K in ((7168, 7168, 7168), (6144, 6144, 12288), (4104, 4104, 4104), (3328, 5120, 8192),
+                    (8448, 8192, 8192), (2304, 7424, 4096)):
+        assert L.lcma_plan_info(L.lcma_plan_ex(M, N, K, "bf16", num_cus=CUS))[0] == "classic", (M, N, K)
     # split="none": no K split, no workspace
     for M, N, K in ((3328, 5120, 8192), (4096, 256, 8192), (1, 4096, 14336)):
         assert L.lcma_plan_info(L.lcma_plan_ex(M, N, K, "bf16", force="classic", split="none", num_cus=CUS))[1] == 0
