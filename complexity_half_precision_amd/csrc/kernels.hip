@@ -2,7 +2,12 @@
 //
 //  * k_classic_m16 -- classic GEMM, C = A * B (fp32 accumulate, one RNE
 //                    cast), 256 x 256 tiles, 8 waves of 128 x 64 on 16x16x32
-//                    MFMAs, direct-to-LDS loads.
+//                    MFMAs, direct-to-LDS loads (128 x 128 tiles of 8 waves
+//                    for long K).  Its partial mode runs one piece of K per
+//                    workgroup and writes fp32 partial tiles: for few tiles
+//                    (full M x N planes, added by k_split_reduce) or for the
+//                    last, partial round of a multi-round grid (compact
+//                    tiles, added by k_tail_reduce).
 //  * k_classic_q4 -- the same for 128 x 128 tiles: 4 waves (one per SIMD) of
 //                    64 x 64 on 32x32x16 MFMAs.
 //  * k_skinny     -- M <= 32 products, built to stream B from HBM (private
@@ -43,6 +48,8 @@
 //  * k_fused<2>   -- all 49 products of one output coordinate on one
 //                    workgroup (16 outputs on chip, 64 x 64 tiles) on the
 //                    register-staged path.
+//  * k_ref_mfma, k_ref_copy, k_ref_read -- measured machine references (an
+//                    MFMA loop, a device copy, a read-only stream).
 //
 // Sources: "FalconGEMM: Surpassing Hardware Peaks with Lower-Complexity
 // Matrix Multiplication", sections "从 LCMA 到 FalconGEMM" (combine A/B,
