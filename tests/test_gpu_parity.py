@@ -609,7 +609,7 @@ def test_decode_k_split_strided_operands_and_output(M, N, K, ldc_pad):
     assert torch.all(Cbig[:, N:].cpu() == 7.0)
 
 
-@pytest.mark.parametrize("M,N,K", [(48, 4104, 8200), (8, 4104, 14336), (1024, 1024, 8192)])
+@pytest.mark.parametrize("M,N,K", [(48, 4104, 8200), (8, 4104, 14336), (1024, 1024, 8192), (2304, 7424, 4096)])
 def test_decode_k_split_graph_replays_with_new_inputs(M, N, K):
     # a captured call (the split kernel and the kernel that adds its
     # partials) replays with the inputs changed in place: each replay equals
