@@ -379,6 +379,7 @@ def main():
             for v in leg.values():
                 v["frac_of_read_ref"] = round(v["hbm_gbps"] / out["machine"]["hbm_read_gbps"], 3)
         out["sweep"] = sweep_picks(L, si, torch, time_calls)
+        out["k_split"] = k_split_gains(L, si, torch, time_calls)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(A, B, args.cpu_seconds)
         out["cpu_baseline"]["one_core"] = cpu_baseline_one_core(A, B, args.cpu_seconds)
@@ -616,6 +617,37 @@ def decode_bandwidth(L, si, torch, time_calls, shape=None):
         del calls, ws, Ad, Bs, Cd
     torch.cuda.empty_cache()
     return res
+
+
+K_SPLIT_SHAPES = ((1, 4096, 14336), (64, 4096, 14336), (4096, 256, 8192), (512, 2048, 16384), (256, 256, 16384),
+                  (3328, 5120, 8192), (4104, 4104, 4104), (7168, 7168, 7168))
+
+
+def k_split_gains(L, si, torch, time_calls):
+    """Classic plans whose K is split (decode strips, few tiles, the last
+    partial round of a multi-round grid) against the same product planned
+    with split="none" (the unsplit kernels): bfloat16, A ~ N(0,1)/sqrt(K),
+    prepared calls on resident operands."""
+    rows = []
+    for i, (M, N, K) in enumerate(K_SPLIT_SHAPES):
+        A, B = si.gen(M, N, K, "bf16", "normal_sqrtk", 500 + i)
+        Ad, Bd = A.to("cuda"), B.to("cuda")
+        Cd = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        calls = {mode: L.lcma_gemm_prepared(p, Ad, Bd, Cd, L.workspace_for(p))
+                 for mode in ("auto", "none")
+                 for p in [L.lcma_plan_ex(M, N, K, "bf16", force="classic", split=mode)]}
+        reps = 20 if 2.0 * M * N * K > 1e11 else 100
+        ts = {"auto": [], "none": []}
+        for rnd in range(4):                  # alternating order, median of the rounds
+            for mode in (("auto", "none") if rnd % 2 == 0 else ("none", "auto")):
+                ts[mode].append(time_calls(calls[mode], reps, 5))
+        t = {mode: sorted(v)[len(v) // 2] for mode, v in ts.items()}
+        rows.append({"shape": [M, N, K], "split_us": round(t["auto"] * 1e3, 2), "unsplit_us": round(t["none"] * 1e3, 2),
+                     "speedup": round(t["none"] / t["auto"], 3),
+                     "split_tflops": round(2.0 * M * N * K / (t["auto"] * 1e-3) / 1e12, 1)})
+        del Ad, Bd, Cd
+    torch.cuda.empty_cache()
+    return rows
 
 
 def sweep_picks(L, si, torch, time_calls):
