@@ -213,10 +213,19 @@ def main():
         ts.sort()
         return sum(ts) / len(ts), ts[len(ts) // 2]
 
+    # normwise error of each plan against the float64 product of the same
+    # (already rounded) inputs, formed by torch on the device
+    Cref = torch.matmul(Ad.double(), Bd.double())
+    ref_norm = Cref.norm().item()
+
+    def rel_err():
+        torch.cuda.synchronize()
+        return ((C.double() - Cref).norm() / ref_norm).item()
+
     detail = {}
     only = set(a for a in args.only.split(",") if a)
     plans = {}
-    for algo in ("classic", "l1", "l2", "l2_bf16_operands", "l1_unfused", "l1_at_load"):
+    for algo in ("classic", "l1", "l1_f16_operands", "l2", "l2_bf16_operands", "l1_unfused", "l1_at_load"):
         if only and algo not in only:
             continue
         try:
@@ -229,10 +238,15 @@ def main():
                 # the fused group kernel after a pre-pass (the planner itself
                 # takes the unfused path for large blocks)
                 p = L.lcma_plan_ex(M, N, K, dtype, force="l1", combine="prepass")
+            elif algo == "l1_f16_operands":
+                # one level with the combined operands rounded to binary16
+                # (the default keeps bfloat16 operands at one level)
+                p = L.lcma_plan_ex(M, N, K, dtype, force="l1", combine="prepass", bf16_ops_f16=1)
             elif algo == "l2_bf16_operands":
                 # two levels with the combined operands rounded to bfloat16
-                # (the default rounds them to binary16 for bfloat16 inputs)
-                p = L.lcma_plan_ex(M, N, K, dtype, force="l2", bf16_ops_f16=-1)
+                # (the default rounds them to binary16 for bfloat16 inputs);
+                # outside the 4x error band, so it needs the opt-in
+                p = L.lcma_plan_ex(M, N, K, dtype, force="l2", bf16_ops_f16=-1, accuracy_optin=1)
             else:
                 p = L.lcma_plan_ex(M, N, K, dtype, force=algo)
         except L.LcmaError:
@@ -243,6 +257,8 @@ def main():
     for algo, (p, ws) in plans.items():
         t_all = time_calls(lambda: L.lcma_gemm(p, Ad, Bd, C, ws), reps, args.warmup)
         d = {"ms": t_all, "eff_tflops": flops / (t_all * 1e-3) / 1e12, "est_ms": L.lcma_plan_info(p)[2] * 1e3}
+        L.lcma_gemm(p, Ad, Bd, C, ws)
+        d["rel_err"] = float("%.4g" % rel_err())
         if algo == "l1_at_load":
             mfma_flops = 2.0 * 7 * (M // 2) * (N // 2) * (K // 2)
             d.update({"fused_mfma_tflop": mfma_flops / 1e12, "fused_tflops_actual": mfma_flops / (t_all * 1e-3) / 1e12})
@@ -269,6 +285,10 @@ def main():
         if args.server or algo in ("classic", "l1", "l2", "l1_unfused"):
             d["server_mean_ms"], d["server_p50_ms"] = time_gapped(lambda: L.lcma_gemm(p, Ad, Bd, C, ws), 50)
         detail[algo] = d
+    if "classic" in detail:
+        for d in detail.values():
+            d["err_over_classic"] = d["rel_err"] / detail["classic"]["rel_err"]
+    del Cref
 
     # ---- the step: plan + planned product on the workload
     auto = L.lcma_plan(M, N, K, dtype)
@@ -343,7 +363,7 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2),
         "roofline": roofline,
         "dist": dist,
-        "detail": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+        "detail": {k: {kk: (round(vv, 4) if isinstance(vv, float) and kk != "rel_err" else vv) for kk, vv in v.items()}
                    for k, v in detail.items()},
     }
     if "l1" in detail and "classic" in detail:
@@ -527,8 +547,10 @@ def power_and_clock(L, torch, seconds=2.0):
 def large_square(L, si, torch, time_calls, time_cold):
     """16384^3 bfloat16, A, B ~ N(0,1)/sqrt(K): classic against one level (the
     planner's unfused form and the fused group kernel after a pre-pass) and
-    two levels (binary16 combined operands, the default for bfloat16), each
-    timed back to back on resident inputs; effective TFLOP/s = 2 n^3 / t."""
+    two levels (binary16 combined operands, the default for bfloat16, and
+    bfloat16 operands under the accuracy opt-in), each timed back to back on
+    resident inputs; effective TFLOP/s = 2 n^3 / t.  Each plan's normwise
+    error is taken against the float64 product of the same inputs."""
     w = si.SQUARE_16384_BF16
     n = w["M"]
     A, B = si.gen(**w)
@@ -537,16 +559,22 @@ def large_square(L, si, torch, time_calls, time_cold):
     C = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
     flops = 2.0 * n ** 3
     res = {"workload": f"square GEMM M=N=K={n}, bf16 A,B ~ N(0,1)/sqrt(K), fp32 accumulate, bf16 out"}
+    Cref = torch.matmul(Ad.double(), Bd.double())
+    ref_norm = Cref.norm().item()
     for name, kw in (("classic", dict(force="classic")), ("l1", dict(force="l1")),
-                     ("l1_fused", dict(force="l1", combine="prepass")), ("l2", dict(force="l2"))):
+                     ("l1_fused", dict(force="l1", combine="prepass")), ("l2", dict(force="l2")),
+                     ("l2_bf16_operands", dict(force="l2", bf16_ops_f16=-1, accuracy_optin=1))):
         p = L.lcma_plan_ex(n, n, n, "bf16", **kw)
         ws = L.workspace_for(p)
         t = time_calls(lambda: L.lcma_gemm(p, Ad, Bd, C, ws), 6, 2)
         d = {"ms": round(t, 4), "eff_tflops": round(flops / (t * 1e-3) / 1e12, 1)}
+        L.lcma_gemm(p, Ad, Bd, C, ws)
+        torch.cuda.synchronize()
+        d["rel_err"] = float("%.4g" % ((C.double() - Cref).norm() / ref_norm).item())
         if name != "classic":
             t_pre = time_calls(lambda: L.lcma_prepass(p, Ad, Bd, ws), 6, 1)
-            R = 49 if name == "l2" else 7
-            S = 4 if name == "l2" else 2
+            R = 49 if name.startswith("l2") else 7
+            S = 4 if name.startswith("l2") else 2
             nw = sum(1 for r in range(R) for side in (0, 1) if L.lcma_plan_operand(p, side, r)[0] >= 0)
             pre_bytes = 2.0 * 2 * n * n + 2.0 * nw * (n // S) ** 2
             d.update({"prepass_ms": round(t_pre, 4), "prepass_gbps": round(pre_bytes / (t_pre * 1e-3) / 1e9, 1),
@@ -556,8 +584,10 @@ def large_square(L, si, torch, time_calls, time_cold):
         res[name] = d
         del ws
         torch.cuda.empty_cache()
-    for name in ("l1", "l1_fused", "l2"):
+    for name in ("l1", "l1_fused", "l2", "l2_bf16_operands"):
         res[name]["over_classic"] = round(res["classic"]["ms"] / res[name]["ms"], 4)
+        res[name]["err_over_classic"] = round(res[name]["rel_err"] / res["classic"]["rel_err"], 3)
+    del Cref
     del Ad, Bd, C
     torch.cuda.empty_cache()
     return res
