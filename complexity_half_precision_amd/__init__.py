@@ -86,12 +86,14 @@ _lib_plan_operand = _sig("lcma_plan_operand", _i32, [_vp, _i32, _i32, ctypes.POI
                                                      ctypes.POINTER(_i64), ctypes.POINTER(_i32)])
 _lib_plan_schedule = _sig("lcma_plan_schedule", _i32, [_vp, ctypes.POINTER(_i32), _i64,
                                                        ctypes.POINTER(_i64), ctypes.POINTER(_i32)])
+_lib_plan_runs = _sig("lcma_plan_runs", _i32, [_vp, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32),
+                                               ctypes.POINTER(ctypes.c_int8)])
 _lib_classic = _sig("gemm_classic", _i32, [_i64, _i64, _i64, _i32, _vp, _i64, _vp, _i64, _vp, _i64, _vp])
 _lib_plan_destroy = _sig("lcma_plan_destroy", None, [_vp])
 
 EXPORTED = ["lcma_status_str", "lcma_desc_builtin", "lcma_desc_validate", "lcma_plan", "lcma_plan_ex",
             "lcma_plan_info", "lcma_plan_estimate", "lcma_gemm", "lcma_prepass", "lcma_fused",
-            "lcma_plan_operand", "lcma_plan_schedule", "gemm_classic", "lcma_plan_destroy", "lcma_gemm_noalloc",
+            "lcma_plan_operand", "lcma_plan_schedule", "lcma_plan_runs", "gemm_classic", "lcma_plan_destroy", "lcma_gemm_noalloc",
             "lcma_measure_mfma", "lcma_measure_copy", "lcma_measure_read"]
 SCRATCH_BYTES = 64 << 20   # LCMA_SCRATCH_BYTES
 
@@ -315,6 +317,22 @@ def lcma_plan_schedule(plan: Plan):
     _check(_lib_plan_schedule(plan.handle, buf, n.value, ctypes.byref(n), order), "lcma_plan_schedule")
     items = [tuple(buf[5 * i:5 * i + 5]) for i in range(n.value)]
     return items, list(order)
+
+
+def lcma_plan_runs(plan: Plan, nblocks: int):
+    """Run schedule of a persistent unfused plan: a list of (product, carry,
+    folds into each of the `nblocks` output blocks), one entry per run."""
+    out = []
+    prod, carry = _i32(), _i32()
+    fold = (ctypes.c_int8 * nblocks)()
+    for j in range(64):           # runs 0..rank-1; the first index past them is rejected
+        st = _lib_plan_runs(plan.handle, j, ctypes.byref(prod), ctypes.byref(carry), fold)
+        if st != 0:
+            if j == 0:
+                _check(st, "lcma_plan_runs")
+            break
+        out.append((prod.value, carry.value, list(fold)))
+    return out
 
 
 def lcma_gemm(plan: Plan, A, B, C, workspace=None, workspace_bytes=None, stream=None, lda=None, ldb=None,

@@ -331,6 +331,17 @@ double est_lcma(int64_t M, int64_t N, int64_t K, int levels, int split_req, bool
 
 // ---------------------------------------------------------------- plan
 
+// Run order of the persistent unfused kernel: run j computes product prod[j]
+// starting from zero accumulators (carry 0), from the previous run's
+// accumulators (1) or from their negation (2), then folds w[j][o] times its
+// accumulators into output block o.
+struct RunSchedule {
+    int8_t prod[kGenMaxRank];
+    int8_t carry[kGenMaxRank];
+    int8_t w[kGenMaxRank][kGenMaxBlocks];
+    int searched;          // 1: the exhaustive search below found it
+};
+
 struct lcma_plan_s {
     int64_t M, N, K;
     lcma_dtype dt;
@@ -363,6 +374,7 @@ struct lcma_plan_s {
     int64_t offGA, offGB, offGC;
     int gGroup;            // all products in one persistent launch (enough 256 x 256 positions)
     int gPackA;            // ... with the combined A operands tile-packed (whole 256 x 256 tiles)
+    RunSchedule gRuns;     // ... its run order, carries and folds
     // padded plan: a forced LCMA on a shape that does not split evenly runs
     // `inner` on zero-padded Mp x Kp and Kp x Np copies of A and B in the
     // workspace and crops its Mp x Np product into C
@@ -531,6 +543,263 @@ int tail_split_pieces(int64_t M, int64_t N, int64_t K, int P)
     return S > 1 ? S : 0;
 }
 
+// fp32 bytes that the folds of an output block move per element when k runs
+// feed it: one run rounds straight into C (2 bytes written); otherwise the
+// first stores (4), each middle one reads and writes (8), and the last reads
+// and writes C (4 + 2).
+int fold_bytes(int k) { return k == 0 ? 0 : k == 1 ? 2 : 8 * k - 6; }
+
+int schedule_fold_bytes(const RunSchedule& s, int R, int nout)
+{
+    int b = 0;
+    for (int o = 0; o < nout; ++o) {
+        int k = 0;
+        for (int j = 0; j < R; ++j)
+            k += s.w[j][o] != 0;
+        b += fold_bytes(k);
+    }
+    return b;
+}
+
+// Pairing rule (any description): a product that feeds a single output block
+// o with coefficient +-1 runs right after a product that also feeds o with
+// coefficient +-1 and continues its accumulators: the first run folds its
+// other blocks from the accumulators (which then hold its product alone) and
+// carries o; the second starts from them (negated when the two coefficients
+// differ in sign) and folds the sum, so o takes one fp32 round trip less.
+// The remaining products follow in their own order.
+void pair_schedule(const int8_t* W, int R, int nout, RunSchedule* s)
+{
+    auto w = [&](int r, int o) { return (int)W[r * kGenMaxBlocks + o]; };
+    auto single = [&](int r, int* o_out) {
+        int n = 0, o1 = -1;
+        for (int o = 0; o < nout; ++o)
+            if (w(r, o) != 0) {
+                ++n;
+                o1 = o;
+            }
+        *o_out = o1;
+        return n == 1 && (w(r, o1) == 1 || w(r, o1) == -1);
+    };
+    bool used[kGenMaxRank] = {};
+    int seq[kGenMaxRank], carried[kGenMaxRank], n = 0;   // carried: block a run hands to the next, or -1
+    for (int q = 0; q < R; ++q) {
+        int o;
+        if (used[q] || !single(q, &o))
+            continue;
+        for (int r = 0; r < R; ++r) {
+            if (r == q || used[r] || (w(r, o) != 1 && w(r, o) != -1))
+                continue;
+            used[r] = used[q] = true;
+            seq[n] = r; carried[n] = o; ++n;
+            seq[n] = q; carried[n] = -1; ++n;
+            break;
+        }
+    }
+    for (int r = 0; r < R; ++r)
+        if (!used[r]) {
+            seq[n] = r; carried[n] = -1; ++n;
+        }
+    // the head of a chain does not fold the carried block; the tail folds it
+    // with its own coefficient (its accumulators hold that sign times the sum)
+    memset(s, 0, sizeof *s);
+    for (int j = 0; j < R; ++j) {
+        const int r = seq[j];
+        const bool tail = j > 0 && carried[j - 1] >= 0;
+        s->prod[j] = (int8_t)r;
+        s->carry[j] = (int8_t)(!tail ? 0 : (w(r, carried[j - 1]) == w(seq[j - 1], carried[j - 1]) ? 1 : 2));
+        for (int o = 0; o < nout; ++o)
+            s->w[j][o] = (int8_t)(o == carried[j] ? 0 : w(r, o));
+    }
+}
+
+// Exhaustive search over run orders and carries (descriptions of up to 7
+// products).  After run j the accumulators hold a signed sum of products,
+// its snapshot; output block o must be the sum of some snapshots, each taken
+// with coefficient +-1, equal to its column of W.  The search keeps the
+// schedule whose folds move the fewest fp32 bytes (fold_bytes per block,
+// each block written with at most three snapshots).  Chains (maximal runs
+// that continue their accumulators) commute, so they are enumerated in the
+// order of their first products: about 10^6 candidates at rank 7, 0.2 s.
+// A snapshot is coded as sum_r x_r 7^r (x_r in -1..1); a sum of up to three
+// has digits in -3..3, so equal codes mean equal sums.
+class RunSearch {
+public:
+    static constexpr int kMaxRank = 7;
+
+    bool run(const int8_t* W, int R, int nout, RunSchedule* out)
+    {
+        if (R < 1 || R > kMaxRank || nout < 1 || nout > kGenMaxBlocks)
+            return false;
+        R_ = R;
+        nout_ = nout;
+        int p7 = 1;
+        for (int r = 0; r < R; ++r) {
+            pw_[r] = p7;
+            p7 *= 7;
+        }
+        half_ = p7 / 2;
+        for (int o = 0; o < nout; ++o) {
+            int t = 0;
+            for (int r = 0; r < R; ++r) {
+                const int x = W[r * kGenMaxBlocks + o];
+                if (x < -3 || x > 3)
+                    return false;
+                t += x * pw_[r];
+            }
+            if (t == 0)
+                return false;
+            tgt_[o] = t;
+        }
+        map_.assign((size_t)p7, 0);
+        best_ = 1 << 30;
+        dfs(0, 0, -1, 0);
+        if (best_ == 1 << 30)
+            return false;
+        *out = best_s_;
+        out->searched = 1;
+        return true;
+    }
+
+private:
+    int R_ = 0, nout_ = 0, half_ = 0, best_ = 0;
+    int pw_[kMaxRank], tgt_[kGenMaxBlocks];
+    int seq_[kMaxRank], car_[kMaxRank], snap_[kMaxRank];
+    std::vector<int8_t> map_;   // code + half -> +-(1 + run of that snapshot), 0 if none
+    RunSchedule best_s_;
+
+    int find(int code) const { return code < -half_ || code > half_ ? 0 : map_[(size_t)(code + half_)]; }
+
+    // fewest snapshots (at most kmax) that write block o; 0 if none
+    int rep(int o, int kmax, int* idx, int* coef) const
+    {
+        const int t = tgt_[o];
+        const int e = find(t);
+        if (e != 0) {
+            idx[0] = std::abs(e) - 1;
+            coef[0] = e > 0 ? 1 : -1;
+            return 1;
+        }
+        if (kmax < 2)
+            return 0;
+        for (int i = 0; i < R_; ++i)
+            for (int si = -1; si <= 1; si += 2) {
+                const int f = find(t - si * snap_[i]);
+                if (f != 0 && std::abs(f) - 1 != i) {
+                    idx[0] = i; coef[0] = si;
+                    idx[1] = std::abs(f) - 1; coef[1] = f > 0 ? 1 : -1;
+                    return 2;
+                }
+            }
+        if (kmax < 3)
+            return 0;
+        for (int i = 0; i < R_; ++i)
+            for (int j = i + 1; j < R_; ++j)
+                for (int si = -1; si <= 1; si += 2)
+                    for (int sj = -1; sj <= 1; sj += 2) {
+                        const int f = find(t - si * snap_[i] - sj * snap_[j]);
+                        const int l = std::abs(f) - 1;
+                        if (f != 0 && l != i && l != j) {
+                            idx[0] = i; coef[0] = si;
+                            idx[1] = j; coef[1] = sj;
+                            idx[2] = l; coef[2] = f > 0 ? 1 : -1;
+                            return 3;
+                        }
+                    }
+        return 0;
+    }
+
+    void evaluate()
+    {
+        for (int j = 0; j < R_; ++j) {
+            map_[(size_t)(snap_[j] + half_)] = (int8_t)(1 + j);
+            map_[(size_t)(-snap_[j] + half_)] = (int8_t)(-(1 + j));
+        }
+        int cost = 0, ks[kGenMaxBlocks], idx[kGenMaxBlocks][3], coef[kGenMaxBlocks][3];
+        bool ok = true;
+        for (int o = 0; o < nout_ && ok; ++o) {
+            // the most this block may cost with the schedule still beating the best
+            const int room = best_ - 1 - cost - 2 * (nout_ - 1 - o);
+            const int kmax = room >= fold_bytes(3) ? 3 : room >= fold_bytes(2) ? 2 : room >= fold_bytes(1) ? 1 : 0;
+            ks[o] = kmax > 0 ? rep(o, kmax, idx[o], coef[o]) : 0;
+            ok = ks[o] > 0;
+            cost += ok ? fold_bytes(ks[o]) : 0;
+        }
+        for (int j = 0; j < R_; ++j) {
+            map_[(size_t)(snap_[j] + half_)] = 0;
+            map_[(size_t)(-snap_[j] + half_)] = 0;
+        }
+        if (!ok)
+            return;
+        best_ = cost;
+        memset(&best_s_, 0, sizeof best_s_);
+        for (int j = 0; j < R_; ++j) {
+            best_s_.prod[j] = (int8_t)seq_[j];
+            best_s_.carry[j] = (int8_t)car_[j];
+        }
+        for (int o = 0; o < nout_; ++o)
+            for (int q = 0; q < ks[o]; ++q)
+                best_s_.w[idx[o][q]][o] = (int8_t)coef[o][q];
+    }
+
+    void dfs(int j, int used, int head, int acc)
+    {
+        if (j == R_) {
+            evaluate();
+            return;
+        }
+        for (int p = 0; p < R_; ++p) {
+            if (used >> p & 1)
+                continue;
+            for (int c = 0; c < (j == 0 ? 1 : 3); ++c) {
+                if (c == 0 && p < head)
+                    continue;       // chains in the order of their first products
+                const int v = (c == 0 ? 0 : c == 1 ? acc : -acc) + pw_[p];
+                seq_[j] = p;
+                car_[j] = c;
+                snap_[j] = v;
+                dfs(j + 1, used | 1 << p, c == 0 ? p : head, v);
+            }
+        }
+    }
+};
+
+// The schedule of a description: the searched one when the search applies
+// and moves fewer bytes than the pairing rule, else the pairing rule.
+// Searches are cached per table (a plan is made once per shape).
+void plan_runs(const int8_t* W, int R, int nout, RunSchedule* s)
+{
+    pair_schedule(W, R, nout, s);
+    if (R > RunSearch::kMaxRank)
+        return;
+    struct Entry {
+        int R, nout;
+        int8_t W[kGenMaxRank * kGenMaxBlocks];
+        RunSchedule s;
+        bool found;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const Entry& e : cache)
+        if (e.R == R && e.nout == nout && memcmp(e.W, W, sizeof e.W) == 0) {
+            if (e.found)
+                *s = e.s;
+            return;
+        }
+    Entry e;
+    e.R = R;
+    e.nout = nout;
+    memcpy(e.W, W, sizeof e.W);
+    RunSearch search;
+    e.found = search.run(W, R, nout, &e.s) &&
+              schedule_fold_bytes(e.s, R, nout) < schedule_fold_bytes(*s, R, nout);
+    if (cache.size() < 16)
+        cache.push_back(e);
+    if (e.found)
+        *s = e.s;
+}
+
 }  // namespace
 
 lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const lcma_desc* desc,
@@ -648,18 +917,37 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
     est[LCMA_ALGO_CLASSIC] = est_classic(M, N, K, m);
     bool ok1 = allow_l1 && (unfused ? admissible_unfused() : admissible(1));
     bool ok2 = allow_l2 && !unfused && !at_load && admissible(2);
+    // fp32 fold bytes per element of an output block, summed over the blocks
+    // of a description's unfused path: with enough 256 x 256 positions for
+    // one persistent launch, those of its run schedule; else each product
+    // folds on its own, fold_bytes(c) for a block fed by c products.
+    auto unfused_fold_bytes = [&](const lcma_desc& d) -> double {
+        const int64_t Mb = M / d.ms, Nb = N / d.ns;
+        const int nout = d.ms * d.ns;
+        if (((Mb + 255) / 256) * ((Nb + 255) / 256) >= m.P) {
+            int8_t Wt[kGenMaxRank * kGenMaxBlocks] = {};
+            for (int r = 0; r < d.rank; ++r)
+                for (int o = 0; o < nout; ++o)
+                    Wt[r * kGenMaxBlocks + o] = d.W[r * nout + o];
+            RunSchedule rs;
+            plan_runs(Wt, d.rank, nout, &rs);
+            return schedule_fold_bytes(rs, d.rank, nout);
+        }
+        double b = 0;
+        for (int o = 0; o < nout; ++o) {
+            int c = 0;
+            for (int r = 0; r < d.rank; ++r)
+                c += d.W[r * nout + o] != 0;
+            b += fold_bytes(c);
+        }
+        return b;
+    };
     if (ok1 && unfused) {
-        // pre-pass (every operand written), one GEMM per product, fp32
-        // read-modify-write of the touched output blocks, final cast
+        // pre-pass (every operand written), one GEMM per product, fp32 folds
+        // into the output blocks (the last one rounds into C)
         const int64_t Mb = M / gen.ms, Nb = N / gen.ns, Kb = K / gen.ks;
-        int nnzW = 0;
-        for (int x = 0; x < gen.rank * gen.ms * gen.ns; ++x)
-            nnzW += gen.W[x] != 0;
         const double pre = 2.0 * ((double)M * K + (double)K * N) + 2.0 * gen.rank * ((double)Mb * Kb + (double)Kb * Nb);
-        // fold traffic per element of an output block fed by c products:
-        // 4 bytes stored by the first, 8 read and written by each middle one,
-        // 4 read by the last (which writes 2 bytes of C): 8c - 6
-        const double comb = (8.0 * nnzW - 6.0 * gen.ms * gen.ns) * (double)Mb * Nb;
+        const double comb = unfused_fold_bytes(gen) * (double)Mb * Nb;
         est[LCMA_ALGO_L1] = (pre + comb) / (m.eta_bw * m.bw) + gen.rank * est_classic(Mb, Nb, Kb, m) + 2 * m.launch;
     } else if (ok1 && at_load) {
         est[LCMA_ALGO_L1] = est_lcma(M, N, K, 1, o.split, false, false, m, true);
@@ -676,7 +964,7 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         o.order == LCMA_ORDER_AUTO && admissible_unfused()) {
         const int64_t Mb = M / 2, Nb = N / 2, Kb = K / 2;
         const double pre = 2.0 * ((double)M * K + (double)K * N) + 2.0 * 7 * ((double)Mb * Kb + (double)Kb * Nb);
-        const double comb = (8.0 * 12 - 6.0 * 4) * (double)Mb * Nb;
+        const double comb = unfused_fold_bytes(gen) * (double)Mb * Nb;
         const double t_unf = (pre + comb) / (m.eta_bw * m.bw) + 7 * est_classic(Mb, Nb, Kb, m) + 2 * m.launch;
         if (t_unf < 0.98 * est[LCMA_ALGO_L1]) {
             est[LCMA_ALGO_L1] = t_unf;
@@ -827,6 +1115,8 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         // pre-pass writes the A operands in the engine's stage layout.
         p->gGroup = ((p->gMb + 255) / 256) * ((p->gNb + 255) / 256) >= p->P;
         p->gPackA = p->gGroup && p->gMb % kPackRows == 0 && p->gNb % 256 == 0 && p->gKb % kPackCols == 0;
+        if (p->gGroup)
+            plan_runs(p->gW, gen.rank, gen.ms * gen.ns, &p->gRuns);
     } else if (p->levels > 0) {
         const int L = p->levels;
         p->op_bf16 = op_bf16_for(L);
@@ -955,6 +1245,19 @@ lcma_status lcma_plan_operand(lcma_plan_t p, int32_t side, int32_t r, int64_t* o
         *ld = side == 0 ? p->geo.Kb : p->geo.Nb;
     if (dtype)
         *dtype = p->op_bf16 ? LCMA_BF16 : LCMA_F16;
+    return LCMA_OK;
+}
+
+lcma_status lcma_plan_runs(lcma_plan_t p, int32_t run, int32_t* product, int32_t* carry, int8_t* fold)
+{
+    if (p && p->inner)
+        return lcma_plan_runs(p->inner, run, product, carry, fold);
+    if (!p || !p->unfused || !p->gGroup || run < 0 || run >= p->gR || !product || !carry || !fold)
+        return LCMA_E_INVALID;
+    *product = p->gRuns.prod[run];
+    *carry = p->gRuns.carry[run];
+    for (int o = 0; o < p->gms * p->gns; ++o)
+        fold[o] = p->gRuns.w[run][o];
     return LCMA_OK;
 }
 
@@ -1250,70 +1553,26 @@ lcma_status do_gen_prepass(const lcma_plan_s* p, const void* A, int64_t lda, con
 // one rounds it into C (a block fed by one product goes straight to C), so
 // no fill or final rounding pass is needed.  Brent's identity gives every
 // output block at least one product.
-// Run order and folds of the persistent unfused kernel.  A product that
-// feeds a single output block o with coefficient +-1 runs right after a
-// product that also feeds o with coefficient +-1 and continues its
-// accumulators: the first run folds its other blocks from the accumulators
-// (which then hold its product alone) and carries o; the second starts from
-// them (negated when the two coefficients differ in sign) and folds the sum,
-// so o takes one fp32 round trip less.  The remaining products follow in
-// their own order.  Fold modes (store, add, finish, only) are then those of
-// the run sequence.
+// The persistent launch runs the plan's run schedule; fold modes (store,
+// add, finish, only) follow from the order of the runs that fold into each
+// block.
 void gen_group_runs(const lcma_plan_s* p, int nout, GenGroupLaunch* G)
 {
-    const int R = p->gR;
-    auto W = [&](int r, int o) { return (int)p->gW[r * kGenMaxBlocks + o]; };
-    auto single = [&](int r, int* o_out) {
-        int n = 0, o1 = -1;
-        for (int o = 0; o < nout; ++o)
-            if (W(r, o) != 0) {
-                ++n;
-                o1 = o;
-            }
-        *o_out = o1;
-        return n == 1 && (W(r, o1) == 1 || W(r, o1) == -1);
-    };
-    bool used[kGenMaxRank] = {};
-    int seq[kGenMaxRank], carried[kGenMaxRank], n = 0;   // carried: block a run hands to the next, or -1
-    for (int q = 0; q < R; ++q) {
-        int o;
-        if (used[q] || !single(q, &o))
-            continue;
-        for (int r = 0; r < R; ++r) {
-            if (r == q || used[r] || (W(r, o) != 1 && W(r, o) != -1))
-                continue;
-            used[r] = used[q] = true;
-            seq[n] = r; carried[n] = o; ++n;
-            seq[n] = q; carried[n] = -1; ++n;
-            break;
-        }
-    }
-    for (int r = 0; r < R; ++r)
-        if (!used[r]) {
-            seq[n] = r; carried[n] = -1; ++n;
-        }
-    // Fold coefficient of run j into block o (0 = no fold): the head of a
-    // chain does not fold the carried block; the tail folds it with its own
-    // coefficient (its accumulators hold that sign times the partial sum).
-    int fw[kGenMaxRank][kGenMaxBlocks];
-    for (int j = 0; j < R; ++j) {
-        const int r = seq[j];
-        G->prod[j] = (int8_t)r;
-        const bool tail = j > 0 && carried[j - 1] >= 0;
-        G->carry[j] = !tail ? 0 : (W(r, carried[j - 1]) == W(seq[j - 1], carried[j - 1]) ? 1 : 2);
-        for (int o = 0; o < nout; ++o)
-            fw[j][o] = o == carried[j] ? 0 : W(r, o);
+    const RunSchedule& s = p->gRuns;
+    for (int j = 0; j < p->gR; ++j) {
+        G->prod[j] = s.prod[j];
+        G->carry[j] = s.carry[j];
     }
     for (int o = 0; o < nout; ++o) {
         int f = -1, l = -1, c = 0;
-        for (int j = 0; j < R; ++j)
-            if (fw[j][o] != 0) {
+        for (int j = 0; j < p->gR; ++j)
+            if (s.w[j][o] != 0) {
                 f = f < 0 ? j : f;
                 l = j;
                 ++c;
             }
-        for (int j = 0; j < R; ++j) {
-            const int w = fw[j][o];
+        for (int j = 0; j < p->gR; ++j) {
+            const int w = s.w[j][o];
             G->w[j * kGenMaxBlocks + o] = (int8_t)w;
             G->mode[j * kGenMaxBlocks + o] = w == 0  ? kOuterNone
                                              : c == 1 ? kOuterOnly

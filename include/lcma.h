@@ -351,6 +351,24 @@ lcma_status lcma_plan_operand(lcma_plan_t plan, int32_t side, int32_t r, int64_t
 lcma_status lcma_plan_schedule(lcma_plan_t plan, int32_t* items, int64_t cap, int64_t* count,
                                int32_t* order);
 
+/* Source: [FG] "从 LCMA 到 FalconGEMM" (each output block is the W-weighted
+ * sum of the products; the products of a position accumulate on chip).
+ * Run schedule of an unfused plan whose products run in one persistent
+ * launch, for host-side checking.  Run j (0 <= j < rank) computes product
+ * *product starting from zero accumulators (*carry = 0), from the previous
+ * run's accumulators (1) or from their negation (2), then adds fold[o]
+ * times its accumulators into output block o (ms * ns entries, row-major
+ * block order; 0 = no fold).  Each block is the sum of its folds.  For
+ * descriptions of up to 7 products the planner searches every run order and
+ * carry for the schedule whose fp32 folds move the fewest bytes (a block fed
+ * by k runs moves 2 bytes per element for k = 1, else 8k - 6), which takes
+ * up to about 0.2 s at plan creation (once per table; later plans reuse
+ * it); otherwise a product feeding a single block continues the
+ * accumulators of another product feeding that block.  LCMA_E_INVALID for
+ * any other plan, a run outside 0..rank-1 or NULL outputs.  A padded plan
+ * reports the schedule of its padded product. */
+lcma_status lcma_plan_runs(lcma_plan_t plan, int32_t run, int32_t* product, int32_t* carry, int8_t* fold);
+
 /* Classic MFMA GEMM without a plan (enqueues one kernel on `stream`).
  * Same layout, alignment and error rules as lcma_gemm; K or N not a
  * multiple of 8, or unaligned operands, take the element-load kernel.

@@ -131,6 +131,81 @@ def test_winograd_variant_validates_in_library_and_oracle():
     assert L.lcma_plan_info(p)[0] == "l1"
 
 
+def simulate_runs(runs, R, nblocks):
+    """Replays a run schedule on symbolic products: each run's accumulators
+    are a vector over the R products; block o receives fold[o] times them.
+    Returns the per-block sums (an R x nblocks matrix) and the fp32 bytes
+    the folds move per block element (2 for one fold, else 8k - 6)."""
+    acc = np.zeros(R, np.int64)
+    got = np.zeros((R, nblocks), np.int64)
+    k = np.zeros(nblocks, np.int64)
+    assert sorted(r[0] for r in runs) == list(range(R))
+    for j, (prod, carry, fold) in enumerate(runs):
+        assert carry in (0, 1, 2) and (j > 0 or carry == 0)
+        acc = (np.zeros(R, np.int64) if carry == 0 else acc if carry == 1 else -acc)
+        acc[prod] += 1
+        for o in range(nblocks):
+            if fold[o]:
+                got[:, o] += fold[o] * acc
+                k[o] += 1
+    return got, int(sum(2 if c == 1 else 8 * c - 6 for c in k))
+
+
+def test_unfused_run_schedules_rebuild_each_output_block():
+    # The persistent unfused kernel's runs (order, carried accumulators,
+    # folds) must sum to each output block's column of W.  Strassen's
+    # pairing schedule moves 56 fp32 bytes per block element; Winograd's
+    # searched one 32; the rank-8 block product (beyond the search) pairs
+    # its products so each block takes one fold.
+    n = 8192
+    cases = [(None, oracle.strassen().W, 56),
+             (L.Desc(2, 2, 2, D.WINOGRAD_U, D.WINOGRAD_V, D.WINOGRAD_W), D.WINOGRAD_W, 32)]
+    d8 = oracle.naive()
+    cases.append((L.Desc(2, 2, 2, d8.U, d8.V, d8.W), d8.W, 8))
+    for desc, W, want in cases:
+        if desc is None:
+            p = L.lcma_plan_ex(n, n, n, "bf16", force="l1", combine="unfused", num_cus=CUS)
+        else:
+            p = L.lcma_plan_ex(n, n, n, "bf16", desc=desc, force="l1", num_cus=CUS)
+        runs = L.lcma_plan_runs(p, 4)
+        got, fold_bytes = simulate_runs(runs, W.shape[0], 4)
+        assert np.array_equal(got, W.astype(np.int64)), runs
+        assert fold_bytes == want, (fold_bytes, runs)
+
+
+def test_winograd_schedule_meets_the_lower_bound():
+    # A block written by one fold equals one snapshot, a signed prefix sum of
+    # one chain of carried runs.  Every column of Winograd's W contains
+    # product 1, which lies in one chain, so two single-fold blocks would
+    # have nested supports; no two columns do.  Hence at most one block takes
+    # one fold (2 bytes) and the others at least two (10 bytes each): 32 is
+    # the least any schedule moves, and the searched schedule reaches it.
+    W = D.WINOGRAD_W.astype(np.int64)
+    sup = [set(np.nonzero(W[:, o])[0]) for o in range(4)]
+    assert all(0 in s for s in sup)
+    assert not any(a <= b for a, b in itertools.permutations(sup, 2))
+    p = L.lcma_plan_ex(8192, 8192, 8192, "f16", desc=L.Desc(2, 2, 2, D.WINOGRAD_U, D.WINOGRAD_V, D.WINOGRAD_W),
+                       force="l1", num_cus=CUS)
+    assert simulate_runs(L.lcma_plan_runs(p, 4), 7, 4)[1] == 2 + 3 * 10
+
+
+def test_run_schedules_exist_only_for_persistent_unfused_plans():
+    cases = [L.lcma_plan_ex(4096, 4096, 4096, "bf16", force="classic", num_cus=CUS),
+             L.lcma_plan_ex(4096, 4096, 4096, "bf16", force="l1", combine="prepass", num_cus=CUS),
+             # 512 x 512 blocks: 4 positions, the per-product kernels
+             L.lcma_plan_ex(1024, 1024, 1024, "bf16", force="l1", combine="unfused", num_cus=CUS)]
+    for p in cases:
+        with pytest.raises(L.LcmaError) as e:
+            L.lcma_plan_runs(p, 4)
+        assert e.value.status == L.E_INVALID
+    p = L.lcma_plan_ex(8192, 8192, 8192, "bf16", force="l1", combine="unfused", num_cus=CUS)
+    prod, carry = ctypes.c_int32(), ctypes.c_int32()
+    fold = (ctypes.c_int8 * 4)()
+    for j in (-1, 7):
+        assert L._lib_plan_runs(p.handle, j, ctypes.byref(prod), ctypes.byref(carry), fold) == L.E_INVALID
+    assert L._lib_plan_runs(p.handle, 0, None, ctypes.byref(carry), fold) == L.E_INVALID
+
+
 def test_builtin_scheme_can_be_forced_unfused():
     p = L.lcma_plan_ex(1024, 1024, 1024, "bf16", force="l1", combine="unfused", num_cus=CUS)
     algo, ws, _ = L.lcma_plan_info(p)

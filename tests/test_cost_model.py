@@ -19,6 +19,7 @@ import math
 import pytest
 
 import complexity_half_precision_amd as L
+import descriptors as D
 
 P = 256
 PEAK = 2000e12          # peak_tflops = 2000
@@ -107,15 +108,46 @@ def test_one_level_combined_at_load_4096_cubed():
 
 def test_one_level_unfused_16384_cubed():
     # pre-pass writing all 7 operands per side, 7 classic products of 8192^3,
-    # and the fp32 folds: 8c - 6 bytes per element of an output block fed by c
-    # products; Strassen's W has 12 nonzeros over 4 blocks: (8 * 12 - 6 * 4) Mb Nb
+    # and the fp32 folds: 8c - 6 bytes per element of an output block that
+    # takes c folds (2 for one).  C11 (P1, P4, P5, P7) and C22 (P1, P2, P3, P6)
+    # are fed by four products, C12 and C21 by two; in one persistent launch
+    # P6 continues P1's accumulators and P7 continues P4's, one fold less in
+    # C22 and in C11: 2 * (8 * 3 - 6) + 2 * (8 * 2 - 6) = 56 bytes per Mb Nb
     n, h = 16384, 8192
     pre = 2.0 * 2 * n * n + 2.0 * 7 * 2 * h * h
-    comb = (8.0 * 12 - 6.0 * 4) * h * h
+    comb = 56.0 * h * h
     Fh = 2.0 * h ** 3
     prod = kernel(Fh, 2.0 * 3 * h * h, 128.0, 1.0, ETA_C)      # 1024 tiles of 256^2: 4 full rounds
     want = (pre + comb) / (0.8 * BW) + 7 * prod + 2 * LAUNCH
     p = L.lcma_plan_ex(n, n, n, "bf16", force="l1", combine="unfused", **OPTS)
+    assert close(L.lcma_plan_estimate(p, "l1"), want)
+
+
+def test_one_level_unfused_per_product_2048_cubed():
+    # 1024^2 blocks hold 16 positions of 256^2, too few for one persistent
+    # launch: each product folds on its own, every nonzero of W is a fold:
+    # (8 * 4 - 6) * 2 + (8 * 2 - 6) * 2 = 8 * 12 - 6 * 4 = 72 bytes per Mb Nb;
+    # the 1024^3 products run on 128^2 tiles (64 of them, a quarter round)
+    n, h = 2048, 1024
+    pre = 2.0 * 2 * n * n + 2.0 * 7 * 2 * h * h
+    comb = 72.0 * h * h
+    prod = kernel(2.0 * h ** 3, 2.0 * 3 * h * h, 64.0, 0.25, 0.7 * ETA_C)
+    want = (pre + comb) / (0.8 * BW) + 7 * prod + 2 * LAUNCH
+    p = L.lcma_plan_ex(n, n, n, "bf16", force="l1", combine="unfused", **OPTS)
+    assert close(L.lcma_plan_estimate(p, "l1"), want)
+
+
+def test_one_level_unfused_winograd_16384_cubed():
+    # Winograd's variant in one persistent launch: its searched schedule
+    # writes one block with a single fold (2 bytes) and the other three with
+    # two folds each (10 bytes): 32 per Mb Nb
+    n, h = 16384, 8192
+    pre = 2.0 * 2 * n * n + 2.0 * 7 * 2 * h * h
+    comb = 32.0 * h * h
+    prod = kernel(2.0 * h ** 3, 2.0 * 3 * h * h, 128.0, 1.0, ETA_C)
+    want = (pre + comb) / (0.8 * BW) + 7 * prod + 2 * LAUNCH
+    d = L.Desc(2, 2, 2, D.WINOGRAD_U, D.WINOGRAD_V, D.WINOGRAD_W)
+    p = L.lcma_plan_ex(n, n, n, "bf16", desc=d, force="l1", **OPTS)
     assert close(L.lcma_plan_estimate(p, "l1"), want)
 
 

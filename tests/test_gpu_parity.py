@@ -765,13 +765,20 @@ def test_unfused_group_kernel_matches_oracle(M, N, K, dtype, scheme):
         check_scheme(C, A64, B64, dtype, "l1", e_c, C_ref, desc=winograd_oracle(), unfused=True)
 
 
-def test_unfused_group_kernel_integer_inputs_are_exact():
+@pytest.mark.parametrize("scheme", ["builtin", "winograd"])
+def test_unfused_group_kernel_integer_inputs_are_exact(scheme):
     # the persistent unfused kernel (k-loops of 8 k-tiles over 4096 x 4096
     # blocks, chained accumulators and fp32 folds) on binary16 integers:
-    # |combined operands| <= 4, |H| <= 16 * 256, |C| <= 2048, all exact
-    say("unfused group exact")
+    # |combined operands| <= 4 (Winograd: <= 8), |H| <= 64 * 256 and every
+    # partial sum of the chained runs below 2^24, all exact.  Winograd's
+    # searched schedule chains four runs and negates one.
+    say("unfused group exact", scheme)
     A, B, A64, B64 = gen(8192, 8192, 512, "f16", "int2", seed=38)
-    check_exact(planned(A, B, "l1", combine="unfused"), A64, B64, "f16")
+    if scheme == "builtin":
+        C = planned(A, B, "l1", combine="unfused")
+    else:
+        C = planned_desc(A, B, winograd())
+    check_exact(C, A64, B64, "f16")
 
 
 @pytest.mark.parametrize("M,N,K,dtype", [(1024, 1024, 1024, "bf16"), (512, 768, 640, "f16"), (400, 272, 144, "f16")])
