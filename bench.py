@@ -417,8 +417,9 @@ def targets(out):
         t["lcma_over_classic_4096"] = {"target": 1.08, "measured": round(best, 4)}
     if "large" in out:
         lg = out["large"]
-        t["lcma_over_classic_16384"] = {"target": 1.08, "measured": max(
-            lg[a]["over_classic"] for a in ("l1", "l1_fused", "l2") if a in lg)}
+        forms = [a for a in ("l1", "l1_fused", "l1_winograd", "l2") if a in lg]
+        best = max(forms, key=lambda a: lg[a]["over_classic"])
+        t["lcma_over_classic_16384"] = {"target": 1.08, "measured": lg[best]["over_classic"], "form": best}
     for v in t.values():
         v["met"] = v["measured"] >= v["target"]
     return t
@@ -547,7 +548,8 @@ def power_and_clock(L, torch, seconds=2.0):
 def large_square(L, si, torch, time_calls, time_cold):
     """16384^3 bfloat16, A, B ~ N(0,1)/sqrt(K): classic against one level (the
     planner's unfused form and the fused group kernel after a pre-pass) and
-    two levels (binary16 combined operands, the default for bfloat16, and
+    Winograd's variant on the unfused path (its run schedule moves the fewest
+    fold bytes), two levels (binary16 combined operands, the default for bfloat16, and
     bfloat16 operands under the accuracy opt-in), each timed back to back on
     resident inputs; effective TFLOP/s = 2 n^3 / t.  Each plan's normwise
     error is taken against the float64 product of the same inputs."""
@@ -562,7 +564,8 @@ def large_square(L, si, torch, time_calls, time_cold):
     Cref = torch.matmul(Ad.double(), Bd.double())
     ref_norm = Cref.norm().item()
     for name, kw in (("classic", dict(force="classic")), ("l1", dict(force="l1")),
-                     ("l1_fused", dict(force="l1", combine="prepass")), ("l2", dict(force="l2")),
+                     ("l1_fused", dict(force="l1", combine="prepass")),
+                     ("l1_winograd", dict(force="l1", desc=L.winograd_desc())), ("l2", dict(force="l2")),
                      ("l2_bf16_operands", dict(force="l2", bf16_ops_f16=-1, accuracy_optin=1))):
         p = L.lcma_plan_ex(n, n, n, "bf16", **kw)
         ws = L.workspace_for(p)
@@ -584,7 +587,7 @@ def large_square(L, si, torch, time_calls, time_cold):
         res[name] = d
         del ws
         torch.cuda.empty_cache()
-    for name in ("l1", "l1_fused", "l2", "l2_bf16_operands"):
+    for name in ("l1", "l1_fused", "l1_winograd", "l2", "l2_bf16_operands"):
         res[name]["over_classic"] = round(res["classic"]["ms"] / res[name]["ms"], 4)
         res[name]["err_over_classic"] = round(res[name]["rel_err"] / res["classic"]["rel_err"], 3)
     del Cref

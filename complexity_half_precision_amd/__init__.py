@@ -69,6 +69,7 @@ def _sig(name, res, args):
 
 _lib_status_str = _sig("lcma_status_str", ctypes.c_char_p, [_i32])
 _lib_desc_builtin = _sig("lcma_desc_builtin", _i32, [_i32, ctypes.POINTER(lcma_desc)])
+_lib_desc_winograd = _sig("lcma_desc_winograd", _i32, [ctypes.POINTER(lcma_desc)])
 _lib_desc_validate = _sig("lcma_desc_validate", _i32, [ctypes.POINTER(lcma_desc)])
 _lib_plan_ex = _sig("lcma_plan_ex", _i32, [_i64, _i64, _i64, _i32, ctypes.POINTER(lcma_desc), _i32,
                                            ctypes.POINTER(lcma_options), ctypes.POINTER(_vp)])
@@ -91,7 +92,7 @@ _lib_plan_runs = _sig("lcma_plan_runs", _i32, [_vp, _i32, ctypes.POINTER(_i32), 
 _lib_classic = _sig("gemm_classic", _i32, [_i64, _i64, _i64, _i32, _vp, _i64, _vp, _i64, _vp, _i64, _vp])
 _lib_plan_destroy = _sig("lcma_plan_destroy", None, [_vp])
 
-EXPORTED = ["lcma_status_str", "lcma_desc_builtin", "lcma_desc_validate", "lcma_plan", "lcma_plan_ex",
+EXPORTED = ["lcma_status_str", "lcma_desc_builtin", "lcma_desc_winograd", "lcma_desc_validate", "lcma_plan", "lcma_plan_ex",
             "lcma_plan_info", "lcma_plan_estimate", "lcma_gemm", "lcma_prepass", "lcma_fused",
             "lcma_plan_operand", "lcma_plan_schedule", "lcma_plan_runs", "gemm_classic", "lcma_plan_destroy", "lcma_gemm_noalloc",
             "lcma_measure_mfma", "lcma_measure_copy", "lcma_measure_read"]
@@ -234,14 +235,31 @@ class Desc:
         self.c = lcma_desc(ms, ks, ns, rank, p(self.U), p(self.V), p(self.W))
 
 
-def lcma_desc_builtin(levels: int):
-    """The built-in Strassen scheme as (ms, ks, ns, rank, U, V, W) numpy int8 tables."""
+def _desc_tables(d):
     import numpy as np
-    d = lcma_desc()
-    _check(_lib_desc_builtin(levels, ctypes.byref(d)), "lcma_desc_builtin")
     tab = lambda ptr, n: np.ctypeslib.as_array(ptr, shape=(n,)).copy()
     return (d.ms, d.ks, d.ns, d.rank, tab(d.U, d.rank * d.ms * d.ks).reshape(d.rank, -1),
             tab(d.V, d.rank * d.ks * d.ns).reshape(d.rank, -1), tab(d.W, d.rank * d.ms * d.ns).reshape(d.rank, -1))
+
+
+def lcma_desc_builtin(levels: int):
+    """The built-in Strassen scheme as (ms, ks, ns, rank, U, V, W) numpy int8 tables."""
+    d = lcma_desc()
+    _check(_lib_desc_builtin(levels, ctypes.byref(d)), "lcma_desc_builtin")
+    return _desc_tables(d)
+
+
+def lcma_desc_winograd():
+    """Winograd's variant (rank 7) as (ms, ks, ns, rank, U, V, W) numpy int8 tables."""
+    d = lcma_desc()
+    _check(_lib_desc_winograd(ctypes.byref(d)), "lcma_desc_winograd")
+    return _desc_tables(d)
+
+
+def winograd_desc() -> "Desc":
+    """Winograd's variant as a description for lcma_plan_ex(desc=...)."""
+    ms, ks, ns, _, U, V, W = lcma_desc_winograd()
+    return Desc(ms, ks, ns, U, V, W)
 
 
 def lcma_desc_validate(desc: Desc) -> int:

@@ -458,6 +458,15 @@ lcma_status lcma_desc_builtin(int32_t levels, lcma_desc* out)
     return LCMA_OK;
 }
 
+lcma_status lcma_desc_winograd(lcma_desc* out)
+{
+    if (!out)
+        return LCMA_E_INVALID;
+    static_assert(sizeof kUw == 28 && sizeof kVw == 28 && sizeof kWw == 28, "rank-7 tables of 2x2 blocks");
+    *out = lcma_desc{2, 2, 2, 7, &kUw[0][0], &kVw[0][0], &kWw[0][0]};
+    return LCMA_OK;
+}
+
 lcma_status lcma_desc_validate(const lcma_desc* d)
 {
     if (!d)

@@ -59,4 +59,22 @@ template <> struct Scheme<2> {
     LCMA_HD static constexpr int w(int r, int i, int j) { return coef2(kW1, r, i, j); }
 };
 
+// Winograd's variant of the one-level scheme (rank 7, the same 2x2 split;
+// a textbook description, not one of the pages'), written from its shared
+// sums S1 = A21 + A22, S2 = S1 - A11, S3 = A11 - A21, S4 = A12 - S2 and
+// T1 = B12 - B11, T2 = B22 - T1, T3 = B22 - B12, T4 = T2 - B21:
+//   M1 = A11 B11, M2 = A12 B21, M3 = S4 B22, M4 = A22 T4, M5 = S1 T1,
+//   M6 = S2 T2, M7 = S3 T3;
+//   C11 = M1 + M2, C12 = M1 + M6 + M5 + M3, C21 = M1 + M6 + M7 - M4,
+//   C22 = M1 + M6 + M7 + M5.
+// Three products on each side take a single input block, and its output
+// sums nest, which lets the unfused path's run schedule carry
+// accumulators from product to product.
+constexpr int8_t kUw[7][4] = {{1, 0, 0, 0}, {0, 1, 0, 0}, {1, 1, -1, -1}, {0, 0, 0, 1},
+                              {0, 0, 1, 1}, {-1, 0, 1, 1}, {1, 0, -1, 0}};
+constexpr int8_t kVw[7][4] = {{1, 0, 0, 0}, {0, 0, 1, 0}, {0, 0, 0, 1}, {1, -1, -1, 1},
+                              {-1, 1, 0, 0}, {1, -1, 0, 1}, {0, -1, 0, 1}};
+constexpr int8_t kWw[7][4] = {{1, 1, 1, 1}, {1, 0, 0, 0}, {0, 1, 0, 0}, {0, 0, -1, 0},
+                              {0, 1, 0, 1}, {0, 1, 1, 1}, {0, 0, 1, 1}};
+
 }  // namespace lcma

@@ -178,6 +178,23 @@ typedef struct lcma_plan_s* lcma_plan_t;
  * applied twice, 49 products instead of 64; the U/V/W description). */
 lcma_status lcma_desc_builtin(int32_t levels, lcma_desc* out);
 
+/* Winograd's variant of the one-level scheme (2x2x2, rank 7; a textbook
+ * description, not from the pages), for the unfused path that runs any valid
+ * description: M1 = A11 B11, M2 = A12 B21, M3 = (A11 + A12 - A21 - A22) B22,
+ * M4 = A22 (B11 - B12 - B21 + B22), M5 = (A21 + A22)(B12 - B11),
+ * M6 = (A21 + A22 - A11)(B11 - B12 + B22), M7 = (A11 - A21)(B22 - B12);
+ * C11 = M1 + M2, C12 = M1 + M3 + M5 + M6, C21 = M1 - M4 + M6 + M7,
+ * C22 = M1 + M5 + M6 + M7.  Its output sums nest, so the run schedule of a
+ * persistent unfused plan moves 32 fp32 fold bytes per output block element
+ * against Strassen's 56 (see lcma_plan_runs).  Accuracy: with operands of
+ * the input type its normwise error is about 3.8x that of the classic
+ * product (Strassen's about 2.8x), within the 4x gate; bfloat16 inputs with
+ * binary16 operands (bf16_ops_f16 = 1) about 1.03x.  Static storage owned
+ * by the library.  Errors: LCMA_E_INVALID (out == NULL).
+ * Source: [FG] "从 LCMA 到 FalconGEMM" (a scheme is its U/V/W description;
+ * the same kernels run any of them). */
+lcma_status lcma_desc_winograd(lcma_desc* out);
+
 /* Checks a description: positive sizes, coefficients in [-8, 8], and
  * Brent's identity sum_r U[r][i,k] V[r][k',j] W[r][i',j'] =
  * [k==k'][i==i'][j==j'] (exact integers).  LCMA_OK or LCMA_E_BAD_DESCRIPTOR

@@ -129,6 +129,12 @@ def test_winograd_variant_validates_in_library_and_oracle():
             assert L.lcma_desc_validate(L.Desc(2, 2, 2, *tabs)) == L.E_BAD_DESCRIPTOR
     p = L.lcma_plan_ex(1024, 1024, 1024, "bf16", desc=desc, force="l1", num_cus=CUS)
     assert L.lcma_plan_info(p)[0] == "l1"
+    # the library's own copy of the table, written from the same formulas
+    ms, ks, ns, rank, U, V, W = L.lcma_desc_winograd()
+    assert (ms, ks, ns, rank) == (2, 2, 2, 7)
+    assert np.array_equal(U, D.WINOGRAD_U) and np.array_equal(V, D.WINOGRAD_V) and np.array_equal(W, D.WINOGRAD_W)
+    assert L.lcma_desc_validate(L.winograd_desc()) == L.OK
+    assert L._lib_desc_winograd(None) == L.E_INVALID
 
 
 def simulate_runs(runs, R, nblocks):
