@@ -225,7 +225,8 @@ def main():
     detail = {}
     only = set(a for a in args.only.split(",") if a)
     plans = {}
-    for algo in ("classic", "l1", "l1_f16_operands", "l2", "l2_bf16_operands", "l1_unfused", "l1_at_load"):
+    for algo in ("classic", "l1", "l1_f16_operands", "l2", "l2_bf16_operands", "l1_unfused", "l1_winograd",
+                 "l1_at_load"):
         if only and algo not in only:
             continue
         try:
@@ -242,6 +243,9 @@ def main():
                 # one level with the combined operands rounded to binary16
                 # (the default keeps bfloat16 operands at one level)
                 p = L.lcma_plan_ex(M, N, K, dtype, force="l1", combine="prepass", bf16_ops_f16=1)
+            elif algo == "l1_winograd":
+                # Winograd's variant: the unfused path (any description)
+                p = L.lcma_plan_ex(M, N, K, dtype, desc=L.winograd_desc(), force="l1")
             elif algo == "l2_bf16_operands":
                 # two levels with the combined operands rounded to bfloat16
                 # (the default rounds them to binary16 for bfloat16 inputs);
@@ -336,7 +340,8 @@ def main():
 
     # ---- roofline of the dominant kernel of the chosen path
     if chosen == "classic":
-        t_k = detail["classic"]["ms"]
+        # (an --only run without the classic leg takes the per-call median)
+        t_k = detail["classic"]["ms"] if "classic" in detail else dist["median_ms"]
         achieved = flops / (t_k * 1e-3) / 1e12
         kname, kprefix = "k_classic_m16 (256x256 tile, 8 waves, 16x16x32 MFMA; 2MNK flops per launch)", "k_classic_m16"
     else:
