@@ -71,7 +71,7 @@ def parse():
                     help="only the decode-shape bandwidth measurement (one JSON line), for profiling runs")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the decode-shape bandwidth, 24-shape sweep, 16384^3 and machine measurements")
-    ap.add_argument("--no-large", action="store_true", help="skip the 16384^3 comparison")
+    ap.add_argument("--no-large", action="store_true", help="skip the 16384^3 and 32768^3 comparisons")
     ap.add_argument("--cold", action="store_true",
                     help="also time every kernel with the caches flushed before each call (writes a 512 MiB "
                          "buffer between calls, outside the timed region)")
@@ -397,6 +397,7 @@ def main():
             roofline["frac_at_held_clock"] = round(roofline["achieved"] / held["peak_at_clock_tflops"], 4)
         if not args.no_large:
             out["large"] = large_square(L, si, torch, time_calls, time_cold)
+            out["huge"] = huge_square(L, si, torch)
         out["square_512_f16"] = small_square(L, si, torch, time_calls)
         out["decode"] = decode_bandwidth(L, si, torch, time_calls)
         out["decode_long_k"] = decode_bandwidth(L, si, torch, time_calls, si.decode_long_k_shape)
@@ -425,6 +426,10 @@ def targets(out):
         forms = [a for a in ("l1", "l1_fused", "l1_winograd", "l2") if a in lg]
         best = max(forms, key=lambda a: lg[a]["over_classic"])
         t["lcma_over_classic_16384"] = {"target": 1.08, "measured": lg[best]["over_classic"], "form": best}
+    if "huge" in out:
+        hg = out["huge"]
+        best = max(("l1", "l1_winograd"), key=lambda a: hg[a]["over_classic"])
+        t["lcma_over_classic_32768"] = {"target": 1.08, "measured": hg[best]["over_classic"], "form": best}
     for v in t.values():
         v["met"] = v["measured"] >= v["target"]
     return t
@@ -597,6 +602,53 @@ def large_square(L, si, torch, time_calls, time_cold):
         res[name]["err_over_classic"] = round(res[name]["rel_err"] / res["classic"]["rel_err"], 3)
     del Cref
     del Ad, Bd, C
+    torch.cuda.empty_cache()
+    return res
+
+
+def huge_square(L, si, torch):
+    """32768^3 bfloat16, A, B ~ N(0,1)/sqrt(K): classic against one level on the
+    unfused path, Strassen's scheme and Winograd's variant (each run schedule
+    the planner's), timed in alternating rounds on resident inputs; each
+    plan's normwise error against the float64 product of the same inputs."""
+    w = si.SQUARE_32768_BF16
+    n = w["M"]
+    A, B = si.gen(**w)
+    Ad, Bd = A.to("cuda"), B.to("cuda")
+    del A, B
+    C = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    flops = 2.0 * n ** 3
+    res = {"workload": f"square GEMM M=N=K={n}, bf16 A,B ~ N(0,1)/sqrt(K), fp32 accumulate, bf16 out"}
+    plans = {}
+    for name, kw in (("classic", dict(force="classic")), ("l1", dict(force="l1")),
+                     ("l1_winograd", dict(force="l1", desc=L.winograd_desc()))):
+        p = L.lcma_plan_ex(n, n, n, "bf16", **kw)
+        plans[name] = (p, L.workspace_for(p))
+    ts = {k: [] for k in plans}
+    for rnd in range(4):
+        for k in (list(plans) if rnd % 2 == 0 else list(plans)[::-1]):
+            p, ws = plans[k]
+            L.lcma_gemm(p, Ad, Bd, C, ws)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(2):
+                L.lcma_gemm(p, Ad, Bd, C, ws)
+            e1.record()
+            torch.cuda.synchronize()
+            ts[k].append(e0.elapsed_time(e1) / 2)
+    Cref = torch.matmul(Ad.double(), Bd.double())
+    ref_norm = Cref.norm().item()
+    for k, (p, ws) in plans.items():
+        t = sorted(ts[k])[len(ts[k]) // 2]
+        L.lcma_gemm(p, Ad, Bd, C, ws)
+        torch.cuda.synchronize()
+        res[k] = {"ms": round(t, 4), "eff_tflops": round(flops / (t * 1e-3) / 1e12, 1),
+                  "rel_err": float("%.4g" % ((C.double() - Cref).norm() / ref_norm).item())}
+    for k in ("l1", "l1_winograd"):
+        res[k]["over_classic"] = round(res["classic"]["ms"] / res[k]["ms"], 4)
+        res[k]["err_over_classic"] = round(res[k]["rel_err"] / res["classic"]["rel_err"], 3)
+    del Ad, Bd, C, Cref, plans
     torch.cuda.empty_cache()
     return res
 

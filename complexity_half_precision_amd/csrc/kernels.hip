@@ -2468,7 +2468,25 @@ __global__ void __launch_bounds__(256) k_gen_prepass(const GenPrepassParams gp)
     const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (c >= (int64_t)gp.rows * cpr)
         return;
-    const int row = (int)(c / cpr), col = (int)(c % cpr) * 8;
+    int row, col;
+    u16* out;
+    if constexpr (PK) {
+        // c is the chunk's place in the packed layout, so a wave writes 1 KB
+        // of whole lines: tile row tr, k-tile kt, row rr of the tile,
+        // position pos holding chunk pos ^ ((rr >> 1) & 3) of that row (a
+        // wave reads 64 bytes of 16 rows; the other half of each line is
+        // read by the workgroup four ahead, from L2)
+        const int pos = (int)(c % 4), rr = (int)((c / 4) % kPackRows);
+        const int64_t blk = c / (4 * kPackRows);
+        const int kts = gp.cols / kPackCols;
+        row = (int)(blk / kts) * kPackRows + rr;
+        col = (int)(blk % kts) * kPackCols + (pos ^ ((rr >> 1) & 3)) * 8;
+        out = gp.out + c * 8;
+    } else {
+        row = (int)(c / cpr);
+        col = (int)(c % cpr) * 8;
+        out = gp.out + (int64_t)row * gp.ldo + col;
+    }
     u32x4 v[kGenMaxBlocks];
 #pragma unroll
     for (int b = 0; b < kGenMaxBlocks; ++b) {
@@ -2477,16 +2495,6 @@ __global__ void __launch_bounds__(256) k_gen_prepass(const GenPrepassParams gp)
             v[b] = *reinterpret_cast<const u32x4*>(gp.X + (int64_t)(br * gp.rows + row) * gp.ldx +
                                                    (int64_t)bc * gp.cols + col);
         }
-    }
-    u16* out;
-    if constexpr (PK) {
-        // tile row row / 256, k-tile col / 32, row in the tile rr, chunk
-        // (col / 8) % 4 at position chunk ^ ((rr >> 1) & 3) of its row
-        const int rr = row % kPackRows, ch = (col / 8) % 4;
-        out = gp.out + ((int64_t)(row / kPackRows) * gp.cols + (col / kPackCols) * kPackCols) * kPackRows +
-              rr * kPackCols + (ch ^ ((rr >> 1) & 3)) * 8;
-    } else {
-        out = gp.out + (int64_t)row * gp.ldo + col;
     }
     for (int r = 0; r < gp.rank; ++r) {
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};

@@ -87,6 +87,7 @@ SQUARE_512_F16 = dict(M=512, N=512, K=512, dtype="f16", dist="uniform", seed=0)
 SQUARE_512_F16_INT = dict(M=512, N=512, K=512, dtype="f16", dist="int2", seed=0)
 SQUARE_4096_BF16 = dict(M=4096, N=4096, K=4096, dtype="bf16", dist="normal_sqrtk", seed=0)
 SQUARE_16384_BF16 = dict(M=16384, N=16384, K=16384, dtype="bf16", dist="normal_sqrtk", seed=0)
+SQUARE_32768_BF16 = dict(M=32768, N=32768, K=32768, dtype="bf16", dist="normal_sqrtk", seed=0)
 DECODE_MS = (1, 4, 16, 64)
 
 

@@ -8,6 +8,7 @@ type, which is what the GPU path computes up to fp32 accumulation order.
 import numpy as np
 import pytest
 
+import descriptors as D
 import oracle
 import seeded_inputs as si
 from oracle import metrics
@@ -89,6 +90,41 @@ def test_banded_freivalds_sees_one_zeroed_tile_among_16384_columns():
     assert rows.max() > 2 * u
     # the whole-matrix Freivalds residual does not see it
     assert metrics.freivalds(Cz, A64, B64) <= 4 * u
+
+
+def test_banded_freivalds_of_winograd_and_a_zeroed_tile_among_16384_columns():
+    # Winograd's variant (bfloat16 operands) carries more error than
+    # Strassen's, most in C21 and C22: its 128-row and -column bands stay
+    # within 3 u_out, and a zeroed 16 x 16 tile in C22 still exceeds 3 u_out
+    M, N, K = 512, 16384, 256
+    A, B = si.gen(M, N, K, "bf16", "normal_sqrtk", 8)
+    A64, B64 = si.f64(A), si.f64(B)
+    u = metrics.UNIT_ROUNDOFF["bf16"]
+    d = oracle.Desc(2, 2, 2, D.WINOGRAD_U, D.WINOGRAD_V, D.WINOGRAD_W)
+    Cw, _ = oracle.lcma(A64, B64, d, 1, round_operands="bf16")
+    C = emulate("bf16", Cw)
+    rows, cols = metrics.freivalds_bands(C, A64, B64)
+    assert max(rows.max(), cols.max()) <= 3 * u, (rows.max() / u, cols.max() / u)
+    Cz = C.copy()
+    Cz[400:416, 12000:12016] = 0.0
+    rows, cols = metrics.freivalds_bands(Cz, A64, B64)
+    assert rows.max() > 3 * u and cols.max() > 3 * u, (rows.max() / u, cols.max() / u)
+
+
+def test_banded_freivalds_with_64_wide_bands_among_32768_columns():
+    # twice the columns halve a zeroed tile's share of a 128-row band; a
+    # 64-row band restores it (about 2.8 u_out), above the 2 u_out bound
+    M, N, K = 256, 32768, 64
+    A, B = si.gen(M, N, K, "bf16", "normal_sqrtk", 9)
+    A64, B64 = si.f64(A), si.f64(B)
+    u = metrics.UNIT_ROUNDOFF["bf16"]
+    C = emulate("bf16", oracle.gemm(A64, B64))
+    rows, cols = metrics.freivalds_bands(C, A64, B64, band=64)
+    assert rows.max() <= 2 * u and cols.max() <= 2 * u
+    Cz = C.copy()
+    Cz[100:116, 20000:20016] = 0.0
+    rows, cols = metrics.freivalds_bands(Cz, A64, B64, band=64)
+    assert rows.max() > 2 * u
 
 
 @pytest.mark.parametrize("dtype,dist", [("bf16", "normal_sqrtk"), ("f16", "uniform")])
