@@ -648,6 +648,9 @@ def huge_square(L, si, torch):
     for k in ("l1", "l1_winograd"):
         res[k]["over_classic"] = round(res["classic"]["ms"] / res[k]["ms"], 4)
         res[k]["err_over_classic"] = round(res[k]["rel_err"] / res["classic"]["rel_err"], 3)
+    # the planner's own pick (built-in scheme) against the faster of the two it chooses from
+    res["auto_pick"] = L.lcma_plan_info(L.lcma_plan(n, n, n, "bf16"))[0]
+    res["auto_agrees"] = res["auto_pick"] == min(("classic", "l1"), key=lambda a: res[a]["ms"])
     del Ad, Bd, C, Cref, plans
     torch.cuda.empty_cache()
     return res
