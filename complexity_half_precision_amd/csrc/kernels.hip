@@ -2471,17 +2471,31 @@ __global__ void __launch_bounds__(256) k_gen_prepass(const GenPrepassParams gp)
     int row, col;
     u16* out;
     if constexpr (PK) {
-        // c is the chunk's place in the packed layout, so a wave writes 1 KB
-        // of whole lines: tile row tr, k-tile kt, row rr of the tile,
-        // position pos holding chunk pos ^ ((rr >> 1) & 3) of that row (a
-        // wave reads 64 bytes of 16 rows; the other half of each line is
-        // read by the workgroup four ahead, from L2)
-        const int pos = (int)(c % 4), rr = (int)((c / 4) % kPackRows);
-        const int64_t blk = c / (4 * kPackRows);
+        // Threads walk the packed layout (tile row tr, k-tile kt, row rr of
+        // the tile, position pos holding chunk pos ^ ((rr >> 1) & 3) of that
+        // row).  With an even number of k-tiles, 8 consecutive threads take
+        // the 8 chunks of one row over a pair of k-tiles: a wave reads 8 whole
+        // 128-byte lines of 8 rows and writes two runs of 512 bytes.  Else 4
+        // threads take one k-tile's row (64 bytes read per row).
         const int kts = gp.cols / kPackCols;
-        row = (int)(blk / kts) * kPackRows + rr;
-        col = (int)(blk % kts) * kPackCols + (pos ^ ((rr >> 1) & 3)) * 8;
-        out = gp.out + c * 8;
+        int pos, rr, kt, tr;
+        if ((kts & 1) == 0) {
+            const int j = (int)(c % 8);
+            rr = (int)((c / 8) % kPackRows);
+            const int64_t pr = c / (8 * kPackRows);
+            tr = (int)(pr / (kts / 2));
+            kt = (int)(pr % (kts / 2)) * 2 + j / 4;
+            pos = j % 4;
+        } else {
+            pos = (int)(c % 4);
+            rr = (int)((c / 4) % kPackRows);
+            const int64_t blk = c / (4 * kPackRows);
+            tr = (int)(blk / kts);
+            kt = (int)(blk % kts);
+        }
+        row = tr * kPackRows + rr;
+        col = kt * kPackCols + (pos ^ ((rr >> 1) & 3)) * 8;
+        out = gp.out + (((int64_t)tr * kts + kt) * kPackRows + rr) * kPackCols + pos * 8;
     } else {
         row = (int)(c / cpr);
         col = (int)(c % cpr) * 8;
