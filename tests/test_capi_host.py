@@ -368,6 +368,24 @@ def test_measured_efficiencies_pick_classic_on_big_squares():
         assert L.lcma_plan_info(p)[0] == "classic", n
 
 
+def test_auto_picks_the_unfused_one_level_from_24576_cubed():
+    # with the default efficiencies the model's unfused estimate (pre-pass,
+    # products at the classic rate, the run schedule's folds) falls 2% below
+    # the classic one from 24576^3 on; measured on MI355X, the unfused one
+    # level is 1.014-1.024x the classic kernel at 24576^3 and 32768^3 (the
+    # bench's 32768^3 leg reports the pick and whether it agrees)
+    for n, want in ((16384, "classic"), (24576, "l1"), (32768, "l1")):
+        p = L.lcma_plan_ex(n, n, n, "bf16", num_cus=CUS)
+        assert L.lcma_plan_info(p)[0] == want, n
+        if want == "l1":
+            # the unfused path, all products in one persistent launch
+            assert len(L.lcma_plan_runs(p, 4)) == 7
+    # the model treats binary16 inputs alike (one level keeps the input type
+    # for its operands); that pick is the model's, not measured
+    p = L.lcma_plan_ex(32768, 32768, 32768, "f16", num_cus=CUS)
+    assert L.lcma_plan_info(p)[0] == "l1"
+
+
 def test_efficiency_options_are_validated():
     for kw in ({"classic_eff": -0.1}, {"classic_eff": 1.5}, {"fused_eff": 2.0}, {"fused_eff": float("nan")}):
         with pytest.raises(L.LcmaError):
