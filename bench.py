@@ -83,6 +83,9 @@ def parse():
                          "none/auto and locality/plain order on a tail shape, an all-split shape and 4096^3")
     ap.add_argument("--study-case", default="",
                     help="with --study: run only the case named 'MxNxK:split:order' (for counter runs)")
+    ap.add_argument("--crossover", action="store_true",
+                    help="only the classic / unfused one level comparison on n^3 bfloat16 for n from 8192 to "
+                         "32768 (one JSON line)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="first run 3 device copies of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -106,6 +109,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.crossover:
+        print(json.dumps({"crossover": crossover(L, torch)}), flush=True)
+        return
 
     if args.decode_only:
         def tc(fn, reps, warm):
@@ -654,6 +661,48 @@ def huge_square(L, si, torch):
     del Ad, Bd, C, Cref, plans
     torch.cuda.empty_cache()
     return res
+
+
+def crossover(L, torch, sizes=(8192, 12288, 16384, 20480, 24576, 28672, 32768)):
+    """Where the unfused one level overtakes the classic kernel: n^3 bfloat16
+    with A, B ~ N(0,1)/sqrt(n) drawn on the device (torch's seeded Philox
+    generator; timing only), classic against Strassen and Winograd on the
+    unfused path, timed in alternating rounds (median of 4 rounds of 2 calls),
+    plus the planner's AUTO pick."""
+    g = torch.Generator(device="cuda").manual_seed(0)
+    out = {}
+    for n in sizes:
+        A = (torch.randn(n, n, device="cuda", generator=g) / n ** 0.5).to(torch.bfloat16)
+        B = (torch.randn(n, n, device="cuda", generator=g) / n ** 0.5).to(torch.bfloat16)
+        C = torch.empty(n, n, dtype=torch.bfloat16, device="cuda")
+        plans = {}
+        for name, kw in (("classic", dict(force="classic")), ("strassen", dict(force="l1", combine="unfused")),
+                         ("winograd", dict(force="l1", desc=L.winograd_desc()))):
+            p = L.lcma_plan_ex(n, n, n, "bf16", **kw)
+            plans[name] = (p, L.workspace_for(p))
+        ts = {k: [] for k in plans}
+        for rnd in range(4):
+            for k in (list(plans) if rnd % 2 == 0 else list(plans)[::-1]):
+                p, ws = plans[k]
+                L.lcma_gemm(p, A, B, C, ws)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(2):
+                    L.lcma_gemm(p, A, B, C, ws)
+                e1.record()
+                torch.cuda.synchronize()
+                ts[k].append(e0.elapsed_time(e1) / 2)
+        med = {k: sorted(v)[len(v) // 2] for k, v in ts.items()}
+        row = {k: round(v, 4) for k, v in med.items()}
+        row["strassen_over_classic"] = round(med["classic"] / med["strassen"], 4)
+        row["winograd_over_classic"] = round(med["classic"] / med["winograd"], 4)
+        row["auto_pick"] = L.lcma_plan_info(L.lcma_plan(n, n, n, "bf16"))[0]
+        out[str(n)] = row
+        print(json.dumps({"n": n, **row}), file=sys.stderr, flush=True)
+        del A, B, C, plans
+        torch.cuda.empty_cache()
+    return out
 
 
 def small_square(L, si, torch, time_calls):
