@@ -1655,7 +1655,10 @@ __device__ __forceinline__ void fold_target(rsrc_t rt, rsrc_t rc, int ld, int ld
     if (mode == kOuterNone)
         return;
     auto off_t = [&](int m, int n) { return (m < rows && n < cols) ? (u32)(m * ld + n) * 4u : kOob; };
-    auto put_c = [&](int m, int n, const f32x4& v) {
+    // C gets v + 0: a zero sum written as -0 (a product folded with
+    // coefficient -1, say) becomes +0, as the classic product writes it
+    auto put_c = [&](int m, int n, const f32x4& v0) {
+        const f32x4 v = v0 + 0.0f;
         const u32 oc = (m < rows && n < cols) ? (u32)(m * ldc + n) * 2u : kOob;
         __builtin_amdgcn_raw_buffer_store_b64(
             __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
@@ -2646,9 +2649,16 @@ __device__ __forceinline__ void outer_update(const FusedParams& fp, int m0, int 
                             __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, t[i][j]), ra,
                             off_of(i, j), 0, 0);
             }
-            if (mode == kOuterFinish || mode == kOuterOnly)
+            if (mode == kOuterFinish || mode == kOuterOnly) {
+                // + 0: a zero sum written as -0 becomes +0 (as in the classic product)
+#pragma unroll
+                for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::FN; ++j)
+                        t[i][j] = t[i][j] + 0.0f;
                 store_c<C, CBF, true>(t, fp.C + (int64_t)(bi * fp.Mb + m0) * fp.ldc + bj * fp.Nb + n0, fp.ldc, rows,
                                       cols, wm, wn, lane);
+            }
         }
     }
 }

@@ -17,3 +17,15 @@ WINOGRAD_V = np.array([[1, 0, 0, 0], [0, 0, 1, 0], [0, 0, 0, 1], [1, -1, -1, 1],
                        [-1, 1, 0, 0], [1, -1, 0, 1], [0, -1, 0, 1]], np.int8)
 WINOGRAD_W = np.array([[1, 1, 1, 1], [1, 0, 0, 0], [0, 1, 0, 0], [0, 0, -1, 0],
                        [0, 1, 0, 1], [0, 1, 1, 1], [0, 0, 1, 1]], np.int8)
+
+
+def equivalent(U, V, W, seed):
+    """An equivalent description: products permuted and, per product, U and V
+    negated independently (W takes both signs), which keeps Brent's
+    identity."""
+    U, V, W = (np.asarray(x, np.int64) for x in (U, V, W))
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(U.shape[0])
+    su = rng.choice([-1, 1], U.shape[0])[:, None]
+    sv = rng.choice([-1, 1], U.shape[0])[:, None]
+    return ((U * su)[perm].astype(np.int8), (V * sv)[perm].astype(np.int8), (W * su * sv)[perm].astype(np.int8))

@@ -179,6 +179,23 @@ def test_unfused_run_schedules_rebuild_each_output_block():
         assert fold_bytes == want, (fold_bytes, runs)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_run_schedule_search_is_invariant_under_equivalent_descriptions(seed):
+    # permuting the products and flipping signs changes the tables but not
+    # the least fold bytes a schedule can reach: the search finds 56 for
+    # every form of Strassen's scheme and 32 for every form of Winograd's,
+    # and its runs rebuild the transformed W exactly
+    for U0, V0, W0, want in ((oracle.strassen().U, oracle.strassen().V, oracle.strassen().W, 56),
+                             (D.WINOGRAD_U, D.WINOGRAD_V, D.WINOGRAD_W, 32)):
+        U, V, W = D.equivalent(U0, V0, W0, seed)
+        d = oracle.Desc(2, 2, 2, U, V, W)
+        assert oracle.brent_violations(d) == 0
+        p = L.lcma_plan_ex(8192, 8192, 8192, "bf16", desc=L.Desc(2, 2, 2, U, V, W), force="l1", num_cus=CUS)
+        got, fold_bytes = simulate_runs(L.lcma_plan_runs(p, 4), 7, 4)
+        assert np.array_equal(got, W.astype(np.int64))
+        assert fold_bytes == want, (seed, fold_bytes)
+
+
 def test_winograd_schedule_meets_the_lower_bound():
     # A block written by one fold equals one snapshot, a signed prefix sum of
     # one chain of carried runs.  Every column of Winograd's W contains

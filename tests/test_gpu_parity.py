@@ -765,7 +765,7 @@ def test_unfused_group_kernel_matches_oracle(M, N, K, dtype, scheme):
         check_scheme(C, A64, B64, dtype, "l1", e_c, C_ref, desc=winograd_oracle(), unfused=True)
 
 
-@pytest.mark.parametrize("scheme", ["builtin", "winograd"])
+@pytest.mark.parametrize("scheme", ["builtin", "winograd", "winograd_signed"])
 def test_unfused_group_kernel_integer_inputs_are_exact(scheme):
     # the persistent unfused kernel (k-loops of 8 k-tiles over 4096 x 4096
     # blocks, chained accumulators and fp32 folds) on binary16 integers:
@@ -776,8 +776,12 @@ def test_unfused_group_kernel_integer_inputs_are_exact(scheme):
     A, B, A64, B64 = gen(8192, 8192, 512, "f16", "int2", seed=38)
     if scheme == "builtin":
         C = planned(A, B, "l1", combine="unfused")
-    else:
+    elif scheme == "winograd":
         C = planned_desc(A, B, winograd())
+    else:
+        # an equivalent form with permuted products and flipped signs: other
+        # chains, carries and negated folds, same result
+        C = planned_desc(A, B, L.Desc(2, 2, 2, *D.equivalent(D.WINOGRAD_U, D.WINOGRAD_V, D.WINOGRAD_W, 3)))
     check_exact(C, A64, B64, "f16")
 
 
