@@ -374,6 +374,7 @@ struct lcma_plan_s {
     int64_t offGA, offGB, offGC;
     int gGroup;            // all products in one persistent launch (enough 256 x 256 positions)
     int gPackA;            // ... with the combined A operands tile-packed (whole 256 x 256 tiles)
+    int64_t gLdB;          // leading dimension of the written B operands (Nb, padded in one launch)
     RunSchedule gRuns;     // ... its run order, carries and folds
     // padded plan: a forced LCMA on a shape that does not split evenly runs
     // `inner` on zero-padded Mp x Kp and Kp x Np copies of A and B in the
@@ -551,6 +552,12 @@ int tail_split_pieces(int64_t M, int64_t N, int64_t K, int P)
         S *= 2;
     return S > 1 ? S : 0;
 }
+
+// Padding of the written B operands' rows in one persistent unfused launch
+// (elements): 8192-element rows (16 KB) at a 16 KB + 128 B pitch.  Measured
+// at 32768^3 bfloat16: 48.10 -> 46.83 ms (Winograd), 48.37 -> 47.69 ms
+// (Strassen); within noise at 8192^3 and 16384^3 (64, 128 and 256 alike).
+constexpr int64_t kGenBPad = 64;
 
 // fp32 bytes that the folds of an output block move per element when k runs
 // feed it: one run rounds straight into C (2 bytes written); otherwise the
@@ -1111,11 +1118,12 @@ lcma_status lcma_plan_ex(int64_t M, int64_t N, int64_t K, lcma_dtype dt, const l
         }
         // geometry of the one level (for lcma_plan_operand)
         p->geo.Mb = p->gMb; p->geo.Kb = p->gKb; p->geo.Nb = p->gNb; p->geo.R = gen.rank; p->geo.S = 0;
+        p->gLdB = p->gNb + ((((p->gMb + 255) / 256) * ((p->gNb + 255) / 256) >= p->P) ? kGenBPad : 0);
         int64_t off = 0;
         p->offGA = off;
         off = align_up(off + (int64_t)gen.rank * p->gMb * p->gKb * 2, 256);
         p->offGB = off;
-        off = align_up(off + (int64_t)gen.rank * p->gKb * p->gNb * 2, 256);
+        off = align_up(off + (int64_t)gen.rank * p->gKb * p->gLdB * 2, 256);
         p->offGC = off;
         off = align_up(off + (int64_t)gen.ms * gen.ns * p->gMb * p->gNb * 4, 256);
         p->ws_bytes = (size_t)off;
@@ -1238,9 +1246,9 @@ lcma_status lcma_plan_operand(lcma_plan_t p, int32_t side, int32_t r, int64_t* o
     }
     if (p->unfused) {
         if (offset)
-            *offset = side == 0 ? p->offGA + (int64_t)r * p->gMb * p->gKb * 2 : p->offGB + (int64_t)r * p->gKb * p->gNb * 2;
+            *offset = side == 0 ? p->offGA + (int64_t)r * p->gMb * p->gKb * 2 : p->offGB + (int64_t)r * p->gKb * p->gLdB * 2;
         if (ld)
-            *ld = side == 0 ? (p->gPackA ? 0 : p->gKb) : p->gNb;
+            *ld = side == 0 ? (p->gPackA ? 0 : p->gKb) : p->gLdB;
         if (dtype)
             *dtype = p->op_bf16 ? LCMA_BF16 : LCMA_F16;
         return LCMA_OK;
@@ -1552,7 +1560,7 @@ lcma_status do_gen_prepass(const lcma_plan_s* p, const void* A, int64_t lda, con
     L.X = B; L.ldx = ldb; L.rows = (int32_t)p->gKb; L.cols = (int32_t)p->gNb; L.bcols = p->gns;
     L.nblocks = p->gks * p->gns;
     memcpy(L.coef, p->gV, sizeof L.coef);
-    L.out = (char*)ws + p->offGB; L.ldo = p->gNb; L.stride = p->gKb * p->gNb;
+    L.out = (char*)ws + p->offGB; L.ldo = p->gLdB; L.stride = p->gKb * p->gLdB;
     return hip_status(launch_gen_prepass(L, st), "launch_gen_prepass");
 }
 
@@ -1616,7 +1624,7 @@ lcma_status do_gen_products(const lcma_plan_s* p, void* C, int64_t ldc, void* ws
         GenGroupLaunch G;
         memset(&G, 0, sizeof G);
         G.A0 = (const char*)ws + p->offGA; G.strideA = p->gMb * p->gKb;
-        G.B0 = (const char*)ws + p->offGB; G.strideB = p->gKb * p->gNb;
+        G.B0 = (const char*)ws + p->offGB; G.strideB = p->gKb * p->gLdB; G.ldb = p->gLdB;
         G.M = (int32_t)p->gMb; G.N = (int32_t)p->gNb; G.K = (int32_t)p->gKb; G.R = p->gR;
         G.op_bf16 = p->op_bf16; G.out_bf16 = p->dt == LCMA_BF16; G.P = p->P;
         G.nout = nout; G.ncols = p->gns;
@@ -1629,7 +1637,7 @@ lcma_status do_gen_products(const lcma_plan_s* p, void* C, int64_t ldc, void* ws
         GenProductLaunch L;
         memset(&L, 0, sizeof L);
         L.A = (const char*)ws + p->offGA + (int64_t)r * p->gMb * p->gKb * 2; L.lda = p->gKb;
-        L.B = (const char*)ws + p->offGB + (int64_t)r * p->gKb * p->gNb * 2; L.ldb = p->gNb;
+        L.B = (const char*)ws + p->offGB + (int64_t)r * p->gKb * p->gLdB * 2; L.ldb = p->gLdB;
         L.M = (int32_t)p->gMb; L.N = (int32_t)p->gNb; L.K = (int32_t)p->gKb;
         L.op_bf16 = p->op_bf16; L.P = p->P; L.ldt = p->gNb;
         L.ldc = ldc; L.out_bf16 = p->dt == LCMA_BF16;

@@ -1762,7 +1762,8 @@ k_gen_product(const u16* __restrict__ A, int64_t lda, const u16* __restrict__ B,
 // folds of different workgroups fall at different times.
 struct GenGroupParams {
     const u16* A0; int64_t strideA;    // combined A operand r at A0 + r * strideA (M x K, ld K)
-    const u16* B0; int64_t strideB;    // combined B operand r at B0 + r * strideB (K x N, ld N)
+    const u16* B0; int64_t strideB;    // combined B operand r at B0 + r * strideB (K x N, ld ldb)
+    int ldb;
     int M, N, K, R, P, nout, ncols;
     float* acc;                        // fp32 block o at acc + o * M * N (ld N)
     u16* C; int64_t ldc;               // block o of C at row (o / ncols) * M, column (o % ncols) * N
@@ -1804,7 +1805,7 @@ __global__ void __launch_bounds__(C::NT, 1) k_gen_group_m16(const GenGroupParams
             const u16* Ab = gp.A0 + r * gp.strideA + (int64_t)m0 * gp.K;
             const u16* Bb = gp.B0 + r * gp.strideB + n0;
             auto src = [&](int t) {
-                return tiles::TileSrc{Ab, gp.K, rows, Bb, gp.N, cols, t * C::BK, gp.K};
+                return tiles::TileSrc{Ab, gp.K, rows, Bb, gp.ldb, cols, t * C::BK, gp.K};
             };
             if (cy == 0) {
                 zero_acc<C>(acc);
@@ -1846,6 +1847,9 @@ hipError_t launch_gen_group_t(const GenGroupLaunch& L, hipStream_t st)
     GenGroupParams gp;
     gp.A0 = (const u16*)L.A0; gp.strideA = L.strideA;
     gp.B0 = (const u16*)L.B0; gp.strideB = L.strideB;
+    if (L.ldb < L.N || L.ldb >= ((int64_t)1 << 21))
+        return hipErrorInvalidValue;
+    gp.ldb = (int)L.ldb;
     gp.M = L.M; gp.N = L.N; gp.K = L.K; gp.R = L.R; gp.P = L.P; gp.nout = L.nout; gp.ncols = L.ncols;
     gp.acc = L.acc;
     gp.C = (u16*)L.C; gp.ldc = L.ldc;

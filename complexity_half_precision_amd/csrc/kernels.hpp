@@ -157,7 +157,7 @@ hipError_t launch_gen_product(const GenProductLaunch& L, hipStream_t stream);
 // block o of C at row (o / ncols) * M, column (o % ncols) * N.
 struct GenGroupLaunch {
     const void* A0; int64_t strideA;       // packed_a = 1: the A operands are tile-packed (GenPrepassLaunch)
-    const void* B0; int64_t strideB;
+    const void* B0; int64_t strideB; int64_t ldb;   // B operands: leading dimension ldb >= N
     int32_t M, N, K, R, op_bf16, out_bf16, P, nout, ncols;
     float* acc;
     void* C; int64_t ldc;

@@ -429,17 +429,22 @@ def test_workspace_layout_of_one_level_plan():
 
 def test_unfused_plan_packs_its_a_operands_only_on_whole_tiles():
     # one persistent launch on whole 256 x 256 tiles: every combined A operand
-    # is tile-packed (ld 0), the B operands stay row-major
-    for (M, N, K), packed in (((8192, 8192, 512), True), ((8192, 8192, 528), False), ((8192, 8000, 512), False),
-                              ((2048, 2048, 512), False)):
+    # is tile-packed (ld 0); the B operands stay row-major, their rows padded
+    # by 64 elements in one persistent launch (one launch per product: ld Nb)
+    for (M, N, K), packed, group in (((8192, 8192, 512), True, True), ((8192, 8192, 528), False, True),
+                                     ((8192, 8000, 512), False, True), ((2048, 2048, 512), False, False)):
         p = L.lcma_plan_ex(M, N, K, "bf16", force="l1", combine="unfused", num_cus=CUS)
         assert L.lcma_plan_info(p)[0] == "l1"
+        ldb = N // 2 + (64 if group else 0)
+        offs = []
         for r in range(7):
             off_a, ld_a, _ = L.lcma_plan_operand(p, 0, r)
             off_b, ld_b, _ = L.lcma_plan_operand(p, 1, r)
             assert off_a >= 0 and off_b >= 0
             assert ld_a == (0 if packed else K // 2), (M, N, K, ld_a)
-            assert ld_b == N // 2
+            assert ld_b == ldb, (M, N, K, ld_b)
+            offs.append(off_b)
+        assert [o - offs[0] for o in offs] == [r * (K // 2) * ldb * 2 for r in range(7)]
 
 
 def test_decode_shaped_classic_plans_take_the_k_split_workspace():

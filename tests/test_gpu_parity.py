@@ -357,8 +357,9 @@ def _unpack_a(x, rows, cols):
 
 def test_unfused_prepass_writes_tile_packed_a_operands():
     # blocks of 4096 x 4096 on whole 256 x 256 tiles: the A operands are
-    # tile-packed (ld 0), the B operands row-major; both are the RNE of the
-    # exact combination, bit for bit where the fp32 sum is exact
+    # tile-packed (ld 0), the B operands row-major with rows padded by 64
+    # elements; both are the RNE of the exact combination, bit for bit where
+    # the fp32 sum is exact
     say("unfused packed operands")
     M, N, K = 8192, 8192, 512
     A, B, A64, B64 = gen(M, N, K, "bf16", "normal_sqrtk", seed=12)
@@ -371,10 +372,14 @@ def test_unfused_prepass_writes_tile_packed_a_operands():
         rows, cols = (M // 2, K // 2) if side == 0 else (K // 2, N // 2)
         for r in range(7):
             off, ld, odt = L.lcma_plan_operand(plan, side, r)
-            assert off >= 0 and ld == (0 if side == 0 else cols)
+            assert off >= 0 and ld == (0 if side == 0 else cols + 64)
             odt = "f16" if odt == L.F16 else "bf16"
-            got = ws[off:off + rows * cols * 2].cpu().view(torch.int16).numpy().view(np.uint16)
-            got = _unpack_a(got, rows, cols) if side == 0 else got.reshape(rows, cols)
+            if side == 0:
+                got = ws[off:off + rows * cols * 2].cpu().view(torch.int16).numpy().view(np.uint16)
+                got = _unpack_a(got, rows, cols)
+            else:
+                raw = ws[off:off + ((rows - 1) * ld + cols) * 2].cpu().view(torch.int16).numpy().view(np.uint16)
+                got = np.lib.stride_tricks.as_strided(raw, (rows, cols), (ld * 2, 2))
             exact = oracle.combine_block(X, T[r], 2, 2)
             want = oracle.encode(odt, exact)
             fp32_exact = np.float32(exact).astype(np.float64) == exact
