@@ -637,8 +637,10 @@ void pair_schedule(const int8_t* W, int R, int nout, RunSchedule* s)
 // each block written with at most three snapshots).  Chains (maximal runs
 // that continue their accumulators) commute, so they are enumerated in the
 // order of their first products: about 10^6 candidates at rank 7, 0.2 s.
-// A snapshot is coded as sum_r x_r 7^r (x_r in -1..1); a sum of up to three
-// has digits in -3..3, so equal codes mean equal sums.
+// A vector over the products is coded as sum_r x_r 7^r.  Snapshots have
+// entries in -1..1 and W's columns (checked) in -3..3, so a column minus two
+// signed snapshots, compared with a third, differs from it by entries of
+// magnitude at most 6: two codes are equal only if the vectors are (base 7).
 class RunSearch {
 public:
     static constexpr int kMaxRank = 7;
